@@ -1,0 +1,251 @@
+"""Seeded synthetic inputs for the KDA workloads.
+
+This module only draws random numbers and lays them out. It holds none of the
+recurrence's arithmetic, so both the HIP path (through the binding) and the CPU
+oracle (through the tests and the benchmark's CPU leg) take their inputs from
+here and from nowhere else.
+
+Recipe (per (sequence, head, 4096-token block) the generator is
+``numpy.random.default_rng([seed, seq, head, block])`` (PCG64), and it draws, in
+this order, for the block's n tokens):
+
+1. q ~ N(0, 1) [n, d_k]; 2. k ~ N(0, 1) [n, d_k]; 3. v ~ N(0, 1) [n, d_v];
+4. z ~ N(0, 1) [n], beta = sigmoid(z); 5. g ~ U(-0.1, 0) [n, d_k] (log-decay).
+
+q and k are then L2-normalised per token in fp32 (the recurrence assumes unit
+keys; the caller, not the kernel, normalises) and cast to the workload dtype
+(bf16 by round-to-nearest-even, or kept fp32).  An initial state, where a
+workload has one, is N(0, 0.02^2) fp32 from ``default_rng([seed, seq, head,
+STATE_TAG])``.  Accepted verify lengths and ragged sequence lengths come from
+their own streams (``ACC_TAG``, ``LEN_TAG``).
+
+Arrays are packed the way the library takes them: q, k, v, g as
+[T_total, H, d]; beta as [T_total, H]; states as [N, H, d_k, d_v] (rows are key
+channels); ``cu_seqlens`` int32 [N + 1].  bf16 tensors are returned as numpy
+uint16 bit patterns; ``bf16_bits_to_f32`` widens them exactly.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+
+BLOCK = 4096
+STATE_TAG = 0x5354415445  # "STATE"
+ACC_TAG = 0x414343  # "ACC"
+LEN_TAG = 0x4C454E  # "LEN"
+STATE_STD = 0.02
+
+
+# --------------------------------------------------------------------------
+# dtype helpers (exact conversions; no arithmetic of the method)
+# --------------------------------------------------------------------------
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns (uint16), round to nearest, ties to even."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    rounding = 0x7FFF + ((u >> 16) & 1)
+    out = ((u + rounding) >> 16).astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = 0x7FC0
+    return out
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> fp32, exact."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def as_f64(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact fp64 value of an input array held as ``dtype`` ('bf16' or 'f32')."""
+    if dtype == "bf16":
+        return bf16_bits_to_f32(x).astype(np.float64)
+    return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# one (sequence, head, block) draw
+# --------------------------------------------------------------------------
+def _draw_block(seed: int, seq: int, head: int, block: int, n: int, dk: int, dv: int):
+    rng = np.random.default_rng([seed, seq, head, block])
+    q = rng.standard_normal((n, dk), dtype=np.float32)
+    k = rng.standard_normal((n, dk), dtype=np.float32)
+    v = rng.standard_normal((n, dv), dtype=np.float32)
+    z = rng.standard_normal(n, dtype=np.float32)
+    g = rng.random((n, dk), dtype=np.float32) * np.float32(-0.1)
+    q /= np.sqrt(np.sum(q * q, axis=1, keepdims=True, dtype=np.float32))
+    k /= np.sqrt(np.sum(k * k, axis=1, keepdims=True, dtype=np.float32))
+    beta = (np.float32(1.0) / (np.float32(1.0) + np.exp(-z))).astype(np.float32)
+    return q, k, v, beta, g
+
+
+def draw_state(seed: int, seq: int, head: int, dk: int, dv: int) -> np.ndarray:
+    rng = np.random.default_rng([seed, seq, head, STATE_TAG])
+    return (rng.standard_normal((dk, dv), dtype=np.float32) * np.float32(STATE_STD)).astype(np.float32)
+
+
+@dataclass
+class Packed:
+    """A packed ragged batch, as the library takes it."""
+
+    dtype: str                 # 'bf16' or 'f32' (q, k, v); g, beta, states are fp32
+    q: np.ndarray              # [T, H, dk]  uint16 bits (bf16) or float32
+    k: np.ndarray              # [T, H, dk]
+    v: np.ndarray              # [T, H, dv]
+    g: np.ndarray              # [T, H, dk]  float32 log-decay
+    beta: np.ndarray           # [T, H]      float32
+    cu_seqlens: np.ndarray     # [N + 1]     int32
+    initial_state: Optional[np.ndarray]  # [N, H, dk, dv] float32 or None (zeros)
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.cu_seqlens.shape[0] - 1)
+
+    @property
+    def H(self) -> int:
+        return int(self.q.shape[1])
+
+    @property
+    def T(self) -> int:
+        return int(self.q.shape[0])
+
+    def f64(self, name: str) -> np.ndarray:
+        """Exact fp64 copy of one input tensor."""
+        x = getattr(self, name)
+        if name in ("q", "k", "v"):
+            return as_f64(x, self.dtype)
+        return np.asarray(x, dtype=np.float64)
+
+
+def _cast(x: np.ndarray, dtype: str) -> np.ndarray:
+    return f32_to_bf16_bits(x) if dtype == "bf16" else x.astype(np.float32)
+
+
+def packed_batch(seed: int, seqlens: Sequence[int], H: int, dk: int = 128, dv: int = 128,
+                 dtype: str = "bf16", init_state: Sequence[bool] | bool = False) -> Packed:
+    """Ragged batch of ``len(seqlens)`` sequences, each slice drawn per (seq, head, block).
+
+    ``init_state`` selects, per sequence (or for all), whether it gets an
+    N(0, 0.02^2) initial state (others start from zeros).
+    """
+    seqlens = [int(s) for s in seqlens]
+    N = len(seqlens)
+    cu = np.zeros(N + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(seqlens)
+    T = int(cu[-1])
+    qd = np.uint16 if dtype == "bf16" else np.float32
+    q = np.empty((T, H, dk), dtype=qd)
+    k = np.empty((T, H, dk), dtype=qd)
+    v = np.empty((T, H, dv), dtype=qd)
+    g = np.empty((T, H, dk), dtype=np.float32)
+    beta = np.empty((T, H), dtype=np.float32)
+    for s in range(N):
+        for h in range(H):
+            for b0 in range(0, seqlens[s], BLOCK):
+                n = min(BLOCK, seqlens[s] - b0)
+                qq, kk, vv, bb, gg = _draw_block(seed, s, h, b0 // BLOCK, n, dk, dv)
+                t0 = int(cu[s]) + b0
+                q[t0:t0 + n, h] = _cast(qq, dtype)
+                k[t0:t0 + n, h] = _cast(kk, dtype)
+                v[t0:t0 + n, h] = _cast(vv, dtype)
+                g[t0:t0 + n, h] = gg
+                beta[t0:t0 + n, h] = bb
+    if isinstance(init_state, bool):
+        init_state = [init_state] * N
+    S0 = None
+    if any(init_state):
+        S0 = np.zeros((N, H, dk, dv), dtype=np.float32)
+        for s in range(N):
+            if init_state[s]:
+                for h in range(H):
+                    S0[s, h] = draw_state(seed, s, h, dk, dv)
+    return Packed(dtype, q, k, v, g, beta, cu, S0)
+
+
+# --------------------------------------------------------------------------
+# decode / verify batches: one "sequence" per request, gamma1 tokens each
+# --------------------------------------------------------------------------
+@dataclass
+class StepBatch:
+    dtype: str
+    q: np.ndarray        # [N, G, H, dk] (G = gamma1; G == 1 for decode)
+    k: np.ndarray
+    v: np.ndarray        # [N, G, H, dv]
+    g: np.ndarray        # [N, G, H, dk] float32
+    beta: np.ndarray     # [N, G, H]     float32
+    state: np.ndarray    # [N, H, dk, dv] float32
+    accepted_len: Optional[np.ndarray] = None  # [N] int32 in 1..G
+
+    def f64(self, name: str) -> np.ndarray:
+        x = getattr(self, name)
+        if name in ("q", "k", "v"):
+            return as_f64(x, self.dtype)
+        return np.asarray(x, dtype=np.float64)
+
+
+def step_batch(seed: int, N: int, G: int, H: int, dk: int = 128, dv: int = 128,
+               dtype: str = "bf16", accepted: bool = False) -> StepBatch:
+    qd = np.uint16 if dtype == "bf16" else np.float32
+    q = np.empty((N, G, H, dk), dtype=qd)
+    k = np.empty((N, G, H, dk), dtype=qd)
+    v = np.empty((N, G, H, dv), dtype=qd)
+    g = np.empty((N, G, H, dk), dtype=np.float32)
+    beta = np.empty((N, G, H), dtype=np.float32)
+    state = np.empty((N, H, dk, dv), dtype=np.float32)
+    for n in range(N):
+        for h in range(H):
+            qq, kk, vv, bb, gg = _draw_block(seed, n, h, 0, G, dk, dv)
+            q[n, :, h] = _cast(qq, dtype)
+            k[n, :, h] = _cast(kk, dtype)
+            v[n, :, h] = _cast(vv, dtype)
+            g[n, :, h] = gg
+            beta[n, :, h] = bb
+            state[n, h] = draw_state(seed, n, h, dk, dv)
+    acc = accepted_lengths(seed, N, G) if accepted else None
+    return StepBatch(dtype, q, k, v, g, beta, state, acc)
+
+
+def accepted_lengths(seed: int, N: int, G: int = 8, p: float = 0.64) -> np.ndarray:
+    """Accepted prefix length per request: 1 + run of consecutive acceptances.
+
+    Each of the G - 1 drafts is accepted with probability p until the first
+    rejection; with p = 0.64 and G = 8 the mean is (1 - p^8) / (1 - p) = 2.70.
+    """
+    rng = np.random.default_rng([seed, ACC_TAG])
+    u = rng.random((N, G - 1))
+    acc = np.ones(N, dtype=np.int32)
+    for n in range(N):
+        for j in range(G - 1):
+            if u[n, j] < p:
+                acc[n] += 1
+            else:
+                break
+    return acc
+
+
+def loguniform_lengths(seed: int, count: int, lo: int = 1024, hi: int = 32768) -> list:
+    """Ragged lengths floor(exp(U(ln lo, ln hi))), not rounded to any chunk size."""
+    rng = np.random.default_rng([seed, LEN_TAG])
+    u = rng.random(count)
+    return [int(math.floor(math.exp(math.log(lo) + x * (math.log(hi) - math.log(lo))))) for x in u]
+
+
+# --------------------------------------------------------------------------
+# the five workloads (sizes as stated for the KDA hot path)
+# --------------------------------------------------------------------------
+WORKLOADS = {
+    "tiny_prefill_f32": dict(seed=1, seqlens=[256], H=1, dtype="f32"),
+    "decode_64x12": dict(seed=2, N=64, G=1, H=12, dtype="bf16"),
+    "prefill_4096x12": dict(seed=3, seqlens=[4096], H=12, dtype="bf16"),
+    "verify_32x12x8": dict(seed=4, N=32, G=8, H=12, dtype="bf16"),
+    "long_1m_plus_8": dict(seed=5, long_len=1 << 20, n_segments=16, n_extra=8, H=12, dtype="bf16"),
+}
+
+
+def long_context_layout(seed: int = 5, long_len: int = 1 << 20, n_extra: int = 8):
+    """Lengths of the long-context batch: one long sequence, then the extras."""
+    return [long_len] + loguniform_lengths(seed, n_extra)
