@@ -1,0 +1,110 @@
+// C ABI of the KDA library: argument validation and dispatch to the kernels.
+// Nothing here computes the recurrence; every arithmetic step runs on the GPU.
+#include "../../include/kda.h"
+#include "kda_common.hpp"
+#include "kda_internal.hpp"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+bool dims_ok(int32_t d_k, int32_t d_v) { return d_k == kda::kD && d_v == kda::kD; }
+bool dtype_ok(kda_dtype_t d) { return d == KDA_F32 || d == KDA_BF16; }
+
+kda_status_t hip_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int kda_version(void) { return kVersion; }
+
+const char* kda_status_string(kda_status_t status) {
+  switch (status) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_INVALID_ARG: return "invalid argument";
+    case KDA_ERR_UNSUPPORTED: return "unsupported (only d_k = d_v = 128 and dtype bf16/f32)";
+    case KDA_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+kda_status_t kda_decode_step(const void* q, const void* k, const void* v, const float* g,
+                             const float* beta, float* state_pool, const int32_t* slots, int32_t N,
+                             int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t dtype, float scale,
+                             void* o, void* stream) {
+  if (N < 0 || H <= 0) return KDA_ERR_INVALID_ARG;
+  if (!dims_ok(d_k, d_v) || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
+  if (N == 0) return KDA_OK;
+  if (!q || !k || !v || !g || !beta || !state_pool) return KDA_ERR_INVALID_ARG;
+  const int cols = kda::step_cols_for(int64_t(N) * H);
+  return hip_status(kda::launch_decode(q, k, v, g, beta, state_pool, slots, N, H, dtype == KDA_BF16, scale,
+                                       o, cols, static_cast<hipStream_t>(stream)));
+}
+
+kda_status_t kda_verify_commit(const void* k, const void* v, const float* g, const float* beta,
+                               float* state_pool, const int32_t* slots, const int32_t* accepted_len,
+                               int32_t N, int32_t gamma1, int32_t H, int32_t d_k, int32_t d_v,
+                               kda_dtype_t dtype, void* stream) {
+  if (N < 0 || H <= 0 || gamma1 <= 0) return KDA_ERR_INVALID_ARG;
+  if (!dims_ok(d_k, d_v) || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
+  if (N == 0) return KDA_OK;
+  if (!k || !v || !g || !beta || !state_pool || !accepted_len) return KDA_ERR_INVALID_ARG;
+  const int cols = kda::step_cols_for(int64_t(N) * H);
+  return hip_status(kda::launch_commit(k, v, g, beta, state_pool, state_pool, slots, accepted_len, N, gamma1,
+                                       H, dtype == KDA_BF16, cols, static_cast<hipStream_t>(stream)));
+}
+
+kda_status_t kda_verify_block(const void* q, const void* k, const void* v, const float* g,
+                              const float* beta, const float* state_pool, const int32_t* slots,
+                              int32_t N, int32_t gamma1, int32_t H, int32_t d_k, int32_t d_v,
+                              kda_dtype_t dtype, float scale, void* o, const int32_t* accepted_len,
+                              float* state_out_pool, void* stream) {
+  if (N < 0 || H <= 0 || gamma1 <= 0) return KDA_ERR_INVALID_ARG;
+  if (!dims_ok(d_k, d_v) || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
+  if (N == 0) return KDA_OK;
+  if (!q || !k || !v || !g || !beta || !state_pool || !o) return KDA_ERR_INVALID_ARG;
+  if (accepted_len && !state_out_pool) return KDA_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int cols = kda::step_cols_for(int64_t(N) * H);
+  hipError_t e = kda::launch_verify(q, k, v, g, beta, state_pool, slots, N, gamma1, H, dtype == KDA_BF16,
+                                    scale, o, cols, s);
+  if (e != hipSuccess || !accepted_len) return hip_status(e);
+  return hip_status(kda::launch_commit(k, v, g, beta, state_pool, state_out_pool, slots, accepted_len, N,
+                                       gamma1, H, dtype == KDA_BF16, cols, s));
+}
+
+kda_status_t kda_prefill(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const int32_t* cu_seqlens,
+                         const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t H, int32_t d_k,
+                         int32_t d_v, kda_dtype_t dtype, float scale, const float* initial_state,
+                         float* final_state, void* o, float* transition_out, void* stream) {
+  if (num_seqs < 0 || H <= 0) return KDA_ERR_INVALID_ARG;
+  if (!dims_ok(d_k, d_v) || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return KDA_OK;
+  if (!cu_seqlens) return KDA_ERR_INVALID_ARG;
+  if (cu_seqlens_host) {
+    if (cu_seqlens_host[0] != 0) return KDA_ERR_INVALID_ARG;
+    for (int32_t i = 0; i < num_seqs; ++i)
+      if (cu_seqlens_host[i + 1] < cu_seqlens_host[i]) return KDA_ERR_INVALID_ARG;
+  }
+  const bool any_tokens = !cu_seqlens_host || cu_seqlens_host[num_seqs] > 0;
+  if (any_tokens && (!q || !k || !v || !g || !beta)) return KDA_ERR_INVALID_ARG;
+  if (!final_state && !o && !transition_out) return KDA_OK;  // nothing requested
+  kda::PrefillLaunch p{q, k, v, g, beta, cu_seqlens, num_seqs, H, scale, initial_state, final_state, o,
+                       transition_out};
+  return hip_status(kda::launch_prefill(p, dtype == KDA_BF16, static_cast<hipStream_t>(stream)));
+}
+
+kda_status_t kda_compose_segments(const float* M, const float* S_tilde, const float* S_in0,
+                                  float* S_in, float* S_final, int32_t n_seg, int32_t H,
+                                  int32_t d_k, int32_t d_v, void* stream) {
+  if (n_seg < 0 || H <= 0) return KDA_ERR_INVALID_ARG;
+  if (!dims_ok(d_k, d_v)) return KDA_ERR_UNSUPPORTED;
+  if (n_seg == 0 && !S_final) return KDA_OK;
+  if ((n_seg > 0 && (!M || !S_tilde || !S_in))) return KDA_ERR_INVALID_ARG;
+  return hip_status(kda::launch_compose(M, S_tilde, S_in0, S_in, S_final, n_seg, H,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

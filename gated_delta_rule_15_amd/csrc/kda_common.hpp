@@ -1,0 +1,74 @@
+// Shared device helpers for the KDA kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int kD = 128;  // d_k = d_v handled by every kernel
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32 (bf16 held as raw 16-bit patterns)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xFFFF0000u); }
+
+// Round to nearest, ties to even.  NaN inputs map to a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return 0x7FC0u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return f32_to_bf16_rne(a) | (f32_to_bf16_rne(b) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// Element-type traits for q/k/v/o.
+// ---------------------------------------------------------------------------
+struct BF16 {
+  using storage = uint16_t;
+  // load 4 consecutive elements as floats (8-byte aligned)
+  __device__ __forceinline__ static void load4(const void* base, int64_t idx, float out[4]) {
+    const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + idx);
+    out[0] = bf16_lo(w.x); out[1] = bf16_hi(w.x);
+    out[2] = bf16_lo(w.y); out[3] = bf16_hi(w.y);
+  }
+  __device__ __forceinline__ static void store4(void* base, int64_t idx, const float in[4]) {
+    uint2 w;
+    w.x = pack_bf16x2(in[0], in[1]);
+    w.y = pack_bf16x2(in[2], in[3]);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(base) + idx) = w;
+  }
+  __device__ __forceinline__ static float load1(const void* base, int64_t idx) {
+    return __uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(base)[idx]) << 16);
+  }
+  __device__ __forceinline__ static void store1(void* base, int64_t idx, float x) {
+    reinterpret_cast<uint16_t*>(base)[idx] = uint16_t(f32_to_bf16_rne(x));
+  }
+};
+
+struct F32 {
+  using storage = float;
+  __device__ __forceinline__ static void load4(const void* base, int64_t idx, float out[4]) {
+    const float4 w = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + idx);
+    out[0] = w.x; out[1] = w.y; out[2] = w.z; out[3] = w.w;
+  }
+  __device__ __forceinline__ static void store4(void* base, int64_t idx, const float in[4]) {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + idx) = make_float4(in[0], in[1], in[2], in[3]);
+  }
+  __device__ __forceinline__ static float load1(const void* base, int64_t idx) {
+    return reinterpret_cast<const float*>(base)[idx];
+  }
+  __device__ __forceinline__ static void store1(void* base, int64_t idx, float x) {
+    reinterpret_cast<float*>(base)[idx] = x;
+  }
+};
+
+__device__ __forceinline__ float4 ld_f4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ void st_f4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+
+}  // namespace kda

@@ -1,0 +1,48 @@
+// Host-side launcher declarations shared between the kernel files and the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+// ---- decode / verify / commit (kda_step.hip) ------------------------------
+int step_cols_for(int64_t tiles);
+
+hipError_t launch_decode(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                         float* state, const int32_t* slots, int N, int H, bool bf16, float scale,
+                         void* o, int cols, hipStream_t stream);
+
+hipError_t launch_verify(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                         const float* state, const int32_t* slots, int N, int G, int H, bool bf16,
+                         float scale, void* o, int cols, hipStream_t stream);
+
+hipError_t launch_commit(const void* k, const void* v, const float* g, const float* beta,
+                         const float* state_in, float* state_out, const int32_t* slots,
+                         const int32_t* accepted_len, int N, int G, int H, bool bf16, int cols,
+                         hipStream_t stream);
+
+// ---- segment composition (kda_compose.hip) --------------------------------
+hipError_t launch_compose(const float* M, const float* S_tilde, const float* S_in0, float* S_in,
+                          float* S_final, int n_seg, int H, hipStream_t stream);
+
+// ---- chunked prefill (kda_prefill.hip) ------------------------------------
+struct PrefillLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  const int32_t* cu_seqlens;
+  int32_t num_seqs;
+  int32_t H;
+  float scale;
+  const float* initial_state;  // [num_seqs, H, 128, 128] or null (zeros)
+  float* final_state;          // or null
+  void* o;                     // or null
+  float* transition_out;       // or null
+};
+
+hipError_t launch_prefill(const PrefillLaunch& p, bool bf16, hipStream_t stream);
+
+}  // namespace kda

@@ -1,0 +1,206 @@
+"""Thin torch binding of the KDA C ABI (include/kda.h).
+
+Argument marshalling only: shape/dtype/device checks, output allocation with
+torch, raw pointers and the current HIP stream handed to libkda.so.  Every
+step of the computation runs in the library's HIP kernels; there is no CPU
+fallback, and a missing library raises ``KdaError``.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+D = 128
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return _lib.KDA_BF16
+    if t.dtype == torch.float32:
+        return _lib.KDA_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _need(t: Optional[torch.Tensor], name: str, shape, dtype=None, device=None) -> None:
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def kda_decode_step(q, k, v, g, beta, state_pool, o=None, slots=None, scale: float = 1.0,
+                    with_output: bool = True):
+    """One token per request; ``state_pool`` [P, H, 128, 128] fp32 is updated in place.
+
+    q, k, v, g: [N, H, 128]; beta: [N, H]; slots: int32 [N] pool rows (None = 0..N-1).
+    Returns o [N, H, 128] (dtype of q) or None when ``with_output`` is False.
+    """
+    N, H, _ = q.shape
+    dt = q.dtype
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, (N, H, D), dt, dev)
+    _need(g, "g", (N, H, D), torch.float32, dev)
+    _need(beta, "beta", (N, H), torch.float32, dev)
+    if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (H, D, D):
+        raise ValueError("state_pool must be [P, H, 128, 128]")
+    _need(state_pool, "state_pool", state_pool.shape, torch.float32, dev)
+    if slots is None and state_pool.shape[0] < N:
+        raise ValueError("state_pool has fewer rows than requests")
+    if slots is not None:
+        _need(slots, "slots", (N,), torch.int32, dev)
+    if with_output and o is None:
+        o = torch.empty((N, H, D), dtype=dt, device=dev)
+    _need(o, "o", (N, H, D), dt, dev)
+    lib = _lib.load()
+    _lib.check(lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), _ptr(slots),
+                                   N, H, D, D, _dtype_code(q), float(scale), _ptr(o), _stream()),
+               "kda_decode_step")
+    return o
+
+
+def kda_verify_block(q, k, v, g, beta, state_pool, o=None, slots=None, accepted_len=None,
+                     state_out_pool=None, scale: float = 1.0):
+    """Verify gamma1 draft tokens per request from the committed (read-only) states.
+
+    q, k, v, g: [N, G, H, 128]; beta: [N, G, H].  Returns o [N, G, H, 128].
+    With ``accepted_len`` (int32 [N] on the device) the commit of the accepted
+    prefix is also enqueued, into ``state_out_pool`` (defaults to ``state_pool``).
+    """
+    N, G, H, _ = q.shape
+    dt = q.dtype
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, (N, G, H, D), dt, dev)
+    _need(g, "g", (N, G, H, D), torch.float32, dev)
+    _need(beta, "beta", (N, G, H), torch.float32, dev)
+    if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (H, D, D):
+        raise ValueError("state_pool must be [P, H, 128, 128]")
+    _need(state_pool, "state_pool", state_pool.shape, torch.float32, dev)
+    if slots is None and state_pool.shape[0] < N:
+        raise ValueError("state_pool has fewer rows than requests")
+    if slots is not None:
+        _need(slots, "slots", (N,), torch.int32, dev)
+    if o is None:
+        o = torch.empty((N, G, H, D), dtype=dt, device=dev)
+    _need(o, "o", (N, G, H, D), dt, dev)
+    if accepted_len is not None:
+        _need(accepted_len, "accepted_len", (N,), torch.int32, dev)
+        if state_out_pool is None:
+            state_out_pool = state_pool
+        _need(state_out_pool, "state_out_pool", state_pool.shape, torch.float32, dev)
+    lib = _lib.load()
+    _lib.check(lib.kda_verify_block(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), _ptr(slots),
+                                    N, G, H, D, D, _dtype_code(q), float(scale), _ptr(o), _ptr(accepted_len),
+                                    _ptr(state_out_pool), _stream()),
+               "kda_verify_block")
+    return o
+
+
+def kda_verify_commit(k, v, g, beta, state_pool, accepted_len, slots=None):
+    """Replay each request's accepted prefix from its committed state, in place."""
+    N, G, H, _ = k.shape
+    dt = k.dtype
+    dev = k.device
+    _need(k, "k", (N, G, H, D), dt, dev)
+    _need(v, "v", (N, G, H, D), dt, dev)
+    _need(g, "g", (N, G, H, D), torch.float32, dev)
+    _need(beta, "beta", (N, G, H), torch.float32, dev)
+    if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (H, D, D):
+        raise ValueError("state_pool must be [P, H, 128, 128]")
+    _need(state_pool, "state_pool", state_pool.shape, torch.float32, dev)
+    _need(accepted_len, "accepted_len", (N,), torch.int32, dev)
+    if slots is not None:
+        _need(slots, "slots", (N,), torch.int32, dev)
+    elif state_pool.shape[0] < N:
+        raise ValueError("state_pool has fewer rows than requests")
+    lib = _lib.load()
+    _lib.check(lib.kda_verify_commit(_ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), _ptr(slots),
+                                     _ptr(accepted_len), N, G, H, D, D, _dtype_code(k), _stream()),
+               "kda_verify_commit")
+
+
+def kda_prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host=None, initial_state=None, final_state=None,
+                o=None, transition_out=None, scale: float = 1.0, with_output: bool = True,
+                with_final_state: bool = True):
+    """Chunked prefill of a packed ragged batch.
+
+    q, k, v, g: [T, H, 128]; beta: [T, H]; cu_seqlens: int32 [N + 1] on the device
+    (``cu_seqlens_host``: optional CPU int32 copy, validated by the library).
+    Returns (o or None, final_state or None).  ``final_state`` may be the same
+    tensor as ``initial_state`` (in-place continuation).
+    """
+    T, H, _ = q.shape
+    dt = q.dtype
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, (T, H, D), dt, dev)
+    _need(g, "g", (T, H, D), torch.float32, dev)
+    _need(beta, "beta", (T, H), torch.float32, dev)
+    if cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be 1-D")
+    _need(cu_seqlens, "cu_seqlens", cu_seqlens.shape, torch.int32, dev)
+    N = cu_seqlens.shape[0] - 1
+    if cu_seqlens_host is not None:
+        if cu_seqlens_host.is_cuda or cu_seqlens_host.dtype != torch.int32 or not cu_seqlens_host.is_contiguous():
+            raise ValueError("cu_seqlens_host must be a contiguous CPU int32 tensor")
+        if cu_seqlens_host.shape != cu_seqlens.shape:
+            raise ValueError("cu_seqlens_host and cu_seqlens differ in shape")
+        if int(cu_seqlens_host[-1]) != T:
+            raise ValueError("cu_seqlens_host[-1] must equal the number of packed tokens")
+    _need(initial_state, "initial_state", (N, H, D, D), torch.float32, dev)
+    if with_final_state and final_state is None:
+        final_state = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
+    _need(final_state, "final_state", (N, H, D, D), torch.float32, dev)
+    if with_output and o is None:
+        o = torch.empty((T, H, D), dtype=dt, device=dev)
+    _need(o, "o", (T, H, D), dt, dev)
+    _need(transition_out, "transition_out", (N, H, D, D), torch.float32, dev)
+    lib = _lib.load()
+    _lib.check(lib.kda_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                               _ptr(cu_seqlens_host), N, H, D, D, _dtype_code(q), float(scale),
+                               _ptr(initial_state), _ptr(final_state), _ptr(o), _ptr(transition_out), _stream()),
+               "kda_prefill")
+    return o, final_state
+
+
+def kda_compose_segments(M, S_tilde, S_in0=None, S_in=None, S_final=None, with_final: bool = True):
+    """Entry states of consecutive segments: S_in[0] = S_in0, S_in[i+1] = M[i] S_in[i] + S~[i].
+
+    M, S_tilde: [n_seg, H, 128, 128] fp32.  Returns (S_in, S_final).
+    """
+    n, H = S_tilde.shape[0], S_tilde.shape[1]
+    dev = S_tilde.device
+    _need(M, "M", (n, H, D, D), torch.float32, dev)
+    _need(S_tilde, "S_tilde", (n, H, D, D), torch.float32, dev)
+    _need(S_in0, "S_in0", (H, D, D), torch.float32, dev)
+    if S_in is None:
+        S_in = torch.empty((n, H, D, D), dtype=torch.float32, device=dev)
+    _need(S_in, "S_in", (n, H, D, D), torch.float32, dev)
+    if with_final and S_final is None:
+        S_final = torch.empty((H, D, D), dtype=torch.float32, device=dev)
+    _need(S_final, "S_final", (H, D, D), torch.float32, dev)
+    lib = _lib.load()
+    _lib.check(lib.kda_compose_segments(_ptr(M), _ptr(S_tilde), _ptr(S_in0), _ptr(S_in), _ptr(S_final), n, H, D, D,
+                                        _stream()),
+               "kda_compose_segments")
+    return S_in, S_final

@@ -1,0 +1,157 @@
+/*
+ * kda.h — C ABI of the MI355X (gfx950) Kimi Delta Attention (KDA) library.
+ *
+ * The recurrence, per sequence and head, token by token:
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,   o_t = S_t^T (scale * q_t)
+ * with alpha_t = exp(g_t) per key channel (g = log-decay, g <= 0), beta_t a
+ * scalar per token and head, and S a d_k x d_v fp32 matrix whose rows are key
+ * channels.  Source: "Kimi K3：架构与 SGLang Day-0 Support" (yichizhang.dev),
+ * section "attention 机制详解：KDA" (math-details box: the full update and its
+ * gate-then-delta split), and section "attention 机制详解：linear attention"
+ * (readout o = S^T q after the write).
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is DEVICE memory owned by the caller, except the
+ *     ones named *_host.  The library never allocates, frees or keeps memory.
+ *   - Layouts are dense row-major.  q, k, g are [.., d_k]; v, o are [.., d_v];
+ *     states are [.., d_k, d_v] fp32.  Only d_k = d_v = 128 is implemented.
+ *   - q, k, v (and o) are bf16 (KDA_BF16) or fp32 (KDA_F32); g, beta and all
+ *     states are always fp32.  bf16 outputs are rounded to nearest even.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream) and never synchronise the device.  Host-side argument errors are
+ *     reported before anything is enqueued; KDA_ERR_HIP reports a failed launch.
+ *   - Outputs must not alias inputs except where an entry point says so.
+ *   - No global mutable state: calls on different streams are independent as
+ *     long as their output buffers are disjoint.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kda_status {
+  KDA_OK = 0,
+  KDA_ERR_INVALID_ARG = 1, /* null pointer, bad size, inconsistent cu_seqlens_host */
+  KDA_ERR_UNSUPPORTED = 2, /* d_k or d_v != 128, unknown dtype */
+  KDA_ERR_HIP = 3          /* the HIP runtime rejected a launch */
+} kda_status_t;
+
+typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int kda_version(void);
+
+/* Static English text for a status code. */
+const char* kda_status_string(kda_status_t status);
+
+/*
+ * kda_decode_step — one token per request: gate, delta write, readout, in place.
+ *
+ * Per request n and head h (the step is the gate-then-delta split of the KDA
+ * update, section "attention 机制详解：KDA" of the Day-0 lesson page):
+ *     S~ = Diag(exp g) S;  r = S~^T k;  u = beta (v - r);  S <- S~ + k u^T;  o = S^T (scale q)
+ *   q, k, g : [N, H, 128]  (q, k in `dtype`; g fp32)
+ *   v       : [N, H, 128]  (`dtype`)
+ *   beta    : [N, H]       fp32
+ *   state_pool : [P, H, 128, 128] fp32, read and overwritten IN PLACE at pool
+ *                row slots[n] (slots == NULL means slots[n] = n and P >= N).
+ *                Slots must be distinct; they are not range-checked on the device.
+ *   o       : [N, H, 128] in `dtype`, or NULL to skip the readout.
+ * N == 0 is a no-op.
+ */
+kda_status_t kda_decode_step(const void* q, const void* k, const void* v, const float* g,
+                             const float* beta, float* state_pool, const int32_t* slots,
+                             int32_t N, int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t dtype,
+                             float scale, void* o, void* stream);
+
+/*
+ * kda_verify_block — score a block of gamma1 draft tokens per request from its
+ * committed state, which is only READ (ReplaySSM: "SGLang 和 Miles 为 Kimi K3
+ * 提供首日支持", section "ReplaySSM：针对 KDA 状态的原始输入重放"; and section 7
+ * of "Kimi K3 的训练与 Serving Infra").
+ *   q, k, g : [N, gamma1, H, 128];  v : [N, gamma1, H, 128];  beta : [N, gamma1, H]
+ *   state_pool : [P, H, 128, 128] fp32, read at slots[n] (NULL = identity), never written.
+ *   o       : [N, gamma1, H, 128]: o[n, t] = readout after tokens 1..t+1 of request n.
+ * If accepted_len (device int32 [N], values in 1..gamma1) is non-NULL the call
+ * also enqueues kda_verify_commit into state_out_pool (same slots), which may
+ * be state_pool itself; the commit replays the accepted prefix from the state
+ * that was verified, with the same per-token routine, so its result is
+ * bit-identical to that many kda_decode_step calls.
+ */
+kda_status_t kda_verify_block(const void* q, const void* k, const void* v, const float* g,
+                              const float* beta, const float* state_pool, const int32_t* slots,
+                              int32_t N, int32_t gamma1, int32_t H, int32_t d_k, int32_t d_v,
+                              kda_dtype_t dtype, float scale, void* o, const int32_t* accepted_len,
+                              float* state_out_pool, void* stream);
+
+/*
+ * kda_verify_commit — the fold: advance each request's state by its accepted
+ * prefix by replaying the stored raw inputs (k, v, g, beta) from the committed
+ * state, in place (same page and section as kda_verify_block).  The caller
+ * keeps the verify call's input buffers unchanged until this call has run, so
+ * the fold consumes exactly the gates the verify consumed.
+ *   k, g : [N, gamma1, H, 128];  v : [N, gamma1, H, 128];  beta : [N, gamma1, H]
+ *   state_pool : [P, H, 128, 128] fp32 at slots[n] (NULL = identity), updated in place.
+ *   accepted_len : device int32 [N]; entries are clamped to 0..gamma1 on the
+ *                  device (0 leaves the state unchanged).
+ */
+kda_status_t kda_verify_commit(const void* k, const void* v, const float* g, const float* beta,
+                               float* state_pool, const int32_t* slots, const int32_t* accepted_len,
+                               int32_t N, int32_t gamma1, int32_t H, int32_t d_k, int32_t d_v,
+                               kda_dtype_t dtype, void* stream);
+
+/*
+ * kda_prefill — chunk-parallel prefill of a packed ragged batch.
+ *
+ * Computes, for every sequence n (tokens cu_seqlens[n] .. cu_seqlens[n+1]-1)
+ * and head h, exactly the token-by-token recurrence above, from its initial
+ * state, with chunks of 64 tokens that restart at every sequence start (the
+ * chunkwise form rescales keys by the inverse cumulative decay, as the KDA
+ * math box of the Day-0 lesson page describes).
+ *   q, k, g : [T_total, H, 128];  v : [T_total, H, 128];  beta : [T_total, H]
+ *   cu_seqlens      : device int32 [num_seqs + 1], non-decreasing, cu_seqlens[0] = 0.
+ *   cu_seqlens_host : optional host copy of the same array; when given it is
+ *                     validated (non-decreasing, starts at 0).  The device
+ *                     array is trusted to hold the same values.
+ *   initial_state : [num_seqs, H, 128, 128] fp32, or NULL for zeros.
+ *   final_state   : [num_seqs, H, 128, 128] fp32, or NULL; may alias initial_state.
+ *   o             : [T_total, H, 128] in `dtype`, or NULL to skip outputs.
+ *   transition_out: [num_seqs, H, 128, 128] fp32, or NULL.  When given, it
+ *                   receives each sequence's transition M = M_T ... M_1 with
+ *                   M_t = (I - beta_t k_t k_t^T) Diag(alpha_t), so that
+ *                   final = M initial + S~ ("Kimi K3 的训练与 Serving Infra",
+ *                   section 4.2, KCP fragments).
+ * Empty sequences pass their initial state through.
+ */
+kda_status_t kda_prefill(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const int32_t* cu_seqlens,
+                         const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t H, int32_t d_k,
+                         int32_t d_v, kda_dtype_t dtype, float scale, const float* initial_state,
+                         float* final_state, void* o, float* transition_out, void* stream);
+
+/*
+ * kda_compose_segments — entry states of consecutive segments of one sequence
+ * from their fragments ("Kimi K3 的训练与 Serving Infra", section 4.2: after
+ * exchanging the fixed-size fragments, a prefix scan recovers each segment's
+ * true entry state):
+ *     S_in[0] = S_in0;   S_in[i+1] = M[i] S_in[i] + S~[i]
+ *   M       : [n_seg, H, 128, 128] fp32 (d_k x d_k transitions)
+ *   S_tilde : [n_seg, H, 128, 128] fp32 (zero-entry states)
+ *   S_in0   : [H, 128, 128] fp32, or NULL for zeros
+ *   S_in    : [n_seg, H, 128, 128] fp32 output (may not alias M or S_tilde)
+ *   S_final : [H, 128, 128] fp32 output M[n-1] S_in[n-1] + S~[n-1], or NULL
+ */
+kda_status_t kda_compose_segments(const float* M, const float* S_tilde, const float* S_in0,
+                                  float* S_in, float* S_final, int32_t n_seg, int32_t H,
+                                  int32_t d_k, int32_t d_v, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

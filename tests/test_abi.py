@@ -1,0 +1,109 @@
+"""The C ABI library: loads, exports every declared symbol, rejects bad host arguments.
+
+No test here launches a kernel: every call either returns before touching the
+device (argument errors, empty work) or is a pure host query.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_15_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libkda.so not built (run __graft_entry__.build())")
+    return _lib.load()
+
+
+def test_header_declares_the_entry_points():
+    syms = declared_symbols()
+    for name in ("kda_prefill", "kda_decode_step", "kda_verify_block", "kda_verify_commit",
+                 "kda_compose_segments", "kda_status_string", "kda_version"):
+        assert name in syms
+    assert set(syms) == set(_lib.SIGNATURES), "binding signatures and header disagree"
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.kda_version() >= 100
+    for code in range(4):
+        assert lib.kda_status_string(code)
+    assert b"unknown" in lib.kda_status_string(99)
+
+
+def test_decode_argument_errors(lib):
+    p = ctypes.c_void_p(16)  # never dereferenced: every call below fails validation first
+    # unsupported head dims
+    assert lib.kda_decode_step(p, p, p, p, p, p, None, 4, 2, 64, 128, 1, 1.0, p, None) == _lib.KDA_ERR_UNSUPPORTED
+    assert lib.kda_decode_step(p, p, p, p, p, p, None, 4, 2, 128, 256, 1, 1.0, p, None) == _lib.KDA_ERR_UNSUPPORTED
+    # unknown dtype
+    assert lib.kda_decode_step(p, p, p, p, p, p, None, 4, 2, 128, 128, 7, 1.0, p, None) == _lib.KDA_ERR_UNSUPPORTED
+    # negative sizes, null pointers
+    assert lib.kda_decode_step(p, p, p, p, p, p, None, -1, 2, 128, 128, 1, 1.0, p, None) == _lib.KDA_ERR_INVALID_ARG
+    assert lib.kda_decode_step(p, p, p, p, p, None, None, 4, 2, 128, 128, 1, 1.0, p, None) == _lib.KDA_ERR_INVALID_ARG
+    assert lib.kda_decode_step(None, p, p, p, p, p, None, 4, 2, 128, 128, 1, 1.0, p, None) == _lib.KDA_ERR_INVALID_ARG
+    # empty batch is a no-op
+    assert lib.kda_decode_step(None, None, None, None, None, None, None, 0, 2, 128, 128, 1, 1.0, None, None) == 0
+
+
+def test_verify_argument_errors(lib):
+    p = ctypes.c_void_p(16)
+    assert lib.kda_verify_block(p, p, p, p, p, p, None, 4, 0, 2, 128, 128, 1, 1.0, p, None, None, None) == \
+        _lib.KDA_ERR_INVALID_ARG
+    # accepted_len without an output pool
+    assert lib.kda_verify_block(p, p, p, p, p, p, None, 4, 8, 2, 128, 128, 1, 1.0, p, p, None, None) == \
+        _lib.KDA_ERR_INVALID_ARG
+    assert lib.kda_verify_commit(p, p, p, p, p, None, None, 4, 8, 2, 128, 128, 1, None) == _lib.KDA_ERR_INVALID_ARG
+    assert lib.kda_verify_commit(p, p, p, p, p, None, p, 4, 8, 2, 96, 128, 1, None) == _lib.KDA_ERR_UNSUPPORTED
+
+
+def test_prefill_argument_errors(lib):
+    p = ctypes.c_void_p(16)
+    bad_start = (ctypes.c_int32 * 3)(1, 5, 9)
+    decreasing = (ctypes.c_int32 * 3)(0, 9, 5)
+    for cu in (bad_start, decreasing):
+        assert lib.kda_prefill(p, p, p, p, p, p, cu, 2, 2, 128, 128, 1, 1.0, None, p, p, None, None) == \
+            _lib.KDA_ERR_INVALID_ARG
+    good = (ctypes.c_int32 * 3)(0, 5, 9)
+    assert lib.kda_prefill(p, p, p, p, p, None, good, 2, 2, 128, 128, 1, 1.0, None, p, p, None, None) == \
+        _lib.KDA_ERR_INVALID_ARG  # no device cu_seqlens
+    assert lib.kda_prefill(p, None, p, p, p, p, good, 2, 2, 128, 128, 1, 1.0, None, p, p, None, None) == \
+        _lib.KDA_ERR_INVALID_ARG  # no k
+    assert lib.kda_prefill(p, p, p, p, p, p, good, 2, 2, 128, 64, 1, 1.0, None, p, p, None, None) == \
+        _lib.KDA_ERR_UNSUPPORTED
+    # nothing requested / no sequences: no-op
+    assert lib.kda_prefill(p, p, p, p, p, p, good, 2, 2, 128, 128, 1, 1.0, None, None, None, None, None) == 0
+    assert lib.kda_prefill(None, None, None, None, None, None, None, 0, 2, 128, 128, 1, 1.0, None, None, None,
+                           None, None) == 0
+
+
+def test_compose_argument_errors(lib):
+    p = ctypes.c_void_p(16)
+    assert lib.kda_compose_segments(p, p, None, p, None, -1, 2, 128, 128, None) == _lib.KDA_ERR_INVALID_ARG
+    assert lib.kda_compose_segments(None, p, None, p, None, 3, 2, 128, 128, None) == _lib.KDA_ERR_INVALID_ARG
+    assert lib.kda_compose_segments(p, p, None, p, None, 3, 2, 32, 128, None) == _lib.KDA_ERR_UNSUPPORTED
+    assert lib.kda_compose_segments(None, None, None, None, None, 0, 2, 128, 128, None) == 0
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libkda.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(_lib.KdaError, match="no CPU fallback"):
+        _lib.load()

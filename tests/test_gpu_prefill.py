@@ -1,0 +1,156 @@
+"""GPU parity: chunked prefill, transitions and segment composition against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_15_amd import inputs as gen
+from oracle import kda_oracle as orc
+
+from kda_testutil import bf16_floor, packed_to_dev, rel_l2, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-3, "f32": 1e-5}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _run(p: gen.Packed, **kw):
+    from gated_delta_rule_15_amd.kda import kda_prefill
+    d = packed_to_dev(p)
+    o, S = kda_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], d["cu_seqlens_host"],
+                       initial_state=d["initial_state"], **kw)
+    torch.cuda.synchronize()
+    return o, S, d
+
+
+def _oracle(p: gen.Packed, scale=1.0):
+    return orc.prefill(p.f64("q"), p.f64("k"), p.f64("v"), p.f64("g"), p.f64("beta"), p.cu_seqlens,
+                       p.initial_state, scale)
+
+
+def _check(p, o, S, tag, scale=1.0):
+    o_ref, S_ref = _oracle(p, scale)
+    eo = rel_l2(to_f64(o), o_ref) if o_ref.size else 0.0
+    es = rel_l2(to_f64(S), S_ref)
+    floor = bf16_floor(o_ref) if p.dtype == "bf16" and o_ref.size else 0.0
+    print(f"{tag}: rel-L2 o={eo:.3e} (bf16 floor {floor:.3e}) S={es:.3e}")
+    assert eo <= TOL[p.dtype], eo
+    assert es <= TOL[p.dtype], es
+    return eo, es
+
+
+def test_tiny_prefill_fp32():
+    """1 head, T = 256, fp32 throughout, zero initial state (tolerance 1e-5)."""
+    p = gen.packed_batch(seed=1, seqlens=[256], H=1, dtype="f32")
+    o, S, _ = _run(p)
+    _check(p, o, S, "tiny fp32 T=256")
+
+
+def test_prefill_4096x12_bf16():
+    """One sequence of 4096 tokens, 12 heads, bf16 q/k/v, zero initial state."""
+    p = gen.packed_batch(seed=3, seqlens=[4096], H=12, dtype="bf16")
+    o, S, _ = _run(p)
+    _check(p, o, S, "prefill 4096x12 bf16")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 130])
+def test_prefill_ragged_lengths_nonzero_state(T, dtype):
+    p = gen.packed_batch(seed=100 + T, seqlens=[T], H=2, dtype=dtype, init_state=True)
+    o, S, _ = _run(p)
+    _check(p, o, S, f"T={T} {dtype} S0!=0")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_packed_batch_with_empty_sequence(dtype):
+    p = gen.packed_batch(seed=7, seqlens=[5, 0, 64, 100, 1, 200], H=3, dtype=dtype,
+                         init_state=[True, True, False, True, True, False])
+    o, S, _ = _run(p)
+    _check(p, o, S, f"packed batch {dtype}")
+
+
+def test_prefill_wide_slices_many_sequences():
+    """>= 256 (sequence, head) pairs select 128-column workgroups."""
+    lens = [1 + (37 * i) % 150 for i in range(32)]
+    p = gen.packed_batch(seed=8, seqlens=lens, H=8, dtype="bf16", init_state=True)
+    o, S, _ = _run(p)
+    _check(p, o, S, "32 seqs x 8 heads (wide)")
+
+
+def test_prefill_scale_and_in_place_state():
+    from gated_delta_rule_15_amd.kda import kda_prefill
+    p = gen.packed_batch(seed=9, seqlens=[77, 150], H=2, dtype="f32", init_state=True)
+    d = packed_to_dev(p)
+    st = d["initial_state"]
+    o, S = kda_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], initial_state=st,
+                       final_state=st, scale=0.5)
+    torch.cuda.synchronize()
+    assert S.data_ptr() == st.data_ptr()
+    _check(p, o, S, "in-place state, scale 0.5", scale=0.5)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_transition_output(dtype):
+    """M = M_T ... M_1 per sequence, so that final = M S0 + S~."""
+    p = gen.packed_batch(seed=10, seqlens=[100, 64, 3], H=2, dtype=dtype, init_state=True)
+    M = torch.empty((3, 2, 128, 128), device="cuda:0")
+    o, S, _ = _run(p, transition_out=M)
+    _check(p, o, S, f"with transition {dtype}")
+    M_ref = np.empty((3, 2, 128, 128))
+    for n in range(3):
+        a, b = p.cu_seqlens[n], p.cu_seqlens[n + 1]
+        for h in range(2):
+            M_ref[n, h] = orc.transition(p.f64("k")[a:b, h], p.f64("g")[a:b, h], p.f64("beta")[a:b, h])
+    e = rel_l2(to_f64(M), M_ref)
+    print(f"transition {dtype}: rel-L2 M={e:.3e}")
+    assert e <= TOL[dtype]
+
+
+def test_compose_matches_oracle():
+    from gated_delta_rule_15_amd.kda import kda_compose_segments
+    rng = np.random.default_rng(5)
+    n, H = 5, 3
+    M = (rng.standard_normal((n, H, 128, 128)) / np.sqrt(128)).astype(np.float32)
+    St = rng.standard_normal((n, H, 128, 128)).astype(np.float32)
+    S0 = rng.standard_normal((H, 128, 128)).astype(np.float32)
+    S_in, S_fin = kda_compose_segments(to_dev(M), to_dev(St), to_dev(S0))
+    torch.cuda.synchronize()
+    for h in range(H):
+        ref_in, ref_fin = orc.compose(M[:, h], St[:, h], S0[h])
+        assert rel_l2(to_f64(S_in[:, h]), ref_in) <= 1e-5
+        assert rel_l2(to_f64(S_fin[h]), ref_fin) <= 1e-5
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_split_prefill_composes_to_unsplit(dtype):
+    """Fragments (M, S~) of 3 segments -> compose -> per-segment outputs equal the unsplit sequence."""
+    from gated_delta_rule_15_amd.kda import kda_compose_segments, kda_prefill
+    T, H = 3 * 128 + 50, 2
+    p = gen.packed_batch(seed=11, seqlens=[T], H=H, dtype=dtype, init_state=True)
+    d = packed_to_dev(p)
+    seg = torch.tensor([0, 128, 256, T], dtype=torch.int32)
+    cu = seg.to("cuda:0")
+    M = torch.empty((3, H, 128, 128), device="cuda:0")
+    _, St = kda_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu, seg, transition_out=M, with_output=False)
+    S_in, S_fin = kda_compose_segments(M, St, d["initial_state"][0])
+    o, S_seg = kda_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu, seg, initial_state=S_in)
+    torch.cuda.synchronize()
+    o_ref, S_ref = _oracle(p)
+    eo = rel_l2(to_f64(o), o_ref)
+    es = rel_l2(to_f64(S_fin), S_ref[0])
+    es2 = rel_l2(to_f64(S_seg[2]), S_ref[0])
+    print(f"split+compose {dtype}: o={eo:.3e} S(compose)={es:.3e} S(pass 2)={es2:.3e}")
+    assert eo <= TOL[dtype] and es <= TOL[dtype] and es2 <= TOL[dtype]
+
+
+def test_prefill_deterministic():
+    p = gen.packed_batch(seed=12, seqlens=[300, 20], H=4, dtype="bf16", init_state=True)
+    o1, S1, _ = _run(p)
+    o2, S2, _ = _run(p)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(S1.view(torch.int32), S2.view(torch.int32))
