@@ -1,0 +1,338 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA hot path on one MI355X.
+
+Headline (the JSON line's ``value``): decode state-update HBM GB/s for one
+single-token decode step of 64 requests x 12 heads (d_k = d_v = 128, fp32
+state updated in place, bf16 q/k/v/o).  A timed step is one decode launch over
+one batch; K steps run back to back from a HIP graph, rotating 8 independent
+state sets (8 x 48 MiB, beyond the 256 MB Infinity Cache) so that the state
+bytes come from HBM.  ``ms_per_step`` is the mean step time.
+
+The other rows of the hot path are timed in the same run and reported under
+``rows``: chunked prefill of 4096 tokens x 12 heads (bf16), draft-block verify
+plus replay commit for 32 requests x 12 heads x 8 tokens, and (with --long)
+the 1,048,576-token + 8 ragged-sequence long-context prefill through segment
+composition.
+
+``roofline`` is for the decode kernel (algorithmic bytes per launch / mean
+launch time vs 8 TB/s).  ``cpu_baseline`` is the CPU oracle (fp64, token by
+token) timed on this host's cores on a bounded sample of the same decode
+workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--long] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+D = 128
+FLOP_PER_TOKEN_HEAD_PREFILL = 6 * D * D + 10 * 64 * D  # 180,224 algorithmic flop (chunk 64)
+BYTES_PER_TOKEN_HEAD_PREFILL_BF16 = 3 * 2 * D + 4 * D + 4 + 2 * D  # q,k,v bf16 + g fp32 + beta + o bf16 = 1540
+STATE_BYTES = D * D * 4
+
+
+def decode_bytes_per_head(in_bytes=2):
+    # state read + write, q/k/v/g/beta in, o out
+    return 2 * STATE_BYTES + 3 * in_bytes * D + 4 * D + 4 + in_bytes * D
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def src_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "gated_delta_rule_15_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+def to_dev(x, dtype="f32"):
+    import numpy as np
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    return torch.from_numpy(np.ascontiguousarray(x)).to("cuda:0")
+
+
+EAGER = False  # --eager: plain launches (for counter collection), no graph
+
+
+def eager_time_ms(fns, warmup):
+    import torch
+    for _ in range(warmup):
+        for f in fns[: min(len(fns), 8)]:
+            f()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for f in fns:
+        f()
+    end.record()
+    end.synchronize()
+    return start.elapsed_time(end) / len(fns)
+
+
+def graph_time_ms(fns, warmup):
+    """Capture fns (called in order) into one HIP graph; return mean ms per fn over one replay."""
+    import torch
+    if EAGER:
+        return eager_time_ms(fns, warmup)
+    for _ in range(warmup):
+        for f in fns[: min(len(fns), 8)]:
+            f()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for f in fns[: min(len(fns), 8)]:  # warm the capture stream
+            f()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    g.replay()  # untimed replay
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    g.replay()
+    end.record()
+    end.synchronize()
+    return start.elapsed_time(end) / len(fns)
+
+
+def bench_decode(steps, warmup, n_sets=8):
+    import torch
+    from gated_delta_rule_15_amd import inputs as gen
+    from gated_delta_rule_15_amd import kda
+    N, H = 64, 12
+    b = gen.step_batch(seed=2, N=N, G=1, H=H, dtype="bf16")
+    sets = []
+    for i in range(n_sets):
+        sets.append(dict(q=to_dev(b.q[:, 0], "bf16"), k=to_dev(b.k[:, 0], "bf16"), v=to_dev(b.v[:, 0], "bf16"),
+                         g=to_dev(b.g[:, 0]), beta=to_dev(b.beta[:, 0]), state=to_dev(b.state),
+                         o=torch.empty((N, H, D), dtype=torch.bfloat16, device="cuda:0")))
+    fns = []
+    for i in range(steps):
+        s = sets[i % n_sets]
+        fns.append(lambda s=s: kda.kda_decode_step(s["q"], s["k"], s["v"], s["g"], s["beta"], s["state"], o=s["o"]))
+    ms = graph_time_ms(fns, warmup)
+    nbytes = N * H * decode_bytes_per_head(2)
+    return dict(ms=ms, bytes=nbytes, gbps=nbytes / (ms * 1e-3) / 1e9, N=N, H=H, n_sets=n_sets)
+
+
+def bench_verify(reps, warmup, n_sets=8):
+    import numpy as np
+    import torch
+    from gated_delta_rule_15_amd import inputs as gen
+    from gated_delta_rule_15_amd import kda
+    N, G, H = 32, 8, 12
+    b = gen.step_batch(seed=4, N=N, G=G, H=H, dtype="bf16", accepted=True)
+    sets = []
+    for i in range(n_sets):
+        sets.append(dict(q=to_dev(b.q, "bf16"), k=to_dev(b.k, "bf16"), v=to_dev(b.v, "bf16"), g=to_dev(b.g),
+                         beta=to_dev(b.beta), state=to_dev(b.state), acc=to_dev(b.accepted_len),
+                         o=torch.empty((N, G, H, D), dtype=torch.bfloat16, device="cuda:0")))
+    fns = []
+    for i in range(reps):
+        s = sets[i % n_sets]
+        fns.append(lambda s=s: kda.kda_verify_block(s["q"], s["k"], s["v"], s["g"], s["beta"], s["state"], o=s["o"],
+                                                    accepted_len=s["acc"]))
+    ms = graph_time_ms(fns, warmup)
+    per_head_verify = STATE_BYTES + G * (3 * 2 * D + 4 * D + 4) + G * 2 * D
+    per_token_commit = 2 * D + 2 * D + 4 * D + 4
+    acc = b.accepted_len.astype(np.int64)
+    nbytes = H * (N * per_head_verify + N * 2 * STATE_BYTES + int(acc.sum()) * per_token_commit)
+    return dict(ms=ms, bytes=nbytes, gbps=nbytes / (ms * 1e-3) / 1e9, N=N, G=G, H=H,
+                mean_accepted=float(acc.mean()))
+
+
+def bench_prefill(reps, warmup):
+    import torch
+    from gated_delta_rule_15_amd import inputs as gen
+    from gated_delta_rule_15_amd import kda
+    p = gen.packed_batch(seed=3, seqlens=[4096], H=12, dtype="bf16")
+    q, k, v = to_dev(p.q, "bf16"), to_dev(p.k, "bf16"), to_dev(p.v, "bf16")
+    g, beta, cu = to_dev(p.g), to_dev(p.beta), to_dev(p.cu_seqlens)
+    o = torch.empty_like(q)
+    S = torch.empty((1, 12, D, D), device="cuda:0")
+    run = lambda: kda.kda_prefill(q, k, v, g, beta, cu, o=o, final_state=S)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        run()
+    end.record()
+    end.synchronize()
+    ms = start.elapsed_time(end) / reps
+    th = 4096 * 12
+    flops = th * FLOP_PER_TOKEN_HEAD_PREFILL
+    nbytes = th * BYTES_PER_TOKEN_HEAD_PREFILL_BF16 + 12 * STATE_BYTES
+    return dict(ms=ms, tokens_per_s=4096 / (ms * 1e-3), algorithmic_tflops=flops / (ms * 1e-3) / 1e12,
+                frac_mfma_peak=flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                gbps=nbytes / (ms * 1e-3) / 1e9, frac_hbm_peak=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS)
+
+
+def bench_long(reps):
+    import torch
+    from gated_delta_rule_15_amd import long_context
+    r = long_context.benchmark(reps=reps, log=log)
+    return r
+
+
+# ---------------------------------------------------------------------------
+def _oracle_decode_worker(args):
+    seed, lo, hi, rounds = args
+    import numpy as np
+    from gated_delta_rule_15_amd import inputs as gen
+    from oracle import kda_oracle as orc
+    b = gen.step_batch(seed=seed, N=64, G=1, H=12, dtype="bf16")
+    q, k, v, g, beta, S = b.f64("q")[:, 0], b.f64("k")[:, 0], b.f64("v")[:, 0], b.f64("g")[:, 0], \
+        b.f64("beta")[:, 0], b.f64("state")
+    t0 = time.perf_counter()
+    for _ in range(rounds):
+        orc.decode_step(q[lo:hi], k[lo:hi], v[lo:hi], g[lo:hi], beta[lo:hi], S[lo:hi])
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(target_s=12.0):
+    """The oracle's decode step on host cores: all 64 requests x 12 heads, split over workers."""
+    import multiprocessing as mp
+    cores = len(os.sched_getaffinity(0))
+    cores = max(1, min(cores, 16))
+    # calibrate one round on one core
+    t1 = _oracle_decode_worker((2, 0, 64, 1))
+    rounds = max(1, int(round(target_s * cores / max(t1, 1e-3) / cores)))
+    chunks = [(2, 64 * i // cores, 64 * (i + 1) // cores, rounds) for i in range(cores)]
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(cores) as pool:
+        times = pool.map(_oracle_decode_worker, chunks)
+    wall = max(times)  # the slowest worker's compute time (pool start-up excluded)
+    nbytes = rounds * 64 * 12 * decode_bytes_per_head(2)
+    return dict(value=nbytes / wall / 1e9, unit="GB/s", cores=cores, kind="oracle",
+                sample=f"{rounds} decode steps of 64 requests x 12 heads (fp64 numpy, token by token), "
+                       f"requests split over {cores} worker processes; slowest worker {wall:.1f} s")
+
+
+def traffic_from_profile(kernel_hash):
+    path = os.path.join(ROOT, "profiles", "decode_64x12_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != kernel_hash:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def calibrate_copy(nbytes=256 << 20, reps=20):
+    import torch
+    src = torch.ones(nbytes // 4, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes_read": nbytes, "bytes_written": nbytes, "launches": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--long", action="store_true", help="also time the 1M-token long-context prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-decode", action="store_true", help="time only the decode rows (for profiling)")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="launch without a HIP graph (counter collection)")
+    args = ap.parse_args()
+    global EAGER
+    EAGER = args.eager
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only (the KDA hot path here is single-GPU; "
+              "multi-GPU sharding is design-only). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    from gated_delta_rule_15_amd import _lib
+    _lib.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    log("decode: 64 requests x 12 heads ...")
+    dec = bench_decode(args.steps, args.warmup)
+    log(f"decode: {dec['ms'] * 1e3:.2f} us/step, {dec['gbps']:.0f} GB/s")
+    rows = {}
+    if not args.only_decode:
+        log("prefill: 4096 tokens x 12 heads ...")
+        pf = bench_prefill(reps=max(5, args.steps // 20), warmup=3)
+        log(f"prefill: {pf['ms']:.3f} ms, {pf['tokens_per_s'] / 1e6:.2f} M tokens/s")
+        rows["prefill_4096x12_bf16"] = pf
+        log("verify+commit: 32 requests x 12 heads x 8 drafts ...")
+        vf = bench_verify(reps=max(16, args.steps // 2), warmup=args.warmup)
+        log(f"verify+commit: {vf['ms'] * 1e3:.2f} us, {vf['gbps']:.0f} GB/s")
+        rows["verify_commit_32x12x8_bf16"] = vf
+        if args.long:
+            log("long context: 1,048,576 + 8 ragged sequences x 12 heads ...")
+            rows["long_context_1m_plus_8"] = bench_long(reps=2)
+
+    khash = src_hash("kda_step.hip", "kda_common.hpp")
+    traffic = traffic_from_profile(khash)
+    roof = dict(bound="hbm", achieved=round(dec["gbps"], 1), peak=HBM_PEAK_GBPS, unit="GB/s",
+                frac=round(dec["gbps"] / HBM_PEAK_GBPS, 4), traffic=traffic,
+                kernel="kda_step_kernel<decode>", algorithmic_bytes_per_launch=dec["bytes"],
+                mean_launch_us=round(dec["ms"] * 1e3, 3))
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline()
+        log(f"cpu baseline: {cpu['value']:.4f} GB/s on {cpu['cores']} cores")
+
+    line = {
+        "metric": "KDA prefill tokens/s and decode state-update HBM GB/s (12 heads, 1 GPU)",
+        "value": round(dec["gbps"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode step, 64 requests x 12 heads, d_k=d_v=128, fp32 state in place, "
+                               "bf16 q/k/v/o, 8 rotated state sets",
+                   "requests": 64, "heads": 12, "d": 128, "state_sets": dec["n_sets"]},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "rows": rows,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
