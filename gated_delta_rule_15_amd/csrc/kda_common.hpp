@@ -31,6 +31,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // ---------------------------------------------------------------------------
 struct BF16 {
   using storage = uint16_t;
+  using raw4 = uint2;      // 4 packed elements as loaded
+  using raw1 = uint32_t;   // 1 element (low 16 bits)
+  __device__ __forceinline__ static raw4 load4raw(const void* base, int64_t idx) {
+    return *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + idx);
+  }
+  __device__ __forceinline__ static void unpack4(raw4 w, float out[4]) {
+    out[0] = bf16_lo(w.x); out[1] = bf16_hi(w.x);
+    out[2] = bf16_lo(w.y); out[3] = bf16_hi(w.y);
+  }
+  __device__ __forceinline__ static raw1 load1raw(const void* base, int64_t idx) {
+    return reinterpret_cast<const uint16_t*>(base)[idx];
+  }
+  __device__ __forceinline__ static float unpack1(raw1 w) { return __uint_as_float(w << 16); }
   // load 4 consecutive elements as floats (8-byte aligned)
   __device__ __forceinline__ static void load4(const void* base, int64_t idx, float out[4]) {
     const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + idx);
@@ -53,6 +66,18 @@ struct BF16 {
 
 struct F32 {
   using storage = float;
+  using raw4 = float4;
+  using raw1 = float;
+  __device__ __forceinline__ static raw4 load4raw(const void* base, int64_t idx) {
+    return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + idx);
+  }
+  __device__ __forceinline__ static void unpack4(raw4 w, float out[4]) {
+    out[0] = w.x; out[1] = w.y; out[2] = w.z; out[3] = w.w;
+  }
+  __device__ __forceinline__ static raw1 load1raw(const void* base, int64_t idx) {
+    return reinterpret_cast<const float*>(base)[idx];
+  }
+  __device__ __forceinline__ static float unpack1(raw1 w) { return w; }
   __device__ __forceinline__ static void load4(const void* base, int64_t idx, float out[4]) {
     const float4 w = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + idx);
     out[0] = w.x; out[1] = w.y; out[2] = w.z; out[3] = w.w;
