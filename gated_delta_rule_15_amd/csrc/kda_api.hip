@@ -84,11 +84,11 @@ kda_status_t kda_prefill(const void* q, const void* k, const void* v, const floa
   if (num_seqs == 0) return KDA_OK;
   if (!cu_seqlens) return KDA_ERR_INVALID_ARG;
   if (cu_seqlens_host) {
-    if (cu_seqlens_host[0] != 0) return KDA_ERR_INVALID_ARG;
+    if (cu_seqlens_host[0] < 0) return KDA_ERR_INVALID_ARG;
     for (int32_t i = 0; i < num_seqs; ++i)
       if (cu_seqlens_host[i + 1] < cu_seqlens_host[i]) return KDA_ERR_INVALID_ARG;
   }
-  const bool any_tokens = !cu_seqlens_host || cu_seqlens_host[num_seqs] > 0;
+  const bool any_tokens = !cu_seqlens_host || cu_seqlens_host[num_seqs] > cu_seqlens_host[0];
   if (any_tokens && (!q || !k || !v || !g || !beta)) return KDA_ERR_INVALID_ARG;
   if (!final_state && !o && !transition_out) return KDA_OK;  // nothing requested
   kda::PrefillLaunch p{q, k, v, g, beta, cu_seqlens, num_seqs, H, scale, initial_state, final_state, o,

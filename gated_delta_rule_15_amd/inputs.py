@@ -45,9 +45,9 @@ STATE_STD = 0.02
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """fp32 -> bf16 bit patterns (uint16), round to nearest, ties to even."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    rounding = 0x7FFF + ((u >> 16) & 1)
-    out = ((u + rounding) >> 16).astype(np.uint16)
+    u = x.view(np.uint32)
+    # finite inputs cannot carry past bit 31 (largest finite pattern 0xFF7FFFFF + 0x8000)
+    out = ((u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)).astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
         out[nan] = 0x7FC0
@@ -249,3 +249,112 @@ WORKLOADS = {
 def long_context_layout(seed: int = 5, long_len: int = 1 << 20, n_extra: int = 8):
     """Lengths of the long-context batch: one long sequence, then the extras."""
     return [long_len] + loguniform_lengths(seed, n_extra)
+
+
+# --------------------------------------------------------------------------
+# parallel generation (same streams, same arrays) for the 1M-token workload
+# --------------------------------------------------------------------------
+def _fill_units(args):
+    """Worker: fill (seq, head, block) units into shared-memory arrays."""
+    from multiprocessing import shared_memory
+    names, shapes, dtypes, units, seed, dk, dv, dtype, cu = args
+    shms = [shared_memory.SharedMemory(name=nm) for nm in names]
+    try:
+        arrs = [np.ndarray(sh, dtype=np.dtype(dt), buffer=m.buf) for m, sh, dt in zip(shms, shapes, dtypes)]
+        q, k, v, g, beta = arrs
+        for s, h, blk, n in units:
+            qq, kk, vv, bb, gg = _draw_block(seed, s, h, blk, n, dk, dv)
+            t0 = int(cu[s]) + blk * BLOCK
+            q[t0:t0 + n, h] = _cast(qq, dtype)
+            k[t0:t0 + n, h] = _cast(kk, dtype)
+            v[t0:t0 + n, h] = _cast(vv, dtype)
+            g[t0:t0 + n, h] = gg
+            beta[t0:t0 + n, h] = bb
+        del arrs, q, k, v, g, beta
+    finally:
+        for m in shms:
+            m.close()
+    return len(units)
+
+
+class SharedPacked(Packed):
+    """A Packed whose big arrays live in shared memory; call release() when done."""
+
+    _shms: list = []
+
+    def release(self):
+        """Drop the shared arrays and free their memory (shapes stay readable via ``T``/``H``)."""
+        import gc
+        self._T, self._H = self.T, self.H
+        self.q = self.k = self.v = self.g = self.beta = None
+        gc.collect()
+        for m in self._shms:
+            try:
+                m.close()
+            except BufferError:  # a view is still alive somewhere; the name is still removed
+                pass
+            try:
+                m.unlink()
+            except FileNotFoundError:
+                pass
+        self._shms = []
+
+    @property
+    def T(self) -> int:
+        return int(self.q.shape[0]) if self.q is not None else self._T
+
+    @property
+    def H(self) -> int:
+        return int(self.q.shape[1]) if self.q is not None else self._H
+
+
+def packed_batch_parallel(seed: int, seqlens: Sequence[int], H: int, dk: int = 128, dv: int = 128,
+                          dtype: str = "bf16", init_state: Sequence[bool] | bool = False,
+                          workers: int = 8) -> SharedPacked:
+    """Same arrays as ``packed_batch`` (identical per-block streams), drawn by a process pool."""
+    import multiprocessing as mp
+    from multiprocessing import shared_memory
+    seqlens = [int(s) for s in seqlens]
+    N = len(seqlens)
+    cu = np.zeros(N + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(seqlens)
+    T = int(cu[-1])
+    qd = np.uint16 if dtype == "bf16" else np.float32
+    specs = [((T, H, dk), qd), ((T, H, dk), qd), ((T, H, dv), qd), ((T, H, dk), np.float32), ((T, H), np.float32)]
+    shms, arrs = [], []
+    for shape, dt in specs:
+        nbytes = max(1, int(np.prod(shape)) * np.dtype(dt).itemsize)
+        m = shared_memory.SharedMemory(create=True, size=nbytes)
+        shms.append(m)
+        arrs.append(np.ndarray(shape, dtype=dt, buffer=m.buf))
+    units = [(s, h, b0 // BLOCK, min(BLOCK, seqlens[s] - b0))
+             for s in range(N) for h in range(H) for b0 in range(0, seqlens[s], BLOCK)]
+    workers = max(1, min(workers, len(units)))
+    chunks = [units[i::workers] for i in range(workers)]
+    args = [([m.name for m in shms], [sp[0] for sp in specs], [np.dtype(sp[1]).str for sp in specs], c, seed, dk, dv,
+             dtype, cu) for c in chunks]
+    with mp.get_context("spawn").Pool(workers) as pool:
+        pool.map(_fill_units, args)
+    if isinstance(init_state, bool):
+        init_state = [init_state] * N
+    S0 = None
+    if any(init_state):
+        S0 = np.zeros((N, H, dk, dv), dtype=np.float32)
+        for s in range(N):
+            if init_state[s]:
+                for h in range(H):
+                    S0[s, h] = draw_state(seed, s, h, dk, dv)
+    out = SharedPacked(dtype, arrs[0], arrs[1], arrs[2], arrs[3], arrs[4], cu, S0)
+    out._shms = shms
+    return out
+
+
+def long_context_batch(seed: int = 5, long_len: int = 1 << 20, n_extra: int = 8, H: int = 12,
+                       dtype: str = "bf16", workers: int = 8):
+    """The long-context workload: one long sequence (zero initial state) followed by
+    ``n_extra`` log-uniform 1K-32K sequences with N(0, 0.02^2) initial states."""
+    lens = long_context_layout(seed, long_len, n_extra)
+    init = [False] + [True] * n_extra
+    if workers > 1:
+        return packed_batch_parallel(seed, lens, H, dtype=dtype, init_state=init, workers=workers)
+    return packed_batch(seed, lens, H, dtype=dtype, init_state=init)

@@ -165,8 +165,8 @@ def kda_prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host=None, initial_stat
             raise ValueError("cu_seqlens_host must be a contiguous CPU int32 tensor")
         if cu_seqlens_host.shape != cu_seqlens.shape:
             raise ValueError("cu_seqlens_host and cu_seqlens differ in shape")
-        if int(cu_seqlens_host[-1]) != T:
-            raise ValueError("cu_seqlens_host[-1] must equal the number of packed tokens")
+        if int(cu_seqlens_host[-1]) > T or int(cu_seqlens_host[0]) < 0:
+            raise ValueError("cu_seqlens_host must lie within the packed tokens")
     _need(initial_state, "initial_state", (N, H, D, D), torch.float32, dev)
     if with_final_state and final_state is None:
         final_state = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)

@@ -1,0 +1,134 @@
+"""Segmented (KCP-style) prefill of long sequences on one GPU.
+
+A sequence longer than ``seg_len`` tokens is cut into segments that run in
+parallel.  Every step runs in the library's kernels; this module only plans the
+segment rows and sequences three library calls
+("Kimi K3 的训练与 Serving Infra：KDA 换掉 attention 后，系统要重做什么",
+sections 4.1-4.2: each segment computes its fixed-size fragments (M, S~), a
+prefix scan over them recovers each segment's true entry state, then each
+segment computes its outputs):
+
+  pass 1   kda_prefill over the segments 0..n-2 of every multi-segment
+           sequence: zero entry state, no outputs; final state = S~, and the
+           transition M (transition_out).
+  compose  kda_compose_segments per multi-segment sequence: entry states
+           S_in(i+1) = M(i) S_in(i) + S~(i), written straight into the rows of
+           pass 2's initial-state buffer.
+  pass 2   kda_prefill over every segment of every sequence from its true entry
+           state: the outputs and the final states.
+
+Segment boundaries are multiples of 64 tokens from each sequence start, so
+the chunking inside every segment is the one the unsplit sequence would use.
+Copies of the caller's initial states into pass 2's row buffer, and of final
+states out of it, are plain device-to-device moves (buffer marshalling).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+from . import kda
+
+D = 128
+
+
+@dataclass
+class SegmentPlan:
+    seg_len: int
+    rows: np.ndarray            # [R + 1] int32 token offsets of all segment rows (pass 2)
+    row_of_seq: List[range]     # pass-2 rows of each sequence
+    multi: List[int]            # sequences with >= 2 segments
+
+    @property
+    def n_rows(self) -> int:
+        return int(self.rows.shape[0] - 1)
+
+
+def plan_segments(cu_seqlens_host, seg_len: int) -> SegmentPlan:
+    if seg_len <= 0 or seg_len % 64:
+        raise ValueError("seg_len must be a positive multiple of 64")
+    cu = np.asarray(cu_seqlens_host, dtype=np.int64)
+    rows = [int(cu[0])]
+    row_of_seq, multi = [], []
+    for n in range(cu.shape[0] - 1):
+        a, b = int(cu[n]), int(cu[n + 1])
+        first = len(rows) - 1
+        cuts = list(range(a + seg_len, b, seg_len))
+        rows.extend(cuts + [b])
+        row_of_seq.append(range(first, len(rows) - 1))
+        if cuts:
+            multi.append(n)
+    return SegmentPlan(seg_len, np.asarray(rows, dtype=np.int32), row_of_seq, multi)
+
+
+def kda_prefill_segmented(q, k, v, g, beta, cu_seqlens_host, seg_len: int = 65536, initial_state=None,
+                          o=None, final_state=None, scale: float = 1.0, plan: Optional[SegmentPlan] = None,
+                          work: Optional[dict] = None):
+    """Prefill of a packed ragged batch with long sequences split into segments.
+
+    Same arguments and results as ``kda.kda_prefill`` (cu_seqlens_host: CPU
+    int32 [N + 1]); returns (o, final_state).  ``work`` may hold preallocated
+    buffers from ``alloc_work`` so repeated calls allocate nothing.
+    """
+    dev = q.device
+    H = q.shape[1]
+    cu_host = torch.as_tensor(np.asarray(cu_seqlens_host, dtype=np.int32))
+    N = cu_host.shape[0] - 1
+    plan = plan or plan_segments(cu_host.numpy(), seg_len)
+    work = work or alloc_work(plan, H, dev)
+    if o is None:
+        o = torch.empty_like(q)
+    if final_state is None:
+        final_state = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
+    init2, fin2 = work["init2"], work["fin2"]
+
+    # entry states of first segments: the caller's initial states (or zeros)
+    first_rows = work["first_rows"]
+    if initial_state is not None:
+        init2.index_copy_(0, first_rows, initial_state)
+    else:
+        init2.index_fill_(0, first_rows, 0.0)
+
+    for n in plan.multi:
+        r = plan.row_of_seq[n]
+        nseg = len(r)
+        frag_cu_h = torch.from_numpy(plan.rows[r.start:r.start + nseg].copy())
+        frag_cu_d = work["frag_cu"][n]
+        M, St = work["M"][n], work["St"][n]
+        # pass 1: fragments of segments 0 .. nseg-2
+        kda.kda_prefill(q, k, v, g, beta, frag_cu_d, frag_cu_h, final_state=St, transition_out=M,
+                        with_output=False, scale=scale)
+        # compose: entry states of segments 1 .. nseg-1 (segment 0's is the sequence's own),
+        # written into pass 2's rows; S_in[0] lands on row r.start, which already holds S_in0
+        nf = nseg - 1
+        kda.kda_compose_segments(M, St, init2[r.start], S_in=init2[r.start:r.start + nf],
+                                 S_final=init2[r.start + nf])
+
+    # pass 2: every segment from its entry state
+    kda.kda_prefill(q, k, v, g, beta, work["rows_d"], work["rows_h"], initial_state=init2, final_state=fin2, o=o,
+                    scale=scale)
+    final_state.copy_(fin2.index_select(0, work["last_rows"]))
+    return o, final_state
+
+
+def alloc_work(plan: SegmentPlan, H: int, dev) -> dict:
+    R = plan.n_rows
+    work = {
+        "init2": torch.empty((R, H, D, D), dtype=torch.float32, device=dev),
+        "fin2": torch.empty((R, H, D, D), dtype=torch.float32, device=dev),
+        "rows_d": torch.from_numpy(plan.rows.copy()).to(dev),
+        "rows_h": torch.from_numpy(plan.rows.copy()),
+        "first_rows": torch.tensor([r.start for r in plan.row_of_seq], dtype=torch.long, device=dev),
+        "last_rows": torch.tensor([r.stop - 1 for r in plan.row_of_seq], dtype=torch.long, device=dev),
+        "M": {}, "St": {}, "frag_cu": {},
+    }
+    for n in plan.multi:
+        r = plan.row_of_seq[n]
+        nf = len(r) - 1
+        work["M"][n] = torch.empty((nf, H, D, D), dtype=torch.float32, device=dev)
+        work["St"][n] = torch.empty((nf, H, D, D), dtype=torch.float32, device=dev)
+        work["frag_cu"][n] = torch.from_numpy(plan.rows[r.start:r.start + nf + 1].copy()).to(dev)
+    return work

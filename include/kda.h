@@ -114,9 +114,11 @@ kda_status_t kda_verify_commit(const void* k, const void* v, const float* g, con
  * chunkwise form rescales keys by the inverse cumulative decay, as the KDA
  * math box of the Day-0 lesson page describes).
  *   q, k, g : [T_total, H, 128];  v : [T_total, H, 128];  beta : [T_total, H]
- *   cu_seqlens      : device int32 [num_seqs + 1], non-decreasing, cu_seqlens[0] = 0.
+ *   cu_seqlens      : device int32 [num_seqs + 1], non-decreasing, cu_seqlens[0] >= 0;
+ *                     row n covers tokens cu_seqlens[n] .. cu_seqlens[n+1]-1 of the
+ *                     packed arrays (a row set need not start at token 0).
  *   cu_seqlens_host : optional host copy of the same array; when given it is
- *                     validated (non-decreasing, starts at 0).  The device
+ *                     validated (non-negative start, non-decreasing).  The device
  *                     array is trusted to hold the same values.
  *   initial_state : [num_seqs, H, 128, 128] fp32, or NULL for zeros.
  *   final_state   : [num_seqs, H, 128, 128] fp32, or NULL; may alias initial_state.
@@ -142,7 +144,7 @@ kda_status_t kda_prefill(const void* q, const void* k, const void* v, const floa
  *     S_in[0] = S_in0;   S_in[i+1] = M[i] S_in[i] + S~[i]
  *   M       : [n_seg, H, 128, 128] fp32 (d_k x d_k transitions)
  *   S_tilde : [n_seg, H, 128, 128] fp32 (zero-entry states)
- *   S_in0   : [H, 128, 128] fp32, or NULL for zeros
+ *   S_in0   : [H, 128, 128] fp32, or NULL for zeros; may be the same memory as S_in[0]
  *   S_in    : [n_seg, H, 128, 128] fp32 output (may not alias M or S_tilde)
  *   S_final : [H, 128, 128] fp32 output M[n-1] S_in[n-1] + S~[n-1], or NULL
  */

@@ -76,7 +76,7 @@ def test_verify_argument_errors(lib):
 
 def test_prefill_argument_errors(lib):
     p = ctypes.c_void_p(16)
-    bad_start = (ctypes.c_int32 * 3)(1, 5, 9)
+    bad_start = (ctypes.c_int32 * 3)(-1, 5, 9)
     decreasing = (ctypes.c_int32 * 3)(0, 9, 5)
     for cu in (bad_start, decreasing):
         assert lib.kda_prefill(p, p, p, p, p, p, cu, 2, 2, 128, 128, 1, 1.0, None, p, p, None, None) == \
