@@ -3,7 +3,7 @@
 // Math (the update is from "Kimi K3：架构与 SGLang Day-0 Support",
 // section "attention 机制详解：KDA"; the chunkwise form rescales keys by the
 // inverse cumulative decay, as remarked in the same math box).  For a chunk of
-// n <= 64 tokens with entry state S (128 x 128, rows = key channels) and
+// n tokens with entry state S (128 x 128, rows = key channels) and
 // b_r = sum_{s<=r} g_s per key channel:
 //   Kh = K e^{b}, Kc = K e^{-b}, Qh = scale Q e^{b}, Kb = K e^{b_last - b}
 //   A  = strict_lower(diag(beta) Kh Kc^T)          (n x n)
@@ -14,248 +14,79 @@
 //   S <- Diag(e^{b_last}) S + Kb^T U
 // which is the WY form of the chunk's product of (I - beta k k^T) Diag(alpha)
 // factors.  The transition M of a sequence is the same pass run from S = I
-// with V = 0 and no outputs.
+// with V = 0 and no outputs.  Chunks are 32 tokens here; every sequence (and
+// every segment a caller cuts at a multiple of 64 tokens) starts a chunk, so
+// the result is the same recurrence whatever the chunk size.
 //
-// Decomposition.  A workgroup (4 waves) owns one (sequence, head, column
-// slice) and walks the sequence's chunks in order.  Each wave owns 16*JB
-// value columns of the state, held in MFMA accumulator registers for the
-// whole sequence (value columns never interact).  Per chunk:
-//   stage 0  all threads: the chunk's g, k, q, beta, v were prefetched into
-//            registers during the previous chunk; cumulative sum of g per
-//            channel (in-thread over 8 tokens, then across 8 lanes); build
-//            Kh, Kc, Qh and Kb^T in LDS; beta and e^{b_last} in LDS.
-//   stage 1  wave 0: the four diagonal 16x16 tiles of A on MFMA, then their
-//            unit-lower-triangular inverses T_II by right-looking
-//            substitution in registers; waves 1-3 meanwhile: the six
-//            off-diagonal tiles of A and the ten lower tiles of P.
-//   stage 2  the UT factor T = (I + A)^{-1} by 16-column blocks, one wave
-//            per block: T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ on MFMA with the
-//            block column kept in registers; T' = T diag(beta) to LDS.
-//   stage 3  per wave, all on MFMA with the state never leaving registers:
-//            R = V - Kh S, U = T' R, O = Qh S + P U, S = Gamma S + Kb^T U;
-//            the next chunk's inputs are fetched at its start.
-// MFMA operands from registers (S, R, U, T blocks) are used in their
-// accumulator layout: a lane holds rows {4q..4q+3} of two consecutive 16-row
-// tiles, and the contraction index inside every 32-deep step is permuted to
-// match; LDS operands are stored with the same permutation so each lane's 8
-// values are one contiguous 16-byte read.
-//
-// Precision policies.  bf16 inputs run every product on bf16 MFMA with each
-// fp32-derived operand split into hi + lo bf16 halves (hi*hi + hi*lo + lo*hi,
-// fp32 accumulation); a single bf16 rounding of the derived operands misses a
-// 2e-3 relative-L2 bar on the outputs.  fp32 inputs run the same dataflow on
-// fp32 MFMA (16x16x4).
+// Decomposition: one workgroup of 8 waves per (sequence, head, column slice),
+// walking the sequence's chunks in order with the state in registers.
+//   waves 0-3 (state): each owns 16*JB value columns of S in MFMA accumulator
+//             registers for the whole sequence and, per chunk, computes
+//             R = V - Kh S, O = Qh S + P U with U = T' R, S = Gamma S + Kb^T U.
+//   waves 4-7 (prep):  build the NEXT chunk's operands: cumulative decay
+//             (in-thread over 4 tokens, then across 8 lanes), Kh, Kc, Qh,
+//             Kb^T, the A and P tiles on MFMA, the 16x16 diagonal inverses of
+//             I + A by right-looking substitution in registers, the
+//             off-diagonal block T_10 = -T_11 A_10 T_00 on MFMA, and T'.
+// Operand sets are double-buffered in LDS: in step i the prep waves write set
+// i % 2 (chunk i) while the state waves read set (i - 1) % 2 (chunk i - 1).
+// Each step has three workgroup barriers that both groups pass in lockstep:
+//   phase A  state: Kh S, Qh S           | prep: decay scan, operands
+//   phase B  state: T' R, P U, outputs   | prep: A, P tiles; diagonal inverses
+//   phase C  state: Gamma S + Kb^T U     | prep: T_10, T'
+// Inputs are fetched one chunk ahead into registers (prep: g, k, q, beta in
+// phase B; state: v in phase C).  Two waves share each SIMD, so one wave's
+// MFMA work overlaps the other's LDS and VALU work.
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
+#include "kda_mfma.hpp"
 
 namespace kda {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+constexpr int kC = 32;           // chunk length (tokens)
+constexpr int kThreads = 512;    // 8 waves
+constexpr int kStateWaves = 4;
 
-constexpr int kC = 64;        // chunk length (tokens)
-constexpr int kThreads = 256; // 4 waves
-
-// Position of logical index x inside its 32-block so that lane group q's
-// eight contraction slots {4q..4q+3, 16+4q..16+4q+3} are contiguous.
-__host__ __device__ constexpr int kperm(int x) {
-  return (x & ~31) + (((x & 15) >> 2) << 3) + (x & 3) + (((x & 31) >> 4) << 2);
-}
-
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// ---------------------------------------------------------------------------
-// Precision policies: operand storage in LDS and the MFMA steps.
-//   Frag   : one lane's 8 contraction slots of a 32-deep step
-//   Frag16 : one lane's 4 contraction slots of a 16-deep step
-//   mma_part(acc, a, b, p), p < kParts   : accumulate part p of a 32-deep step
-//   mma16_part(acc, a, b, p), p < kParts16
-// Issuing part p over many independent accumulators before part p+1 keeps the
-// MFMA pipe busy.
-// ---------------------------------------------------------------------------
-struct PolBF16x3 {
-  static constexpr int kPlanes = 2;  // hi plane, lo plane
-  static constexpr int kElem = 2;    // bytes per element per plane
-  static constexpr int kParts = 3;
-  static constexpr int kParts16 = 3;
-  struct Frag {
-    bf16x8_t hi, lo;
-  };
-  struct Frag16 {
-    s16x4_t hi, lo;
-  };
-  // x = hi + lo with hi = bf16(x), lo = bf16(x - hi): two values per call,
-  // packed as two bf16 halves of a 32-bit word (v_cvt_pk_bf16_f32).
-  __device__ __forceinline__ static void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
-    const bf16x2_t h = {(__bf16)a, (__bf16)b};
-    const uint32_t hw = __builtin_bit_cast(uint32_t, h);
-    const float ra = a - __uint_as_float(hw << 16);
-    const float rb = b - __uint_as_float(hw & 0xFFFF0000u);
-    const bf16x2_t l = {(__bf16)ra, (__bf16)rb};
-    hi = hw;
-    lo = __builtin_bit_cast(uint32_t, l);
-  }
-  __device__ __forceinline__ static void store4(char* base, int plane, int off, const float v[4]) {
-    uint32_t h0, l0, h1, l1;
-    split2(v[0], v[1], h0, l0);
-    split2(v[2], v[3], h1, l1);
-    *reinterpret_cast<uint2*>(base + off) = make_uint2(h0, h1);
-    *reinterpret_cast<uint2*>(base + plane + off) = make_uint2(l0, l1);
-  }
-  __device__ __forceinline__ static void store1(char* base, int plane, int off, float v) {
-    const __bf16 h = (__bf16)v;
-    const __bf16 l = (__bf16)(v - (float)h);
-    *reinterpret_cast<__bf16*>(base + off) = h;
-    *reinterpret_cast<__bf16*>(base + plane + off) = l;
-  }
-  __device__ __forceinline__ static Frag load(const char* base, int plane, int off) {
-    Frag f;
-    f.hi = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(base + off));
-    f.lo = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(base + plane + off));
-    return f;
-  }
-  __device__ __forceinline__ static Frag16 load16(const char* base, int plane, int off) {
-    Frag16 f;
-    f.hi = __builtin_bit_cast(s16x4_t, *reinterpret_cast<const u32x2_t*>(base + off));
-    f.lo = __builtin_bit_cast(s16x4_t, *reinterpret_cast<const u32x2_t*>(base + plane + off));
-    return f;
-  }
-  __device__ __forceinline__ static Frag make(const float v[8]) {
-    u32x4_t hw, lw;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      uint32_t h, l;
-      split2(v[2 * e], v[2 * e + 1], h, l);
-      hw[e] = h;
-      lw[e] = l;
-    }
-    Frag f;
-    f.hi = __builtin_bit_cast(bf16x8_t, hw);
-    f.lo = __builtin_bit_cast(bf16x8_t, lw);
-    return f;
-  }
-  __device__ __forceinline__ static Frag16 make16(const float v[4]) {
-    u32x2_t hw, lw;
-    uint32_t h, l;
-    split2(v[0], v[1], h, l);
-    hw[0] = h; lw[0] = l;
-    split2(v[2], v[3], h, l);
-    hw[1] = h; lw[1] = l;
-    Frag16 f;
-    f.hi = __builtin_bit_cast(s16x4_t, hw);
-    f.lo = __builtin_bit_cast(s16x4_t, lw);
-    return f;
-  }
-  __device__ __forceinline__ static void mma_part(f32x4_t& acc, const Frag& a, const Frag& b, int p) {
-    if (p == 0) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
-    else if (p == 1) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, acc, 0, 0, 0);
-    else acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc, 0, 0, 0);
-  }
-  __device__ __forceinline__ static void mma16_part(f32x4_t& acc, const Frag16& a, const Frag16& b, int p) {
-    if (p == 0) acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.hi, acc, 0, 0, 0);
-    else if (p == 1) acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.lo, acc, 0, 0, 0);
-    else acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.lo, b.hi, acc, 0, 0, 0);
-  }
-};
-
-struct PolF32 {
-  static constexpr int kPlanes = 1;
-  static constexpr int kElem = 4;
-  static constexpr int kParts = 8;
-  static constexpr int kParts16 = 4;
-  struct Frag {
-    float v[8];
-  };
-  struct Frag16 {
-    float v[4];
-  };
-  __device__ __forceinline__ static void store4(char* base, int, int off, const float v[4]) {
-    *reinterpret_cast<float4*>(base + off) = make_float4(v[0], v[1], v[2], v[3]);
-  }
-  __device__ __forceinline__ static void store1(char* base, int, int off, float v) {
-    *reinterpret_cast<float*>(base + off) = v;
-  }
-  __device__ __forceinline__ static Frag load(const char* base, int, int off) {
-    Frag f;
-    const float4 a = *reinterpret_cast<const float4*>(base + off);
-    const float4 b = *reinterpret_cast<const float4*>(base + off + 16);
-    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
-    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
-    return f;
-  }
-  __device__ __forceinline__ static Frag16 load16(const char* base, int, int off) {
-    Frag16 f;
-    const float4 a = *reinterpret_cast<const float4*>(base + off);
-    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
-    return f;
-  }
-  __device__ __forceinline__ static Frag make(const float v[8]) {
-    Frag f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) f.v[e] = v[e];
-    return f;
-  }
-  __device__ __forceinline__ static Frag16 make16(const float v[4]) {
-    Frag16 f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) f.v[e] = v[e];
-    return f;
-  }
-  __device__ __forceinline__ static void mma_part(f32x4_t& acc, const Frag& a, const Frag& b, int p) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[p], b.v[p], acc, 0, 0, 0);
-  }
-  __device__ __forceinline__ static void mma16_part(f32x4_t& acc, const Frag16& a, const Frag16& b, int p) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[p], b.v[p], acc, 0, 0, 0);
-  }
-};
-
-// ---------------------------------------------------------------------------
-// LDS layout (bytes).  Row strides are padded so that the 16 rows read by one
-// MFMA operand load fall in distinct banks.
-// ---------------------------------------------------------------------------
 template <class Pol>
 struct Lds {
   static constexpr int E = Pol::kElem;
   static constexpr int P = Pol::kPlanes;
-  static constexpr int kOpRow = kD * E + 16;              // [64 tok][128 ch]: Kh, Kc, Qh
+  static constexpr int kOpRow = kD * E + 16;               // [32 tok][128 ch]: Kh, Kc, Qh
   static constexpr int kOpPlane = kC * kOpRow;
   static constexpr int kOpBytes = P * kOpPlane;
-  static constexpr int kKbRow = kC * E + 16;              // [128 ch][64 tok]: Kb^T
+  static constexpr int kKbRow = kC * E + 16;               // [128 ch][32 tok]: Kb^T
   static constexpr int kKbPlane = kD * kKbRow;
   static constexpr int kKbBytes = P * kKbPlane;
-  static constexpr int kSqRow = kC * E + 16;              // [64][64] operands: A, P, T'
+  static constexpr int kSqRow = kC * E + 16;               // [32][32]: T', P
   static constexpr int kSqPlane = kC * kSqRow;
   static constexpr int kSqBytes = P * kSqPlane;
-  static constexpr int kDgRow = E == 2 ? 40 : 80;         // [4 x 16 rows][16 cols]: T_II (natural order)
-  static constexpr int kDgPlane = kC * kDgRow;
+  static constexpr int kNatRow = 16 * E + (E == 2 ? 8 : 16);  // [rows][16], natural order: A_10, T_II
+  static constexpr int kAopPlane = 16 * kNatRow;
+  static constexpr int kAopBytes = P * kAopPlane;
+  static constexpr int kDgPlane = kC * kNatRow;
   static constexpr int kDgBytes = P * kDgPlane;
-  static constexpr int kBlkLd = 20;                       // fp32 [4][16][20] blocks
-  static constexpr int kBlkBytes = 4 * 16 * kBlkLd * 4;
-  // regions
-  static constexpr int kKh = 0;
-  static constexpr int kKc = kKh + kOpBytes;              // Kc; then A (operand) | P; A's part becomes T'
-  static constexpr int kKcBytes = kOpBytes > 2 * kSqBytes ? kOpBytes : 2 * kSqBytes;
-  static constexpr int kAop = kKc;
-  static constexpr int kPbuf = kKc + kSqBytes;
-  static constexpr int kQh = kKc + kKcBytes;
-  static constexpr int kKb = kQh + kOpBytes;
-  static constexpr int kDg = kKb + kKbBytes;              // T_II as MFMA operands
-  static constexpr int kAt = kDg + kDgBytes;              // A_II transposed, fp32: At[I][s][r]
-  static constexpr int kTd = kAt + kBlkBytes;             // T_II column-major, fp32: Td[I][j][r]
-  static constexpr int kBeta = kTd + kBlkBytes;           // 64 floats
-  static constexpr int kGamma = kBeta + kC * 4;           // 128 floats
-  static constexpr int kBytes = kGamma + kD * 4;
+  static constexpr int kFLd = 20;                          // fp32 [2 blocks][16][20]
+  static constexpr int kFBytes = 2 * 16 * kFLd * 4;
+  // one operand set (read by the state waves)
+  static constexpr int kSetKh = 0;
+  static constexpr int kSetQh = kSetKh + kOpBytes;
+  static constexpr int kSetKb = kSetQh + kOpBytes;
+  static constexpr int kSetTp = kSetKb + kKbBytes;
+  static constexpr int kSetP = kSetTp + kSqBytes;
+  static constexpr int kSetGamma = kSetP + kSqBytes;
+  static constexpr int kSetBytes = kSetGamma + kD * 4;
+  // prep scratch
+  static constexpr int kKc = 2 * kSetBytes;
+  static constexpr int kAop = kKc + kOpBytes;              // A_10 (beta-scaled), MFMA operand
+  static constexpr int kDg = kAop + kAopBytes;             // T_00 | T_11 as MFMA operands
+  static constexpr int kAt = kDg + kDgBytes;               // A_II transposed, fp32: At[I][s][r]
+  static constexpr int kTd = kAt + kFBytes;                // T_II column-major, fp32: Td[I][j][r]
+  static constexpr int kBeta = kTd + kFBytes;              // 32 floats
+  static constexpr int kBytes = kBeta + kC * 4;
   static_assert(kBytes <= 160 * 1024, "LDS budget");
-  static_assert(kOpRow % 16 == 0 && kKbRow % 16 == 0 && kSqRow % 16 == 0 && kDgRow % 8 == 0, "aligned rows");
+  static_assert(kOpRow % 16 == 0 && kKbRow % 16 == 0 && kSqRow % 16 == 0 && kSetBytes % 16 == 0, "aligned");
+  static_assert(kNatRow % 8 == 0 && (E == 2 || kNatRow % 16 == 0), "aligned natural rows");
 };
 
 struct PrefillArgs {
@@ -275,58 +106,52 @@ struct PrefillArgs {
   float* transition_out;
 };
 
-// Stage-1 tile lists of waves 1..3, entry u of wave w packed in 5 bits as
-// (is_P << 4) | (I << 2) | J; waves hold 6, 5, 5 tiles:
-//   wave 1: A10 A20 A21 A30 P00 P10;  wave 2: A31 A32 P11 P20 P21;  wave 3: P22 P30 P31 P32 P33
-__host__ __device__ constexpr uint32_t tile_code(int isP, int I, int J) { return uint32_t((isP << 4) | (I << 2) | J); }
-__host__ __device__ constexpr uint32_t pack6(uint32_t a, uint32_t b, uint32_t c, uint32_t d, uint32_t e, uint32_t f) {
-  return a | (b << 5) | (c << 10) | (d << 15) | (e << 20) | (f << 25);
-}
-constexpr uint32_t kTiles1 = pack6(tile_code(0, 1, 0), tile_code(0, 2, 0), tile_code(0, 2, 1), tile_code(0, 3, 0),
-                                   tile_code(1, 0, 0), tile_code(1, 1, 0));
-constexpr uint32_t kTiles2 = pack6(tile_code(0, 3, 1), tile_code(0, 3, 2), tile_code(1, 1, 1), tile_code(1, 2, 0),
-                                   tile_code(1, 2, 1), 0);
-constexpr uint32_t kTiles3 = pack6(tile_code(1, 2, 2), tile_code(1, 3, 0), tile_code(1, 3, 1), tile_code(1, 3, 2),
-                                   tile_code(1, 3, 3), 0);
-
-// Inputs of one chunk as loaded (packed) into registers.
-template <class InT, int JB>
-struct ChunkIn {
-  float4 g[8];
-  typename InT::raw4 k[8], q[8];
+// Prep-thread inputs of one chunk (4 tokens x 4 channels), as loaded.
+template <class InT>
+struct PrepIn {
+  float4 g[4];
+  typename InT::raw4 k[4], q[4];
   float beta;
-  typename InT::raw1 v[JB][4][4];
 };
 
-template <class InT, int JB>
-__device__ __forceinline__ void load_chunk(ChunkIn<InT, JB>& in, const PrefillArgs& a, int t0, int n, int h,
-                                           int tg, int c0, int tid, int lq, int lj, int colw, bool load_v) {
+template <class InT>
+__device__ __forceinline__ void load_prep(PrepIn<InT>& in, const PrefillArgs& a, int t0, int n, int h, int tg, int c0,
+                                          int ptid) {
   const int64_t H = a.H;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = tg * 8 + i;
-    const int rr = r < n ? r : n - 1;  // clamp: always a valid token; zeroed later
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * tg + i;
+    const int rr = r < n ? r : n - 1;  // clamped: always a valid token; zeroed when used
     const int64_t base = (int64_t(t0 + rr) * H + h) * kD + c0;
     in.g[i] = ld_f4(a.g + base);
     in.k[i] = InT::load4raw(a.k, base);
     in.q[i] = InT::load4raw(a.q, base);
   }
-  {
-    const int rr = tid < n ? tid : n - 1;
-    in.beta = (tid < kC) ? a.beta[int64_t(t0 + rr) * H + h] : 0.0f;
-  }
-  if (load_v) {
+  // unconditional (clamped) so that nothing waits on it before its use
+  const int rr = ptid < n ? ptid : n - 1;
+  in.beta = a.beta[int64_t(t0 + rr) * H + h];
+}
+
+// State-wave v at this wave's columns, accumulator layout (rows 16rt+4lq+i).
+template <class InT, int JB>
+struct StateV {
+  typename InT::raw1 v[JB][2][4];
+};
+
+template <class InT, int JB>
+__device__ __forceinline__ void load_state_v(StateV<InT, JB>& sv, const PrefillArgs& a, int t0, int n, int h, int lq,
+                                             int lj, int colw) {
+  const int64_t H = a.H;
 #pragma unroll
-    for (int jb = 0; jb < JB; ++jb)
+  for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
+    for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * rt + 4 * lq + i;
-          const int rr = r < n ? r : n - 1;
-          in.v[jb][rt][i] = InT::load1raw(a.v, (int64_t(t0 + rr) * H + h) * kD + colw + 16 * jb + lj);
-        }
-  }
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * lq + i;
+        const int rr = r < n ? r : n - 1;
+        sv.v[jb][rt][i] = InT::load1raw(a.v, (int64_t(t0 + rr) * H + h) * kD + colw + 16 * jb + lj);
+      }
 }
 
 template <class Pol, class InT, int JB>
@@ -337,15 +162,15 @@ __global__ __launch_bounds__(kThreads) void kda_prefill_kernel(PrefillArgs a) {
   constexpr int E = L::E;
   __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
   float* s_beta = reinterpret_cast<float*>(smem + L::kBeta);
-  float* s_gamma = reinterpret_cast<float*>(smem + L::kGamma);
   float* s_at = reinterpret_cast<float*>(smem + L::kAt);
   float* s_td = reinterpret_cast<float*>(smem + L::kTd);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int lq = lane >> 4;  // lane group (contraction slots / output rows 4lq..)
-  const int lj = lane & 15;  // output column / operand row within a tile
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lq = lane >> 4;
+  const int lj = lane & 15;
+  const bool is_state = wave < kStateWaves;
 
   const int slice = blockIdx.x % a.n_slices;
   const int sh = blockIdx.x / a.n_slices;
@@ -353,456 +178,418 @@ __global__ __launch_bounds__(kThreads) void kda_prefill_kernel(PrefillArgs a) {
   const int seq = sh / a.H;
   const bool is_transition = slice >= a.n_value_slices;
   const int vslice = is_transition ? slice - a.n_value_slices : slice;
-  const int colw = vslice * (64 * JB) + wave * (16 * JB);  // first column of this wave
   const int64_t H = a.H;
   const int64_t tile_base = (int64_t(seq) * H + h) * (kD * kD);
-
   const int bos = a.cu_seqlens[seq];
   const int eos = a.cu_seqlens[seq + 1];
+  const int nch = (eos - bos + kC - 1) / kC;
   const bool want_o = !is_transition && a.o != nullptr;
-  float* const s_out = is_transition ? a.transition_out : a.final_state;
 
-  // ---- entry state in accumulator layout: S[jb][ct][i] = S0[16ct+4lq+i][colw+16jb+lj]
+  // state-wave roles
+  const int colw = vslice * (64 * JB) + (is_state ? wave : 0) * (16 * JB);
+  // prep-thread roles: 4 consecutive tokens x 4 consecutive channels
+  const int ptid = tid - kStateWaves * 64;
+  const int tg = ptid & 7;
+  const int c0 = (ptid >> 3) * 4;
+  const int pw = wave - kStateWaves;
+
   f32x4_t S[JB][8];
-  if (is_transition) {
-#pragma unroll
-    for (int jb = 0; jb < JB; ++jb)
-#pragma unroll
-      for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) S[jb][ct][i] = (16 * ct + 4 * lq + i == colw + 16 * jb + lj) ? 1.0f : 0.0f;
-  } else if (a.initial_state != nullptr) {
-    const float* src = a.initial_state + tile_base + colw + lj;
-#pragma unroll
-    for (int jb = 0; jb < JB; ++jb)
-#pragma unroll
-      for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) S[jb][ct][i] = src[(16 * ct + 4 * lq + i) * kD + 16 * jb];
-  } else {
-#pragma unroll
-    for (int jb = 0; jb < JB; ++jb)
-#pragma unroll
-      for (int ct = 0; ct < 8; ++ct) S[jb][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
-
-  // stage-0 thread roles: 8 consecutive tokens x 4 consecutive channels
-  const int tg = tid & 7;
-  const int cq = tid >> 3;
-  const int c0 = cq * 4;
-
-  ChunkIn<InT, JB> in;
-  if (bos < eos) load_chunk<InT, JB>(in, a, bos, (eos - bos) < kC ? (eos - bos) : kC, h, tg, c0, tid, lq, lj, colw,
-                                     !is_transition);
-
-  for (int t0 = bos; t0 < eos; t0 += kC) {
-    const int n = (eos - t0) < kC ? (eos - t0) : kC;
-
-    // ================= stage 0: decay prefix, rescaled operands =================
-    float vreg[JB][4][4];
-    {
-      float gq[8][4], kq[8][4], qv[8][4];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const bool ok = tg * 8 + i < n;
-        float kk[4], qq[4];
-        InT::unpack4(in.k[i], kk);
-        InT::unpack4(in.q[i], qq);
-        gq[i][0] = ok ? in.g[i].x : 0.0f; gq[i][1] = ok ? in.g[i].y : 0.0f;
-        gq[i][2] = ok ? in.g[i].z : 0.0f; gq[i][3] = ok ? in.g[i].w : 0.0f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kq[i][e] = ok ? kk[e] : 0.0f;
-          qv[i][e] = ok ? qq[e] * a.scale : 0.0f;
-        }
-      }
+  if (is_state) {
+    if (is_transition) {
 #pragma unroll
       for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
+        for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            vreg[jb][rt][i] = (!is_transition && 16 * rt + 4 * lq + i < n) ? InT::unpack1(in.v[jb][rt][i]) : 0.0f;
-      if (tid < kC) s_beta[tid] = tid < n ? in.beta : 0.0f;
+          for (int i = 0; i < 4; ++i) S[jb][ct][i] = (16 * ct + 4 * lq + i == colw + 16 * jb + lj) ? 1.0f : 0.0f;
+    } else if (a.initial_state != nullptr) {
+      const float* src = a.initial_state + tile_base + colw + lj;
 #pragma unroll
-      for (int i = 1; i < 8; ++i) {
+      for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) gq[i][e] += gq[i - 1][e];
-      }
-      float incl[4], excl[4], blast[4];
+        for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) incl[e] = gq[7][e];
-#pragma unroll
-      for (int d = 1; d < 8; d <<= 1) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float y = __shfl_up(incl[e], d, 8);
-          if (tg >= d) incl[e] += y;
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float y = __shfl_up(incl[e], 1, 8);
-        excl[e] = (tg == 0) ? 0.0f : y;
-        blast[e] = __shfl(excl[e] + gq[7][e], 7, 8);  // b at the chunk's last row
-      }
-      float kbv[8][4], gam[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) gam[e] = __expf(blast[e]);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = tg * 8 + i;
-        float kh[4], kc[4], qh[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float b = excl[e] + gq[i][e];
-          const float eb = __expf(b);
-          kh[e] = kq[i][e] * eb;
-          kc[e] = kq[i][e] * __expf(-b);
-          qh[e] = qv[i][e] * eb;
-          kbv[i][e] = kc[e] * gam[e];  // k e^{b_last - b}
-        }
-        const int off = r * L::kOpRow + kperm(c0) * E;
-        Pol::store4(smem + L::kKh, L::kOpPlane, off, kh);
-        Pol::store4(smem + L::kKc, L::kOpPlane, off, kc);
-        Pol::store4(smem + L::kQh, L::kOpPlane, off, qh);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = (c0 + e) * L::kKbRow;
-        const float lo4[4] = {kbv[0][e], kbv[1][e], kbv[2][e], kbv[3][e]};
-        const float hi4[4] = {kbv[4][e], kbv[5][e], kbv[6][e], kbv[7][e]};
-        Pol::store4(smem + L::kKb, L::kKbPlane, row + kperm(8 * tg) * E, lo4);
-        Pol::store4(smem + L::kKb, L::kKbPlane, row + kperm(8 * tg + 4) * E, hi4);
-      }
-      if (tg == 0) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s_gamma[c0 + e] = gam[e];
-      }
-    }
-    __syncthreads();  // B1
-
-    // ================= stage 1: A, P tiles; diagonal inverses =================
-    f32x4_t acc1[6];
-    if (wave == 0) {
-      // diagonal tiles of A
-#pragma unroll
-      for (int I = 0; I < 4; ++I) acc1[I] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int koff = (32 * ks + 8 * lq) * E;
-        Frag fa[4], fb[4];
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-          fa[I] = Pol::load(smem + L::kKh, L::kOpPlane, (16 * I + lj) * L::kOpRow + koff);
-          fb[I] = Pol::load(smem + L::kKc, L::kOpPlane, (16 * I + lj) * L::kOpRow + koff);
-        }
-#pragma unroll
-        for (int p = 0; p < Pol::kParts; ++p)
-#pragma unroll
-          for (int I = 0; I < 4; ++I) Pol::mma_part(acc1[I], fa[I], fb[I], p);
-      }
-      // At[I][s][r] = A[16I+r][16I+s] = beta_r * (Kh Kc^T)[r][s] for r > s
-#pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        float4 w;
-        float* wp = reinterpret_cast<float*>(&w);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * lq + i;
-          wp[i] = (r > lj) ? acc1[I][i] * s_beta[16 * I + r] : 0.0f;
-        }
-        *reinterpret_cast<float4*>(s_at + (I * 16 + lj) * L::kBlkLd + 4 * lq) = w;
-      }
-      wave_sync();
-      // T_II = (I + A_II)^{-1}: lane (I = lane/16, column j); right-looking substitution
-      {
-        const int I = lane >> 4, j = lane & 15;
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = (r == j) ? 1.0f : 0.0f;
-#pragma unroll
-        for (int s = 0; s < 15; ++s) {
-          const float* col = s_at + (I * 16 + s) * L::kBlkLd;  // column s of A_II
-          float cv[16];
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const float4 w = *reinterpret_cast<const float4*>(col + 4 * r4);
-            cv[4 * r4] = w.x; cv[4 * r4 + 1] = w.y; cv[4 * r4 + 2] = w.z; cv[4 * r4 + 3] = w.w;
-          }
-#pragma unroll
-          for (int r = s + 1; r < 16; ++r) x[r] = fmaf(-cv[r], x[s], x[r]);
-        }
-        // Td[I][j][r] = T_II[r][j] (column-major fp32) and T_II as an MFMA operand
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4)
-          *reinterpret_cast<float4*>(s_td + (I * 16 + j) * L::kBlkLd + 4 * r4) =
-              make_float4(x[4 * r4], x[4 * r4 + 1], x[4 * r4 + 2], x[4 * r4 + 3]);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) Pol::store1(smem + L::kDg, L::kDgPlane, (16 * I + r) * L::kDgRow + j * E, x[r]);
-      }
+          for (int i = 0; i < 4; ++i) S[jb][ct][i] = src[(16 * ct + 4 * lq + i) * kD + 16 * jb];
     } else {
-      const uint32_t tiles = wave == 1 ? kTiles1 : (wave == 2 ? kTiles2 : kTiles3);
-      const int cnt = (wave == 1) ? 6 : 5;
 #pragma unroll
-      for (int u = 0; u < 6; ++u) acc1[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int koff = (32 * ks + 8 * lq) * E;
-        Frag fa[6], fb[6];
-#pragma unroll
-        for (int u = 0; u < 6; ++u) {
-          if (u < cnt) {
-            const uint32_t code = (tiles >> (5 * u)) & 31u;
-            const char* abase = smem + ((code >> 4) ? L::kQh : L::kKh);
-            fa[u] = Pol::load(abase, L::kOpPlane, (16 * int((code >> 2) & 3u) + lj) * L::kOpRow + koff);
-            fb[u] = Pol::load(smem + L::kKc, L::kOpPlane, (16 * int(code & 3u) + lj) * L::kOpRow + koff);
-          }
-        }
-#pragma unroll
-        for (int p = 0; p < Pol::kParts; ++p)
-#pragma unroll
-          for (int u = 0; u < 6; ++u)
-            if (u < cnt) Pol::mma_part(acc1[u], fa[u], fb[u], p);
-      }
+        for (int ct = 0; ct < 8; ++ct) S[jb][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    __syncthreads();  // B2: Kc is dead; its region takes A (operand) and P
-    if (wave != 0) {
-      const uint32_t tiles = wave == 1 ? kTiles1 : (wave == 2 ? kTiles2 : kTiles3);
-      const int cnt = (wave == 1) ? 6 : 5;
-#pragma unroll
-      for (int u = 0; u < 6; ++u) {
-        if (u < cnt) {
-          const uint32_t code = (tiles >> (5 * u)) & 31u;
-          const bool isP = (code >> 4) != 0;
-          const int I = int((code >> 2) & 3u), J = int(code & 3u);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 16 * I + 4 * lq + i;
-            const int s = 16 * J + lj;
-            if (isP) Pol::store1(smem + L::kPbuf, L::kSqPlane, r * L::kSqRow + kperm(s) * E, (s <= r) ? acc1[u][i] : 0.0f);
-            else Pol::store1(smem + L::kAop, L::kSqPlane, r * L::kSqRow + kperm(s) * E, acc1[u][i] * s_beta[r]);
-          }
-        }
-      }
-      // zero the upper tiles of P (read by the 32-deep steps of P U): 6 tiles x 256 over 192 threads
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int idx = (tid - 64) + 192 * e;  // 0 .. 1535
-        const int ut = idx >> 8, wi = idx & 255;
-        const int I = (ut < 3) ? 0 : (ut < 5 ? 1 : 2);
-        const int J = (ut < 3) ? ut + 1 : (ut < 5 ? ut - 1 : 3);
-        const int r = 16 * I + (wi >> 4), s = 16 * J + (wi & 15);
-        Pol::store1(smem + L::kPbuf, L::kSqPlane, r * L::kSqRow + kperm(s) * E, 0.0f);
-      }
-    }
-    __syncthreads();  // B3
+  }
 
-    // ================= stage 2: T = (I + A)^{-1} by column blocks =================
-    f32x4_t Tt[4];
-#pragma unroll
-    for (int I = 0; I < 4; ++I) Tt[I] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    {
-      const int J = wave;
-      {
-        const float4 w = *reinterpret_cast<const float4*>(s_td + (J * 16 + lj) * L::kBlkLd + 4 * lq);
-        Tt[J] = f32x4_t{w.x, w.y, w.z, w.w};  // rows 4lq.. of column lj of T_JJ
-      }
-#pragma unroll
-      for (int I = 1; I < 4; ++I) {
-        if (I > J) {
-          f32x4_t X = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int K = 0; K < 3; ++K) {
-            if (K >= J && K < I) {
-              const Frag16 fa = Pol::load16(smem + L::kAop, L::kSqPlane,
-                                            (16 * I + lj) * L::kSqRow + kperm(16 * K + 4 * lq) * E);
-              const float bv[4] = {Tt[K][0], Tt[K][1], Tt[K][2], Tt[K][3]};
-              const Frag16 fb = Pol::make16(bv);
-#pragma unroll
-              for (int p = 0; p < Pol::kParts16; ++p) Pol::mma16_part(X, fa, fb, p);
+  // The two roles run separate loops (so each keeps only its own values in
+  // registers) with the same three barriers per step.
+  if (is_state) {
+    StateV<InT, JB> sv;
+    f32x4_t accR[JB][2], accO[JB][2];
+    Frag uf[JB];
+    // step 0: the prep waves build chunk 0; fetch chunk 0's v
+    if (nch > 0) load_state_v<InT, JB>(sv, a, bos, eos - bos < kC ? eos - bos : kC, h, lq, lj, colw);
+    __syncthreads();
+    __syncthreads();
+    __syncthreads();
+    for (int i = 1; i <= nch; ++i) {
+      // this step consumes chunk i - 1 from operand set (i - 1) % 2
+      const int ts = bos + (i - 1) * kC;
+      const int ns = eos - ts < kC ? eos - ts : kC;
+      const char* sset = smem + ((i + 1) & 1) * L::kSetBytes;
+
+      // ============================== phase A ==============================
+        {
+  #pragma unroll
+          for (int jb = 0; jb < JB; ++jb)
+  #pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+  #pragma unroll
+              for (int e = 0; e < 4; ++e)
+                accR[jb][rt][e] = (!is_transition && 16 * rt + 4 * lq + e < ns) ? -InT::unpack1(sv.v[jb][rt][e]) : 0.0f;
+              accO[jb][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+          // R = V - Kh S (accumulated as Kh S - V), then O = Qh S
+  #pragma unroll
+          for (int pass = 0; pass < 2; ++pass) {
+            if (pass == 1 && !want_o) break;
+            const char* abase = sset + (pass == 0 ? L::kSetKh : L::kSetQh);
+  #pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+              Frag sf[JB];
+  #pragma unroll
+              for (int jb = 0; jb < JB; ++jb) {
+                const float v8[8] = {S[jb][2 * ks][0], S[jb][2 * ks][1], S[jb][2 * ks][2], S[jb][2 * ks][3],
+                                     S[jb][2 * ks + 1][0], S[jb][2 * ks + 1][1], S[jb][2 * ks + 1][2],
+                                     S[jb][2 * ks + 1][3]};
+                sf[jb] = Pol::make(v8);
+              }
+              const int koff = (32 * ks + 8 * lq) * E;
+              Frag fk[2];
+  #pragma unroll
+              for (int rt = 0; rt < 2; ++rt) fk[rt] = Pol::load(abase, L::kOpPlane, (16 * rt + lj) * L::kOpRow + koff);
+  #pragma unroll
+              for (int p = 0; p < Pol::kParts; ++p)
+  #pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+  #pragma unroll
+                  for (int jb = 0; jb < JB; ++jb) {
+                    if (pass == 0) Pol::mma_part(accR[jb][rt], fk[rt], sf[jb], p);
+                    else Pol::mma_part(accO[jb][rt], fk[rt], sf[jb], p);
+                  }
             }
           }
-          const Frag16 ft = Pol::load16(smem + L::kDg, L::kDgPlane, (16 * I + lj) * L::kDgRow + 4 * lq * E);
+        }
+      __syncthreads();
+      // ============================== phase B ==============================
+        {
+          // U = T' R (one 32-deep step), then O += P U and the outputs
+          Frag rf[JB];
+  #pragma unroll
+          for (int jb = 0; jb < JB; ++jb) {
+            const float v8[8] = {-accR[jb][0][0], -accR[jb][0][1], -accR[jb][0][2], -accR[jb][0][3],
+                                 -accR[jb][1][0], -accR[jb][1][1], -accR[jb][1][2], -accR[jb][1][3]};
+            rf[jb] = Pol::make(v8);
+          }
+          f32x4_t accU[JB][2];
+  #pragma unroll
+          for (int jb = 0; jb < JB; ++jb)
+  #pragma unroll
+            for (int rt = 0; rt < 2; ++rt) accU[jb][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          {
+            Frag ft[2];
+  #pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+              ft[rt] = Pol::load(sset + L::kSetTp, L::kSqPlane, (16 * rt + lj) * L::kSqRow + 8 * lq * E);
+  #pragma unroll
+            for (int p = 0; p < Pol::kParts; ++p)
+  #pragma unroll
+              for (int rt = 0; rt < 2; ++rt)
+  #pragma unroll
+                for (int jb = 0; jb < JB; ++jb) Pol::mma_part(accU[jb][rt], ft[rt], rf[jb], p);
+          }
+  #pragma unroll
+          for (int jb = 0; jb < JB; ++jb) {
+            const float v8[8] = {accU[jb][0][0], accU[jb][0][1], accU[jb][0][2], accU[jb][0][3],
+                                 accU[jb][1][0], accU[jb][1][1], accU[jb][1][2], accU[jb][1][3]};
+            uf[jb] = Pol::make(v8);
+          }
+          if (want_o) {
+            Frag fp[2];
+  #pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+              fp[rt] = Pol::load(sset + L::kSetP, L::kSqPlane, (16 * rt + lj) * L::kSqRow + 8 * lq * E);
+  #pragma unroll
+            for (int p = 0; p < Pol::kParts; ++p)
+  #pragma unroll
+              for (int rt = 0; rt < 2; ++rt)
+  #pragma unroll
+                for (int jb = 0; jb < JB; ++jb) Pol::mma_part(accO[jb][rt], fp[rt], uf[jb], p);
+  #pragma unroll
+            for (int jb = 0; jb < JB; ++jb)
+  #pragma unroll
+              for (int rt = 0; rt < 2; ++rt)
+  #pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const int r = 16 * rt + 4 * lq + e;
+                  if (r < ns) InT::store1(a.o, (int64_t(ts + r) * H + h) * kD + colw + 16 * jb + lj, accO[jb][rt][e]);
+                }
+          }
+        }
+      __syncthreads();
+      // ============================== phase C ==============================
+        {
+          // S = Gamma S + Kb^T U, in two halves of four row tiles
+          const float* s_gamma = reinterpret_cast<const float*>(sset + L::kSetGamma);
+  #pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            Frag fb[4];
+  #pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const int ct = 4 * half + c;
+              const float4 gm = *reinterpret_cast<const float4*>(s_gamma + 16 * ct + 4 * lq);
+  #pragma unroll
+              for (int jb = 0; jb < JB; ++jb) {
+                S[jb][ct][0] *= gm.x; S[jb][ct][1] *= gm.y; S[jb][ct][2] *= gm.z; S[jb][ct][3] *= gm.w;
+              }
+              fb[c] = Pol::load(sset + L::kSetKb, L::kKbPlane, (16 * ct + lj) * L::kKbRow + 8 * lq * E);
+            }
+  #pragma unroll
+            for (int p = 0; p < Pol::kParts; ++p)
+  #pragma unroll
+              for (int c = 0; c < 4; ++c)
+  #pragma unroll
+                for (int jb = 0; jb < JB; ++jb) Pol::mma_part(S[jb][4 * half + c], fb[c], uf[jb], p);
+          }
+        }
+        {  // fetch chunk i's v (clamped to the last chunk; unconditional so nothing waits on it)
+          const int tv = bos + (i < nch ? i : nch - 1) * kC;
+          load_state_v<InT, JB>(sv, a, tv, eos - tv < kC ? eos - tv : kC, h, lq, lj, colw);
+        }
+      __syncthreads();
+    }
+  } else {
+    PrepIn<InT> pin;
+    if (nch > 0) load_prep<InT>(pin, a, bos, eos - bos < kC ? eos - bos : kC, h, tg, c0, ptid);
+    for (int i = 0; i < nch; ++i) {
+      // this step builds chunk i into operand set i % 2
+      const int tp = bos + i * kC;
+      const int np = eos - tp < kC ? eos - tp : kC;
+      char* pset = smem + (i & 1) * L::kSetBytes;
+
+      // ============================== phase A ==============================
+      {
+        // decay prefix and rescaled operands of chunk i
+        float gq[4][4], kq[4][4], qv[4][4];
+  #pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const bool ok = 4 * tg + r4 < np;
+          float kk[4], qq[4];
+          InT::unpack4(pin.k[r4], kk);
+          InT::unpack4(pin.q[r4], qq);
+          gq[r4][0] = ok ? pin.g[r4].x : 0.0f; gq[r4][1] = ok ? pin.g[r4].y : 0.0f;
+          gq[r4][2] = ok ? pin.g[r4].z : 0.0f; gq[r4][3] = ok ? pin.g[r4].w : 0.0f;
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            kq[r4][e] = ok ? kk[e] : 0.0f;
+            qv[r4][e] = ok ? qq[e] * a.scale : 0.0f;
+          }
+        }
+        if (ptid < kC) s_beta[ptid] = ptid < np ? pin.beta : 0.0f;
+  #pragma unroll
+        for (int r4 = 1; r4 < 4; ++r4)
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) gq[r4][e] += gq[r4 - 1][e];
+        float incl[4], excl[4], blast[4], gam[4];
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) incl[e] = gq[3][e];
+  #pragma unroll
+        for (int d = 1; d < 8; d <<= 1) {
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float y = __shfl_up(incl[e], d, 8);
+            if (tg >= d) incl[e] += y;
+          }
+        }
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float y = __shfl_up(incl[e], 1, 8);
+          excl[e] = (tg == 0) ? 0.0f : y;
+          blast[e] = __shfl(excl[e] + gq[3][e], 7, 8);  // b at the chunk's last row
+          gam[e] = __expf(blast[e]);
+        }
+        float kbv[4][4];
+  #pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int r = 4 * tg + r4;
+          float kh[4], kc[4], qh[4];
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float b = excl[e] + gq[r4][e];
+            const float eb = __expf(b);
+            kh[e] = kq[r4][e] * eb;
+            kc[e] = kq[r4][e] * __expf(-b);
+            qh[e] = qv[r4][e] * eb;
+            kbv[r4][e] = kc[e] * gam[e];  // k e^{b_last - b}
+          }
+          const int off = r * L::kOpRow + kperm(c0) * E;
+          Pol::store4(pset + L::kSetKh, L::kOpPlane, off, kh);
+          Pol::store4(smem + L::kKc, L::kOpPlane, off, kc);
+          Pol::store4(pset + L::kSetQh, L::kOpPlane, off, qh);
+        }
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float w4[4] = {kbv[0][e], kbv[1][e], kbv[2][e], kbv[3][e]};
+          Pol::store4(pset + L::kSetKb, L::kKbPlane, (c0 + e) * L::kKbRow + kperm(4 * tg) * E, w4);
+        }
+        if (tg == 0) {
+          float* g_out = reinterpret_cast<float*>(pset + L::kSetGamma);
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) g_out[c0 + e] = gam[e];
+        }
+      }
+      __syncthreads();
+      // ============================== phase B ==============================
+      {
+        {  // fetch chunk i + 1's inputs (clamped; unconditional so nothing waits on them)
+          const int tn = bos + (i + 1 < nch ? i + 1 : nch - 1) * kC;
+          load_prep<InT>(pin, a, tn, eos - tn < kC ? eos - tn : kC, h, tg, c0, ptid);
+        }
+        if (pw < 2) {
+          // diagonal tile A_II (I = pw), then T_II = (I + A_II)^{-1}
+          const int I = pw;
+          f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const int koff = (32 * ks + 8 * lq) * E;
+            const Frag fa = Pol::load(pset + L::kSetKh, L::kOpPlane, (16 * I + lj) * L::kOpRow + koff);
+            const Frag fb = Pol::load(smem + L::kKc, L::kOpPlane, (16 * I + lj) * L::kOpRow + koff);
+  #pragma unroll
+            for (int p = 0; p < Pol::kParts; ++p) Pol::mma_part(acc, fa, fb, p);
+          }
+          {  // At[I][s][r] = A[16I+r][16I+s] = beta_r (Kh Kc^T)[r][s] for r > s
+            float4 w;
+            float* wp = reinterpret_cast<float*>(&w);
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * lq + e;
+              wp[e] = (r > lj) ? acc[e] * s_beta[16 * I + r] : 0.0f;
+            }
+            *reinterpret_cast<float4*>(s_at + (I * 16 + lj) * L::kFLd + 4 * lq) = w;
+          }
+          wave_sync();
+          // every lane solves column j = lane % 16 (four copies per wave)
+          float x[16];
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) x[r] = (r == lj) ? 1.0f : 0.0f;
+  #pragma unroll
+          for (int s = 0; s < 15; ++s) {
+            const float* col = s_at + (I * 16 + s) * L::kFLd;  // column s of A_II
+            float cv[16];
+  #pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+              const float4 w = *reinterpret_cast<const float4*>(col + 4 * r4);
+              cv[4 * r4] = w.x; cv[4 * r4 + 1] = w.y; cv[4 * r4 + 2] = w.z; cv[4 * r4 + 3] = w.w;
+            }
+  #pragma unroll
+            for (int r = s + 1; r < 16; ++r) x[r] = fmaf(-cv[r], x[s], x[r]);
+          }
+          if (lq == 0) {
+  #pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4)
+              *reinterpret_cast<float4*>(s_td + (I * 16 + lj) * L::kFLd + 4 * r4) =
+                  make_float4(x[4 * r4], x[4 * r4 + 1], x[4 * r4 + 2], x[4 * r4 + 3]);
+  #pragma unroll
+            for (int r = 0; r < 16; ++r) Pol::store1(smem + L::kDg, L::kDgPlane, (16 * I + r) * L::kNatRow + lj * E, x[r]);
+          }
+        } else {
+          // pw 2: A_10 and P_00;  pw 3: P_10 and P_11
+          const bool w2 = (pw == 2);
+          f32x4_t acc0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, acc1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const int koff = (32 * ks + 8 * lq) * E;
+            // tile 0: w2 ? A_10 = Kh[16..31] Kc[0..15] : P_10 = Qh[16..31] Kc[0..15]
+            // tile 1: w2 ? P_00 = Qh[0..15] Kc[0..15]  : P_11 = Qh[16..31] Kc[16..31]
+            const Frag fa0 = Pol::load(pset + (w2 ? L::kSetKh : L::kSetQh), L::kOpPlane, (16 + lj) * L::kOpRow + koff);
+            const Frag fa1 = Pol::load(pset + L::kSetQh, L::kOpPlane, ((w2 ? 0 : 16) + lj) * L::kOpRow + koff);
+            const Frag fb0 = Pol::load(smem + L::kKc, L::kOpPlane, lj * L::kOpRow + koff);
+            const Frag fb1 = Pol::load(smem + L::kKc, L::kOpPlane, ((w2 ? 0 : 16) + lj) * L::kOpRow + koff);
+  #pragma unroll
+            for (int p = 0; p < Pol::kParts; ++p) {
+              Pol::mma_part(acc0, fa0, fb0, p);
+              Pol::mma_part(acc1, fa1, fb1, p);
+            }
+          }
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * lq + e;  // row within the 16-row tile
+            if (w2) {
+              // A_10 (beta-scaled rows), natural order [r][s] for a 16-deep operand
+              Pol::store1(smem + L::kAop, L::kAopPlane, r * L::kNatRow + lj * E, acc0[e] * s_beta[16 + r]);
+              Pol::store1(pset + L::kSetP, L::kSqPlane, r * L::kSqRow + kperm(lj) * E, (lj <= r) ? acc1[e] : 0.0f);
+            } else {
+              Pol::store1(pset + L::kSetP, L::kSqPlane, (16 + r) * L::kSqRow + kperm(lj) * E, acc0[e]);
+              Pol::store1(pset + L::kSetP, L::kSqPlane, (16 + r) * L::kSqRow + kperm(16 + lj) * E,
+                          (lj <= r) ? acc1[e] : 0.0f);
+              Pol::store1(pset + L::kSetP, L::kSqPlane, r * L::kSqRow + kperm(16 + lj) * E, 0.0f);  // upper block
+            }
+          }
+        }
+      }
+      __syncthreads();
+      // ============================== phase C ==============================
+      {
+        if (pw == 0) {
+          // T_10 = -T_11 (A_10 T_00)
+          const float4 w = *reinterpret_cast<const float4*>(s_td + (0 * 16 + lj) * L::kFLd + 4 * lq);
+          const float t00[4] = {w.x, w.y, w.z, w.w};  // rows 4lq.. of column lj of T_00
+          const Frag16 fa = Pol::load16(smem + L::kAop, L::kAopPlane, lj * L::kNatRow + 4 * lq * E);
+          const Frag16 fb = Pol::make16(t00);
+          f32x4_t X = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+          for (int p = 0; p < Pol::kParts16; ++p) Pol::mma16_part(X, fa, fb, p);
+          const Frag16 ft = Pol::load16(smem + L::kDg, L::kDgPlane, (16 + lj) * L::kNatRow + 4 * lq * E);
           const float xv[4] = {X[0], X[1], X[2], X[3]};
           const Frag16 fx = Pol::make16(xv);
           f32x4_t Y = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
+  #pragma unroll
           for (int p = 0; p < Pol::kParts16; ++p) Pol::mma16_part(Y, ft, fx, p);
-          Tt[I] = -Y;
+          const float bj = s_beta[lj];
+  #pragma unroll
+          for (int e = 0; e < 4; ++e)
+            Pol::store1(pset + L::kSetTp, L::kSqPlane, (16 + 4 * lq + e) * L::kSqRow + kperm(lj) * E, -Y[e] * bj);
+        } else if (pw <= 2) {
+          // diagonal blocks T'_II = T_II diag(beta) (pw 1: I = 0 and the zero upper block; pw 2: I = 1)
+          const int I = pw - 1;
+          const float4 w = *reinterpret_cast<const float4*>(s_td + (I * 16 + lj) * L::kFLd + 4 * lq);
+          const float tv[4] = {w.x, w.y, w.z, w.w};
+          const float bj = s_beta[16 * I + lj];
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * lq + e;
+            Pol::store1(pset + L::kSetTp, L::kSqPlane, (16 * I + r) * L::kSqRow + kperm(16 * I + lj) * E,
+                        (r >= lj) ? tv[e] * bj : 0.0f);
+            if (I == 0) Pol::store1(pset + L::kSetTp, L::kSqPlane, r * L::kSqRow + kperm(16 + lj) * E, 0.0f);
+          }
         }
       }
+      __syncthreads();
     }
-    __syncthreads();  // B4: every read of A is done; its region takes T'
-    {
-      const int J = wave;
-      const float bj = s_beta[16 * J + lj];
-#pragma unroll
-      for (int I = 0; I < 4; ++I) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * I + 4 * lq + i;
-          const int s = 16 * J + lj;
-          const float val = (I > J || (I == J && r >= s)) ? Tt[I][i] * bj : 0.0f;
-          Pol::store1(smem + L::kAop, L::kSqPlane, r * L::kSqRow + kperm(s) * E, val);
-        }
-      }
-    }
-    __syncthreads();  // B5
-
-    // ================= stage 3: state pass (per wave, registers) =================
-    {
-      f32x4_t accR[JB][4], accO[JB][4];
-#pragma unroll
-      for (int jb = 0; jb < JB; ++jb)
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          accR[jb][rt] = f32x4_t{-vreg[jb][rt][0], -vreg[jb][rt][1], -vreg[jb][rt][2], -vreg[jb][rt][3]};
-          accO[jb][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
-      // R = V - Kh S (accumulated as Kh S - V), then O = Qh S; one operand set live at a time
-#pragma unroll
-      for (int pass = 0; pass < 2; ++pass) {
-        if (pass == 1 && !want_o) break;
-        const char* abase = smem + (pass == 0 ? L::kKh : L::kQh);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          Frag sf[JB];
-#pragma unroll
-          for (int jb = 0; jb < JB; ++jb) {
-            const float v8[8] = {S[jb][2 * ks][0], S[jb][2 * ks][1], S[jb][2 * ks][2], S[jb][2 * ks][3],
-                                 S[jb][2 * ks + 1][0], S[jb][2 * ks + 1][1], S[jb][2 * ks + 1][2], S[jb][2 * ks + 1][3]};
-            sf[jb] = Pol::make(v8);
-          }
-          const int koff = (32 * ks + 8 * lq) * E;
-          Frag fk[4];
-#pragma unroll
-          for (int rt = 0; rt < 4; ++rt) fk[rt] = Pol::load(abase, L::kOpPlane, (16 * rt + lj) * L::kOpRow + koff);
-#pragma unroll
-          for (int p = 0; p < Pol::kParts; ++p)
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-              for (int jb = 0; jb < JB; ++jb) {
-                if (pass == 0) Pol::mma_part(accR[jb][rt], fk[rt], sf[jb], p);
-                else Pol::mma_part(accO[jb][rt], fk[rt], sf[jb], p);
-              }
-        }
-      }
-      {  // fetch the next chunk's inputs; they land while the rest of this chunk runs
-        const int t1 = t0 + kC;
-        if (t1 < eos) load_chunk<InT, JB>(in, a, t1, (eos - t1) < kC ? (eos - t1) : kC, h, tg, c0, tid, lq, lj, colw,
-                                          !is_transition);
-      }
-      // U = T' R  (T' lower triangular: row tiles 0,1 use contraction tiles 0..1 only)
-      Frag rf[JB][2];
-#pragma unroll
-      for (int jb = 0; jb < JB; ++jb)
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const float v8[8] = {-accR[jb][2 * m][0], -accR[jb][2 * m][1], -accR[jb][2 * m][2], -accR[jb][2 * m][3],
-                               -accR[jb][2 * m + 1][0], -accR[jb][2 * m + 1][1], -accR[jb][2 * m + 1][2],
-                               -accR[jb][2 * m + 1][3]};
-          rf[jb][m] = Pol::make(v8);
-        }
-      f32x4_t accU[JB][4];
-#pragma unroll
-      for (int jb = 0; jb < JB; ++jb)
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) accU[jb][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      {
-        Frag ft[6];  // (rt, m): (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
-#pragma unroll
-        for (int x = 0; x < 6; ++x) {
-          const int rt = x < 2 ? x : 2 + ((x - 2) >> 1);
-          const int m = x < 2 ? 0 : ((x - 2) & 1);
-          ft[x] = Pol::load(smem + L::kAop, L::kSqPlane, (16 * rt + lj) * L::kSqRow + (32 * m + 8 * lq) * E);
-        }
-#pragma unroll
-        for (int p = 0; p < Pol::kParts; ++p)
-#pragma unroll
-          for (int x = 0; x < 6; ++x) {
-            const int rt = x < 2 ? x : 2 + ((x - 2) >> 1);
-            const int m = x < 2 ? 0 : ((x - 2) & 1);
-#pragma unroll
-            for (int jb = 0; jb < JB; ++jb) Pol::mma_part(accU[jb][rt], ft[x], rf[jb][m], p);
-          }
-      }
-      Frag uf[JB][2];
-#pragma unroll
-      for (int jb = 0; jb < JB; ++jb)
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const float v8[8] = {accU[jb][2 * m][0], accU[jb][2 * m][1], accU[jb][2 * m][2], accU[jb][2 * m][3],
-                               accU[jb][2 * m + 1][0], accU[jb][2 * m + 1][1], accU[jb][2 * m + 1][2],
-                               accU[jb][2 * m + 1][3]};
-          uf[jb][m] = Pol::make(v8);
-        }
-      // O += P U, then store the chunk's outputs
-      if (want_o) {
-        Frag fp[6];
-#pragma unroll
-        for (int x = 0; x < 6; ++x) {
-          const int rt = x < 2 ? x : 2 + ((x - 2) >> 1);
-          const int m = x < 2 ? 0 : ((x - 2) & 1);
-          fp[x] = Pol::load(smem + L::kPbuf, L::kSqPlane, (16 * rt + lj) * L::kSqRow + (32 * m + 8 * lq) * E);
-        }
-#pragma unroll
-        for (int p = 0; p < Pol::kParts; ++p)
-#pragma unroll
-          for (int x = 0; x < 6; ++x) {
-            const int rt = x < 2 ? x : 2 + ((x - 2) >> 1);
-            const int m = x < 2 ? 0 : ((x - 2) & 1);
-#pragma unroll
-            for (int jb = 0; jb < JB; ++jb) Pol::mma_part(accO[jb][rt], fp[x], uf[jb][m], p);
-          }
-#pragma unroll
-        for (int jb = 0; jb < JB; ++jb)
-#pragma unroll
-          for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int r = 16 * rt + 4 * lq + i;
-              if (r < n) InT::store1(a.o, (int64_t(t0 + r) * H + h) * kD + colw + 16 * jb + lj, accO[jb][rt][i]);
-            }
-      }
-      // S = Gamma S + Kb^T U, in two halves of four row tiles
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        Frag fb[4][2];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int ct = 4 * half + c;
-          const float4 gm = *reinterpret_cast<const float4*>(s_gamma + 16 * ct + 4 * lq);
-#pragma unroll
-          for (int jb = 0; jb < JB; ++jb) {
-            S[jb][ct][0] *= gm.x; S[jb][ct][1] *= gm.y; S[jb][ct][2] *= gm.z; S[jb][ct][3] *= gm.w;
-          }
-#pragma unroll
-          for (int m = 0; m < 2; ++m)
-            fb[c][m] = Pol::load(smem + L::kKb, L::kKbPlane, (16 * ct + lj) * L::kKbRow + (32 * m + 8 * lq) * E);
-        }
-#pragma unroll
-        for (int p = 0; p < Pol::kParts; ++p)
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-#pragma unroll
-              for (int jb = 0; jb < JB; ++jb) Pol::mma_part(S[jb][4 * half + c], fb[c][m], uf[jb][m], p);
-      }
-    }
-    __syncthreads();  // B6: LDS is rewritten by the next chunk
+    // step nch: the state waves consume the last chunk
+    __syncthreads();
+    __syncthreads();
+    __syncthreads();
   }
 
-  if (s_out != nullptr) {
-    float* dst = s_out + tile_base + colw + lj;
+  if (is_state) {
+    float* const s_out = is_transition ? a.transition_out : a.final_state;
+    if (s_out != nullptr) {
+      float* dst = s_out + tile_base + colw + lj;
 #pragma unroll
-    for (int jb = 0; jb < JB; ++jb)
+      for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct)
+        for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[(16 * ct + 4 * lq + i) * kD + 16 * jb] = S[jb][ct][i];
+          for (int e = 0; e < 4; ++e) dst[(16 * ct + 4 * lq + e) * kD + 16 * jb] = S[jb][ct][e];
+    }
   }
 }
 
@@ -827,9 +614,12 @@ hipError_t launch_jb(const PrefillLaunch& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_prefill(const PrefillLaunch& p, bool bf16, hipStream_t stream) {
-  // 64-column slices: two workgroups per (sequence, head) and value half.
-  if (bf16) return launch_jb<PolBF16x3, BF16, 1>(p, stream);
-  return launch_jb<PolF32, F32, 1>(p, stream);
+  // 128 value columns per workgroup when the grid has enough (sequence, head)
+  // work to fill the chip; otherwise 64 (two workgroups per sequence and head).
+  const int64_t units = int64_t(p.num_seqs) * p.H * (p.transition_out ? 2 : 1);
+  const bool wide = units >= 256;
+  if (bf16) return wide ? launch_jb<PolBF16x3, BF16, 2>(p, stream) : launch_jb<PolBF16x3, BF16, 1>(p, stream);
+  return wide ? launch_jb<PolF32, F32, 2>(p, stream) : launch_jb<PolF32, F32, 1>(p, stream);
 }
 
 }  // namespace kda
