@@ -72,6 +72,12 @@ struct PolBF16x3 {
     *reinterpret_cast<uint2*>(base + off) = make_uint2(h0, h1);
     *reinterpret_cast<uint2*>(base + plane + off) = make_uint2(l0, l1);
   }
+  __device__ __forceinline__ static void store2(char* base, int plane, int off, float a, float b) {
+    uint32_t h, l;
+    split2(a, b, h, l);
+    *reinterpret_cast<uint32_t*>(base + off) = h;
+    *reinterpret_cast<uint32_t*>(base + plane + off) = l;
+  }
   __device__ __forceinline__ static void store1(char* base, int plane, int off, float v) {
     const __bf16 h = (__bf16)v;
     const __bf16 l = (__bf16)(v - (float)h);
@@ -141,6 +147,9 @@ struct PolF32 {
   };
   __device__ __forceinline__ static void store4(char* base, int, int off, const float v[4]) {
     *reinterpret_cast<float4*>(base + off) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+  __device__ __forceinline__ static void store2(char* base, int, int off, float a, float b) {
+    *reinterpret_cast<float2*>(base + off) = make_float2(a, b);
   }
   __device__ __forceinline__ static void store1(char* base, int, int off, float v) {
     *reinterpret_cast<float*>(base + off) = v;

@@ -117,19 +117,22 @@ struct PrepIn {
 template <class InT>
 __device__ __forceinline__ void load_prep(PrepIn<InT>& in, const PrefillArgs& a, int t0, int n, int h, int tg, int c0,
                                           int ptid) {
-  const int64_t H = a.H;
+  // wave-uniform chunk base + 32-bit per-lane offsets; rows past the chunk end
+  // are clamped to its last token (always valid) and masked where they are used
+  const int64_t cbase = (int64_t(t0) * a.H + h) * kD;
+  const int rstride = a.H * kD;
+  const float* gb = a.g + cbase;
+  const char* kb = reinterpret_cast<const char*>(a.k) + cbase * int64_t(sizeof(typename InT::storage));
+  const char* qb = reinterpret_cast<const char*>(a.q) + cbase * int64_t(sizeof(typename InT::storage));
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 4 * tg + i;
-    const int rr = r < n ? r : n - 1;  // clamped: always a valid token; zeroed when used
-    const int64_t base = (int64_t(t0 + rr) * H + h) * kD + c0;
-    in.g[i] = ld_f4(a.g + base);
-    in.k[i] = InT::load4raw(a.k, base);
-    in.q[i] = InT::load4raw(a.q, base);
+    const int off = (r < n ? r : n - 1) * rstride + c0;
+    in.g[i] = ld_f4(gb + off);
+    in.k[i] = InT::load4raw(kb, off);
+    in.q[i] = InT::load4raw(qb, off);
   }
-  // unconditional (clamped) so that nothing waits on it before its use
-  const int rr = ptid < n ? ptid : n - 1;
-  in.beta = a.beta[int64_t(t0 + rr) * H + h];
+  in.beta = a.beta[int64_t(t0) * a.H + h + (ptid < n ? ptid : n - 1) * a.H];
 }
 
 // State-wave v at this wave's columns, accumulator layout (rows 16rt+4lq+i).
@@ -141,7 +144,9 @@ struct StateV {
 template <class InT, int JB>
 __device__ __forceinline__ void load_state_v(StateV<InT, JB>& sv, const PrefillArgs& a, int t0, int n, int h, int lq,
                                              int lj, int colw) {
-  const int64_t H = a.H;
+  const char* vb = reinterpret_cast<const char*>(a.v) +
+                   ((int64_t(t0) * a.H + h) * kD + colw) * int64_t(sizeof(typename InT::storage));
+  const int rstride = a.H * kD;
 #pragma unroll
   for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
@@ -149,8 +154,7 @@ __device__ __forceinline__ void load_state_v(StateV<InT, JB>& sv, const PrefillA
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rt + 4 * lq + i;
-        const int rr = r < n ? r : n - 1;
-        sv.v[jb][rt][i] = InT::load1raw(a.v, (int64_t(t0 + rr) * H + h) * kD + colw + 16 * jb + lj);
+        sv.v[jb][rt][i] = InT::load1raw(vb, (r < n ? r : n - 1) * rstride + 16 * jb + lj);
       }
 }
 
@@ -312,6 +316,8 @@ __global__ __launch_bounds__(kThreads) void kda_prefill_kernel(PrefillArgs a) {
             uf[jb] = Pol::make(v8);
           }
           if (want_o) {
+            char* obase = reinterpret_cast<char*>(a.o) +
+                          ((int64_t(ts) * H + h) * kD + colw) * int64_t(sizeof(typename InT::storage));
             Frag fp[2];
   #pragma unroll
             for (int rt = 0; rt < 2; ++rt)
@@ -329,7 +335,7 @@ __global__ __launch_bounds__(kThreads) void kda_prefill_kernel(PrefillArgs a) {
   #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                   const int r = 16 * rt + 4 * lq + e;
-                  if (r < ns) InT::store1(a.o, (int64_t(ts + r) * H + h) * kD + colw + 16 * jb + lj, accO[jb][rt][e]);
+                  if (r < ns) InT::store1(obase, r * int(H * kD) + 16 * jb + lj, accO[jb][rt][e]);
                 }
           }
         }
@@ -376,21 +382,18 @@ __global__ __launch_bounds__(kThreads) void kda_prefill_kernel(PrefillArgs a) {
 
       // ============================== phase A ==============================
       {
-        // decay prefix and rescaled operands of chunk i
+        // decay prefix and rescaled operands of chunk i.  Rows past the chunk end
+        // only need g = 0 (the prefix stops) and beta = 0 (their rows and columns
+        // of A, T' vanish, so their finite k, q, v never reach a kept result).
+        constexpr float kLog2e = 1.4426950408889634f;
         float gq[4][4], kq[4][4], qv[4][4];
   #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const bool ok = 4 * tg + r4 < np;
-          float kk[4], qq[4];
-          InT::unpack4(pin.k[r4], kk);
-          InT::unpack4(pin.q[r4], qq);
-          gq[r4][0] = ok ? pin.g[r4].x : 0.0f; gq[r4][1] = ok ? pin.g[r4].y : 0.0f;
-          gq[r4][2] = ok ? pin.g[r4].z : 0.0f; gq[r4][3] = ok ? pin.g[r4].w : 0.0f;
-  #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            kq[r4][e] = ok ? kk[e] : 0.0f;
-            qv[r4][e] = ok ? qq[e] * a.scale : 0.0f;
-          }
+          const float gm = (4 * tg + r4 < np) ? kLog2e : 0.0f;  // log2-domain prefix
+          InT::unpack4(pin.k[r4], kq[r4]);
+          InT::unpack4(pin.q[r4], qv[r4]);
+          gq[r4][0] = pin.g[r4].x * gm; gq[r4][1] = pin.g[r4].y * gm;
+          gq[r4][2] = pin.g[r4].z * gm; gq[r4][3] = pin.g[r4].w * gm;
         }
         if (ptid < kC) s_beta[ptid] = ptid < np ? pin.beta : 0.0f;
   #pragma unroll
@@ -412,8 +415,8 @@ __global__ __launch_bounds__(kThreads) void kda_prefill_kernel(PrefillArgs a) {
         for (int e = 0; e < 4; ++e) {
           const float y = __shfl_up(incl[e], 1, 8);
           excl[e] = (tg == 0) ? 0.0f : y;
-          blast[e] = __shfl(excl[e] + gq[3][e], 7, 8);  // b at the chunk's last row
-          gam[e] = __expf(blast[e]);
+          blast[e] = __shfl(excl[e] + gq[3][e], 7, 8);  // b at the chunk's last row (log2 domain)
+          gam[e] = __builtin_amdgcn_exp2f(blast[e]);
         }
         float kbv[4][4];
   #pragma unroll
@@ -422,11 +425,11 @@ __global__ __launch_bounds__(kThreads) void kda_prefill_kernel(PrefillArgs a) {
           float kh[4], kc[4], qh[4];
   #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float b = excl[e] + gq[r4][e];
-            const float eb = __expf(b);
+            const float b = excl[e] + gq[r4][e];  // log2 of the cumulative decay
+            const float eb = __builtin_amdgcn_exp2f(b);
             kh[e] = kq[r4][e] * eb;
-            kc[e] = kq[r4][e] * __expf(-b);
-            qh[e] = qv[r4][e] * eb;
+            kc[e] = kq[r4][e] * __builtin_amdgcn_exp2f(-b);
+            qh[e] = (qv[r4][e] * a.scale) * eb;
             kbv[r4][e] = kc[e] * gam[e];  // k e^{b_last - b}
           }
           const int off = r * L::kOpRow + kperm(c0) * E;
@@ -444,14 +447,14 @@ __global__ __launch_bounds__(kThreads) void kda_prefill_kernel(PrefillArgs a) {
   #pragma unroll
           for (int e = 0; e < 4; ++e) g_out[c0 + e] = gam[e];
         }
-      }
-      __syncthreads();
-      // ============================== phase B ==============================
-      {
         {  // fetch chunk i + 1's inputs (clamped; unconditional so nothing waits on them)
           const int tn = bos + (i + 1 < nch ? i + 1 : nch - 1) * kC;
           load_prep<InT>(pin, a, tn, eos - tn < kC ? eos - tn : kC, h, tg, c0, ptid);
         }
+      }
+      __syncthreads();
+      // ============================== phase B ==============================
+      {
         if (pw < 2) {
           // diagonal tile A_II (I = pw), then T_II = (I + A_II)^{-1}
           const int I = pw;
