@@ -255,9 +255,10 @@ def cpu_baseline(target_s=12.0):
     import multiprocessing as mp
     cores = len(os.sched_getaffinity(0))
     cores = max(1, min(cores, 16))
-    # calibrate one round on one core
+    # one round of all 64 requests on one core takes t1; a worker holds 64 / cores requests,
+    # so `rounds` rounds keep each worker busy for about target_s seconds
     t1 = _oracle_decode_worker((2, 0, 64, 1))
-    rounds = max(1, int(round(target_s * cores / max(t1, 1e-3) / cores)))
+    rounds = max(1, int(round(target_s * cores / max(t1, 1e-3))))
     chunks = [(2, 64 * i // cores, 64 * (i + 1) // cores, rounds) for i in range(cores)]
     ctx = mp.get_context("spawn")
     with ctx.Pool(cores) as pool:

@@ -53,7 +53,7 @@ def _chunk_pass(q, k, v, g, beta, S0, C, scale=1.0, pad=True, form="residual"):
     return o, S
 
 
-@pytest.mark.parametrize("C", [16, 64])
+@pytest.mark.parametrize("C", [16, 32, 64])
 @pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 130, 256])
 @pytest.mark.parametrize("form", ["residual", "wy"])
 def test_chunk_form_equals_token_loop(C, T, form):
