@@ -37,9 +37,8 @@ kda_status_t kda_decode_step(const void* q, const void* k, const void* v, const 
   if (!dims_ok(d_k, d_v) || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
   if (N == 0) return KDA_OK;
   if (!q || !k || !v || !g || !beta || !state_pool) return KDA_ERR_INVALID_ARG;
-  const int cols = kda::step_cols_for(int64_t(N) * H);
   return hip_status(kda::launch_decode(q, k, v, g, beta, state_pool, slots, N, H, dtype == KDA_BF16, scale,
-                                       o, cols, static_cast<hipStream_t>(stream)));
+                                       o, static_cast<hipStream_t>(stream)));
 }
 
 kda_status_t kda_verify_commit(const void* k, const void* v, const float* g, const float* beta,
@@ -50,9 +49,8 @@ kda_status_t kda_verify_commit(const void* k, const void* v, const float* g, con
   if (!dims_ok(d_k, d_v) || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
   if (N == 0) return KDA_OK;
   if (!k || !v || !g || !beta || !state_pool || !accepted_len) return KDA_ERR_INVALID_ARG;
-  const int cols = kda::step_cols_for(int64_t(N) * H);
   return hip_status(kda::launch_commit(k, v, g, beta, state_pool, state_pool, slots, accepted_len, N, gamma1,
-                                       H, dtype == KDA_BF16, cols, static_cast<hipStream_t>(stream)));
+                                       H, dtype == KDA_BF16, static_cast<hipStream_t>(stream)));
 }
 
 kda_status_t kda_verify_block(const void* q, const void* k, const void* v, const float* g,
@@ -66,12 +64,11 @@ kda_status_t kda_verify_block(const void* q, const void* k, const void* v, const
   if (!q || !k || !v || !g || !beta || !state_pool || !o) return KDA_ERR_INVALID_ARG;
   if (accepted_len && !state_out_pool) return KDA_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int cols = kda::step_cols_for(int64_t(N) * H);
   hipError_t e = kda::launch_verify(q, k, v, g, beta, state_pool, slots, N, gamma1, H, dtype == KDA_BF16,
-                                    scale, o, cols, s);
+                                    scale, o, s);
   if (e != hipSuccess || !accepted_len) return hip_status(e);
   return hip_status(kda::launch_commit(k, v, g, beta, state_pool, state_out_pool, slots, accepted_len, N,
-                                       gamma1, H, dtype == KDA_BF16, cols, s));
+                                       gamma1, H, dtype == KDA_BF16, s));
 }
 
 kda_status_t kda_prefill(const void* q, const void* k, const void* v, const float* g,

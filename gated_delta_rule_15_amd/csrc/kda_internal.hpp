@@ -7,20 +7,17 @@
 namespace kda {
 
 // ---- decode / verify / commit (kda_step.hip) ------------------------------
-int step_cols_for(int64_t tiles);
-
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* g, const float* beta,
                          float* state, const int32_t* slots, int N, int H, bool bf16, float scale,
-                         void* o, int cols, hipStream_t stream);
+                         void* o, hipStream_t stream);
 
 hipError_t launch_verify(const void* q, const void* k, const void* v, const float* g, const float* beta,
                          const float* state, const int32_t* slots, int N, int G, int H, bool bf16,
-                         float scale, void* o, int cols, hipStream_t stream);
+                         float scale, void* o, hipStream_t stream);
 
 hipError_t launch_commit(const void* k, const void* v, const float* g, const float* beta,
                          const float* state_in, float* state_out, const int32_t* slots,
-                         const int32_t* accepted_len, int N, int G, int H, bool bf16, int cols,
-                         hipStream_t stream);
+                         const int32_t* accepted_len, int N, int G, int H, bool bf16, hipStream_t stream);
 
 // ---- segment composition (kda_compose.hip) --------------------------------
 hipError_t launch_compose(const float* M, const float* S_tilde, const float* S_in0, float* S_in,

@@ -9,15 +9,26 @@
 // only the accepted prefix from that state in place ("SGLang 和 Miles 为 Kimi K3
 // 提供首日支持", section "ReplaySSM：针对 KDA 状态的原始输入重放").
 //
-// These kernels are HBM streams of the fp32 state: a workgroup owns one
-// (request, head, column slice) tile of 128 rows x COLS columns in registers;
-// the column reductions r = S~^T k and s = S~^T q run in-thread over the
-// thread's rows, then across lanes with wave shuffles, then across the four
-// waves through 1.2 KB of LDS in a fixed order.  Decode, verify and commit call
-// the same per-token routine with the same decomposition and no atomics, so a
-// commit of L tokens is bit-identical to L decode steps and verify's o_t is
-// bit-identical to the t-th of t decode steps.  This file is built with
-// -ffp-contract=off and every multiply-add is an explicit fmaf.
+// These kernels are HBM streams of the fp32 state.  A workgroup of four waves
+// owns one (request, head, 64-column half) of the 128 x 128 state in
+// registers: waves 2s and 2s+1 hold column slice s (32 columns), rows 0..63
+// and 64..127; lane = 8 * rg + cg holds 8 rows (8rg .. 8rg+7 of its wave's
+// half) and columns 4cg .. 4cg+3 of the slice, so one load instruction of a
+// wave covers eight full 128-byte row segments.  The column sums r = S~^T k,
+// s = S~^T q and q . k run in-thread over 8 rows, then across the wave's 8 row
+// groups in registers (a DPP row rotation by 8 lanes and the 16- and 32-lane
+// permute-swaps, each a butterfly whose two partners add the same two values),
+// then across the slice's two waves through one float2 LDS read per value,
+// summed in wave order.  Every lane of a column ends with the same sums.
+//
+// Per-token inputs: decode loads them straight from memory; verify and commit
+// stage blocks of 8 tokens in LDS (k, scale * q and alpha = exp(g) as fp32,
+// v of the slice, beta) once per workgroup, so the dependent steps never wait
+// on memory.  Both paths produce the same fp32 values (same conversions, same
+// exp), every step runs the same code, the file is built with
+// -ffp-contract=off with explicit fmaf, and nothing is atomic: a commit of L
+// tokens is bit-identical to L decode steps, and verify's o_t to the t-th of t
+// decode steps.
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
@@ -25,16 +36,13 @@ namespace kda {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
-
-template <int COLS>
-struct TileMap {
-  static constexpr int CG = COLS / 4;     // column groups of 4 columns
-  static constexpr int RG = kThreads / CG; // row groups
-  static constexpr int R = kD / RG;       // rows per thread
-  static_assert(CG <= 64 && 64 % CG == 0, "column groups must tile a wave");
-  static_assert(R % 4 == 0, "rows per thread must be a multiple of 4");
-};
+constexpr int kSliceCols = 32;               // columns of one slice (8 column groups of 4)
+constexpr int kWgCols = 64;                  // columns per workgroup: two slices
+constexpr int kWgPerHead = kD / kWgCols;     // workgroups per (request, head)
+constexpr int kCG = 8;                       // column groups per slice
+constexpr int kR = 8;                        // rows per lane
+constexpr int kRowsPerWave = 8 * kR;         // 64: two waves per slice
+constexpr int kBlockT = 8;                   // tokens staged per block (verify / commit)
 
 enum StepMode { kDecode = 0, kVerify = 1, kCommit = 2 };
 
@@ -53,198 +61,293 @@ struct StepArgs {
   float scale;
 };
 
-// Per-thread partial sums -> full column sums, identical in every thread that
-// shares a column group.  red: LDS [kWaves][CG][NV].
-template <int COLS, int NV>
-__device__ __forceinline__ void reduce_columns(float (&x)[NV], float* red, int lane, int wave, int cg) {
-  using M = TileMap<COLS>;
-#pragma unroll
-  for (int off = M::CG; off < 64; off <<= 1) {
-#pragma unroll
-    for (int e = 0; e < NV; ++e) x[e] += __shfl_xor(x[e], off, 64);
-  }
-  if (lane < M::CG) {
-#pragma unroll
-    for (int e = 0; e < NV; ++e) red[(wave * M::CG + cg) * NV + e] = x[e];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int e = 0; e < NV; ++e) {
-    float acc = red[(0 * M::CG + cg) * NV + e];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) acc += red[(w * M::CG + cg) * NV + e];
-    x[e] = acc;
-  }
+// One token's inputs at this lane's 8 rows and 4 columns, as fp32.
+struct TokenVals {
+  float k[kR], qs[kR], alpha[kR], v[4];
+  float beta;
+};
+
+// Staged inputs of up to kBlockT tokens (verify / commit).
+struct __align__(16) Stage {
+  float k[kBlockT][kD];
+  float qs[kBlockT][kD];     // scale * q
+  float alpha[kBlockT][kD];  // exp(g)
+  float v[kBlockT][kWgCols]; // this workgroup's columns
+  float beta[kBlockT];
+};
+
+// Cross-wave partial sums: [buffer][slice][column group][value][wave of the slice].
+struct __align__(16) Red {
+  float x[2][2][kCG][9][2];
+};
+
+// Sum over the 8 row groups of a wave (lane bits 3..5).
+__device__ __forceinline__ float rowgroup_sum(float x) {
+  x = x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));  // row_ror:8
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);  // rows 2m and 2m+1 of 16 lanes
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);  // lanes 0..31 and 32..63
 }
 
-// One token.  S: this thread's R x 4 state block (rows row0.., columns col..col+3).
-// kk/qq/gg: the token's k, scale*q, g at this thread's rows; vv: v at its columns.
-// READOUT additionally produces o at the thread's 4 columns.
-template <int COLS, bool READOUT>
-__device__ __forceinline__ void token_step(float (&S)[TileMap<COLS>::R][4],
-                                           const float (&kk)[TileMap<COLS>::R],
-                                           const float (&qq)[TileMap<COLS>::R],
-                                           const float (&gg)[TileMap<COLS>::R], const float (&vv)[4],
-                                           float beta, float* red, int lane, int wave, int cg,
-                                           float (&o)[4]) {
-  using M = TileMap<COLS>;
+template <class InT, bool READOUT>
+__device__ __forceinline__ void load_token(TokenVals& x, const StepArgs& a, int n, int t, int h, int row0, int col) {
+  const int64_t tok = (int64_t(n) * a.G + t) * a.H + h;  // [N, G, H] token-head index
+  const int64_t vec = tok * kD;
+#pragma unroll
+  for (int i = 0; i < kR; i += 4) {
+    InT::unpack4(InT::load4raw(a.k, vec + row0 + i), &x.k[i]);
+    const float4 g = ld_f4(a.g + vec + row0 + i);
+    x.alpha[i] = __expf(g.x); x.alpha[i + 1] = __expf(g.y); x.alpha[i + 2] = __expf(g.z); x.alpha[i + 3] = __expf(g.w);
+    if constexpr (READOUT) {
+      float q[4];
+      InT::unpack4(InT::load4raw(a.q, vec + row0 + i), q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x.qs[i + e] = q[e] * a.scale;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x.qs[i + e] = 0.0f;
+    }
+  }
+  InT::unpack4(InT::load4raw(a.v, vec + col), x.v);
+  x.beta = a.beta[tok];
+}
+
+__device__ __forceinline__ void read_token(TokenVals& x, const Stage& st, int t, int row0, int wcol, bool readout) {
+#pragma unroll
+  for (int i = 0; i < kR; i += 4) {
+    const float4 k = *reinterpret_cast<const float4*>(&st.k[t][row0 + i]);
+    const float4 al = *reinterpret_cast<const float4*>(&st.alpha[t][row0 + i]);
+    x.k[i] = k.x; x.k[i + 1] = k.y; x.k[i + 2] = k.z; x.k[i + 3] = k.w;
+    x.alpha[i] = al.x; x.alpha[i + 1] = al.y; x.alpha[i + 2] = al.z; x.alpha[i + 3] = al.w;
+    if (readout) {
+      const float4 q = *reinterpret_cast<const float4*>(&st.qs[t][row0 + i]);
+      x.qs[i] = q.x; x.qs[i + 1] = q.y; x.qs[i + 2] = q.z; x.qs[i + 3] = q.w;
+    } else {
+      x.qs[i] = x.qs[i + 1] = x.qs[i + 2] = x.qs[i + 3] = 0.0f;
+    }
+  }
+  const float4 v = *reinterpret_cast<const float4*>(&st.v[t][wcol]);
+  x.v[0] = v.x; x.v[1] = v.y; x.v[2] = v.z; x.v[3] = v.w;
+  x.beta = st.beta[t];
+}
+
+// Stage tokens b0 .. b0 + kBlockT - 1 (indices past `last` repeat `last`).
+// Thread tid owns channel group tid % 32 of token tid / 32 for k, q and g, and
+// (threads 0..127) column group tid % 16 of token tid / 16 for v: every load
+// is issued before the first LDS store.
+template <class InT, bool READOUT>
+__device__ __forceinline__ void stage_block(Stage& st, const StepArgs& a, int n, int h, int col0, int b0, int last,
+                                            int tid) {
+  static_assert(kBlockT * 32 == kThreads, "one 4-channel group of one token per thread");
+  const int t = tid >> 5, c4 = 4 * (tid & 31);
+  const int tt = b0 + t <= last ? b0 + t : last;
+  const int64_t vec = ((int64_t(n) * a.G + tt) * a.H + h) * kD;
+  const auto kr = InT::load4raw(a.k, vec + c4);
+  const float4 g = ld_f4(a.g + vec + c4);
+  typename InT::raw4 qr{};
+  if constexpr (READOUT) qr = InT::load4raw(a.q, vec + c4);
+  constexpr int kVPieces = kWgCols / 4;  // 16 per token
+  const int tv = tid / kVPieces, cv = 4 * (tid % kVPieces);
+  const int ttv = b0 + tv <= last ? b0 + tv : last;
+  typename InT::raw4 vr{};
+  if (tid < kBlockT * kVPieces) vr = InT::load4raw(a.v, ((int64_t(n) * a.G + ttv) * a.H + h) * kD + col0 + cv);
+  float beta = 0.0f;
+  if (tid < kBlockT) beta = a.beta[(int64_t(n) * a.G + (b0 + tid <= last ? b0 + tid : last)) * a.H + h];
+
+  float f[4];
+  InT::unpack4(kr, f);
+  *reinterpret_cast<float4*>(&st.k[t][c4]) = make_float4(f[0], f[1], f[2], f[3]);
+  if constexpr (READOUT) {
+    InT::unpack4(qr, f);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[e] = f[e] * a.scale;
+  } else {
+    f[0] = f[1] = f[2] = f[3] = 0.0f;
+  }
+  *reinterpret_cast<float4*>(&st.qs[t][c4]) = make_float4(f[0], f[1], f[2], f[3]);
+  *reinterpret_cast<float4*>(&st.alpha[t][c4]) = make_float4(__expf(g.x), __expf(g.y), __expf(g.z), __expf(g.w));
+  if (tid < kBlockT * kVPieces) {
+    InT::unpack4(vr, f);
+    *reinterpret_cast<float4*>(&st.v[tv][cv]) = make_float4(f[0], f[1], f[2], f[3]);
+  }
+  if (tid < kBlockT) st.beta[tid] = beta;
+}
+
+// One token on this lane's 8 x 4 block of S.  red: this slice's [cg][value][2]
+// partials in the current buffer; ws: the wave's index within its slice.
+// Returns o at the lane's 4 columns when READOUT.
+template <bool READOUT>
+__device__ __forceinline__ void token_step(float (&S)[kR][4], const TokenVals& x, float (*red)[9][2], int lane,
+                                           int ws, int cg, float (&o)[4]) {
   constexpr int NV = READOUT ? 9 : 4;
   float acc[NV];
 #pragma unroll
   for (int e = 0; e < NV; ++e) acc[e] = 0.0f;
 #pragma unroll
-  for (int i = 0; i < M::R; ++i) {
-    const float alpha = __expf(gg[i]);
+  for (int i = 0; i < kR; ++i) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      S[i][j] = S[i][j] * alpha;                       // S~ = Diag(alpha) S (row scale)
-      acc[j] = fmaf(kk[i], S[i][j], acc[j]);           // r = S~^T k
-      if constexpr (READOUT) acc[4 + j] = fmaf(qq[i], S[i][j], acc[4 + j]);  // s = S~^T q
+      S[i][j] = S[i][j] * x.alpha[i];                                        // S~ = Diag(alpha) S
+      acc[j] = fmaf(x.k[i], S[i][j], acc[j]);                                // r = S~^T k
+      if constexpr (READOUT) acc[4 + j] = fmaf(x.qs[i], S[i][j], acc[4 + j]);  // s = S~^T q
     }
-    if constexpr (READOUT) acc[8] = fmaf(qq[i], kk[i], acc[8]);              // q . k
+    if constexpr (READOUT) acc[8] = fmaf(x.qs[i], x.k[i], acc[8]);           // q . k
   }
-  reduce_columns<COLS, NV>(acc, red, lane, wave, cg);
+#pragma unroll
+  for (int e = 0; e < NV; ++e) acc[e] = rowgroup_sum(acc[e]);
+  if (lane < kCG) {
+#pragma unroll
+    for (int e = 0; e < NV; ++e) red[cg][e][ws] = acc[e];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < NV; ++e) {
+    const float2 w = *reinterpret_cast<const float2*>(&red[cg][e][0]);
+    acc[e] = w.x + w.y;
+  }
   float u[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) u[j] = beta * (vv[j] - acc[j]);
+  for (int j = 0; j < 4; ++j) u[j] = x.beta * (x.v[j] - acc[j]);
 #pragma unroll
-  for (int i = 0; i < M::R; ++i) {
+  for (int i = 0; i < kR; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) S[i][j] = fmaf(kk[i], u[j], S[i][j]);  // S = S~ + k u^T
+    for (int j = 0; j < 4; ++j) S[i][j] = fmaf(x.k[i], u[j], S[i][j]);     // S = S~ + k u^T
   }
   if constexpr (READOUT) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = fmaf(acc[8], u[j], acc[4 + j]);  // o = s + (q.k) u
+    for (int j = 0; j < 4; ++j) o[j] = fmaf(acc[8], u[j], acc[4 + j]);     // o = s + (q.k) u
   }
 }
 
-template <int COLS, class InT, int MODE>
+template <bool NT>
+__device__ __forceinline__ float4 ld_state(const float* p) {
+  if constexpr (NT) {
+    return make_float4(__builtin_nontemporal_load(p), __builtin_nontemporal_load(p + 1),
+                       __builtin_nontemporal_load(p + 2), __builtin_nontemporal_load(p + 3));
+  } else {
+    return ld_f4(p);
+  }
+}
+
+template <bool NT>
+__device__ __forceinline__ void st_state(float* p, const float (&s)[4]) {
+  if constexpr (NT) {
+    __builtin_nontemporal_store(s[0], p);
+    __builtin_nontemporal_store(s[1], p + 1);
+    __builtin_nontemporal_store(s[2], p + 2);
+    __builtin_nontemporal_store(s[3], p + 3);
+  } else {
+    st_f4(p, make_float4(s[0], s[1], s[2], s[3]));
+  }
+}
+
+template <class InT, int MODE>
 __global__ __launch_bounds__(kThreads) void kda_step_kernel(StepArgs a) {
-  using M = TileMap<COLS>;
-  constexpr int NS = kD / COLS;
   constexpr bool READOUT = (MODE != kCommit);
-  __shared__ float red[2][kWaves * M::CG * 9];
+  constexpr bool NT = (MODE == kDecode);  // the decode state is streamed once per call
+  __shared__ Red red;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int cg = tid % M::CG;
-  const int rg = tid / M::CG;
-  const int row0 = rg * M::R;
+  const int ws = wave & 1;        // wave within its slice: rows 64 ws ..
+  const int sl = wave >> 1;       // slice within the workgroup
+  const int cg = lane % kCG;
+  const int rg = lane / kCG;
+  const int row0 = ws * kRowsPerWave + rg * kR;
 
-  const int slice = blockIdx.x % NS;
-  const int nh = blockIdx.x / NS;
+  const int half = blockIdx.x % kWgPerHead;
+  const int nh = blockIdx.x / kWgPerHead;
   const int h = nh % a.H;
   const int n = nh / a.H;
-  const int col = slice * COLS + cg * 4;
+  const int col0 = half * kWgCols;               // first column of the workgroup
+  const int wcol = sl * kSliceCols + cg * 4;     // column within the workgroup
+  const int col = col0 + wcol;
 
   int steps = a.G;
   if (MODE == kCommit) {
     const int L = a.accepted_len[n];
     steps = L < 0 ? 0 : (L > a.G ? a.G : L);
-  }
-  if (MODE == kDecode && a.o == nullptr) {
-    // decode without readout still follows the same arithmetic for the state
+    if (steps == 0 && a.state_out == a.state_in) return;  // nothing accepted, in place: nothing to do
   }
   const int64_t pool_row = a.slots ? int64_t(a.slots[n]) : int64_t(n);
   const int64_t tile = (pool_row * a.H + h) * int64_t(kD * kD);
   const float* Sin = a.state_in + tile;
 
-  float S[M::R][4];
+  float S[kR][4];
 #pragma unroll
-  for (int i = 0; i < M::R; ++i) {
-    const float4 w = ld_f4(Sin + (row0 + i) * kD + col);
+  for (int i = 0; i < kR; ++i) {
+    const float4 w = ld_state<NT>(Sin + (row0 + i) * kD + col);
     S[i][0] = w.x; S[i][1] = w.y; S[i][2] = w.z; S[i][3] = w.w;
   }
 
-  for (int t = 0; t < steps; ++t) {
-    const int64_t tok = (int64_t(n) * a.G + t) * a.H + h;  // [N, G, H] token-head index
-    const int64_t vec = tok * kD;
-    float kk[M::R], qq[M::R], gg[M::R], vv[4];
+  float o[4];
+  const bool writer = (ws == 0 && rg == 0 && a.o != nullptr);
+  if constexpr (MODE == kDecode) {
+    TokenVals x;
+    load_token<InT, true>(x, a, n, 0, h, row0, col);
+    token_step<true>(S, x, red.x[0][sl], lane, ws, cg, o);
+    if (writer) InT::store4(a.o, (int64_t(n) * a.H + h) * kD + col, o);
+  } else {
+    __shared__ Stage st;
+    const int last = steps > 0 ? steps - 1 : 0;
+    for (int b0 = 0; b0 < steps; b0 += kBlockT) {
+      if (b0 > 0) __syncthreads();  // every step of the previous block has read the stage
+      stage_block<InT, READOUT>(st, a, n, h, col0, b0, last, tid);
+      __syncthreads();
 #pragma unroll
-    for (int i = 0; i < M::R; i += 4) {
-      InT::load4(a.k, vec + row0 + i, &kk[i]);
-      const float4 w = ld_f4(a.g + vec + row0 + i);
-      gg[i] = w.x; gg[i + 1] = w.y; gg[i + 2] = w.z; gg[i + 3] = w.w;
-      if constexpr (READOUT) {
-        InT::load4(a.q, vec + row0 + i, &qq[i]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) qq[i + e] = qq[i + e] * a.scale;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) qq[i + e] = 0.0f;
+      for (int t = 0; t < kBlockT; ++t) {
+        if (b0 + t < steps) {
+          TokenVals x;
+          read_token(x, st, t, row0, wcol, READOUT);
+          token_step<READOUT>(S, x, red.x[(b0 + t) & 1][sl], lane, ws, cg, o);
+          if constexpr (READOUT) {
+            if (writer) InT::store4(a.o, ((int64_t(n) * a.G + b0 + t) * a.H + h) * kD + col, o);
+          }
+        }
       }
-    }
-    InT::load4(a.v, vec + col, vv);
-    const float beta = a.beta[tok];
-    float o[4];
-    token_step<COLS, READOUT>(S, kk, qq, gg, vv, beta, red[t & 1], lane, wave, cg, o);
-    if constexpr (READOUT) {
-      if (rg == 0 && a.o != nullptr) InT::store4(a.o, vec + col, o);
     }
   }
 
   if constexpr (MODE != kVerify) {
     float* Sout = a.state_out + tile;
 #pragma unroll
-    for (int i = 0; i < M::R; ++i)
-      st_f4(Sout + (row0 + i) * kD + col, make_float4(S[i][0], S[i][1], S[i][2], S[i][3]));
-  }
-}
-
-template <int COLS, class InT, int MODE>
-hipError_t launch_cols(const StepArgs& a, hipStream_t stream) {
-  constexpr int NS = kD / COLS;
-  const int64_t blocks = int64_t(a.N) * a.H * NS;
-  hipLaunchKernelGGL((kda_step_kernel<COLS, InT, MODE>), dim3(unsigned(blocks)), dim3(kThreads), 0,
-                     stream, a);
-  return hipGetLastError();
-}
-
-template <class InT, int MODE>
-hipError_t launch_mode(const StepArgs& a, int cols, hipStream_t stream) {
-  switch (cols) {
-    case 128: return launch_cols<128, InT, MODE>(a, stream);
-    case 64: return launch_cols<64, InT, MODE>(a, stream);
-    default: return launch_cols<32, InT, MODE>(a, stream);
+    for (int i = 0; i < kR; ++i) st_state<NT>(Sout + (row0 + i) * kD + col, S[i]);
   }
 }
 
 template <int MODE>
-hipError_t launch_step(const StepArgs& a, bool bf16, int cols, hipStream_t stream) {
-  return bf16 ? launch_mode<BF16, MODE>(a, cols, stream) : launch_mode<F32, MODE>(a, cols, stream);
+hipError_t launch_step(const StepArgs& a, bool bf16, hipStream_t stream) {
+  const int64_t blocks = int64_t(a.N) * a.H * kWgPerHead;
+  if (bf16)
+    hipLaunchKernelGGL((kda_step_kernel<BF16, MODE>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((kda_step_kernel<F32, MODE>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace
 
-// Column-slice width per workgroup: narrow enough that the grid has >= ~2048
-// workgroups (8 per CU) so that every CU has several tiles in flight.
-int step_cols_for(int64_t tiles) {
-  if (tiles * 1 >= 2048) return 128;
-  if (tiles * 2 >= 2048) return 64;
-  return 32;
-}
-
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                         float* state, const int32_t* slots, int N, int H, bool bf16, float scale,
-                         void* o, int cols, hipStream_t stream) {
+                         float* state, const int32_t* slots, int N, int H, bool bf16, float scale, void* o,
+                         hipStream_t stream) {
   StepArgs a{q, k, v, g, beta, state, state, slots, nullptr, o, N, 1, H, scale};
-  return launch_step<kDecode>(a, bf16, cols, stream);
+  return launch_step<kDecode>(a, bf16, stream);
 }
 
 hipError_t launch_verify(const void* q, const void* k, const void* v, const float* g, const float* beta,
                          const float* state, const int32_t* slots, int N, int G, int H, bool bf16,
-                         float scale, void* o, int cols, hipStream_t stream) {
+                         float scale, void* o, hipStream_t stream) {
   StepArgs a{q, k, v, g, beta, state, nullptr, slots, nullptr, o, N, G, H, scale};
-  return launch_step<kVerify>(a, bf16, cols, stream);
+  return launch_step<kVerify>(a, bf16, stream);
 }
 
 hipError_t launch_commit(const void* k, const void* v, const float* g, const float* beta,
                          const float* state_in, float* state_out, const int32_t* slots,
-                         const int32_t* accepted_len, int N, int G, int H, bool bf16, int cols,
-                         hipStream_t stream) {
+                         const int32_t* accepted_len, int N, int G, int H, bool bf16, hipStream_t stream) {
   StepArgs a{nullptr, k, v, g, beta, state_in, state_out, slots, accepted_len, nullptr, N, G, H, 1.0f};
-  return launch_step<kCommit>(a, bf16, cols, stream);
+  return launch_step<kCommit>(a, bf16, stream);
 }
 
 }  // namespace kda
