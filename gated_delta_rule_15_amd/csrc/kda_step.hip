@@ -35,14 +35,20 @@
 namespace kda {
 namespace {
 
+#ifndef KDA_STEP_ROWS_PER_LANE
+#define KDA_STEP_ROWS_PER_LANE 8
+#endif
 constexpr int kThreads = 256;
-constexpr int kSliceCols = 32;               // columns of one slice (8 column groups of 4)
-constexpr int kWgCols = 64;                  // columns per workgroup: two slices
-constexpr int kWgPerHead = kD / kWgCols;     // workgroups per (request, head)
-constexpr int kCG = 8;                       // column groups per slice
-constexpr int kR = 8;                        // rows per lane
-constexpr int kRowsPerWave = 8 * kR;         // 64: two waves per slice
-constexpr int kBlockT = 8;                   // tokens staged per block (verify / commit)
+constexpr int kSliceCols = 32;                      // columns of one slice (8 column groups of 4)
+constexpr int kCG = 8;                              // column groups per slice
+constexpr int kR = KDA_STEP_ROWS_PER_LANE;          // rows per lane (8 or 16)
+constexpr int kRowsPerWave = 8 * kR;                // 8 row groups per wave
+constexpr int kWavesPerSlice = kD / kRowsPerWave;   // 2 (kR = 8) or 1 (kR = 16)
+constexpr int kSlicesPerWg = (kThreads / 64) / kWavesPerSlice;
+constexpr int kWgCols = kSliceCols * kSlicesPerWg;  // columns per workgroup
+constexpr int kWgPerHead = kD / kWgCols;            // workgroups per (request, head)
+constexpr int kBlockT = 8;                          // tokens staged per block (verify / commit)
+static_assert(kR == 8 || kR == 16, "rows per lane");
 
 enum StepMode { kDecode = 0, kVerify = 1, kCommit = 2 };
 
@@ -78,7 +84,7 @@ struct __align__(16) Stage {
 
 // Cross-wave partial sums: [buffer][slice][column group][value][wave of the slice].
 struct __align__(16) Red {
-  float x[2][2][kCG][9][2];
+  float x[2][kSlicesPerWg][kCG][9][kWavesPerSlice];
 };
 
 // Sum over the 8 row groups of a wave (lane bits 3..5).
@@ -147,7 +153,7 @@ __device__ __forceinline__ void stage_block(Stage& st, const StepArgs& a, int n,
   const float4 g = ld_f4(a.g + vec + c4);
   typename InT::raw4 qr{};
   if constexpr (READOUT) qr = InT::load4raw(a.q, vec + c4);
-  constexpr int kVPieces = kWgCols / 4;  // 16 per token
+  constexpr int kVPieces = kWgCols / 4;  // v pieces per token
   const int tv = tid / kVPieces, cv = 4 * (tid % kVPieces);
   const int ttv = b0 + tv <= last ? b0 + tv : last;
   typename InT::raw4 vr{};
@@ -178,7 +184,7 @@ __device__ __forceinline__ void stage_block(Stage& st, const StepArgs& a, int n,
 // partials in the current buffer; ws: the wave's index within its slice.
 // Returns o at the lane's 4 columns when READOUT.
 template <bool READOUT>
-__device__ __forceinline__ void token_step(float (&S)[kR][4], const TokenVals& x, float (*red)[9][2], int lane,
+__device__ __forceinline__ void token_step(float (&S)[kR][4], const TokenVals& x, float (*red)[9][kWavesPerSlice], int lane,
                                            int ws, int cg, float (&o)[4]) {
   constexpr int NV = READOUT ? 9 : 4;
   float acc[NV];
@@ -196,15 +202,17 @@ __device__ __forceinline__ void token_step(float (&S)[kR][4], const TokenVals& x
   }
 #pragma unroll
   for (int e = 0; e < NV; ++e) acc[e] = rowgroup_sum(acc[e]);
-  if (lane < kCG) {
+  if constexpr (kWavesPerSlice == 2) {
+    if (lane < kCG) {
 #pragma unroll
-    for (int e = 0; e < NV; ++e) red[cg][e][ws] = acc[e];
-  }
-  __syncthreads();
+      for (int e = 0; e < NV; ++e) red[cg][e][ws] = acc[e];
+    }
+    __syncthreads();
 #pragma unroll
-  for (int e = 0; e < NV; ++e) {
-    const float2 w = *reinterpret_cast<const float2*>(&red[cg][e][0]);
-    acc[e] = w.x + w.y;
+    for (int e = 0; e < NV; ++e) {
+      const float2 w = *reinterpret_cast<const float2*>(&red[cg][e][0]);
+      acc[e] = w.x + w.y;
+    }
   }
   float u[4];
 #pragma unroll
@@ -251,8 +259,8 @@ __global__ __launch_bounds__(kThreads) void kda_step_kernel(StepArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int ws = wave & 1;        // wave within its slice: rows 64 ws ..
-  const int sl = wave >> 1;       // slice within the workgroup
+  const int ws = wave % kWavesPerSlice;  // wave within its slice: rows kRowsPerWave * ws ..
+  const int sl = wave / kWavesPerSlice;  // slice within the workgroup
   const int cg = lane % kCG;
   const int rg = lane / kCG;
   const int row0 = ws * kRowsPerWave + rg * kR;
