@@ -45,8 +45,10 @@ namespace kda {
 namespace {
 
 constexpr int kC = 32;           // chunk length (tokens)
-constexpr int kThreads = 512;    // 8 waves
-constexpr int kStateWaves = 4;
+
+// SW state waves + PW prep waves (PW = 4: 4 tokens x 4 channels per prep
+// thread; PW = 8: 2 tokens x 4 channels).
+__host__ __device__ constexpr int prefill_threads(int sw, int pw) { return 64 * (sw + pw); }
 
 template <class Pol>
 struct Lds {
@@ -89,6 +91,16 @@ struct Lds {
   static_assert(kNatRow % 8 == 0 && (E == 2 || kNatRow % 16 == 0), "aligned natural rows");
 };
 
+// x from lane (lane - D) of the same G-lane group, 0 for the first D lanes of
+// the group (G = 8 or 16; groups start at multiples of G).  A DPP row shift
+// (16 lanes) moves values across the 8-lane groups of a row; those are zeroed.
+template <int D, int G>
+__device__ __forceinline__ float dpp_shr_in_group(float x, int idx_in_group) {
+  const float y = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + D, 0xF, 0xF, false));
+  if constexpr (G == 16) return y;
+  else return idx_in_group >= D ? y : 0.0f;
+}
+
 struct PrefillArgs {
   const void* q;
   const void* k;
@@ -97,7 +109,7 @@ struct PrefillArgs {
   const float* beta;
   const int32_t* cu_seqlens;
   int32_t H;
-  int32_t n_value_slices;  // 128 / (64 * JB)
+  int32_t n_value_slices;  // 128 / (16 * JB * SW)
   int32_t n_slices;        // value slices (+ as many transition slices)
   float scale;
   const float* initial_state;
@@ -106,17 +118,17 @@ struct PrefillArgs {
   float* transition_out;
 };
 
-// Prep-thread inputs of one chunk (4 tokens x 4 channels), as loaded.
-template <class InT>
+// Prep-thread inputs of one chunk (TPT tokens x 4 channels), as loaded.
+template <class InT, int TPT>
 struct PrepIn {
-  float4 g[4];
-  typename InT::raw4 k[4], q[4];
+  float4 g[TPT];
+  typename InT::raw4 k[TPT], q[TPT];
   float beta;
 };
 
-template <class InT>
-__device__ __forceinline__ void load_prep(PrepIn<InT>& in, const PrefillArgs& a, int t0, int n, int h, int tg, int c0,
-                                          int ptid) {
+template <class InT, int TPT>
+__device__ __forceinline__ void load_prep(PrepIn<InT, TPT>& in, const PrefillArgs& a, int t0, int n, int h, int tg,
+                                          int c0, int ptid) {
   // wave-uniform chunk base + 32-bit per-lane offsets; rows past the chunk end
   // are clamped to its last token (always valid) and masked where they are used
   const int64_t cbase = (int64_t(t0) * a.H + h) * kD;
@@ -125,8 +137,8 @@ __device__ __forceinline__ void load_prep(PrepIn<InT>& in, const PrefillArgs& a,
   const char* kb = reinterpret_cast<const char*>(a.k) + cbase * int64_t(sizeof(typename InT::storage));
   const char* qb = reinterpret_cast<const char*>(a.q) + cbase * int64_t(sizeof(typename InT::storage));
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 4 * tg + i;
+  for (int i = 0; i < TPT; ++i) {
+    const int r = TPT * tg + i;
     const int off = (r < n ? r : n - 1) * rstride + c0;
     in.g[i] = ld_f4(gb + off);
     in.k[i] = InT::load4raw(kb, off);
@@ -158,8 +170,11 @@ __device__ __forceinline__ void load_state_v(StateV<InT, JB>& sv, const PrefillA
       }
 }
 
-template <class Pol, class InT, int JB>
-__global__ __launch_bounds__(kThreads) void kda_prefill_kernel(PrefillArgs a) {
+template <class Pol, class InT, int SW, int JB, int PW>
+__global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(PrefillArgs a) {
+  static_assert(PW == 4 || PW == 8, "prep waves");
+  constexpr int TPT = 16 / PW;  // tokens per prep thread (4 or 2)
+  constexpr int NTG = kC / TPT; // token groups per channel group (8 or 16 lanes)
   using L = Lds<Pol>;
   using Frag = typename Pol::Frag;
   using Frag16 = typename Pol::Frag16;
@@ -174,7 +189,7 @@ __global__ __launch_bounds__(kThreads) void kda_prefill_kernel(PrefillArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane >> 4;
   const int lj = lane & 15;
-  const bool is_state = wave < kStateWaves;
+  const bool is_state = wave < SW;
 
   const int slice = blockIdx.x % a.n_slices;
   const int sh = blockIdx.x / a.n_slices;
@@ -190,12 +205,13 @@ __global__ __launch_bounds__(kThreads) void kda_prefill_kernel(PrefillArgs a) {
   const bool want_o = !is_transition && a.o != nullptr;
 
   // state-wave roles
-  const int colw = vslice * (64 * JB) + (is_state ? wave : 0) * (16 * JB);
-  // prep-thread roles: 4 consecutive tokens x 4 consecutive channels
-  const int ptid = tid - kStateWaves * 64;
-  const int tg = ptid & 7;
-  const int c0 = (ptid >> 3) * 4;
-  const int pw = wave - kStateWaves;
+  const int colw = vslice * (16 * JB * SW) + (is_state ? wave : 0) * (16 * JB);
+  // prep-thread roles: TPT consecutive tokens x 4 consecutive channels; the
+  // NTG token groups of a channel group are NTG consecutive lanes of a DPP row
+  const int ptid = tid - SW * 64;
+  const int tg = ptid % NTG;
+  const int c0 = (ptid / NTG) * 4;
+  const int pw = wave - SW;
 
   f32x4_t S[JB][8];
   if (is_state) {
@@ -372,8 +388,8 @@ __global__ __launch_bounds__(kThreads) void kda_prefill_kernel(PrefillArgs a) {
       __syncthreads();
     }
   } else {
-    PrepIn<InT> pin;
-    if (nch > 0) load_prep<InT>(pin, a, bos, eos - bos < kC ? eos - bos : kC, h, tg, c0, ptid);
+    PrepIn<InT, TPT> pin;
+    if (nch > 0) load_prep<InT, TPT>(pin, a, bos, eos - bos < kC ? eos - bos : kC, h, tg, c0, ptid);
     for (int i = 0; i < nch; ++i) {
       // this step builds chunk i into operand set i % 2
       const int tp = bos + i * kC;
@@ -386,51 +402,46 @@ __global__ __launch_bounds__(kThreads) void kda_prefill_kernel(PrefillArgs a) {
         // only need g = 0 (the prefix stops) and beta = 0 (their rows and columns
         // of A, T' vanish, so their finite k, q, v never reach a kept result).
         constexpr float kLog2e = 1.4426950408889634f;
-        float gq[4][4], kq[4][4], qv[4][4];
+        float gq[TPT][4], kq[TPT][4], qv[TPT][4];
   #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const float gm = (4 * tg + r4 < np) ? kLog2e : 0.0f;  // log2-domain prefix
-          InT::unpack4(pin.k[r4], kq[r4]);
-          InT::unpack4(pin.q[r4], qv[r4]);
-          gq[r4][0] = pin.g[r4].x * gm; gq[r4][1] = pin.g[r4].y * gm;
-          gq[r4][2] = pin.g[r4].z * gm; gq[r4][3] = pin.g[r4].w * gm;
+        for (int rr = 0; rr < TPT; ++rr) {
+          const float gm = (TPT * tg + rr < np) ? kLog2e : 0.0f;  // log2-domain prefix
+          InT::unpack4(pin.k[rr], kq[rr]);
+          InT::unpack4(pin.q[rr], qv[rr]);
+          gq[rr][0] = pin.g[rr].x * gm; gq[rr][1] = pin.g[rr].y * gm;
+          gq[rr][2] = pin.g[rr].z * gm; gq[rr][3] = pin.g[rr].w * gm;
         }
         if (ptid < kC) s_beta[ptid] = ptid < np ? pin.beta : 0.0f;
   #pragma unroll
-        for (int r4 = 1; r4 < 4; ++r4)
+        for (int rr = 1; rr < TPT; ++rr)
   #pragma unroll
-          for (int e = 0; e < 4; ++e) gq[r4][e] += gq[r4 - 1][e];
-        float incl[4], excl[4], blast[4], gam[4];
-  #pragma unroll
-        for (int e = 0; e < 4; ++e) incl[e] = gq[3][e];
-  #pragma unroll
-        for (int d = 1; d < 8; d <<= 1) {
-  #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float y = __shfl_up(incl[e], d, 8);
-            if (tg >= d) incl[e] += y;
-          }
-        }
+          for (int e = 0; e < 4; ++e) gq[rr][e] += gq[rr - 1][e];
+        // inclusive scan over the NTG token groups (consecutive lanes of one
+        // DPP row); lanes shifted in from outside the group contribute 0
+        float excl[4], gam[4];
   #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float y = __shfl_up(incl[e], 1, 8);
-          excl[e] = (tg == 0) ? 0.0f : y;
-          blast[e] = __shfl(excl[e] + gq[3][e], 7, 8);  // b at the chunk's last row (log2 domain)
-          gam[e] = __builtin_amdgcn_exp2f(blast[e]);
+          float x = gq[TPT - 1][e];
+          x += dpp_shr_in_group<1, NTG>(x, tg);
+          x += dpp_shr_in_group<2, NTG>(x, tg);
+          x += dpp_shr_in_group<4, NTG>(x, tg);
+          if constexpr (NTG == 16) x += dpp_shr_in_group<8, NTG>(x, tg);
+          excl[e] = dpp_shr_in_group<1, NTG>(x, tg);
+          gam[e] = __builtin_amdgcn_exp2f(__shfl(x, NTG - 1, NTG));  // decay over the whole chunk
         }
-        float kbv[4][4];
+        float kbv[TPT][4];
   #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int r = 4 * tg + r4;
+        for (int rr = 0; rr < TPT; ++rr) {
+          const int r = TPT * tg + rr;
           float kh[4], kc[4], qh[4];
   #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float b = excl[e] + gq[r4][e];  // log2 of the cumulative decay
+            const float b = excl[e] + gq[rr][e];  // log2 of the cumulative decay
             const float eb = __builtin_amdgcn_exp2f(b);
-            kh[e] = kq[r4][e] * eb;
-            kc[e] = kq[r4][e] * __builtin_amdgcn_exp2f(-b);
-            qh[e] = (qv[r4][e] * a.scale) * eb;
-            kbv[r4][e] = kc[e] * gam[e];  // k e^{b_last - b}
+            kh[e] = kq[rr][e] * eb;
+            kc[e] = kq[rr][e] * __builtin_amdgcn_exp2f(-b);
+            qh[e] = (qv[rr][e] * a.scale) * eb;
+            kbv[rr][e] = kc[e] * gam[e];  // k e^{b_last - b}
           }
           const int off = r * L::kOpRow + kperm(c0) * E;
           Pol::store4(pset + L::kSetKh, L::kOpPlane, off, kh);
@@ -439,8 +450,13 @@ __global__ __launch_bounds__(kThreads) void kda_prefill_kernel(PrefillArgs a) {
         }
   #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float w4[4] = {kbv[0][e], kbv[1][e], kbv[2][e], kbv[3][e]};
-          Pol::store4(pset + L::kSetKb, L::kKbPlane, (c0 + e) * L::kKbRow + kperm(4 * tg) * E, w4);
+          const int off = (c0 + e) * L::kKbRow + kperm(TPT * tg) * E;
+          if constexpr (TPT == 4) {
+            const float w4[4] = {kbv[0][e], kbv[1][e], kbv[2][e], kbv[3][e]};
+            Pol::store4(pset + L::kSetKb, L::kKbPlane, off, w4);
+          } else {
+            Pol::store2(pset + L::kSetKb, L::kKbPlane, off, kbv[0][e], kbv[1][e]);
+          }
         }
         if (tg == 0) {
           float* g_out = reinterpret_cast<float*>(pset + L::kSetGamma);
@@ -449,7 +465,7 @@ __global__ __launch_bounds__(kThreads) void kda_prefill_kernel(PrefillArgs a) {
         }
         {  // fetch chunk i + 1's inputs (clamped; unconditional so nothing waits on them)
           const int tn = bos + (i + 1 < nch ? i + 1 : nch - 1) * kC;
-          load_prep<InT>(pin, a, tn, eos - tn < kC ? eos - tn : kC, h, tg, c0, ptid);
+          load_prep<InT, TPT>(pin, a, tn, eos - tn < kC ? eos - tn : kC, h, tg, c0, ptid);
         }
       }
       __syncthreads();
@@ -502,36 +518,51 @@ __global__ __launch_bounds__(kThreads) void kda_prefill_kernel(PrefillArgs a) {
   #pragma unroll
             for (int r = 0; r < 16; ++r) Pol::store1(smem + L::kDg, L::kDgPlane, (16 * I + r) * L::kNatRow + lj * E, x[r]);
           }
-        } else {
-          // pw 2: A_10 and P_00;  pw 3: P_10 and P_11
-          const bool w2 = (pw == 2);
-          f32x4_t acc0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, acc1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        } else if (pw < 6) {
+          // the four remaining 16 x 16 tiles, one per wave (PW = 8) or two (PW = 4):
+          //   tile 2: A_10 = Kh[16..31] Kc[0..15]^T (beta-scaled rows)
+          //   tile 3: P_00 = Qh[0..15] Kc[0..15]^T    tile 4: P_10 = Qh[16..31] Kc[0..15]^T
+          //   tile 5: P_11 = Qh[16..31] Kc[16..31]^T, and the zero upper block of P
+          constexpr int NT = (PW == 8) ? 1 : 2;
+          int tile[NT];
+          if constexpr (PW == 8) tile[0] = pw;
+          else { tile[0] = 2 * pw - 2; tile[NT - 1] = 2 * pw - 1; }
+          f32x4_t acc[NT];
+  #pragma unroll
+          for (int u = 0; u < NT; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   #pragma unroll
           for (int ks = 0; ks < 4; ++ks) {
             const int koff = (32 * ks + 8 * lq) * E;
-            // tile 0: w2 ? A_10 = Kh[16..31] Kc[0..15] : P_10 = Qh[16..31] Kc[0..15]
-            // tile 1: w2 ? P_00 = Qh[0..15] Kc[0..15]  : P_11 = Qh[16..31] Kc[16..31]
-            const Frag fa0 = Pol::load(pset + (w2 ? L::kSetKh : L::kSetQh), L::kOpPlane, (16 + lj) * L::kOpRow + koff);
-            const Frag fa1 = Pol::load(pset + L::kSetQh, L::kOpPlane, ((w2 ? 0 : 16) + lj) * L::kOpRow + koff);
-            const Frag fb0 = Pol::load(smem + L::kKc, L::kOpPlane, lj * L::kOpRow + koff);
-            const Frag fb1 = Pol::load(smem + L::kKc, L::kOpPlane, ((w2 ? 0 : 16) + lj) * L::kOpRow + koff);
+            Frag fa[NT], fb[NT];
   #pragma unroll
-            for (int p = 0; p < Pol::kParts; ++p) {
-              Pol::mma_part(acc0, fa0, fb0, p);
-              Pol::mma_part(acc1, fa1, fb1, p);
+            for (int u = 0; u < NT; ++u) {
+              const int arow = (tile[u] == 3) ? 0 : 16;
+              const int brow = (tile[u] == 5) ? 16 : 0;
+              fa[u] = Pol::load(pset + (tile[u] == 2 ? L::kSetKh : L::kSetQh), L::kOpPlane, (arow + lj) * L::kOpRow + koff);
+              fb[u] = Pol::load(smem + L::kKc, L::kOpPlane, (brow + lj) * L::kOpRow + koff);
             }
+  #pragma unroll
+            for (int p = 0; p < Pol::kParts; ++p)
+  #pragma unroll
+              for (int u = 0; u < NT; ++u) Pol::mma_part(acc[u], fa[u], fb[u], p);
           }
+  #pragma unroll
+          for (int u = 0; u < NT; ++u)
   #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * lq + e;  // row within the 16-row tile
-            if (w2) {
+            const int pwt = tile[u];
+            const f32x4_t& accu = acc[u];
+            if (pwt == 2) {
               // A_10 (beta-scaled rows), natural order [r][s] for a 16-deep operand
-              Pol::store1(smem + L::kAop, L::kAopPlane, r * L::kNatRow + lj * E, acc0[e] * s_beta[16 + r]);
-              Pol::store1(pset + L::kSetP, L::kSqPlane, r * L::kSqRow + kperm(lj) * E, (lj <= r) ? acc1[e] : 0.0f);
+              Pol::store1(smem + L::kAop, L::kAopPlane, r * L::kNatRow + lj * E, accu[e] * s_beta[16 + r]);
+            } else if (pwt == 3) {
+              Pol::store1(pset + L::kSetP, L::kSqPlane, r * L::kSqRow + kperm(lj) * E, (lj <= r) ? accu[e] : 0.0f);
+            } else if (pwt == 4) {
+              Pol::store1(pset + L::kSetP, L::kSqPlane, (16 + r) * L::kSqRow + kperm(lj) * E, accu[e]);
             } else {
-              Pol::store1(pset + L::kSetP, L::kSqPlane, (16 + r) * L::kSqRow + kperm(lj) * E, acc0[e]);
               Pol::store1(pset + L::kSetP, L::kSqPlane, (16 + r) * L::kSqRow + kperm(16 + lj) * E,
-                          (lj <= r) ? acc1[e] : 0.0f);
+                          (lj <= r) ? accu[e] : 0.0f);
               Pol::store1(pset + L::kSetP, L::kSqPlane, r * L::kSqRow + kperm(16 + lj) * E, 0.0f);  // upper block
             }
           }
@@ -596,13 +627,13 @@ __global__ __launch_bounds__(kThreads) void kda_prefill_kernel(PrefillArgs a) {
   }
 }
 
-template <class Pol, class InT, int JB>
-hipError_t launch_jb(const PrefillLaunch& p, hipStream_t stream) {
+template <class Pol, class InT, int SW, int JB, int PW>
+hipError_t launch_cfg(const PrefillLaunch& p, hipStream_t stream) {
   PrefillArgs a;
   a.q = p.q; a.k = p.k; a.v = p.v; a.g = p.g; a.beta = p.beta;
   a.cu_seqlens = p.cu_seqlens;
   a.H = p.H;
-  a.n_value_slices = kD / (64 * JB);
+  a.n_value_slices = kD / (16 * JB * SW);
   a.n_slices = a.n_value_slices * (p.transition_out ? 2 : 1);
   a.scale = p.scale;
   a.initial_state = p.initial_state;
@@ -610,19 +641,24 @@ hipError_t launch_jb(const PrefillLaunch& p, hipStream_t stream) {
   a.o = p.o;
   a.transition_out = p.transition_out;
   const int64_t blocks = int64_t(p.num_seqs) * p.H * a.n_slices;
-  hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, JB>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, SW, JB, PW>), dim3(unsigned(blocks)),
+                     dim3(prefill_threads(SW, PW)), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_prefill(const PrefillLaunch& p, bool bf16, hipStream_t stream) {
-  // 128 value columns per workgroup when the grid has enough (sequence, head)
-  // work to fill the chip; otherwise 64 (two workgroups per sequence and head).
+  // Large grids (enough (sequence, head) work to fill the chip): 128 value
+  // columns per workgroup (4 state waves x 32 columns, 4 prep waves), so each
+  // chunk is prepared once per head.  Small grids: 64 value columns per
+  // workgroup (4 state waves x 16 columns) and 8 prep waves, which shortens
+  // the per-chunk critical path at the cost of preparing each chunk twice.
   const int64_t units = int64_t(p.num_seqs) * p.H * (p.transition_out ? 2 : 1);
   const bool wide = units >= 256;
-  if (bf16) return wide ? launch_jb<PolBF16x3, BF16, 2>(p, stream) : launch_jb<PolBF16x3, BF16, 1>(p, stream);
-  return wide ? launch_jb<PolF32, F32, 2>(p, stream) : launch_jb<PolF32, F32, 1>(p, stream);
+  if (bf16)
+    return wide ? launch_cfg<PolBF16x3, BF16, 4, 2, 4>(p, stream) : launch_cfg<PolBF16x3, BF16, 4, 1, 8>(p, stream);
+  return wide ? launch_cfg<PolF32, F32, 4, 2, 4>(p, stream) : launch_cfg<PolF32, F32, 4, 1, 8>(p, stream);
 }
 
 }  // namespace kda
