@@ -266,35 +266,34 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
                 accR[jb][rt][e] = (!is_transition && 16 * rt + 4 * lq + e < ns) ? -InT::unpack1(sv.v[jb][rt][e]) : 0.0f;
               accO[jb][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             }
-          // R = V - Kh S (accumulated as Kh S - V), then O = Qh S
+          // R = V - Kh S (accumulated as Kh S - V) and O = Qh S; each 32-row
+          // block of S is split once and feeds both products
   #pragma unroll
-          for (int pass = 0; pass < 2; ++pass) {
-            if (pass == 1 && !want_o) break;
-            const char* abase = sset + (pass == 0 ? L::kSetKh : L::kSetQh);
+          for (int ks = 0; ks < 4; ++ks) {
+            Frag sf[JB];
   #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-              Frag sf[JB];
-  #pragma unroll
-              for (int jb = 0; jb < JB; ++jb) {
-                const float v8[8] = {S[jb][2 * ks][0], S[jb][2 * ks][1], S[jb][2 * ks][2], S[jb][2 * ks][3],
-                                     S[jb][2 * ks + 1][0], S[jb][2 * ks + 1][1], S[jb][2 * ks + 1][2],
-                                     S[jb][2 * ks + 1][3]};
-                sf[jb] = Pol::make(v8);
-              }
-              const int koff = (32 * ks + 8 * lq) * E;
-              Frag fk[2];
-  #pragma unroll
-              for (int rt = 0; rt < 2; ++rt) fk[rt] = Pol::load(abase, L::kOpPlane, (16 * rt + lj) * L::kOpRow + koff);
-  #pragma unroll
-              for (int p = 0; p < Pol::kParts; ++p)
-  #pragma unroll
-                for (int rt = 0; rt < 2; ++rt)
-  #pragma unroll
-                  for (int jb = 0; jb < JB; ++jb) {
-                    if (pass == 0) Pol::mma_part(accR[jb][rt], fk[rt], sf[jb], p);
-                    else Pol::mma_part(accO[jb][rt], fk[rt], sf[jb], p);
-                  }
+            for (int jb = 0; jb < JB; ++jb) {
+              const float v8[8] = {S[jb][2 * ks][0], S[jb][2 * ks][1], S[jb][2 * ks][2], S[jb][2 * ks][3],
+                                   S[jb][2 * ks + 1][0], S[jb][2 * ks + 1][1], S[jb][2 * ks + 1][2],
+                                   S[jb][2 * ks + 1][3]};
+              sf[jb] = Pol::make(v8);
             }
+            const int koff = (32 * ks + 8 * lq) * E;
+            Frag fk[2], fq[2];
+  #pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+              fk[rt] = Pol::load(sset + L::kSetKh, L::kOpPlane, (16 * rt + lj) * L::kOpRow + koff);
+              if (want_o) fq[rt] = Pol::load(sset + L::kSetQh, L::kOpPlane, (16 * rt + lj) * L::kOpRow + koff);
+            }
+  #pragma unroll
+            for (int p = 0; p < Pol::kParts; ++p)
+  #pragma unroll
+              for (int rt = 0; rt < 2; ++rt)
+  #pragma unroll
+                for (int jb = 0; jb < JB; ++jb) {
+                  Pol::mma_part(accR[jb][rt], fk[rt], sf[jb], p);
+                  if (want_o) Pol::mma_part(accO[jb][rt], fq[rt], sf[jb], p);
+                }
           }
         }
       __syncthreads();
