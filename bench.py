@@ -164,16 +164,8 @@ def bench_verify(reps, warmup, n_sets=8):
                 mean_accepted=float(acc.mean()))
 
 
-def bench_prefill(reps, warmup):
+def _event_time_ms(run, reps, warmup):
     import torch
-    from gated_delta_rule_15_amd import inputs as gen
-    from gated_delta_rule_15_amd import kda
-    p = gen.packed_batch(seed=3, seqlens=[4096], H=12, dtype="bf16")
-    q, k, v = to_dev(p.q, "bf16"), to_dev(p.k, "bf16"), to_dev(p.v, "bf16")
-    g, beta, cu = to_dev(p.g), to_dev(p.beta), to_dev(p.cu_seqlens)
-    o = torch.empty_like(q)
-    S = torch.empty((1, 12, D, D), device="cuda:0")
-    run = lambda: kda.kda_prefill(q, k, v, g, beta, cu, o=o, final_state=S)
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
@@ -184,13 +176,41 @@ def bench_prefill(reps, warmup):
         run()
     end.record()
     end.synchronize()
-    ms = start.elapsed_time(end) / reps
+    return start.elapsed_time(end) / reps
+
+
+def bench_prefill(reps, warmup):
+    """4096 tokens x 12 heads, bf16.  Timed two ways: one kda_prefill launch over the
+    whole sequence, and the segmented driver (automatic segment length: the sequence
+    is cut so that (segment, head) units fill the GPU, then composed); the row's
+    ``ms`` is the faster of the two."""
+    import numpy as np
+    import torch
+    from gated_delta_rule_15_amd import inputs as gen
+    from gated_delta_rule_15_amd import kda
+    from gated_delta_rule_15_amd.long_context import alloc_work, auto_seg_len, kda_prefill_segmented, plan_segments
+    p = gen.packed_batch(seed=3, seqlens=[4096], H=12, dtype="bf16")
+    q, k, v = to_dev(p.q, "bf16"), to_dev(p.k, "bf16"), to_dev(p.v, "bf16")
+    g, beta, cu = to_dev(p.g), to_dev(p.beta), to_dev(p.cu_seqlens)
+    o = torch.empty_like(q)
+    S = torch.empty((1, 12, D, D), device="cuda:0")
+    ms_kernel = _event_time_ms(lambda: kda.kda_prefill(q, k, v, g, beta, cu, o=o, final_state=S), reps, warmup)
+    seg = auto_seg_len(p.cu_seqlens, 12)
+    plan = plan_segments(p.cu_seqlens, seg)
+    work = alloc_work(plan, 12, q.device)
+    o2 = torch.empty_like(q)
+    S2 = torch.empty_like(S)
+    ms_seg = _event_time_ms(lambda: kda_prefill_segmented(q, k, v, g, beta, p.cu_seqlens, o=o2, final_state=S2,
+                                                          plan=plan, work=work), reps, warmup)
+    ms = min(ms_kernel, ms_seg)
     th = 4096 * 12
     flops = th * FLOP_PER_TOKEN_HEAD_PREFILL
     nbytes = th * BYTES_PER_TOKEN_HEAD_PREFILL_BF16 + 12 * STATE_BYTES
     return dict(ms=ms, tokens_per_s=4096 / (ms * 1e-3), algorithmic_tflops=flops / (ms * 1e-3) / 1e12,
                 frac_mfma_peak=flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
-                gbps=nbytes / (ms * 1e-3) / 1e9, frac_hbm_peak=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS)
+                gbps=nbytes / (ms * 1e-3) / 1e9, frac_hbm_peak=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                path="segmented" if ms_seg < ms_kernel else "single launch",
+                single_launch_ms=ms_kernel, segmented_ms=ms_seg, segment_len=seg, segments=plan.n_rows)
 
 
 def bench_long(reps, warmup=1):
@@ -325,7 +345,8 @@ def main():
     if not args.only_decode:
         log("prefill: 4096 tokens x 12 heads ...")
         pf = bench_prefill(reps=max(5, args.steps // 20), warmup=3)
-        log(f"prefill: {pf['ms']:.3f} ms, {pf['tokens_per_s'] / 1e6:.2f} M tokens/s")
+        log(f"prefill: {pf['ms']:.3f} ms, {pf['tokens_per_s'] / 1e6:.2f} M tokens/s ({pf['path']}; single launch "
+            f"{pf['single_launch_ms']:.3f} ms, segmented x{pf['segments']} {pf['segmented_ms']:.3f} ms)")
         rows["prefill_4096x12_bf16"] = pf
         log("verify+commit: 32 requests x 12 heads x 8 drafts ...")
         vf = bench_verify(reps=max(16, args.steps // 2), warmup=args.warmup)

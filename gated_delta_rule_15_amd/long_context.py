@@ -47,6 +47,29 @@ class SegmentPlan:
         return int(self.rows.shape[0] - 1)
 
 
+def auto_seg_len(cu_seqlens_host, H: int, n_cu: int = 256, min_seg: int = 512) -> int:
+    """Segment length for a batch whose (sequence, head) units are too few to fill the GPU.
+
+    A prefill walks each sequence's chunks in order, so a batch of few long
+    sequences leaves most compute units idle.  Cutting every sequence into
+    ``n`` segments gives ``n`` times the units at the cost of the segment
+    passes (transition columns in pass 1, composition, recomputed outputs).
+    The rule aims at about ``n_cu / 4`` (segment, head) units with segments of
+    at least ``min_seg`` tokens; with 4096 tokens x 12 heads it picks
+    704-token segments.  Returns the longest sequence length rounded up to 64
+    (no cut) when the batch already has enough units or is short.
+    """
+    cu = np.asarray(cu_seqlens_host, dtype=np.int64)
+    lens = np.diff(cu)
+    t_max = int(lens.max()) if lens.size else 0
+    units = int((lens > 0).sum()) * H
+    if units == 0:
+        return 64
+    n_seg = max(1, -(-n_cu // (4 * units)))
+    seg = max(min_seg, -(-t_max // n_seg))
+    return ((seg + 63) // 64) * 64
+
+
 def plan_segments(cu_seqlens_host, seg_len: int) -> SegmentPlan:
     if seg_len <= 0 or seg_len % 64:
         raise ValueError("seg_len must be a positive multiple of 64")
@@ -64,19 +87,22 @@ def plan_segments(cu_seqlens_host, seg_len: int) -> SegmentPlan:
     return SegmentPlan(seg_len, np.asarray(rows, dtype=np.int32), row_of_seq, multi)
 
 
-def kda_prefill_segmented(q, k, v, g, beta, cu_seqlens_host, seg_len: int = 65536, initial_state=None,
+def kda_prefill_segmented(q, k, v, g, beta, cu_seqlens_host, seg_len: Optional[int] = 65536, initial_state=None,
                           o=None, final_state=None, scale: float = 1.0, plan: Optional[SegmentPlan] = None,
                           work: Optional[dict] = None):
     """Prefill of a packed ragged batch with long sequences split into segments.
 
     Same arguments and results as ``kda.kda_prefill`` (cu_seqlens_host: CPU
-    int32 [N + 1]); returns (o, final_state).  ``work`` may hold preallocated
-    buffers from ``alloc_work`` so repeated calls allocate nothing.
+    int32 [N + 1]); returns (o, final_state).  ``seg_len=None`` picks it with
+    ``auto_seg_len``.  ``work`` may hold preallocated buffers from
+    ``alloc_work`` so repeated calls allocate nothing.
     """
     dev = q.device
     H = q.shape[1]
     cu_host = torch.as_tensor(np.asarray(cu_seqlens_host, dtype=np.int32))
     N = cu_host.shape[0] - 1
+    if plan is None and seg_len is None:
+        seg_len = auto_seg_len(cu_host.numpy(), H)
     plan = plan or plan_segments(cu_host.numpy(), seg_len)
     work = work or alloc_work(plan, H, dev)
     if o is None:
