@@ -8,16 +8,25 @@
 //
 // Value columns are independent (column j of S_in(i+1) uses only column j of
 // S_in(i) and of S~(i)), so a workgroup owns one (head, 16-column slice) and
-// runs the scan serially over segments; the current slice lives in LDS and
-// each step is a 128 x 128 x 16 fp32 product with fixed summation order.
+// runs the scan serially over segments.  Each step is a 128 x 128 x 16 fp32
+// product on fp32 MFMA (v_mfma_f32_16x16x4_f32, exact products, fp32
+// accumulation): wave w computes output rows 32w .. 32w+31 as two 16 x 16
+// tiles.  The contraction index of lane group q at step s is k = 32q + s, so a
+// lane streams 32 contiguous floats of its M row (global) and of its column
+// of the running state, which is kept transposed in LDS.  Two accumulator
+// chains per tile (even and odd s) halve the dependent MFMA latency; their sum
+// is taken in a fixed order, so results are deterministic.
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
 namespace kda {
 namespace {
 
-constexpr int kCols = 16;           // columns per workgroup
-constexpr int kThreads = 128;       // thread t: row t, all 16 columns
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+constexpr int kCols = 16;            // columns per workgroup
+constexpr int kSlices = kD / kCols;  // workgroups per head
+constexpr int kThreads = 256;        // 4 waves x 32 output rows
 
 __global__ __launch_bounds__(kThreads) void kda_compose_kernel(const float* __restrict__ M,
                                                                const float* __restrict__ S_tilde,
@@ -25,50 +34,74 @@ __global__ __launch_bounds__(kThreads) void kda_compose_kernel(const float* __re
                                                                float* __restrict__ S_in,
                                                                float* __restrict__ S_final, int n_seg,
                                                                int H) {
-  __shared__ float cur[kD][kCols + 1];
-  const int slice = blockIdx.x % (kD / kCols);
-  const int h = blockIdx.x / (kD / kCols);
-  const int r = threadIdx.x;
+  // Workgroups are numbered so that the 8 slices of a head share blockIdx % 8
+  // (one XCD, one L2 for the head's M): id = (h / 8) * 64 + slice * 8 + h % 8.
+  const int id = blockIdx.x;
+  const int slice = (id >> 3) & 7;
+  const int h = (id >> 6) * 8 + (id & 7);
+  if (h >= H) return;
+  __shared__ __align__(16) float curT[kCols][kD + 4];  // running S_in slice, transposed: [column][row]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int q = lane >> 4;   // contraction group / output row group
+  const int n = lane & 15;   // output column within the slice; A-operand row within a tile
   const int c0 = slice * kCols;
   const int64_t tile = int64_t(kD) * kD;
 
-  float s[kCols];
-#pragma unroll
-  for (int j = 0; j < kCols; ++j) s[j] = S_in0 ? S_in0[h * tile + r * kD + c0 + j] : 0.0f;
+  // entry state of segment 0
+  for (int e = tid; e < kD * kCols; e += kThreads) {
+    const int r = e / kCols, c = e % kCols;
+    curT[c][r] = S_in0 ? S_in0[h * tile + int64_t(r) * kD + c0 + c] : 0.0f;
+  }
+  __syncthreads();
 
-  for (int i = 0; i < n_seg; ++i) {
-    const int64_t base = (int64_t(i) * H + h) * tile;
-    float* out = S_in + base + r * kD + c0;
-#pragma unroll
-    for (int j = 0; j < kCols; j += 4) st_f4(out + j, make_float4(s[j], s[j + 1], s[j + 2], s[j + 3]));
-#pragma unroll
-    for (int j = 0; j < kCols; ++j) cur[r][j] = s[j];
-    __syncthreads();
-    float acc[kCols];
-    const float* st = S_tilde + base + r * kD + c0;
-#pragma unroll
-    for (int j = 0; j < kCols; j += 4) {
-      const float4 w = ld_f4(st + j);
-      acc[j] = w.x; acc[j + 1] = w.y; acc[j + 2] = w.z; acc[j + 3] = w.w;
-    }
-    const float* Mrow = M + base + int64_t(r) * kD;
-    for (int c = 0; c < kD; c += 4) {
-      const float4 m = ld_f4(Mrow + c);
-      const float mv[4] = {m.x, m.y, m.z, m.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-#pragma unroll
-        for (int j = 0; j < kCols; ++j) acc[j] = fmaf(mv[e], cur[c + e][j], acc[j]);
+  for (int i = 0; i <= n_seg; ++i) {
+    // publish S_in(i) (S_final for i == n_seg) from LDS
+    float* dst = (i < n_seg) ? S_in + (int64_t(i) * H + h) * tile : S_final ? S_final + h * tile : nullptr;
+    if (dst != nullptr) {
+      for (int e = tid; e < kD * kCols / 4; e += kThreads) {
+        const int r = e / (kCols / 4), c4 = 4 * (e % (kCols / 4));
+        st_f4(dst + int64_t(r) * kD + c0 + c4, make_float4(curT[c4][r], curT[c4 + 1][r], curT[c4 + 2][r], curT[c4 + 3][r]));
       }
     }
+    if (i == n_seg) break;
+    const int64_t base = (int64_t(i) * H + h) * tile;
+    f32x4v acc[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int row = wave * 32 + t * 16 + 4 * q;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[t][0][e] = S_tilde[base + int64_t(row + e) * kD + c0 + n];
+      acc[t][1] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    }
+    // B operand: column n of S_in(i), rows 32q .. 32q+31
+    const float* bcol = &curT[n][32 * q];
+    const float* arow0 = M + base + int64_t(wave * 32 + n) * kD + 32 * q;
+    const float* arow1 = arow0 + 16 * kD;
+#pragma unroll
+    for (int s4 = 0; s4 < 8; ++s4) {
+      const float4 b = *reinterpret_cast<const float4*>(bcol + 4 * s4);
+      const float4 a0 = ld_f4(arow0 + 4 * s4);
+      const float4 a1 = ld_f4(arow1 + 4 * s4);
+      const float bv[4] = {b.x, b.y, b.z, b.w};
+      const float av0[4] = {a0.x, a0.y, a0.z, a0.w};
+      const float av1[4] = {a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[0][e & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av0[e], bv[e], acc[0][e & 1], 0, 0, 0);
+        acc[1][e & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av1[e], bv[e], acc[1][e & 1], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // every wave has read S_in(i) from LDS
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int row = wave * 32 + t * 16 + 4 * q;
+      const f32x4v v = acc[t][0] + acc[t][1];
+      *reinterpret_cast<float4*>(&curT[n][row]) = make_float4(v[0], v[1], v[2], v[3]);
+    }
     __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kCols; ++j) s[j] = acc[j];
-  }
-  if (S_final) {
-    float* out = S_final + h * tile + r * kD + c0;
-#pragma unroll
-    for (int j = 0; j < kCols; j += 4) st_f4(out + j, make_float4(s[j], s[j + 1], s[j + 2], s[j + 3]));
   }
 }
 
@@ -76,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void kda_compose_kernel(const float* __re
 
 hipError_t launch_compose(const float* M, const float* S_tilde, const float* S_in0, float* S_in,
                           float* S_final, int n_seg, int H, hipStream_t stream) {
-  const unsigned blocks = unsigned(H * (kD / kCols));
+  const unsigned blocks = unsigned(((H + 7) / 8) * 64);
   hipLaunchKernelGGL(kda_compose_kernel, dim3(blocks), dim3(kThreads), 0, stream, M, S_tilde, S_in0,
                      S_in, S_final, n_seg, H);
   return hipGetLastError();
