@@ -325,6 +325,66 @@ __global__ __launch_bounds__(kThreads) void kda_step_kernel(StepArgs a) {
   }
 }
 
+#ifndef KDA_DECODE_TILES
+#define KDA_DECODE_TILES 1
+#endif
+// Decode: each workgroup takes kDecodeTiles (request, head, 64-column half)
+// tiles and issues all their loads before the first token step.  One tile per
+// workgroup is fastest on the 64 x 12 step (18.6 us; 2 tiles 19.2 us, 4 tiles
+// 21.2 us: fewer, longer workgroups lose more to the ramp than they gain from
+// overlapping a tile's stores with the next tile's loads).
+constexpr int kDecodeTiles = KDA_DECODE_TILES;
+
+template <class InT>
+__global__ __launch_bounds__(kThreads) void kda_decode_kernel(StepArgs a, int n_tiles) {
+  __shared__ Red red;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int ws = wave % kWavesPerSlice;
+  const int sl = wave / kWavesPerSlice;
+  const int cg = lane % kCG;
+  const int rg = lane / kCG;
+  const int row0 = ws * kRowsPerWave + rg * kR;
+  const int wcol = sl * kSliceCols + cg * 4;
+
+  float S[kDecodeTiles][kR][4];
+  TokenVals x[kDecodeTiles];
+  int64_t toff[kDecodeTiles], ooff[kDecodeTiles];
+  bool valid[kDecodeTiles];
+#pragma unroll
+  for (int j = 0; j < kDecodeTiles; ++j) {
+    const int t = blockIdx.x * kDecodeTiles + j;
+    valid[j] = t < n_tiles;
+    const int tc = valid[j] ? t : blockIdx.x * kDecodeTiles;  // a spare slot repeats the first tile, unstored
+    const int half = tc % kWgPerHead;
+    const int nh = tc / kWgPerHead;
+    const int h = nh % a.H;
+    const int n = nh / a.H;
+    const int col = half * kWgCols + wcol;
+    const int64_t pool_row = a.slots ? int64_t(a.slots[n]) : int64_t(n);
+    toff[j] = (pool_row * a.H + h) * int64_t(kD * kD) + int64_t(row0) * kD + col;
+    ooff[j] = (int64_t(n) * a.H + h) * kD + col;
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+      const float4 w = ld_state<true>(a.state_in + toff[j] + i * kD);
+      S[j][i][0] = w.x; S[j][i][1] = w.y; S[j][i][2] = w.z; S[j][i][3] = w.w;
+    }
+    load_token<InT, true>(x[j], a, n, 0, h, row0, col);
+  }
+  const bool writer = (ws == 0 && rg == 0 && a.o != nullptr);
+#pragma unroll
+  for (int j = 0; j < kDecodeTiles; ++j) {
+    float o[4];
+    token_step<true>(S[j], x[j], red.x[j & 1][sl], lane, ws, cg, o);
+    if (valid[j]) {
+      if (writer) InT::store4(a.o, ooff[j], o);
+#pragma unroll
+      for (int i = 0; i < kR; ++i) st_state<true>(a.state_out + toff[j] + i * kD, S[j][i]);
+    }
+  }
+}
+
 template <int MODE>
 hipError_t launch_step(const StepArgs& a, bool bf16, hipStream_t stream) {
   const int64_t blocks = int64_t(a.N) * a.H * kWgPerHead;
@@ -341,7 +401,13 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const floa
                          float* state, const int32_t* slots, int N, int H, bool bf16, float scale, void* o,
                          hipStream_t stream) {
   StepArgs a{q, k, v, g, beta, state, state, slots, nullptr, o, N, 1, H, scale};
-  return launch_step<kDecode>(a, bf16, stream);
+  const int n_tiles = N * H * kWgPerHead;
+  const unsigned blocks = unsigned((n_tiles + kDecodeTiles - 1) / kDecodeTiles);
+  if (bf16)
+    hipLaunchKernelGGL((kda_decode_kernel<BF16>), dim3(blocks), dim3(kThreads), 0, stream, a, n_tiles);
+  else
+    hipLaunchKernelGGL((kda_decode_kernel<F32>), dim3(blocks), dim3(kThreads), 0, stream, a, n_tiles);
+  return hipGetLastError();
 }
 
 hipError_t launch_verify(const void* q, const void* k, const void* v, const float* g, const float* beta,
