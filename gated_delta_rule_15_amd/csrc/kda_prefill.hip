@@ -76,8 +76,9 @@ struct Lds {
   static constexpr int kSetKb = kSetQh + kOpBytes;
   static constexpr int kSetTp = kSetKb + kKbBytes;
   static constexpr int kSetP = kSetTp + kSqBytes;
-  static constexpr int kSetGamma = kSetP + kSqBytes;
-  static constexpr int kSetBytes = kSetGamma + kD * 4;
+  static constexpr int kSetGamma = kSetP + kSqBytes;       // e^{b_last - b_mid} per channel
+  static constexpr int kSetEm = kSetGamma + kD * 4;         // e^{b_mid} per channel
+  static constexpr int kSetBytes = kSetEm + kD * 4;
   // prep scratch
   static constexpr int kKc = 2 * kSetBytes;
   static constexpr int kAop = kKc + kOpBytes;              // A_10 (beta-scaled), MFMA operand
@@ -266,6 +267,19 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
                 accR[jb][rt][e] = (!is_transition && 16 * rt + 4 * lq + e < ns) ? -InT::unpack1(sv.v[jb][rt][e]) : 0.0f;
               accO[jb][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             }
+          // the chunk's operands are referenced at b_mid: carry S as e^{b_mid} S
+          // (rows = key channels); phase C applies e^{b_last - b_mid}
+          {
+            const float* s_em = reinterpret_cast<const float*>(sset + L::kSetEm);
+  #pragma unroll
+            for (int ct = 0; ct < 8; ++ct) {
+              const float4 em = *reinterpret_cast<const float4*>(s_em + 16 * ct + 4 * lq);
+  #pragma unroll
+              for (int jb = 0; jb < JB; ++jb) {
+                S[jb][ct][0] *= em.x; S[jb][ct][1] *= em.y; S[jb][ct][2] *= em.z; S[jb][ct][3] *= em.w;
+              }
+            }
+          }
           // R = V - Kh S (accumulated as Kh S - V) and O = Qh S; each 32-row
           // block of S is split once and feeds both products
   #pragma unroll
@@ -417,7 +431,7 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
           for (int e = 0; e < 4; ++e) gq[rr][e] += gq[rr - 1][e];
         // inclusive scan over the NTG token groups (consecutive lanes of one
         // DPP row); lanes shifted in from outside the group contribute 0
-        float excl[4], gam[4];
+        float excl[4], gam[4], emid[4];
   #pragma unroll
         for (int e = 0; e < 4; ++e) {
           float x = gq[TPT - 1][e];
@@ -425,8 +439,13 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
           x += dpp_shr_in_group<2, NTG>(x, tg);
           x += dpp_shr_in_group<4, NTG>(x, tg);
           if constexpr (NTG == 16) x += dpp_shr_in_group<8, NTG>(x, tg);
-          excl[e] = dpp_shr_in_group<1, NTG>(x, tg);
-          gam[e] = __builtin_amdgcn_exp2f(__shfl(x, NTG - 1, NTG));  // decay over the whole chunk
+          // reference: b at the chunk's row 15 (its middle), so that every
+          // rescaling exponent b - b_mid of the chunk lies within the decay of
+          // 16 tokens (e^{+-80} at the lower bound g >= -5, inside fp32 range)
+          const float bmid = __shfl(x, 15 / TPT, NTG);
+          excl[e] = dpp_shr_in_group<1, NTG>(x, tg) - bmid;
+          gam[e] = __builtin_amdgcn_exp2f(__shfl(x, NTG - 1, NTG) - bmid);  // e^{b_last - b_mid}
+          emid[e] = __builtin_amdgcn_exp2f(bmid);                            // e^{b_mid}
         }
         float kbv[TPT][4];
   #pragma unroll
@@ -435,12 +454,12 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
           float kh[4], kc[4], qh[4];
   #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float b = excl[e] + gq[rr][e];  // log2 of the cumulative decay
+            const float b = excl[e] + gq[rr][e];  // log2 of the cumulative decay, relative to b_mid
             const float eb = __builtin_amdgcn_exp2f(b);
             kh[e] = kq[rr][e] * eb;
             kc[e] = kq[rr][e] * __builtin_amdgcn_exp2f(-b);
             qh[e] = (qv[rr][e] * a.scale) * eb;
-            kbv[rr][e] = kc[e] * gam[e];  // k e^{b_last - b}
+            kbv[rr][e] = kc[e] * gam[e];  // k e^{b_last - b} (the reference cancels)
           }
           const int off = r * L::kOpRow + kperm(c0) * E;
           Pol::store4(pset + L::kSetKh, L::kOpPlane, off, kh);
@@ -459,8 +478,12 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
         }
         if (tg == 0) {
           float* g_out = reinterpret_cast<float*>(pset + L::kSetGamma);
+          float* m_out = reinterpret_cast<float*>(pset + L::kSetEm);
   #pragma unroll
-          for (int e = 0; e < 4; ++e) g_out[c0 + e] = gam[e];
+          for (int e = 0; e < 4; ++e) {
+            g_out[c0 + e] = gam[e];
+            m_out[c0 + e] = emid[e];
+          }
         }
         {  // fetch chunk i + 1's inputs (clamped; unconditional so nothing waits on them)
           const int tn = bos + (i + 1 < nch ? i + 1 : nch - 1) * kC;

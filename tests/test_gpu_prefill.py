@@ -111,6 +111,30 @@ def test_prefill_transition_output(dtype):
     assert e <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("gate", ["uniform", "bound"])
+def test_prefill_strong_decay(dtype, gate):
+    """Gates down to the lower bound on log-decay (-5): log alpha ~ U(-5, 0), or -5 everywhere.
+    A 32-token chunk then decays by up to e^-160, beyond fp32 range for a chunk-start reference."""
+    p = gen.packed_batch(seed=13, seqlens=[300, 77, 32, 5], H=2, dtype=dtype, init_state=True)
+    if gate == "uniform":
+        p.g *= np.float32(50.0)
+    else:
+        p.g[:] = np.float32(-5.0)
+    M = torch.empty((4, 2, 128, 128), device="cuda:0")
+    o, S, _ = _run(p, transition_out=M)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(S).all() and torch.isfinite(M).all()
+    _check(p, o, S, f"strong decay ({gate}) {dtype}")
+    M_ref = np.empty((4, 2, 128, 128))
+    for n in range(4):
+        a, b = p.cu_seqlens[n], p.cu_seqlens[n + 1]
+        for h in range(2):
+            M_ref[n, h] = orc.transition(p.f64("k")[a:b, h], p.f64("g")[a:b, h], p.f64("beta")[a:b, h])
+    e = rel_l2(to_f64(M), M_ref)
+    print(f"strong decay ({gate}) {dtype}: rel-L2 M={e:.3e}")
+    assert e <= TOL[dtype]
+
+
 def test_compose_matches_oracle():
     from gated_delta_rule_15_amd.kda import kda_compose_segments
     rng = np.random.default_rng(5)
