@@ -93,9 +93,10 @@ def _verify(b: gen.StepBatch, commit: bool, out_pool: bool = False):
 
 
 @pytest.mark.parametrize("N,G,H,dtype", [(32, 8, 12, "bf16"), (4, 8, 3, "f32"), (7, 3, 5, "bf16"),
-                                         (40, 8, 32, "bf16")])
+                                         (40, 8, 32, "bf16"), (5, 13, 3, "f32"), (3, 17, 2, "bf16")])
 def test_verify_and_commit_match_oracle(N, G, H, dtype):
-    """(32, 8, 12, bf16) is the verify workload: 32 requests x 12 heads x 8 draft tokens."""
+    """(32, 8, 12, bf16) is the verify workload: 32 requests x 12 heads x 8 draft tokens; G = 13 and 17
+    run more than one staged block of 8 tokens."""
     b = gen.step_batch(seed=4, N=N, G=G, H=H, dtype=dtype, accepted=True)
     o, S_after, _, _ = _verify(b, commit=True)
     o_ref, S_ref = orc.verify_block(b.f64("q"), b.f64("k"), b.f64("v"), b.f64("g"), b.f64("beta"),
@@ -107,6 +108,22 @@ def test_verify_and_commit_match_oracle(N, G, H, dtype):
     # per position too: the error does not grow along the draft block
     for t in range(G):
         assert rel_l2(to_f64(o[:, t]), o_ref[:, t]) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_strong_decay_steps(dtype):
+    """Gates down to the lower bound on log-decay: log alpha ~ U(-5, 0), decode and verify + commit."""
+    b = gen.step_batch(seed=42, N=6, G=1, H=3, dtype=dtype)
+    b.g *= np.float32(50.0)
+    o, S = _decode(b)
+    o_ref, S_ref = _oracle_decode(b)
+    assert rel_l2(to_f64(o), o_ref) <= TOL[dtype] and rel_l2(to_f64(S), S_ref) <= TOL[dtype]
+    b = gen.step_batch(seed=43, N=6, G=8, H=3, dtype=dtype, accepted=True)
+    b.g *= np.float32(50.0)
+    o, S_after, _, _ = _verify(b, commit=True)
+    o_ref, S_ref = orc.verify_block(b.f64("q"), b.f64("k"), b.f64("v"), b.f64("g"), b.f64("beta"),
+                                    b.f64("state"), b.accepted_len)
+    assert rel_l2(to_f64(o), o_ref) <= TOL[dtype] and rel_l2(to_f64(S_after), S_ref) <= TOL[dtype]
 
 
 def test_verify_never_writes_the_committed_state():
