@@ -15,6 +15,35 @@ kda_status_t hip_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ER
 
 }  // namespace
 
+namespace {
+
+kda_status_t prefill_impl(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                          const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t H,
+                          int32_t d_k, int32_t d_v, kda_dtype_t dtype, float scale, const float* initial_state,
+                          float* final_state, void* o, float* transition_out, int32_t ckpt_interval,
+                          float* checkpoints, void* stream) {
+  if (num_seqs < 0 || H <= 0) return KDA_ERR_INVALID_ARG;
+  if (!dims_ok(d_k, d_v) || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
+  if (checkpoints && (ckpt_interval <= 0 || ckpt_interval % 64 != 0)) return KDA_ERR_INVALID_ARG;
+  if (num_seqs == 0) return KDA_OK;
+  if (!cu_seqlens) return KDA_ERR_INVALID_ARG;
+  if (cu_seqlens_host) {
+    if (cu_seqlens_host[0] < 0) return KDA_ERR_INVALID_ARG;
+    for (int32_t i = 0; i < num_seqs; ++i)
+      if (cu_seqlens_host[i + 1] < cu_seqlens_host[i]) return KDA_ERR_INVALID_ARG;
+  }
+  const bool any_tokens = !cu_seqlens_host || cu_seqlens_host[num_seqs] > cu_seqlens_host[0];
+  if (any_tokens && (!q || !k || !v || !g || !beta)) return KDA_ERR_INVALID_ARG;
+  if (!final_state && !o && !transition_out && !checkpoints) return KDA_OK;  // nothing requested
+  kda::PrefillLaunch p{q, k, v, g, beta, cu_seqlens, num_seqs, H, scale, initial_state, final_state, o,
+                       transition_out};
+  p.checkpoints = checkpoints;
+  p.ckpt_interval = checkpoints ? ckpt_interval : 0;
+  return hip_status(kda::launch_prefill(p, dtype == KDA_BF16, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
 extern "C" {
 
 int kda_version(void) { return kVersion; }
@@ -76,21 +105,30 @@ kda_status_t kda_prefill(const void* q, const void* k, const void* v, const floa
                          const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t H, int32_t d_k,
                          int32_t d_v, kda_dtype_t dtype, float scale, const float* initial_state,
                          float* final_state, void* o, float* transition_out, void* stream) {
-  if (num_seqs < 0 || H <= 0) return KDA_ERR_INVALID_ARG;
-  if (!dims_ok(d_k, d_v) || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
-  if (num_seqs == 0) return KDA_OK;
-  if (!cu_seqlens) return KDA_ERR_INVALID_ARG;
-  if (cu_seqlens_host) {
-    if (cu_seqlens_host[0] < 0) return KDA_ERR_INVALID_ARG;
-    for (int32_t i = 0; i < num_seqs; ++i)
-      if (cu_seqlens_host[i + 1] < cu_seqlens_host[i]) return KDA_ERR_INVALID_ARG;
+  return prefill_impl(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, num_seqs, H, d_k, d_v, dtype, scale,
+                      initial_state, final_state, o, transition_out, 0, nullptr, stream);
+}
+
+kda_status_t kda_prefill_checkpointed(const void* q, const void* k, const void* v, const float* g,
+                                      const float* beta, const int32_t* cu_seqlens,
+                                      const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t H, int32_t d_k,
+                                      int32_t d_v, kda_dtype_t dtype, float scale, const float* initial_state,
+                                      float* final_state, void* o, int32_t ckpt_interval, float* checkpoints,
+                                      void* stream) {
+  if (!checkpoints) return KDA_ERR_INVALID_ARG;
+  return prefill_impl(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, num_seqs, H, d_k, d_v, dtype, scale,
+                      initial_state, final_state, o, nullptr, ckpt_interval, checkpoints, stream);
+}
+
+int64_t kda_prefill_checkpoint_count(const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t ckpt_interval) {
+  if (!cu_seqlens_host || num_seqs < 0 || ckpt_interval <= 0 || ckpt_interval % 64 != 0) return -1;
+  int64_t n = 0;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const int64_t len = int64_t(cu_seqlens_host[i + 1]) - cu_seqlens_host[i];
+    if (len < 0) return -1;
+    n += len > 0 ? (len - 1) / ckpt_interval : 0;
   }
-  const bool any_tokens = !cu_seqlens_host || cu_seqlens_host[num_seqs] > cu_seqlens_host[0];
-  if (any_tokens && (!q || !k || !v || !g || !beta)) return KDA_ERR_INVALID_ARG;
-  if (!final_state && !o && !transition_out) return KDA_OK;  // nothing requested
-  kda::PrefillLaunch p{q, k, v, g, beta, cu_seqlens, num_seqs, H, scale, initial_state, final_state, o,
-                       transition_out};
-  return hip_status(kda::launch_prefill(p, dtype == KDA_BF16, static_cast<hipStream_t>(stream)));
+  return n;
 }
 
 kda_status_t kda_compose_segments(const float* M, const float* S_tilde, const float* S_in0,

@@ -38,6 +38,8 @@ struct PrefillLaunch {
   float* final_state;          // or null
   void* o;                     // or null
   float* transition_out;       // or null
+  float* checkpoints = nullptr;  // or null: [n_ckpt, H, 128, 128]
+  int32_t ckpt_interval = 0;     // positive multiple of 64 when checkpoints is set
 };
 
 hipError_t launch_prefill(const PrefillLaunch& p, bool bf16, hipStream_t stream);

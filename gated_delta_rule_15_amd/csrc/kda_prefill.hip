@@ -117,6 +117,8 @@ struct PrefillArgs {
   float* final_state;
   void* o;
   float* transition_out;
+  float* checkpoints;       // or null: states at multiples of ckpt_interval tokens
+  int32_t ckpt_interval;    // positive multiple of 64 when checkpoints is set
 };
 
 // Prep-thread inputs of one chunk (TPT tokens x 4 channels), as loaded.
@@ -236,6 +238,17 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
       for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) S[jb][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+
+  // Checkpoint rows of this sequence start after those of the earlier ones:
+  // a sequence of length L stores floor((L - 1) / interval) checkpoints.
+  const bool ckpt_on = a.checkpoints != nullptr && !is_transition;
+  int ckpt_base = 0;
+  if (ckpt_on && is_state) {
+    for (int n = 0; n < seq; ++n) {
+      const int len = a.cu_seqlens[n + 1] - a.cu_seqlens[n];
+      ckpt_base += len > 0 ? (len - 1) / a.ckpt_interval : 0;
     }
   }
 
@@ -397,6 +410,18 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
         {  // fetch chunk i's v (clamped to the last chunk; unconditional so nothing waits on it)
           const int tv = bos + (i < nch ? i : nch - 1) * kC;
           load_state_v<InT, JB>(sv, a, tv, eos - tv < kC ? eos - tv : kC, h, lq, lj, colw);
+        }
+        if (ckpt_on) {  // S is now the state after the sequence's first i * kC tokens
+          const int pos = i * kC;
+          if (pos % a.ckpt_interval == 0 && pos < eos - bos) {
+            float* dst = a.checkpoints + (int64_t(ckpt_base + pos / a.ckpt_interval - 1) * H + h) * (kD * kD) + colw + lj;
+  #pragma unroll
+            for (int jb = 0; jb < JB; ++jb)
+  #pragma unroll
+              for (int ct = 0; ct < 8; ++ct)
+  #pragma unroll
+                for (int e = 0; e < 4; ++e) dst[(16 * ct + 4 * lq + e) * kD + 16 * jb] = S[jb][ct][e];
+          }
         }
       __syncthreads();
     }
@@ -662,6 +687,8 @@ hipError_t launch_cfg(const PrefillLaunch& p, hipStream_t stream) {
   a.final_state = p.final_state;
   a.o = p.o;
   a.transition_out = p.transition_out;
+  a.checkpoints = p.checkpoints;
+  a.ckpt_interval = p.ckpt_interval;
   const int64_t blocks = int64_t(p.num_seqs) * p.H * a.n_slices;
   hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, SW, JB, PW>), dim3(unsigned(blocks)),
                      dim3(prefill_threads(SW, PW)), 0, stream, a);

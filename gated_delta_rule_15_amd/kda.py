@@ -183,6 +183,59 @@ def kda_prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host=None, initial_stat
     return o, final_state
 
 
+def kda_prefill_checkpoint_count(cu_seqlens_host, ckpt_interval: int) -> int:
+    """Rows kda_prefill_checkpointed writes: sum over sequences of floor((len - 1) / ckpt_interval)."""
+    cu = torch.as_tensor(cu_seqlens_host, dtype=torch.int32).contiguous()
+    if cu.is_cuda or cu.dim() != 1:
+        raise ValueError("cu_seqlens_host must be a 1-D CPU int32 array")
+    n = _lib.load().kda_prefill_checkpoint_count(_ptr(cu), cu.shape[0] - 1, int(ckpt_interval))
+    if n < 0:
+        raise ValueError("ckpt_interval must be a positive multiple of 64 and cu_seqlens non-decreasing")
+    return int(n)
+
+
+def kda_prefill_checkpointed(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, ckpt_interval: int, initial_state=None,
+                             final_state=None, o=None, checkpoints=None, scale: float = 1.0, with_output: bool = True,
+                             with_final_state: bool = True):
+    """kda_prefill that also returns the state after every ``ckpt_interval`` tokens of each sequence
+    (strictly inside the sequence).  ``cu_seqlens_host`` (CPU int32) is required to size the
+    checkpoint buffer.  Returns (o or None, final_state or None, checkpoints [n_ckpt, H, 128, 128])."""
+    T, H, _ = q.shape
+    dt = q.dtype
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, (T, H, D), dt, dev)
+    _need(g, "g", (T, H, D), torch.float32, dev)
+    _need(beta, "beta", (T, H), torch.float32, dev)
+    _need(cu_seqlens, "cu_seqlens", cu_seqlens.shape, torch.int32, dev)
+    N = cu_seqlens.shape[0] - 1
+    if cu_seqlens_host is None or cu_seqlens_host.is_cuda or cu_seqlens_host.dtype != torch.int32 \
+            or cu_seqlens_host.shape != cu_seqlens.shape or not cu_seqlens_host.is_contiguous():
+        raise ValueError("cu_seqlens_host must be a contiguous CPU int32 copy of cu_seqlens")
+    if int(cu_seqlens_host[-1]) > T or int(cu_seqlens_host[0]) < 0:
+        raise ValueError("cu_seqlens_host must lie within the packed tokens")
+    n_ckpt = kda_prefill_checkpoint_count(cu_seqlens_host, ckpt_interval)
+    _need(initial_state, "initial_state", (N, H, D, D), torch.float32, dev)
+    if with_final_state and final_state is None:
+        final_state = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
+    _need(final_state, "final_state", (N, H, D, D), torch.float32, dev)
+    if with_output and o is None:
+        o = torch.empty((T, H, D), dtype=dt, device=dev)
+    _need(o, "o", (T, H, D), dt, dev)
+    if checkpoints is None:
+        checkpoints = torch.empty((max(n_ckpt, 1), H, D, D), dtype=torch.float32, device=dev)
+    if checkpoints.shape[0] < n_ckpt:
+        raise ValueError(f"checkpoints needs {n_ckpt} rows")
+    _need(checkpoints, "checkpoints", tuple(checkpoints.shape), torch.float32, dev)
+    lib = _lib.load()
+    _lib.check(lib.kda_prefill_checkpointed(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                                            _ptr(cu_seqlens_host), N, H, D, D, _dtype_code(q), float(scale),
+                                            _ptr(initial_state), _ptr(final_state), _ptr(o), int(ckpt_interval),
+                                            _ptr(checkpoints), _stream()),
+               "kda_prefill_checkpointed")
+    return o, final_state, checkpoints[:n_ckpt]
+
+
 def kda_compose_segments(M, S_tilde, S_in0=None, S_in=None, S_final=None, with_final: bool = True):
     """Entry states of consecutive segments: S_in[0] = S_in0, S_in[i+1] = M[i] S_in[i] + S~[i].
 

@@ -137,6 +137,35 @@ kda_status_t kda_prefill(const void* q, const void* k, const void* v, const floa
                          float* final_state, void* o, float* transition_out, void* stream);
 
 /*
+ * kda_prefill_checkpointed — kda_prefill that also stores the state at chunk
+ * boundaries, for restoring a prefix later (prefix caching / copy-on-write
+ * restore of a state, as the serving pages describe for KDA's fixed-size
+ * state).  Same arguments and results as kda_prefill, without transitions, plus:
+ *   ckpt_interval : positive multiple of 64 (checkpoints fall on chunk ends).
+ *   checkpoints   : [n_ckpt, H, 128, 128] fp32, required.  For sequence n of
+ *                   length L and m = 1, 2, ... with m * ckpt_interval < L, row
+ *                   base(n) + m - 1 receives the state after the sequence's
+ *                   first m * ckpt_interval tokens (from its initial state),
+ *                   where base(n) sums floor((L' - 1) / ckpt_interval) over the
+ *                   earlier sequences.  kda_prefill_checkpoint_count gives n_ckpt.
+ * Errors: KDA_ERR_INVALID_ARG for a missing buffer or a bad interval, otherwise
+ * as kda_prefill.
+ */
+kda_status_t kda_prefill_checkpointed(const void* q, const void* k, const void* v, const float* g,
+                                      const float* beta, const int32_t* cu_seqlens,
+                                      const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t H, int32_t d_k,
+                                      int32_t d_v, kda_dtype_t dtype, float scale, const float* initial_state,
+                                      float* final_state, void* o, int32_t ckpt_interval, float* checkpoints,
+                                      void* stream);
+
+/*
+ * kda_prefill_checkpoint_count — number of checkpoint rows kda_prefill_checkpointed
+ * writes for this batch (host only; reads cu_seqlens_host [num_seqs + 1]).
+ * Returns -1 for a bad interval, a NULL array or a decreasing cu_seqlens_host.
+ */
+int64_t kda_prefill_checkpoint_count(const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t ckpt_interval);
+
+/*
  * kda_compose_segments — entry states of consecutive segments of one sequence
  * from their fragments ("Kimi K3 的训练与 Serving Infra", section 4.2: after
  * exchanging the fixed-size fragments, a prefix scan recovers each segment's

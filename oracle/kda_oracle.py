@@ -106,6 +106,34 @@ def prefill(q, k, v, g, beta, cu_seqlens, S0=None, scale=1.0, heads=None):
     return o, S_final
 
 
+def prefill_checkpoints(k, v, g, beta, cu_seqlens, interval, S0=None):
+    """States at chunk boundaries of a packed batch: for each sequence (length L)
+    and m = 1, 2, ... with m * interval < L, the state after its first
+    m * interval tokens, in sequence order (the rows a checkpointed prefill
+    stores; a fixed-size state is what a prefix cache keeps, per the serving
+    pages).  Each state is ``recurrence`` chained over the interval-long pieces.
+    Returns [n_ckpt, H, d_k, d_v].
+    """
+    k, v, g, beta = _f64(k), _f64(v), _f64(g), _f64(beta)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    T, H, dk = k.shape
+    dv = v.shape[2]
+    out = []
+    for n in range(cu.shape[0] - 1):
+        a, b = int(cu[n]), int(cu[n + 1])
+        m_count = (b - a - 1) // interval if b > a else 0
+        rows = np.empty((m_count, H, dk, dv))
+        for h in range(H):
+            S = np.zeros((dk, dv)) if S0 is None else np.array(S0[n, h], dtype=np.float64)
+            for m in range(m_count):
+                lo, hi = a + m * interval, a + (m + 1) * interval
+                zq = np.zeros((hi - lo, dk))
+                _, S = recurrence(zq, k[lo:hi, h], v[lo:hi, h], g[lo:hi, h], beta[lo:hi, h], S)
+                rows[m, h] = S
+        out.append(rows)
+    return np.concatenate(out, axis=0) if out else np.empty((0, H, dk, dv))
+
+
 def decode_step(q, k, v, g, beta, S, scale=1.0):
     """One token per request: q,k,g [N, H, d_k]; v [N, H, d_v]; beta [N, H]; S [N, H, d_k, d_v].
 

@@ -31,7 +31,8 @@ def lib():
 def test_header_declares_the_entry_points():
     syms = declared_symbols()
     for name in ("kda_prefill", "kda_decode_step", "kda_verify_block", "kda_verify_commit",
-                 "kda_compose_segments", "kda_status_string", "kda_version"):
+                 "kda_compose_segments", "kda_prefill_checkpointed", "kda_prefill_checkpoint_count",
+                 "kda_status_string", "kda_version"):
         assert name in syms
     assert set(syms) == set(_lib.SIGNATURES), "binding signatures and header disagree"
 
@@ -92,6 +93,23 @@ def test_prefill_argument_errors(lib):
     assert lib.kda_prefill(p, p, p, p, p, p, good, 2, 2, 128, 128, 1, 1.0, None, None, None, None, None) == 0
     assert lib.kda_prefill(None, None, None, None, None, None, None, 0, 2, 128, 128, 1, 1.0, None, None, None,
                            None, None) == 0
+
+
+def test_checkpoint_argument_errors(lib):
+    p = ctypes.c_void_p(16)
+    good = (ctypes.c_int32 * 3)(0, 130, 200)
+    for interval in (0, -64, 100):
+        assert lib.kda_prefill_checkpointed(p, p, p, p, p, p, good, 2, 2, 128, 128, 1, 1.0, None, p, p, interval, p,
+                                            None) == _lib.KDA_ERR_INVALID_ARG
+        assert lib.kda_prefill_checkpoint_count(good, 2, interval) == -1
+    # the checkpoint buffer is required
+    assert lib.kda_prefill_checkpointed(p, p, p, p, p, p, good, 2, 2, 128, 128, 1, 1.0, None, p, p, 64, None,
+                                        None) == _lib.KDA_ERR_INVALID_ARG
+    # counts: floor((130 - 1) / 64) + floor((70 - 1) / 64) = 2 + 1
+    assert lib.kda_prefill_checkpoint_count(good, 2, 64) == 3
+    assert lib.kda_prefill_checkpoint_count(good, 2, 128) == 1
+    decreasing = (ctypes.c_int32 * 3)(0, 9, 5)
+    assert lib.kda_prefill_checkpoint_count(decreasing, 2, 64) == -1
 
 
 def test_compose_argument_errors(lib):

@@ -135,6 +135,31 @@ def test_prefill_strong_decay(dtype, gate):
     assert e <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype,lens,H,interval,init", [
+    ("bf16", [300, 64, 65, 0, 1, 200], 3, 64, True),
+    ("f32", [300, 64, 65, 0, 1, 200], 3, 64, False),
+    ("bf16", [1000, 129, 128], 2, 128, True),
+    ("bf16", [1 + (37 * i) % 300 for i in range(32)], 8, 64, True),   # >= 256 units: 128-column workgroups
+])
+def test_prefill_checkpoints(dtype, lens, H, interval, init):
+    """States after every `interval` tokens of each sequence, against the oracle's chained recurrence."""
+    from gated_delta_rule_15_amd.kda import kda_prefill_checkpoint_count, kda_prefill_checkpointed
+    p = gen.packed_batch(seed=14, seqlens=lens, H=H, dtype=dtype, init_state=init)
+    d = packed_to_dev(p)
+    n = kda_prefill_checkpoint_count(d["cu_seqlens_host"], interval)
+    assert n == sum((L - 1) // interval if L else 0 for L in lens)
+    o, S, C = kda_prefill_checkpointed(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"],
+                                       d["cu_seqlens_host"], interval, initial_state=d["initial_state"])
+    torch.cuda.synchronize()
+    _check(p, o, S, f"checkpointed prefill {dtype}")
+    C_ref = orc.prefill_checkpoints(p.f64("k"), p.f64("v"), p.f64("g"), p.f64("beta"), p.cu_seqlens, interval,
+                                    p.initial_state)
+    assert C.shape[0] == C_ref.shape[0] == n
+    e = rel_l2(to_f64(C), C_ref)
+    print(f"checkpoints {dtype} x{n}: rel-L2 {e:.3e}")
+    assert e <= TOL[dtype]
+
+
 def test_compose_matches_oracle():
     from gated_delta_rule_15_amd.kda import kda_compose_segments
     rng = np.random.default_rng(5)

@@ -292,3 +292,36 @@ def test_rel_l2():
     a = np.array([3.0, 4.0])
     assert orc.rel_l2(a, a) == 0.0
     assert orc.rel_l2(a + np.array([0.3, 0.4]), a) == pytest.approx(0.1)
+
+
+def test_checkpoints_are_affine_prefixes():
+    """A checkpoint at p maps to the final state through the explicit-product transition of
+    tokens p..L plus the zero-start state of those tokens (affinity), for every checkpoint."""
+    rng = np.random.default_rng(77)
+    dk = dv = 4
+    lens = [13, 8, 1, 0, 9]
+    cu = np.cumsum([0] + lens)
+    T, H = int(cu[-1]), 2
+    k = rng.standard_normal((T, H, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((T, H, dv))
+    g = -0.3 * rng.random((T, H, dk))
+    beta = 1 / (1 + np.exp(-rng.standard_normal((T, H))))
+    q = rng.standard_normal((T, H, dk))
+    S0 = rng.standard_normal((len(lens), H, dk, dv))
+    interval = 4
+    C = orc.prefill_checkpoints(k, v, g, beta, cu, interval, S0)
+    assert C.shape == (sum((L - 1) // interval if L else 0 for L in lens), H, dk, dv)
+    _, S_fin = orc.prefill(q, k, v, g, beta, cu, S0)
+    row = 0
+    for n, L in enumerate(lens):
+        a = int(cu[n])
+        for m in range(1, ((L - 1) // interval if L else 0) + 1):
+            p = a + m * interval
+            for h in range(H):
+                M = orc.transition(k[p:a + L, h], g[p:a + L, h], beta[p:a + L, h])
+                _, S_tail = orc.recurrence(q[p:a + L, h], k[p:a + L, h], v[p:a + L, h], g[p:a + L, h],
+                                           beta[p:a + L, h], None)
+                assert np.allclose(M @ C[row, h] + S_tail, S_fin[n, h], atol=1e-12)
+            row += 1
+    assert row == C.shape[0]
