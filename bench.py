@@ -202,6 +202,11 @@ def bench_prefill(reps, warmup):
     S2 = torch.empty_like(S)
     ms_seg = _event_time_ms(lambda: kda_prefill_segmented(q, k, v, g, beta, p.cu_seqlens, o=o2, final_state=S2,
                                                           plan=plan, work=work), reps, warmup)
+    # checkpoints every 512 tokens (7 per sequence and head) in the single launch
+    cu_h = torch.from_numpy(p.cu_seqlens.copy())
+    C = torch.empty((kda.kda_prefill_checkpoint_count(cu_h, 512), 12, D, D), device="cuda:0")
+    ms_ckpt = _event_time_ms(lambda: kda.kda_prefill_checkpointed(q, k, v, g, beta, cu, cu_h, 512, o=o, final_state=S,
+                                                                    checkpoints=C), reps, warmup)
     ms = min(ms_kernel, ms_seg)
     th = 4096 * 12
     flops = th * FLOP_PER_TOKEN_HEAD_PREFILL
@@ -210,7 +215,8 @@ def bench_prefill(reps, warmup):
                 frac_mfma_peak=flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
                 gbps=nbytes / (ms * 1e-3) / 1e9, frac_hbm_peak=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                 path="segmented" if ms_seg < ms_kernel else "single launch",
-                single_launch_ms=ms_kernel, segmented_ms=ms_seg, segment_len=seg, segments=plan.n_rows)
+                single_launch_ms=ms_kernel, segmented_ms=ms_seg, segment_len=seg, segments=plan.n_rows,
+                single_launch_checkpoints_every_512_ms=ms_ckpt)
 
 
 def bench_long(reps, warmup=1):

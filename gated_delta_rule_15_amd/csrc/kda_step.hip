@@ -48,6 +48,10 @@ constexpr int kSlicesPerWg = (kThreads / 64) / kWavesPerSlice;
 constexpr int kWgCols = kSliceCols * kSlicesPerWg;  // columns per workgroup
 constexpr int kWgPerHead = kD / kWgCols;            // workgroups per (request, head)
 constexpr int kBlockT = 8;                          // tokens staged per block (verify / commit)
+#ifndef KDA_BLOCK_HALVES
+#define KDA_BLOCK_HALVES 1
+#endif
+constexpr int kBlockHalves = KDA_BLOCK_HALVES;      // 64-column halves per verify / commit workgroup
 static_assert(kR == 8 || kR == 16, "rows per lane");
 
 enum StepMode { kDecode = 0, kVerify = 1, kCommit = 2 };
@@ -78,7 +82,7 @@ struct __align__(16) Stage {
   float k[kBlockT][kD];
   float qs[kBlockT][kD];     // scale * q
   float alpha[kBlockT][kD];  // exp(g)
-  float v[kBlockT][kWgCols]; // this workgroup's columns
+  float v[kBlockT][kWgCols * kBlockHalves];  // v of the workgroup's columns
   float beta[kBlockT];
 };
 
@@ -153,7 +157,7 @@ __device__ __forceinline__ void stage_block(Stage& st, const StepArgs& a, int n,
   const float4 g = ld_f4(a.g + vec + c4);
   typename InT::raw4 qr{};
   if constexpr (READOUT) qr = InT::load4raw(a.q, vec + c4);
-  constexpr int kVPieces = kWgCols / 4;  // v pieces per token
+  constexpr int kVPieces = kWgCols * kBlockHalves / 4;  // v pieces per token
   const int tv = tid / kVPieces, cv = 4 * (tid % kVPieces);
   const int ttv = b0 + tv <= last ? b0 + tv : last;
   typename InT::raw4 vr{};
@@ -250,28 +254,38 @@ __device__ __forceinline__ void st_state(float* p, const float (&s)[4]) {
   }
 }
 
+// Verify / commit: a workgroup walks kBlockHalves 64-column halves of one
+// (request, head), one half's token steps after the other, with every state
+// load issued before the first step and the token inputs staged once.  One
+// half per workgroup is the default: two (one workgroup per head) measured
+// 37 us against 27 us for verify + commit of 32 x 12 x 8, because 384
+// workgroups leave the chip under-occupied and each runs 16 dependent steps.
+static_assert(kBlockHalves == 1 || kBlockHalves * kWgCols == kD, "halves cover the state");
+
 template <class InT, int MODE>
 __global__ __launch_bounds__(kThreads) void kda_step_kernel(StepArgs a) {
+  static_assert(MODE != kDecode, "decode runs kda_decode_kernel");
   constexpr bool READOUT = (MODE != kCommit);
-  constexpr bool NT = (MODE == kDecode);  // the decode state is streamed once per call
+  constexpr int NH = kBlockHalves;
   __shared__ Red red;
+  __shared__ Stage st;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int ws = wave % kWavesPerSlice;  // wave within its slice: rows kRowsPerWave * ws ..
-  const int sl = wave / kWavesPerSlice;  // slice within the workgroup
+  const int sl = wave / kWavesPerSlice;  // slice within the workgroup's columns
   const int cg = lane % kCG;
   const int rg = lane / kCG;
   const int row0 = ws * kRowsPerWave + rg * kR;
 
-  const int half = blockIdx.x % kWgPerHead;
-  const int nh = blockIdx.x / kWgPerHead;
+  const int wgs_per_head = kWgPerHead / NH;
+  const int part = blockIdx.x % wgs_per_head;        // which half (NH == 1) or 0
+  const int nh = blockIdx.x / wgs_per_head;
   const int h = nh % a.H;
   const int n = nh / a.H;
-  const int col0 = half * kWgCols;               // first column of the workgroup
-  const int wcol = sl * kSliceCols + cg * 4;     // column within the workgroup
-  const int col = col0 + wcol;
+  const int col0 = part * kWgCols * NH;              // first column of the workgroup
+  const int wcol = sl * kSliceCols + cg * 4;         // column within a half
 
   int steps = a.G;
   if (MODE == kCommit) {
@@ -283,35 +297,35 @@ __global__ __launch_bounds__(kThreads) void kda_step_kernel(StepArgs a) {
   const int64_t tile = (pool_row * a.H + h) * int64_t(kD * kD);
   const float* Sin = a.state_in + tile;
 
-  float S[kR][4];
+  float S[NH][kR][4];
 #pragma unroll
-  for (int i = 0; i < kR; ++i) {
-    const float4 w = ld_state<NT>(Sin + (row0 + i) * kD + col);
-    S[i][0] = w.x; S[i][1] = w.y; S[i][2] = w.z; S[i][3] = w.w;
-  }
+  for (int j = 0; j < NH; ++j)
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+      const float4 w = ld_f4(Sin + (row0 + i) * kD + col0 + j * kWgCols + wcol);
+      S[j][i][0] = w.x; S[j][i][1] = w.y; S[j][i][2] = w.z; S[j][i][3] = w.w;
+    }
 
-  float o[4];
   const bool writer = (ws == 0 && rg == 0 && a.o != nullptr);
-  if constexpr (MODE == kDecode) {
-    TokenVals x;
-    load_token<InT, true>(x, a, n, 0, h, row0, col);
-    token_step<true>(S, x, red.x[0][sl], lane, ws, cg, o);
-    if (writer) InT::store4(a.o, (int64_t(n) * a.H + h) * kD + col, o);
-  } else {
-    __shared__ Stage st;
-    const int last = steps > 0 ? steps - 1 : 0;
-    for (int b0 = 0; b0 < steps; b0 += kBlockT) {
-      if (b0 > 0) __syncthreads();  // every step of the previous block has read the stage
-      stage_block<InT, READOUT>(st, a, n, h, col0, b0, last, tid);
-      __syncthreads();
+  const int last = steps > 0 ? steps - 1 : 0;
+  int c = 0;  // token steps so far (alternates the reduction buffers)
+  for (int b0 = 0; b0 < steps; b0 += kBlockT) {
+    if (b0 > 0) __syncthreads();  // every step of the previous block has read the stage
+    stage_block<InT, READOUT>(st, a, n, h, col0, b0, last, tid);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NH; ++j) {
 #pragma unroll
       for (int t = 0; t < kBlockT; ++t) {
         if (b0 + t < steps) {
           TokenVals x;
-          read_token(x, st, t, row0, wcol, READOUT);
-          token_step<READOUT>(S, x, red.x[(b0 + t) & 1][sl], lane, ws, cg, o);
+          float o[4];
+          read_token(x, st, t, row0, j * kWgCols + wcol, READOUT);
+          token_step<READOUT>(S[j], x, red.x[c & 1][sl], lane, ws, cg, o);
+          ++c;
           if constexpr (READOUT) {
-            if (writer) InT::store4(a.o, ((int64_t(n) * a.G + b0 + t) * a.H + h) * kD + col, o);
+            if (writer)
+              InT::store4(a.o, ((int64_t(n) * a.G + b0 + t) * a.H + h) * kD + col0 + j * kWgCols + wcol, o);
           }
         }
       }
@@ -321,7 +335,9 @@ __global__ __launch_bounds__(kThreads) void kda_step_kernel(StepArgs a) {
   if constexpr (MODE != kVerify) {
     float* Sout = a.state_out + tile;
 #pragma unroll
-    for (int i = 0; i < kR; ++i) st_state<NT>(Sout + (row0 + i) * kD + col, S[i]);
+    for (int j = 0; j < NH; ++j)
+#pragma unroll
+      for (int i = 0; i < kR; ++i) st_state<false>(Sout + (row0 + i) * kD + col0 + j * kWgCols + wcol, S[j][i]);
   }
 }
 
@@ -387,7 +403,7 @@ __global__ __launch_bounds__(kThreads) void kda_decode_kernel(StepArgs a, int n_
 
 template <int MODE>
 hipError_t launch_step(const StepArgs& a, bool bf16, hipStream_t stream) {
-  const int64_t blocks = int64_t(a.N) * a.H * kWgPerHead;
+  const int64_t blocks = int64_t(a.N) * a.H * (kWgPerHead / kBlockHalves);
   if (bf16)
     hipLaunchKernelGGL((kda_step_kernel<BF16, MODE>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a);
   else
