@@ -150,10 +150,20 @@ __device__ __forceinline__ void load_prep(PrepIn<InT, TPT>& in, const PrefillArg
   in.beta = a.beta[int64_t(t0) * a.H + h + (ptid < n ? ptid : n - 1) * a.H];
 }
 
-// State-wave v at this wave's columns, accumulator layout (rows 16rt+4lq+i).
+// State-wave v of one chunk at this wave's columns.
+//  fp32 inputs: the accumulator layout directly (rows 16rt+4lq+i, column lj).
+//  bf16 inputs: lane (lq, lj) holds token 16rt+lj, columns 4lq..4lq+3 of each
+//  16-column block (one 8-byte load); one bf16 MFMA against a negated
+//  identity moves the block into the accumulator layout as -V, exactly.
 template <class InT, int JB>
 struct StateV {
+  static constexpr bool kBf16 = false;
   typename InT::raw1 v[JB][2][4];
+};
+template <int JB>
+struct StateV<BF16, JB> {
+  static constexpr bool kBf16 = true;
+  uint2 vb[JB][2];
 };
 
 template <class InT, int JB>
@@ -162,18 +172,28 @@ __device__ __forceinline__ void load_state_v(StateV<InT, JB>& sv, const PrefillA
   const char* vb = reinterpret_cast<const char*>(a.v) +
                    ((int64_t(t0) * a.H + h) * kD + colw) * int64_t(sizeof(typename InT::storage));
   const int rstride = a.H * kD;
+  if constexpr (StateV<InT, JB>::kBf16) {
 #pragma unroll
-  for (int jb = 0; jb < JB; ++jb)
+    for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * lq + i;
-        sv.v[jb][rt][i] = InT::load1raw(vb, (r < n ? r : n - 1) * rstride + 16 * jb + lj);
+      for (int rt = 0; rt < 2; ++rt) {
+        const int r = 16 * rt + lj;
+        sv.vb[jb][rt] = *reinterpret_cast<const uint2*>(vb + int64_t((r < n ? r : n - 1) * rstride + 16 * jb + 4 * lq) * 2);
       }
+  } else {
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * rt + 4 * lq + i;
+          sv.v[jb][rt][i] = InT::load1raw(vb, (r < n ? r : n - 1) * rstride + 16 * jb + lj);
+        }
+  }
 }
 
-template <class Pol, class InT, int SW, int JB, int PW>
+template <class Pol, class InT, int SW, int JB, int PW, bool CKPT>
 __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(PrefillArgs a) {
   static_assert(PW == 4 || PW == 8, "prep waves");
   constexpr int TPT = 16 / PW;  // tokens per prep thread (4 or 2)
@@ -243,7 +263,7 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
 
   // Checkpoint rows of this sequence start after those of the earlier ones:
   // a sequence of length L stores floor((L - 1) / interval) checkpoints.
-  const bool ckpt_on = a.checkpoints != nullptr && !is_transition;
+  const bool ckpt_on = CKPT && !is_transition;
   int ckpt_base = 0;
   if (ckpt_on && is_state) {
     for (int n = 0; n < seq; ++n) {
@@ -257,6 +277,13 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
   if (is_state) {
     StateV<InT, JB> sv;
     f32x4_t accR[JB][2], accO[JB][2];
+    // B operand -I for the V transposition: slot e < 4 of lane group lq is
+    // column 4lq + e, the other four slots are zero
+    bf16x8_t neg_eye = {};
+    if constexpr (StateV<InT, JB>::kBf16) {
+  #pragma unroll
+      for (int e = 0; e < 4; ++e) neg_eye[e] = (4 * lq + e == lj) ? (__bf16)(-1.0f) : (__bf16)(0.0f);
+    }
     Frag uf[JB];
     // step 0: the prep waves build chunk 0; fetch chunk 0's v
     if (nch > 0) load_state_v<InT, JB>(sv, a, bos, eos - bos < kC ? eos - bos : kC, h, lq, lj, colw);
@@ -275,9 +302,18 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
           for (int jb = 0; jb < JB; ++jb)
   #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
+              if constexpr (StateV<InT, JB>::kBf16) {
+                // -V block by MFMA: A = V rows (tokens past the chunk end and
+                // transition runs give zero rows), B = -I in this lane's slots
+                const bool keep = !is_transition && 16 * rt + lj < ns;
+                const u32x4_t aw = {keep ? sv.vb[jb][rt].x : 0u, keep ? sv.vb[jb][rt].y : 0u, 0u, 0u};
+                accR[jb][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, aw), neg_eye,
+                                                                     f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+              } else {
   #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                accR[jb][rt][e] = (!is_transition && 16 * rt + 4 * lq + e < ns) ? -InT::unpack1(sv.v[jb][rt][e]) : 0.0f;
+                for (int e = 0; e < 4; ++e)
+                  accR[jb][rt][e] = (!is_transition && 16 * rt + 4 * lq + e < ns) ? -InT::unpack1(sv.v[jb][rt][e]) : 0.0f;
+              }
               accO[jb][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             }
           // the chunk's operands are referenced at b_mid: carry S as e^{b_mid} S
@@ -411,7 +447,7 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
           const int tv = bos + (i < nch ? i : nch - 1) * kC;
           load_state_v<InT, JB>(sv, a, tv, eos - tv < kC ? eos - tv : kC, h, lq, lj, colw);
         }
-        if (ckpt_on) {  // S is now the state after the sequence's first i * kC tokens
+        if (CKPT && ckpt_on) {  // S is now the state after the sequence's first i * kC tokens
           const int pos = i * kC;
           if (pos % a.ckpt_interval == 0 && pos < eos - bos) {
             float* dst = a.checkpoints + (int64_t(ckpt_base + pos / a.ckpt_interval - 1) * H + h) * (kD * kD) + colw + lj;
@@ -690,8 +726,12 @@ hipError_t launch_cfg(const PrefillLaunch& p, hipStream_t stream) {
   a.checkpoints = p.checkpoints;
   a.ckpt_interval = p.ckpt_interval;
   const int64_t blocks = int64_t(p.num_seqs) * p.H * a.n_slices;
-  hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, SW, JB, PW>), dim3(unsigned(blocks)),
-                     dim3(prefill_threads(SW, PW)), 0, stream, a);
+  if (p.checkpoints)
+    hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, SW, JB, PW, true>), dim3(unsigned(blocks)),
+                       dim3(prefill_threads(SW, PW)), 0, stream, a);
+  else
+    hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, SW, JB, PW, false>), dim3(unsigned(blocks)),
+                       dim3(prefill_threads(SW, PW)), 0, stream, a);
   return hipGetLastError();
 }
 
