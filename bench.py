@@ -219,12 +219,14 @@ def bench_prefill(reps, warmup):
                 single_launch_checkpoints_every_512_ms=ms_ckpt)
 
 
-def bench_long(reps, warmup=1):
-    """1,048,576-token sequence (16 segments of 65,536) + 8 ragged 1K-32K sequences, 12 heads, bf16."""
+def bench_long(reps, warmup=1, gen_workers=None):
+    """1,048,576-token sequence (16 segments of 65,536) + 8 ragged 1K-32K sequences, 12 heads, bf16.
+    Inputs are drawn by ``gen_workers`` spawned processes (default: the host's cores, at most 16);
+    1 draws them in this process (for runs under a profiler)."""
     import torch
     from gated_delta_rule_15_amd import inputs as gen
     from gated_delta_rule_15_amd.long_context import alloc_work, kda_prefill_segmented, plan_segments
-    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    workers = gen_workers or max(1, min(16, len(os.sched_getaffinity(0))))
     t = time.time()
     p = gen.long_context_batch(seed=5, workers=workers)
     log(f"long context: inputs drawn in {time.time() - t:.1f}s (T={p.T})")
@@ -232,7 +234,8 @@ def bench_long(reps, warmup=1):
         q, k, v = to_dev(p.q, "bf16"), to_dev(p.k, "bf16"), to_dev(p.v, "bf16")
         g, beta = to_dev(p.g), to_dev(p.beta)
     finally:
-        p.release()
+        if hasattr(p, "release"):
+            p.release()
     init = to_dev(p.initial_state)
     H, T = 12, p.T
     plan = plan_segments(p.cu_seqlens, 65536)
@@ -327,6 +330,8 @@ def main():
     ap.add_argument("--only-decode", action="store_true", help="time only the decode rows (for profiling)")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch without a HIP graph (counter collection)")
+    ap.add_argument("--gen-workers", type=int, default=None,
+                    help="processes drawing the long-context inputs (1: in this process, e.g. under a profiler)")
     args = ap.parse_args()
     global EAGER
     EAGER = args.eager
@@ -360,7 +365,7 @@ def main():
         rows["verify_commit_32x12x8_bf16"] = vf
         if args.long:
             log("long context: 1,048,576 + 8 ragged sequences x 12 heads ...")
-            lc = bench_long(reps=2)
+            lc = bench_long(reps=2, gen_workers=args.gen_workers)
             log(f"long context: {lc['ms']:.2f} ms, {lc['tokens_per_s'] / 1e6:.1f} M tokens/s")
             rows["long_context_1m_plus_8"] = lc
 
