@@ -469,6 +469,9 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
       const int tp = bos + i * kC;
       const int np = eos - tp < kC ? eos - tp : kC;
       char* pset = smem + (i & 1) * L::kSetBytes;
+      // K-bar of this chunk: computed with the other operands in phase A, split
+      // and stored in phase C (the state waves first read it a step later)
+      float kbv[TPT][4];
 
       // ============================== phase A ==============================
       {
@@ -508,7 +511,6 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
           gam[e] = __builtin_amdgcn_exp2f(__shfl(x, NTG - 1, NTG) - bmid);  // e^{b_last - b_mid}
           emid[e] = __builtin_amdgcn_exp2f(bmid);                            // e^{b_mid}
         }
-        float kbv[TPT][4];
   #pragma unroll
         for (int rr = 0; rr < TPT; ++rr) {
           const int r = TPT * tg + rr;
@@ -526,16 +528,6 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
           Pol::store4(pset + L::kSetKh, L::kOpPlane, off, kh);
           Pol::store4(smem + L::kKc, L::kOpPlane, off, kc);
           Pol::store4(pset + L::kSetQh, L::kOpPlane, off, qh);
-        }
-  #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int off = (c0 + e) * L::kKbRow + kperm(TPT * tg) * E;
-          if constexpr (TPT == 4) {
-            const float w4[4] = {kbv[0][e], kbv[1][e], kbv[2][e], kbv[3][e]};
-            Pol::store4(pset + L::kSetKb, L::kKbPlane, off, w4);
-          } else {
-            Pol::store2(pset + L::kSetKb, L::kKbPlane, off, kbv[0][e], kbv[1][e]);
-          }
         }
         if (tg == 0) {
           float* g_out = reinterpret_cast<float*>(pset + L::kSetGamma);
@@ -685,6 +677,17 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
             Pol::store1(pset + L::kSetTp, L::kSqPlane, (16 * I + r) * L::kSqRow + kperm(16 * I + lj) * E,
                         (r >= lj) ? tv[e] * bj : 0.0f);
             if (I == 0) Pol::store1(pset + L::kSetTp, L::kSqPlane, r * L::kSqRow + kperm(16 + lj) * E, 0.0f);
+          }
+        }
+        // K-bar^T of this chunk (every prep thread, its own tokens and channels)
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int off = (c0 + e) * L::kKbRow + kperm(TPT * tg) * E;
+          if constexpr (TPT == 4) {
+            const float w4[4] = {kbv[0][e], kbv[1][e], kbv[2][e], kbv[3][e]};
+            Pol::store4(pset + L::kSetKb, L::kKbPlane, off, w4);
+          } else {
+            Pol::store2(pset + L::kSetKb, L::kKbPlane, off, kbv[0][e], kbv[1][e]);
           }
         }
       }
