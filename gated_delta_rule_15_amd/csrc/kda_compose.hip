@@ -11,11 +11,13 @@
 // runs the scan serially over segments.  Each step is a 128 x 128 x 16 fp32
 // product on fp32 MFMA (v_mfma_f32_16x16x4_f32, exact products, fp32
 // accumulation): wave w computes output rows 32w .. 32w+31 as two 16 x 16
-// tiles.  The contraction index of lane group q at step s is k = 32q + s, so a
-// lane streams 32 contiguous floats of its M row (global) and of its column
+// tiles.  The contraction index of lane group q at step s is k = 32q + s, so
+// a lane streams 32 contiguous floats of its M row (global) and of its column
 // of the running state, which is kept transposed in LDS.  Two accumulator
 // chains per tile (even and odd s) halve the dependent MFMA latency; their sum
-// is taken in a fixed order, so results are deterministic.
+// is taken in a fixed order, so results are deterministic.  The next
+// segment's M rows and S~ values are fetched into a second register set while
+// the current product runs.
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
@@ -25,8 +27,27 @@ namespace {
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 constexpr int kCols = 16;            // columns per workgroup
-constexpr int kSlices = kD / kCols;  // workgroups per head
 constexpr int kThreads = 256;        // 4 waves x 32 output rows
+
+// One segment's operands as this lane uses them: its two M row pieces
+// (32 contiguous floats each) and the S~ values its accumulators start from.
+struct SegOps {
+  float4 a[2][8];
+  float st[2][4];
+};
+
+__device__ __forceinline__ void load_seg(SegOps& x, const float* __restrict__ M, const float* __restrict__ S_tilde,
+                                         int64_t base, int wave, int q, int n, int c0) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const float* arow = M + base + int64_t(wave * 32 + t * 16 + n) * kD + 32 * q;
+#pragma unroll
+    for (int s4 = 0; s4 < 8; ++s4) x.a[t][s4] = ld_f4(arow + 4 * s4);
+    const int row = wave * 32 + t * 16 + 4 * q;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x.st[t][e] = S_tilde[base + int64_t(row + e) * kD + c0 + n];
+  }
+}
 
 __global__ __launch_bounds__(kThreads) void kda_compose_kernel(const float* __restrict__ M,
                                                                const float* __restrict__ S_tilde,
@@ -57,8 +78,8 @@ __global__ __launch_bounds__(kThreads) void kda_compose_kernel(const float* __re
   }
   __syncthreads();
 
-  for (int i = 0; i <= n_seg; ++i) {
-    // publish S_in(i) (S_final for i == n_seg) from LDS
+  // publish S_in(i) (S_final for i == n_seg) from LDS
+  auto publish = [&](int i) {
     float* dst = (i < n_seg) ? S_in + (int64_t(i) * H + h) * tile : S_final ? S_final + h * tile : nullptr;
     if (dst != nullptr) {
       for (int e = tid; e < kD * kCols / 4; e += kThreads) {
@@ -66,28 +87,22 @@ __global__ __launch_bounds__(kThreads) void kda_compose_kernel(const float* __re
         st_f4(dst + int64_t(r) * kD + c0 + c4, make_float4(curT[c4][r], curT[c4 + 1][r], curT[c4 + 2][r], curT[c4 + 3][r]));
       }
     }
-    if (i == n_seg) break;
-    const int64_t base = (int64_t(i) * H + h) * tile;
+  };
+  // S_in(i+1) = M(i) S_in(i) + S~(i) into curT, from operands x
+  auto advance = [&](const SegOps& x) {
     f32x4v acc[2][2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int row = wave * 32 + t * 16 + 4 * q;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[t][0][e] = S_tilde[base + int64_t(row + e) * kD + c0 + n];
+      acc[t][0] = f32x4v{x.st[t][0], x.st[t][1], x.st[t][2], x.st[t][3]};
       acc[t][1] = f32x4v{0.f, 0.f, 0.f, 0.f};
     }
-    // B operand: column n of S_in(i), rows 32q .. 32q+31
-    const float* bcol = &curT[n][32 * q];
-    const float* arow0 = M + base + int64_t(wave * 32 + n) * kD + 32 * q;
-    const float* arow1 = arow0 + 16 * kD;
+    const float* bcol = &curT[n][32 * q];  // column n of S_in(i), rows 32q .. 32q+31
 #pragma unroll
     for (int s4 = 0; s4 < 8; ++s4) {
       const float4 b = *reinterpret_cast<const float4*>(bcol + 4 * s4);
-      const float4 a0 = ld_f4(arow0 + 4 * s4);
-      const float4 a1 = ld_f4(arow1 + 4 * s4);
       const float bv[4] = {b.x, b.y, b.z, b.w};
-      const float av0[4] = {a0.x, a0.y, a0.z, a0.w};
-      const float av1[4] = {a1.x, a1.y, a1.z, a1.w};
+      const float av0[4] = {x.a[0][s4].x, x.a[0][s4].y, x.a[0][s4].z, x.a[0][s4].w};
+      const float av1[4] = {x.a[1][s4].x, x.a[1][s4].y, x.a[1][s4].z, x.a[1][s4].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         acc[0][e & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av0[e], bv[e], acc[0][e & 1], 0, 0, 0);
@@ -102,7 +117,25 @@ __global__ __launch_bounds__(kThreads) void kda_compose_kernel(const float* __re
       *reinterpret_cast<float4*>(&curT[n][row]) = make_float4(v[0], v[1], v[2], v[3]);
     }
     __syncthreads();
+  };
+
+  // Segment i's operands are loaded while segment i - 1 is composed (two
+  // register sets used alternately; indices past the last segment repeat it).
+  SegOps A, B;
+  const int last = n_seg > 0 ? n_seg - 1 : 0;
+  if (n_seg > 0) load_seg(A, M, S_tilde, (int64_t(0) * H + h) * tile, wave, q, n, c0);
+  int i = 0;
+  while (i < n_seg) {
+    publish(i);
+    load_seg(B, M, S_tilde, (int64_t(i + 1 <= last ? i + 1 : last) * H + h) * tile, wave, q, n, c0);
+    advance(A);
+    if (++i >= n_seg) break;
+    publish(i);
+    load_seg(A, M, S_tilde, (int64_t(i + 1 <= last ? i + 1 : last) * H + h) * tile, wave, q, n, c0);
+    advance(B);
+    ++i;
   }
+  publish(n_seg);
 }
 
 }  // namespace
