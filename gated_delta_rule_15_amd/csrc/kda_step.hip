@@ -16,10 +16,11 @@
 // half) and columns 4cg .. 4cg+3 of the slice, so one load instruction of a
 // wave covers eight full 128-byte row segments.  The column sums r = S~^T k,
 // s = S~^T q and q . k run in-thread over 8 rows, then across the wave's 8 row
-// groups in registers (a DPP row rotation by 8 lanes and the 16- and 32-lane
-// permute-swaps, each a butterfly whose two partners add the same two values),
-// then across the slice's two waves through one float2 LDS read per value,
-// summed in wave order.  Every lane of a column ends with the same sums.
+// groups in registers as a reduce-scatter (each 32- and 16-lane permute-swap
+// and the DPP rotation by 8 lanes pairs two different values, so every sum is
+// formed once, in one lane), then across the slice's two waves through LDS,
+// summed in wave order, and an all-gather hands every lane of a column the
+// same sums.
 //
 // Per-token inputs: decode loads them straight from memory; verify and commit
 // stage blocks of 8 tokens in LDS (k, scale * q and alpha = exp(g) as fp32,
@@ -91,13 +92,109 @@ struct __align__(16) Red {
   float x[2][kSlicesPerWg][kCG][9][kWavesPerSlice];
 };
 
-// Sum over the 8 row groups of a wave (lane bits 3..5).
-__device__ __forceinline__ float rowgroup_sum(float x) {
-  x = x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));  // row_ror:8
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);  // rows 2m and 2m+1 of 16 lanes
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);  // lanes 0..31 and 32..63
+// Lane exchanges for the column sums over a wave's 8 row groups (lane bits
+// 3..5).  swap32 / swap16 exchange, between two registers, the upper 32 lanes
+// of the first with the lower 32 lanes of the second (v_permlane32_swap), or
+// the odd 16-lane rows of the first with the even rows of the second
+// (v_permlane16_swap); ror8 reads lane l ^ 8 within each 16-lane row.
+__device__ __forceinline__ void swap32(float& x, float& y) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  x = __uint_as_float(r[0]);
+  y = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap16(float& x, float& y) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  x = __uint_as_float(r[0]);
+  y = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float ror8(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+}
+
+// Column sums of NV per-lane partials (NV = 9: r0..r3, s0..s3, q.k; NV = 4:
+// r0..r3) over the wave's 8 row groups and then the slice's waves, returned
+// in every lane of the column group.  Reduce-scatter: at each lane bit a swap
+// pairs two different values, so each sum is formed once, in one lane (the
+// lane whose row-group bits (b5, b4, b3) = idx bits (0, 1, 2)); the partials
+// of the slice's waves are added through LDS in wave order; an all-gather
+// then hands every lane all sums.  The tree is the same for both NV (r's are
+// summed identically), so decode, verify and commit agree bit for bit.
+template <int NV>
+__device__ __forceinline__ void column_sums(float (&v)[NV], float (*red)[9][kWavesPerSlice], int lane, int ws,
+                                            int cg) {
+  const bool b3 = (lane >> 3) & 1;
+  const int idx = ((lane >> 5) & 1) | (((lane >> 4) & 1) << 1) | (int(b3) << 2);
+  // bit 5: (v0, v1) (v2, v3) [(v4, v5) (v6, v7)]
+  swap32(v[0], v[1]);
+  swap32(v[2], v[3]);
+  float z01 = v[0] + v[1], z23 = v[2] + v[3];
+  float z45 = 0.0f, z67 = 0.0f, qk = 0.0f;
+  if constexpr (NV == 9) {
+    swap32(v[4], v[5]);
+    swap32(v[6], v[7]);
+    z45 = v[4] + v[5];
+    z67 = v[6] + v[7];
+    float t = v[8];
+    swap32(v[8], t);
+    qk = v[8] + t;
+  }
+  // bit 4: (z01, z23) [(z45, z67)]
+  swap16(z01, z23);
+  const float w0123 = z01 + z23;
+  float w4567 = 0.0f;
+  if constexpr (NV == 9) {
+    swap16(z45, z67);
+    w4567 = z45 + z67;
+    float t = qk;
+    swap16(qk, t);
+    qk = qk + t;
+  }
+  // bit 3: lanes with b3 = 0 keep v[idx] of w0123, b3 = 1 of w4567 (NV = 9)
+  float f;
+  if constexpr (NV == 9) {
+    const float mine = b3 ? w4567 : w0123;
+    const float other = b3 ? w0123 : w4567;
+    f = mine + ror8(other);
+    qk = qk + ror8(qk);
+  } else {
+    f = w0123 + ror8(w0123);  // both b3 lanes form v[idx & 3]
+  }
+  // across the slice's waves
+  if constexpr (kWavesPerSlice == 2) {
+    if (NV == 9 || !b3) red[cg][NV == 9 ? idx : (idx & 3)][ws] = f;
+    if (NV == 9 && (lane >> 3) == 0) red[cg][8][ws] = qk;
+    __syncthreads();
+    const float2 w = *reinterpret_cast<const float2*>(&red[cg][NV == 9 ? idx : (idx & 3)][0]);
+    f = w.x + w.y;
+    if constexpr (NV == 9) {
+      const float2 u = *reinterpret_cast<const float2*>(&red[cg][8][0]);
+      qk = u.x + u.y;
+    }
+  }
+  // all-gather: bit 3, then 4, then 5
+  float g[2];
+  if constexpr (NV == 9) {
+    const float fp = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(f), 0x128, 0xF, 0xF, false));
+    g[0] = b3 ? fp : f;  // v[b5 + 2 b4]
+    g[1] = b3 ? f : fp;  // v[b5 + 2 b4 + 4]
+  } else {
+    g[0] = f;
+    g[1] = 0.0f;
+  }
+  constexpr int NG = NV == 9 ? 2 : 1;
+#pragma unroll
+  for (int j = 0; j < NG; ++j) {
+    float h0 = g[j], h2 = g[j];
+    swap16(h0, h2);  // h0: b4 = 0 value, h2: b4 = 1 value
+    float h1 = h0, h3 = h2;
+    swap32(h0, h1);  // h0: b5 = 0, h1: b5 = 1
+    swap32(h2, h3);
+    v[4 * j + 0] = h0;
+    v[4 * j + 1] = h1;
+    v[4 * j + 2] = h2;
+    v[4 * j + 3] = h3;
+  }
+  if constexpr (NV == 9) v[8] = qk;
 }
 
 template <class InT, bool READOUT>
@@ -204,20 +301,7 @@ __device__ __forceinline__ void token_step(float (&S)[kR][4], const TokenVals& x
     }
     if constexpr (READOUT) acc[8] = fmaf(x.qs[i], x.k[i], acc[8]);           // q . k
   }
-#pragma unroll
-  for (int e = 0; e < NV; ++e) acc[e] = rowgroup_sum(acc[e]);
-  if constexpr (kWavesPerSlice == 2) {
-    if (lane < kCG) {
-#pragma unroll
-      for (int e = 0; e < NV; ++e) red[cg][e][ws] = acc[e];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < NV; ++e) {
-      const float2 w = *reinterpret_cast<const float2*>(&red[cg][e][0]);
-      acc[e] = w.x + w.y;
-    }
-  }
+  column_sums<NV>(acc, red, lane, ws, cg);
   float u[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) u[j] = x.beta * (x.v[j] - acc[j]);
