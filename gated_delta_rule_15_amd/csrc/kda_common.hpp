@@ -14,17 +14,16 @@ constexpr int kD = 128;  // d_k = d_v handled by every kernel
 __device__ __forceinline__ float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xFFFF0000u); }
 
-// Round to nearest, ties to even.  NaN inputs map to a quiet NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return 0x7FC0u;
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest, ties to even, two values per instruction
+// (gfx950 v_cvt_pk_bf16_f32; NaN stays NaN).  a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2_t h = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, h);
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return f32_to_bf16_rne(a) | (f32_to_bf16_rne(b) << 16);
-}
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) { return pack_bf16x2(x, 0.0f) & 0xFFFFu; }
 
 // ---------------------------------------------------------------------------
 // Element-type traits for q/k/v/o.

@@ -87,9 +87,12 @@ struct __align__(16) Stage {
   float beta[kBlockT];
 };
 
-// Cross-wave partial sums: [buffer][slice][column group][value][wave of the slice].
+// Cross-wave partial sums: [buffer][slice][column group][value][wave of the
+// slice]; 9 values padded to 10 so that a column group's partials start on a
+// 16-byte boundary.
+constexpr int kRedVals = 10;
 struct __align__(16) Red {
-  float x[2][kSlicesPerWg][kCG][9][kWavesPerSlice];
+  float x[2][kSlicesPerWg][kCG][kRedVals][kWavesPerSlice];
 };
 
 // Lane exchanges for the column sums over a wave's 8 row groups (lane bits
@@ -115,13 +118,16 @@ __device__ __forceinline__ float ror8(float x) {
 // r0..r3) over the wave's 8 row groups and then the slice's waves, returned
 // in every lane of the column group.  Reduce-scatter: at each lane bit a swap
 // pairs two different values, so each sum is formed once, in one lane (the
-// lane whose row-group bits (b5, b4, b3) = idx bits (0, 1, 2)); the partials
-// of the slice's waves are added through LDS in wave order; an all-gather
-// then hands every lane all sums.  The tree is the same for both NV (r's are
-// summed identically), so decode, verify and commit agree bit for bit.
+// lane whose row-group bits (b5, b4, b3) = idx bits (0, 1, 2)).  With two
+// waves per slice each lane then writes its one partial to LDS and, after the
+// barrier, every lane reads both waves' partials of its column group and adds
+// them in wave order; with one wave per slice an all-gather in registers hands
+// every lane the sums.  need_s (wave-uniform): s and q.k are wanted in this
+// wave; otherwise only r is returned.  The tree is the same for both NV (r's
+// are summed identically), so decode, verify and commit agree bit for bit.
 template <int NV>
-__device__ __forceinline__ void column_sums(float (&v)[NV], float (*red)[9][kWavesPerSlice], int lane, int ws,
-                                            int cg) {
+__device__ __forceinline__ void column_sums(float (&v)[NV], float (*red)[kRedVals][kWavesPerSlice], int lane, int ws,
+                                            int cg, bool need_s) {
   const bool b3 = (lane >> 3) & 1;
   const int idx = ((lane >> 5) & 1) | (((lane >> 4) & 1) << 1) | (int(b3) << 2);
   // bit 5: (v0, v1) (v2, v3) [(v4, v5) (v6, v7)]
@@ -159,42 +165,53 @@ __device__ __forceinline__ void column_sums(float (&v)[NV], float (*red)[9][kWav
   } else {
     f = w0123 + ror8(w0123);  // both b3 lanes form v[idx & 3]
   }
-  // across the slice's waves
   if constexpr (kWavesPerSlice == 2) {
     if (NV == 9 || !b3) red[cg][NV == 9 ? idx : (idx & 3)][ws] = f;
     if (NV == 9 && (lane >> 3) == 0) red[cg][8][ws] = qk;
     __syncthreads();
-    const float2 w = *reinterpret_cast<const float2*>(&red[cg][NV == 9 ? idx : (idx & 3)][0]);
-    f = w.x + w.y;
+    const float4* p = reinterpret_cast<const float4*>(&red[cg][0][0]);  // [value][wave] pairs
+    const float4 r01 = p[0], r23 = p[1];
+    v[0] = r01.x + r01.y;
+    v[1] = r01.z + r01.w;
+    v[2] = r23.x + r23.y;
+    v[3] = r23.z + r23.w;
     if constexpr (NV == 9) {
-      const float2 u = *reinterpret_cast<const float2*>(&red[cg][8][0]);
-      qk = u.x + u.y;
+      if (need_s) {
+        const float4 s01 = p[2], s23 = p[3];
+        const float2 qq = *reinterpret_cast<const float2*>(&red[cg][8][0]);
+        v[4] = s01.x + s01.y;
+        v[5] = s01.z + s01.w;
+        v[6] = s23.x + s23.y;
+        v[7] = s23.z + s23.w;
+        v[8] = qq.x + qq.y;
+      }
     }
-  }
-  // all-gather: bit 3, then 4, then 5
-  float g[2];
-  if constexpr (NV == 9) {
-    const float fp = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(f), 0x128, 0xF, 0xF, false));
-    g[0] = b3 ? fp : f;  // v[b5 + 2 b4]
-    g[1] = b3 ? f : fp;  // v[b5 + 2 b4 + 4]
   } else {
-    g[0] = f;
-    g[1] = 0.0f;
-  }
-  constexpr int NG = NV == 9 ? 2 : 1;
+    // all-gather: bit 3, then 4, then 5
+    float g[2];
+    if constexpr (NV == 9) {
+      const float fp = ror8(f);
+      g[0] = b3 ? fp : f;  // v[b5 + 2 b4]
+      g[1] = b3 ? f : fp;  // v[b5 + 2 b4 + 4]
+    } else {
+      g[0] = f;
+      g[1] = 0.0f;
+    }
+    constexpr int NG = NV == 9 ? 2 : 1;
 #pragma unroll
-  for (int j = 0; j < NG; ++j) {
-    float h0 = g[j], h2 = g[j];
-    swap16(h0, h2);  // h0: b4 = 0 value, h2: b4 = 1 value
-    float h1 = h0, h3 = h2;
-    swap32(h0, h1);  // h0: b5 = 0, h1: b5 = 1
-    swap32(h2, h3);
-    v[4 * j + 0] = h0;
-    v[4 * j + 1] = h1;
-    v[4 * j + 2] = h2;
-    v[4 * j + 3] = h3;
+    for (int j = 0; j < NG; ++j) {
+      float h0 = g[j], h2 = g[j];
+      swap16(h0, h2);  // h0: b4 = 0 value, h2: b4 = 1 value
+      float h1 = h0, h3 = h2;
+      swap32(h0, h1);  // h0: b5 = 0, h1: b5 = 1
+      swap32(h2, h3);
+      v[4 * j + 0] = h0;
+      v[4 * j + 1] = h1;
+      v[4 * j + 2] = h2;
+      v[4 * j + 3] = h3;
+    }
+    if constexpr (NV == 9) v[8] = qk;
   }
-  if constexpr (NV == 9) v[8] = qk;
 }
 
 template <class InT, bool READOUT>
@@ -283,10 +300,11 @@ __device__ __forceinline__ void stage_block(Stage& st, const StepArgs& a, int n,
 
 // One token on this lane's 8 x 4 block of S.  red: this slice's [cg][value][2]
 // partials in the current buffer; ws: the wave's index within its slice.
-// Returns o at the lane's 4 columns when READOUT.
+// Returns o at the lane's 4 columns when READOUT and need_o (wave-uniform).
 template <bool READOUT>
-__device__ __forceinline__ void token_step(float (&S)[kR][4], const TokenVals& x, float (*red)[9][kWavesPerSlice], int lane,
-                                           int ws, int cg, float (&o)[4]) {
+__device__ __forceinline__ void token_step(float (&S)[kR][4], const TokenVals& x,
+                                           float (*red)[kRedVals][kWavesPerSlice], int lane, int ws, int cg,
+                                           bool need_o, float (&o)[4]) {
   constexpr int NV = READOUT ? 9 : 4;
   float acc[NV];
 #pragma unroll
@@ -301,7 +319,7 @@ __device__ __forceinline__ void token_step(float (&S)[kR][4], const TokenVals& x
     }
     if constexpr (READOUT) acc[8] = fmaf(x.qs[i], x.k[i], acc[8]);           // q . k
   }
-  column_sums<NV>(acc, red, lane, ws, cg);
+  column_sums<NV>(acc, red, lane, ws, cg, need_o);
   float u[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) u[j] = x.beta * (x.v[j] - acc[j]);
@@ -311,8 +329,10 @@ __device__ __forceinline__ void token_step(float (&S)[kR][4], const TokenVals& x
     for (int j = 0; j < 4; ++j) S[i][j] = fmaf(x.k[i], u[j], S[i][j]);     // S = S~ + k u^T
   }
   if constexpr (READOUT) {
+    if (need_o) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = fmaf(acc[8], u[j], acc[4 + j]);     // o = s + (q.k) u
+      for (int j = 0; j < 4; ++j) o[j] = fmaf(acc[8], u[j], acc[4 + j]);   // o = s + (q.k) u
+    }
   }
 }
 
@@ -356,7 +376,7 @@ __global__ __launch_bounds__(kThreads) void kda_step_kernel(StepArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ws = wave % kWavesPerSlice;  // wave within its slice: rows kRowsPerWave * ws ..
   const int sl = wave / kWavesPerSlice;  // slice within the workgroup's columns
   const int cg = lane % kCG;
@@ -390,7 +410,8 @@ __global__ __launch_bounds__(kThreads) void kda_step_kernel(StepArgs a) {
       S[j][i][0] = w.x; S[j][i][1] = w.y; S[j][i][2] = w.z; S[j][i][3] = w.w;
     }
 
-  const bool writer = (ws == 0 && rg == 0 && a.o != nullptr);
+  const bool out_wave = (ws == 0 && a.o != nullptr);  // wave-uniform: forms o
+  const bool writer = out_wave && rg == 0;
   const int last = steps > 0 ? steps - 1 : 0;
   int c = 0;  // token steps so far (alternates the reduction buffers)
   for (int b0 = 0; b0 < steps; b0 += kBlockT) {
@@ -405,7 +426,7 @@ __global__ __launch_bounds__(kThreads) void kda_step_kernel(StepArgs a) {
           TokenVals x;
           float o[4];
           read_token(x, st, t, row0, j * kWgCols + wcol, READOUT);
-          token_step<READOUT>(S[j], x, red.x[c & 1][sl], lane, ws, cg, o);
+          token_step<READOUT>(S[j], x, red.x[c & 1][sl], lane, ws, cg, out_wave, o);
           ++c;
           if constexpr (READOUT) {
             if (writer)
@@ -440,7 +461,7 @@ __global__ __launch_bounds__(kThreads) void kda_decode_kernel(StepArgs a, int n_
   __shared__ Red red;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ws = wave % kWavesPerSlice;
   const int sl = wave / kWavesPerSlice;
   const int cg = lane % kCG;
@@ -472,11 +493,12 @@ __global__ __launch_bounds__(kThreads) void kda_decode_kernel(StepArgs a, int n_
     }
     load_token<InT, true>(x[j], a, n, 0, h, row0, col);
   }
-  const bool writer = (ws == 0 && rg == 0 && a.o != nullptr);
+  const bool out_wave = (ws == 0 && a.o != nullptr);  // wave-uniform: forms o
+  const bool writer = out_wave && rg == 0;
 #pragma unroll
   for (int j = 0; j < kDecodeTiles; ++j) {
     float o[4];
-    token_step<true>(S[j], x[j], red.x[j & 1][sl], lane, ws, cg, o);
+    token_step<true>(S[j], x[j], red.x[j & 1][sl], lane, ws, cg, out_wave, o);
     if (valid[j]) {
       if (writer) InT::store4(a.o, ooff[j], o);
 #pragma unroll
