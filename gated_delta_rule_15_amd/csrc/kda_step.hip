@@ -76,6 +76,7 @@ struct StepArgs {
 struct TokenVals {
   float k[kR], qs[kR], alpha[kR], v[4];
   float beta;
+  float qk;  // scale * q . k, when staged
 };
 
 // Staged inputs of up to kBlockT tokens (verify / commit).
@@ -85,7 +86,14 @@ struct __align__(16) Stage {
   float alpha[kBlockT][kD];  // exp(g)
   float v[kBlockT][kWgCols * kBlockHalves];  // v of the workgroup's columns
   float beta[kBlockT];
+  float qk[kBlockT];         // scale * q . k
 };
+
+// Verify stages q . k per token (formed once per workgroup instead of in
+// every lane), by the same arithmetic as the in-lane form of the decode step:
+// a sequential fma chain over each 8-channel group, then the groups summed
+// by the same tree.  Needs 8 rows per lane.
+constexpr bool kStageQK = (kR == 8);
 
 // Cross-wave partial sums: [buffer][slice][column group][value][wave of the
 // slice]; 9 values padded to 10 so that a column group's partials start on a
@@ -114,20 +122,24 @@ __device__ __forceinline__ float ror8(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
 }
 
-// Column sums of NV per-lane partials (NV = 9: r0..r3, s0..s3, q.k; NV = 4:
-// r0..r3) over the wave's 8 row groups and then the slice's waves, returned
-// in every lane of the column group.  Reduce-scatter: at each lane bit a swap
-// pairs two different values, so each sum is formed once, in one lane (the
-// lane whose row-group bits (b5, b4, b3) = idx bits (0, 1, 2)).  With two
-// waves per slice each lane then writes its one partial to LDS and, after the
-// barrier, every lane reads both waves' partials of its column group and adds
-// them in wave order; with one wave per slice an all-gather in registers hands
-// every lane the sums.  need_s (wave-uniform): s and q.k are wanted in this
-// wave; otherwise only r is returned.  The tree is the same for both NV (r's
-// are summed identically), so decode, verify and commit agree bit for bit.
+// Column sums of NV per-lane partials (NV = 9: r0..r3, s0..s3, q.k; NV = 8:
+// r, s; NV = 4: r) over the wave's 8 row groups and then the slice's waves,
+// returned in every lane of the column group.  Reduce-scatter: at each lane
+// bit a swap pairs two different values, so each sum is formed once, in one
+// lane (the lane whose row-group bits (b5, b4, b3) = idx bits (0, 1, 2)); q.k
+// is summed by a butterfly (rows paired across bit 5, then 4, then 3).  With
+// two waves per slice each lane then writes its one partial to LDS and, after
+// the barrier, every lane reads both waves' partials of its column group and
+// adds them in wave order; with one wave per slice an all-gather in registers
+// hands every lane the sums.  need_s (wave-uniform): s and q.k are wanted in
+// this wave; otherwise only r is returned.  The tree is the same for every NV
+// (r's are summed identically), so decode, verify and commit agree bit for
+// bit.
 template <int NV>
 __device__ __forceinline__ void column_sums(float (&v)[NV], float (*red)[kRedVals][kWavesPerSlice], int lane, int ws,
                                             int cg, bool need_s) {
+  constexpr bool HAS_S = NV >= 8;
+  constexpr bool HAS_QK = NV == 9;
   const bool b3 = (lane >> 3) & 1;
   const int idx = ((lane >> 5) & 1) | (((lane >> 4) & 1) << 1) | (int(b3) << 2);
   // bit 5: (v0, v1) (v2, v3) [(v4, v5) (v6, v7)]
@@ -135,39 +147,43 @@ __device__ __forceinline__ void column_sums(float (&v)[NV], float (*red)[kRedVal
   swap32(v[2], v[3]);
   float z01 = v[0] + v[1], z23 = v[2] + v[3];
   float z45 = 0.0f, z67 = 0.0f, qk = 0.0f;
-  if constexpr (NV == 9) {
+  if constexpr (HAS_S) {
     swap32(v[4], v[5]);
     swap32(v[6], v[7]);
     z45 = v[4] + v[5];
     z67 = v[6] + v[7];
-    float t = v[8];
-    swap32(v[8], t);
-    qk = v[8] + t;
+  }
+  if constexpr (HAS_QK) {
+    float t = v[NV - 1];
+    swap32(v[NV - 1], t);
+    qk = v[NV - 1] + t;
   }
   // bit 4: (z01, z23) [(z45, z67)]
   swap16(z01, z23);
   const float w0123 = z01 + z23;
   float w4567 = 0.0f;
-  if constexpr (NV == 9) {
+  if constexpr (HAS_S) {
     swap16(z45, z67);
     w4567 = z45 + z67;
+  }
+  if constexpr (HAS_QK) {
     float t = qk;
     swap16(qk, t);
     qk = qk + t;
   }
-  // bit 3: lanes with b3 = 0 keep v[idx] of w0123, b3 = 1 of w4567 (NV = 9)
+  // bit 3: lanes with b3 = 0 keep v[idx] of w0123, b3 = 1 of w4567 (with s)
   float f;
-  if constexpr (NV == 9) {
+  if constexpr (HAS_S) {
     const float mine = b3 ? w4567 : w0123;
     const float other = b3 ? w0123 : w4567;
     f = mine + ror8(other);
-    qk = qk + ror8(qk);
   } else {
     f = w0123 + ror8(w0123);  // both b3 lanes form v[idx & 3]
   }
+  if constexpr (HAS_QK) qk = qk + ror8(qk);
   if constexpr (kWavesPerSlice == 2) {
-    if (NV == 9 || !b3) red[cg][NV == 9 ? idx : (idx & 3)][ws] = f;
-    if (NV == 9 && (lane >> 3) == 0) red[cg][8][ws] = qk;
+    if (HAS_S || !b3) red[cg][HAS_S ? idx : (idx & 3)][ws] = f;
+    if (HAS_QK && (lane >> 3) == 0) red[cg][8][ws] = qk;
     __syncthreads();
     const float4* p = reinterpret_cast<const float4*>(&red[cg][0][0]);  // [value][wave] pairs
     const float4 r01 = p[0], r23 = p[1];
@@ -175,21 +191,23 @@ __device__ __forceinline__ void column_sums(float (&v)[NV], float (*red)[kRedVal
     v[1] = r01.z + r01.w;
     v[2] = r23.x + r23.y;
     v[3] = r23.z + r23.w;
-    if constexpr (NV == 9) {
+    if constexpr (HAS_S) {
       if (need_s) {
         const float4 s01 = p[2], s23 = p[3];
-        const float2 qq = *reinterpret_cast<const float2*>(&red[cg][8][0]);
         v[4] = s01.x + s01.y;
         v[5] = s01.z + s01.w;
         v[6] = s23.x + s23.y;
         v[7] = s23.z + s23.w;
-        v[8] = qq.x + qq.y;
+        if constexpr (HAS_QK) {
+          const float2 qq = *reinterpret_cast<const float2*>(&red[cg][8][0]);
+          v[8] = qq.x + qq.y;
+        }
       }
     }
   } else {
     // all-gather: bit 3, then 4, then 5
     float g[2];
-    if constexpr (NV == 9) {
+    if constexpr (HAS_S) {
       const float fp = ror8(f);
       g[0] = b3 ? fp : f;  // v[b5 + 2 b4]
       g[1] = b3 ? f : fp;  // v[b5 + 2 b4 + 4]
@@ -197,7 +215,7 @@ __device__ __forceinline__ void column_sums(float (&v)[NV], float (*red)[kRedVal
       g[0] = f;
       g[1] = 0.0f;
     }
-    constexpr int NG = NV == 9 ? 2 : 1;
+    constexpr int NG = HAS_S ? 2 : 1;
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
       float h0 = g[j], h2 = g[j];
@@ -210,7 +228,7 @@ __device__ __forceinline__ void column_sums(float (&v)[NV], float (*red)[kRedVal
       v[4 * j + 2] = h2;
       v[4 * j + 3] = h3;
     }
-    if constexpr (NV == 9) v[8] = qk;
+    if constexpr (HAS_QK) v[8] = qk;
   }
 }
 
@@ -235,6 +253,7 @@ __device__ __forceinline__ void load_token(TokenVals& x, const StepArgs& a, int 
   }
   InT::unpack4(InT::load4raw(a.v, vec + col), x.v);
   x.beta = a.beta[tok];
+  x.qk = 0.0f;  // formed in the step
 }
 
 __device__ __forceinline__ void read_token(TokenVals& x, const Stage& st, int t, int row0, int wcol, bool readout) {
@@ -254,58 +273,93 @@ __device__ __forceinline__ void read_token(TokenVals& x, const Stage& st, int t,
   const float4 v = *reinterpret_cast<const float4*>(&st.v[t][wcol]);
   x.v[0] = v.x; x.v[1] = v.y; x.v[2] = v.z; x.v[3] = v.w;
   x.beta = st.beta[t];
+  x.qk = (readout && kStageQK) ? st.qk[t] : 0.0f;
 }
 
 // Stage tokens b0 .. b0 + kBlockT - 1 (indices past `last` repeat `last`).
-// Thread tid owns channel group tid % 32 of token tid / 32 for k, q and g, and
-// (threads 0..127) column group tid % 16 of token tid / 16 for v: every load
-// is issued before the first LDS store.
+// Threads of the first half own 8 channels (one group of 8 rows of the step's
+// lane layout) of token tid / 16 for k, q and g, and form q . k; threads of
+// the second half own column group u % 16 of token u / 16 (u = tid - 128) for
+// v.  Every load is issued before the first LDS store.
+template <int XOR>
+__device__ __forceinline__ float xor_lane(float x) {  // lane ^ XOR within 32 lanes (XOR < 32)
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x1F | (XOR << 10)));
+}
+
 template <class InT, bool READOUT>
 __device__ __forceinline__ void stage_block(Stage& st, const StepArgs& a, int n, int h, int col0, int b0, int last,
                                             int tid) {
-  static_assert(kBlockT * 32 == kThreads, "one 4-channel group of one token per thread");
-  const int t = tid >> 5, c4 = 4 * (tid & 31);
-  const int tt = b0 + t <= last ? b0 + t : last;
-  const int64_t vec = ((int64_t(n) * a.G + tt) * a.H + h) * kD;
-  const auto kr = InT::load4raw(a.k, vec + c4);
-  const float4 g = ld_f4(a.g + vec + c4);
-  typename InT::raw4 qr{};
-  if constexpr (READOUT) qr = InT::load4raw(a.q, vec + c4);
+  static_assert(kBlockT * 16 == kThreads / 2, "8 channels of one token per thread in the first half");
   constexpr int kVPieces = kWgCols * kBlockHalves / 4;  // v pieces per token
-  const int tv = tid / kVPieces, cv = 4 * (tid % kVPieces);
-  const int ttv = b0 + tv <= last ? b0 + tv : last;
-  typename InT::raw4 vr{};
-  if (tid < kBlockT * kVPieces) vr = InT::load4raw(a.v, ((int64_t(n) * a.G + ttv) * a.H + h) * kD + col0 + cv);
-  float beta = 0.0f;
-  if (tid < kBlockT) beta = a.beta[(int64_t(n) * a.G + (b0 + tid <= last ? b0 + tid : last)) * a.H + h];
+  static_assert(kBlockT * kVPieces <= kThreads / 2, "v pieces fit the second half");
+  if (tid < kThreads / 2) {
+    const int t = tid >> 4, c8 = 8 * (tid & 15);
+    const int tt = b0 + t <= last ? b0 + t : last;
+    const int64_t vec = ((int64_t(n) * a.G + tt) * a.H + h) * kD + c8;
+    const auto k0 = InT::load4raw(a.k, vec);
+    const auto k1 = InT::load4raw(a.k, vec + 4);
+    const float4 g0 = ld_f4(a.g + vec);
+    const float4 g1 = ld_f4(a.g + vec + 4);
+    typename InT::raw4 q0{}, q1{};
+    if constexpr (READOUT) {
+      q0 = InT::load4raw(a.q, vec);
+      q1 = InT::load4raw(a.q, vec + 4);
+    }
+    float beta = 0.0f;
+    if (tid < kBlockT) beta = a.beta[(int64_t(n) * a.G + (b0 + tid <= last ? b0 + tid : last)) * a.H + h];
 
-  float f[4];
-  InT::unpack4(kr, f);
-  *reinterpret_cast<float4*>(&st.k[t][c4]) = make_float4(f[0], f[1], f[2], f[3]);
-  if constexpr (READOUT) {
-    InT::unpack4(qr, f);
+    float k[8];
+    InT::unpack4(k0, k);
+    InT::unpack4(k1, k + 4);
+    *reinterpret_cast<float4*>(&st.k[t][c8]) = make_float4(k[0], k[1], k[2], k[3]);
+    *reinterpret_cast<float4*>(&st.k[t][c8 + 4]) = make_float4(k[4], k[5], k[6], k[7]);
+    *reinterpret_cast<float4*>(&st.alpha[t][c8]) = make_float4(__expf(g0.x), __expf(g0.y), __expf(g0.z), __expf(g0.w));
+    *reinterpret_cast<float4*>(&st.alpha[t][c8 + 4]) = make_float4(__expf(g1.x), __expf(g1.y), __expf(g1.z), __expf(g1.w));
+    if constexpr (READOUT) {
+      float qs[8];
+      InT::unpack4(q0, qs);
+      InT::unpack4(q1, qs + 4);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) f[e] = f[e] * a.scale;
+      for (int e = 0; e < 8; ++e) qs[e] = qs[e] * a.scale;
+      *reinterpret_cast<float4*>(&st.qs[t][c8]) = make_float4(qs[0], qs[1], qs[2], qs[3]);
+      *reinterpret_cast<float4*>(&st.qs[t][c8 + 4]) = make_float4(qs[4], qs[5], qs[6], qs[7]);
+      if constexpr (kStageQK) {
+        // the decode step's q . k: fma chain over the group's 8 channels, then
+        // groups paired across channel-group bit 2, 1, 0, and 3 (the two waves)
+        float p = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p = fmaf(qs[e], k[e], p);
+        p = p + xor_lane<4>(p);
+        p = p + xor_lane<2>(p);
+        p = p + xor_lane<1>(p);
+        p = p + xor_lane<8>(p);
+        if ((tid & 15) == 0) st.qk[t] = p;
+      }
+    }
+    if (tid < kBlockT) st.beta[tid] = beta;
   } else {
-    f[0] = f[1] = f[2] = f[3] = 0.0f;
+    const int u = tid - kThreads / 2;
+    const int tv = u / kVPieces, cv = 4 * (u % kVPieces);
+    if (u < kBlockT * kVPieces) {
+      const int ttv = b0 + tv <= last ? b0 + tv : last;
+      const auto vr = InT::load4raw(a.v, ((int64_t(n) * a.G + ttv) * a.H + h) * kD + col0 + cv);
+      float f[4];
+      InT::unpack4(vr, f);
+      *reinterpret_cast<float4*>(&st.v[tv][cv]) = make_float4(f[0], f[1], f[2], f[3]);
+    }
   }
-  *reinterpret_cast<float4*>(&st.qs[t][c4]) = make_float4(f[0], f[1], f[2], f[3]);
-  *reinterpret_cast<float4*>(&st.alpha[t][c4]) = make_float4(__expf(g.x), __expf(g.y), __expf(g.z), __expf(g.w));
-  if (tid < kBlockT * kVPieces) {
-    InT::unpack4(vr, f);
-    *reinterpret_cast<float4*>(&st.v[tv][cv]) = make_float4(f[0], f[1], f[2], f[3]);
-  }
-  if (tid < kBlockT) st.beta[tid] = beta;
 }
 
 // One token on this lane's 8 x 4 block of S.  red: this slice's [cg][value][2]
 // partials in the current buffer; ws: the wave's index within its slice.
 // Returns o at the lane's 4 columns when READOUT and need_o (wave-uniform).
-template <bool READOUT>
+// QK_IN: x.qk holds the staged q . k; otherwise it is formed here.
+template <bool READOUT, bool QK_IN>
 __device__ __forceinline__ void token_step(float (&S)[kR][4], const TokenVals& x,
                                            float (*red)[kRedVals][kWavesPerSlice], int lane, int ws, int cg,
                                            bool need_o, float (&o)[4]) {
-  constexpr int NV = READOUT ? 9 : 4;
+  static_assert(!QK_IN || READOUT, "q . k is a readout term");
+  constexpr int NV = READOUT ? (QK_IN ? 8 : 9) : 4;
   float acc[NV];
 #pragma unroll
   for (int e = 0; e < NV; ++e) acc[e] = 0.0f;
@@ -317,7 +371,7 @@ __device__ __forceinline__ void token_step(float (&S)[kR][4], const TokenVals& x
       acc[j] = fmaf(x.k[i], S[i][j], acc[j]);                                // r = S~^T k
       if constexpr (READOUT) acc[4 + j] = fmaf(x.qs[i], S[i][j], acc[4 + j]);  // s = S~^T q
     }
-    if constexpr (READOUT) acc[8] = fmaf(x.qs[i], x.k[i], acc[8]);           // q . k
+    if constexpr (NV == 9) acc[8] = fmaf(x.qs[i], x.k[i], acc[8]);           // q . k
   }
   column_sums<NV>(acc, red, lane, ws, cg, need_o);
   float u[4];
@@ -330,8 +384,11 @@ __device__ __forceinline__ void token_step(float (&S)[kR][4], const TokenVals& x
   }
   if constexpr (READOUT) {
     if (need_o) {
+      float qk;
+      if constexpr (QK_IN) qk = x.qk;
+      else qk = acc[NV - 1];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) o[j] = fmaf(acc[8], u[j], acc[4 + j]);   // o = s + (q.k) u
+      for (int j = 0; j < 4; ++j) o[j] = fmaf(qk, u[j], acc[4 + j]);       // o = s + (q.k) u
     }
   }
 }
@@ -426,7 +483,7 @@ __global__ __launch_bounds__(kThreads) void kda_step_kernel(StepArgs a) {
           TokenVals x;
           float o[4];
           read_token(x, st, t, row0, j * kWgCols + wcol, READOUT);
-          token_step<READOUT>(S[j], x, red.x[c & 1][sl], lane, ws, cg, out_wave, o);
+          token_step<READOUT, READOUT && kStageQK>(S[j], x, red.x[c & 1][sl], lane, ws, cg, out_wave, o);
           ++c;
           if constexpr (READOUT) {
             if (writer)
@@ -498,7 +555,7 @@ __global__ __launch_bounds__(kThreads) void kda_decode_kernel(StepArgs a, int n_
 #pragma unroll
   for (int j = 0; j < kDecodeTiles; ++j) {
     float o[4];
-    token_step<true>(S[j], x[j], red.x[j & 1][sl], lane, ws, cg, out_wave, o);
+    token_step<true, false>(S[j], x[j], red.x[j & 1][sl], lane, ws, cg, out_wave, o);
     if (valid[j]) {
       if (writer) InT::store4(a.o, ooff[j], o);
 #pragma unroll
