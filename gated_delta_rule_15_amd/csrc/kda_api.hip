@@ -15,6 +15,15 @@ kda_status_t hip_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ER
 
 }  // namespace
 
+namespace kda {
+int device_cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+  return n;
+}
+}  // namespace kda
+
 namespace {
 
 kda_status_t prefill_impl(const void* q, const void* k, const void* v, const float* g, const float* beta,

@@ -6,6 +6,10 @@
 
 namespace kda {
 
+// Compute units of the current device (256 on MI355X; fewer in a partitioned
+// mode).  Queried per launch, nothing cached.
+int device_cu_count();
+
 // ---- decode / verify / commit (kda_step.hip) ------------------------------
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* g, const float* beta,
                          float* state, const int32_t* slots, int N, int H, bool bf16, float scale,

@@ -747,7 +747,7 @@ hipError_t launch_prefill(const PrefillLaunch& p, bool bf16, hipStream_t stream)
   // workgroup (4 state waves x 16 columns) and 8 prep waves, which shortens
   // the per-chunk critical path at the cost of preparing each chunk twice.
   const int64_t units = int64_t(p.num_seqs) * p.H * (p.transition_out ? 2 : 1);
-  const bool wide = units >= 256;
+  const bool wide = units >= device_cu_count();
   if (bf16)
     return wide ? launch_cfg<PolBF16x3, BF16, 4, 2, 4>(p, stream) : launch_cfg<PolBF16x3, BF16, 4, 1, 8>(p, stream);
   return wide ? launch_cfg<PolF32, F32, 4, 2, 4>(p, stream) : launch_cfg<PolF32, F32, 4, 1, 8>(p, stream);

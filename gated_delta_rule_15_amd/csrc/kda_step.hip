@@ -70,6 +70,7 @@ struct StepArgs {
   void* o;
   int32_t N, G, H;
   float scale;
+  int32_t layer_wgs;  // verify: workgroups per resident layer (the CU count); 0 = no staggering
 };
 
 // One token's inputs at this lane's 8 rows and 4 columns, as fp32.
@@ -457,6 +458,17 @@ __global__ __launch_bounds__(kThreads) void kda_step_kernel(StepArgs a) {
   const int64_t pool_row = a.slots ? int64_t(a.slots[n]) : int64_t(n);
   const int64_t tile = (pool_row * a.H + h) * int64_t(kD * kD);
   const float* Sin = a.state_in + tile;
+  if constexpr (MODE == kVerify) {
+    // Workgroups of the second and third resident layers (blockIdx / CUs = 1,
+    // 2) delay their state loads by ~1.3 us per layer, so that the first
+    // layer's loads complete early and its token steps overlap the later
+    // layers' loads; all layers otherwise wait for the whole state stream
+    // before the first step (measured on 32 x 12 x 8: verify 13.0 -> 12.4 us).
+    if (a.layer_wgs > 0) {
+      const int layer = min(int(blockIdx.x) / a.layer_wgs, 2);
+      for (int i = 0; i < layer; ++i) __builtin_amdgcn_s_sleep(48);
+    }
+  }
 
   float S[NH][kR][4];
 #pragma unroll
@@ -579,7 +591,7 @@ hipError_t launch_step(const StepArgs& a, bool bf16, hipStream_t stream) {
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* g, const float* beta,
                          float* state, const int32_t* slots, int N, int H, bool bf16, float scale, void* o,
                          hipStream_t stream) {
-  StepArgs a{q, k, v, g, beta, state, state, slots, nullptr, o, N, 1, H, scale};
+  StepArgs a{q, k, v, g, beta, state, state, slots, nullptr, o, N, 1, H, scale, 0};
   const int n_tiles = N * H * kWgPerHead;
   const unsigned blocks = unsigned((n_tiles + kDecodeTiles - 1) / kDecodeTiles);
   if (bf16)
@@ -592,14 +604,14 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const floa
 hipError_t launch_verify(const void* q, const void* k, const void* v, const float* g, const float* beta,
                          const float* state, const int32_t* slots, int N, int G, int H, bool bf16,
                          float scale, void* o, hipStream_t stream) {
-  StepArgs a{q, k, v, g, beta, state, nullptr, slots, nullptr, o, N, G, H, scale};
+  StepArgs a{q, k, v, g, beta, state, nullptr, slots, nullptr, o, N, G, H, scale, device_cu_count()};
   return launch_step<kVerify>(a, bf16, stream);
 }
 
 hipError_t launch_commit(const void* k, const void* v, const float* g, const float* beta,
                          const float* state_in, float* state_out, const int32_t* slots,
                          const int32_t* accepted_len, int N, int G, int H, bool bf16, hipStream_t stream) {
-  StepArgs a{nullptr, k, v, g, beta, state_in, state_out, slots, accepted_len, nullptr, N, G, H, 1.0f};
+  StepArgs a{nullptr, k, v, g, beta, state_in, state_out, slots, accepted_len, nullptr, N, G, H, 1.0f, 0};
   return launch_step<kCommit>(a, bf16, stream);
 }
 
