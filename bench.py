@@ -373,7 +373,7 @@ def main():
     traffic = traffic_from_profile(khash)
     roof = dict(bound="hbm", achieved=round(dec["gbps"], 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                 frac=round(dec["gbps"] / HBM_PEAK_GBPS, 4), traffic=traffic,
-                kernel="kda_step_kernel<decode>", algorithmic_bytes_per_launch=dec["bytes"],
+                kernel="kda_decode_kernel<BF16>", algorithmic_bytes_per_launch=dec["bytes"],
                 mean_launch_us=round(dec["ms"] * 1e3, 3))
     cpu = None
     if not args.no_cpu_baseline:

@@ -25,6 +25,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) { return pack_bf16x2(x, 0.0f) & 0xFFFFu; }
 
+// Raw buffer resource over [base, base + bytes) (gfx9 word 3: 32-bit data
+// format).  A raw buffer access takes a 32-bit per-lane offset, so a batch of
+// stores at constant distances needs one address register, not a 64-bit
+// pointer per store.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
 // ---------------------------------------------------------------------------
 // Element-type traits for q/k/v/o.
 // ---------------------------------------------------------------------------

@@ -261,16 +261,7 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
     }
   }
 
-  // Checkpoint rows of this sequence start after those of the earlier ones:
-  // a sequence of length L stores floor((L - 1) / interval) checkpoints.
   const bool ckpt_on = CKPT && !is_transition;
-  int ckpt_base = 0;
-  if (ckpt_on && is_state) {
-    for (int n = 0; n < seq; ++n) {
-      const int len = a.cu_seqlens[n + 1] - a.cu_seqlens[n];
-      ckpt_base += len > 0 ? (len - 1) / a.ckpt_interval : 0;
-    }
-  }
 
   // The two roles run separate loops (so each keeps only its own values in
   // registers) with the same three barriers per step.
@@ -450,13 +441,26 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
         if (CKPT && ckpt_on) {  // S is now the state after the sequence's first i * kC tokens
           const int pos = i * kC;
           if (pos % a.ckpt_interval == 0 && pos < eos - bos) {
-            float* dst = a.checkpoints + (int64_t(ckpt_base + pos / a.ckpt_interval - 1) * H + h) * (kD * kD) + colw + lj;
+            // checkpoint rows of this sequence start after those of the earlier
+            // ones: a sequence of length L stores floor((L - 1) / interval).
+            // Summed here, where it is used, so that nothing stays live across
+            // the step loop.
+            int ckpt_base = 0;
+            for (int n = 0; n < seq; ++n) {
+              const int len = a.cu_seqlens[n + 1] - a.cu_seqlens[n];
+              ckpt_base += len > 0 ? (len - 1) / a.ckpt_interval : 0;
+            }
+            const auto rs = buffer_rsrc(a.checkpoints + (int64_t(ckpt_base + pos / a.ckpt_interval - 1) * H + h) * (kD * kD),
+                                        kD * kD * 4);
+            const int voff = ((4 * lq) * kD + colw + lj) * 4;
   #pragma unroll
             for (int jb = 0; jb < JB; ++jb)
   #pragma unroll
               for (int ct = 0; ct < 8; ++ct)
   #pragma unroll
-                for (int e = 0; e < 4; ++e) dst[(16 * ct + 4 * lq + e) * kD + 16 * jb] = S[jb][ct][e];
+                for (int e = 0; e < 4; ++e)
+                  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(S[jb][ct][e]), rs,
+                                                        voff + ((16 * ct + e) * kD + 16 * jb) * 4, 0, 0);
           }
         }
       __syncthreads();
