@@ -70,7 +70,10 @@ def auto_seg_len(cu_seqlens_host, H: int, n_cu: int = 256, min_seg: int = 512) -
     return ((seg + 63) // 64) * 64
 
 
-def plan_segments(cu_seqlens_host, seg_len: int) -> SegmentPlan:
+def plan_segments(cu_seqlens_host, seg_len: int, cut_longer_than: int = 0) -> SegmentPlan:
+    """Segment rows of a packed batch: every sequence longer than
+    ``max(seg_len, cut_longer_than)`` tokens is cut every ``seg_len`` tokens
+    from its start; the others stay whole."""
     if seg_len <= 0 or seg_len % 64:
         raise ValueError("seg_len must be a positive multiple of 64")
     cu = np.asarray(cu_seqlens_host, dtype=np.int64)
@@ -79,7 +82,7 @@ def plan_segments(cu_seqlens_host, seg_len: int) -> SegmentPlan:
     for n in range(cu.shape[0] - 1):
         a, b = int(cu[n]), int(cu[n + 1])
         first = len(rows) - 1
-        cuts = list(range(a + seg_len, b, seg_len))
+        cuts = list(range(a + seg_len, b, seg_len)) if b - a > cut_longer_than else []
         rows.extend(cuts + [b])
         row_of_seq.append(range(first, len(rows) - 1))
         if cuts:

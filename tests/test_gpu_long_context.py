@@ -72,7 +72,8 @@ def _oracle_slice(args):
 
 
 def test_long_context_full_size_sampled():
-    """1,048,576 tokens in 16 segments + 8 ragged sequences, 12 heads, bf16, as bench.py --long runs it."""
+    """1,048,576 tokens in 16 segments + 8 ragged sequences, 12 heads, bf16, as bench.py --long runs it
+    (each 65,536-token segment as two 32,768-token fragments)."""
     import multiprocessing as mp
     from multiprocessing import shared_memory
 
@@ -86,7 +87,7 @@ def test_long_context_full_size_sampled():
     finally:
         p.release()
     H, T = 12, p.T
-    o, S = kda_prefill_segmented(d["q"], d["k"], d["v"], d["g"], d["beta"], p.cu_seqlens, seg_len=65536,
+    o, S = kda_prefill_segmented(d["q"], d["k"], d["v"], d["g"], d["beta"], p.cu_seqlens, seg_len=32768,
                                  initial_state=d["initial_state"])
     torch.cuda.synchronize()
     del d

@@ -35,3 +35,11 @@ def test_auto_segment_length():
     for lens, H in (([4096], 12), ([100000], 2), ([5, 9000, 30], 4)):
         s = auto_seg_len(np.cumsum([0] + lens), H)
         assert s % 64 == 0 and s >= 512
+
+
+def test_plan_cuts_only_long_sequences():
+    cu = np.cumsum([0, 70000, 30000, 65536, 200000])
+    plan = plan_segments(cu, 32768, cut_longer_than=65536)
+    assert plan.multi == [0, 3]                    # 70,000 and 200,000 are cut; 30,000 and 65,536 stay whole
+    assert [len(r) for r in plan.row_of_seq] == [3, 1, 1, 7]
+    assert plan.rows[1] - plan.rows[0] == 32768
