@@ -22,6 +22,8 @@ SIGNATURES = {
                                         _P]),
     "kda_verify_commit": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_int, _P]),
     "kda_prefill": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _F, _P, _P, _P, _P, _P]),
+    "kda_prefill_ordered": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _F, _P, _P, _P,
+                                           _P, _P, _P]),
     "kda_prefill_checkpointed": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _F, _P, _P,
                                                 _P, _I, _P, _P]),
     "kda_prefill_checkpoint_count": (ctypes.c_int64, [_P, _I, _I]),

@@ -44,6 +44,7 @@ struct PrefillLaunch {
   float* transition_out;       // or null
   float* checkpoints = nullptr;  // or null: [n_ckpt, H, 128, 128]
   int32_t ckpt_interval = 0;     // positive multiple of 64 when checkpoints is set
+  const int32_t* seq_order = nullptr;  // or null: device [num_seqs], the order sequences are started in
 };
 
 hipError_t launch_prefill(const PrefillLaunch& p, bool bf16, hipStream_t stream);

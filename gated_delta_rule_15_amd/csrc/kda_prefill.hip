@@ -119,6 +119,8 @@ struct PrefillArgs {
   float* transition_out;
   float* checkpoints;       // or null: states at multiples of ckpt_interval tokens
   int32_t ckpt_interval;    // positive multiple of 64 when checkpoints is set
+  const int32_t* seq_order; // or null: workgroup rank -> sequence (a permutation of 0 .. num_seqs - 1)
+  int32_t num_seqs;
 };
 
 // Prep-thread inputs of one chunk (TPT tokens x 4 channels), as loaded.
@@ -217,7 +219,8 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
   const int slice = blockIdx.x % a.n_slices;
   const int sh = blockIdx.x / a.n_slices;
   const int h = sh % a.H;
-  const int seq = sh / a.H;
+  const int seq = a.seq_order ? a.seq_order[sh / a.H] : sh / a.H;
+  if (seq < 0 || seq >= a.num_seqs) return;  // not a sequence of the batch (a bad order entry)
   const bool is_transition = slice >= a.n_value_slices;
   const int vslice = is_transition ? slice - a.n_value_slices : slice;
   const int64_t H = a.H;
@@ -722,6 +725,8 @@ hipError_t launch_cfg(const PrefillLaunch& p, hipStream_t stream) {
   PrefillArgs a;
   a.q = p.q; a.k = p.k; a.v = p.v; a.g = p.g; a.beta = p.beta;
   a.cu_seqlens = p.cu_seqlens;
+  a.seq_order = p.seq_order;
+  a.num_seqs = p.num_seqs;
   a.H = p.H;
   a.n_value_slices = kD / (16 * JB * SW);
   a.n_slices = a.n_value_slices * (p.transition_out ? 2 : 1);

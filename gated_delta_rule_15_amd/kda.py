@@ -149,6 +149,23 @@ def kda_prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host=None, initial_stat
     Returns (o or None, final_state or None).  ``final_state`` may be the same
     tensor as ``initial_state`` (in-place continuation).
     """
+    return _prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, initial_state, final_state, o, transition_out,
+                    scale, with_output, with_final_state, None)
+
+
+def kda_prefill_ordered(q, k, v, g, beta, cu_seqlens, seq_order, cu_seqlens_host=None, initial_state=None,
+                        final_state=None, o=None, transition_out=None, scale: float = 1.0, with_output: bool = True,
+                        with_final_state: bool = True):
+    """kda_prefill whose sequences are started in the order ``seq_order`` (device int32 [N], a
+    permutation of 0..N-1; e.g. longest first).  Same results as kda_prefill, bit for bit."""
+    if seq_order is None:
+        raise ValueError("seq_order is required")
+    return _prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, initial_state, final_state, o, transition_out,
+                    scale, with_output, with_final_state, seq_order)
+
+
+def _prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, initial_state, final_state, o, transition_out, scale,
+             with_output, with_final_state, seq_order):
     T, H, _ = q.shape
     dt = q.dtype
     dev = q.device
@@ -176,10 +193,18 @@ def kda_prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host=None, initial_stat
     _need(o, "o", (T, H, D), dt, dev)
     _need(transition_out, "transition_out", (N, H, D, D), torch.float32, dev)
     lib = _lib.load()
-    _lib.check(lib.kda_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
-                               _ptr(cu_seqlens_host), N, H, D, D, _dtype_code(q), float(scale),
-                               _ptr(initial_state), _ptr(final_state), _ptr(o), _ptr(transition_out), _stream()),
-               "kda_prefill")
+    if seq_order is None:
+        _lib.check(lib.kda_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                                   _ptr(cu_seqlens_host), N, H, D, D, _dtype_code(q), float(scale),
+                                   _ptr(initial_state), _ptr(final_state), _ptr(o), _ptr(transition_out), _stream()),
+                   "kda_prefill")
+    else:
+        _need(seq_order, "seq_order", (N,), torch.int32, dev)
+        _lib.check(lib.kda_prefill_ordered(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                                           _ptr(cu_seqlens_host), N, H, D, D, _dtype_code(q), float(scale),
+                                           _ptr(initial_state), _ptr(final_state), _ptr(o), _ptr(transition_out),
+                                           _ptr(seq_order), _stream()),
+                   "kda_prefill_ordered")
     return o, final_state
 
 

@@ -15,7 +15,8 @@ segment computes its outputs):
            S_in(i+1) = M(i) S_in(i) + S~(i), written straight into the rows of
            pass 2's initial-state buffer.
   pass 2   kda_prefill over every segment of every sequence from its true entry
-           state: the outputs and the final states.
+           state, longest rows started first (kda_prefill_ordered): the
+           outputs and the final states.
 
 Segment boundaries are multiples of 64 tokens from each sequence start, so
 the chunking inside every segment is the one the unsplit sequence would use.
@@ -136,16 +137,25 @@ def kda_prefill_segmented(q, k, v, g, beta, cu_seqlens_host, seg_len: Optional[i
         kda.kda_compose_segments(M, St, init2[r.start], S_in=init2[r.start:r.start + nf],
                                  S_final=init2[r.start + nf])
 
-    # pass 2: every segment from its entry state
-    kda.kda_prefill(q, k, v, g, beta, work["rows_d"], work["rows_h"], initial_state=init2, final_state=fin2, o=o,
-                    scale=scale)
+    # pass 2: every segment from its entry state, longest rows started first
+    kda.kda_prefill_ordered(q, k, v, g, beta, work["rows_d"], work["order2"], work["rows_h"], initial_state=init2,
+                            final_state=fin2, o=o, scale=scale)
     final_state.copy_(fin2.index_select(0, work["last_rows"]))
     return o, final_state
+
+
+def longest_first(rows) -> np.ndarray:
+    """Order in which to start the rows of a packed batch (offsets ``rows``): longest first, ties
+    in row order.  A prefill walks each row's chunks in sequence, so a long row started late
+    sets the batch's finish time."""
+    lens = np.diff(np.asarray(rows, dtype=np.int64))
+    return np.argsort(-lens, kind="stable").astype(np.int32)
 
 
 def alloc_work(plan: SegmentPlan, H: int, dev) -> dict:
     R = plan.n_rows
     work = {
+        "order2": torch.from_numpy(longest_first(plan.rows)).to(dev),
         "init2": torch.empty((R, H, D, D), dtype=torch.float32, device=dev),
         "fin2": torch.empty((R, H, D, D), dtype=torch.float32, device=dev),
         "rows_d": torch.from_numpy(plan.rows.copy()).to(dev),

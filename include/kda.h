@@ -137,6 +137,28 @@ kda_status_t kda_prefill(const void* q, const void* k, const void* v, const floa
                          float* final_state, void* o, float* transition_out, void* stream);
 
 /*
+ * kda_prefill_ordered — kda_prefill with a caller-chosen order in which the
+ * sequences' workgroups are started.  A prefill walks each sequence's chunks
+ * in order, so a batch runs as long as its last-started long sequence: with
+ * more (sequence, head) units than compute units, starting the longest first
+ * (as when the segments of cut sequences run beside whole ones,
+ * "Kimi K3 的训练与 Serving Infra", section 4.2) shortens the tail.  Results
+ * are those of kda_prefill, bit for bit, for any order.
+ *   seq_order : device int32 [num_seqs], required: a permutation of
+ *               0 .. num_seqs - 1; entry i is the sequence started i-th.
+ *               Entries outside that range are skipped (that sequence is then
+ *               not computed); a repeated entry computes its sequence twice,
+ *               racing on its outputs.
+ * Errors: KDA_ERR_INVALID_ARG for a NULL seq_order, otherwise as kda_prefill.
+ */
+kda_status_t kda_prefill_ordered(const void* q, const void* k, const void* v, const float* g,
+                                 const float* beta, const int32_t* cu_seqlens,
+                                 const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t H, int32_t d_k,
+                                 int32_t d_v, kda_dtype_t dtype, float scale, const float* initial_state,
+                                 float* final_state, void* o, float* transition_out, const int32_t* seq_order,
+                                 void* stream);
+
+/*
  * kda_prefill_checkpointed — kda_prefill that also stores the state at chunk
  * boundaries, for restoring a prefix later (prefix caching / copy-on-write
  * restore of a state, as the serving pages describe for KDA's fixed-size

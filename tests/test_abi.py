@@ -32,7 +32,7 @@ def test_header_declares_the_entry_points():
     syms = declared_symbols()
     for name in ("kda_prefill", "kda_decode_step", "kda_verify_block", "kda_verify_commit",
                  "kda_compose_segments", "kda_prefill_checkpointed", "kda_prefill_checkpoint_count",
-                 "kda_status_string", "kda_version"):
+                 "kda_prefill_ordered", "kda_status_string", "kda_version"):
         assert name in syms
     assert set(syms) == set(_lib.SIGNATURES), "binding signatures and header disagree"
 
@@ -110,6 +110,22 @@ def test_checkpoint_argument_errors(lib):
     assert lib.kda_prefill_checkpoint_count(good, 2, 128) == 1
     decreasing = (ctypes.c_int32 * 3)(0, 9, 5)
     assert lib.kda_prefill_checkpoint_count(decreasing, 2, 64) == -1
+
+
+def test_ordered_prefill_argument_errors(lib):
+    p = ctypes.c_void_p(16)
+    good = (ctypes.c_int32 * 3)(0, 130, 200)
+    # the order array is required
+    assert lib.kda_prefill_ordered(p, p, p, p, p, p, good, 2, 2, 128, 128, 1, 1.0, None, p, p, None, None,
+                                   None) == _lib.KDA_ERR_INVALID_ARG
+    # the other checks are kda_prefill's (no launch happens for these)
+    bad = (ctypes.c_int32 * 3)(0, 130, 100)
+    assert lib.kda_prefill_ordered(p, p, p, p, p, p, bad, 2, 2, 128, 128, 1, 1.0, None, p, p, None, p,
+                                   None) == _lib.KDA_ERR_INVALID_ARG
+    assert lib.kda_prefill_ordered(p, p, p, p, p, p, good, 2, 2, 64, 128, 1, 1.0, None, p, p, None, p,
+                                   None) == _lib.KDA_ERR_UNSUPPORTED
+    assert lib.kda_prefill_ordered(None, None, None, None, None, None, None, 0, 2, 128, 128, 1, 1.0, None, None,
+                                   None, None, p, None) == 0
 
 
 def test_compose_argument_errors(lib):

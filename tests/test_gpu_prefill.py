@@ -203,3 +203,28 @@ def test_prefill_deterministic():
     o2, S2, _ = _run(p)
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(S1.view(torch.int32), S2.view(torch.int32))
+
+
+@pytest.mark.parametrize("H,transitions", [(2, True), (8, False)])
+def test_prefill_ordered_equals_natural_order(H, transitions):
+    """Starting the sequences in another order changes nothing, bit for bit (narrow and wide grids)."""
+    from gated_delta_rule_15_amd.kda import kda_prefill, kda_prefill_ordered
+    from gated_delta_rule_15_amd.long_context import longest_first
+    lens = [1 + (53 * i) % 200 for i in range(40)]
+    p = gen.packed_batch(seed=13, seqlens=lens, H=H, dtype="bf16", init_state=True)
+    d = packed_to_dev(p)
+    N = len(lens)
+    M1 = torch.empty((N, H, 128, 128), device="cuda:0") if transitions else None
+    M2 = torch.empty((N, H, 128, 128), device="cuda:0") if transitions else None
+    o1, S1 = kda_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], d["cu_seqlens_host"],
+                         initial_state=d["initial_state"], transition_out=M1)
+    for order in (longest_first(p.cu_seqlens), np.random.default_rng(0).permutation(N).astype(np.int32)):
+        o2, S2 = kda_prefill_ordered(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"],
+                                     torch.from_numpy(order).to("cuda:0"), d["cu_seqlens_host"],
+                                     initial_state=d["initial_state"], transition_out=M2)
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+        assert torch.equal(S1.view(torch.int32), S2.view(torch.int32))
+        if transitions:
+            assert torch.equal(M1.view(torch.int32), M2.view(torch.int32))
+    _check(p, o1, S1, f"{N} seqs x {H} heads")

@@ -43,3 +43,11 @@ def test_plan_cuts_only_long_sequences():
     assert plan.multi == [0, 3]                    # 70,000 and 200,000 are cut; 30,000 and 65,536 stay whole
     assert [len(r) for r in plan.row_of_seq] == [3, 1, 1, 7]
     assert plan.rows[1] - plan.rows[0] == 32768
+
+
+def test_longest_first_order():
+    from gated_delta_rule_15_amd.long_context import longest_first
+    rows = np.cumsum([0, 100, 300, 300, 64, 0, 500])
+    order = longest_first(rows)
+    assert order.tolist() == [5, 1, 2, 0, 3, 4]
+    assert sorted(order.tolist()) == list(range(6))
