@@ -63,11 +63,9 @@ struct Lds {
   static constexpr int kSqRow = kC * E + 16;               // [32][32]: T', P
   static constexpr int kSqPlane = kC * kSqRow;
   static constexpr int kSqBytes = P * kSqPlane;
-  static constexpr int kNatRow = 16 * E + (E == 2 ? 8 : 16);  // [rows][16], natural order: A_10, T_II
+  static constexpr int kNatRow = 16 * E + (E == 2 ? 8 : 16);  // [rows][16], natural order: A_10
   static constexpr int kAopPlane = 16 * kNatRow;
   static constexpr int kAopBytes = P * kAopPlane;
-  static constexpr int kDgPlane = kC * kNatRow;
-  static constexpr int kDgBytes = P * kDgPlane;
   static constexpr int kFLd = 20;                          // fp32 [2 blocks][16][20]
   static constexpr int kFBytes = 2 * 16 * kFLd * 4;
   // one operand set (read by the state waves)
@@ -82,8 +80,7 @@ struct Lds {
   // prep scratch
   static constexpr int kKc = 2 * kSetBytes;
   static constexpr int kAop = kKc + kOpBytes;              // A_10 (beta-scaled), MFMA operand
-  static constexpr int kDg = kAop + kAopBytes;             // T_00 | T_11 as MFMA operands
-  static constexpr int kAt = kDg + kDgBytes;               // A_II transposed, fp32: At[I][s][r]
+  static constexpr int kAt = kAop + kAopBytes;             // A_II transposed, fp32: At[I][s][r]
   static constexpr int kTd = kAt + kFBytes;                // T_II column-major, fp32: Td[I][j][r]
   static constexpr int kBeta = kTd + kFBytes;              // 32 floats
   static constexpr int kBytes = kBeta + kC * 4;
@@ -556,15 +553,23 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
         if (pw < 2) {
           // diagonal tile A_II (I = pw), then T_II = (I + A_II)^{-1}
           const int I = pw;
-          f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          // two accumulation chains (contraction blocks 0, 1 and 2, 3), summed
+          f32x4_t acc2[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
   #pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-            const int koff = (32 * ks + 8 * lq) * E;
-            const Frag fa = Pol::load(pset + L::kSetKh, L::kOpPlane, (16 * I + lj) * L::kOpRow + koff);
-            const Frag fb = Pol::load(smem + L::kKc, L::kOpPlane, (16 * I + lj) * L::kOpRow + koff);
+          for (int kp = 0; kp < 2; ++kp) {
+            Frag fa[2], fb[2];
   #pragma unroll
-            for (int p = 0; p < Pol::kParts; ++p) Pol::mma_part(acc, fa, fb, p);
+            for (int c = 0; c < 2; ++c) {
+              const int koff = (32 * (2 * c + kp) + 8 * lq) * E;
+              fa[c] = Pol::load(pset + L::kSetKh, L::kOpPlane, (16 * I + lj) * L::kOpRow + koff);
+              fb[c] = Pol::load(smem + L::kKc, L::kOpPlane, (16 * I + lj) * L::kOpRow + koff);
+            }
+  #pragma unroll
+            for (int p = 0; p < Pol::kParts; ++p)
+  #pragma unroll
+              for (int c = 0; c < 2; ++c) Pol::mma_part(acc2[c], fa[c], fb[c], p);
           }
+          const f32x4_t acc = acc2[0] + acc2[1];
           {  // At[I][s][r] = A[16I+r][16I+s] = beta_r (Kh Kc^T)[r][s] for r > s
             float4 w;
             float* wp = reinterpret_cast<float*>(&w);
@@ -597,8 +602,6 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
             for (int r4 = 0; r4 < 4; ++r4)
               *reinterpret_cast<float4*>(s_td + (I * 16 + lj) * L::kFLd + 4 * r4) =
                   make_float4(x[4 * r4], x[4 * r4 + 1], x[4 * r4 + 2], x[4 * r4 + 3]);
-  #pragma unroll
-            for (int r = 0; r < 16; ++r) Pol::store1(smem + L::kDg, L::kDgPlane, (16 * I + r) * L::kNatRow + lj * E, x[r]);
           }
         } else if (pw < 6) {
           // the four remaining 16 x 16 tiles, one per wave (PW = 8) or two (PW = 4):
@@ -662,7 +665,11 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
           f32x4_t X = f32x4_t{0.f, 0.f, 0.f, 0.f};
   #pragma unroll
           for (int p = 0; p < Pol::kParts16; ++p) Pol::mma16_part(X, fa, fb, p);
-          const Frag16 ft = Pol::load16(smem + L::kDg, L::kDgPlane, (16 + lj) * L::kNatRow + 4 * lq * E);
+          // T_11 as the A operand: row lj, columns 4lq .. 4lq+3, read from its fp32 columns
+          float t11[4];
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) t11[e] = s_td[(16 + 4 * lq + e) * L::kFLd + lj];
+          const Frag16 ft = Pol::make16(t11);
           const float xv[4] = {X[0], X[1], X[2], X[3]};
           const Frag16 fx = Pol::make16(xv);
           f32x4_t Y = f32x4_t{0.f, 0.f, 0.f, 0.f};
