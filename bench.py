@@ -219,19 +219,19 @@ def bench_prefill(reps, warmup):
                 single_launch_checkpoints_every_512_ms=ms_ckpt)
 
 
-LONG_SUB_SEGMENT = 32768  # each 65,536-token segment of the long sequence runs as 2 fragments
+LONG_SUB_SEGMENT = 8192  # each 65,536-token segment of the long sequence runs as 8 fragments
 
 
 def bench_long(reps, warmup=1, gen_workers=None):
     """1,048,576-token sequence (16 segments of 65,536) + 8 ragged 1K-32K sequences, 12 heads, bf16.
 
-    Each 65,536-token segment is computed as two 32,768-token fragments, so pass 1
-    has 31 x 12 x 2 units and pass 2 32 x 12 + 8 x 12 (the scan over the 32
-    fragments equals composing each segment from its halves and scanning the 16
-    segments: the composition is associative).  Measured 31.4 ms with whole
-    65,536-token segments (pass 1's 360 units take two rounds of 256 CUs), 25.2 ms
-    with 32,768, 27.2-27.9 ms with 16,384-4,096 (the extras, last in the grid, then
-    finish late).  Inputs are drawn by ``gen_workers`` spawned processes (default:
+    Each 65,536-token segment is computed as eight 8,192-token fragments, so pass 1
+    has 127 x 12 x 2 units and pass 2 128 x 12 + 8 x 12 (the scan over the 128
+    fragments equals composing each segment from its fragments and then scanning the
+    16 segments: the composition is associative).  Measured: 31.4 ms with whole
+    65,536-token segments (pass 1's 360 units take two rounds of 256 CUs), 23.4 ms
+    with 32,768-token fragments, 22.4 ms with 8,192 (pass 2 starts its longest rows
+    first).  Inputs are drawn by ``gen_workers`` spawned processes (default:
     the host's cores, at most 16); 1 draws them in this process (for runs under a
     profiler)."""
     import torch
@@ -249,7 +249,7 @@ def bench_long(reps, warmup=1, gen_workers=None):
             p.release()
     init = to_dev(p.initial_state)
     H, T = 12, p.T
-    plan = plan_segments(p.cu_seqlens, LONG_SUB_SEGMENT)
+    plan = plan_segments(p.cu_seqlens, LONG_SUB_SEGMENT, cut_longer_than=65536)  # the 8 extras stay whole
     work = alloc_work(plan, H, q.device)
     o = torch.empty_like(q)
     fs = torch.empty((len(p.cu_seqlens) - 1, H, D, D), device="cuda:0")

@@ -130,7 +130,7 @@ struct PrepIn {
 
 template <class InT, int TPT>
 __device__ __forceinline__ void load_prep(PrepIn<InT, TPT>& in, const PrefillArgs& a, int t0, int n, int h, int tg,
-                                          int c0, int ptid) {
+                                          int c0, int ptid, bool need_q) {
   // wave-uniform chunk base + 32-bit per-lane offsets; rows past the chunk end
   // are clamped to its last token (always valid) and masked where they are used
   const int64_t cbase = (int64_t(t0) * a.H + h) * kD;
@@ -144,7 +144,7 @@ __device__ __forceinline__ void load_prep(PrepIn<InT, TPT>& in, const PrefillArg
     const int off = (r < n ? r : n - 1) * rstride + c0;
     in.g[i] = ld_f4(gb + off);
     in.k[i] = InT::load4raw(kb, off);
-    in.q[i] = InT::load4raw(qb, off);
+    in.q[i] = need_q ? InT::load4raw(qb, off) : typename InT::raw4{};
   }
   in.beta = a.beta[int64_t(t0) * a.H + h + (ptid < n ? ptid : n - 1) * a.H];
 }
@@ -467,7 +467,7 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
     }
   } else {
     PrepIn<InT, TPT> pin;
-    if (nch > 0) load_prep<InT, TPT>(pin, a, bos, eos - bos < kC ? eos - bos : kC, h, tg, c0, ptid);
+    if (nch > 0) load_prep<InT, TPT>(pin, a, bos, eos - bos < kC ? eos - bos : kC, h, tg, c0, ptid, want_o);
     for (int i = 0; i < nch; ++i) {
       // this step builds chunk i into operand set i % 2
       const int tp = bos + i * kC;
@@ -525,13 +525,13 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
             const float eb = __builtin_amdgcn_exp2f(b);
             kh[e] = kq[rr][e] * eb;
             kc[e] = kq[rr][e] * __builtin_amdgcn_exp2f(-b);
-            qh[e] = (qv[rr][e] * a.scale) * eb;
+            if (want_o) qh[e] = (qv[rr][e] * a.scale) * eb;
             kbv[rr][e] = kc[e] * gam[e];  // k e^{b_last - b} (the reference cancels)
           }
           const int off = r * L::kOpRow + kperm(c0) * E;
           Pol::store4(pset + L::kSetKh, L::kOpPlane, off, kh);
           Pol::store4(smem + L::kKc, L::kOpPlane, off, kc);
-          Pol::store4(pset + L::kSetQh, L::kOpPlane, off, qh);
+          if (want_o) Pol::store4(pset + L::kSetQh, L::kOpPlane, off, qh);
         }
         if (tg == 0) {
           float* g_out = reinterpret_cast<float*>(pset + L::kSetGamma);
@@ -544,7 +544,7 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
         }
         {  // fetch chunk i + 1's inputs (clamped; unconditional so nothing waits on them)
           const int tn = bos + (i + 1 < nch ? i + 1 : nch - 1) * kC;
-          load_prep<InT, TPT>(pin, a, tn, eos - tn < kC ? eos - tn : kC, h, tg, c0, ptid);
+          load_prep<InT, TPT>(pin, a, tn, eos - tn < kC ? eos - tn : kC, h, tg, c0, ptid, want_o);
         }
       }
       __syncthreads();
@@ -603,8 +603,9 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
               *reinterpret_cast<float4*>(s_td + (I * 16 + lj) * L::kFLd + 4 * r4) =
                   make_float4(x[4 * r4], x[4 * r4 + 1], x[4 * r4 + 2], x[4 * r4 + 3]);
           }
-        } else if (pw < 6) {
-          // the four remaining 16 x 16 tiles, one per wave (PW = 8) or two (PW = 4):
+        } else if (pw < 6 && (want_o || pw == 2)) {
+          // the four remaining 16 x 16 tiles, one per wave (PW = 8) or two (PW = 4);
+          // without outputs only the wave holding A_10 has work:
           //   tile 2: A_10 = Kh[16..31] Kc[0..15]^T (beta-scaled rows)
           //   tile 3: P_00 = Qh[0..15] Kc[0..15]^T    tile 4: P_10 = Qh[16..31] Kc[0..15]^T
           //   tile 5: P_11 = Qh[16..31] Kc[16..31]^T, and the zero upper block of P

@@ -73,11 +73,11 @@ def _oracle_slice(args):
 
 def test_long_context_full_size_sampled():
     """1,048,576 tokens in 16 segments + 8 ragged sequences, 12 heads, bf16, as bench.py --long runs it
-    (each 65,536-token segment as two 32,768-token fragments)."""
+    (each 65,536-token segment as eight 8,192-token fragments)."""
     import multiprocessing as mp
     from multiprocessing import shared_memory
 
-    from gated_delta_rule_15_amd.long_context import kda_prefill_segmented
+    from gated_delta_rule_15_amd.long_context import kda_prefill_segmented, plan_segments
     workers = max(2, min(16, len(os.sched_getaffinity(0))))
     t = time.time()
     p = gen.long_context_batch(seed=5, workers=workers)
@@ -87,7 +87,8 @@ def test_long_context_full_size_sampled():
     finally:
         p.release()
     H, T = 12, p.T
-    o, S = kda_prefill_segmented(d["q"], d["k"], d["v"], d["g"], d["beta"], p.cu_seqlens, seg_len=32768,
+    o, S = kda_prefill_segmented(d["q"], d["k"], d["v"], d["g"], d["beta"], p.cu_seqlens,
+                                 plan=plan_segments(p.cu_seqlens, 8192, cut_longer_than=65536),
                                  initial_state=d["initial_state"])
     torch.cuda.synchronize()
     del d
