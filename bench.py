@@ -332,6 +332,57 @@ def calibrate_copy(nbytes=256 << 20, reps=20):
     print(json.dumps({"calibration_copy_bytes_read": nbytes, "bytes_written": nbytes, "launches": reps}))
 
 
+def write_traffic(prof_dir):
+    """Write profiles/decode_64x12_traffic.json from two rocprofv3 counter passes over the decode
+    launches (``dec_FETCH_SIZE``, ``dec_WRITE_SIZE``) and the same passes over the copy calibration
+    (``copy_FETCH_SIZE``, ``copy_WRITE_SIZE``), all under ``prof_dir`` (CSV output)."""
+    import csv
+    import glob
+    import statistics
+
+    def counter(pass_name, kernel_key):
+        files = glob.glob(os.path.join(prof_dir, pass_name, "*counter_collection.csv"))
+        if not files:
+            raise SystemExit(f"no counter CSV under {os.path.join(prof_dir, pass_name)}")
+        with open(files[0]) as f:
+            return [float(r["Counter_Value"]) for r in csv.DictReader(f) if kernel_key in r["Kernel_Name"]]
+
+    dec_f = counter("dec_FETCH_SIZE", "kda_decode_kernel")
+    dec_w = counter("dec_WRITE_SIZE", "kda_decode_kernel")
+    # the copy run's dispatches: 20 copies and the fill of the source; the median is a copy
+    cp_f = statistics.median(counter("copy_FETCH_SIZE", "elementwise"))
+    cp_w = statistics.median(counter("copy_WRITE_SIZE", "elementwise"))
+    nbytes = 256 << 20
+    ff, fw = nbytes / (cp_f * 1024), nbytes / (cp_w * 1024)
+    fetch = statistics.mean(dec_f) * 1024 * ff
+    write = statistics.mean(dec_w) * 1024 * fw
+    alg = 64 * 12 * decode_bytes_per_head(2)
+    t = {
+        "kernel": "kda_decode_kernel<BF16>",
+        "workload": "decode step, 64 requests x 12 heads, d_k=d_v=128, fp32 state in place, bf16 q/k/v/o",
+        "source_hash": src_hash("kda_step.hip", "kda_common.hpp"),
+        "fetch_size_kib_per_dispatch": round(statistics.mean(dec_f), 1),
+        "write_size_kib_per_dispatch": round(statistics.mean(dec_w), 1),
+        "dispatches": len(dec_f),
+        "copy_calibration": {
+            "kernel": "torch.mul(src, 1.0, out=dst) over 256 MiB fp32",
+            "bytes_read": nbytes, "bytes_written": nbytes,
+            "fetch_size_kib": cp_f, "write_size_kib": cp_w,
+            "fetch_factor": round(ff, 5), "write_factor": round(fw, 5),
+        },
+        "fetch_bytes_per_launch": int(round(fetch)),
+        "write_bytes_per_launch": int(round(write)),
+        "bytes_per_launch": int(round(fetch + write)),
+        "algorithmic_bytes_per_launch": alg,
+        "ratio_to_algorithmic": round((fetch + write) / alg, 4),
+    }
+    out = os.path.join(ROOT, "profiles", "decode_64x12_traffic.json")
+    with open(out, "w") as f:
+        json.dump(t, f, indent=2)
+        f.write("\n")
+    print(json.dumps(t))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -341,6 +392,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-decode", action="store_true", help="time only the decode rows (for profiling)")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--write-traffic", metavar="DIR",
+                    help="write profiles/decode_64x12_traffic.json from rocprofv3 counter CSVs under DIR")
     ap.add_argument("--eager", action="store_true", help="launch without a HIP graph (counter collection)")
     ap.add_argument("--gen-workers", type=int, default=None,
                     help="processes drawing the long-context inputs (1: in this process, e.g. under a profiler)")
@@ -356,6 +409,9 @@ def main():
     import torch
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.write_traffic:
+        write_traffic(args.write_traffic)
         return
     from gated_delta_rule_15_amd import _lib
     _lib.load()

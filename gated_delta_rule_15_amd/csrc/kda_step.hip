@@ -280,8 +280,9 @@ __device__ __forceinline__ void read_token(TokenVals& x, const Stage& st, int t,
 // Stage tokens b0 .. b0 + kBlockT - 1 (indices past `last` repeat `last`).
 // Threads of the first half own 8 channels (one group of 8 rows of the step's
 // lane layout) of token tid / 16 for k, q and g, and form q . k; threads of
-// the second half own column group u % 16 of token u / 16 (u = tid - 128) for
-// v.  Every load is issued before the first LDS store.
+// the second half own v pieces u, u + 128, ... (u = tid - 128; piece p is
+// column group p % (columns / 4) of token p / (columns / 4)).  Every load is
+// issued before the first LDS store.
 template <int XOR>
 __device__ __forceinline__ float xor_lane(float x) {  // lane ^ XOR within 32 lanes (XOR < 32)
   return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x1F | (XOR << 10)));
@@ -292,7 +293,7 @@ __device__ __forceinline__ void stage_block(Stage& st, const StepArgs& a, int n,
                                             int tid) {
   static_assert(kBlockT * 16 == kThreads / 2, "8 channels of one token per thread in the first half");
   constexpr int kVPieces = kWgCols * kBlockHalves / 4;  // v pieces per token
-  static_assert(kBlockT * kVPieces <= kThreads / 2, "v pieces fit the second half");
+  constexpr int kVRounds = (kBlockT * kVPieces + kThreads / 2 - 1) / (kThreads / 2);
   if (tid < kThreads / 2) {
     const int t = tid >> 4, c8 = 8 * (tid & 15);
     const int tt = b0 + t <= last ? b0 + t : last;
@@ -339,14 +340,23 @@ __device__ __forceinline__ void stage_block(Stage& st, const StepArgs& a, int n,
     }
     if (tid < kBlockT) st.beta[tid] = beta;
   } else {
-    const int u = tid - kThreads / 2;
-    const int tv = u / kVPieces, cv = 4 * (u % kVPieces);
-    if (u < kBlockT * kVPieces) {
+    typename InT::raw4 vr[kVRounds];
+#pragma unroll
+    for (int j = 0; j < kVRounds; ++j) {
+      const int u = tid - kThreads / 2 + j * (kThreads / 2);
+      const int tv = u / kVPieces, cv = 4 * (u % kVPieces);
       const int ttv = b0 + tv <= last ? b0 + tv : last;
-      const auto vr = InT::load4raw(a.v, ((int64_t(n) * a.G + ttv) * a.H + h) * kD + col0 + cv);
-      float f[4];
-      InT::unpack4(vr, f);
-      *reinterpret_cast<float4*>(&st.v[tv][cv]) = make_float4(f[0], f[1], f[2], f[3]);
+      if (u < kBlockT * kVPieces) vr[j] = InT::load4raw(a.v, ((int64_t(n) * a.G + ttv) * a.H + h) * kD + col0 + cv);
+    }
+#pragma unroll
+    for (int j = 0; j < kVRounds; ++j) {
+      const int u = tid - kThreads / 2 + j * (kThreads / 2);
+      const int tv = u / kVPieces, cv = 4 * (u % kVPieces);
+      if (u < kBlockT * kVPieces) {
+        float f[4];
+        InT::unpack4(vr[j], f);
+        *reinterpret_cast<float4*>(&st.v[tv][cv]) = make_float4(f[0], f[1], f[2], f[3]);
+      }
     }
   }
 }
