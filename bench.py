@@ -332,7 +332,7 @@ def calibrate_copy(nbytes=256 << 20, reps=20):
     print(json.dumps({"calibration_copy_bytes_read": nbytes, "bytes_written": nbytes, "launches": reps}))
 
 
-def write_traffic(prof_dir):
+def write_traffic(prof_dir, out=None):
     """Write profiles/decode_64x12_traffic.json from two rocprofv3 counter passes over the decode
     launches (``dec_FETCH_SIZE``, ``dec_WRITE_SIZE``) and the same passes over the copy calibration
     (``copy_FETCH_SIZE``, ``copy_WRITE_SIZE``), all under ``prof_dir`` (CSV output)."""
@@ -376,11 +376,12 @@ def write_traffic(prof_dir):
         "algorithmic_bytes_per_launch": alg,
         "ratio_to_algorithmic": round((fetch + write) / alg, 4),
     }
-    out = os.path.join(ROOT, "profiles", "decode_64x12_traffic.json")
+    out = out or os.path.join(ROOT, "profiles", "decode_64x12_traffic.json")
     with open(out, "w") as f:
         json.dump(t, f, indent=2)
         f.write("\n")
     print(json.dumps(t))
+    return t
 
 
 def main():
