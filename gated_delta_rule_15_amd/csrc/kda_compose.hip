@@ -119,20 +119,30 @@ __global__ __launch_bounds__(kThreads) void kda_compose_kernel(const float* __re
     __syncthreads();
   };
 
-  // Segment i's operands are loaded while segment i - 1 is composed (two
-  // register sets used alternately; indices past the last segment repeat it).
-  SegOps A, B;
+  // Segment i's operands are loaded two segments ahead, while segments i - 2
+  // and i - 1 are composed (three register sets used in turn; indices past
+  // the last segment repeat it): one segment of prefetch distance left the
+  // global-load latency exposed at every step.
+  SegOps X0, X1, X2;
   const int last = n_seg > 0 ? n_seg - 1 : 0;
-  if (n_seg > 0) load_seg(A, M, S_tilde, (int64_t(0) * H + h) * tile, wave, q, n, c0);
+  auto seg_base = [&](int i) { return (int64_t(i <= last ? i : last) * H + h) * tile; };
+  if (n_seg > 0) {
+    load_seg(X0, M, S_tilde, seg_base(0), wave, q, n, c0);
+    load_seg(X1, M, S_tilde, seg_base(1), wave, q, n, c0);
+  }
   int i = 0;
   while (i < n_seg) {
     publish(i);
-    load_seg(B, M, S_tilde, (int64_t(i + 1 <= last ? i + 1 : last) * H + h) * tile, wave, q, n, c0);
-    advance(A);
+    load_seg(X2, M, S_tilde, seg_base(i + 2), wave, q, n, c0);
+    advance(X0);
     if (++i >= n_seg) break;
     publish(i);
-    load_seg(A, M, S_tilde, (int64_t(i + 1 <= last ? i + 1 : last) * H + h) * tile, wave, q, n, c0);
-    advance(B);
+    load_seg(X0, M, S_tilde, seg_base(i + 2), wave, q, n, c0);
+    advance(X1);
+    if (++i >= n_seg) break;
+    publish(i);
+    load_seg(X1, M, S_tilde, seg_base(i + 2), wave, q, n, c0);
+    advance(X2);
     ++i;
   }
   publish(n_seg);
