@@ -21,6 +21,12 @@ SIGNATURES = {
     "kda_verify_block": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_int, _F, _P, _P, _P,
                                         _P]),
     "kda_verify_commit": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_int, _P]),
+    "kda_decode_step_prologue": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _F, _P,
+                                                _P, _P]),
+    "kda_verify_block_prologue": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_int, _F,
+                                                 _P, _P, _P, _P, _P]),
+    "kda_verify_commit_prologue": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_int, _P,
+                                                  _P]),
     "kda_prefill": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _F, _P, _P, _P, _P, _P]),
     "kda_prefill_ordered": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _F, _P, _P, _P,
                                            _P, _P, _P]),
@@ -29,6 +35,12 @@ SIGNATURES = {
     "kda_prefill_checkpoint_count": (ctypes.c_int64, [_P, _I, _I]),
     "kda_compose_segments": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
 }
+
+class KdaPrologue(ctypes.Structure):
+    """kda_prologue_t of include/kda.h."""
+    _fields_ = [("l2norm_qk", ctypes.c_int32), ("l2norm_eps", ctypes.c_float),
+                ("gate_logits", ctypes.c_int32), ("g_min", ctypes.c_float)]
+
 
 _lock = threading.Lock()
 _lib = None

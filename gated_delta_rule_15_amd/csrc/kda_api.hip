@@ -13,6 +13,18 @@ bool dtype_ok(kda_dtype_t d) { return d == KDA_F32 || d == KDA_BF16; }
 
 kda_status_t hip_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
 
+// Validates a caller's prologue and converts it; false for a NULL or out-of-range one.
+bool prologue_ok(const kda_prologue_t* p, kda::Prologue& out) {
+  if (!p) return false;
+  out.l2norm = p->l2norm_qk != 0;
+  out.eps = p->l2norm_eps;
+  out.gate = p->gate_logits != 0;
+  out.g_min = p->g_min;
+  if (out.l2norm && !(out.eps >= 0.0f && out.eps <= 3.0e38f)) return false;   // finite, >= 0 (NaN fails)
+  if (out.gate && !(out.g_min < 0.0f && out.g_min >= -3.0e38f)) return false;  // finite, < 0
+  return true;
+}
+
 }  // namespace
 
 namespace kda {
@@ -68,35 +80,37 @@ const char* kda_status_string(kda_status_t status) {
   return "unknown status";
 }
 
-kda_status_t kda_decode_step(const void* q, const void* k, const void* v, const float* g,
-                             const float* beta, float* state_pool, const int32_t* slots, int32_t N,
-                             int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t dtype, float scale,
-                             void* o, void* stream) {
+}  // extern "C"
+
+namespace {
+
+kda_status_t decode_impl(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                         float* state_pool, const int32_t* slots, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
+                         kda_dtype_t dtype, float scale, void* o, const kda::Prologue* pro, void* stream) {
   if (N < 0 || H <= 0) return KDA_ERR_INVALID_ARG;
   if (!dims_ok(d_k, d_v) || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
   if (N == 0) return KDA_OK;
   if (!q || !k || !v || !g || !beta || !state_pool) return KDA_ERR_INVALID_ARG;
   return hip_status(kda::launch_decode(q, k, v, g, beta, state_pool, slots, N, H, dtype == KDA_BF16, scale,
-                                       o, static_cast<hipStream_t>(stream)));
+                                       o, static_cast<hipStream_t>(stream), pro));
 }
 
-kda_status_t kda_verify_commit(const void* k, const void* v, const float* g, const float* beta,
-                               float* state_pool, const int32_t* slots, const int32_t* accepted_len,
-                               int32_t N, int32_t gamma1, int32_t H, int32_t d_k, int32_t d_v,
-                               kda_dtype_t dtype, void* stream) {
+kda_status_t commit_impl(const void* k, const void* v, const float* g, const float* beta, float* state_pool,
+                         const int32_t* slots, const int32_t* accepted_len, int32_t N, int32_t gamma1, int32_t H,
+                         int32_t d_k, int32_t d_v, kda_dtype_t dtype, const kda::Prologue* pro, void* stream) {
   if (N < 0 || H <= 0 || gamma1 <= 0) return KDA_ERR_INVALID_ARG;
   if (!dims_ok(d_k, d_v) || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
   if (N == 0) return KDA_OK;
   if (!k || !v || !g || !beta || !state_pool || !accepted_len) return KDA_ERR_INVALID_ARG;
   return hip_status(kda::launch_commit(k, v, g, beta, state_pool, state_pool, slots, accepted_len, N, gamma1,
-                                       H, dtype == KDA_BF16, static_cast<hipStream_t>(stream)));
+                                       H, dtype == KDA_BF16, static_cast<hipStream_t>(stream), pro));
 }
 
-kda_status_t kda_verify_block(const void* q, const void* k, const void* v, const float* g,
-                              const float* beta, const float* state_pool, const int32_t* slots,
-                              int32_t N, int32_t gamma1, int32_t H, int32_t d_k, int32_t d_v,
-                              kda_dtype_t dtype, float scale, void* o, const int32_t* accepted_len,
-                              float* state_out_pool, void* stream) {
+kda_status_t verify_impl(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                         const float* state_pool, const int32_t* slots, int32_t N, int32_t gamma1, int32_t H,
+                         int32_t d_k, int32_t d_v, kda_dtype_t dtype, float scale, void* o,
+                         const int32_t* accepted_len, float* state_out_pool, const kda::Prologue* pro,
+                         void* stream) {
   if (N < 0 || H <= 0 || gamma1 <= 0) return KDA_ERR_INVALID_ARG;
   if (!dims_ok(d_k, d_v) || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
   if (N == 0) return KDA_OK;
@@ -104,10 +118,67 @@ kda_status_t kda_verify_block(const void* q, const void* k, const void* v, const
   if (accepted_len && !state_out_pool) return KDA_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = kda::launch_verify(q, k, v, g, beta, state_pool, slots, N, gamma1, H, dtype == KDA_BF16,
-                                    scale, o, s);
+                                    scale, o, s, pro);
   if (e != hipSuccess || !accepted_len) return hip_status(e);
   return hip_status(kda::launch_commit(k, v, g, beta, state_pool, state_out_pool, slots, accepted_len, N,
-                                       gamma1, H, dtype == KDA_BF16, s));
+                                       gamma1, H, dtype == KDA_BF16, s, pro));
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status_t kda_decode_step(const void* q, const void* k, const void* v, const float* g,
+                             const float* beta, float* state_pool, const int32_t* slots, int32_t N,
+                             int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t dtype, float scale,
+                             void* o, void* stream) {
+  return decode_impl(q, k, v, g, beta, state_pool, slots, N, H, d_k, d_v, dtype, scale, o, nullptr, stream);
+}
+
+kda_status_t kda_decode_step_prologue(const void* q, const void* k, const void* v, const float* g,
+                                      const float* beta, float* state_pool, const int32_t* slots, int32_t N,
+                                      int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t dtype, float scale, void* o,
+                                      const kda_prologue_t* prologue, void* stream) {
+  kda::Prologue pro;
+  if (!prologue_ok(prologue, pro)) return KDA_ERR_INVALID_ARG;
+  return decode_impl(q, k, v, g, beta, state_pool, slots, N, H, d_k, d_v, dtype, scale, o, &pro, stream);
+}
+
+kda_status_t kda_verify_commit(const void* k, const void* v, const float* g, const float* beta,
+                               float* state_pool, const int32_t* slots, const int32_t* accepted_len,
+                               int32_t N, int32_t gamma1, int32_t H, int32_t d_k, int32_t d_v,
+                               kda_dtype_t dtype, void* stream) {
+  return commit_impl(k, v, g, beta, state_pool, slots, accepted_len, N, gamma1, H, d_k, d_v, dtype, nullptr,
+                     stream);
+}
+
+kda_status_t kda_verify_commit_prologue(const void* k, const void* v, const float* g, const float* beta,
+                                        float* state_pool, const int32_t* slots, const int32_t* accepted_len,
+                                        int32_t N, int32_t gamma1, int32_t H, int32_t d_k, int32_t d_v,
+                                        kda_dtype_t dtype, const kda_prologue_t* prologue, void* stream) {
+  kda::Prologue pro;
+  if (!prologue_ok(prologue, pro)) return KDA_ERR_INVALID_ARG;
+  return commit_impl(k, v, g, beta, state_pool, slots, accepted_len, N, gamma1, H, d_k, d_v, dtype, &pro, stream);
+}
+
+kda_status_t kda_verify_block(const void* q, const void* k, const void* v, const float* g,
+                              const float* beta, const float* state_pool, const int32_t* slots,
+                              int32_t N, int32_t gamma1, int32_t H, int32_t d_k, int32_t d_v,
+                              kda_dtype_t dtype, float scale, void* o, const int32_t* accepted_len,
+                              float* state_out_pool, void* stream) {
+  return verify_impl(q, k, v, g, beta, state_pool, slots, N, gamma1, H, d_k, d_v, dtype, scale, o, accepted_len,
+                     state_out_pool, nullptr, stream);
+}
+
+kda_status_t kda_verify_block_prologue(const void* q, const void* k, const void* v, const float* g,
+                                       const float* beta, const float* state_pool, const int32_t* slots,
+                                       int32_t N, int32_t gamma1, int32_t H, int32_t d_k, int32_t d_v,
+                                       kda_dtype_t dtype, float scale, void* o, const int32_t* accepted_len,
+                                       float* state_out_pool, const kda_prologue_t* prologue, void* stream) {
+  kda::Prologue pro;
+  if (!prologue_ok(prologue, pro)) return KDA_ERR_INVALID_ARG;
+  return verify_impl(q, k, v, g, beta, state_pool, slots, N, gamma1, H, d_k, d_v, dtype, scale, o, accepted_len,
+                     state_out_pool, &pro, stream);
 }
 
 kda_status_t kda_prefill(const void* q, const void* k, const void* v, const float* g,

@@ -10,18 +10,29 @@ namespace kda {
 // mode).  Queried per launch, nothing cached.
 int device_cu_count();
 
+// Input prologue applied inside the kernels: per-token L2 normalisation of q
+// and k (x / sqrt(sum x^2 + eps)) and gate logits x -> log-decay g_min * sigmoid(x).
+struct Prologue {
+  bool l2norm = false;
+  float eps = 0.0f;
+  bool gate = false;
+  float g_min = 0.0f;
+};
+
 // ---- decode / verify / commit (kda_step.hip) ------------------------------
+// pro: null for inputs used as given.
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* g, const float* beta,
                          float* state, const int32_t* slots, int N, int H, bool bf16, float scale,
-                         void* o, hipStream_t stream);
+                         void* o, hipStream_t stream, const Prologue* pro = nullptr);
 
 hipError_t launch_verify(const void* q, const void* k, const void* v, const float* g, const float* beta,
                          const float* state, const int32_t* slots, int N, int G, int H, bool bf16,
-                         float scale, void* o, hipStream_t stream);
+                         float scale, void* o, hipStream_t stream, const Prologue* pro = nullptr);
 
 hipError_t launch_commit(const void* k, const void* v, const float* g, const float* beta,
                          const float* state_in, float* state_out, const int32_t* slots,
-                         const int32_t* accepted_len, int N, int G, int H, bool bf16, hipStream_t stream);
+                         const int32_t* accepted_len, int N, int G, int H, bool bf16, hipStream_t stream,
+                         const Prologue* pro = nullptr);
 
 // ---- segment composition (kda_compose.hip) --------------------------------
 hipError_t launch_compose(const float* M, const float* S_tilde, const float* S_in0, float* S_in,
@@ -45,6 +56,7 @@ struct PrefillLaunch {
   float* checkpoints = nullptr;  // or null: [n_ckpt, H, 128, 128]
   int32_t ckpt_interval = 0;     // positive multiple of 64 when checkpoints is set
   const int32_t* seq_order = nullptr;  // or null: device [num_seqs], the order sequences are started in
+  const Prologue* pro = nullptr;       // or null: inputs used as given
 };
 
 hipError_t launch_prefill(const PrefillLaunch& p, bool bf16, hipStream_t stream);

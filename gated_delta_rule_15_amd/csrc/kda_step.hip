@@ -71,7 +71,18 @@ struct StepArgs {
   int32_t N, G, H;
   float scale;
   int32_t layer_wgs;  // verify: workgroups per resident layer (the CU count); 0 = no staggering
+  int32_t pro_l2;     // prologue kernels: normalise q and k per token
+  float pro_eps;
+  int32_t pro_gate;   // prologue kernels: g holds gate logits
+  float pro_gmin;
 };
+
+// Input prologue (the KDA math-details box of the Day-0 lesson page: unit keys
+// for the readout identity; the log-decay bounded below by a scaled sigmoid,
+// g_min = -5).  The same functions serve the decode step and the staged
+// verify / commit inputs, so all three see bit-identical values.
+__device__ __forceinline__ float gate_log_decay(float x, float g_min) { return g_min / (1.0f + __expf(-x)); }
+__device__ __forceinline__ float inv_l2(float sum_sq, float eps) { return 1.0f / sqrtf(sum_sq + eps); }
 
 // One token's inputs at this lane's 8 rows and 4 columns, as fp32.
 struct TokenVals {
@@ -233,20 +244,26 @@ __device__ __forceinline__ void column_sums(float (&v)[NV], float (*red)[kRedVal
   }
 }
 
-template <class InT, bool READOUT>
+// PRO: g may hold gate logits, and q is left unscaled (the caller normalises
+// and scales it once the norms are known).
+template <class InT, bool READOUT, bool PRO>
 __device__ __forceinline__ void load_token(TokenVals& x, const StepArgs& a, int n, int t, int h, int row0, int col) {
   const int64_t tok = (int64_t(n) * a.G + t) * a.H + h;  // [N, G, H] token-head index
   const int64_t vec = tok * kD;
 #pragma unroll
   for (int i = 0; i < kR; i += 4) {
     InT::unpack4(InT::load4raw(a.k, vec + row0 + i), &x.k[i]);
-    const float4 g = ld_f4(a.g + vec + row0 + i);
+    float4 g = ld_f4(a.g + vec + row0 + i);
+    if (PRO && a.pro_gate) {
+      g.x = gate_log_decay(g.x, a.pro_gmin); g.y = gate_log_decay(g.y, a.pro_gmin);
+      g.z = gate_log_decay(g.z, a.pro_gmin); g.w = gate_log_decay(g.w, a.pro_gmin);
+    }
     x.alpha[i] = __expf(g.x); x.alpha[i + 1] = __expf(g.y); x.alpha[i + 2] = __expf(g.z); x.alpha[i + 3] = __expf(g.w);
     if constexpr (READOUT) {
       float q[4];
       InT::unpack4(InT::load4raw(a.q, vec + row0 + i), q);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x.qs[i + e] = q[e] * a.scale;
+      for (int e = 0; e < 4; ++e) x.qs[i + e] = PRO ? q[e] : q[e] * a.scale;
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e) x.qs[i + e] = 0.0f;
@@ -288,7 +305,7 @@ __device__ __forceinline__ float xor_lane(float x) {  // lane ^ XOR within 32 la
   return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x1F | (XOR << 10)));
 }
 
-template <class InT, bool READOUT>
+template <class InT, bool READOUT, bool PRO>
 __device__ __forceinline__ void stage_block(Stage& st, const StepArgs& a, int n, int h, int col0, int b0, int last,
                                             int tid) {
   static_assert(kBlockT * 16 == kThreads / 2, "8 channels of one token per thread in the first half");
@@ -300,8 +317,8 @@ __device__ __forceinline__ void stage_block(Stage& st, const StepArgs& a, int n,
     const int64_t vec = ((int64_t(n) * a.G + tt) * a.H + h) * kD + c8;
     const auto k0 = InT::load4raw(a.k, vec);
     const auto k1 = InT::load4raw(a.k, vec + 4);
-    const float4 g0 = ld_f4(a.g + vec);
-    const float4 g1 = ld_f4(a.g + vec + 4);
+    float4 g0 = ld_f4(a.g + vec);
+    float4 g1 = ld_f4(a.g + vec + 4);
     typename InT::raw4 q0{}, q1{};
     if constexpr (READOUT) {
       q0 = InT::load4raw(a.q, vec);
@@ -313,14 +330,49 @@ __device__ __forceinline__ void stage_block(Stage& st, const StepArgs& a, int n,
     float k[8];
     InT::unpack4(k0, k);
     InT::unpack4(k1, k + 4);
+    float qs[8];
+    if constexpr (READOUT) {
+      InT::unpack4(q0, qs);
+      InT::unpack4(q1, qs + 4);
+    }
+    if constexpr (PRO) {
+      if (a.pro_gate) {
+        g0.x = gate_log_decay(g0.x, a.pro_gmin); g0.y = gate_log_decay(g0.y, a.pro_gmin);
+        g0.z = gate_log_decay(g0.z, a.pro_gmin); g0.w = gate_log_decay(g0.w, a.pro_gmin);
+        g1.x = gate_log_decay(g1.x, a.pro_gmin); g1.y = gate_log_decay(g1.y, a.pro_gmin);
+        g1.z = gate_log_decay(g1.z, a.pro_gmin); g1.w = gate_log_decay(g1.w, a.pro_gmin);
+      }
+      if (a.pro_l2) {
+        // the decode step's norm: fma chain over the group's 8 channels, then
+        // groups paired across channel-group bit 2, 1, 0, and 3 (the two waves)
+        float pk = 0.0f, pq = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pk = fmaf(k[e], k[e], pk);
+        pk = pk + xor_lane<4>(pk);
+        pk = pk + xor_lane<2>(pk);
+        pk = pk + xor_lane<1>(pk);
+        pk = pk + xor_lane<8>(pk);
+        const float rk = inv_l2(pk, a.pro_eps);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) k[e] = k[e] * rk;
+        if constexpr (READOUT) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pq = fmaf(qs[e], qs[e], pq);
+          pq = pq + xor_lane<4>(pq);
+          pq = pq + xor_lane<2>(pq);
+          pq = pq + xor_lane<1>(pq);
+          pq = pq + xor_lane<8>(pq);
+          const float rq = inv_l2(pq, a.pro_eps);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qs[e] = qs[e] * rq;
+        }
+      }
+    }
     *reinterpret_cast<float4*>(&st.k[t][c8]) = make_float4(k[0], k[1], k[2], k[3]);
     *reinterpret_cast<float4*>(&st.k[t][c8 + 4]) = make_float4(k[4], k[5], k[6], k[7]);
     *reinterpret_cast<float4*>(&st.alpha[t][c8]) = make_float4(__expf(g0.x), __expf(g0.y), __expf(g0.z), __expf(g0.w));
     *reinterpret_cast<float4*>(&st.alpha[t][c8 + 4]) = make_float4(__expf(g1.x), __expf(g1.y), __expf(g1.z), __expf(g1.w));
     if constexpr (READOUT) {
-      float qs[8];
-      InT::unpack4(q0, qs);
-      InT::unpack4(q1, qs + 4);
 #pragma unroll
       for (int e = 0; e < 8; ++e) qs[e] = qs[e] * a.scale;
       *reinterpret_cast<float4*>(&st.qs[t][c8]) = make_float4(qs[0], qs[1], qs[2], qs[3]);
@@ -434,7 +486,7 @@ __device__ __forceinline__ void st_state(float* p, const float (&s)[4]) {
 // workgroups leave the chip under-occupied and each runs 16 dependent steps.
 static_assert(kBlockHalves == 1 || kBlockHalves * kWgCols == kD, "halves cover the state");
 
-template <class InT, int MODE>
+template <class InT, int MODE, bool PRO>
 __global__ __launch_bounds__(kThreads) void kda_step_kernel(StepArgs a) {
   static_assert(MODE != kDecode, "decode runs kda_decode_kernel");
   constexpr bool READOUT = (MODE != kCommit);
@@ -495,7 +547,7 @@ __global__ __launch_bounds__(kThreads) void kda_step_kernel(StepArgs a) {
   int c = 0;  // token steps so far (alternates the reduction buffers)
   for (int b0 = 0; b0 < steps; b0 += kBlockT) {
     if (b0 > 0) __syncthreads();  // every step of the previous block has read the stage
-    stage_block<InT, READOUT>(st, a, n, h, col0, b0, last, tid);
+    stage_block<InT, READOUT, PRO>(st, a, n, h, col0, b0, last, tid);
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < NH; ++j) {
@@ -535,9 +587,23 @@ __global__ __launch_bounds__(kThreads) void kda_step_kernel(StepArgs a) {
 // overlapping a tile's stores with the next tile's loads).
 constexpr int kDecodeTiles = KDA_DECODE_TILES;
 
-template <class InT>
+// Sum of one value over the wave's 8 row groups (lane bits 5, 4, 3), in every
+// lane: the pairing column_sums applies to q . k.
+__device__ __forceinline__ float rowgroup_allsum(float v) {
+  float t = v;
+  swap32(v, t);
+  v = v + t;
+  t = v;
+  swap16(v, t);
+  v = v + t;
+  return v + ror8(v);
+}
+
+template <class InT, bool PRO>
 __global__ __launch_bounds__(kThreads) void kda_decode_kernel(StepArgs a, int n_tiles) {
+  static_assert(!PRO || kWavesPerSlice == 2, "prologue norms pair the slice's two waves");
   __shared__ Red red;
+  __shared__ float nrm[kDecodeTiles][kSlicesPerWg][2][kWavesPerSlice];  // |k|^2, |q|^2 per wave
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -570,7 +636,45 @@ __global__ __launch_bounds__(kThreads) void kda_decode_kernel(StepArgs a, int n_
       const float4 w = ld_state<true>(a.state_in + toff[j] + i * kD);
       S[j][i][0] = w.x; S[j][i][1] = w.y; S[j][i][2] = w.z; S[j][i][3] = w.w;
     }
-    load_token<InT, true>(x[j], a, n, 0, h, row0, col);
+    load_token<InT, true, PRO>(x[j], a, n, 0, h, row0, col);
+  }
+  if constexpr (PRO) {
+    // normalise k and q per token: the staged verify / commit inputs' arithmetic
+    // (8-channel fma chains, groups paired across lane bits 5, 4, 3, then the
+    // slice's two waves in order)
+    if (a.pro_l2) {
+#pragma unroll
+      for (int j = 0; j < kDecodeTiles; ++j) {
+        float pk = 0.0f, pq = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kR; ++i) {
+          pk = fmaf(x[j].k[i], x[j].k[i], pk);
+          pq = fmaf(x[j].qs[i], x[j].qs[i], pq);
+        }
+        pk = rowgroup_allsum(pk);
+        pq = rowgroup_allsum(pq);
+        if (lane == 0) {
+          nrm[j][sl][0][ws] = pk;
+          nrm[j][sl][1][ws] = pq;
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kDecodeTiles; ++j) {
+        const float rk = inv_l2(nrm[j][sl][0][0] + nrm[j][sl][0][1], a.pro_eps);
+        const float rq = inv_l2(nrm[j][sl][1][0] + nrm[j][sl][1][1], a.pro_eps);
+#pragma unroll
+        for (int i = 0; i < kR; ++i) {
+          x[j].k[i] = x[j].k[i] * rk;
+          x[j].qs[i] = (x[j].qs[i] * rq) * a.scale;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kDecodeTiles; ++j)
+#pragma unroll
+        for (int i = 0; i < kR; ++i) x[j].qs[i] = x[j].qs[i] * a.scale;
+    }
   }
   const bool out_wave = (ws == 0 && a.o != nullptr);  // wave-uniform: forms o
   const bool writer = out_wave && rg == 0;
@@ -586,43 +690,76 @@ __global__ __launch_bounds__(kThreads) void kda_decode_kernel(StepArgs a, int n_
   }
 }
 
-template <int MODE>
-hipError_t launch_step(const StepArgs& a, bool bf16, hipStream_t stream) {
+template <int MODE, bool PRO>
+hipError_t launch_step_as(const StepArgs& a, bool bf16, hipStream_t stream) {
   const int64_t blocks = int64_t(a.N) * a.H * (kWgPerHead / kBlockHalves);
   if (bf16)
-    hipLaunchKernelGGL((kda_step_kernel<BF16, MODE>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((kda_step_kernel<BF16, MODE, PRO>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((kda_step_kernel<F32, MODE>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((kda_step_kernel<F32, MODE, PRO>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
+}
+
+// The prologue's norms use the 8-rows-per-lane layout (two waves per slice).
+constexpr bool kPrologueBuilt = (kWavesPerSlice == 2);
+
+void set_prologue(StepArgs& a, const Prologue* pro) {
+  a.pro_l2 = pro && pro->l2norm;
+  a.pro_eps = pro ? pro->eps : 0.0f;
+  a.pro_gate = pro && pro->gate;
+  a.pro_gmin = pro ? pro->g_min : 0.0f;
+}
+
+template <int MODE>
+hipError_t launch_step(StepArgs a, bool bf16, hipStream_t stream, const Prologue* pro) {
+  if (!pro) return launch_step_as<MODE, false>(a, bf16, stream);
+  if constexpr (kPrologueBuilt) {
+    set_prologue(a, pro);
+    return launch_step_as<MODE, true>(a, bf16, stream);
+  }
+  return hipErrorNotSupported;
 }
 
 }  // namespace
 
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* g, const float* beta,
                          float* state, const int32_t* slots, int N, int H, bool bf16, float scale, void* o,
-                         hipStream_t stream) {
-  StepArgs a{q, k, v, g, beta, state, state, slots, nullptr, o, N, 1, H, scale, 0};
+                         hipStream_t stream, const Prologue* pro) {
+  StepArgs a{q, k, v, g, beta, state, state, slots, nullptr, o, N, 1, H, scale, 0, 0, 0.0f, 0, 0.0f};
   const int n_tiles = N * H * kWgPerHead;
   const unsigned blocks = unsigned((n_tiles + kDecodeTiles - 1) / kDecodeTiles);
-  if (bf16)
-    hipLaunchKernelGGL((kda_decode_kernel<BF16>), dim3(blocks), dim3(kThreads), 0, stream, a, n_tiles);
-  else
-    hipLaunchKernelGGL((kda_decode_kernel<F32>), dim3(blocks), dim3(kThreads), 0, stream, a, n_tiles);
-  return hipGetLastError();
+  if (!pro) {
+    if (bf16)
+      hipLaunchKernelGGL((kda_decode_kernel<BF16, false>), dim3(blocks), dim3(kThreads), 0, stream, a, n_tiles);
+    else
+      hipLaunchKernelGGL((kda_decode_kernel<F32, false>), dim3(blocks), dim3(kThreads), 0, stream, a, n_tiles);
+    return hipGetLastError();
+  }
+  if constexpr (kPrologueBuilt) {
+    set_prologue(a, pro);
+    if (bf16)
+      hipLaunchKernelGGL((kda_decode_kernel<BF16, true>), dim3(blocks), dim3(kThreads), 0, stream, a, n_tiles);
+    else
+      hipLaunchKernelGGL((kda_decode_kernel<F32, true>), dim3(blocks), dim3(kThreads), 0, stream, a, n_tiles);
+    return hipGetLastError();
+  }
+  return hipErrorNotSupported;
 }
 
 hipError_t launch_verify(const void* q, const void* k, const void* v, const float* g, const float* beta,
                          const float* state, const int32_t* slots, int N, int G, int H, bool bf16,
-                         float scale, void* o, hipStream_t stream) {
-  StepArgs a{q, k, v, g, beta, state, nullptr, slots, nullptr, o, N, G, H, scale, device_cu_count()};
-  return launch_step<kVerify>(a, bf16, stream);
+                         float scale, void* o, hipStream_t stream, const Prologue* pro) {
+  StepArgs a{q, k, v, g, beta, state, nullptr, slots, nullptr, o, N, G, H, scale, device_cu_count(), 0, 0.0f, 0, 0.0f};
+  return launch_step<kVerify>(a, bf16, stream, pro);
 }
 
 hipError_t launch_commit(const void* k, const void* v, const float* g, const float* beta,
                          const float* state_in, float* state_out, const int32_t* slots,
-                         const int32_t* accepted_len, int N, int G, int H, bool bf16, hipStream_t stream) {
-  StepArgs a{nullptr, k, v, g, beta, state_in, state_out, slots, accepted_len, nullptr, N, G, H, 1.0f, 0};
-  return launch_step<kCommit>(a, bf16, stream);
+                         const int32_t* accepted_len, int N, int G, int H, bool bf16, hipStream_t stream,
+                         const Prologue* pro) {
+  StepArgs a{nullptr, k, v, g, beta, state_in, state_out, slots, accepted_len, nullptr, N, G, H, 1.0f, 0, 0, 0.0f, 0,
+             0.0f};
+  return launch_step<kCommit>(a, bf16, stream, pro);
 }
 
 }  // namespace kda

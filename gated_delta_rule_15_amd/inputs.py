@@ -19,6 +19,12 @@ workload has one, is N(0, 0.02^2) fp32 from ``default_rng([seed, seq, head,
 STATE_TAG])``.  Accepted verify lengths and ragged sequence lengths come from
 their own streams (``ACC_TAG``, ``LEN_TAG``).
 
+Raw inputs for the in-kernel prologue (``raw=True``): the same draws, but q and
+k are left unnormalised (cast straight from N(0, 1)), and the g array holds gate
+logits x ~ N(-4, 2) drawn after the five above (6.), so that the log-decay
+g_min * sigmoid(x) spans mostly slow channels (x = -4: g = -0.09) with a tail
+of fast ones (x > 0: g < -2.5).
+
 Arrays are packed the way the library takes them: q, k, v, g as
 [T_total, H, d]; beta as [T_total, H]; states as [N, H, d_k, d_v] (rows are key
 channels); ``cu_seqlens`` int32 [N + 1].  bf16 tensors are returned as numpy
@@ -70,15 +76,18 @@ def as_f64(x: np.ndarray, dtype: str) -> np.ndarray:
 # --------------------------------------------------------------------------
 # one (sequence, head, block) draw
 # --------------------------------------------------------------------------
-def _draw_block(seed: int, seq: int, head: int, block: int, n: int, dk: int, dv: int):
+def _draw_block(seed: int, seq: int, head: int, block: int, n: int, dk: int, dv: int, raw: bool = False):
     rng = np.random.default_rng([seed, seq, head, block])
     q = rng.standard_normal((n, dk), dtype=np.float32)
     k = rng.standard_normal((n, dk), dtype=np.float32)
     v = rng.standard_normal((n, dv), dtype=np.float32)
     z = rng.standard_normal(n, dtype=np.float32)
     g = rng.random((n, dk), dtype=np.float32) * np.float32(-0.1)
-    q /= np.sqrt(np.sum(q * q, axis=1, keepdims=True, dtype=np.float32))
-    k /= np.sqrt(np.sum(k * k, axis=1, keepdims=True, dtype=np.float32))
+    if raw:
+        g = (rng.standard_normal((n, dk), dtype=np.float32) * np.float32(2.0) - np.float32(4.0)).astype(np.float32)
+    else:
+        q /= np.sqrt(np.sum(q * q, axis=1, keepdims=True, dtype=np.float32))
+        k /= np.sqrt(np.sum(k * k, axis=1, keepdims=True, dtype=np.float32))
     beta = (np.float32(1.0) / (np.float32(1.0) + np.exp(-z))).astype(np.float32)
     return q, k, v, beta, g
 
@@ -126,11 +135,12 @@ def _cast(x: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def packed_batch(seed: int, seqlens: Sequence[int], H: int, dk: int = 128, dv: int = 128,
-                 dtype: str = "bf16", init_state: Sequence[bool] | bool = False) -> Packed:
+                 dtype: str = "bf16", init_state: Sequence[bool] | bool = False, raw: bool = False) -> Packed:
     """Ragged batch of ``len(seqlens)`` sequences, each slice drawn per (seq, head, block).
 
     ``init_state`` selects, per sequence (or for all), whether it gets an
-    N(0, 0.02^2) initial state (others start from zeros).
+    N(0, 0.02^2) initial state (others start from zeros).  ``raw``: prologue
+    inputs (unnormalised q, k; gate logits in g).
     """
     seqlens = [int(s) for s in seqlens]
     N = len(seqlens)
@@ -147,7 +157,7 @@ def packed_batch(seed: int, seqlens: Sequence[int], H: int, dk: int = 128, dv: i
         for h in range(H):
             for b0 in range(0, seqlens[s], BLOCK):
                 n = min(BLOCK, seqlens[s] - b0)
-                qq, kk, vv, bb, gg = _draw_block(seed, s, h, b0 // BLOCK, n, dk, dv)
+                qq, kk, vv, bb, gg = _draw_block(seed, s, h, b0 // BLOCK, n, dk, dv, raw)
                 t0 = int(cu[s]) + b0
                 q[t0:t0 + n, h] = _cast(qq, dtype)
                 k[t0:t0 + n, h] = _cast(kk, dtype)
@@ -188,7 +198,7 @@ class StepBatch:
 
 
 def step_batch(seed: int, N: int, G: int, H: int, dk: int = 128, dv: int = 128,
-               dtype: str = "bf16", accepted: bool = False) -> StepBatch:
+               dtype: str = "bf16", accepted: bool = False, raw: bool = False) -> StepBatch:
     qd = np.uint16 if dtype == "bf16" else np.float32
     q = np.empty((N, G, H, dk), dtype=qd)
     k = np.empty((N, G, H, dk), dtype=qd)
@@ -198,7 +208,7 @@ def step_batch(seed: int, N: int, G: int, H: int, dk: int = 128, dv: int = 128,
     state = np.empty((N, H, dk, dv), dtype=np.float32)
     for n in range(N):
         for h in range(H):
-            qq, kk, vv, bb, gg = _draw_block(seed, n, h, 0, G, dk, dv)
+            qq, kk, vv, bb, gg = _draw_block(seed, n, h, 0, G, dk, dv, raw)
             q[n, :, h] = _cast(qq, dtype)
             k[n, :, h] = _cast(kk, dtype)
             v[n, :, h] = _cast(vv, dtype)

@@ -7,6 +7,8 @@ fallback, and a missing library raises ``KdaError``.
 """
 from __future__ import annotations
 
+import ctypes
+from dataclasses import dataclass
 from typing import Optional
 
 import torch
@@ -14,6 +16,20 @@ import torch
 from . import _lib
 
 D = 128
+
+
+@dataclass(frozen=True)
+class Prologue:
+    """Input prologue applied inside the kernels (kda_prologue_t): per-token L2 normalisation of q
+    and k, x / sqrt(sum x^2 + eps), and gate logits x -> log-decay g_min * sigmoid(x)."""
+    l2norm_qk: bool = True
+    l2norm_eps: float = 1e-6
+    gate_logits: bool = True
+    g_min: float = -5.0
+
+    def _c(self) -> "_lib.KdaPrologue":
+        return _lib.KdaPrologue(int(bool(self.l2norm_qk)), float(self.l2norm_eps), int(bool(self.gate_logits)),
+                                float(self.g_min))
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -48,11 +64,12 @@ def _need(t: Optional[torch.Tensor], name: str, shape, dtype=None, device=None) 
 
 
 def kda_decode_step(q, k, v, g, beta, state_pool, o=None, slots=None, scale: float = 1.0,
-                    with_output: bool = True):
+                    with_output: bool = True, prologue: Optional[Prologue] = None):
     """One token per request; ``state_pool`` [P, H, 128, 128] fp32 is updated in place.
 
     q, k, v, g: [N, H, 128]; beta: [N, H]; slots: int32 [N] pool rows (None = 0..N-1).
     Returns o [N, H, 128] (dtype of q) or None when ``with_output`` is False.
+    With ``prologue`` the call goes to kda_decode_step_prologue (raw q, k; g may hold gate logits).
     """
     N, H, _ = q.shape
     dt = q.dtype
@@ -72,14 +89,28 @@ def kda_decode_step(q, k, v, g, beta, state_pool, o=None, slots=None, scale: flo
         o = torch.empty((N, H, D), dtype=dt, device=dev)
     _need(o, "o", (N, H, D), dt, dev)
     lib = _lib.load()
-    _lib.check(lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), _ptr(slots),
-                                   N, H, D, D, _dtype_code(q), float(scale), _ptr(o), _stream()),
-               "kda_decode_step")
+    if prologue is None:
+        _lib.check(lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool),
+                                       _ptr(slots), N, H, D, D, _dtype_code(q), float(scale), _ptr(o), _stream()),
+                   "kda_decode_step")
+    else:
+        pc = prologue._c()
+        _lib.check(lib.kda_decode_step_prologue(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool),
+                                                _ptr(slots), N, H, D, D, _dtype_code(q), float(scale), _ptr(o),
+                                                ctypes.addressof(pc), _stream()),
+                   "kda_decode_step_prologue")
     return o
 
 
+def kda_decode_step_prologue(q, k, v, g, beta, state_pool, prologue: Prologue, **kw):
+    """kda_decode_step with the input prologue (required)."""
+    if prologue is None:
+        raise ValueError("prologue is required")
+    return kda_decode_step(q, k, v, g, beta, state_pool, prologue=prologue, **kw)
+
+
 def kda_verify_block(q, k, v, g, beta, state_pool, o=None, slots=None, accepted_len=None,
-                     state_out_pool=None, scale: float = 1.0):
+                     state_out_pool=None, scale: float = 1.0, prologue: Optional[Prologue] = None):
     """Verify gamma1 draft tokens per request from the committed (read-only) states.
 
     q, k, v, g: [N, G, H, 128]; beta: [N, G, H].  Returns o [N, G, H, 128].
@@ -109,15 +140,31 @@ def kda_verify_block(q, k, v, g, beta, state_pool, o=None, slots=None, accepted_
             state_out_pool = state_pool
         _need(state_out_pool, "state_out_pool", state_pool.shape, torch.float32, dev)
     lib = _lib.load()
-    _lib.check(lib.kda_verify_block(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), _ptr(slots),
-                                    N, G, H, D, D, _dtype_code(q), float(scale), _ptr(o), _ptr(accepted_len),
-                                    _ptr(state_out_pool), _stream()),
-               "kda_verify_block")
+    if prologue is None:
+        _lib.check(lib.kda_verify_block(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool),
+                                        _ptr(slots), N, G, H, D, D, _dtype_code(q), float(scale), _ptr(o),
+                                        _ptr(accepted_len), _ptr(state_out_pool), _stream()),
+                   "kda_verify_block")
+    else:
+        pc = prologue._c()
+        _lib.check(lib.kda_verify_block_prologue(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool),
+                                                 _ptr(slots), N, G, H, D, D, _dtype_code(q), float(scale), _ptr(o),
+                                                 _ptr(accepted_len), _ptr(state_out_pool), ctypes.addressof(pc),
+                                                 _stream()),
+                   "kda_verify_block_prologue")
     return o
 
 
-def kda_verify_commit(k, v, g, beta, state_pool, accepted_len, slots=None):
-    """Replay each request's accepted prefix from its committed state, in place."""
+def kda_verify_block_prologue(q, k, v, g, beta, state_pool, prologue: Prologue, **kw):
+    """kda_verify_block with the input prologue (required)."""
+    if prologue is None:
+        raise ValueError("prologue is required")
+    return kda_verify_block(q, k, v, g, beta, state_pool, prologue=prologue, **kw)
+
+
+def kda_verify_commit(k, v, g, beta, state_pool, accepted_len, slots=None, prologue: Optional[Prologue] = None):
+    """Replay each request's accepted prefix from its committed state, in place (with ``prologue``:
+    the one the verify used)."""
     N, G, H, _ = k.shape
     dt = k.dtype
     dev = k.device
@@ -134,9 +181,23 @@ def kda_verify_commit(k, v, g, beta, state_pool, accepted_len, slots=None):
     elif state_pool.shape[0] < N:
         raise ValueError("state_pool has fewer rows than requests")
     lib = _lib.load()
-    _lib.check(lib.kda_verify_commit(_ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), _ptr(slots),
-                                     _ptr(accepted_len), N, G, H, D, D, _dtype_code(k), _stream()),
-               "kda_verify_commit")
+    if prologue is None:
+        _lib.check(lib.kda_verify_commit(_ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), _ptr(slots),
+                                         _ptr(accepted_len), N, G, H, D, D, _dtype_code(k), _stream()),
+                   "kda_verify_commit")
+    else:
+        pc = prologue._c()
+        _lib.check(lib.kda_verify_commit_prologue(_ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool),
+                                                  _ptr(slots), _ptr(accepted_len), N, G, H, D, D, _dtype_code(k),
+                                                  ctypes.addressof(pc), _stream()),
+                   "kda_verify_commit_prologue")
+
+
+def kda_verify_commit_prologue(k, v, g, beta, state_pool, accepted_len, prologue: Prologue, **kw):
+    """kda_verify_commit with the input prologue (required)."""
+    if prologue is None:
+        raise ValueError("prologue is required")
+    return kda_verify_commit(k, v, g, beta, state_pool, accepted_len, prologue=prologue, **kw)
 
 
 def kda_prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host=None, initial_state=None, final_state=None,

@@ -106,6 +106,49 @@ kda_status_t kda_verify_commit(const void* k, const void* v, const float* g, con
                                kda_dtype_t dtype, void* stream);
 
 /*
+ * Input prologue — applied inside the kernels to the raw per-token inputs,
+ * for callers that hand over unnormalised q, k and gate logits.  The KDA
+ * math-details box of the Day-0 lesson page ("attention 机制详解：KDA") states
+ * its readout identity for unit keys and bounds the log-decay below with a
+ * scaled sigmoid (g_min = -5, so each step keeps more than e^-5 of the state).
+ *   l2norm_qk   : nonzero: q <- q / sqrt(sum q^2 + l2norm_eps) and k likewise,
+ *                 per token and head, in fp32 (the scale argument then
+ *                 multiplies the normalised q).
+ *   l2norm_eps  : finite, >= 0 (read when l2norm_qk is set); 1e-6 is usual.
+ *   gate_logits : nonzero: the g buffer holds gate logits x, and the
+ *                 log-decay used is g_min * sigmoid(x) (a reading of the
+ *                 page's scaled sigmoid: its orientation is not printed).
+ *   g_min       : finite, < 0 (read when gate_logits is set).
+ * The *_prologue entry points below take the arguments of their plain
+ * counterparts plus `prologue` (required); KDA_ERR_INVALID_ARG for a NULL
+ * prologue or a value outside the ranges above.  A verify and the commit that
+ * follows it must use the same prologue: the commit then reproduces, bit for
+ * bit, the state of as many prologue decode steps.
+ */
+typedef struct kda_prologue {
+  int32_t l2norm_qk;
+  float l2norm_eps;
+  int32_t gate_logits;
+  float g_min;
+} kda_prologue_t;
+
+kda_status_t kda_decode_step_prologue(const void* q, const void* k, const void* v, const float* g,
+                                      const float* beta, float* state_pool, const int32_t* slots, int32_t N,
+                                      int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t dtype, float scale, void* o,
+                                      const kda_prologue_t* prologue, void* stream);
+
+kda_status_t kda_verify_block_prologue(const void* q, const void* k, const void* v, const float* g,
+                                       const float* beta, const float* state_pool, const int32_t* slots,
+                                       int32_t N, int32_t gamma1, int32_t H, int32_t d_k, int32_t d_v,
+                                       kda_dtype_t dtype, float scale, void* o, const int32_t* accepted_len,
+                                       float* state_out_pool, const kda_prologue_t* prologue, void* stream);
+
+kda_status_t kda_verify_commit_prologue(const void* k, const void* v, const float* g, const float* beta,
+                                        float* state_pool, const int32_t* slots, const int32_t* accepted_len,
+                                        int32_t N, int32_t gamma1, int32_t H, int32_t d_k, int32_t d_v,
+                                        kda_dtype_t dtype, const kda_prologue_t* prologue, void* stream);
+
+/*
  * kda_prefill — chunk-parallel prefill of a packed ragged batch.
  *
  * Computes, for every sequence n (tokens cu_seqlens[n] .. cu_seqlens[n+1]-1)

@@ -32,7 +32,8 @@ def test_header_declares_the_entry_points():
     syms = declared_symbols()
     for name in ("kda_prefill", "kda_decode_step", "kda_verify_block", "kda_verify_commit",
                  "kda_compose_segments", "kda_prefill_checkpointed", "kda_prefill_checkpoint_count",
-                 "kda_prefill_ordered", "kda_status_string", "kda_version"):
+                 "kda_prefill_ordered", "kda_decode_step_prologue", "kda_verify_block_prologue",
+                 "kda_verify_commit_prologue", "kda_status_string", "kda_version"):
         assert name in syms
     assert set(syms) == set(_lib.SIGNATURES), "binding signatures and header disagree"
 
@@ -126,6 +127,29 @@ def test_ordered_prefill_argument_errors(lib):
                                    None) == _lib.KDA_ERR_UNSUPPORTED
     assert lib.kda_prefill_ordered(None, None, None, None, None, None, None, 0, 2, 128, 128, 1, 1.0, None, None,
                                    None, None, p, None) == 0
+
+
+def test_prologue_argument_errors(lib):
+    p = ctypes.c_void_p(16)
+    Pro = _lib.KdaPrologue
+    bad = [None, Pro(1, -1.0, 0, 0.0), Pro(1, float("nan"), 0, 0.0), Pro(1, float("inf"), 0, 0.0),
+           Pro(0, 0.0, 1, 0.0), Pro(0, 0.0, 1, 1.0), Pro(0, 0.0, 1, float("nan")), Pro(0, 0.0, 1, float("-inf"))]
+    for pro in bad:
+        ref = None if pro is None else ctypes.addressof(pro)
+        assert lib.kda_decode_step_prologue(p, p, p, p, p, p, None, 2, 2, 128, 128, 1, 1.0, p, ref,
+                                            None) == _lib.KDA_ERR_INVALID_ARG
+        assert lib.kda_verify_block_prologue(p, p, p, p, p, p, None, 2, 8, 2, 128, 128, 1, 1.0, p, None, None, ref,
+                                             None) == _lib.KDA_ERR_INVALID_ARG
+        assert lib.kda_verify_commit_prologue(p, p, p, p, p, None, p, 2, 8, 2, 128, 128, 1, ref,
+                                              None) == _lib.KDA_ERR_INVALID_ARG
+    # a valid prologue leaves the plain checks in place (no launch happens for these)
+    ok = Pro(1, 1e-6, 1, -5.0)
+    assert lib.kda_decode_step_prologue(p, p, p, p, p, p, None, 2, 2, 64, 128, 1, 1.0, p, ctypes.addressof(ok),
+                                        None) == _lib.KDA_ERR_UNSUPPORTED
+    assert lib.kda_decode_step_prologue(p, p, p, p, p, p, None, 0, 2, 128, 128, 1, 1.0, p, ctypes.addressof(ok),
+                                        None) == 0
+    assert lib.kda_verify_commit_prologue(p, p, p, p, p, None, None, 2, 8, 2, 128, 128, 1, ctypes.addressof(ok),
+                                          None) == _lib.KDA_ERR_INVALID_ARG
 
 
 def test_compose_argument_errors(lib):

@@ -1,0 +1,102 @@
+"""GPU parity of the in-kernel input prologue (unnormalised q, k; gate logits) against the CPU
+oracle's prologue followed by the recurrence, and its bitwise replay invariants."""
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_15_amd import inputs as gen
+from oracle import kda_oracle as orc
+from oracle import kda_prologue as pro
+
+from kda_testutil import packed_to_dev, rel_l2, steps_to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-3, "f32": 1e-5}
+VARIANTS = [(True, True), (True, False), (False, True)]  # (l2norm_qk, gate_logits)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _prologue(l2, gate):
+    from gated_delta_rule_15_amd.kda import Prologue
+    return Prologue(l2norm_qk=l2, l2norm_eps=1e-6, gate_logits=gate, g_min=-5.0)
+
+
+def _ref_inputs(q, k, g, l2, gate):
+    return pro.apply_prologue(q, k, g, l2norm=l2, eps=1e-6, gate_logits=gate, g_min=-5.0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("l2,gate", VARIANTS)
+def test_decode_prologue_matches_oracle(dtype, l2, gate):
+    from gated_delta_rule_15_amd.kda import kda_decode_step
+    b = gen.step_batch(seed=61, N=24, G=1, H=6, dtype=dtype, raw=True)
+    d = steps_to_dev(b, squeeze_g=True)
+    o = kda_decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], scale=0.8,
+                        prologue=_prologue(l2, gate))
+    torch.cuda.synchronize()
+    q, k, g = _ref_inputs(b.f64("q")[:, 0], b.f64("k")[:, 0], b.f64("g")[:, 0], l2, gate)
+    o_ref, S_ref = orc.decode_step(q, k, b.f64("v")[:, 0], g, b.f64("beta")[:, 0], b.f64("state"), 0.8)
+    eo, es = rel_l2(to_f64(o), o_ref), rel_l2(to_f64(d["state"]), S_ref)
+    print(f"decode prologue {dtype} l2={l2} gate={gate}: rel-L2 o={eo:.3e} S={es:.3e}")
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("l2,gate", VARIANTS)
+def test_verify_commit_prologue_matches_oracle(dtype, l2, gate):
+    from gated_delta_rule_15_amd.kda import kda_verify_block
+    b = gen.step_batch(seed=62, N=12, G=8, H=5, dtype=dtype, accepted=True, raw=True)
+    d = steps_to_dev(b)
+    o = kda_verify_block(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], accepted_len=d["accepted_len"],
+                         scale=0.8, prologue=_prologue(l2, gate))
+    torch.cuda.synchronize()
+    q, k, g = _ref_inputs(b.f64("q"), b.f64("k"), b.f64("g"), l2, gate)
+    o_ref, S_ref = orc.verify_block(q, k, b.f64("v"), g, b.f64("beta"), b.f64("state"), b.accepted_len, 0.8)
+    eo, es = rel_l2(to_f64(o), o_ref), rel_l2(to_f64(d["state"]), S_ref)
+    print(f"verify+commit prologue {dtype} l2={l2} gate={gate}: rel-L2 o={eo:.3e} S={es:.3e}")
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
+@pytest.mark.parametrize("N,H", [(6, 3), (32, 12)])
+def test_prologue_verify_and_commit_bitwise_equal_decode_steps(N, H):
+    """With the prologue, verify's o_t equals the t-th decode step's o and commit(L) equals L decode
+    steps, bit for bit (the norms and gates are formed by the same arithmetic on every path)."""
+    from gated_delta_rule_15_amd.kda import kda_decode_step, kda_verify_block, kda_verify_commit
+    G = 8
+    p = _prologue(True, True)
+    b = gen.step_batch(seed=63, N=N, G=G, H=H, dtype="bf16", accepted=True, raw=True)
+    d = steps_to_dev(b)
+    o_ver = kda_verify_block(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], scale=0.8, prologue=p)
+    committed = d["state"].clone()
+    kda_verify_commit(d["k"], d["v"], d["g"], d["beta"], committed, d["accepted_len"], prologue=p)
+    S = d["state"].clone()
+    S_at_L = torch.empty_like(S)
+    for t in range(G):
+        o_t = kda_decode_step(d["q"][:, t].contiguous(), d["k"][:, t].contiguous(), d["v"][:, t].contiguous(),
+                              d["g"][:, t].contiguous(), d["beta"][:, t].contiguous(), S, scale=0.8, prologue=p)
+        assert torch.equal(o_t.view(torch.int16), o_ver[:, t].contiguous().view(torch.int16)), f"step {t}"
+        for n in range(N):
+            if b.accepted_len[n] == t + 1:
+                S_at_L[n] = S[n]
+    torch.cuda.synchronize()
+    assert torch.equal(committed.view(torch.int32), S_at_L.view(torch.int32))
+
+
+def test_prologue_on_prenormalised_inputs_is_close_to_plain():
+    """Inputs that are already unit vectors (the standard workloads) pass the normalisation almost
+    unchanged: the prologue decode agrees with the plain decode to fp32 rounding of the norm."""
+    from gated_delta_rule_15_amd.kda import kda_decode_step
+    b = gen.step_batch(seed=64, N=16, G=1, H=4, dtype="f32")
+    d1 = steps_to_dev(b, squeeze_g=True)
+    d2 = steps_to_dev(b, squeeze_g=True)
+    o1 = kda_decode_step(d1["q"], d1["k"], d1["v"], d1["g"], d1["beta"], d1["state"])
+    o2 = kda_decode_step(d2["q"], d2["k"], d2["v"], d2["g"], d2["beta"], d2["state"],
+                         prologue=_prologue(True, False))
+    torch.cuda.synchronize()
+    assert rel_l2(to_f64(o2), to_f64(o1)) <= 1e-5
