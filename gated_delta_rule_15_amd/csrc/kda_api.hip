@@ -42,7 +42,7 @@ kda_status_t prefill_impl(const void* q, const void* k, const void* v, const flo
                           const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t H,
                           int32_t d_k, int32_t d_v, kda_dtype_t dtype, float scale, const float* initial_state,
                           float* final_state, void* o, float* transition_out, int32_t ckpt_interval,
-                          float* checkpoints, const int32_t* seq_order, void* stream) {
+                          float* checkpoints, const int32_t* seq_order, const kda::Prologue* pro, void* stream) {
   if (num_seqs < 0 || H <= 0) return KDA_ERR_INVALID_ARG;
   if (!dims_ok(d_k, d_v) || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
   if (checkpoints && (ckpt_interval <= 0 || ckpt_interval % 64 != 0)) return KDA_ERR_INVALID_ARG;
@@ -61,6 +61,7 @@ kda_status_t prefill_impl(const void* q, const void* k, const void* v, const flo
   p.checkpoints = checkpoints;
   p.ckpt_interval = checkpoints ? ckpt_interval : 0;
   p.seq_order = seq_order;
+  p.pro = pro;
   return hip_status(kda::launch_prefill(p, dtype == KDA_BF16, static_cast<hipStream_t>(stream)));
 }
 
@@ -187,7 +188,18 @@ kda_status_t kda_prefill(const void* q, const void* k, const void* v, const floa
                          int32_t d_v, kda_dtype_t dtype, float scale, const float* initial_state,
                          float* final_state, void* o, float* transition_out, void* stream) {
   return prefill_impl(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, num_seqs, H, d_k, d_v, dtype, scale,
-                      initial_state, final_state, o, transition_out, 0, nullptr, nullptr, stream);
+                      initial_state, final_state, o, transition_out, 0, nullptr, nullptr, nullptr, stream);
+}
+
+kda_status_t kda_prefill_prologue(const void* q, const void* k, const void* v, const float* g,
+                                  const float* beta, const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                                  int32_t num_seqs, int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t dtype,
+                                  float scale, const float* initial_state, float* final_state, void* o,
+                                  float* transition_out, const kda_prologue_t* prologue, void* stream) {
+  kda::Prologue pro;
+  if (!prologue_ok(prologue, pro)) return KDA_ERR_INVALID_ARG;
+  return prefill_impl(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, num_seqs, H, d_k, d_v, dtype, scale,
+                      initial_state, final_state, o, transition_out, 0, nullptr, nullptr, &pro, stream);
 }
 
 kda_status_t kda_prefill_ordered(const void* q, const void* k, const void* v, const float* g,
@@ -198,7 +210,7 @@ kda_status_t kda_prefill_ordered(const void* q, const void* k, const void* v, co
                                  void* stream) {
   if (!seq_order) return KDA_ERR_INVALID_ARG;
   return prefill_impl(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, num_seqs, H, d_k, d_v, dtype, scale,
-                      initial_state, final_state, o, transition_out, 0, nullptr, seq_order, stream);
+                      initial_state, final_state, o, transition_out, 0, nullptr, seq_order, nullptr, stream);
 }
 
 kda_status_t kda_prefill_checkpointed(const void* q, const void* k, const void* v, const float* g,
@@ -209,7 +221,7 @@ kda_status_t kda_prefill_checkpointed(const void* q, const void* k, const void* 
                                       void* stream) {
   if (!checkpoints) return KDA_ERR_INVALID_ARG;
   return prefill_impl(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, num_seqs, H, d_k, d_v, dtype, scale,
-                      initial_state, final_state, o, nullptr, ckpt_interval, checkpoints, nullptr, stream);
+                      initial_state, final_state, o, nullptr, ckpt_interval, checkpoints, nullptr, nullptr, stream);
 }
 
 int64_t kda_prefill_checkpoint_count(const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t ckpt_interval) {

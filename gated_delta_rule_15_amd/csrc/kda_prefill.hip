@@ -83,7 +83,8 @@ struct Lds {
   static constexpr int kAt = kAop + kAopBytes;             // A_II transposed, fp32: At[I][s][r]
   static constexpr int kTd = kAt + kFBytes;                // T_II column-major, fp32: Td[I][j][r]
   static constexpr int kBeta = kTd + kFBytes;              // 32 floats
-  static constexpr int kBytes = kBeta + kC * 4;
+  static constexpr int kNrm = kBeta + kC * 4;              // prologue: [token][prep wave][k, q] sums of squares
+  static constexpr int kBytes = kNrm + kC * 8 * 2 * 4;
   static_assert(kBytes <= 160 * 1024, "LDS budget");
   static_assert(kOpRow % 16 == 0 && kKbRow % 16 == 0 && kSqRow % 16 == 0 && kSetBytes % 16 == 0, "aligned");
   static_assert(kNatRow % 8 == 0 && (E == 2 || kNatRow % 16 == 0), "aligned natural rows");
@@ -118,7 +119,16 @@ struct PrefillArgs {
   int32_t ckpt_interval;    // positive multiple of 64 when checkpoints is set
   const int32_t* seq_order; // or null: workgroup rank -> sequence (a permutation of 0 .. num_seqs - 1)
   int32_t num_seqs;
+  int32_t pro_l2;           // prologue variant: normalise q and k per token
+  float pro_eps;
+  int32_t pro_gate;         // prologue variant: g holds gate logits
+  float pro_gmin;
 };
+
+// Input prologue (the KDA math-details box of the Day-0 lesson page: unit keys;
+// the log-decay bounded below by a scaled sigmoid, g_min = -5).
+__device__ __forceinline__ float gate_log_decay(float x, float g_min) { return g_min / (1.0f + __expf(-x)); }
+
 
 // Prep-thread inputs of one chunk (TPT tokens x 4 channels), as loaded.
 template <class InT, int TPT>
@@ -147,6 +157,36 @@ __device__ __forceinline__ void load_prep(PrepIn<InT, TPT>& in, const PrefillArg
     in.q[i] = need_q ? InT::load4raw(qb, off) : typename InT::raw4{};
   }
   in.beta = a.beta[int64_t(t0) * a.H + h + (ptid < n ? ptid : n - 1) * a.H];
+}
+
+// Prologue: this prep thread's sums of squares of k and q (its TPT tokens x 4
+// channels), summed over the wave's channel groups (lanes that differ in the
+// bits above the token group) and written per (token, prep wave) to LDS.
+template <class InT, int TPT, int NTG>
+__device__ __forceinline__ void prep_norm_partials(const PrepIn<InT, TPT>& pin, float* nrm, int lane, int tg, int pw,
+                                                   bool want_q) {
+#pragma unroll
+  for (int rr = 0; rr < TPT; ++rr) {
+    float kv[4], qv[4];
+    InT::unpack4(pin.k[rr], kv);
+    InT::unpack4(pin.q[rr], qv);
+    float sk = 0.0f, sq = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sk = fmaf(kv[e], kv[e], sk);
+      sq = fmaf(qv[e], qv[e], sq);
+    }
+#pragma unroll
+    for (int m = NTG; m < 64; m <<= 1) {
+      sk += __shfl_xor(sk, m);
+      sq += __shfl_xor(sq, m);
+    }
+    if (lane < NTG) {
+      float* dst = nrm + ((TPT * tg + rr) * 8 + pw) * 2;
+      dst[0] = sk;
+      dst[1] = want_q ? sq : 0.0f;
+    }
+  }
 }
 
 // State-wave v of one chunk at this wave's columns.
@@ -192,8 +232,9 @@ __device__ __forceinline__ void load_state_v(StateV<InT, JB>& sv, const PrefillA
   }
 }
 
-template <class Pol, class InT, int SW, int JB, int PW, bool CKPT>
+template <class Pol, class InT, int SW, int JB, int PW, bool CKPT, bool PRO>
 __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(PrefillArgs a) {
+  static_assert(!(CKPT && PRO), "checkpoints and the prologue are separate variants");
   static_assert(PW == 4 || PW == 8, "prep waves");
   constexpr int TPT = 16 / PW;  // tokens per prep thread (4 or 2)
   constexpr int NTG = kC / TPT; // token groups per channel group (8 or 16 lanes)
@@ -205,6 +246,7 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
   float* s_beta = reinterpret_cast<float*>(smem + L::kBeta);
   float* s_at = reinterpret_cast<float*>(smem + L::kAt);
   float* s_td = reinterpret_cast<float*>(smem + L::kTd);
+  float* s_nrm = reinterpret_cast<float*>(smem + L::kNrm);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -278,6 +320,7 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
     Frag uf[JB];
     // step 0: the prep waves build chunk 0; fetch chunk 0's v
     if (nch > 0) load_state_v<InT, JB>(sv, a, bos, eos - bos < kC ? eos - bos : kC, h, lq, lj, colw);
+    if constexpr (PRO) __syncthreads();  // the prep waves' chunk-0 norms
     __syncthreads();
     __syncthreads();
     __syncthreads();
@@ -468,6 +511,10 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
   } else {
     PrepIn<InT, TPT> pin;
     if (nch > 0) load_prep<InT, TPT>(pin, a, bos, eos - bos < kC ? eos - bos : kC, h, tg, c0, ptid, want_o);
+    if constexpr (PRO) {
+      if (a.pro_l2 && nch > 0) prep_norm_partials<InT, TPT, NTG>(pin, s_nrm, lane, tg, pw, want_o);
+      __syncthreads();
+    }
     for (int i = 0; i < nch; ++i) {
       // this step builds chunk i into operand set i % 2
       const int tp = bos + i * kC;
@@ -489,8 +536,29 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
           const float gm = (TPT * tg + rr < np) ? kLog2e : 0.0f;  // log2-domain prefix
           InT::unpack4(pin.k[rr], kq[rr]);
           InT::unpack4(pin.q[rr], qv[rr]);
-          gq[rr][0] = pin.g[rr].x * gm; gq[rr][1] = pin.g[rr].y * gm;
-          gq[rr][2] = pin.g[rr].z * gm; gq[rr][3] = pin.g[rr].w * gm;
+          float4 gr = pin.g[rr];
+          if (PRO && a.pro_gate) {
+            gr.x = gate_log_decay(gr.x, a.pro_gmin); gr.y = gate_log_decay(gr.y, a.pro_gmin);
+            gr.z = gate_log_decay(gr.z, a.pro_gmin); gr.w = gate_log_decay(gr.w, a.pro_gmin);
+          }
+          gq[rr][0] = gr.x * gm; gq[rr][1] = gr.y * gm;
+          gq[rr][2] = gr.z * gm; gq[rr][3] = gr.w * gm;
+          if (PRO && a.pro_l2) {
+            // the token's sums of squares: the prep waves' partials, in wave order
+            float sk = 0.0f, sq = 0.0f;
+            const float* src = s_nrm + (TPT * tg + rr) * 8 * 2;
+  #pragma unroll
+            for (int w = 0; w < PW; ++w) {
+              sk += src[2 * w];
+              sq += src[2 * w + 1];
+            }
+            const float rk = 1.0f / sqrtf(sk + a.pro_eps), rq = 1.0f / sqrtf(sq + a.pro_eps);
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              kq[rr][e] = kq[rr][e] * rk;
+              qv[rr][e] = qv[rr][e] * rq;
+            }
+          }
         }
         if (ptid < kC) s_beta[ptid] = ptid < np ? pin.beta : 0.0f;
   #pragma unroll
@@ -705,6 +773,10 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
             Pol::store2(pset + L::kSetKb, L::kKbPlane, off, kbv[0][e], kbv[1][e]);
           }
         }
+        // prologue: the next chunk's norms (its inputs arrived during this step)
+        if constexpr (PRO) {
+          if (a.pro_l2) prep_norm_partials<InT, TPT, NTG>(pin, s_nrm, lane, tg, pw, want_o);
+        }
       }
       __syncthreads();
     }
@@ -745,12 +817,20 @@ hipError_t launch_cfg(const PrefillLaunch& p, hipStream_t stream) {
   a.transition_out = p.transition_out;
   a.checkpoints = p.checkpoints;
   a.ckpt_interval = p.ckpt_interval;
+  a.pro_l2 = p.pro && p.pro->l2norm;
+  a.pro_eps = p.pro ? p.pro->eps : 0.0f;
+  a.pro_gate = p.pro && p.pro->gate;
+  a.pro_gmin = p.pro ? p.pro->g_min : 0.0f;
   const int64_t blocks = int64_t(p.num_seqs) * p.H * a.n_slices;
+  if (p.checkpoints && p.pro) return hipErrorNotSupported;
   if (p.checkpoints)
-    hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, SW, JB, PW, true>), dim3(unsigned(blocks)),
+    hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, SW, JB, PW, true, false>), dim3(unsigned(blocks)),
+                       dim3(prefill_threads(SW, PW)), 0, stream, a);
+  else if (p.pro)
+    hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, SW, JB, PW, false, true>), dim3(unsigned(blocks)),
                        dim3(prefill_threads(SW, PW)), 0, stream, a);
   else
-    hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, SW, JB, PW, false>), dim3(unsigned(blocks)),
+    hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, SW, JB, PW, false, false>), dim3(unsigned(blocks)),
                        dim3(prefill_threads(SW, PW)), 0, stream, a);
   return hipGetLastError();
 }

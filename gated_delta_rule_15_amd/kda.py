@@ -202,16 +202,24 @@ def kda_verify_commit_prologue(k, v, g, beta, state_pool, accepted_len, prologue
 
 def kda_prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host=None, initial_state=None, final_state=None,
                 o=None, transition_out=None, scale: float = 1.0, with_output: bool = True,
-                with_final_state: bool = True):
+                with_final_state: bool = True, prologue: Optional[Prologue] = None):
     """Chunked prefill of a packed ragged batch.
 
     q, k, v, g: [T, H, 128]; beta: [T, H]; cu_seqlens: int32 [N + 1] on the device
     (``cu_seqlens_host``: optional CPU int32 copy, validated by the library).
     Returns (o or None, final_state or None).  ``final_state`` may be the same
-    tensor as ``initial_state`` (in-place continuation).
+    tensor as ``initial_state`` (in-place continuation).  With ``prologue`` the call goes to
+    kda_prefill_prologue (raw q, k; g may hold gate logits).
     """
     return _prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, initial_state, final_state, o, transition_out,
-                    scale, with_output, with_final_state, None)
+                    scale, with_output, with_final_state, None, prologue)
+
+
+def kda_prefill_prologue(q, k, v, g, beta, cu_seqlens, prologue: Prologue, **kw):
+    """kda_prefill with the input prologue (required)."""
+    if prologue is None:
+        raise ValueError("prologue is required")
+    return kda_prefill(q, k, v, g, beta, cu_seqlens, prologue=prologue, **kw)
 
 
 def kda_prefill_ordered(q, k, v, g, beta, cu_seqlens, seq_order, cu_seqlens_host=None, initial_state=None,
@@ -222,11 +230,11 @@ def kda_prefill_ordered(q, k, v, g, beta, cu_seqlens, seq_order, cu_seqlens_host
     if seq_order is None:
         raise ValueError("seq_order is required")
     return _prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, initial_state, final_state, o, transition_out,
-                    scale, with_output, with_final_state, seq_order)
+                    scale, with_output, with_final_state, seq_order, None)
 
 
 def _prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, initial_state, final_state, o, transition_out, scale,
-             with_output, with_final_state, seq_order):
+             with_output, with_final_state, seq_order, prologue):
     T, H, _ = q.shape
     dt = q.dtype
     dev = q.device
@@ -254,7 +262,16 @@ def _prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, initial_state, final
     _need(o, "o", (T, H, D), dt, dev)
     _need(transition_out, "transition_out", (N, H, D, D), torch.float32, dev)
     lib = _lib.load()
-    if seq_order is None:
+    if prologue is not None:
+        if seq_order is not None:
+            raise ValueError("the prologue prefill takes no start order")
+        pc = prologue._c()
+        _lib.check(lib.kda_prefill_prologue(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                                            _ptr(cu_seqlens_host), N, H, D, D, _dtype_code(q), float(scale),
+                                            _ptr(initial_state), _ptr(final_state), _ptr(o), _ptr(transition_out),
+                                            ctypes.addressof(pc), _stream()),
+                   "kda_prefill_prologue")
+    elif seq_order is None:
         _lib.check(lib.kda_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
                                    _ptr(cu_seqlens_host), N, H, D, D, _dtype_code(q), float(scale),
                                    _ptr(initial_state), _ptr(final_state), _ptr(o), _ptr(transition_out), _stream()),

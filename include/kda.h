@@ -180,6 +180,18 @@ kda_status_t kda_prefill(const void* q, const void* k, const void* v, const floa
                          float* final_state, void* o, float* transition_out, void* stream);
 
 /*
+ * kda_prefill_prologue — kda_prefill on raw inputs: the input prologue
+ * (kda_prologue_t above) is applied to q, k and g of every token before the
+ * chunk computation.  Same arguments and results as kda_prefill, plus
+ * `prologue` (required; KDA_ERR_INVALID_ARG for NULL or out-of-range values).
+ */
+kda_status_t kda_prefill_prologue(const void* q, const void* k, const void* v, const float* g,
+                                  const float* beta, const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                                  int32_t num_seqs, int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t dtype,
+                                  float scale, const float* initial_state, float* final_state, void* o,
+                                  float* transition_out, const kda_prologue_t* prologue, void* stream);
+
+/*
  * kda_prefill_ordered — kda_prefill with a caller-chosen order in which the
  * sequences' workgroups are started.  A prefill walks each sequence's chunks
  * in order, so a batch runs as long as its last-started long sequence: with

@@ -33,7 +33,7 @@ def test_header_declares_the_entry_points():
     for name in ("kda_prefill", "kda_decode_step", "kda_verify_block", "kda_verify_commit",
                  "kda_compose_segments", "kda_prefill_checkpointed", "kda_prefill_checkpoint_count",
                  "kda_prefill_ordered", "kda_decode_step_prologue", "kda_verify_block_prologue",
-                 "kda_verify_commit_prologue", "kda_status_string", "kda_version"):
+                 "kda_verify_commit_prologue", "kda_prefill_prologue", "kda_status_string", "kda_version"):
         assert name in syms
     assert set(syms) == set(_lib.SIGNATURES), "binding signatures and header disagree"
 
@@ -142,6 +142,9 @@ def test_prologue_argument_errors(lib):
                                              None) == _lib.KDA_ERR_INVALID_ARG
         assert lib.kda_verify_commit_prologue(p, p, p, p, p, None, p, 2, 8, 2, 128, 128, 1, ref,
                                               None) == _lib.KDA_ERR_INVALID_ARG
+        good = (ctypes.c_int32 * 3)(0, 130, 200)
+        assert lib.kda_prefill_prologue(p, p, p, p, p, p, good, 2, 2, 128, 128, 1, 1.0, None, p, p, None, ref,
+                                        None) == _lib.KDA_ERR_INVALID_ARG
     # a valid prologue leaves the plain checks in place (no launch happens for these)
     ok = Pro(1, 1e-6, 1, -5.0)
     assert lib.kda_decode_step_prologue(p, p, p, p, p, p, None, 2, 2, 64, 128, 1, 1.0, p, ctypes.addressof(ok),

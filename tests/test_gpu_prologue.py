@@ -31,11 +31,28 @@ def _ref_inputs(q, k, g, l2, gate):
     return pro.apply_prologue(q, k, g, l2norm=l2, eps=1e-6, gate_logits=gate, g_min=-5.0)
 
 
+def _valid_inputs(batch, l2, gate):
+    """What the prologue does not do, the caller does: without the gate map the g input must already
+    be a log-decay (<= 0), so the raw logits are mapped on the host in fp32; without the normalisation
+    q and k must already be unit vectors (raw keys of norm ~11 make the recurrence blow up), so they
+    are normalised on the host in fp32 and cast back, as the standard workloads are."""
+    if not gate:
+        x = batch.g.astype(np.float32)
+        batch.g = (np.float32(-5.0) / (np.float32(1.0) + np.exp(-x))).astype(np.float32)
+    if not l2:
+        for name in ("q", "k"):
+            x = getattr(batch, name)
+            f = gen.bf16_bits_to_f32(x) if batch.dtype == "bf16" else x.astype(np.float32)
+            f = f / np.sqrt(np.sum(f * f, axis=-1, keepdims=True, dtype=np.float32))
+            setattr(batch, name, gen.f32_to_bf16_bits(f) if batch.dtype == "bf16" else f.astype(np.float32))
+    return batch
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("l2,gate", VARIANTS)
 def test_decode_prologue_matches_oracle(dtype, l2, gate):
     from gated_delta_rule_15_amd.kda import kda_decode_step
-    b = gen.step_batch(seed=61, N=24, G=1, H=6, dtype=dtype, raw=True)
+    b = _valid_inputs(gen.step_batch(seed=61, N=24, G=1, H=6, dtype=dtype, raw=True), l2, gate)
     d = steps_to_dev(b, squeeze_g=True)
     o = kda_decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], scale=0.8,
                         prologue=_prologue(l2, gate))
@@ -51,7 +68,7 @@ def test_decode_prologue_matches_oracle(dtype, l2, gate):
 @pytest.mark.parametrize("l2,gate", VARIANTS)
 def test_verify_commit_prologue_matches_oracle(dtype, l2, gate):
     from gated_delta_rule_15_amd.kda import kda_verify_block
-    b = gen.step_batch(seed=62, N=12, G=8, H=5, dtype=dtype, accepted=True, raw=True)
+    b = _valid_inputs(gen.step_batch(seed=62, N=12, G=8, H=5, dtype=dtype, accepted=True, raw=True), l2, gate)
     d = steps_to_dev(b)
     o = kda_verify_block(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], accepted_len=d["accepted_len"],
                          scale=0.8, prologue=_prologue(l2, gate))
@@ -100,3 +117,45 @@ def test_prologue_on_prenormalised_inputs_is_close_to_plain():
                          prologue=_prologue(True, False))
     torch.cuda.synchronize()
     assert rel_l2(to_f64(o2), to_f64(o1)) <= 1e-5
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("l2,gate", VARIANTS)
+def test_prefill_prologue_matches_oracle(dtype, l2, gate):
+    """Ragged packed batch with initial states (64-column workgroups), raw inputs."""
+    from gated_delta_rule_15_amd.kda import kda_prefill
+    p = _valid_inputs(gen.packed_batch(seed=65, seqlens=[70, 130, 1, 64, 0, 200], H=3, dtype=dtype,
+                                       init_state=True, raw=True), l2, gate)
+    d = packed_to_dev(p)
+    o, S = kda_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], d["cu_seqlens_host"],
+                       initial_state=d["initial_state"], scale=0.8, prologue=_prologue(l2, gate))
+    torch.cuda.synchronize()
+    q, k, g = _ref_inputs(p.f64("q"), p.f64("k"), p.f64("g"), l2, gate)
+    o_ref, S_ref = orc.prefill(q, k, p.f64("v"), g, p.f64("beta"), p.cu_seqlens, p.initial_state, 0.8)
+    eo, es = rel_l2(to_f64(o), o_ref), rel_l2(to_f64(S), S_ref)
+    print(f"prefill prologue {dtype} l2={l2} gate={gate}: rel-L2 o={eo:.3e} S={es:.3e}")
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
+def test_prefill_prologue_wide_and_transitions():
+    """>= 256 (sequence, head) units (128-column workgroups) with transitions: M of the normalised
+    keys and mapped gates, so that final = M S0 + S~."""
+    from gated_delta_rule_15_amd.kda import kda_prefill
+    lens = [1 + (41 * i) % 120 for i in range(34)]
+    p = gen.packed_batch(seed=66, seqlens=lens, H=8, dtype="bf16", init_state=True, raw=True)
+    d = packed_to_dev(p)
+    N, H = len(lens), 8
+    M = torch.empty((N, H, 128, 128), device="cuda:0")
+    o, S = kda_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], d["cu_seqlens_host"],
+                       initial_state=d["initial_state"], transition_out=M, prologue=_prologue(True, True))
+    torch.cuda.synchronize()
+    q, k, g = _ref_inputs(p.f64("q"), p.f64("k"), p.f64("g"), True, True)
+    o_ref, S_ref = orc.prefill(q, k, p.f64("v"), g, p.f64("beta"), p.cu_seqlens, p.initial_state)
+    eo, es = rel_l2(to_f64(o), o_ref), rel_l2(to_f64(S), S_ref)
+    cu = p.cu_seqlens
+    M_ref = np.stack([np.stack([orc.transition(k[cu[n]:cu[n + 1], h], g[cu[n]:cu[n + 1], h],
+                                               p.f64("beta")[cu[n]:cu[n + 1], h]) for h in range(H)])
+                      for n in range(0, N, 5)])
+    em = rel_l2(to_f64(M)[::5], M_ref)
+    print(f"prefill prologue wide: rel-L2 o={eo:.3e} S={es:.3e} M={em:.3e}")
+    assert eo <= 2e-3 and es <= 2e-3 and em <= 2e-3
