@@ -118,12 +118,15 @@ def graph_time_ms(fns, warmup):
     return start.elapsed_time(end) / len(fns)
 
 
-def bench_decode(steps, warmup, n_sets=8):
+def bench_decode(steps, warmup, n_sets=8, prologue=False):
+    """The decode step (64 x 12, bf16); ``prologue``: raw inputs through kda_decode_step_prologue
+    (same algorithmic bytes: q, k, g are read and o written once either way)."""
     import torch
     from gated_delta_rule_15_amd import inputs as gen
     from gated_delta_rule_15_amd import kda
     N, H = 64, 12
-    b = gen.step_batch(seed=2, N=N, G=1, H=H, dtype="bf16")
+    b = gen.step_batch(seed=2, N=N, G=1, H=H, dtype="bf16", raw=prologue)
+    pro = kda.Prologue() if prologue else None
     sets = []
     for i in range(n_sets):
         sets.append(dict(q=to_dev(b.q[:, 0], "bf16"), k=to_dev(b.k[:, 0], "bf16"), v=to_dev(b.v[:, 0], "bf16"),
@@ -132,19 +135,21 @@ def bench_decode(steps, warmup, n_sets=8):
     fns = []
     for i in range(steps):
         s = sets[i % n_sets]
-        fns.append(lambda s=s: kda.kda_decode_step(s["q"], s["k"], s["v"], s["g"], s["beta"], s["state"], o=s["o"]))
+        fns.append(lambda s=s: kda.kda_decode_step(s["q"], s["k"], s["v"], s["g"], s["beta"], s["state"], o=s["o"],
+                                                   prologue=pro))
     ms = graph_time_ms(fns, warmup)
     nbytes = N * H * decode_bytes_per_head(2)
     return dict(ms=ms, bytes=nbytes, gbps=nbytes / (ms * 1e-3) / 1e9, N=N, H=H, n_sets=n_sets)
 
 
-def bench_verify(reps, warmup, n_sets=8):
+def bench_verify(reps, warmup, n_sets=8, prologue=False):
     import numpy as np
     import torch
     from gated_delta_rule_15_amd import inputs as gen
     from gated_delta_rule_15_amd import kda
     N, G, H = 32, 8, 12
-    b = gen.step_batch(seed=4, N=N, G=G, H=H, dtype="bf16", accepted=True)
+    b = gen.step_batch(seed=4, N=N, G=G, H=H, dtype="bf16", accepted=True, raw=prologue)
+    pro = kda.Prologue() if prologue else None
     sets = []
     for i in range(n_sets):
         sets.append(dict(q=to_dev(b.q, "bf16"), k=to_dev(b.k, "bf16"), v=to_dev(b.v, "bf16"), g=to_dev(b.g),
@@ -154,7 +159,7 @@ def bench_verify(reps, warmup, n_sets=8):
     for i in range(reps):
         s = sets[i % n_sets]
         fns.append(lambda s=s: kda.kda_verify_block(s["q"], s["k"], s["v"], s["g"], s["beta"], s["state"], o=s["o"],
-                                                    accepted_len=s["acc"]))
+                                                    accepted_len=s["acc"], prologue=pro))
     ms = graph_time_ms(fns, warmup)
     per_head_verify = STATE_BYTES + G * (3 * 2 * D + 4 * D + 4) + G * 2 * D
     per_token_commit = 2 * D + 2 * D + 4 * D + 4
@@ -207,6 +212,12 @@ def bench_prefill(reps, warmup):
     C = torch.empty((kda.kda_prefill_checkpoint_count(cu_h, 512), 12, D, D), device="cuda:0")
     ms_ckpt = _event_time_ms(lambda: kda.kda_prefill_checkpointed(q, k, v, g, beta, cu, cu_h, 512, o=o, final_state=S,
                                                                     checkpoints=C), reps, warmup)
+    # raw inputs through the in-kernel prologue (q/k normalisation, gate logits), single launch
+    pr = gen.packed_batch(seed=3, seqlens=[4096], H=12, dtype="bf16", raw=True)
+    qr, kr, gr = to_dev(pr.q, "bf16"), to_dev(pr.k, "bf16"), to_dev(pr.g)
+    pro = kda.Prologue()
+    ms_pro = _event_time_ms(lambda: kda.kda_prefill(qr, kr, v, gr, beta, cu, o=o, final_state=S, prologue=pro),
+                            reps, warmup)
     ms = min(ms_kernel, ms_seg)
     th = 4096 * 12
     flops = th * FLOP_PER_TOKEN_HEAD_PREFILL
@@ -216,7 +227,7 @@ def bench_prefill(reps, warmup):
                 gbps=nbytes / (ms * 1e-3) / 1e9, frac_hbm_peak=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                 path="segmented" if ms_seg < ms_kernel else "single launch",
                 single_launch_ms=ms_kernel, segmented_ms=ms_seg, segment_len=seg, segments=plan.n_rows,
-                single_launch_checkpoints_every_512_ms=ms_ckpt)
+                single_launch_checkpoints_every_512_ms=ms_ckpt, single_launch_prologue_ms=ms_pro)
 
 
 LONG_SUB_SEGMENT = 8192  # each 65,536-token segment of the long sequence runs as 8 fragments
@@ -432,6 +443,12 @@ def main():
         vf = bench_verify(reps=max(16, args.steps // 2), warmup=args.warmup)
         log(f"verify+commit: {vf['ms'] * 1e3:.2f} us, {vf['gbps']:.0f} GB/s")
         rows["verify_commit_32x12x8_bf16"] = vf
+        log("prologue (raw q/k, gate logits): decode 64 x 12, verify+commit 32 x 12 x 8 ...")
+        dp = bench_decode(max(40, args.steps // 4), args.warmup, prologue=True)
+        vp = bench_verify(reps=max(16, args.steps // 2), warmup=args.warmup, prologue=True)
+        log(f"prologue: decode {dp['ms'] * 1e3:.2f} us ({dp['gbps']:.0f} GB/s), verify+commit {vp['ms'] * 1e3:.2f} us")
+        rows["prologue_decode_64x12_bf16"] = dict(ms=dp["ms"], gbps=dp["gbps"])
+        rows["prologue_verify_commit_32x12x8_bf16"] = dict(ms=vp["ms"], gbps=vp["gbps"])
         if args.long:
             log("long context: 1,048,576 + 8 ragged sequences x 12 heads ...")
             lc = bench_long(reps=2, gen_workers=args.gen_workers)

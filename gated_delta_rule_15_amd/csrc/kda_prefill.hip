@@ -127,7 +127,9 @@ struct PrefillArgs {
 
 // Input prologue (the KDA math-details box of the Day-0 lesson page: unit keys;
 // the log-decay bounded below by a scaled sigmoid, g_min = -5).
-__device__ __forceinline__ float gate_log_decay(float x, float g_min) { return g_min / (1.0f + __expf(-x)); }
+__device__ __forceinline__ float gate_log_decay(float x, float g_min) {
+  return g_min * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
 
 
 // Prep-thread inputs of one chunk (TPT tokens x 4 channels), as loaded.
@@ -159,12 +161,30 @@ __device__ __forceinline__ void load_prep(PrepIn<InT, TPT>& in, const PrefillArg
   in.beta = a.beta[int64_t(t0) * a.H + h + (ptid < n ? ptid : n - 1) * a.H];
 }
 
-// Prologue: this prep thread's sums of squares of k and q (its TPT tokens x 4
-// channels), summed over the wave's channel groups (lanes that differ in the
-// bits above the token group) and written per (token, prep wave) to LDS.
+// Sum over the lanes that differ in bits log2(NTG) .. 5 (a wave's channel
+// groups), in every lane: a DPP rotation by 8 within 16-lane rows (NTG = 8),
+// then the 16- and 32-lane permute-swaps.
+template <int NTG>
+__device__ __forceinline__ float sum_channel_groups(float v) {
+  if constexpr (NTG == 8) v = v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+  {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  return v;
+}
+
+// Prologue norms, one chunk ahead of their use: this prep thread's sums of
+// squares of k and q (TPT tokens x 4 channels), summed over the wave's channel
+// groups, are written per (token, prep wave) to LDS.
 template <class InT, int TPT, int NTG>
-__device__ __forceinline__ void prep_norm_partials(const PrepIn<InT, TPT>& pin, float* nrm, int lane, int tg, int pw,
-                                                   bool want_q) {
+__device__ __forceinline__ void prep_prologue(const PrepIn<InT, TPT>& pin, const PrefillArgs& a, float* nrm,
+                                              int lane, int tg, int pw, bool want_q) {
+  if (!a.pro_l2) return;
 #pragma unroll
   for (int rr = 0; rr < TPT; ++rr) {
     float kv[4], qv[4];
@@ -176,11 +196,8 @@ __device__ __forceinline__ void prep_norm_partials(const PrepIn<InT, TPT>& pin, 
       sk = fmaf(kv[e], kv[e], sk);
       sq = fmaf(qv[e], qv[e], sq);
     }
-#pragma unroll
-    for (int m = NTG; m < 64; m <<= 1) {
-      sk += __shfl_xor(sk, m);
-      sq += __shfl_xor(sq, m);
-    }
+    sk = sum_channel_groups<NTG>(sk);
+    sq = sum_channel_groups<NTG>(sq);
     if (lane < NTG) {
       float* dst = nrm + ((TPT * tg + rr) * 8 + pw) * 2;
       dst[0] = sk;
@@ -512,7 +529,7 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
     PrepIn<InT, TPT> pin;
     if (nch > 0) load_prep<InT, TPT>(pin, a, bos, eos - bos < kC ? eos - bos : kC, h, tg, c0, ptid, want_o);
     if constexpr (PRO) {
-      if (a.pro_l2 && nch > 0) prep_norm_partials<InT, TPT, NTG>(pin, s_nrm, lane, tg, pw, want_o);
+      if (nch > 0) prep_prologue<InT, TPT, NTG>(pin, a, s_nrm, lane, tg, pw, want_o);
       __syncthreads();
     }
     for (int i = 0; i < nch; ++i) {
@@ -552,7 +569,7 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
               sk += src[2 * w];
               sq += src[2 * w + 1];
             }
-            const float rk = 1.0f / sqrtf(sk + a.pro_eps), rq = 1.0f / sqrtf(sq + a.pro_eps);
+            const float rk = __builtin_amdgcn_rsqf(sk + a.pro_eps), rq = __builtin_amdgcn_rsqf(sq + a.pro_eps);
   #pragma unroll
             for (int e = 0; e < 4; ++e) {
               kq[rr][e] = kq[rr][e] * rk;
@@ -775,7 +792,7 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
         }
         // prologue: the next chunk's norms (its inputs arrived during this step)
         if constexpr (PRO) {
-          if (a.pro_l2) prep_norm_partials<InT, TPT, NTG>(pin, s_nrm, lane, tg, pw, want_o);
+          prep_prologue<InT, TPT, NTG>(pin, a, s_nrm, lane, tg, pw, want_o);
         }
       }
       __syncthreads();

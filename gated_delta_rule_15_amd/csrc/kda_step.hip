@@ -81,8 +81,10 @@ struct StepArgs {
 // for the readout identity; the log-decay bounded below by a scaled sigmoid,
 // g_min = -5).  The same functions serve the decode step and the staged
 // verify / commit inputs, so all three see bit-identical values.
-__device__ __forceinline__ float gate_log_decay(float x, float g_min) { return g_min / (1.0f + __expf(-x)); }
-__device__ __forceinline__ float inv_l2(float sum_sq, float eps) { return 1.0f / sqrtf(sum_sq + eps); }
+__device__ __forceinline__ float gate_log_decay(float x, float g_min) {
+  return g_min * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
+__device__ __forceinline__ float inv_l2(float sum_sq, float eps) { return __builtin_amdgcn_rsqf(sum_sq + eps); }
 
 // One token's inputs at this lane's 8 rows and 4 columns, as fp32.
 struct TokenVals {
