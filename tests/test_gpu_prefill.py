@@ -228,3 +228,26 @@ def test_prefill_ordered_equals_natural_order(H, transitions):
         if transitions:
             assert torch.equal(M1.view(torch.int32), M2.view(torch.int32))
     _check(p, o1, S1, f"{N} seqs x {H} heads")
+
+
+def test_prefill_all_sequences_empty():
+    """No tokens at all: every final state is the initial state, and no output row is written."""
+    from gated_delta_rule_15_amd.kda import kda_prefill
+    p = gen.packed_batch(seed=14, seqlens=[0, 0, 0], H=2, dtype="bf16", init_state=True)
+    d = packed_to_dev(p)
+    q = torch.zeros((1, 2, 128), dtype=torch.bfloat16, device="cuda:0")
+    g = torch.zeros((1, 2, 128), device="cuda:0")
+    beta = torch.zeros((1, 2), device="cuda:0")
+    o = torch.full((1, 2, 128), 7.0, dtype=torch.bfloat16, device="cuda:0")
+    _, S = kda_prefill(q, q, q, g, beta, d["cu_seqlens"], d["cu_seqlens_host"], initial_state=d["initial_state"],
+                       o=o)
+    torch.cuda.synchronize()
+    assert torch.equal(S, d["initial_state"])
+    assert torch.all(o.float() == 7.0)
+
+
+def test_prefill_long_single_head_bf16():
+    """One head, 3,001 tokens (94 chunks, a ragged tail), bf16: the longest chunk walk of the suite."""
+    p = gen.packed_batch(seed=15, seqlens=[3001], H=1, dtype="bf16", init_state=True)
+    o, S, _ = _run(p)
+    _check(p, o, S, "3001 tokens x 1 head")

@@ -183,3 +183,20 @@ def test_step_kernels_are_deterministic():
     o2, s2, _, _ = _verify(b, commit=True)
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+
+
+def test_verify_of_one_token_is_a_decode_step():
+    """gamma1 = 1: verify's output and the commit of L = 1 equal one decode step, bit for bit."""
+    from gated_delta_rule_15_amd.kda import kda_decode_step, kda_verify_block
+    b = gen.step_batch(seed=45, N=9, G=1, H=5, dtype="bf16")
+    d = steps_to_dev(b)
+    acc = torch.ones(9, dtype=torch.int32, device="cuda:0")
+    committed = d["state"].clone()
+    o_ver = kda_verify_block(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], accepted_len=acc,
+                             state_out_pool=committed)
+    S = d["state"].clone()
+    o_dec = kda_decode_step(d["q"][:, 0].contiguous(), d["k"][:, 0].contiguous(), d["v"][:, 0].contiguous(),
+                            d["g"][:, 0].contiguous(), d["beta"][:, 0].contiguous(), S)
+    torch.cuda.synchronize()
+    assert torch.equal(o_ver[:, 0].contiguous().view(torch.int16), o_dec.view(torch.int16))
+    assert torch.equal(committed.view(torch.int32), S.view(torch.int32))
