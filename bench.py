@@ -230,6 +230,27 @@ def bench_prefill(reps, warmup):
                 single_launch_checkpoints_every_512_ms=ms_ckpt, single_launch_prologue_ms=ms_pro)
 
 
+def bench_prefill_batch(reps, warmup):
+    """32 sequences x 4096 tokens x 12 heads, bf16: 384 (sequence, head) units, the 128-column
+    workgroup shape, one launch (the throughput shape of many independent prompts)."""
+    import torch
+    from gated_delta_rule_15_amd import inputs as gen
+    from gated_delta_rule_15_amd import kda
+    n, T, H = 32, 4096, 12
+    p = gen.packed_batch(seed=3, seqlens=[T] * n, H=H, dtype="bf16")
+    q, k, v = to_dev(p.q, "bf16"), to_dev(p.k, "bf16"), to_dev(p.v, "bf16")
+    g, beta, cu = to_dev(p.g), to_dev(p.beta), to_dev(p.cu_seqlens)
+    o = torch.empty_like(q)
+    S = torch.empty((n, H, D, D), device="cuda:0")
+    ms = _event_time_ms(lambda: kda.kda_prefill(q, k, v, g, beta, cu, o=o, final_state=S), reps, warmup)
+    th = n * T * H
+    flops = th * FLOP_PER_TOKEN_HEAD_PREFILL
+    nbytes = th * BYTES_PER_TOKEN_HEAD_PREFILL_BF16 + n * H * STATE_BYTES
+    return dict(ms=ms, tokens_per_s=n * T / (ms * 1e-3), algorithmic_tflops=flops / (ms * 1e-3) / 1e12,
+                frac_mfma_peak=flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                gbps=nbytes / (ms * 1e-3) / 1e9, frac_hbm_peak=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS)
+
+
 LONG_SUB_SEGMENT = 8192  # each 65,536-token segment of the long sequence runs as 8 fragments
 
 
@@ -403,6 +424,8 @@ def main():
     ap.add_argument("--long", action="store_true", help="also time the 1M-token long-context prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-decode", action="store_true", help="time only the decode rows (for profiling)")
+    ap.add_argument("--only-prefill", action="store_true",
+                    help="time only the prefill rows, 4096 x 12 and 32 x 4096 x 12 (for profiling)")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--write-traffic", metavar="DIR",
                     help="write profiles/decode_64x12_traffic.json from rocprofv3 counter CSVs under DIR")
@@ -430,6 +453,11 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
     log("decode: 64 requests x 12 heads ...")
+    if args.only_prefill:
+        pf = bench_prefill(reps=5, warmup=2)
+        pb = bench_prefill_batch(reps=5, warmup=2)
+        print(json.dumps({"prefill_4096x12_bf16": pf, "prefill_32x4096x12_bf16": pb}), flush=True)
+        return
     dec = bench_decode(args.steps, args.warmup)
     log(f"decode: {dec['ms'] * 1e3:.2f} us/step, {dec['gbps']:.0f} GB/s")
     rows = {}
@@ -439,6 +467,10 @@ def main():
         log(f"prefill: {pf['ms']:.3f} ms, {pf['tokens_per_s'] / 1e6:.2f} M tokens/s ({pf['path']}; single launch "
             f"{pf['single_launch_ms']:.3f} ms, segmented x{pf['segments']} {pf['segmented_ms']:.3f} ms)")
         rows["prefill_4096x12_bf16"] = pf
+        log("prefill: 32 sequences x 4096 tokens x 12 heads ...")
+        pb = bench_prefill_batch(reps=max(3, args.steps // 80), warmup=2)
+        log(f"prefill batch: {pb['ms']:.3f} ms, {pb['tokens_per_s'] / 1e6:.1f} M tokens/s")
+        rows["prefill_32x4096x12_bf16"] = pb
         log("verify+commit: 32 requests x 12 heads x 8 drafts ...")
         vf = bench_verify(reps=max(16, args.steps // 2), warmup=args.warmup)
         log(f"verify+commit: {vf['ms'] * 1e3:.2f} us, {vf['gbps']:.0f} GB/s")
