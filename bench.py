@@ -390,7 +390,7 @@ def write_traffic(prof_dir, out=None):
     write = statistics.mean(dec_w) * 1024 * fw
     alg = 64 * 12 * decode_bytes_per_head(2)
     t = {
-        "kernel": "kda_decode_kernel<BF16>",
+        "kernel": "kda_decode_kernel<BF16, false>",
         "workload": "decode step, 64 requests x 12 heads, d_k=d_v=128, fp32 state in place, bf16 q/k/v/o",
         "source_hash": src_hash("kda_step.hip", "kda_common.hpp"),
         "fetch_size_kib_per_dispatch": round(statistics.mean(dec_f), 1),
@@ -491,7 +491,7 @@ def main():
     traffic = traffic_from_profile(khash)
     roof = dict(bound="hbm", achieved=round(dec["gbps"], 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                 frac=round(dec["gbps"] / HBM_PEAK_GBPS, 4), traffic=traffic,
-                kernel="kda_decode_kernel<BF16>", algorithmic_bytes_per_launch=dec["bytes"],
+                kernel="kda_decode_kernel<BF16, false>", algorithmic_bytes_per_launch=dec["bytes"],
                 mean_launch_us=round(dec["ms"] * 1e3, 3))
     cpu = None
     if not args.no_cpu_baseline:
