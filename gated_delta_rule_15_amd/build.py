@@ -18,9 +18,11 @@ OUT = os.path.join(PKG, "libkda.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
 SOURCES = ["kda_step.hip", "kda_compose.hip", "kda_prefill.hip", "kda_api.hip"]
-# The step kernels must be bit-reproducible between decode, verify and commit:
-# no contraction of separate multiplies and adds into fused operations.
-PER_FILE_FLAGS = {"kda_step.hip": ["-ffp-contract=off"]}
+# No contraction of separate multiplies and adds into fused operations where
+# results must be bit-reproducible across code paths: the step kernels between
+# decode, verify and commit; the prefill between its two workgroup shapes (the
+# compiler's fusion choices could differ between the instantiations).
+PER_FILE_FLAGS = {"kda_step.hip": ["-ffp-contract=off"], "kda_prefill.hip": ["-ffp-contract=off"]}
 
 ARCH = "gfx950"
 COMMON_FLAGS = [

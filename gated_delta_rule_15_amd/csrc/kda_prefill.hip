@@ -24,7 +24,7 @@
 //             registers for the whole sequence and, per chunk, computes
 //             R = V - Kh S, O = Qh S + P U with U = T' R, S = Gamma S + Kb^T U.
 //   waves 4-7 (prep):  build the NEXT chunk's operands: cumulative decay
-//             (in-thread over 4 tokens, then across 8 lanes), Kh, Kc, Qh,
+//             (token pairs in-thread, then a scan over the 16 pairs), Kh, Kc, Qh,
 //             Kb^T, the A and P tiles on MFMA, the 16x16 diagonal inverses of
 //             I + A by right-looking substitution in registers, the
 //             off-diagonal block T_10 = -T_11 A_10 T_00 on MFMA, and T'.
@@ -163,7 +163,9 @@ __device__ __forceinline__ void load_prep(PrepIn<InT, TPT>& in, const PrefillArg
 
 // Sum over the lanes that differ in bits log2(NTG) .. 5 (a wave's channel
 // groups), in every lane: a DPP rotation by 8 within 16-lane rows (NTG = 8),
-// then the 16- and 32-lane permute-swaps.
+// then the 16- and 32-lane permute-swaps.  Either shape sums 4 consecutive
+// channel groups as ((c0 + c1) + (c2 + c3)); the 128-column shape then adds
+// two such sums, the 64-column one leaves that to the cross-wave sum.
 template <int NTG>
 __device__ __forceinline__ float sum_channel_groups(float v) {
   if constexpr (NTG == 8) v = v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
@@ -561,13 +563,27 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
           gq[rr][0] = gr.x * gm; gq[rr][1] = gr.y * gm;
           gq[rr][2] = gr.z * gm; gq[rr][3] = gr.w * gm;
           if (PRO && a.pro_l2) {
-            // the token's sums of squares: the prep waves' partials, in wave order
-            float sk = 0.0f, sq = 0.0f;
+            // the token's sums of squares from the prep waves' partials, in one
+            // association for both shapes: 8-group sums (one wave of 4 prep
+            // waves, or a pair of waves of 8) added in order
             const float* src = s_nrm + (TPT * tg + rr) * 8 * 2;
+            float sk, sq;
+            if constexpr (PW == 8) {
+              sk = src[0] + src[2];
+              sq = src[1] + src[3];
   #pragma unroll
-            for (int w = 0; w < PW; ++w) {
-              sk += src[2 * w];
-              sq += src[2 * w + 1];
+              for (int m = 1; m < 4; ++m) {
+                sk += src[4 * m] + src[4 * m + 2];
+                sq += src[4 * m + 1] + src[4 * m + 3];
+              }
+            } else {
+              sk = src[0];
+              sq = src[1];
+  #pragma unroll
+              for (int m = 1; m < 4; ++m) {
+                sk += src[2 * m];
+                sq += src[2 * m + 1];
+              }
             }
             const float rk = __builtin_amdgcn_rsqf(sk + a.pro_eps), rq = __builtin_amdgcn_rsqf(sq + a.pro_eps);
   #pragma unroll
@@ -578,27 +594,61 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
           }
         }
         if (ptid < kC) s_beta[ptid] = ptid < np ? pin.beta : 0.0f;
-  #pragma unroll
-        for (int rr = 1; rr < TPT; ++rr)
-  #pragma unroll
-          for (int e = 0; e < 4; ++e) gq[rr][e] += gq[rr - 1][e];
-        // inclusive scan over the NTG token groups (consecutive lanes of one
-        // DPP row); lanes shifted in from outside the group contribute 0
-        float excl[4], gam[4], emid[4];
+        // Decay prefix over the chunk's 32 tokens in one association for both
+        // workgroup shapes, so that a sequence's results do not depend on the
+        // launch shape: token pairs (2j, 2j+1) are summed in-thread, the 16 pair
+        // sums are scanned by Hillis-Steele steps of 1, 2, 4 and 8 pairs (DPP
+        // row shifts; pairs before the chunk contribute 0), and a token's
+        // prefix is the exclusive pair prefix plus its own part of its pair.
+        // Reference: b at the chunk's row 15 (its middle), so that every
+        // rescaling exponent b - b_mid of the chunk lies within the decay of
+        // 16 tokens (e^{+-80} at the lower bound g >= -5, inside fp32 range).
+        static_assert(TPT == 2 || TPT == 4, "tokens per prep thread");
+        float bl[TPT][4], gam[4], emid[4];  // log2 cumulative decay relative to b_mid, per token
   #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float x = gq[TPT - 1][e];
-          x += dpp_shr_in_group<1, NTG>(x, tg);
-          x += dpp_shr_in_group<2, NTG>(x, tg);
-          x += dpp_shr_in_group<4, NTG>(x, tg);
-          if constexpr (NTG == 16) x += dpp_shr_in_group<8, NTG>(x, tg);
-          // reference: b at the chunk's row 15 (its middle), so that every
-          // rescaling exponent b - b_mid of the chunk lies within the decay of
-          // 16 tokens (e^{+-80} at the lower bound g >= -5, inside fp32 range)
-          const float bmid = __shfl(x, 15 / TPT, NTG);
-          excl[e] = dpp_shr_in_group<1, NTG>(x, tg) - bmid;
-          gam[e] = __builtin_amdgcn_exp2f(__shfl(x, NTG - 1, NTG) - bmid);  // e^{b_last - b_mid}
-          emid[e] = __builtin_amdgcn_exp2f(bmid);                            // e^{b_mid}
+          float bmid, blast;
+          if constexpr (TPT == 2) {  // one pair per lane, 16 lanes
+            const float p = gq[0][e] + gq[1][e];
+            float y = p;
+            y += dpp_shr_in_group<1, NTG>(y, tg);
+            y += dpp_shr_in_group<2, NTG>(y, tg);
+            y += dpp_shr_in_group<4, NTG>(y, tg);
+            y += dpp_shr_in_group<8, NTG>(y, tg);
+            bmid = __shfl(y, 7, NTG);
+            blast = __shfl(y, 15, NTG);
+            const float ex = dpp_shr_in_group<1, NTG>(y, tg) - bmid;
+            bl[0][e] = ex + gq[0][e];
+            bl[1][e] = ex + p;
+          } else {  // pairs 2 tg and 2 tg + 1 in this lane, 8 lanes
+            const float p0 = gq[0][e] + gq[1][e], p1 = gq[2][e] + gq[3][e];
+            float y0 = p0 + dpp_shr_in_group<1, NTG>(p1, tg);
+            float y1 = p1 + p0;
+            {
+              const float t0 = dpp_shr_in_group<1, NTG>(y0, tg), t1 = dpp_shr_in_group<1, NTG>(y1, tg);
+              y0 += t0;
+              y1 += t1;
+            }
+            {
+              const float t0 = dpp_shr_in_group<2, NTG>(y0, tg), t1 = dpp_shr_in_group<2, NTG>(y1, tg);
+              y0 += t0;
+              y1 += t1;
+            }
+            {
+              const float t0 = dpp_shr_in_group<4, NTG>(y0, tg), t1 = dpp_shr_in_group<4, NTG>(y1, tg);
+              y0 += t0;
+              y1 += t1;
+            }
+            bmid = __shfl(y1, 3, NTG);
+            blast = __shfl(y1, 7, NTG);
+            const float ex0 = dpp_shr_in_group<1, NTG>(y1, tg) - bmid, ex1 = y0 - bmid;
+            bl[0][e] = ex0 + gq[0][e];
+            bl[1][e] = ex0 + p0;
+            bl[2][e] = ex1 + gq[2][e];
+            bl[3][e] = ex1 + p1;
+          }
+          gam[e] = __builtin_amdgcn_exp2f(blast - bmid);  // e^{b_last - b_mid}
+          emid[e] = __builtin_amdgcn_exp2f(bmid);         // e^{b_mid}
         }
   #pragma unroll
         for (int rr = 0; rr < TPT; ++rr) {
@@ -606,7 +656,7 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
           float kh[4], kc[4], qh[4];
   #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float b = excl[e] + gq[rr][e];  // log2 of the cumulative decay, relative to b_mid
+            const float b = bl[rr][e];  // log2 of the cumulative decay, relative to b_mid
             const float eb = __builtin_amdgcn_exp2f(b);
             kh[e] = kq[rr][e] * eb;
             kc[e] = kq[rr][e] * __builtin_amdgcn_exp2f(-b);

@@ -251,3 +251,33 @@ def test_prefill_long_single_head_bf16():
     p = gen.packed_batch(seed=15, seqlens=[3001], H=1, dtype="bf16", init_state=True)
     o, S, _ = _run(p)
     _check(p, o, S, "3001 tokens x 1 head")
+
+
+@pytest.mark.parametrize("prologue", [False, True])
+def test_prefill_batch_invariant_across_launch_shapes(prologue):
+    """A sequence's outputs, final state and transition are bit-identical whether it runs in a small
+    batch (64-column workgroups) or a large one (128-column workgroups): the shapes share one
+    association of every reduction (decay prefix, and the prologue's norms)."""
+    from gated_delta_rule_15_amd.kda import Prologue, kda_prefill
+    lens = [1 + (67 * i) % 180 for i in range(40)]
+    H = 8
+    pro = Prologue() if prologue else None
+    p = gen.packed_batch(seed=16, seqlens=lens, H=H, dtype="bf16", init_state=True, raw=prologue)
+    d = packed_to_dev(p)
+    o_all, S_all = kda_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], d["cu_seqlens_host"],
+                               initial_state=d["initial_state"], prologue=pro)      # 320 units: 128-column shape
+    n = 10
+    cu_sub = d["cu_seqlens"][:n + 1].contiguous()
+    o_sub, S_sub = kda_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_sub, d["cu_seqlens_host"][:n + 1],
+                               initial_state=d["initial_state"][:n].contiguous(), prologue=pro)  # 80 units: 64
+    M_all = torch.empty((len(lens), H, 128, 128), device="cuda:0")
+    M_sub = torch.empty((n, H, 128, 128), device="cuda:0")
+    kda_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], d["cu_seqlens_host"],
+                initial_state=d["initial_state"], transition_out=M_all, prologue=pro)
+    kda_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_sub, d["cu_seqlens_host"][:n + 1],
+                initial_state=d["initial_state"][:n].contiguous(), transition_out=M_sub, prologue=pro)
+    torch.cuda.synchronize()
+    t = int(p.cu_seqlens[n])
+    assert torch.equal(o_all[:t].view(torch.int16), o_sub[:t].view(torch.int16))
+    assert torch.equal(S_all[:n].view(torch.int32), S_sub.view(torch.int32))
+    assert torch.equal(M_all[:n].view(torch.int32), M_sub.view(torch.int32))
