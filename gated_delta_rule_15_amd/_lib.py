@@ -36,6 +36,11 @@ SIGNATURES = {
                                                 _P, _I, _P, _P]),
     "kda_prefill_checkpoint_count": (ctypes.c_int64, [_P, _I, _I]),
     "kda_compose_segments": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
+    "kda_contract_prefill": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _F, _P, _P,
+                                            _P, _P, _P, _P]),
+    "kda_contract_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _F, _P, _P, _P, _P,
+                                           _P, _P]),
+    "kda_contract_state": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
 }
 
 class KdaPrologue(ctypes.Structure):

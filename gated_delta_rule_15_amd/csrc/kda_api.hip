@@ -246,4 +246,48 @@ kda_status_t kda_compose_segments(const float* M, const float* S_tilde, const fl
                                         static_cast<hipStream_t>(stream)));
 }
 
+kda_status_t kda_contract_prefill(const void* q, const void* k, const void* v, const float* g,
+                                  const float* beta, const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                                  int32_t num_seqs, int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t dtype,
+                                  float scale, float* S_pool, float* rows_pool, int32_t* pos_pool,
+                                  const int32_t* slots, void* o, void* stream) {
+  if (num_seqs < 0 || H <= 0) return KDA_ERR_INVALID_ARG;
+  if (!dims_ok(d_k, d_v) || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return KDA_OK;
+  if (!cu_seqlens || !S_pool || !rows_pool || !pos_pool) return KDA_ERR_INVALID_ARG;
+  if (cu_seqlens_host) {
+    if (cu_seqlens_host[0] < 0) return KDA_ERR_INVALID_ARG;
+    for (int32_t i = 0; i < num_seqs; ++i)
+      if (cu_seqlens_host[i + 1] < cu_seqlens_host[i]) return KDA_ERR_INVALID_ARG;
+  }
+  const bool any_tokens = !cu_seqlens_host || cu_seqlens_host[num_seqs] > cu_seqlens_host[0];
+  if (!any_tokens) return KDA_OK;
+  if (!q || !k || !v || !g || !beta) return KDA_ERR_INVALID_ARG;
+  kda::ContractLaunch c{q, k, v, g, beta, cu_seqlens, slots, S_pool, rows_pool, pos_pool, o, num_seqs, H, scale};
+  return hip_status(kda::launch_contract(c, dtype == KDA_BF16, static_cast<hipStream_t>(stream)));
+}
+
+kda_status_t kda_contract_decode(const void* q, const void* k, const void* v, const float* g,
+                                 const float* beta, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
+                                 kda_dtype_t dtype, float scale, float* S_pool, float* rows_pool,
+                                 int32_t* pos_pool, const int32_t* slots, void* o, void* stream) {
+  if (N < 0 || H <= 0) return KDA_ERR_INVALID_ARG;
+  if (!dims_ok(d_k, d_v) || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
+  if (N == 0) return KDA_OK;
+  if (!q || !k || !v || !g || !beta || !S_pool || !rows_pool || !pos_pool) return KDA_ERR_INVALID_ARG;
+  kda::ContractLaunch c{q, k, v, g, beta, nullptr, slots, S_pool, rows_pool, pos_pool, o, N, H, scale};
+  return hip_status(kda::launch_contract(c, dtype == KDA_BF16, static_cast<hipStream_t>(stream)));
+}
+
+kda_status_t kda_contract_state(const float* S_pool, const float* rows_pool, const int32_t* pos_pool,
+                                const int32_t* slots, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
+                                float* state_out, void* stream) {
+  if (N < 0 || H <= 0) return KDA_ERR_INVALID_ARG;
+  if (!dims_ok(d_k, d_v)) return KDA_ERR_UNSUPPORTED;
+  if (N == 0) return KDA_OK;
+  if (!S_pool || !rows_pool || !pos_pool || !state_out) return KDA_ERR_INVALID_ARG;
+  return hip_status(kda::launch_contract_state(S_pool, rows_pool, pos_pool, slots, state_out, N, H,
+                                               static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -1,0 +1,424 @@
+// Batch-invariant row contract: one per-token computation for prefill and decode.
+//
+// The contract (the "Kimi K3.1 Pro" inference / zero-mismatch article,
+// section 6.1 on KDA) replaces the running state by the state S_e at the
+// entry of the open 16-token chunk plus that chunk's rows so far.  A token at
+// position r of the chunk is computed from S_e and the earlier rows only:
+//
+//   b_r = b_{r-1} + g_r                       (cumulative log-decay, b_{-1} = 0)
+//   a_r = S_e^T (k_r e^{b_r}),  w_r = S_e^T (q'_r e^{b_r})          (q' = scale q)
+//   G_k[r,s] = sum_c k_rc k_sc e^{b_rc - b_sc},  G_q[r,s] = sum_c q'_rc k_sc e^{b_rc - b_sc}
+//   u_r = beta_r (v_r - a_r - sum_{s<r} G_k[r,s] u_s)
+//   o_r = w_r + sum_{s<=r} G_q[r,s] u_s
+//
+// and the 16th row closes the chunk: S_e <- Diag(e^{b_15}) S_e +
+// sum_s (k_s e^{b_15 - b_s}) u_s^T.  This is the UT/WY chunk form of the
+// update in "Kimi K3：架构与 SGLang Day-0 Support" ("attention 机制详解：KDA"),
+// restated per row.
+//
+// Every fp32 result is produced by one fixed sequence of operations that does
+// not depend on how many rows a launch takes at once: the decode (one row per
+// call) and the prefill (up to 16 rows of a chunk at once) run the same kernel
+// body, each reduction has one association (a sequential fused multiply-add
+// chain over 16 channels, then the tree ((p0+p1)+(p2+p3))+((p4+p5)+(p6+p7))
+// over the 8 channel groups), sums over earlier rows run in row order, and the
+// file is built without floating-point contraction.  A token's output, the
+// rows and the chunk-entry state are therefore bit-identical whether the
+// token came through a prefill of any length, a decode step, or a batch of
+// any size.
+//
+// Layout per (slot, head): S_e fp32 [128 key][128 value]; rows fp32 [16][3][128]
+// (k_s, b_s, u_s of the open chunk); position int32 (rows held, 0..15).
+// A workgroup (4 waves) owns one (sequence, head).  Wave w holds value columns
+// 32w .. 32w+31 of S_e in registers: lane (m = lane >> 3, jq = lane & 7) holds
+// key rows 16m .. 16m+15 of columns 32w + 4jq .. +3, so the 8 channel groups of
+// every S_e^T x product meet inside the wave (lane bits 3, 4, 5).
+#include "kda_common.hpp"
+#include "kda_internal.hpp"
+
+namespace kda {
+namespace {
+
+constexpr int kChunk = 16;
+constexpr int kThreads = 256;
+constexpr int kRowFloats = 3 * kD;  // k, b, u
+constexpr float kLog2e = 1.4426950408889634f;
+
+// e^x as 2^(x log2 e) on the hardware exponential: one rounding of the
+// product, then v_exp_f32 (about 1 ulp).  Every path of the contract uses it.
+__device__ __forceinline__ float exp_c(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+
+// Value of lane (lane ^ X) for X in {1, 2, 4, 8, 16, 32}.
+template <int X>
+__device__ __forceinline__ float xor_lane(float x) {
+  if constexpr (X == 8) {  // rotate each 16-lane row by 8: lane i reads i ^ 8
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
+  } else if constexpr (X < 32) {  // swizzle bit mode within 32 lanes: and 0x1F, xor X
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x1F | (X << 10)));
+  } else {
+    return __shfl_xor(x, 32, 64);
+  }
+}
+
+struct ContractArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  const int32_t* cu;     // prefill: [num_seqs + 1] token offsets; null: one token per sequence (token n)
+  const int32_t* slots;  // [num_seqs] or null (identity)
+  float* S;              // [P, H, 128, 128]
+  float* rows;           // [P, H, 16, 3, 128]
+  int32_t* pos;          // [P, H]
+  void* o;               // [tokens, H, 128] or null
+  int num_seqs;
+  int H;
+  float scale;
+};
+
+// Rows of the batch being computed (at most MR) next to the open chunk's rows.
+template <int MR>
+struct Lds {
+  float rk[kChunk][kD];  // k_s of the open chunk (k_s e^{b_15 - b_s} while closing)
+  float rb[kChunk][kD];  // b_s
+  float ru[kChunk][kD];  // u_s
+  float sq[MR][kD];      // scale * q_r
+  float kh[MR][kD];      // k_r e^{b_r}
+  float qh[MR][kD];      // scale * q_r e^{b_r}
+  float vv[MR][kD];      // v_r
+  float aa[MR][kD];      // S_e^T k_hat
+  float ww[MR][kD];      // S_e^T q_hat
+  float gk[MR][kChunk];  // G_k[r, s]
+  float gq[MR][kChunk];  // G_q[r, s]
+  float bt[MR];          // beta_r
+  float gam[kD];         // e^{b_15} while closing
+};
+
+// The chunk close on this lane's 16 x 4 block: S <- e^{b_last} S + sum_s kbar_s u_s^T
+// over rows s = 0 .. nrows-1 (kbar already in rk, e^{b_last} in gam).
+__device__ __forceinline__ void close_block(float (&S)[16][4], const float (*rk)[kD], const float (*ru)[kD],
+                                            const float* gam, int nrows, int c0, int j0) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float e = gam[c0 + i];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) S[i][x] = e * S[i][x];
+  }
+  for (int s = 0; s < nrows; ++s) {
+    const float4 u4 = *reinterpret_cast<const float4*>(&ru[s][j0]);
+    const float u[4] = {u4.x, u4.y, u4.z, u4.w};
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const float4 kb4 = *reinterpret_cast<const float4*>(&rk[s][c0 + 4 * i4]);
+      const float kb[4] = {kb4.x, kb4.y, kb4.z, kb4.w};
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) S[4 * i4 + ii][x] = __builtin_fmaf(kb[ii], u[x], S[4 * i4 + ii][x]);
+    }
+  }
+}
+
+// kbar_s = k_s e^{b_last - b_s} in place and gam = e^{b_last}, for rows 0 .. nrows-1.
+__device__ __forceinline__ void close_factors(float (*rk)[kD], const float (*rb)[kD], float* gam, int nrows, int tid) {
+  const int last = nrows - 1;
+  for (int e = tid; e < nrows * kD; e += kThreads) {
+    const int s = e / kD, c = e % kD;
+    rk[s][c] = rk[s][c] * exp_c(rb[last][c] - rb[s][c]);
+  }
+  for (int c = tid; c < kD; c += kThreads) gam[c] = exp_c(rb[last][c]);
+}
+
+template <typename InT, int MR>
+__global__ __launch_bounds__(kThreads) void kda_contract_kernel(ContractArgs a) {
+  __shared__ __align__(16) Lds<MR> L;
+  const int n = blockIdx.x / a.H;
+  const int h = blockIdx.x % a.H;
+  if (n >= a.num_seqs) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  int tok0, count;
+  if (a.cu != nullptr) {
+    tok0 = a.cu[n];
+    count = a.cu[n + 1] - tok0;
+  } else {
+    tok0 = n;
+    count = 1;
+  }
+  if (count <= 0) return;
+  const int64_t unit = int64_t(a.slots ? a.slots[n] : n) * a.H + h;
+  float* Sp = a.S + unit * kD * kD;
+  float* Rp = a.rows + unit * kChunk * kRowFloats;
+  int p = a.pos[unit] & (kChunk - 1);
+  const int p_first = p;
+
+  // this lane's block of S_e: key rows c0 .. c0+15, value columns j0 .. j0+3
+  const int m = lane >> 3;
+  const int c0 = 16 * m;
+  const int j0 = 32 * wave + 4 * (lane & 7);
+  float S[16][4];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float4 s4 = ld_f4(Sp + (c0 + i) * kD + j0);
+    S[i][0] = s4.x; S[i][1] = s4.y; S[i][2] = s4.z; S[i][3] = s4.w;
+  }
+  // the open chunk's rows
+  for (int e = tid; e < p * (kRowFloats / 4); e += kThreads) {
+    const int s = e / (kRowFloats / 4), f = 4 * (e % (kRowFloats / 4));
+    const float4 x = ld_f4(Rp + s * kRowFloats + f);
+    float* dst = (f < kD) ? &L.rk[s][f] : (f < 2 * kD) ? &L.rb[s][f - kD] : &L.ru[s][f - 2 * kD];
+    *reinterpret_cast<float4*>(dst) = x;
+  }
+
+  bool closed = false;
+  int done = 0;
+  while (done < count) {
+    const int r0 = p;
+    const int nr = min(min(MR, kChunk - p), count - done);
+    const int t0 = tok0 + done;
+    // ---- stage the batch rows: k (into the rows), scale * q, v, g (into rb), beta
+    for (int e = tid; e < nr * (kD / 4); e += kThreads) {
+      const int i = e / (kD / 4), c = 4 * (e % (kD / 4));
+      const int64_t base = (int64_t(t0 + i) * a.H + h) * kD + c;
+      float kk[4], qq[4], vv[4];
+      InT::load4(a.k, base, kk);
+      InT::load4(a.q, base, qq);
+      InT::load4(a.v, base, vv);
+      const float4 gg = ld_f4(a.g + base);
+      *reinterpret_cast<float4*>(&L.rk[r0 + i][c]) = make_float4(kk[0], kk[1], kk[2], kk[3]);
+      *reinterpret_cast<float4*>(&L.sq[i][c]) =
+          make_float4(a.scale * qq[0], a.scale * qq[1], a.scale * qq[2], a.scale * qq[3]);
+      *reinterpret_cast<float4*>(&L.vv[i][c]) = make_float4(vv[0], vv[1], vv[2], vv[3]);
+      *reinterpret_cast<float4*>(&L.rb[r0 + i][c]) = gg;
+    }
+    if (tid < nr) L.bt[tid] = a.beta[int64_t(t0 + tid) * a.H + h];
+    __syncthreads();
+    // ---- cumulative decay in row order; rescaled key and query
+    if (tid < kD) {
+      const int c = tid;
+      float b = (r0 > 0) ? L.rb[r0 - 1][c] : 0.0f;
+      for (int i = 0; i < nr; ++i) {
+        b = b + L.rb[r0 + i][c];
+        L.rb[r0 + i][c] = b;
+        const float e = exp_c(b);
+        L.kh[i][c] = L.rk[r0 + i][c] * e;
+        L.qh[i][c] = L.sq[i][c] * e;
+      }
+    }
+    __syncthreads();
+    // ---- a = S_e^T k_hat and w = S_e^T q_hat for every batch row (wave-local)
+    for (int i = 0; i < nr; ++i) {
+      float pa[4] = {0.f, 0.f, 0.f, 0.f}, pw[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const float4 k4 = *reinterpret_cast<const float4*>(&L.kh[i][c0 + 4 * c4]);
+        const float4 q4 = *reinterpret_cast<const float4*>(&L.qh[i][c0 + 4 * c4]);
+        const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
+        const float qv[4] = {q4.x, q4.y, q4.z, q4.w};
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            pa[x] = __builtin_fmaf(S[4 * c4 + cc][x], kv[cc], pa[x]);
+            pw[x] = __builtin_fmaf(S[4 * c4 + cc][x], qv[cc], pw[x]);
+          }
+      }
+      // tree over the 8 channel groups, reduce-scattered: level 1 pairs m, m^1
+      // (lane bit 3) and splits a / w; level 2 pairs m, m^2 (bit 4) and splits
+      // the columns in halves; level 3 pairs m, m^4 (bit 5).
+      const bool b3 = lane & 8, b4 = lane & 16, b5 = lane & 32;
+      float l1[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const float send = b3 ? pa[x] : pw[x];
+        const float keep = b3 ? pw[x] : pa[x];
+        l1[x] = keep + xor_lane<8>(send);
+      }
+      float l2[2];
+#pragma unroll
+      for (int y = 0; y < 2; ++y) {
+        const float send = b4 ? l1[y] : l1[2 + y];
+        const float keep = b4 ? l1[2 + y] : l1[y];
+        l2[y] = keep + xor_lane<16>(send);
+      }
+      const float send = b5 ? l2[0] : l2[1];
+      const float keep = b5 ? l2[1] : l2[0];
+      const float fin = keep + xor_lane<32>(send);
+      const int col = j0 + (b4 ? 2 : 0) + (b5 ? 1 : 0);
+      (b3 ? L.ww : L.aa)[i][col] = fin;
+    }
+    // ---- Gram entries G_k[r, s], G_q[r, s] for s <= r, 8 lanes per entry
+    {
+      const int ntask = nr * (r0 + 1) + nr * (nr - 1) / 2;  // sum over i of (r0 + i + 1)
+      const int cm = 16 * (lane & 7);
+      for (int base = 0; base < ntask; base += kThreads / 8) {
+        const int task = base + (tid >> 3);
+        int i = 0, s = task;
+        while (i < nr - 1 && s >= r0 + i + 1) {  // task -> (batch row i, earlier row s)
+          s -= r0 + i + 1;
+          ++i;
+        }
+        const bool valid = task < ntask;
+        if (!valid) s = 0;
+        const int r = r0 + i;
+        float pk = 0.f, pq = 0.f;
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+          const float4 br = *reinterpret_cast<const float4*>(&L.rb[r][cm + 4 * c4]);
+          const float4 bs = *reinterpret_cast<const float4*>(&L.rb[s][cm + 4 * c4]);
+          const float4 kr = *reinterpret_cast<const float4*>(&L.rk[r][cm + 4 * c4]);
+          const float4 ks = *reinterpret_cast<const float4*>(&L.rk[s][cm + 4 * c4]);
+          const float4 qr = *reinterpret_cast<const float4*>(&L.sq[i][cm + 4 * c4]);
+          const float brv[4] = {br.x, br.y, br.z, br.w}, bsv[4] = {bs.x, bs.y, bs.z, bs.w};
+          const float krv[4] = {kr.x, kr.y, kr.z, kr.w}, ksv[4] = {ks.x, ks.y, ks.z, ks.w};
+          const float qrv[4] = {qr.x, qr.y, qr.z, qr.w};
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc) {
+            const float t = ksv[cc] * exp_c(brv[cc] - bsv[cc]);
+            pk = __builtin_fmaf(krv[cc], t, pk);
+            pq = __builtin_fmaf(qrv[cc], t, pq);
+          }
+        }
+        pk = pk + xor_lane<1>(pk);
+        pq = pq + xor_lane<1>(pq);
+        pk = pk + xor_lane<2>(pk);
+        pq = pq + xor_lane<2>(pq);
+        pk = pk + xor_lane<4>(pk);
+        pq = pq + xor_lane<4>(pq);
+        if (valid && (lane & 7) == 0) {
+          L.gk[i][s] = pk;
+          L.gq[i][s] = pq;
+        }
+      }
+    }
+    __syncthreads();
+    // ---- u for each batch row in row order (one thread per value column)
+    if (tid < kD) {
+      const int j = tid;
+      for (int i = 0; i < nr; ++i) {
+        const int r = r0 + i;
+        float acc = L.vv[i][j] - L.aa[i][j];
+        for (int s = 0; s < r; ++s) acc = __builtin_fmaf(-L.gk[i][s], L.ru[s][j], acc);
+        L.ru[r][j] = L.bt[i] * acc;
+      }
+    }
+    __syncthreads();
+    // ---- outputs
+    if (a.o != nullptr) {
+      for (int e = tid; e < nr * (kD / 4); e += kThreads) {
+        const int i = e / (kD / 4), j = 4 * (e % (kD / 4));
+        const int r = r0 + i;
+        const float4 w4 = *reinterpret_cast<const float4*>(&L.ww[i][j]);
+        float out[4] = {w4.x, w4.y, w4.z, w4.w};
+        for (int s = 0; s <= r; ++s) {
+          const float gq = L.gq[i][s];
+          const float4 u4 = *reinterpret_cast<const float4*>(&L.ru[s][j]);
+          out[0] = __builtin_fmaf(gq, u4.x, out[0]);
+          out[1] = __builtin_fmaf(gq, u4.y, out[1]);
+          out[2] = __builtin_fmaf(gq, u4.z, out[2]);
+          out[3] = __builtin_fmaf(gq, u4.w, out[3]);
+        }
+        InT::store4(a.o, (int64_t(t0 + i) * a.H + h) * kD + j, out);
+      }
+    }
+    p += nr;
+    done += nr;
+    if (p == kChunk) {  // close the chunk
+      close_factors(L.rk, L.rb, L.gam, kChunk, tid);
+      __syncthreads();
+      close_block(S, L.rk, L.ru, L.gam, kChunk, c0, j0);
+      p = 0;
+      closed = true;
+    }
+    __syncthreads();
+  }
+
+  // ---- write back: S_e if a chunk closed, the new open rows, the position
+  if (closed) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) st_f4(Sp + (c0 + i) * kD + j0, make_float4(S[i][0], S[i][1], S[i][2], S[i][3]));
+  }
+  const int first_new = closed ? 0 : p_first;
+  for (int e = tid; e < (p - first_new) * (kRowFloats / 4); e += kThreads) {
+    const int s = first_new + e / (kRowFloats / 4), f = 4 * (e % (kRowFloats / 4));
+    const float* src = (f < kD) ? &L.rk[s][f] : (f < 2 * kD) ? &L.rb[s][f - kD] : &L.ru[s][f - 2 * kD];
+    st_f4(Rp + s * kRowFloats + f, *reinterpret_cast<const float4*>(src));
+  }
+  if (tid == 0) a.pos[unit] = p;
+}
+
+// The running state S_t = Diag(e^{b_p-1}) S_e + sum_{s<p} (k_s e^{b_p-1 - b_s}) u_s^T:
+// the chunk close's arithmetic applied to the rows held, without changing them.
+__global__ __launch_bounds__(kThreads) void kda_contract_state_kernel(const float* __restrict__ S_pool,
+                                                                      const float* __restrict__ rows_pool,
+                                                                      const int32_t* __restrict__ pos_pool,
+                                                                      const int32_t* __restrict__ slots,
+                                                                      float* __restrict__ out, int N, int H) {
+  __shared__ __align__(16) float rk[kChunk][kD];
+  __shared__ __align__(16) float rb[kChunk][kD];
+  __shared__ __align__(16) float ru[kChunk][kD];
+  __shared__ __align__(16) float gam[kD];
+  const int n = blockIdx.x / H;
+  const int h = blockIdx.x % H;
+  if (n >= N) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t unit = int64_t(slots ? slots[n] : n) * H + h;
+  const float* Sp = S_pool + unit * kD * kD;
+  const float* Rp = rows_pool + unit * kChunk * kRowFloats;
+  const int p = pos_pool[unit] & (kChunk - 1);
+  const int c0 = 16 * (lane >> 3);
+  const int j0 = 32 * wave + 4 * (lane & 7);
+  float S[16][4];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float4 s4 = ld_f4(Sp + (c0 + i) * kD + j0);
+    S[i][0] = s4.x; S[i][1] = s4.y; S[i][2] = s4.z; S[i][3] = s4.w;
+  }
+  if (p > 0) {
+    for (int e = tid; e < p * (kRowFloats / 4); e += kThreads) {
+      const int s = e / (kRowFloats / 4), f = 4 * (e % (kRowFloats / 4));
+      const float4 x = ld_f4(Rp + s * kRowFloats + f);
+      float* dst = (f < kD) ? &rk[s][f] : (f < 2 * kD) ? &rb[s][f - kD] : &ru[s][f - 2 * kD];
+      *reinterpret_cast<float4*>(dst) = x;
+    }
+    __syncthreads();
+    close_factors(rk, rb, gam, p, tid);
+    __syncthreads();
+    close_block(S, rk, ru, gam, p, c0, j0);
+  }
+  float* dst = out + int64_t(n * H + h) * kD * kD;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) st_f4(dst + (c0 + i) * kD + j0, make_float4(S[i][0], S[i][1], S[i][2], S[i][3]));
+}
+
+template <typename InT, int MR>
+hipError_t launch_as(const ContractArgs& a, hipStream_t stream) {
+  const unsigned blocks = unsigned(a.num_seqs) * unsigned(a.H);
+  hipLaunchKernelGGL((kda_contract_kernel<InT, MR>), dim3(blocks), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_contract(const ContractLaunch& c, bool bf16, hipStream_t stream) {
+  if (c.num_seqs == 0) return hipSuccess;
+  ContractArgs a{c.q, c.k, c.v, c.g, c.beta, c.cu_seqlens, c.slots, c.S_pool, c.rows_pool, c.pos_pool,
+                 c.o, c.num_seqs, c.H, c.scale};
+  if (c.cu_seqlens == nullptr) return bf16 ? launch_as<BF16, 1>(a, stream) : launch_as<F32, 1>(a, stream);
+  return bf16 ? launch_as<BF16, kChunk>(a, stream) : launch_as<F32, kChunk>(a, stream);
+}
+
+hipError_t launch_contract_state(const float* S_pool, const float* rows_pool, const int32_t* pos_pool,
+                                 const int32_t* slots, float* out, int N, int H, hipStream_t stream) {
+  if (N == 0) return hipSuccess;
+  hipLaunchKernelGGL(kda_contract_state_kernel, dim3(unsigned(N) * unsigned(H)), dim3(kThreads), 0, stream,
+                     S_pool, rows_pool, pos_pool, slots, out, N, H);
+  return hipGetLastError();
+}
+
+}  // namespace kda

@@ -61,4 +61,26 @@ struct PrefillLaunch {
 
 hipError_t launch_prefill(const PrefillLaunch& p, bool bf16, hipStream_t stream);
 
+// ---- batch-invariant row contract (kda_contract.hip) ----------------------
+struct ContractLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  const int32_t* cu_seqlens;  // prefill: [num_seqs + 1]; null: decode, token n is sequence n's one token
+  const int32_t* slots;       // [num_seqs] or null (identity)
+  float* S_pool;              // [P, H, 128, 128] chunk-entry states
+  float* rows_pool;           // [P, H, 16, 3, 128] open-chunk rows
+  int32_t* pos_pool;          // [P, H] rows held
+  void* o;                    // or null
+  int32_t num_seqs;
+  int32_t H;
+  float scale;
+};
+
+hipError_t launch_contract(const ContractLaunch& c, bool bf16, hipStream_t stream);
+hipError_t launch_contract_state(const float* S_pool, const float* rows_pool, const int32_t* pos_pool,
+                                 const int32_t* slots, float* out, int N, int H, hipStream_t stream);
+
 }  // namespace kda

@@ -360,3 +360,121 @@ def kda_compose_segments(M, S_tilde, S_in0=None, S_in=None, S_final=None, with_f
                                         _stream()),
                "kda_compose_segments")
     return S_in, S_final
+
+
+# ---------------------------------------------------------------------------
+# Batch-invariant row contract (kda_contract_* of include/kda.h)
+# ---------------------------------------------------------------------------
+CONTRACT_CHUNK = 16
+
+
+def kda_contract_pools(P: int, H: int, device, initial_state=None):
+    """Allocate contract pools for P slots: (S_pool [P, H, 128, 128] fp32 = initial_state or zeros,
+    rows_pool [P, H, 16, 3, 128] fp32, pos_pool [P, H] int32 = 0)."""
+    S = torch.zeros((P, H, D, D), dtype=torch.float32, device=device)
+    if initial_state is not None:
+        S.copy_(initial_state)
+    rows = torch.zeros((P, H, CONTRACT_CHUNK, 3, D), dtype=torch.float32, device=device)
+    pos = torch.zeros((P, H), dtype=torch.int32, device=device)
+    return S, rows, pos
+
+
+def _need_pools(S_pool, rows_pool, pos_pool, H, dev):
+    if S_pool.dim() != 4 or tuple(S_pool.shape[1:]) != (H, D, D):
+        raise ValueError("S_pool must be [P, H, 128, 128]")
+    P = S_pool.shape[0]
+    _need(S_pool, "S_pool", (P, H, D, D), torch.float32, dev)
+    _need(rows_pool, "rows_pool", (P, H, CONTRACT_CHUNK, 3, D), torch.float32, dev)
+    _need(pos_pool, "pos_pool", (P, H), torch.int32, dev)
+    return P
+
+
+def kda_contract_prefill(q, k, v, g, beta, cu_seqlens, S_pool, rows_pool, pos_pool, cu_seqlens_host=None,
+                         slots=None, o=None, scale: float = 1.0, with_output: bool = True):
+    """Packed ragged batch through the row contract, pools updated in place.
+
+    q, k, v, g: [T, H, 128]; beta: [T, H]; cu_seqlens: device int32 [N + 1]; slots: int32 [N] pool rows
+    (None = 0..N-1).  Returns o [T, H, 128] (dtype of q) or None."""
+    T, H, _ = q.shape
+    dt = q.dtype
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, (T, H, D), dt, dev)
+    _need(g, "g", (T, H, D), torch.float32, dev)
+    _need(beta, "beta", (T, H), torch.float32, dev)
+    if cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be 1-D")
+    _need(cu_seqlens, "cu_seqlens", cu_seqlens.shape, torch.int32, dev)
+    N = cu_seqlens.shape[0] - 1
+    if cu_seqlens_host is not None:
+        if cu_seqlens_host.is_cuda or cu_seqlens_host.dtype != torch.int32 or not cu_seqlens_host.is_contiguous():
+            raise ValueError("cu_seqlens_host must be a contiguous CPU int32 tensor")
+        if cu_seqlens_host.shape != cu_seqlens.shape:
+            raise ValueError("cu_seqlens_host and cu_seqlens differ in shape")
+        if int(cu_seqlens_host[-1]) > T or int(cu_seqlens_host[0]) < 0:
+            raise ValueError("cu_seqlens_host must lie within the packed tokens")
+    P = _need_pools(S_pool, rows_pool, pos_pool, H, dev)
+    if slots is not None:
+        _need(slots, "slots", (N,), torch.int32, dev)
+    elif P < N:
+        raise ValueError("the pools have fewer rows than sequences")
+    if with_output and o is None:
+        o = torch.empty((T, H, D), dtype=dt, device=dev)
+    _need(o, "o", (T, H, D), dt, dev)
+    lib = _lib.load()
+    _lib.check(lib.kda_contract_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                                        _ptr(cu_seqlens_host), N, H, D, D, _dtype_code(q), float(scale),
+                                        _ptr(S_pool), _ptr(rows_pool), _ptr(pos_pool), _ptr(slots), _ptr(o),
+                                        _stream()),
+               "kda_contract_prefill")
+    return o
+
+
+def kda_contract_decode(q, k, v, g, beta, S_pool, rows_pool, pos_pool, slots=None, o=None, scale: float = 1.0,
+                        with_output: bool = True):
+    """One token per request through the row contract, pools updated in place.
+
+    q, k, v, g: [N, H, 128]; beta: [N, H].  Returns o [N, H, 128] (dtype of q) or None."""
+    N, H, _ = q.shape
+    dt = q.dtype
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, (N, H, D), dt, dev)
+    _need(g, "g", (N, H, D), torch.float32, dev)
+    _need(beta, "beta", (N, H), torch.float32, dev)
+    P = _need_pools(S_pool, rows_pool, pos_pool, H, dev)
+    if slots is not None:
+        _need(slots, "slots", (N,), torch.int32, dev)
+    elif P < N:
+        raise ValueError("the pools have fewer rows than requests")
+    if with_output and o is None:
+        o = torch.empty((N, H, D), dtype=dt, device=dev)
+    _need(o, "o", (N, H, D), dt, dev)
+    lib = _lib.load()
+    _lib.check(lib.kda_contract_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), N, H, D, D, _dtype_code(q),
+                                       float(scale), _ptr(S_pool), _ptr(rows_pool), _ptr(pos_pool), _ptr(slots),
+                                       _ptr(o), _stream()),
+               "kda_contract_decode")
+    return o
+
+
+def kda_contract_state(S_pool, rows_pool, pos_pool, slots=None, N: Optional[int] = None, state_out=None):
+    """The running states S_t of N contract slots (slots: int32 [N] or None = 0..N-1) as
+    [N, H, 128, 128] fp32; the pools are not changed."""
+    H = S_pool.shape[1]
+    dev = S_pool.device
+    P = _need_pools(S_pool, rows_pool, pos_pool, H, dev)
+    if N is None:
+        N = slots.shape[0] if slots is not None else P
+    if slots is not None:
+        _need(slots, "slots", (N,), torch.int32, dev)
+    elif P < N:
+        raise ValueError("the pools have fewer rows than requested")
+    if state_out is None:
+        state_out = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
+    _need(state_out, "state_out", (N, H, D, D), torch.float32, dev)
+    lib = _lib.load()
+    _lib.check(lib.kda_contract_state(_ptr(S_pool), _ptr(rows_pool), _ptr(pos_pool), _ptr(slots), N, H, D, D,
+                                      _ptr(state_out), _stream()),
+               "kda_contract_state")
+    return state_out

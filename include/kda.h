@@ -258,6 +258,66 @@ kda_status_t kda_compose_segments(const float* M, const float* S_tilde, const fl
                                   float* S_in, float* S_final, int32_t n_seg, int32_t H,
                                   int32_t d_k, int32_t d_v, void* stream);
 
+/*
+ * Batch-invariant row contract ("Kimi K3.1 Pro" inference / zero-mismatch
+ * article, LLMNews 2026-11-05, section 6.1 on KDA): prefill and decode share
+ * one per-row computation, so a token's output and the stored state are
+ * bit-identical whichever call (prefill of any length, decode step) and
+ * whatever batch computed it.  The state of a (slot, head) is not the running
+ * S_t but the state at the entry of the open 16-token chunk plus that chunk's
+ * rows; a chunk closes (folds its rows into the entry state) when its 16th
+ * row is written.
+ *   S_pool    : [P, H, 128, 128] fp32, chunk-entry states (rows = key channels).
+ *   rows_pool : [P, H, 16, 3, 128] fp32; row s of the open chunk holds its key
+ *               k_s, its cumulative log-decay b_s = g_0 + ... + g_s since the
+ *               chunk entry, and its delta-write vector u_s.
+ *   pos_pool  : [P, H] int32, rows held (0 .. 15); read as pos & 15.
+ *   slots     : device int32 [N] (pool row of request / sequence n), or NULL
+ *               for the identity.  Two entries naming one slot race.
+ * A fresh state is S_pool = S0 (zeros or any initial state) and pos_pool = 0;
+ * rows_pool then needs no initialisation.  The pools are updated in place.
+ * Each row's arithmetic is fp32 with one fixed order of operations; the
+ * results equal the recurrence up to fp32 rounding (the chunk form, restated
+ * per row), not bit for bit the kda_decode_step path.
+ */
+
+/*
+ * kda_contract_prefill — run each sequence's tokens (cu_seqlens as in
+ * kda_prefill; optional host copy validated) through the contract from its
+ * slot's state.  o: [T_total, H, 128] in `dtype`, or NULL.  Empty sequences
+ * leave their state unchanged.
+ * Errors: KDA_ERR_INVALID_ARG for a NULL buffer or a bad cu_seqlens_host;
+ * KDA_ERR_UNSUPPORTED for d != 128 or another dtype; KDA_ERR_HIP on a launch error.
+ */
+kda_status_t kda_contract_prefill(const void* q, const void* k, const void* v, const float* g,
+                                  const float* beta, const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                                  int32_t num_seqs, int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t dtype,
+                                  float scale, float* S_pool, float* rows_pool, int32_t* pos_pool,
+                                  const int32_t* slots, void* o, void* stream);
+
+/*
+ * kda_contract_decode — one token per request (inputs laid out as for
+ * kda_decode_step: q, k, g [N, H, 128], v [N, H, 128], beta [N, H]) through the
+ * contract; o: [N, H, 128] in `dtype`, or NULL.  Reads the entry state and the
+ * open rows, appends one row, and writes the entry state only when the row
+ * closes the chunk.  Errors as kda_contract_prefill.
+ */
+kda_status_t kda_contract_decode(const void* q, const void* k, const void* v, const float* g,
+                                 const float* beta, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
+                                 kda_dtype_t dtype, float scale, float* S_pool, float* rows_pool,
+                                 int32_t* pos_pool, const int32_t* slots, void* o, void* stream);
+
+/*
+ * kda_contract_state — the running state S_t of N contract states:
+ *   S_t = Diag(e^{b_last}) S_e + sum_{s < pos} (k_s e^{b_last - b_s}) u_s^T
+ * (the chunk close applied to the rows held, which stay unchanged), into
+ * state_out [N, H, 128, 128] fp32, e.g. to hand a sequence over to
+ * kda_decode_step.  Errors as kda_contract_prefill.
+ */
+kda_status_t kda_contract_state(const float* S_pool, const float* rows_pool, const int32_t* pos_pool,
+                                const int32_t* slots, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
+                                float* state_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -33,7 +33,8 @@ def test_header_declares_the_entry_points():
     for name in ("kda_prefill", "kda_decode_step", "kda_verify_block", "kda_verify_commit",
                  "kda_compose_segments", "kda_prefill_checkpointed", "kda_prefill_checkpoint_count",
                  "kda_prefill_ordered", "kda_decode_step_prologue", "kda_verify_block_prologue",
-                 "kda_verify_commit_prologue", "kda_prefill_prologue", "kda_status_string", "kda_version"):
+                 "kda_verify_commit_prologue", "kda_prefill_prologue", "kda_contract_prefill",
+                 "kda_contract_decode", "kda_contract_state", "kda_status_string", "kda_version"):
         assert name in syms
     assert set(syms) == set(_lib.SIGNATURES), "binding signatures and header disagree"
 
@@ -161,6 +162,41 @@ def test_compose_argument_errors(lib):
     assert lib.kda_compose_segments(None, p, None, p, None, 3, 2, 128, 128, None) == _lib.KDA_ERR_INVALID_ARG
     assert lib.kda_compose_segments(p, p, None, p, None, 3, 2, 32, 128, None) == _lib.KDA_ERR_UNSUPPORTED
     assert lib.kda_compose_segments(None, None, None, None, None, 0, 2, 128, 128, None) == 0
+
+
+def test_contract_argument_errors(lib):
+    p = ctypes.c_void_p(16)  # never dereferenced: every call below fails validation first
+    E, U = _lib.KDA_ERR_INVALID_ARG, _lib.KDA_ERR_UNSUPPORTED
+    # decode: sizes, dims, dtype, missing buffers (o and slots may be NULL)
+    assert lib.kda_contract_decode(p, p, p, p, p, -1, 2, 128, 128, 1, 1.0, p, p, p, None, p, None) == E
+    assert lib.kda_contract_decode(p, p, p, p, p, 4, 0, 128, 128, 1, 1.0, p, p, p, None, p, None) == E
+    assert lib.kda_contract_decode(p, p, p, p, p, 4, 2, 64, 128, 1, 1.0, p, p, p, None, p, None) == U
+    assert lib.kda_contract_decode(p, p, p, p, p, 4, 2, 128, 128, 5, 1.0, p, p, p, None, p, None) == U
+    assert lib.kda_contract_decode(p, p, p, p, p, 4, 2, 128, 128, 1, 1.0, p, None, p, None, p, None) == E
+    assert lib.kda_contract_decode(p, p, p, p, p, 4, 2, 128, 128, 1, 1.0, p, p, None, None, p, None) == E
+    assert lib.kda_contract_decode(None, p, p, p, p, 4, 2, 128, 128, 1, 1.0, p, p, p, None, p, None) == E
+    assert lib.kda_contract_decode(None, None, None, None, None, 0, 2, 128, 128, 1, 1.0, None, None, None, None,
+                                   None, None) == 0
+    # prefill: cu_seqlens checks on the host copy, missing pools
+    good = (ctypes.c_int32 * 3)(0, 5, 9)
+    bad = (ctypes.c_int32 * 3)(0, 5, 4)
+    neg = (ctypes.c_int32 * 3)(-1, 5, 9)
+    empty = (ctypes.c_int32 * 3)(3, 3, 3)
+    args = lambda cu_h, S=p, R=p, P=p: (p, p, p, p, p, p, cu_h, 2, 2, 128, 128, 1, 1.0, S, R, P, None, p, None)
+    assert lib.kda_contract_prefill(*args(bad)) == E
+    assert lib.kda_contract_prefill(*args(neg)) == E
+    assert lib.kda_contract_prefill(*args(good, R=None)) == E
+    assert lib.kda_contract_prefill(*args(good, P=None)) == E
+    assert lib.kda_contract_prefill(None, None, None, None, None, p, empty, 2, 2, 128, 128, 1, 1.0, p, p, p, None,
+                                    None, None) == 0  # no tokens: nothing to do, inputs may be NULL
+    assert lib.kda_contract_prefill(None, p, p, p, p, p, good, 2, 2, 128, 128, 1, 1.0, p, p, p, None, p, None) == E
+    assert lib.kda_contract_prefill(p, p, p, p, p, None, good, 2, 2, 128, 128, 1, 1.0, p, p, p, None, p, None) == E
+    assert lib.kda_contract_prefill(p, p, p, p, p, p, good, 2, 2, 128, 128, 3, 1.0, p, p, p, None, p, None) == U
+    # state
+    assert lib.kda_contract_state(p, p, p, None, 2, 2, 128, 128, None, None) == E
+    assert lib.kda_contract_state(p, None, p, None, 2, 2, 128, 128, p, None) == E
+    assert lib.kda_contract_state(p, p, p, None, 2, 2, 128, 96, p, None) == U
+    assert lib.kda_contract_state(None, None, None, None, 0, 2, 128, 128, None, None) == 0
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

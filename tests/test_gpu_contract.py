@@ -1,0 +1,280 @@
+"""GPU tests of the batch-invariant row contract (kda_contract_*).
+
+Parity: outputs, the chunk-entry states, the open rows and the running state
+(kda_contract_state) against the fp64 contract oracle and the token recurrence,
+relative L2 within 2e-3 for bf16 inputs and 1e-5 for fp32 inputs.
+Bit-identity, the contract's purpose: one sequence gives the same output and
+state bits whether it runs as one prefill, as a prefill cut anywhere followed
+by decode steps and more prefill, alone or inside a batch.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_15_amd import inputs as gen
+from oracle import kda_contract as cf
+from oracle import kda_oracle as orc
+
+from kda_testutil import DEV, bf16_floor, rel_l2, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-3, "f32": 1e-5}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib_loaded():
+    from gated_delta_rule_15_amd import kda  # noqa: F401
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _kda():
+    from gated_delta_rule_15_amd import kda
+    return kda
+
+
+def _slice(p: gen.Packed, ranges):
+    """Device tensors of the token ranges [a_n, b_n) of each sequence of p, packed."""
+    idx, cu = [], [0]
+    for n, (a, b) in enumerate(ranges):
+        s0 = int(p.cu_seqlens[n])
+        idx.extend(range(s0 + a, s0 + b))
+        cu.append(cu[-1] + (b - a))
+    idx = np.asarray(idx, dtype=np.int64)
+    pick = lambda x: np.ascontiguousarray(x[idx])
+    return dict(q=to_dev(pick(p.q), p.dtype), k=to_dev(pick(p.k), p.dtype), v=to_dev(pick(p.v), p.dtype),
+                g=to_dev(pick(p.g)), beta=to_dev(pick(p.beta)),
+                cu_seqlens=to_dev(np.asarray(cu, dtype=np.int32)),
+                cu_seqlens_host=torch.tensor(cu, dtype=torch.int32))
+
+
+def _prefill(d, pools, **kw):
+    S, R, P = pools
+    o = _kda().kda_contract_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], S, R, P,
+                                    cu_seqlens_host=d["cu_seqlens_host"], **kw)
+    torch.cuda.synchronize()
+    return o
+
+
+def _decode_token(p: gen.Packed, t_of_seq, pools, **kw):
+    """One decode step: token t_of_seq[n] of every sequence n."""
+    idx = np.asarray([int(p.cu_seqlens[n]) + t for n, t in enumerate(t_of_seq)], dtype=np.int64)
+    pick = lambda x: np.ascontiguousarray(x[idx])
+    S, R, P = pools
+    o = _kda().kda_contract_decode(to_dev(pick(p.q), p.dtype), to_dev(pick(p.k), p.dtype),
+                                   to_dev(pick(p.v), p.dtype), to_dev(pick(p.g)), to_dev(pick(p.beta)),
+                                   S, R, P, **kw)
+    torch.cuda.synchronize()
+    return o
+
+
+def _pools(p: gen.Packed):
+    S0 = None if p.initial_state is None else to_dev(p.initial_state)
+    return _kda().kda_contract_pools(p.num_seqs, p.H, DEV, S0)
+
+
+def _oracle_states(p: gen.Packed):
+    dk, dv = p.k.shape[2], p.v.shape[2]
+    S0 = p.initial_state if p.initial_state is not None else np.zeros((p.num_seqs, p.H, dk, dv))
+    return [[cf.ContractState(S0[n, h]) for h in range(p.H)] for n in range(p.num_seqs)]
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+def _assert_same_state(a, b, slots=None):
+    """Same entry-state bits, positions and open rows (rows at or past the position are stale)."""
+    sl = slice(None) if slots is None else slots
+    assert torch.equal(a[2][sl], b[2][sl])
+    assert torch.equal(_bits(a[0][sl]), _bits(b[0][sl]))
+    pos = a[2][sl].cpu()
+    ra, rb = a[1][sl].cpu(), b[1][sl].cpu()
+    for i in range(pos.shape[0]):
+        for h in range(pos.shape[1]):
+            r = int(pos[i, h])
+            assert torch.equal(_bits(ra[i, h, :r]), _bits(rb[i, h, :r]))
+
+
+def _check_pools_against_oracle(pools, states, tol):
+    S, R, P = (x.cpu() for x in pools)
+    for n, row in enumerate(states):
+        for h, st in enumerate(row):
+            assert int(P[n, h]) == st.pos
+            assert rel_l2(S[n, h].double().numpy(), st.S_e) <= tol
+            for s, (k_s, b_s, u_s) in enumerate(st.rows):
+                assert np.array_equal(R[n, h, s, 0].double().numpy(), k_s)  # keys are stored exactly
+                np.testing.assert_allclose(R[n, h, s, 1].double().numpy(), b_s, rtol=1e-6, atol=1e-6)
+                assert rel_l2(R[n, h, s, 2].double().numpy(), u_s) <= 10 * tol
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_then_decode_match_oracle(dtype):
+    lens = [1, 15, 16, 17, 50, 0, 77, 33]
+    H = 3
+    p = gen.packed_batch(seed=31, seqlens=[L + 20 for L in lens], H=H, dtype=dtype,
+                         init_state=[True, False, True, True, False, True, False, True])
+    pools = _pools(p)
+    states = _oracle_states(p)
+    # prefill the first lens[n] tokens of every sequence
+    o = _prefill(_slice(p, [(0, L) for L in lens]), pools, scale=0.75)
+    q, k, v, g, beta = (p.f64(x) for x in ("q", "k", "v", "g", "beta"))
+    o_ref = np.full((sum(lens), H, 128), np.nan)
+    t = 0
+    for n, L in enumerate(lens):
+        s0 = int(p.cu_seqlens[n])
+        for h in range(H):
+            o_ref[t:t + L, h] = cf.contract_tokens(states[n][h], q[s0:s0 + L, h], k[s0:s0 + L, h], v[s0:s0 + L, h],
+                                                   g[s0:s0 + L, h], beta[s0:s0 + L, h], scale=0.75)
+        t += L
+    eo = rel_l2(to_f64(o), o_ref)
+    print(f"contract prefill {dtype}: rel-L2 o={eo:.3e} (bf16 floor {bf16_floor(o_ref):.3e})")
+    assert eo <= TOL[dtype]
+    _check_pools_against_oracle(pools, states, TOL[dtype])
+    # 20 decode steps on top (crossing chunk closes at different steps per sequence)
+    errs = []
+    for step in range(20):
+        od = _decode_token(p, [L + step for L in lens], pools, scale=0.75)
+        od_ref = np.empty((len(lens), H, 128))
+        for n, L in enumerate(lens):
+            tt = int(p.cu_seqlens[n]) + L + step
+            for h in range(H):
+                od_ref[n, h] = cf.contract_tokens(states[n][h], q[tt:tt + 1, h], k[tt:tt + 1, h], v[tt:tt + 1, h],
+                                                  g[tt:tt + 1, h], beta[tt:tt + 1, h], scale=0.75)[0]
+        errs.append(rel_l2(to_f64(od), od_ref))
+    print(f"contract decode {dtype}: max rel-L2 o over 20 steps {max(errs):.3e}")
+    assert max(errs) <= TOL[dtype]
+    _check_pools_against_oracle(pools, states, TOL[dtype])
+    # the running state equals the token recurrence over all tokens taken
+    S_run = to_f64(_kda().kda_contract_state(*pools))
+    _, S_ref = orc.prefill(q, k, v, g, beta, p.cu_seqlens, p.initial_state, scale=0.75)
+    es = rel_l2(S_run, S_ref)
+    print(f"contract running state {dtype}: rel-L2 {es:.3e}")
+    assert es <= TOL[dtype]
+
+
+def test_paths_are_bit_identical():
+    """One prefill of everything == prefill of a prefix, decode steps, prefill of the rest."""
+    lens = [40, 23, 64, 9, 18]
+    p = gen.packed_batch(seed=32, seqlens=lens, H=2, dtype="bf16", init_state=True)
+    whole = _pools(p)
+    o_whole = _prefill(_slice(p, [(0, L) for L in lens]), whole)
+    cut = [13, 0, 16, 2, 11]
+    steps = 5
+    split = _pools(p)
+    o1 = _prefill(_slice(p, [(0, c) for c in cut]), split)
+    od = [_decode_token(p, [c + s for c in cut], split) for s in range(steps)]
+    o3 = _prefill(_slice(p, [(c + steps, L) for c, L in zip(cut, lens)]), split)
+    # reassemble the split run's outputs in packed order
+    parts, a1, a3 = [], 0, 0
+    for n, (c, L) in enumerate(zip(cut, lens)):
+        parts.append(o1[a1:a1 + c])
+        parts.extend(od[s][n:n + 1] for s in range(steps))
+        parts.append(o3[a3:a3 + L - c - steps])
+        a1 += c
+        a3 += L - c - steps
+    o_split = torch.cat(parts)
+    assert torch.equal(_bits(o_split), _bits(o_whole))
+    _assert_same_state(whole, split)
+
+
+def test_batch_invariance():
+    """A sequence's bits do not depend on what else is in its batch (prefill and decode)."""
+    lens = [37, 5, 64, 19, 1, 50]
+    p = gen.packed_batch(seed=33, seqlens=[L + 1 for L in lens] + [3], H=4, dtype="bf16", init_state=True)
+    full = _pools(p)
+    o_full = _prefill(_slice(p, [(0, L) for L in lens] + [(0, 0)]), full)
+    od_full = _decode_token(p, lens + [0], full)
+    for n in (0, 2, 4):
+        alone = _pools(p)
+        slots = torch.tensor([n], dtype=torch.int32, device=DEV)
+        d = _slice(p, [(0, lens[n]) if m == n else (0, 0) for m in range(len(lens) + 1)])
+        keep = torch.arange(sum(lens[:n]), sum(lens[:n + 1]))
+        d1 = dict(q=d["q"], k=d["k"], v=d["v"], g=d["g"], beta=d["beta"],
+                  cu_seqlens=torch.tensor([0, lens[n]], dtype=torch.int32, device=DEV),
+                  cu_seqlens_host=torch.tensor([0, lens[n]], dtype=torch.int32))
+        o1 = _prefill(d1, alone, slots=slots)
+        assert torch.equal(_bits(o1), _bits(o_full[keep.to(DEV)]))
+        tt = int(p.cu_seqlens[n]) + lens[n]
+        od1 = _kda().kda_contract_decode(to_dev(p.q[tt:tt + 1], "bf16"), to_dev(p.k[tt:tt + 1], "bf16"),
+                                         to_dev(p.v[tt:tt + 1], "bf16"), to_dev(p.g[tt:tt + 1]),
+                                         to_dev(p.beta[tt:tt + 1]), *alone, slots=slots)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(od1[0]), _bits(od_full[n]))
+        _assert_same_state(alone, full, [n])
+
+
+def test_empty_sequences_and_slots():
+    """Empty sequences leave their slot untouched; slots route sequences to pool rows."""
+    lens = [0, 21, 0, 16]
+    p = gen.packed_batch(seed=34, seqlens=lens, H=2, dtype="bf16", init_state=True)
+    P = 6
+    S0 = torch.zeros((P, 2, 128, 128), dtype=torch.float32, device=DEV)
+    S0[:4] = to_dev(p.initial_state)
+    pools = _kda().kda_contract_pools(P, 2, DEV, S0)
+    pools[1].normal_()  # stale rows in the pool must not matter at position 0
+    slots = torch.tensor([5, 0, 2, 3], dtype=torch.int32, device=DEV)
+    # sequence n of the batch uses slot slots[n]; give each slot its sequence's initial state
+    for n in range(4):
+        pools[0][int(slots[n])] = S0[n]
+    before = [x.clone() for x in pools]
+    o = _prefill(_slice(p, [(0, L) for L in lens]), pools, slots=slots)
+    for n in (0, 2):  # empty: slot unchanged, bit for bit
+        sl = int(slots[n])
+        for x, y in zip(pools, before):
+            assert torch.equal(x[sl], y[sl])
+    for sl in (1, 4):  # untouched slots
+        for x, y in zip(pools, before):
+            assert torch.equal(x[sl], y[sl])
+    states = _oracle_states(p)
+    q, k, v, g, beta = (p.f64(x) for x in ("q", "k", "v", "g", "beta"))
+    o_ref = np.empty((37, 2, 128))
+    for n, (a, b) in ((1, (0, 21)), (3, (21, 37))):
+        for h in range(2):
+            o_ref[a:b, h] = cf.contract_tokens(states[n][h], q[a:b, h], k[a:b, h], v[a:b, h], g[a:b, h], beta[a:b, h])
+    assert rel_l2(to_f64(o), o_ref) <= 2e-3
+    assert int(pools[2][int(slots[1]), 0]) == 5 and int(pools[2][int(slots[3]), 1]) == 0
+    # an all-empty batch is a no-op
+    _prefill(_slice(p, [(0, 0)] * 4), pools, slots=slots)
+    # no output buffer: same state as with one
+    again = _kda().kda_contract_pools(P, 2, DEV, S0)
+    for n in range(4):
+        again[0][int(slots[n])] = S0[n]
+    _prefill(_slice(p, [(0, L) for L in lens]), again, slots=slots, with_output=False)
+    for x, y in zip(again[:1] + again[2:], pools[:1] + pools[2:]):
+        assert torch.equal(x, y)
+
+
+def test_decode_workload_sampled_parity():
+    """Decode at 64 requests x 12 heads, each at its own position in the open chunk (prefix of
+    16 + pos tokens prefilled), one step; sampled (request, head) units against the oracle."""
+    N, H = 64, 12
+    rng = np.random.default_rng(35)
+    pos = rng.integers(0, 16, N)
+    lens = [16 + int(x) + 1 for x in pos]
+    p = gen.packed_batch(seed=35, seqlens=lens, H=H, dtype="bf16", init_state=True)
+    pools = _pools(p)
+    _prefill(_slice(p, [(0, L - 1) for L in lens]), pools, with_output=False)
+    assert torch.equal(pools[2].cpu(), torch.tensor(np.repeat(pos[:, None], H, 1), dtype=torch.int32))
+    od = _decode_token(p, [L - 1 for L in lens], pools)
+    q, k, v, g, beta = (p.f64(x) for x in ("q", "k", "v", "g", "beta"))
+    for n, h in [(0, 0), (5, 11), (17, 3), (31, 7), (42, 0), (63, 11)] + [(int(np.argmax(pos == 15)), 2)]:
+        a, b = int(p.cu_seqlens[n]), int(p.cu_seqlens[n + 1])
+        o_ref, _ = orc.recurrence(q[a:b, h], k[a:b, h], v[a:b, h], g[a:b, h], beta[a:b, h], p.initial_state[n, h])
+        assert rel_l2(to_f64(od[n, h]), o_ref[-1]) <= 2e-3
+
+
+def test_prefill_workload_sampled_parity():
+    """4096 tokens x 12 heads in one prefill; heads 0 and 7 against the token recurrence."""
+    p = gen.packed_batch(seed=36, seqlens=[4096], H=12, dtype="bf16")
+    pools = _pools(p)
+    o = _prefill(_slice(p, [(0, 4096)]), pools)
+    S_run = to_f64(_kda().kda_contract_state(*pools))
+    q, k, v, g, beta = (p.f64(x) for x in ("q", "k", "v", "g", "beta"))
+    for h in (0, 7):
+        o_ref, S_ref = orc.recurrence(q[:, h], k[:, h], v[:, h], g[:, h], beta[:, h])
+        eo, es = rel_l2(to_f64(o[:, h]), o_ref), rel_l2(S_run[0, h], S_ref)
+        print(f"contract prefill 4096 x 12, head {h}: rel-L2 o={eo:.3e} S={es:.3e}")
+        assert eo <= 2e-3 and es <= 2e-3
+    assert int(pools[2][0, 0]) == 0  # 4096 = 256 closed chunks
