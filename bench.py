@@ -39,6 +39,21 @@ D = 128
 FLOP_PER_TOKEN_HEAD_PREFILL = 6 * D * D + 10 * 64 * D  # 180,224 algorithmic flop (chunk 64)
 BYTES_PER_TOKEN_HEAD_PREFILL_BF16 = 3 * 2 * D + 4 * D + 4 + 2 * D  # q,k,v bf16 + g fp32 + beta + o bf16 = 1540
 STATE_BYTES = D * D * 4
+FP32_VALU_PEAK_TFLOPS = 157.3
+
+# Row contract (16-token chunks), per token-head, averaged over the 16 positions r of a chunk:
+#   S_e^T k_hat and S_e^T q_hat: 2 * 2 * D * D flop; Gram entries for s <= r: (r + 1) * D * 7
+#   (difference, exponential, product, two fused multiply-adds); u and o: (2r + 1) * 2 * D;
+#   the close once per 16 tokens: 16 * D * 3 (key factors) + D * D * (1 + 2 * 16) (the S_e update).
+CONTRACT_CHUNK = 16
+FLOP_PER_TOKEN_HEAD_CONTRACT = (4 * D * D + sum((r + 1) * D * 7 + (2 * r + 1) * 2 * D for r in range(16)) / 16
+                                + (16 * D * 3 + D * D * 33) / 16)
+# Decode through the contract, per (request, head) and step, averaged over the 16 positions: read
+# S_e; read the r open rows (k, b, u fp32); write the new row unless it closes the chunk; write S_e
+# when it does; q/k/v bf16, g fp32, beta in; o bf16 out; position read and written.
+ROW_BYTES = 3 * D * 4
+CONTRACT_DECODE_BYTES_PER_HEAD = (STATE_BYTES + sum(r * ROW_BYTES for r in range(16)) / 16
+                                  + ROW_BYTES * 15 / 16 + STATE_BYTES / 16 + 3 * 2 * D + 4 * D + 4 + 2 * D + 8)
 
 
 def decode_bytes_per_head(in_bytes=2):
@@ -251,6 +266,55 @@ def bench_prefill_batch(reps, warmup):
                 gbps=nbytes / (ms * 1e-3) / 1e9, frac_hbm_peak=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS)
 
 
+def bench_contract(steps, warmup, n_sets=8):
+    """The batch-invariant row contract: decode 64 x 12 (each request at its own position in the
+    open 16-token chunk, uniform over 0..15; 8 rotated pool sets; every set takes a multiple of 16
+    calls per replay, so each request passes every position equally often), and the contract
+    prefill of 4096 x 12 and 32 x 4096 x 12 (bf16)."""
+    import numpy as np
+    import torch
+    from gated_delta_rule_15_amd import inputs as gen
+    from gated_delta_rule_15_amd import kda
+    N, H = 64, 12
+    rng = np.random.default_rng(37)
+    pos = rng.integers(0, CONTRACT_CHUNK, N)
+    lens = [CONTRACT_CHUNK + int(x) + 1 for x in pos]
+    p = gen.packed_batch(seed=37, seqlens=lens, H=H, dtype="bf16", init_state=True)
+    pre = np.concatenate([np.arange(p.cu_seqlens[n], p.cu_seqlens[n + 1] - 1) for n in range(N)])
+    last = p.cu_seqlens[1:] - 1
+    cu_pre = np.concatenate([[0], np.cumsum([L - 1 for L in lens])]).astype(np.int32)
+    base = kda.kda_contract_pools(N, H, "cuda:0", to_dev(p.initial_state))
+    kda.kda_contract_prefill(to_dev(p.q[pre], "bf16"), to_dev(p.k[pre], "bf16"), to_dev(p.v[pre], "bf16"),
+                             to_dev(p.g[pre]), to_dev(p.beta[pre]), to_dev(cu_pre), *base, with_output=False)
+    tok = dict(q=to_dev(p.q[last], "bf16"), k=to_dev(p.k[last], "bf16"), v=to_dev(p.v[last], "bf16"),
+               g=to_dev(p.g[last]), beta=to_dev(p.beta[last]))
+    sets = [tuple(x.clone() for x in base) for _ in range(n_sets)]
+    outs = [torch.empty((N, H, D), dtype=torch.bfloat16, device="cuda:0") for _ in range(n_sets)]
+    calls = max(CONTRACT_CHUNK * n_sets, (steps // (CONTRACT_CHUNK * n_sets)) * CONTRACT_CHUNK * n_sets)
+    fns = [lambda i=i: kda.kda_contract_decode(tok["q"], tok["k"], tok["v"], tok["g"], tok["beta"],
+                                               *sets[i % n_sets], o=outs[i % n_sets]) for i in range(calls)]
+    ms = graph_time_ms(fns, warmup)
+    nbytes = N * H * CONTRACT_DECODE_BYTES_PER_HEAD
+    dec = dict(ms=ms, bytes=nbytes, gbps=nbytes / (ms * 1e-3) / 1e9,
+               frac_hbm_peak=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, N=N, H=H, n_sets=n_sets, calls=calls)
+    del sets, outs
+    res = {"contract_decode_64x12_bf16": dec}
+    for n_seq in (1, 32):
+        T = 4096
+        pf = gen.packed_batch(seed=3, seqlens=[T] * n_seq, H=H, dtype="bf16")
+        q, k, v = to_dev(pf.q, "bf16"), to_dev(pf.k, "bf16"), to_dev(pf.v, "bf16")
+        g, beta, cu = to_dev(pf.g), to_dev(pf.beta), to_dev(pf.cu_seqlens)
+        o = torch.empty_like(q)
+        pools = kda.kda_contract_pools(n_seq, H, "cuda:0")
+        ms = _event_time_ms(lambda: kda.kda_contract_prefill(q, k, v, g, beta, cu, *pools, o=o), 3, 1)
+        flops = n_seq * T * H * FLOP_PER_TOKEN_HEAD_CONTRACT
+        res[f"contract_prefill_{'' if n_seq == 1 else '32x'}4096x12_bf16"] = dict(
+            ms=ms, tokens_per_s=n_seq * T / (ms * 1e-3), fp32_tflops=flops / (ms * 1e-3) / 1e12,
+            frac_fp32_valu_peak=flops / (ms * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS)
+        del q, k, v, g, beta, o, pools
+    return res
+
+
 LONG_SUB_SEGMENT = 8192  # each 65,536-token segment of the long sequence runs as 8 fragments
 
 
@@ -426,6 +490,8 @@ def main():
     ap.add_argument("--only-decode", action="store_true", help="time only the decode rows (for profiling)")
     ap.add_argument("--only-prefill", action="store_true",
                     help="time only the prefill rows, 4096 x 12 and 32 x 4096 x 12 (for profiling)")
+    ap.add_argument("--only-contract", action="store_true",
+                    help="time only the row-contract rows, decode 64 x 12 and prefill (for profiling)")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--write-traffic", metavar="DIR",
                     help="write profiles/decode_64x12_traffic.json from rocprofv3 counter CSVs under DIR")
@@ -458,6 +524,9 @@ def main():
         pb = bench_prefill_batch(reps=5, warmup=2)
         print(json.dumps({"prefill_4096x12_bf16": pf, "prefill_32x4096x12_bf16": pb}), flush=True)
         return
+    if args.only_contract:
+        print(json.dumps(bench_contract(args.steps, args.warmup)), flush=True)
+        return
     dec = bench_decode(args.steps, args.warmup)
     log(f"decode: {dec['ms'] * 1e3:.2f} us/step, {dec['gbps']:.0f} GB/s")
     rows = {}
@@ -481,6 +550,13 @@ def main():
         log(f"prologue: decode {dp['ms'] * 1e3:.2f} us ({dp['gbps']:.0f} GB/s), verify+commit {vp['ms'] * 1e3:.2f} us")
         rows["prologue_decode_64x12_bf16"] = dict(ms=dp["ms"], gbps=dp["gbps"])
         rows["prologue_verify_commit_32x12x8_bf16"] = dict(ms=vp["ms"], gbps=vp["gbps"])
+        log("row contract: decode 64 x 12, prefill 4096 x 12 and 32 x 4096 x 12 ...")
+        ct = bench_contract(max(128, args.steps), args.warmup)
+        cd = ct["contract_decode_64x12_bf16"]
+        log(f"row contract: decode {cd['ms'] * 1e3:.2f} us ({cd['gbps']:.0f} GB/s), prefill "
+            f"{ct['contract_prefill_4096x12_bf16']['ms']:.3f} ms, 32 x 4096 x 12 "
+            f"{ct['contract_prefill_32x4096x12_bf16']['ms']:.3f} ms")
+        rows.update(ct)
         if args.long:
             log("long context: 1,048,576 + 8 ragged sequences x 12 heads ...")
             lc = bench_long(reps=2, gen_workers=args.gen_workers)

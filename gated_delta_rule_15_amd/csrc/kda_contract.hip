@@ -86,17 +86,15 @@ struct Lds {
   float sq[MR][kD];      // scale * q_r
   float kh[MR][kD];      // k_r e^{b_r}
   float qh[MR][kD];      // scale * q_r e^{b_r}
-  float vv[MR][kD];      // v_r
   float aa[MR][kD];      // S_e^T k_hat
   float ww[MR][kD];      // S_e^T q_hat
   float gk[MR][kChunk];  // G_k[r, s]
   float gq[MR][kChunk];  // G_q[r, s]
-  float bt[MR];          // beta_r
   float gam[kD];         // e^{b_15} while closing
 };
 
 // The chunk close on this lane's 16 x 4 block: S <- e^{b_last} S + sum_s kbar_s u_s^T
-// over rows s = 0 .. nrows-1 (kbar already in rk, e^{b_last} in gam).
+// over rows s = 0 .. nrows-1 in order (kbar already in rk, e^{b_last} in gam).
 __device__ __forceinline__ void close_block(float (&S)[16][4], const float (*rk)[kD], const float (*ru)[kD],
                                             const float* gam, int nrows, int c0, int j0) {
 #pragma unroll
@@ -120,14 +118,42 @@ __device__ __forceinline__ void close_block(float (&S)[16][4], const float (*rk)
   }
 }
 
-// kbar_s = k_s e^{b_last - b_s} in place and gam = e^{b_last}, for rows 0 .. nrows-1.
-__device__ __forceinline__ void close_factors(float (*rk)[kD], const float (*rb)[kD], float* gam, int nrows, int tid) {
-  const int last = nrows - 1;
-  for (int e = tid; e < nrows * kD; e += kThreads) {
-    const int s = e / kD, c = e % kD;
-    rk[s][c] = rk[s][c] * exp_c(rb[last][c] - rb[s][c]);
+// Channel c's close factors: kbar_s = k_s e^{b_last - b_s} in place for rows 0 .. nrows-1,
+// and gam = e^{b_last}.
+__device__ __forceinline__ void close_factors(float (*rk)[kD], const float (*rb)[kD], float* gam, int nrows, int c) {
+  const float bl = rb[nrows - 1][c];
+  for (int s = 0; s < nrows; ++s) rk[s][c] = rk[s][c] * exp_c(bl - rb[s][c]);
+  gam[c] = exp_c(bl);
+}
+
+// One batch's inputs as this thread holds them: channel threads (tid < 128,
+// channel c = tid) hold k, q and g of channel c; value threads (tid >= 128,
+// column j = tid - 128) hold v of column j and beta.
+template <typename InT, int MR>
+struct BatchIn {
+  typename InT::raw1 x0[MR];  // k (channel) / v (value)
+  typename InT::raw1 x1[MR];  // q (channel)
+  float f[MR];                // g (channel) / beta (value)
+};
+
+template <typename InT, int MR>
+__device__ __forceinline__ void load_batch(BatchIn<InT, MR>& in, const ContractArgs& a, int h, int t0, int nr,
+                                           int tid) {
+  const int c = tid & (kD - 1);
+#pragma unroll
+  for (int i = 0; i < MR; ++i) {
+    if (i < nr) {
+      const int64_t tok = int64_t(t0 + i) * a.H + h;
+      if (tid < kD) {
+        in.x0[i] = InT::load1raw(a.k, tok * kD + c);
+        in.x1[i] = InT::load1raw(a.q, tok * kD + c);
+        in.f[i] = a.g[tok * kD + c];
+      } else {
+        in.x0[i] = InT::load1raw(a.v, tok * kD + c);
+        in.f[i] = a.beta[tok];
+      }
+    }
   }
-  for (int c = tid; c < kD; c += kThreads) gam[c] = exp_c(rb[last][c]);
 }
 
 template <typename InT, int MR>
@@ -156,8 +182,7 @@ __global__ __launch_bounds__(kThreads) void kda_contract_kernel(ContractArgs a) 
   const int p_first = p;
 
   // this lane's block of S_e: key rows c0 .. c0+15, value columns j0 .. j0+3
-  const int m = lane >> 3;
-  const int c0 = 16 * m;
+  const int c0 = 16 * (lane >> 3);
   const int j0 = 32 * wave + 4 * (lane & 7);
   float S[16][4];
 #pragma unroll
@@ -165,51 +190,47 @@ __global__ __launch_bounds__(kThreads) void kda_contract_kernel(ContractArgs a) 
     const float4 s4 = ld_f4(Sp + (c0 + i) * kD + j0);
     S[i][0] = s4.x; S[i][1] = s4.y; S[i][2] = s4.z; S[i][3] = s4.w;
   }
+  BatchIn<InT, MR> in;
+  int nr = min(min(MR, kChunk - p), count);
+  load_batch<InT, MR>(in, a, h, tok0, nr, tid);
   // the open chunk's rows
-  for (int e = tid; e < p * (kRowFloats / 4); e += kThreads) {
-    const int s = e / (kRowFloats / 4), f = 4 * (e % (kRowFloats / 4));
-    const float4 x = ld_f4(Rp + s * kRowFloats + f);
-    float* dst = (f < kD) ? &L.rk[s][f] : (f < 2 * kD) ? &L.rb[s][f - kD] : &L.ru[s][f - 2 * kD];
-    *reinterpret_cast<float4*>(dst) = x;
+  if (p > 0) {
+    for (int e = tid; e < p * (kRowFloats / 4); e += kThreads) {
+      const int s = e / (kRowFloats / 4), f = 4 * (e % (kRowFloats / 4));
+      const float4 x = ld_f4(Rp + s * kRowFloats + f);
+      float* dst = (f < kD) ? &L.rk[s][f] : (f < 2 * kD) ? &L.rb[s][f - kD] : &L.ru[s][f - 2 * kD];
+      *reinterpret_cast<float4*>(dst) = x;
+    }
+    __syncthreads();
   }
 
   bool closed = false;
   int done = 0;
-  while (done < count) {
+  while (true) {
     const int r0 = p;
-    const int nr = min(min(MR, kChunk - p), count - done);
     const int t0 = tok0 + done;
-    // ---- stage the batch rows: k (into the rows), scale * q, v, g (into rb), beta
-    for (int e = tid; e < nr * (kD / 4); e += kThreads) {
-      const int i = e / (kD / 4), c = 4 * (e % (kD / 4));
-      const int64_t base = (int64_t(t0 + i) * a.H + h) * kD + c;
-      float kk[4], qq[4], vv[4];
-      InT::load4(a.k, base, kk);
-      InT::load4(a.q, base, qq);
-      InT::load4(a.v, base, vv);
-      const float4 gg = ld_f4(a.g + base);
-      *reinterpret_cast<float4*>(&L.rk[r0 + i][c]) = make_float4(kk[0], kk[1], kk[2], kk[3]);
-      *reinterpret_cast<float4*>(&L.sq[i][c]) =
-          make_float4(a.scale * qq[0], a.scale * qq[1], a.scale * qq[2], a.scale * qq[3]);
-      *reinterpret_cast<float4*>(&L.vv[i][c]) = make_float4(vv[0], vv[1], vv[2], vv[3]);
-      *reinterpret_cast<float4*>(&L.rb[r0 + i][c]) = gg;
-    }
-    if (tid < nr) L.bt[tid] = a.beta[int64_t(t0 + tid) * a.H + h];
-    __syncthreads();
-    // ---- cumulative decay in row order; rescaled key and query
+    const bool closes = (r0 + nr == kChunk);
+    // ---- B: cumulative decay in row order, rescaled key and query (channel threads)
     if (tid < kD) {
       const int c = tid;
       float b = (r0 > 0) ? L.rb[r0 - 1][c] : 0.0f;
-      for (int i = 0; i < nr; ++i) {
-        b = b + L.rb[r0 + i][c];
-        L.rb[r0 + i][c] = b;
-        const float e = exp_c(b);
-        L.kh[i][c] = L.rk[r0 + i][c] * e;
-        L.qh[i][c] = L.sq[i][c] * e;
+#pragma unroll
+      for (int i = 0; i < MR; ++i) {
+        if (i < nr) {
+          const float kk = InT::unpack1(in.x0[i]);
+          const float sq = a.scale * InT::unpack1(in.x1[i]);
+          b = b + in.f[i];
+          const float e = exp_c(b);
+          L.rk[r0 + i][c] = kk;
+          L.rb[r0 + i][c] = b;
+          L.sq[i][c] = sq;
+          L.kh[i][c] = kk * e;
+          L.qh[i][c] = sq * e;
+        }
       }
     }
     __syncthreads();
-    // ---- a = S_e^T k_hat and w = S_e^T q_hat for every batch row (wave-local)
+    // ---- C1: a = S_e^T k_hat and w = S_e^T q_hat for every batch row (wave-local)
     for (int i = 0; i < nr; ++i) {
       float pa[4] = {0.f, 0.f, 0.f, 0.f}, pw[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -250,7 +271,7 @@ __global__ __launch_bounds__(kThreads) void kda_contract_kernel(ContractArgs a) 
       const int col = j0 + (b4 ? 2 : 0) + (b5 ? 1 : 0);
       (b3 ? L.ww : L.aa)[i][col] = fin;
     }
-    // ---- Gram entries G_k[r, s], G_q[r, s] for s <= r, 8 lanes per entry
+    // ---- C2: Gram entries G_k[r, s], G_q[r, s] for s <= r, 8 lanes per entry
     {
       const int ntask = nr * (r0 + 1) + nr * (nr - 1) / 2;  // sum over i of (r0 + i + 1)
       const int cm = 16 * (lane & 7);
@@ -295,44 +316,65 @@ __global__ __launch_bounds__(kThreads) void kda_contract_kernel(ContractArgs a) 
       }
     }
     __syncthreads();
-    // ---- u for each batch row in row order (one thread per value column)
-    if (tid < kD) {
-      const int j = tid;
-      for (int i = 0; i < nr; ++i) {
-        const int r = r0 + i;
-        float acc = L.vv[i][j] - L.aa[i][j];
-        for (int s = 0; s < r; ++s) acc = __builtin_fmaf(-L.gk[i][s], L.ru[s][j], acc);
-        L.ru[r][j] = L.bt[i] * acc;
-      }
-    }
-    __syncthreads();
-    // ---- outputs
-    if (a.o != nullptr) {
-      for (int e = tid; e < nr * (kD / 4); e += kThreads) {
-        const int i = e / (kD / 4), j = 4 * (e % (kD / 4));
-        const int r = r0 + i;
-        const float4 w4 = *reinterpret_cast<const float4*>(&L.ww[i][j]);
-        float out[4] = {w4.x, w4.y, w4.z, w4.w};
-        for (int s = 0; s <= r; ++s) {
-          const float gq = L.gq[i][s];
-          const float4 u4 = *reinterpret_cast<const float4*>(&L.ru[s][j]);
-          out[0] = __builtin_fmaf(gq, u4.x, out[0]);
-          out[1] = __builtin_fmaf(gq, u4.y, out[1]);
-          out[2] = __builtin_fmaf(gq, u4.z, out[2]);
-          out[3] = __builtin_fmaf(gq, u4.w, out[3]);
+    // ---- D: forward substitution for u and the outputs (value threads), close factors (channel threads)
+    const int nr_next = min(MR, count - done - nr);  // after a close the next batch starts a chunk
+    if (tid >= kD) {
+      const int j = tid - kD;
+      float acc[MR], out[MR];
+#pragma unroll
+      for (int i = 0; i < MR; ++i) {
+        if (i < nr) {
+          acc[i] = InT::unpack1(in.x0[i]) - L.aa[i][j];
+          out[i] = L.ww[i][j];
         }
-        InT::store4(a.o, (int64_t(t0 + i) * a.H + h) * kD + j, out);
       }
+      // u_r = beta_r (v_r - a_r - sum_{s<r} G_k[r,s] u_s), o_r = w_r + sum_{s<=r} G_q[r,s] u_s,
+      // each sum taken over s in ascending order: the earlier rows of the open chunk first ...
+      for (int s = 0; s < r0; ++s) {
+        const float u = L.ru[s][j];
+#pragma unroll
+        for (int i = 0; i < MR; ++i) {
+          if (i < nr) {
+            acc[i] = __builtin_fmaf(-L.gk[i][s], u, acc[i]);
+            out[i] = __builtin_fmaf(L.gq[i][s], u, out[i]);
+          }
+        }
+      }
+      // ... then the batch rows, each final once the rows before it are in
+#pragma unroll
+      for (int is = 0; is < MR; ++is) {
+        if (is < nr) {
+          const float u = in.f[is] * acc[is];
+          L.ru[r0 + is][j] = u;
+#pragma unroll
+          for (int i = is; i < MR; ++i) {
+            if (i < nr) {
+              if (i > is) acc[i] = __builtin_fmaf(-L.gk[i][r0 + is], u, acc[i]);
+              out[i] = __builtin_fmaf(L.gq[i][r0 + is], u, out[i]);
+            }
+          }
+        }
+      }
+      if (a.o != nullptr) {
+#pragma unroll
+        for (int i = 0; i < MR; ++i)
+          if (i < nr) InT::store1(a.o, (int64_t(t0 + i) * a.H + h) * kD + j, out[i]);
+      }
+    } else if (closes) {
+      close_factors(L.rk, L.rb, L.gam, kChunk, tid);
     }
+    // the next batch's inputs, in flight during the close
+    if (nr_next > 0) load_batch<InT, MR>(in, a, h, t0 + nr, nr_next, tid);
+    __syncthreads();
     p += nr;
     done += nr;
-    if (p == kChunk) {  // close the chunk
-      close_factors(L.rk, L.rb, L.gam, kChunk, tid);
-      __syncthreads();
-      close_block(S, L.rk, L.ru, L.gam, kChunk, c0, j0);
-      p = 0;
-      closed = true;
-    }
+    if (!closes) break;  // a batch that does not close the chunk ends the sequence
+    // ---- E: close the chunk
+    close_block(S, L.rk, L.ru, L.gam, kChunk, c0, j0);
+    p = 0;
+    closed = true;
+    if (nr_next <= 0) break;
+    nr = nr_next;
     __syncthreads();
   }
 
@@ -387,7 +429,7 @@ __global__ __launch_bounds__(kThreads) void kda_contract_state_kernel(const floa
       *reinterpret_cast<float4*>(dst) = x;
     }
     __syncthreads();
-    close_factors(rk, rb, gam, p, tid);
+    if (tid < kD) close_factors(rk, rb, gam, p, tid);
     __syncthreads();
     close_block(S, rk, ru, gam, p, c0, j0);
   }
