@@ -20,8 +20,10 @@
 // not depend on how many rows a launch takes at once: the decode (one row per
 // call) and the prefill (up to 16 rows of a chunk at once) run the same kernel
 // body, each reduction has one association (a sequential fused multiply-add
-// chain over 16 channels, then the tree ((p0+p1)+(p2+p3))+((p4+p5)+(p6+p7))
-// over the 8 channel groups), sums over earlier rows run in row order, and the
+// chain over 16 channels, then a fixed tree over the 8 channel groups:
+// ((p0+p4)+(p2+p6))+((p1+p5)+(p3+p7)) for the S_e products,
+// ((p0+p1)+(p2+p3))+((p4+p5)+(p6+p7)) for the Gram entries), sums over earlier
+// rows run in row order, and the
 // file is built without floating-point contraction.  A token's output, the
 // rows and the chunk-entry state are therefore bit-identical whether the
 // token came through a prefill of any length, a decode step, or a batch of
@@ -32,7 +34,7 @@
 // A workgroup (4 waves) owns one (sequence, head).  Wave w holds value columns
 // 32w .. 32w+31 of S_e in registers: lane (m = lane >> 3, jq = lane & 7) holds
 // key rows 16m .. 16m+15 of columns 32w + 4jq .. +3, so the 8 channel groups of
-// every S_e^T x product meet inside the wave (lane bits 3, 4, 5).
+// every S_e^T x product meet inside the wave (lane bits 5, 4, 3, in that order).
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
@@ -48,16 +50,26 @@ constexpr float kLog2e = 1.4426950408889634f;
 // product, then v_exp_f32 (about 1 ulp).  Every path of the contract uses it.
 __device__ __forceinline__ float exp_c(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
-// Value of lane (lane ^ X) for X in {1, 2, 4, 8, 16, 32}.
-template <int X>
-__device__ __forceinline__ float xor_lane(float x) {
-  if constexpr (X == 8) {  // rotate each 16-lane row by 8: lane i reads i ^ 8
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
-  } else if constexpr (X < 32) {  // swizzle bit mode within 32 lanes: and 0x1F, xor X
-    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x1F | (X << 10)));
-  } else {
-    return __shfl_xor(x, 32, 64);
-  }
+// Lane exchanges, all on the VALU (no LDS round trip).  swap32 / swap16
+// exchange, between two registers, the upper 32 lanes of the first with the
+// lower 32 lanes of the second (v_permlane32_swap), or the odd 16-lane rows of
+// the first with the even rows of the second (v_permlane16_swap); dpp<CTRL>
+// reads another lane through a DPP move: 0x128 lane l ^ 8 within a 16-lane row
+// (row rotate by 8), 0x141 lane 7 - l within each 8 lanes (half-row mirror),
+// 0xB1 lane l ^ 1 and 0x4E lane l ^ 2 (quad permutes).
+__device__ __forceinline__ void swap32(float& x, float& y) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  x = __uint_as_float(r[0]);
+  y = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap16(float& x, float& y) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  x = __uint_as_float(r[0]);
+  y = __uint_as_float(r[1]);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
 struct ContractArgs {
@@ -86,10 +98,12 @@ struct Lds {
   float sq[MR][kD];      // scale * q_r
   float kh[MR][kD];      // k_r e^{b_r}
   float qh[MR][kD];      // scale * q_r e^{b_r}
+  float vv[MR][kD];      // v_r
   float aa[MR][kD];      // S_e^T k_hat
   float ww[MR][kD];      // S_e^T q_hat
-  float gk[MR][kChunk];  // G_k[r, s]
-  float gq[MR][kChunk];  // G_q[r, s]
+  float gk[kChunk][MR];  // G_k[r, s] at [s][r - r0]
+  float gq[kChunk][MR];  // G_q[r, s] at [s][r - r0]
+  float bt[MR < 4 ? 4 : MR];  // beta_r
   float gam[kD];         // e^{b_15} while closing
 };
 
@@ -103,18 +117,27 @@ __device__ __forceinline__ void close_block(float (&S)[16][4], const float (*rk)
 #pragma unroll
     for (int x = 0; x < 4; ++x) S[i][x] = e * S[i][x];
   }
+  // row s's operands are read while row s - 1's products are formed
+  float4 un = *reinterpret_cast<const float4*>(&ru[0][j0]);
+  float4 kn[4];
+#pragma unroll
+  for (int i4 = 0; i4 < 4; ++i4) kn[i4] = *reinterpret_cast<const float4*>(&rk[0][c0 + 4 * i4]);
   for (int s = 0; s < nrows; ++s) {
-    const float4 u4 = *reinterpret_cast<const float4*>(&ru[s][j0]);
-    const float u[4] = {u4.x, u4.y, u4.z, u4.w};
+    const float u[4] = {un.x, un.y, un.z, un.w};
+    float kb[16];
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
-      const float4 kb4 = *reinterpret_cast<const float4*>(&rk[s][c0 + 4 * i4]);
-      const float kb[4] = {kb4.x, kb4.y, kb4.z, kb4.w};
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii)
-#pragma unroll
-        for (int x = 0; x < 4; ++x) S[4 * i4 + ii][x] = __builtin_fmaf(kb[ii], u[x], S[4 * i4 + ii][x]);
+      kb[4 * i4] = kn[i4].x; kb[4 * i4 + 1] = kn[i4].y; kb[4 * i4 + 2] = kn[i4].z; kb[4 * i4 + 3] = kn[i4].w;
     }
+    if (s + 1 < nrows) {
+      un = *reinterpret_cast<const float4*>(&ru[s + 1][j0]);
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) kn[i4] = *reinterpret_cast<const float4*>(&rk[s + 1][c0 + 4 * i4]);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) S[i][x] = __builtin_fmaf(kb[i], u[x], S[i][x]);
   }
 }
 
@@ -124,6 +147,21 @@ __device__ __forceinline__ void close_factors(float (*rk)[kD], const float (*rb)
   const float bl = rb[nrows - 1][c];
   for (int s = 0; s < nrows; ++s) rk[s][c] = rk[s][c] * exp_c(bl - rb[s][c]);
   gam[c] = exp_c(bl);
+}
+
+// MR consecutive floats from LDS (16-byte aligned when MR >= 4), as wide reads.
+template <int MR>
+__device__ __forceinline__ void load_row(float (&dst)[MR], const float* src) {
+  if constexpr (MR % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < MR / 4; ++q) {
+      const float4 t = reinterpret_cast<const float4*>(src)[q];
+      dst[4 * q] = t.x; dst[4 * q + 1] = t.y; dst[4 * q + 2] = t.z; dst[4 * q + 3] = t.w;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < MR; ++q) dst[q] = src[q];
+  }
 }
 
 // One batch's inputs as this thread holds them: channel threads (tid < 128,
@@ -157,7 +195,7 @@ __device__ __forceinline__ void load_batch(BatchIn<InT, MR>& in, const ContractA
 }
 
 template <typename InT, int MR>
-__global__ __launch_bounds__(kThreads) void kda_contract_kernel(ContractArgs a) {
+__global__ __launch_bounds__(kThreads, MR == 1 ? 3 : 2) void kda_contract_kernel(ContractArgs a) {
   __shared__ __align__(16) Lds<MR> L;
   const int n = blockIdx.x / a.H;
   const int h = blockIdx.x % a.H;
@@ -228,48 +266,63 @@ __global__ __launch_bounds__(kThreads) void kda_contract_kernel(ContractArgs a) 
           L.qh[i][c] = sq * e;
         }
       }
+    } else {
+      const int j = tid - kD;
+#pragma unroll
+      for (int i = 0; i < MR; ++i) {
+        if (i < nr) {
+          L.vv[i][j] = InT::unpack1(in.x0[i]);
+          if (j == 0) L.bt[i] = in.f[i];
+        }
+      }
     }
     __syncthreads();
-    // ---- C1: a = S_e^T k_hat and w = S_e^T q_hat for every batch row (wave-local)
-    for (int i = 0; i < nr; ++i) {
-      float pa[4] = {0.f, 0.f, 0.f, 0.f}, pw[4] = {0.f, 0.f, 0.f, 0.f};
+    // ---- C1: a = S_e^T k_hat and w = S_e^T q_hat for every batch row (wave-local),
+    // two rows per pass (the second repeats the last row when nr is odd)
+    for (int i0 = 0; i0 < nr; i0 += 2) {
+      const int rows[2] = {i0, min(i0 + 1, nr - 1)};
+      float pa[2][4], pw[2][4];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) pa[t][x] = pw[t][x] = 0.f;
 #pragma unroll
       for (int c4 = 0; c4 < 4; ++c4) {
-        const float4 k4 = *reinterpret_cast<const float4*>(&L.kh[i][c0 + 4 * c4]);
-        const float4 q4 = *reinterpret_cast<const float4*>(&L.qh[i][c0 + 4 * c4]);
-        const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
-        const float qv[4] = {q4.x, q4.y, q4.z, q4.w};
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc)
+        for (int t = 0; t < 2; ++t) {
+          const float4 k4 = *reinterpret_cast<const float4*>(&L.kh[rows[t]][c0 + 4 * c4]);
+          const float4 q4 = *reinterpret_cast<const float4*>(&L.qh[rows[t]][c0 + 4 * c4]);
+          const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
+          const float qv[4] = {q4.x, q4.y, q4.z, q4.w};
 #pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            pa[x] = __builtin_fmaf(S[4 * c4 + cc][x], kv[cc], pa[x]);
-            pw[x] = __builtin_fmaf(S[4 * c4 + cc][x], qv[cc], pw[x]);
-          }
+          for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+              pa[t][x] = __builtin_fmaf(S[4 * c4 + cc][x], kv[cc], pa[t][x]);
+              pw[t][x] = __builtin_fmaf(S[4 * c4 + cc][x], qv[cc], pw[t][x]);
+            }
+        }
       }
-      // tree over the 8 channel groups, reduce-scattered: level 1 pairs m, m^1
-      // (lane bit 3) and splits a / w; level 2 pairs m, m^2 (bit 4) and splits
-      // the columns in halves; level 3 pairs m, m^4 (bit 5).
+      // tree over the 8 channel groups, reduce-scattered: level 1 pairs m, m^4
+      // (lane bit 5) and splits a / w; level 2 pairs m, m^2 (bit 4) and splits
+      // the columns in halves; level 3 pairs m, m^1 (bit 3).
       const bool b3 = lane & 8, b4 = lane & 16, b5 = lane & 32;
-      float l1[4];
+      const int col = j0 + (b4 ? 2 : 0) + (b3 ? 1 : 0);
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const float send = b3 ? pa[x] : pw[x];
-        const float keep = b3 ? pw[x] : pa[x];
-        l1[x] = keep + xor_lane<8>(send);
-      }
-      float l2[2];
+      for (int t = 0; t < 2; ++t) {
 #pragma unroll
-      for (int y = 0; y < 2; ++y) {
-        const float send = b4 ? l1[y] : l1[2 + y];
-        const float keep = b4 ? l1[2 + y] : l1[y];
-        l2[y] = keep + xor_lane<16>(send);
+        for (int x = 0; x < 4; ++x) swap32(pa[t][x], pw[t][x]);
+        float l1[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) l1[x] = pa[t][x] + pw[t][x];  // bit 5 = 0: a, 1: w
+        swap16(l1[0], l1[2]);
+        swap16(l1[1], l1[3]);
+        const float l2a = l1[0] + l1[2], l2b = l1[1] + l1[3];  // bit 4 = 0: columns 0, 1; 1: 2, 3
+        const float mine = b3 ? l2b : l2a;
+        const float other = b3 ? l2a : l2b;
+        const float fin = mine + dpp<0x128>(other);
+        if (t == 0 || rows[1] != rows[0]) (b5 ? L.ww : L.aa)[rows[t]][col] = fin;
       }
-      const float send = b5 ? l2[0] : l2[1];
-      const float keep = b5 ? l2[1] : l2[0];
-      const float fin = keep + xor_lane<32>(send);
-      const int col = j0 + (b4 ? 2 : 0) + (b5 ? 1 : 0);
-      (b3 ? L.ww : L.aa)[i][col] = fin;
     }
     // ---- C2: Gram entries G_k[r, s], G_q[r, s] for s <= r, 8 lanes per entry
     {
@@ -303,15 +356,15 @@ __global__ __launch_bounds__(kThreads) void kda_contract_kernel(ContractArgs a) 
             pq = __builtin_fmaf(qrv[cc], t, pq);
           }
         }
-        pk = pk + xor_lane<1>(pk);
-        pq = pq + xor_lane<1>(pq);
-        pk = pk + xor_lane<2>(pk);
-        pq = pq + xor_lane<2>(pq);
-        pk = pk + xor_lane<4>(pk);
-        pq = pq + xor_lane<4>(pq);
+        pk = pk + dpp<0xB1>(pk);  // groups g, g^1
+        pq = pq + dpp<0xB1>(pq);
+        pk = pk + dpp<0x4E>(pk);  // pairs {0,1} + {2,3} within a quad
+        pq = pq + dpp<0x4E>(pq);
+        pk = pk + dpp<0x141>(pk);  // quads {0,1} of each 8 lanes: each lane adds its mirror lane's quad sum
+        pq = pq + dpp<0x141>(pq);
         if (valid && (lane & 7) == 0) {
-          L.gk[i][s] = pk;
-          L.gq[i][s] = pq;
+          L.gk[s][i] = pk;
+          L.gq[s][i] = pq;
         }
       }
     }
@@ -320,23 +373,28 @@ __global__ __launch_bounds__(kThreads) void kda_contract_kernel(ContractArgs a) 
     const int nr_next = min(MR, count - done - nr);  // after a close the next batch starts a chunk
     if (tid >= kD) {
       const int j = tid - kD;
-      float acc[MR], out[MR];
+      float acc[MR], out[MR], bt[MR];
 #pragma unroll
       for (int i = 0; i < MR; ++i) {
         if (i < nr) {
-          acc[i] = InT::unpack1(in.x0[i]) - L.aa[i][j];
+          acc[i] = L.vv[i][j] - L.aa[i][j];
           out[i] = L.ww[i][j];
         }
       }
+      load_row<MR>(bt, L.bt);
       // u_r = beta_r (v_r - a_r - sum_{s<r} G_k[r,s] u_s), o_r = w_r + sum_{s<=r} G_q[r,s] u_s,
       // each sum taken over s in ascending order: the earlier rows of the open chunk first ...
+#pragma unroll 2
       for (int s = 0; s < r0; ++s) {
         const float u = L.ru[s][j];
+        float gk[MR], gq[MR];
+        load_row<MR>(gk, L.gk[s]);
+        load_row<MR>(gq, L.gq[s]);
 #pragma unroll
         for (int i = 0; i < MR; ++i) {
           if (i < nr) {
-            acc[i] = __builtin_fmaf(-L.gk[i][s], u, acc[i]);
-            out[i] = __builtin_fmaf(L.gq[i][s], u, out[i]);
+            acc[i] = __builtin_fmaf(-gk[i], u, acc[i]);
+            out[i] = __builtin_fmaf(gq[i], u, out[i]);
           }
         }
       }
@@ -344,13 +402,16 @@ __global__ __launch_bounds__(kThreads) void kda_contract_kernel(ContractArgs a) 
 #pragma unroll
       for (int is = 0; is < MR; ++is) {
         if (is < nr) {
-          const float u = in.f[is] * acc[is];
+          const float u = bt[is] * acc[is];
           L.ru[r0 + is][j] = u;
+          float gk[MR], gq[MR];
+          load_row<MR>(gk, L.gk[r0 + is]);
+          load_row<MR>(gq, L.gq[r0 + is]);
 #pragma unroll
           for (int i = is; i < MR; ++i) {
             if (i < nr) {
-              if (i > is) acc[i] = __builtin_fmaf(-L.gk[i][r0 + is], u, acc[i]);
-              out[i] = __builtin_fmaf(L.gq[i][r0 + is], u, out[i]);
+              if (i > is) acc[i] = __builtin_fmaf(-gk[i], u, acc[i]);
+              out[i] = __builtin_fmaf(gq[i], u, out[i]);
             }
           }
         }
