@@ -278,3 +278,56 @@ def test_prefill_workload_sampled_parity():
         print(f"contract prefill 4096 x 12, head {h}: rel-L2 o={eo:.3e} S={es:.3e}")
         assert eo <= 2e-3 and es <= 2e-3
     assert int(pools[2][0, 0]) == 0  # 4096 = 256 closed chunks
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_state_handover_to_the_plain_decode(dtype):
+    """kda_contract_state gives the running state at any position; the plain decode continues from it."""
+    lens = [7, 16, 29]
+    p = gen.packed_batch(seed=38, seqlens=[L + 3 for L in lens], H=2, dtype=dtype, init_state=True)
+    pools = _pools(p)
+    _prefill(_slice(p, [(0, L) for L in lens]), pools, with_output=False)
+    S_run = _kda().kda_contract_state(*pools)
+    q, k, v, g, beta = (p.f64(x) for x in ("q", "k", "v", "g", "beta"))
+    for step in range(3):
+        idx = [int(p.cu_seqlens[n]) + L + step for n, L in enumerate(lens)]
+        pick = lambda x: np.ascontiguousarray(x[idx])
+        o = _kda().kda_decode_step(to_dev(pick(p.q), dtype), to_dev(pick(p.k), dtype), to_dev(pick(p.v), dtype),
+                                   to_dev(pick(p.g)), to_dev(pick(p.beta)), S_run)
+        torch.cuda.synchronize()
+        for n, L in enumerate(lens):
+            a = int(p.cu_seqlens[n])
+            for h in range(2):
+                o_ref, _ = orc.recurrence(q[a:a + L + step + 1, h], k[a:a + L + step + 1, h], v[a:a + L + step + 1, h],
+                                          g[a:a + L + step + 1, h], beta[a:a + L + step + 1, h], p.initial_state[n, h])
+                assert rel_l2(to_f64(o[n, h]), o_ref[-1]) <= TOL[dtype]
+
+
+def test_strong_decay_beyond_the_fused_prefill_range():
+    """log-decays down to -20 per step (the fused prefill supports >= -5): the contract's exponent
+    differences stay finite and the results match the recurrence."""
+    lens = [40, 17]
+    p = gen.packed_batch(seed=39, seqlens=lens, H=2, dtype="f32", init_state=True)
+    rng = np.random.default_rng(39)
+    p.g[:] = rng.uniform(-20.0, 0.0, p.g.shape).astype(np.float32)
+    pools = _pools(p)
+    o = _prefill(_slice(p, [(0, L) for L in lens]), pools)
+    q, k, v, g, beta = (p.f64(x) for x in ("q", "k", "v", "g", "beta"))
+    o_ref, S_ref = orc.prefill(q, k, v, g, beta, p.cu_seqlens, p.initial_state)
+    assert torch.isfinite(o).all()
+    assert rel_l2(to_f64(o), o_ref) <= 1e-5
+    assert rel_l2(to_f64(_kda().kda_contract_state(*pools)), S_ref) <= 1e-5
+
+
+def test_paths_are_bit_identical_f32():
+    lens = [33, 20]
+    p = gen.packed_batch(seed=40, seqlens=lens, H=3, dtype="f32", init_state=True)
+    whole = _pools(p)
+    o_whole = _prefill(_slice(p, [(0, L) for L in lens]), whole)
+    split = _pools(p)
+    o1 = _prefill(_slice(p, [(0, 15), (0, 4)]), split)
+    od = _decode_token(p, [15, 4], split)
+    o3 = _prefill(_slice(p, [(16, 33), (5, 20)]), split)
+    o_split = torch.cat([o1[:15], od[0:1], o3[:17], o1[15:], od[1:2], o3[17:]])
+    assert torch.equal(_bits(o_split), _bits(o_whole))
+    _assert_same_state(whole, split)
