@@ -218,29 +218,57 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : 2) void kda_contract_kernel
   float* Rp = a.rows + unit * kChunk * kRowFloats;
   int p = a.pos[unit] & (kChunk - 1);
   const int p_first = p;
-
-  // this lane's block of S_e: key rows c0 .. c0+15, value columns j0 .. j0+3
   const int c0 = 16 * (lane >> 3);
   const int j0 = 32 * wave + 4 * (lane & 7);
-  float S[16][4];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float4 s4 = ld_f4(Sp + (c0 + i) * kD + j0);
-    S[i][0] = s4.x; S[i][1] = s4.y; S[i][2] = s4.z; S[i][3] = s4.w;
-  }
+
+  // Loads in the order they are needed: the batch inputs and the open rows
+  // first, S_e last, so that everything except the S_e products runs while
+  // S_e streams in (loads complete in issue order).
   BatchIn<InT, MR> in;
   int nr = min(min(MR, kChunk - p), count);
   load_batch<InT, MR>(in, a, h, tok0, nr, tid);
-  // the open chunk's rows
-  if (p > 0) {
-    for (int e = tid; e < p * (kRowFloats / 4); e += kThreads) {
-      const int s = e / (kRowFloats / 4), f = 4 * (e % (kRowFloats / 4));
-      const float4 x = ld_f4(Rp + s * kRowFloats + f);
+  constexpr int kRowVecs = kRowFloats / 4;
+  float S[16][4];
+  if constexpr (MR == 1) {
+    // one row per call: the open rows are issued before S_e and held in registers
+    constexpr int kRowIters = ((kChunk - 1) * kRowVecs + kThreads - 1) / kThreads;
+    float4 rv[kRowIters];
+#pragma unroll
+    for (int t = 0; t < kRowIters; ++t) {
+      const int e = tid + t * kThreads;
+      if (e < p * kRowVecs) rv[t] = ld_f4(Rp + 4 * e);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // this lane's block of S_e: key rows c0 .. c0+15, value columns j0 .. j0+3
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float4 s4 = ld_f4(Sp + (c0 + i) * kD + j0);
+      S[i][0] = s4.x; S[i][1] = s4.y; S[i][2] = s4.z; S[i][3] = s4.w;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < kRowIters; ++t) {
+      const int e = tid + t * kThreads;
+      if (e < p * kRowVecs) {
+        const int s = e / kRowVecs, f = 4 * (e % kRowVecs);
+        float* dst = (f < kD) ? &L.rk[s][f] : (f < 2 * kD) ? &L.rb[s][f - kD] : &L.ru[s][f - 2 * kD];
+        *reinterpret_cast<float4*>(dst) = rv[t];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float4 s4 = ld_f4(Sp + (c0 + i) * kD + j0);
+      S[i][0] = s4.x; S[i][1] = s4.y; S[i][2] = s4.z; S[i][3] = s4.w;
+    }
+    for (int e = tid; e < p * kRowVecs; e += kThreads) {
+      const int s = e / kRowVecs, f = 4 * (e % kRowVecs);
+      const float4 x = ld_f4(Rp + 4 * e);
       float* dst = (f < kD) ? &L.rk[s][f] : (f < 2 * kD) ? &L.rb[s][f - kD] : &L.ru[s][f - 2 * kD];
       *reinterpret_cast<float4*>(dst) = x;
     }
-    __syncthreads();
   }
+  if (p > 0) __syncthreads();
 
   bool closed = false;
   int done = 0;
@@ -277,53 +305,6 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : 2) void kda_contract_kernel
       }
     }
     __syncthreads();
-    // ---- C1: a = S_e^T k_hat and w = S_e^T q_hat for every batch row (wave-local),
-    // two rows per pass (the second repeats the last row when nr is odd)
-    for (int i0 = 0; i0 < nr; i0 += 2) {
-      const int rows[2] = {i0, min(i0 + 1, nr - 1)};
-      float pa[2][4], pw[2][4];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int x = 0; x < 4; ++x) pa[t][x] = pw[t][x] = 0.f;
-#pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const float4 k4 = *reinterpret_cast<const float4*>(&L.kh[rows[t]][c0 + 4 * c4]);
-          const float4 q4 = *reinterpret_cast<const float4*>(&L.qh[rows[t]][c0 + 4 * c4]);
-          const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
-          const float qv[4] = {q4.x, q4.y, q4.z, q4.w};
-#pragma unroll
-          for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-              pa[t][x] = __builtin_fmaf(S[4 * c4 + cc][x], kv[cc], pa[t][x]);
-              pw[t][x] = __builtin_fmaf(S[4 * c4 + cc][x], qv[cc], pw[t][x]);
-            }
-        }
-      }
-      // tree over the 8 channel groups, reduce-scattered: level 1 pairs m, m^4
-      // (lane bit 5) and splits a / w; level 2 pairs m, m^2 (bit 4) and splits
-      // the columns in halves; level 3 pairs m, m^1 (bit 3).
-      const bool b3 = lane & 8, b4 = lane & 16, b5 = lane & 32;
-      const int col = j0 + (b4 ? 2 : 0) + (b3 ? 1 : 0);
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int x = 0; x < 4; ++x) swap32(pa[t][x], pw[t][x]);
-        float l1[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) l1[x] = pa[t][x] + pw[t][x];  // bit 5 = 0: a, 1: w
-        swap16(l1[0], l1[2]);
-        swap16(l1[1], l1[3]);
-        const float l2a = l1[0] + l1[2], l2b = l1[1] + l1[3];  // bit 4 = 0: columns 0, 1; 1: 2, 3
-        const float mine = b3 ? l2b : l2a;
-        const float other = b3 ? l2a : l2b;
-        const float fin = mine + dpp<0x128>(other);
-        if (t == 0 || rows[1] != rows[0]) (b5 ? L.ww : L.aa)[rows[t]][col] = fin;
-      }
-    }
     // ---- C2: Gram entries G_k[r, s], G_q[r, s] for s <= r, 8 lanes per entry
     {
       const int ntask = nr * (r0 + 1) + nr * (nr - 1) / 2;  // sum over i of (r0 + i + 1)
@@ -369,21 +350,21 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : 2) void kda_contract_kernel
       }
     }
     __syncthreads();
-    // ---- D: forward substitution for u and the outputs (value threads), close factors (channel threads)
+    // ---- D1: the sums over the open chunk's earlier rows (value threads), in
+    // row order; u_r = beta_r ((v_r - sum_{s<r} G_k[r,s] u_s) - a_r) and
+    // o_r = (sum_{s<=r} G_q[r,s] u_s) + w_r, each sum over s in ascending
+    // order, so that the association depends on (r, s) only.  Partials wait
+    // in vv (residuals) and sq (outputs), which are free by now.  The channel
+    // threads form the close factors.
     const int nr_next = min(MR, count - done - nr);  // after a close the next batch starts a chunk
     if (tid >= kD) {
       const int j = tid - kD;
-      float acc[MR], out[MR], bt[MR];
+      float acc[MR], out[MR];
 #pragma unroll
       for (int i = 0; i < MR; ++i) {
-        if (i < nr) {
-          acc[i] = L.vv[i][j] - L.aa[i][j];
-          out[i] = L.ww[i][j];
-        }
+        acc[i] = (i < nr) ? L.vv[i][j] : 0.f;
+        out[i] = 0.f;
       }
-      load_row<MR>(bt, L.bt);
-      // u_r = beta_r (v_r - a_r - sum_{s<r} G_k[r,s] u_s), o_r = w_r + sum_{s<=r} G_q[r,s] u_s,
-      // each sum taken over s in ascending order: the earlier rows of the open chunk first ...
 #pragma unroll 2
       for (int s = 0; s < r0; ++s) {
         const float u = L.ru[s][j];
@@ -398,11 +379,69 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : 2) void kda_contract_kernel
           }
         }
       }
-      // ... then the batch rows, each final once the rows before it are in
+#pragma unroll
+      for (int i = 0; i < MR; ++i) {
+        if (i < nr) {
+          L.vv[i][j] = acc[i];
+          L.sq[i][j] = out[i];
+        }
+      }
+    } else if (closes) {
+      close_factors(L.rk, L.rb, L.gam, kChunk, tid);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- C1: a = S_e^T k_hat and w = S_e^T q_hat for every batch row (wave-local)
+    for (int i = 0; i < nr; ++i) {
+      float pa[4] = {0.f, 0.f, 0.f, 0.f}, pw[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const float4 k4 = *reinterpret_cast<const float4*>(&L.kh[i][c0 + 4 * c4]);
+        const float4 q4 = *reinterpret_cast<const float4*>(&L.qh[i][c0 + 4 * c4]);
+        const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
+        const float qv[4] = {q4.x, q4.y, q4.z, q4.w};
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            pa[x] = __builtin_fmaf(S[4 * c4 + cc][x], kv[cc], pa[x]);
+            pw[x] = __builtin_fmaf(S[4 * c4 + cc][x], qv[cc], pw[x]);
+          }
+      }
+      // tree over the 8 channel groups, reduce-scattered: level 1 pairs m, m^4
+      // (lane bit 5) and splits a / w; level 2 pairs m, m^2 (bit 4) and splits
+      // the columns in halves; level 3 pairs m, m^1 (bit 3).
+      const bool b3 = lane & 8, b4 = lane & 16, b5 = lane & 32;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) swap32(pa[x], pw[x]);
+      float l1[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) l1[x] = pa[x] + pw[x];  // bit 5 = 0: a, 1: w
+      swap16(l1[0], l1[2]);
+      swap16(l1[1], l1[3]);
+      const float l2a = l1[0] + l1[2], l2b = l1[1] + l1[3];  // bit 4 = 0: columns 0, 1; 1: 2, 3
+      const float mine = b3 ? l2b : l2a;
+      const float other = b3 ? l2a : l2b;
+      const float fin = mine + dpp<0x128>(other);
+      const int col = j0 + (b4 ? 2 : 0) + (b3 ? 1 : 0);
+      (b5 ? L.ww : L.aa)[i][col] = fin;
+    }
+    __syncthreads();
+    // ---- D2: the batch rows in order (value threads), each final once the
+    // rows before it are in; then the outputs
+    if (tid >= kD) {
+      const int j = tid - kD;
+      float acc[MR], out[MR];
+#pragma unroll
+      for (int i = 0; i < MR; ++i) {
+        if (i < nr) {
+          acc[i] = L.vv[i][j];
+          out[i] = L.sq[i][j];
+        }
+      }
 #pragma unroll
       for (int is = 0; is < MR; ++is) {
         if (is < nr) {
-          const float u = bt[is] * acc[is];
+          const float u = L.bt[is] * (acc[is] - L.aa[is][j]);
           L.ru[r0 + is][j] = u;
           float gk[MR], gq[MR];
           load_row<MR>(gk, L.gk[r0 + is]);
@@ -419,10 +458,8 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : 2) void kda_contract_kernel
       if (a.o != nullptr) {
 #pragma unroll
         for (int i = 0; i < MR; ++i)
-          if (i < nr) InT::store1(a.o, (int64_t(t0 + i) * a.H + h) * kD + j, out[i]);
+          if (i < nr) InT::store1(a.o, (int64_t(t0 + i) * a.H + h) * kD + j, out[i] + L.ww[i][j]);
       }
-    } else if (closes) {
-      close_factors(L.rk, L.rb, L.gam, kChunk, tid);
     }
     // the next batch's inputs, in flight during the close
     if (nr_next > 0) load_batch<InT, MR>(in, a, h, t0 + nr, nr_next, tid);
