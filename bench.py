@@ -269,8 +269,9 @@ def bench_prefill_batch(reps, warmup):
 def bench_contract(steps, warmup, n_sets=8):
     """The batch-invariant row contract: decode 64 x 12 (each request at its own position in the
     open 16-token chunk, uniform over 0..15; 8 rotated pool sets; every set takes a multiple of 16
-    calls per replay, so each request passes every position equally often), and the contract
-    prefill of 4096 x 12 and 32 x 4096 x 12 (bf16)."""
+    calls per replay, so each request passes every position equally often), verify + commit of 8
+    drafts for 32 x 12 (the plain verify workload; positions drift as commits land), and the
+    contract prefill of 4096 x 12 and 32 x 4096 x 12 (bf16)."""
     import numpy as np
     import torch
     from gated_delta_rule_15_amd import inputs as gen
@@ -312,6 +313,32 @@ def bench_contract(steps, warmup, n_sets=8):
             ms=ms, tokens_per_s=n_seq * T / (ms * 1e-3), fp32_tflops=flops / (ms * 1e-3) / 1e12,
             frac_fp32_valu_peak=flops / (ms * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS)
         del q, k, v, g, beta, o, pools
+    # verify (read-only) + commit of 8 drafts for 32 requests x 12 heads, each request at its own position
+    Nv, G = 32, 8
+    posv = rng.integers(0, CONTRACT_CHUNK, Nv)
+    lensv = [CONTRACT_CHUNK + int(x) for x in posv]
+    pv = gen.packed_batch(seed=38, seqlens=[L + G for L in lensv], H=H, dtype="bf16", init_state=True)
+    prev = np.concatenate([np.arange(pv.cu_seqlens[n], pv.cu_seqlens[n] + lensv[n]) for n in range(Nv)])
+    blk = np.stack([pv.cu_seqlens[n] + lensv[n] + np.arange(G) for n in range(Nv)])
+    cu_prev = np.concatenate([[0], np.cumsum(lensv)]).astype(np.int32)
+    basev = kda.kda_contract_pools(Nv, H, "cuda:0", to_dev(pv.initial_state))
+    kda.kda_contract_prefill(to_dev(pv.q[prev], "bf16"), to_dev(pv.k[prev], "bf16"), to_dev(pv.v[prev], "bf16"),
+                             to_dev(pv.g[prev]), to_dev(pv.beta[prev]), to_dev(cu_prev), *basev, with_output=False)
+    bq, bk, bv = to_dev(pv.q[blk], "bf16"), to_dev(pv.k[blk], "bf16"), to_dev(pv.v[blk], "bf16")
+    bg, bb = to_dev(pv.g[blk]), to_dev(pv.beta[blk])
+    acc = to_dev(gen.accepted_lengths(seed=4, N=Nv, G=G))
+    vsets = [tuple(x.clone() for x in basev) for _ in range(n_sets)]
+    vo = torch.empty((Nv, G, H, D), dtype=torch.bfloat16, device="cuda:0")
+    reps = max(16, steps // 4)
+
+    def vc(i):
+        st = vsets[i % n_sets]
+        kda.kda_contract_verify(bq, bk, bv, bg, bb, *st, o=vo)
+        kda.kda_contract_commit(bk, bv, bg, bb, acc, *st, q=bq)
+    ms_vc = graph_time_ms([lambda i=i: vc(i) for i in range(reps)], warmup)
+    res["contract_verify_commit_32x12x8_bf16"] = dict(ms=ms_vc, N=Nv, G=G, H=H,
+                                                      mean_accepted=float(acc.float().mean()))
+    del vsets
     return res
 
 
@@ -553,7 +580,8 @@ def main():
         log("row contract: decode 64 x 12, prefill 4096 x 12 and 32 x 4096 x 12 ...")
         ct = bench_contract(max(128, args.steps), args.warmup)
         cd = ct["contract_decode_64x12_bf16"]
-        log(f"row contract: decode {cd['ms'] * 1e3:.2f} us ({cd['gbps']:.0f} GB/s), prefill "
+        log(f"row contract: decode {cd['ms'] * 1e3:.2f} us ({cd['gbps']:.0f} GB/s), verify+commit "
+            f"{ct['contract_verify_commit_32x12x8_bf16']['ms'] * 1e3:.2f} us, prefill "
             f"{ct['contract_prefill_4096x12_bf16']['ms']:.3f} ms, 32 x 4096 x 12 "
             f"{ct['contract_prefill_32x4096x12_bf16']['ms']:.3f} ms")
         rows.update(ct)

@@ -279,6 +279,38 @@ kda_status_t kda_contract_decode(const void* q, const void* k, const void* v, co
   return hip_status(kda::launch_contract(c, dtype == KDA_BF16, static_cast<hipStream_t>(stream)));
 }
 
+kda_status_t kda_contract_verify(const void* q, const void* k, const void* v, const float* g,
+                                 const float* beta, int32_t N, int32_t gamma1, int32_t H, int32_t d_k,
+                                 int32_t d_v, kda_dtype_t dtype, float scale, const float* S_pool,
+                                 const float* rows_pool, const int32_t* pos_pool, const int32_t* slots, void* o,
+                                 void* stream) {
+  if (N < 0 || H <= 0 || gamma1 <= 0) return KDA_ERR_INVALID_ARG;
+  if (!dims_ok(d_k, d_v) || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
+  if (N == 0) return KDA_OK;
+  if (!q || !k || !v || !g || !beta || !S_pool || !rows_pool || !pos_pool || !o) return KDA_ERR_INVALID_ARG;
+  // read-only: the kernel writes only o (the pool pointers are not written through)
+  kda::ContractLaunch c{q, k, v, g, beta, nullptr, slots, const_cast<float*>(S_pool), const_cast<float*>(rows_pool),
+                        const_cast<int32_t*>(pos_pool), o, N, H, scale};
+  c.gamma = gamma1;
+  c.read_only = true;
+  return hip_status(kda::launch_contract(c, dtype == KDA_BF16, static_cast<hipStream_t>(stream)));
+}
+
+kda_status_t kda_contract_commit(const void* q, const void* k, const void* v, const float* g,
+                                 const float* beta, const int32_t* accepted_len, int32_t N, int32_t gamma1,
+                                 int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t dtype, float* S_pool,
+                                 float* rows_pool, int32_t* pos_pool, const int32_t* slots, void* stream) {
+  if (N < 0 || H <= 0 || gamma1 <= 0) return KDA_ERR_INVALID_ARG;
+  if (!dims_ok(d_k, d_v) || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
+  if (N == 0) return KDA_OK;
+  if (!k || !v || !g || !beta || !accepted_len || !S_pool || !rows_pool || !pos_pool) return KDA_ERR_INVALID_ARG;
+  // without q no outputs are formed; the kernel still reads a query, so it reads the keys
+  kda::ContractLaunch c{q ? q : k, k, v, g, beta, nullptr, slots, S_pool, rows_pool, pos_pool, nullptr, N, H, 1.0f};
+  c.gamma = gamma1;
+  c.counts = accepted_len;
+  return hip_status(kda::launch_contract(c, dtype == KDA_BF16, static_cast<hipStream_t>(stream)));
+}
+
 kda_status_t kda_contract_state(const float* S_pool, const float* rows_pool, const int32_t* pos_pool,
                                 const int32_t* slots, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
                                 float* state_out, void* stream) {

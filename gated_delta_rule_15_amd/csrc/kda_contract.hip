@@ -78,7 +78,7 @@ struct ContractArgs {
   const void* v;
   const float* g;
   const float* beta;
-  const int32_t* cu;     // prefill: [num_seqs + 1] token offsets; null: one token per sequence (token n)
+  const int32_t* cu;     // prefill: [num_seqs + 1] token offsets; null: gamma tokens per sequence (tokens n*gamma ...)
   const int32_t* slots;  // [num_seqs] or null (identity)
   float* S;              // [P, H, 128, 128]
   float* rows;           // [P, H, 16, 3, 128]
@@ -87,6 +87,9 @@ struct ContractArgs {
   int num_seqs;
   int H;
   float scale;
+  int gamma;              // tokens per sequence when cu is null (1: decode)
+  const int32_t* counts;  // with cu null: [num_seqs] tokens to take (clamped to 0..gamma), or null (all gamma)
+  int read_only;          // nonzero: outputs only, the pools are not written (verify)
 };
 
 // Rows of the batch being computed (at most MR) next to the open chunk's rows.
@@ -209,8 +212,8 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : 2) void kda_contract_kernel
     tok0 = a.cu[n];
     count = a.cu[n + 1] - tok0;
   } else {
-    tok0 = n;
-    count = 1;
+    tok0 = n * a.gamma;
+    count = a.counts ? min(max(a.counts[n], 0), a.gamma) : a.gamma;
   }
   if (count <= 0) return;
   const int64_t unit = int64_t(a.slots ? a.slots[n] : n) * a.H + h;
@@ -477,6 +480,7 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : 2) void kda_contract_kernel
   }
 
   // ---- write back: S_e if a chunk closed, the new open rows, the position
+  if (a.read_only) return;
   if (closed) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) st_f4(Sp + (c0 + i) * kD + j0, make_float4(S[i][0], S[i][1], S[i][2], S[i][3]));
@@ -548,8 +552,9 @@ hipError_t launch_as(const ContractArgs& a, hipStream_t stream) {
 hipError_t launch_contract(const ContractLaunch& c, bool bf16, hipStream_t stream) {
   if (c.num_seqs == 0) return hipSuccess;
   ContractArgs a{c.q, c.k, c.v, c.g, c.beta, c.cu_seqlens, c.slots, c.S_pool, c.rows_pool, c.pos_pool,
-                 c.o, c.num_seqs, c.H, c.scale};
-  if (c.cu_seqlens == nullptr) return bf16 ? launch_as<BF16, 1>(a, stream) : launch_as<F32, 1>(a, stream);
+                 c.o, c.num_seqs, c.H, c.scale, c.gamma, c.counts, c.read_only ? 1 : 0};
+  if (c.cu_seqlens == nullptr && c.gamma == 1)
+    return bf16 ? launch_as<BF16, 1>(a, stream) : launch_as<F32, 1>(a, stream);
   return bf16 ? launch_as<BF16, kChunk>(a, stream) : launch_as<F32, kChunk>(a, stream);
 }
 

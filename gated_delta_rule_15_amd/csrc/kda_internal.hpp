@@ -68,7 +68,7 @@ struct ContractLaunch {
   const void* v;
   const float* g;
   const float* beta;
-  const int32_t* cu_seqlens;  // prefill: [num_seqs + 1]; null: decode, token n is sequence n's one token
+  const int32_t* cu_seqlens;  // prefill: [num_seqs + 1]; null: sequence n's tokens are n*gamma .. n*gamma+gamma-1
   const int32_t* slots;       // [num_seqs] or null (identity)
   float* S_pool;              // [P, H, 128, 128] chunk-entry states
   float* rows_pool;           // [P, H, 16, 3, 128] open-chunk rows
@@ -77,6 +77,9 @@ struct ContractLaunch {
   int32_t num_seqs;
   int32_t H;
   float scale;
+  int32_t gamma = 1;                // tokens per sequence when cu_seqlens is null (1: decode)
+  const int32_t* counts = nullptr;  // with cu_seqlens null: device [num_seqs] tokens to apply (0..gamma)
+  bool read_only = false;           // outputs only; the pools are not written (verify)
 };
 
 hipError_t launch_contract(const ContractLaunch& c, bool bf16, hipStream_t stream);

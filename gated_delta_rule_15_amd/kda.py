@@ -478,3 +478,56 @@ def kda_contract_state(S_pool, rows_pool, pos_pool, slots=None, N: Optional[int]
                                       _ptr(state_out), _stream()),
                "kda_contract_state")
     return state_out
+
+
+def _need_block(q, k, v, g, beta):
+    N, G, H, _ = k.shape
+    dt = k.dtype
+    dev = k.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, (N, G, H, D), dt, dev)
+    _need(g, "g", (N, G, H, D), torch.float32, dev)
+    _need(beta, "beta", (N, G, H), torch.float32, dev)
+    return N, G, H, dt, dev
+
+
+def kda_contract_verify(q, k, v, g, beta, S_pool, rows_pool, pos_pool, slots=None, o=None, scale: float = 1.0):
+    """Outputs of gamma1 draft tokens per request from the contract state, which is not changed.
+
+    q, k, v, g: [N, G, H, 128]; beta: [N, G, H].  Returns o [N, G, H, 128]; o[:, t] equals, bit for bit,
+    the output of the (t+1)-th of t+1 kda_contract_decode calls."""
+    N, G, H, dt, dev = _need_block(q, k, v, g, beta)
+    P = _need_pools(S_pool, rows_pool, pos_pool, H, dev)
+    if slots is not None:
+        _need(slots, "slots", (N,), torch.int32, dev)
+    elif P < N:
+        raise ValueError("the pools have fewer rows than requests")
+    if o is None:
+        o = torch.empty((N, G, H, D), dtype=dt, device=dev)
+    _need(o, "o", (N, G, H, D), dt, dev)
+    lib = _lib.load()
+    _lib.check(lib.kda_contract_verify(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), N, G, H, D, D,
+                                       _dtype_code(k), float(scale), _ptr(S_pool), _ptr(rows_pool), _ptr(pos_pool),
+                                       _ptr(slots), _ptr(o), _stream()),
+               "kda_contract_verify")
+    return o
+
+
+def kda_contract_commit(k, v, g, beta, accepted_len, S_pool, rows_pool, pos_pool, slots=None, q=None):
+    """Apply the first accepted_len[n] (device int32 [N], clamped to 0..G) of each request's G tokens to
+    its contract state, in place: bit-identical to that many kda_contract_decode calls."""
+    N, G, H, _ = k.shape
+    dev = k.device
+    qq = q if q is not None else k
+    _need_block(qq, k, v, g, beta)
+    P = _need_pools(S_pool, rows_pool, pos_pool, H, dev)
+    _need(accepted_len, "accepted_len", (N,), torch.int32, dev)
+    if slots is not None:
+        _need(slots, "slots", (N,), torch.int32, dev)
+    elif P < N:
+        raise ValueError("the pools have fewer rows than requests")
+    lib = _lib.load()
+    _lib.check(lib.kda_contract_commit(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(accepted_len), N, G, H,
+                                       D, D, _dtype_code(k), _ptr(S_pool), _ptr(rows_pool), _ptr(pos_pool),
+                                       _ptr(slots), _stream()),
+               "kda_contract_commit")

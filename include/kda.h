@@ -308,6 +308,34 @@ kda_status_t kda_contract_decode(const void* q, const void* k, const void* v, co
                                  int32_t* pos_pool, const int32_t* slots, void* o, void* stream);
 
 /*
+ * kda_contract_verify — score gamma1 draft tokens per request under the
+ * contract, from the request's contract state, which is only READ (the
+ * ReplaySSM verify of "SGLang 和 Miles 为 Kimi K3 提供首日支持", section
+ * "ReplaySSM：针对 KDA 状态的原始输入重放", on the row contract of p4 §6.1).
+ *   q, k, g, v : [N, gamma1, H, 128];  beta : [N, gamma1, H];  o : [N, gamma1, H, 128]
+ * o[n, t] is bit-identical to the output of the (t+1)-th of t+1 successive
+ * kda_contract_decode calls on that state.  gamma1 >= 1 (any length; a chunk
+ * that fills up on the way is closed in registers only).
+ */
+kda_status_t kda_contract_verify(const void* q, const void* k, const void* v, const float* g,
+                                 const float* beta, int32_t N, int32_t gamma1, int32_t H, int32_t d_k,
+                                 int32_t d_v, kda_dtype_t dtype, float scale, const float* S_pool,
+                                 const float* rows_pool, const int32_t* pos_pool, const int32_t* slots, void* o,
+                                 void* stream);
+
+/*
+ * kda_contract_commit — apply the first accepted_len[n] of request n's gamma1
+ * tokens (the inputs the verify saw, same layout) to its contract state, in
+ * place; bit-identical to that many kda_contract_decode calls.  q may be NULL
+ * (no outputs are formed).  accepted_len: device int32 [N], clamped to
+ * 0 .. gamma1 (0 leaves the state unchanged).  Errors as kda_contract_prefill.
+ */
+kda_status_t kda_contract_commit(const void* q, const void* k, const void* v, const float* g,
+                                 const float* beta, const int32_t* accepted_len, int32_t N, int32_t gamma1,
+                                 int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t dtype, float* S_pool,
+                                 float* rows_pool, int32_t* pos_pool, const int32_t* slots, void* stream);
+
+/*
  * kda_contract_state — the running state S_t of N contract states:
  *   S_t = Diag(e^{b_last}) S_e + sum_{s < pos} (k_s e^{b_last - b_s}) u_s^T
  * (the chunk close applied to the rows held, which stay unchanged), into

@@ -34,7 +34,8 @@ def test_header_declares_the_entry_points():
                  "kda_compose_segments", "kda_prefill_checkpointed", "kda_prefill_checkpoint_count",
                  "kda_prefill_ordered", "kda_decode_step_prologue", "kda_verify_block_prologue",
                  "kda_verify_commit_prologue", "kda_prefill_prologue", "kda_contract_prefill",
-                 "kda_contract_decode", "kda_contract_state", "kda_status_string", "kda_version"):
+                 "kda_contract_decode", "kda_contract_state", "kda_contract_verify", "kda_contract_commit",
+                 "kda_status_string", "kda_version"):
         assert name in syms
     assert set(syms) == set(_lib.SIGNATURES), "binding signatures and header disagree"
 
@@ -192,6 +193,15 @@ def test_contract_argument_errors(lib):
     assert lib.kda_contract_prefill(None, p, p, p, p, p, good, 2, 2, 128, 128, 1, 1.0, p, p, p, None, p, None) == E
     assert lib.kda_contract_prefill(p, p, p, p, p, None, good, 2, 2, 128, 128, 1, 1.0, p, p, p, None, p, None) == E
     assert lib.kda_contract_prefill(p, p, p, p, p, p, good, 2, 2, 128, 128, 3, 1.0, p, p, p, None, p, None) == U
+    # verify (read-only; o required) and commit (q may be NULL; accepted_len required)
+    assert lib.kda_contract_verify(p, p, p, p, p, 4, 0, 2, 128, 128, 1, 1.0, p, p, p, None, p, None) == E
+    assert lib.kda_contract_verify(p, p, p, p, p, 4, 8, 2, 128, 128, 1, 1.0, p, p, p, None, None, None) == E
+    assert lib.kda_contract_verify(p, p, p, p, p, 4, 8, 2, 128, 64, 1, 1.0, p, p, p, None, p, None) == U
+    assert lib.kda_contract_verify(None, None, None, None, None, 0, 8, 2, 128, 128, 1, 1.0, None, None, None, None,
+                                   None, None) == 0
+    assert lib.kda_contract_commit(None, p, p, p, p, None, 4, 8, 2, 128, 128, 1, p, p, p, None, None) == E
+    assert lib.kda_contract_commit(None, p, p, p, p, p, 4, -1, 2, 128, 128, 1, p, p, p, None, None) == E
+    assert lib.kda_contract_commit(None, p, p, p, p, p, 4, 8, 2, 128, 128, 9, p, p, p, None, None) == U
     # state
     assert lib.kda_contract_state(p, p, p, None, 2, 2, 128, 128, None, None) == E
     assert lib.kda_contract_state(p, None, p, None, 2, 2, 128, 128, p, None) == E

@@ -331,3 +331,95 @@ def test_paths_are_bit_identical_f32():
     o_split = torch.cat([o1[:15], od[0:1], o3[:17], o1[15:], od[1:2], o3[17:]])
     assert torch.equal(_bits(o_split), _bits(o_whole))
     _assert_same_state(whole, split)
+
+
+def _block_inputs(p: gen.Packed, starts, G):
+    """[N, G, H, 128] blocks: tokens starts[n] .. starts[n] + G - 1 of sequence n."""
+    idx = np.stack([int(p.cu_seqlens[n]) + s + np.arange(G) for n, s in enumerate(starts)])
+    pick = lambda x: np.ascontiguousarray(x[idx])
+    return (to_dev(pick(p.q), p.dtype), to_dev(pick(p.k), p.dtype), to_dev(pick(p.v), p.dtype),
+            to_dev(pick(p.g)), to_dev(pick(p.beta)))
+
+
+def _positioned_pools(seed, N, H, G, dtype="bf16"):
+    """Pools after a prefill of 16 + pos_n tokens (pos_n spread over the chunk), with G more tokens per sequence."""
+    pos = np.arange(N) % 16
+    lens = [16 + int(x) for x in pos]
+    p = gen.packed_batch(seed=seed, seqlens=[L + G for L in lens], H=H, dtype=dtype, init_state=True)
+    pools = _pools(p)
+    _prefill(_slice(p, [(0, L) for L in lens]), pools, with_output=False)
+    return p, pools, lens
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_verify_equals_decode_steps_and_reads_only(dtype):
+    N, H, G = 20, 2, 8
+    p, pools, lens = _positioned_pools(41, N, H, G, dtype)
+    before = [x.clone() for x in pools]
+    q, k, v, g, beta = _block_inputs(p, lens, G)
+    o = _kda().kda_contract_verify(q, k, v, g, beta, *pools)
+    torch.cuda.synchronize()
+    for x, y in zip(pools, before):
+        assert torch.equal(x, y)  # the state is only read
+    steps = [x.clone() for x in pools]
+    for t in range(G):
+        od = _kda().kda_contract_decode(q[:, t].contiguous(), k[:, t].contiguous(), v[:, t].contiguous(),
+                                        g[:, t].contiguous(), beta[:, t].contiguous(), *steps)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(o[:, t]), _bits(od))
+    # and against the oracle
+    states = _oracle_states(p)
+    qq, kk, vv, gg, bb = (p.f64(x) for x in ("q", "k", "v", "g", "beta"))
+    o_ref = np.empty((N, G, H, 128))
+    for n, L in enumerate(lens):
+        a = int(p.cu_seqlens[n])
+        for h in range(H):
+            st = states[n][h]
+            cf.contract_tokens(st, qq[a:a + L, h], kk[a:a + L, h], vv[a:a + L, h], gg[a:a + L, h], bb[a:a + L, h])
+            o_ref[n, :, h] = cf.contract_tokens(st, qq[a + L:a + L + G, h], kk[a + L:a + L + G, h],
+                                                vv[a + L:a + L + G, h], gg[a + L:a + L + G, h],
+                                                bb[a + L:a + L + G, h])
+    assert rel_l2(to_f64(o), o_ref) <= TOL[dtype]
+
+
+def test_commit_equals_decode_steps():
+    N, H, G = 24, 2, 8
+    p, pools, lens = _positioned_pools(42, N, H, G)
+    q, k, v, g, beta = _block_inputs(p, lens, G)
+    acc = np.array([(3 * n) % 9 for n in range(N)], dtype=np.int32)  # 0 .. 8, every value
+    acc[5] = 12  # clamped to G
+    steps = [x.clone() for x in pools]
+    _kda().kda_contract_commit(k, v, g, beta, to_dev(acc), *pools)
+    torch.cuda.synchronize()
+    # reference: decode steps for each request's accepted prefix (requests stepped one slot at a time)
+    for n in range(N):
+        sl = torch.tensor([n], dtype=torch.int32, device=DEV)
+        for t in range(min(int(acc[n]), G)):
+            _kda().kda_contract_decode(q[n:n + 1, t].contiguous(), k[n:n + 1, t].contiguous(),
+                                       v[n:n + 1, t].contiguous(), g[n:n + 1, t].contiguous(),
+                                       beta[n:n + 1, t].contiguous(), *steps, slots=sl)
+    torch.cuda.synchronize()
+    _assert_same_state(pools, steps)
+
+
+def test_verify_commit_workload_sampled():
+    """32 requests x 12 heads x 8 drafts (the verify workload), positions spread over the chunk."""
+    N, H, G = 32, 12, 8
+    p, pools, lens = _positioned_pools(43, N, H, G)
+    q, k, v, g, beta = _block_inputs(p, lens, G)
+    o = _kda().kda_contract_verify(q, k, v, g, beta, *pools)
+    acc = to_dev(gen.accepted_lengths(43, N, G))
+    _kda().kda_contract_commit(k, v, g, beta, acc, *pools, q=q)
+    torch.cuda.synchronize()
+    S_run = to_f64(_kda().kda_contract_state(*pools))
+    qq, kk, vv, gg, bb = (p.f64(x) for x in ("q", "k", "v", "g", "beta"))
+    accn = acc.cpu().numpy()
+    for n, h in [(0, 0), (7, 5), (15, 11), (31, 3)]:
+        a, L = int(p.cu_seqlens[n]), lens[n]
+        o_ref, _ = orc.recurrence(qq[a:a + L + G, h], kk[a:a + L + G, h], vv[a:a + L + G, h], gg[a:a + L + G, h],
+                                  bb[a:a + L + G, h], p.initial_state[n, h])
+        assert rel_l2(to_f64(o[n, :, h]), o_ref[L:]) <= 2e-3
+        m = L + int(accn[n])
+        _, S_ref = orc.recurrence(qq[a:a + m, h], kk[a:a + m, h], vv[a:a + m, h], gg[a:a + m, h], bb[a:a + m, h],
+                                  p.initial_state[n, h])
+        assert rel_l2(S_run[n, h], S_ref) <= 2e-3
