@@ -44,6 +44,7 @@ namespace {
 constexpr int kChunk = 16;
 constexpr int kThreads = 256;
 constexpr int kRowFloats = 3 * kD;  // k, b, u
+constexpr int kRS = kD + 4;         // LDS row stride of the open rows' k and b: rows start 4 banks apart
 constexpr float kLog2e = 1.4426950408889634f;
 
 // e^x as 2^(x log2 e) on the hardware exponential: one rounding of the
@@ -95,8 +96,8 @@ struct ContractArgs {
 // Rows of the batch being computed (at most MR) next to the open chunk's rows.
 template <int MR>
 struct Lds {
-  float rk[kChunk][kD];  // k_s of the open chunk (k_s e^{b_15 - b_s} while closing)
-  float rb[kChunk][kD];  // b_s
+  float rk[kChunk][kRS];  // k_s of the open chunk (k_s e^{b_15 - b_s} while closing)
+  float rb[kChunk][kRS];  // b_s
   float ru[kChunk][kD];  // u_s
   float sq[MR][kD];      // scale * q_r
   float kh[MR][kD];      // k_r e^{b_r}
@@ -112,7 +113,7 @@ struct Lds {
 
 // The chunk close on this lane's 16 x 4 block: S <- e^{b_last} S + sum_s kbar_s u_s^T
 // over rows s = 0 .. nrows-1 in order (kbar already in rk, e^{b_last} in gam).
-__device__ __forceinline__ void close_block(float (&S)[16][4], const float (*rk)[kD], const float (*ru)[kD],
+__device__ __forceinline__ void close_block(float (&S)[16][4], const float (*rk)[kRS], const float (*ru)[kD],
                                             const float* gam, int nrows, int c0, int j0) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -146,7 +147,7 @@ __device__ __forceinline__ void close_block(float (&S)[16][4], const float (*rk)
 
 // Channel c's close factors: kbar_s = k_s e^{b_last - b_s} in place for rows 0 .. nrows-1,
 // and gam = e^{b_last}.
-__device__ __forceinline__ void close_factors(float (*rk)[kD], const float (*rb)[kD], float* gam, int nrows, int c) {
+__device__ __forceinline__ void close_factors(float (*rk)[kRS], const float (*rb)[kRS], float* gam, int nrows, int c) {
   const float bl = rb[nrows - 1][c];
   for (int s = 0; s < nrows; ++s) rk[s][c] = rk[s][c] * exp_c(bl - rb[s][c]);
   gam[c] = exp_c(bl);
@@ -501,8 +502,8 @@ __global__ __launch_bounds__(kThreads) void kda_contract_state_kernel(const floa
                                                                       const int32_t* __restrict__ pos_pool,
                                                                       const int32_t* __restrict__ slots,
                                                                       float* __restrict__ out, int N, int H) {
-  __shared__ __align__(16) float rk[kChunk][kD];
-  __shared__ __align__(16) float rb[kChunk][kD];
+  __shared__ __align__(16) float rk[kChunk][kRS];
+  __shared__ __align__(16) float rb[kChunk][kRS];
   __shared__ __align__(16) float ru[kChunk][kD];
   __shared__ __align__(16) float gam[kD];
   const int n = blockIdx.x / H;
