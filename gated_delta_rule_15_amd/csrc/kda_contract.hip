@@ -8,8 +8,8 @@
 //   b_r = b_{r-1} + g_r                       (cumulative log-decay, b_{-1} = 0)
 //   a_r = S_e^T (k_r e^{b_r}),  w_r = S_e^T (q'_r e^{b_r})          (q' = scale q)
 //   G_k[r,s] = sum_c k_rc k_sc e^{b_rc - b_sc},  G_q[r,s] = sum_c q'_rc k_sc e^{b_rc - b_sc}
-//   u_r = beta_r (v_r - a_r - sum_{s<r} G_k[r,s] u_s)
-//   o_r = w_r + sum_{s<=r} G_q[r,s] u_s
+//   u_r = beta_r ((v_r - sum_{s<r} G_k[r,s] u_s) - a_r)
+//   o_r = (sum_{s<=r} G_q[r,s] u_s) + w_r
 //
 // and the 16th row closes the chunk: S_e <- Diag(e^{b_15}) S_e +
 // sum_s (k_s e^{b_15 - b_s}) u_s^T.  This is the UT/WY chunk form of the
@@ -18,16 +18,16 @@
 //
 // Every fp32 result is produced by one fixed sequence of operations that does
 // not depend on how many rows a launch takes at once: the decode (one row per
-// call) and the prefill (up to 16 rows of a chunk at once) run the same kernel
-// body, each reduction has one association (a sequential fused multiply-add
-// chain over 16 channels, then a fixed tree over the 8 channel groups:
-// ((p0+p4)+(p2+p6))+((p1+p5)+(p3+p7)) for the S_e products,
-// ((p0+p1)+(p2+p3))+((p4+p5)+(p6+p7)) for the Gram entries), sums over earlier
-// rows run in row order, and the
-// file is built without floating-point contraction.  A token's output, the
-// rows and the chunk-entry state are therefore bit-identical whether the
-// token came through a prefill of any length, a decode step, or a batch of
-// any size.
+// call), the prefill (up to 16 rows of a chunk at once), the verify (a
+// request's drafts, pools untouched) and the commit (its accepted prefix) run
+// the same kernel body; each reduction has one association (a sequential
+// fused multiply-add chain over 16 channels, then a fixed tree over the 8
+// channel groups: ((p0+p4)+(p2+p6))+((p1+p5)+(p3+p7)) for the S_e products,
+// ((p0+p1)+(p2+p3))+((p4+p5)+(p6+p7)) for the Gram entries); the sums over
+// earlier rows run in row order, with a_r and w_r added last, so the
+// association depends on (r, s) only; and the file is built without
+// floating-point contraction.  A token's output, the rows and the chunk-entry
+// state are therefore bit-identical whichever call and batch computed them.
 //
 // Layout per (slot, head): S_e fp32 [128 key][128 value]; rows fp32 [16][3][128]
 // (k_s, b_s, u_s of the open chunk); position int32 (rows held, 0..15).
