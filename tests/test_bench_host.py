@@ -39,3 +39,30 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(os.path.dirname(bench.__file__), "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode != 0 and "one GPU" in (r.stdout + r.stderr)
+
+
+def test_contract_decode_bytes_enumerate_the_positions():
+    """The contract decode's per-(request, head) bytes, averaged over the 16 positions of the open chunk,
+    equal an explicit walk: a call at position r reads S_e and r open rows, writes row r unless r = 15,
+    writes S_e when r = 15, and moves the token's inputs, output and position."""
+    D, row = 128, 3 * 128 * 4
+    total = 0
+    for r in range(16):
+        moved = D * D * 4 + r * row            # S_e and the open rows
+        moved += D * D * 4 if r == 15 else row  # the close rewrites S_e; otherwise the new row
+        moved += 3 * 2 * D + 4 * D + 4          # q, k, v bf16; g fp32; beta
+        moved += 2 * D + 8                      # o bf16; position read and written
+        total += moved
+    assert total / 16 == bench.CONTRACT_DECODE_BYTES_PER_HEAD
+
+
+def test_contract_flops_enumerate_one_chunk():
+    """Per token-head flops of the contract prefill, from one 16-token chunk counted operation by operation."""
+    D = 128
+    flops = 0
+    for r in range(16):
+        flops += 2 * (2 * D * D)                # S_e^T k_hat and S_e^T q_hat (fused multiply-add = 2)
+        flops += (r + 1) * D * 7                # Gram entries: difference, exponential, product, 2 fmas
+        flops += (2 * r + 1) * 2 * D            # u (r terms) and o (r + 1 terms)
+    flops += 16 * D * 3 + D * D * (1 + 2 * 16)  # the close: key factors, then S_e update
+    assert flops / 16 == bench.FLOP_PER_TOKEN_HEAD_CONTRACT
