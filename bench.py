@@ -270,7 +270,8 @@ def bench_contract(steps, warmup, n_sets=8):
     """The batch-invariant row contract: decode 64 x 12 (each request at its own position in the
     open 16-token chunk, uniform over 0..15; 8 rotated pool sets; every set takes a multiple of 16
     calls per replay, so each request passes every position equally often), verify + commit of 8
-    drafts for 32 x 12 (the plain verify workload; positions drift as commits land), and the
+    drafts for 32 x 12 (the plain verify workload; positions drift as commits land; the commit
+    copies the rows the verify stashed, and the recomputing commit is timed beside it), and the
     contract prefill of 4096 x 12 and 32 x 4096 x 12 (bf16)."""
     import numpy as np
     import torch
@@ -331,12 +332,20 @@ def bench_contract(steps, warmup, n_sets=8):
     vo = torch.empty((Nv, G, H, D), dtype=torch.bfloat16, device="cuda:0")
     reps = max(16, steps // 4)
 
-    def vc(i):
+    stash = kda.kda_contract_stash(Nv, G, H, "cuda:0")
+
+    def vc(i):  # verify keeping its rows, commit from them
+        st = vsets[i % n_sets]
+        kda.kda_contract_verify(bq, bk, bv, bg, bb, *st, o=vo, stash=stash)
+        kda.kda_contract_commit_stash(stash, acc, *st, G=G)
+
+    def vc_recompute(i):  # verify, then a commit that recomputes the accepted rows
         st = vsets[i % n_sets]
         kda.kda_contract_verify(bq, bk, bv, bg, bb, *st, o=vo)
         kda.kda_contract_commit(bk, bv, bg, bb, acc, *st, q=bq)
     ms_vc = graph_time_ms([lambda i=i: vc(i) for i in range(reps)], warmup)
-    res["contract_verify_commit_32x12x8_bf16"] = dict(ms=ms_vc, N=Nv, G=G, H=H,
+    ms_rc = graph_time_ms([lambda i=i: vc_recompute(i) for i in range(reps)], warmup)
+    res["contract_verify_commit_32x12x8_bf16"] = dict(ms=ms_vc, recomputing_commit_ms=ms_rc, N=Nv, G=G, H=H,
                                                       mean_accepted=float(acc.float().mean()))
     del vsets
     return res

@@ -42,7 +42,8 @@ SIGNATURES = {
                                            _P, _P]),
     "kda_contract_state": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
     "kda_contract_verify": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_int, _F, _P, _P, _P, _P,
-                                           _P, _P]),
+                                           _P, _P, _P]),
+    "kda_contract_commit_stash": (ctypes.c_int, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
     "kda_contract_commit": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_int, _P, _P, _P, _P,
                                            _P]),
 }

@@ -283,8 +283,8 @@ kda_status_t kda_contract_verify(const void* q, const void* k, const void* v, co
                                  const float* beta, int32_t N, int32_t gamma1, int32_t H, int32_t d_k,
                                  int32_t d_v, kda_dtype_t dtype, float scale, const float* S_pool,
                                  const float* rows_pool, const int32_t* pos_pool, const int32_t* slots, void* o,
-                                 void* stream) {
-  if (N < 0 || H <= 0 || gamma1 <= 0) return KDA_ERR_INVALID_ARG;
+                                 float* stash, void* stream) {
+  if (N < 0 || H <= 0 || gamma1 <= 0 || (stash && gamma1 > 16)) return KDA_ERR_INVALID_ARG;
   if (!dims_ok(d_k, d_v) || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
   if (N == 0) return KDA_OK;
   if (!q || !k || !v || !g || !beta || !S_pool || !rows_pool || !pos_pool || !o) return KDA_ERR_INVALID_ARG;
@@ -293,7 +293,19 @@ kda_status_t kda_contract_verify(const void* q, const void* k, const void* v, co
                         const_cast<int32_t*>(pos_pool), o, N, H, scale};
   c.gamma = gamma1;
   c.read_only = true;
+  c.stash = stash;
   return hip_status(kda::launch_contract(c, dtype == KDA_BF16, static_cast<hipStream_t>(stream)));
+}
+
+kda_status_t kda_contract_commit_stash(const float* stash, const int32_t* accepted_len, int32_t N, int32_t gamma1,
+                                       int32_t H, int32_t d_k, int32_t d_v, float* S_pool, float* rows_pool,
+                                       int32_t* pos_pool, const int32_t* slots, void* stream) {
+  if (N < 0 || H <= 0 || gamma1 <= 0 || gamma1 > 16) return KDA_ERR_INVALID_ARG;
+  if (!dims_ok(d_k, d_v)) return KDA_ERR_UNSUPPORTED;
+  if (N == 0) return KDA_OK;
+  if (!stash || !accepted_len || !S_pool || !rows_pool || !pos_pool) return KDA_ERR_INVALID_ARG;
+  return hip_status(kda::launch_contract_commit_stash(stash, accepted_len, slots, S_pool, rows_pool, pos_pool, N, H,
+                                                      gamma1, static_cast<hipStream_t>(stream)));
 }
 
 kda_status_t kda_contract_commit(const void* q, const void* k, const void* v, const float* g,

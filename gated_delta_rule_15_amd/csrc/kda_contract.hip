@@ -91,6 +91,8 @@ struct ContractArgs {
   int gamma;              // tokens per sequence when cu is null (1: decode)
   const int32_t* counts;  // with cu null: [num_seqs] tokens to take (clamped to 0..gamma), or null (all gamma)
   int read_only;          // nonzero: outputs only, the pools are not written (verify)
+  float* stash;           // verify, or null: per (sequence, head) the rows of its gamma tokens
+                          // [gamma][3][128] and the entry state after a chunk closes [128][128]
 };
 
 // Rows of the batch being computed (at most MR) next to the open chunk's rows.
@@ -198,7 +200,7 @@ __device__ __forceinline__ void load_batch(BatchIn<InT, MR>& in, const ContractA
   }
 }
 
-template <typename InT, int MR>
+template <typename InT, int MR, bool STASH>
 __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : 2) void kda_contract_kernel(ContractArgs a) {
   __shared__ __align__(16) Lds<MR> L;
   const int n = blockIdx.x / a.H;
@@ -220,6 +222,8 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : 2) void kda_contract_kernel
   const int64_t unit = int64_t(a.slots ? a.slots[n] : n) * a.H + h;
   float* Sp = a.S + unit * kD * kD;
   float* Rp = a.rows + unit * kChunk * kRowFloats;
+  // stash of this (sequence, head): indexed by the sequence, not the slot
+  const int64_t unit_stash = STASH ? (int64_t(n) * a.H + h) * (int64_t(a.gamma) * kRowFloats + kD * kD) : 0;
   int p = a.pos[unit] & (kChunk - 1);
   const int p_first = p;
   const int c0 = 16 * (lane >> 3);
@@ -293,6 +297,11 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : 2) void kda_contract_kernel
           const float e = exp_c(b);
           L.rk[r0 + i][c] = kk;
           L.rb[r0 + i][c] = b;
+          if constexpr (STASH) {  // verify: the row's key and decay, for a later commit
+            float* row = a.stash + unit_stash + int64_t(done + i) * kRowFloats;
+            row[c] = kk;
+            row[kD + c] = b;
+          }
           L.sq[i][c] = sq;
           L.kh[i][c] = kk * e;
           L.qh[i][c] = sq * e;
@@ -447,6 +456,7 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : 2) void kda_contract_kernel
         if (is < nr) {
           const float u = L.bt[is] * (acc[is] - L.aa[is][j]);
           L.ru[r0 + is][j] = u;
+          if constexpr (STASH) a.stash[unit_stash + int64_t(done + is) * kRowFloats + 2 * kD + j] = u;
           float gk[MR], gq[MR];
           load_row<MR>(gk, L.gk[r0 + is]);
           load_row<MR>(gq, L.gq[r0 + is]);
@@ -473,6 +483,11 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : 2) void kda_contract_kernel
     if (!closes) break;  // a batch that does not close the chunk ends the sequence
     // ---- E: close the chunk
     close_block(S, L.rk, L.ru, L.gam, kChunk, c0, j0);
+    if constexpr (STASH) {  // verify: the closed entry state, for a commit that accepts past the chunk end
+      float* Sx = a.stash + unit_stash + int64_t(a.gamma) * kRowFloats;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st_f4(Sx + (c0 + i) * kD + j0, make_float4(S[i][0], S[i][1], S[i][2], S[i][3]));
+    }
     p = 0;
     closed = true;
     if (nr_next <= 0) break;
@@ -493,6 +508,42 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : 2) void kda_contract_kernel
     st_f4(Rp + s * kRowFloats + f, *reinterpret_cast<const float4*>(src));
   }
   if (tid == 0) a.pos[unit] = p;
+}
+
+// Commit from a verify's stash: the first L = accepted[n] (clamped to 0 .. gamma, gamma <= 16)
+// draft rows of (n, h) go to the open chunk; if the accepted rows reach the chunk end, the entry
+// state the verify formed at that close replaces S_e and the rows after it start the new chunk.
+// Pure copies of values the verify computed with the decode's arithmetic.
+__global__ __launch_bounds__(kThreads) void kda_contract_commit_stash_kernel(
+    const float* __restrict__ stash, const int32_t* __restrict__ accepted, const int32_t* __restrict__ slots,
+    float* __restrict__ S_pool, float* __restrict__ rows_pool, int32_t* __restrict__ pos_pool, int N, int H,
+    int gamma) {
+  const int n = blockIdx.x / H;
+  const int h = blockIdx.x % H;
+  if (n >= N) return;
+  const int tid = threadIdx.x;
+  const int L = min(max(accepted[n], 0), gamma);
+  if (L == 0) return;
+  const int64_t unit = int64_t(slots ? slots[n] : n) * H + h;
+  const float* st = stash + (int64_t(n) * H + h) * (int64_t(gamma) * kRowFloats + kD * kD);
+  int32_t* pp = pos_pool + unit;
+  const int p = *pp & (kChunk - 1);
+  float* Rp = rows_pool + unit * kChunk * kRowFloats;
+  constexpr int kVecs = kRowFloats / 4;
+  int first = 0, dst = p;                  // draft rows first .. L-1 go to pool rows dst ..
+  if (p + L >= kChunk) {                   // the drafts closed the chunk at draft kChunk - 1 - p
+    const float* Sx = st + int64_t(gamma) * kRowFloats;
+    float* Sp = S_pool + unit * kD * kD;
+    for (int e = tid; e < kD * kD / 4; e += kThreads) st_f4(Sp + 4 * e, ld_f4(Sx + 4 * e));
+    first = kChunk - p;
+    dst = 0;
+  }
+  for (int e = tid; e < (L - first) * kVecs; e += kThreads) {
+    const int r = e / kVecs, f = 4 * (e % kVecs);
+    st_f4(Rp + (dst + r) * kRowFloats + f, ld_f4(st + (first + r) * kRowFloats + f));
+  }
+  __syncthreads();  // every thread has read the position before it changes
+  if (tid == 0) *pp = (p + L) & (kChunk - 1);
 }
 
 // The running state S_t = Diag(e^{b_p-1}) S_e + sum_{s<p} (k_s e^{b_p-1 - b_s}) u_s^T:
@@ -541,10 +592,10 @@ __global__ __launch_bounds__(kThreads) void kda_contract_state_kernel(const floa
   for (int i = 0; i < 16; ++i) st_f4(dst + (c0 + i) * kD + j0, make_float4(S[i][0], S[i][1], S[i][2], S[i][3]));
 }
 
-template <typename InT, int MR>
+template <typename InT, int MR, bool STASH = false>
 hipError_t launch_as(const ContractArgs& a, hipStream_t stream) {
   const unsigned blocks = unsigned(a.num_seqs) * unsigned(a.H);
-  hipLaunchKernelGGL((kda_contract_kernel<InT, MR>), dim3(blocks), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((kda_contract_kernel<InT, MR, STASH>), dim3(blocks), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -553,10 +604,20 @@ hipError_t launch_as(const ContractArgs& a, hipStream_t stream) {
 hipError_t launch_contract(const ContractLaunch& c, bool bf16, hipStream_t stream) {
   if (c.num_seqs == 0) return hipSuccess;
   ContractArgs a{c.q, c.k, c.v, c.g, c.beta, c.cu_seqlens, c.slots, c.S_pool, c.rows_pool, c.pos_pool,
-                 c.o, c.num_seqs, c.H, c.scale, c.gamma, c.counts, c.read_only ? 1 : 0};
+                 c.o, c.num_seqs, c.H, c.scale, c.gamma, c.counts, c.read_only ? 1 : 0, c.stash};
+  if (c.stash != nullptr) return bf16 ? launch_as<BF16, kChunk, true>(a, stream) : launch_as<F32, kChunk, true>(a, stream);
   if (c.cu_seqlens == nullptr && c.gamma == 1)
     return bf16 ? launch_as<BF16, 1>(a, stream) : launch_as<F32, 1>(a, stream);
   return bf16 ? launch_as<BF16, kChunk>(a, stream) : launch_as<F32, kChunk>(a, stream);
+}
+
+hipError_t launch_contract_commit_stash(const float* stash, const int32_t* accepted, const int32_t* slots,
+                                        float* S_pool, float* rows_pool, int32_t* pos_pool, int N, int H, int gamma,
+                                        hipStream_t stream) {
+  if (N == 0) return hipSuccess;
+  hipLaunchKernelGGL(kda_contract_commit_stash_kernel, dim3(unsigned(N) * unsigned(H)), dim3(kThreads), 0, stream,
+                     stash, accepted, slots, S_pool, rows_pool, pos_pool, N, H, gamma);
+  return hipGetLastError();
 }
 
 hipError_t launch_contract_state(const float* S_pool, const float* rows_pool, const int32_t* pos_pool,

@@ -80,9 +80,13 @@ struct ContractLaunch {
   int32_t gamma = 1;                // tokens per sequence when cu_seqlens is null (1: decode)
   const int32_t* counts = nullptr;  // with cu_seqlens null: device [num_seqs] tokens to apply (0..gamma)
   bool read_only = false;           // outputs only; the pools are not written (verify)
+  float* stash = nullptr;           // verify: [num_seqs, H, gamma * 3 * 128 + 128 * 128] rows and closed state
 };
 
 hipError_t launch_contract(const ContractLaunch& c, bool bf16, hipStream_t stream);
+hipError_t launch_contract_commit_stash(const float* stash, const int32_t* accepted, const int32_t* slots,
+                                        float* S_pool, float* rows_pool, int32_t* pos_pool, int N, int H, int gamma,
+                                        hipStream_t stream);
 hipError_t launch_contract_state(const float* S_pool, const float* rows_pool, const int32_t* pos_pool,
                                  const int32_t* slots, float* out, int N, int H, hipStream_t stream);
 

@@ -491,11 +491,18 @@ def _need_block(q, k, v, g, beta):
     return N, G, H, dt, dev
 
 
-def kda_contract_verify(q, k, v, g, beta, S_pool, rows_pool, pos_pool, slots=None, o=None, scale: float = 1.0):
+def kda_contract_stash(N: int, G: int, H: int, device):
+    """A verify stash for kda_contract_verify / kda_contract_commit_stash: fp32 [N, H, G * 3 * 128 + 128 * 128]."""
+    return torch.empty((N, H, G * 3 * D + D * D), dtype=torch.float32, device=device)
+
+
+def kda_contract_verify(q, k, v, g, beta, S_pool, rows_pool, pos_pool, slots=None, o=None, scale: float = 1.0,
+                        stash=None):
     """Outputs of gamma1 draft tokens per request from the contract state, which is not changed.
 
     q, k, v, g: [N, G, H, 128]; beta: [N, G, H].  Returns o [N, G, H, 128]; o[:, t] equals, bit for bit,
-    the output of the (t+1)-th of t+1 kda_contract_decode calls."""
+    the output of the (t+1)-th of t+1 kda_contract_decode calls.  With ``stash`` (kda_contract_stash,
+    G <= 16) the verify also keeps what kda_contract_commit_stash needs."""
     N, G, H, dt, dev = _need_block(q, k, v, g, beta)
     P = _need_pools(S_pool, rows_pool, pos_pool, H, dev)
     if slots is not None:
@@ -505,12 +512,35 @@ def kda_contract_verify(q, k, v, g, beta, S_pool, rows_pool, pos_pool, slots=Non
     if o is None:
         o = torch.empty((N, G, H, D), dtype=dt, device=dev)
     _need(o, "o", (N, G, H, D), dt, dev)
+    if stash is not None:
+        if G > 16:
+            raise ValueError("a stash holds at most 16 drafts")
+        _need(stash, "stash", (N, H, G * 3 * D + D * D), torch.float32, dev)
     lib = _lib.load()
     _lib.check(lib.kda_contract_verify(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), N, G, H, D, D,
                                        _dtype_code(k), float(scale), _ptr(S_pool), _ptr(rows_pool), _ptr(pos_pool),
-                                       _ptr(slots), _ptr(o), _stream()),
+                                       _ptr(slots), _ptr(o), _ptr(stash), _stream()),
                "kda_contract_verify")
     return o
+
+
+def kda_contract_commit_stash(stash, accepted_len, S_pool, rows_pool, pos_pool, G: int, slots=None):
+    """Commit the accepted drafts from a verify's stash, in place: bit-identical to kda_contract_commit."""
+    N, H = stash.shape[0], stash.shape[1]
+    dev = stash.device
+    if G < 1 or G > 16:
+        raise ValueError("G must be in 1 .. 16")
+    _need(stash, "stash", (N, H, G * 3 * D + D * D), torch.float32, dev)
+    P = _need_pools(S_pool, rows_pool, pos_pool, H, dev)
+    _need(accepted_len, "accepted_len", (N,), torch.int32, dev)
+    if slots is not None:
+        _need(slots, "slots", (N,), torch.int32, dev)
+    elif P < N:
+        raise ValueError("the pools have fewer rows than requests")
+    lib = _lib.load()
+    _lib.check(lib.kda_contract_commit_stash(_ptr(stash), _ptr(accepted_len), N, G, H, D, D, _ptr(S_pool),
+                                             _ptr(rows_pool), _ptr(pos_pool), _ptr(slots), _stream()),
+               "kda_contract_commit_stash")
 
 
 def kda_contract_commit(k, v, g, beta, accepted_len, S_pool, rows_pool, pos_pool, slots=None, q=None):

@@ -311,17 +311,36 @@ kda_status_t kda_contract_decode(const void* q, const void* k, const void* v, co
  * kda_contract_verify — score gamma1 draft tokens per request under the
  * contract, from the request's contract state, which is only READ (the
  * ReplaySSM verify of "SGLang 和 Miles 为 Kimi K3 提供首日支持", section
- * "ReplaySSM：针对 KDA 状态的原始输入重放", on the row contract of p4 §6.1).
+ * "ReplaySSM：针对 KDA 状态的原始输入重放", on the row contract of the K3.1
+ * zero-mismatch article, section 6.1).
  *   q, k, g, v : [N, gamma1, H, 128];  beta : [N, gamma1, H];  o : [N, gamma1, H, 128]
  * o[n, t] is bit-identical to the output of the (t+1)-th of t+1 successive
  * kda_contract_decode calls on that state.  gamma1 >= 1 (any length; a chunk
  * that fills up on the way is closed in registers only).
+ *   stash : NULL, or fp32 [N, H, gamma1 * 3 * 128 + 128 * 128] (caller-owned):
+ *           receives each draft's row (k, cumulative log-decay, u) and, when
+ *           the drafts fill the open chunk, the chunk-entry state after that
+ *           close — what kda_contract_commit_stash needs.  Requires gamma1 <= 16.
  */
 kda_status_t kda_contract_verify(const void* q, const void* k, const void* v, const float* g,
                                  const float* beta, int32_t N, int32_t gamma1, int32_t H, int32_t d_k,
                                  int32_t d_v, kda_dtype_t dtype, float scale, const float* S_pool,
                                  const float* rows_pool, const int32_t* pos_pool, const int32_t* slots, void* o,
-                                 void* stream);
+                                 float* stash, void* stream);
+
+/*
+ * kda_contract_commit_stash — the commit of kda_contract_commit, from the stash
+ * a kda_contract_verify call (same N, gamma1, H, slots, and the pools unchanged
+ * since) filled: the accepted draft rows, and the closed entry state when they
+ * reach the chunk end, are copied into the pools.  Bit-identical to
+ * kda_contract_commit and to that many kda_contract_decode calls, without
+ * re-reading the entry state or the inputs.  accepted_len: device int32 [N],
+ * clamped to 0 .. gamma1.  Errors: KDA_ERR_INVALID_ARG for a NULL buffer or
+ * gamma1 outside 1 .. 16; KDA_ERR_UNSUPPORTED for d != 128.
+ */
+kda_status_t kda_contract_commit_stash(const float* stash, const int32_t* accepted_len, int32_t N, int32_t gamma1,
+                                       int32_t H, int32_t d_k, int32_t d_v, float* S_pool, float* rows_pool,
+                                       int32_t* pos_pool, const int32_t* slots, void* stream);
 
 /*
  * kda_contract_commit — apply the first accepted_len[n] of request n's gamma1

@@ -423,3 +423,25 @@ def test_verify_commit_workload_sampled():
         _, S_ref = orc.recurrence(qq[a:a + m, h], kk[a:a + m, h], vv[a:a + m, h], gg[a:a + m, h], bb[a:a + m, h],
                                   p.initial_state[n, h])
         assert rel_l2(S_run[n, h], S_ref) <= 2e-3
+
+
+@pytest.mark.parametrize("G", [8, 16])
+def test_commit_from_the_verify_stash(G):
+    """Verify with a stash, then commit from it: the pools equal those of the recomputing commit, bit for
+    bit, for every accepted length (requests at every position, so drafts cross the chunk end or not);
+    the verify's outputs do not change with the stash."""
+    N, H = 24, 2
+    p, pools, lens = _positioned_pools(44 + G, N, H, G)
+    q, k, v, g, beta = _block_inputs(p, lens, G)
+    acc = np.array([(5 * n) % (G + 1) for n in range(N)], dtype=np.int32)
+    acc[3] = G + 4  # clamped
+    ref = [x.clone() for x in pools]
+    o_plain = _kda().kda_contract_verify(q, k, v, g, beta, *pools)
+    stash = _kda().kda_contract_stash(N, G, H, DEV)
+    o_st = _kda().kda_contract_verify(q, k, v, g, beta, *pools, stash=stash)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(o_plain), _bits(o_st))
+    _kda().kda_contract_commit_stash(stash, to_dev(acc), *pools, G=G)
+    _kda().kda_contract_commit(k, v, g, beta, to_dev(acc), *ref, q=q)
+    torch.cuda.synchronize()
+    _assert_same_state(pools, ref)
