@@ -281,3 +281,21 @@ def test_prefill_batch_invariant_across_launch_shapes(prologue):
     assert torch.equal(o_all[:t].view(torch.int16), o_sub[:t].view(torch.int16))
     assert torch.equal(S_all[:n].view(torch.int32), S_sub.view(torch.int32))
     assert torch.equal(M_all[:n].view(torch.int32), M_sub.view(torch.int32))
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_prefill_random_batches(case):
+    """Seeded random batches: head count, ragged lengths with empty sequences, initial states on some
+    sequences, input type and scale all vary; outputs and final states against the oracle."""
+    rng = np.random.default_rng(900 + case)
+    H = int(rng.choice([1, 3, 5, 12]))
+    n_seq = int(rng.integers(1, 7))
+    lens = [int(x) if rng.random() > 0.15 else 0 for x in rng.integers(1, 300, n_seq)]
+    if sum(lens) == 0:
+        lens[0] = 37
+    dtype = "bf16" if case % 2 == 0 else "f32"
+    init = [bool(x) for x in rng.random(n_seq) < 0.6]
+    scale = float(rng.uniform(0.2, 1.5))
+    p = gen.packed_batch(seed=900 + case, seqlens=lens, H=H, dtype=dtype, init_state=init)
+    o, S, _ = _run(p, scale=scale)
+    _check(p, o, S, f"random batch {case}: H={H} lens={lens} {dtype}", scale=scale)
