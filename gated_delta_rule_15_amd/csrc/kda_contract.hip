@@ -324,13 +324,19 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : 2) void kda_contract_kernel
       const int cm = 16 * (lane & 7);
       for (int base = 0; base < ntask; base += kThreads / 8) {
         const int task = base + (tid >> 3);
-        int i = 0, s = task;
-        while (i < nr - 1 && s >= r0 + i + 1) {  // task -> (batch row i, earlier row s)
-          s -= r0 + i + 1;
-          ++i;
+        // task -> (batch row i, earlier row s): row i owns r0 + i + 1 entries from
+        // first(i) = i (r0 + 1) + i (i - 1) / 2, so i is the floor of the root of
+        // first(i) = task, corrected by one either way for the rounding of the root
+        int i = 0;
+        if constexpr (MR > 1) {
+          const int a2 = 2 * r0 + 1;
+          i = int((__builtin_amdgcn_sqrtf(float(a2 * a2 + 8 * task)) - float(a2)) * 0.5f);
+          if ((i + 1) * (r0 + 1) + (i + 1) * i / 2 <= task) ++i;
+          if (i * (r0 + 1) + i * (i - 1) / 2 > task) --i;
+          i = min(i, nr - 1);
         }
         const bool valid = task < ntask;
-        if (!valid) s = 0;
+        const int s = valid ? task - (i * (r0 + 1) + i * (i - 1) / 2) : 0;
         const int r = r0 + i;
         float pk = 0.f, pq = 0.f;
 #pragma unroll
@@ -443,30 +449,36 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : 2) void kda_contract_kernel
     // rows before it are in; then the outputs
     if (tid >= kD) {
       const int j = tid - kD;
+      // Within a step every later row of the pass is updated, also those past
+      // nr (their values are unused and never stored), so the update has no
+      // per-row branches; a row's arithmetic involves only the rows before it.
       float acc[MR], out[MR];
 #pragma unroll
       for (int i = 0; i < MR; ++i) {
-        if (i < nr) {
-          acc[i] = L.vv[i][j];
-          out[i] = L.sq[i][j];
+        acc[i] = L.vv[i][j];
+        out[i] = L.sq[i][j];
+      }
+      // u_r replaces its residual in acc; the rows are stored after the chain
+#pragma unroll
+      for (int is = 0; is < MR; ++is) {
+        if (is < nr) {
+          float gk[MR], gq[MR];
+          load_row<MR>(gk, L.gk[r0 + is]);
+          load_row<MR>(gq, L.gq[r0 + is]);
+          const float u = L.bt[is] * (acc[is] - L.aa[is][j]);
+          acc[is] = u;
+#pragma unroll
+          for (int i = is; i < MR; ++i) {
+            if (i > is) acc[i] = __builtin_fmaf(-gk[i], u, acc[i]);
+            out[i] = __builtin_fmaf(gq[i], u, out[i]);
+          }
         }
       }
 #pragma unroll
       for (int is = 0; is < MR; ++is) {
         if (is < nr) {
-          const float u = L.bt[is] * (acc[is] - L.aa[is][j]);
-          L.ru[r0 + is][j] = u;
-          if constexpr (STASH) a.stash[unit_stash + int64_t(done + is) * kRowFloats + 2 * kD + j] = u;
-          float gk[MR], gq[MR];
-          load_row<MR>(gk, L.gk[r0 + is]);
-          load_row<MR>(gq, L.gq[r0 + is]);
-#pragma unroll
-          for (int i = is; i < MR; ++i) {
-            if (i < nr) {
-              if (i > is) acc[i] = __builtin_fmaf(-gk[i], u, acc[i]);
-              out[i] = __builtin_fmaf(gq[i], u, out[i]);
-            }
-          }
+          L.ru[r0 + is][j] = acc[is];
+          if constexpr (STASH) a.stash[unit_stash + int64_t(done + is) * kRowFloats + 2 * kD + j] = acc[is];
         }
       }
       if (a.o != nullptr) {
