@@ -617,9 +617,16 @@ hipError_t launch_contract(const ContractLaunch& c, bool bf16, hipStream_t strea
   if (c.num_seqs == 0) return hipSuccess;
   ContractArgs a{c.q, c.k, c.v, c.g, c.beta, c.cu_seqlens, c.slots, c.S_pool, c.rows_pool, c.pos_pool,
                  c.o, c.num_seqs, c.H, c.scale, c.gamma, c.counts, c.read_only ? 1 : 0, c.stash};
-  if (c.stash != nullptr) return bf16 ? launch_as<BF16, kChunk, true>(a, stream) : launch_as<F32, kChunk, true>(a, stream);
+  // Rows per pass: 1 for decode, 8 for draft blocks of up to 8 tokens, 16
+  // otherwise (a row's arithmetic does not depend on it, only registers do).
+  const bool block8 = c.cu_seqlens == nullptr && c.gamma <= 8;
+  if (c.stash != nullptr) {
+    if (block8) return bf16 ? launch_as<BF16, 8, true>(a, stream) : launch_as<F32, 8, true>(a, stream);
+    return bf16 ? launch_as<BF16, kChunk, true>(a, stream) : launch_as<F32, kChunk, true>(a, stream);
+  }
   if (c.cu_seqlens == nullptr && c.gamma == 1)
     return bf16 ? launch_as<BF16, 1>(a, stream) : launch_as<F32, 1>(a, stream);
+  if (block8) return bf16 ? launch_as<BF16, 8>(a, stream) : launch_as<F32, 8>(a, stream);
   return bf16 ? launch_as<BF16, kChunk>(a, stream) : launch_as<F32, kChunk>(a, stream);
 }
 
