@@ -543,16 +543,32 @@ __global__ __launch_bounds__(kThreads) void kda_contract_commit_stash_kernel(
   float* Rp = rows_pool + unit * kChunk * kRowFloats;
   constexpr int kVecs = kRowFloats / 4;
   int first = 0, dst = p;                  // draft rows first .. L-1 go to pool rows dst ..
+  // every load of a thread is issued before its first store, so the copies
+  // wait for memory once rather than once per vector
   if (p + L >= kChunk) {                   // the drafts closed the chunk at draft kChunk - 1 - p
     const float* Sx = st + int64_t(gamma) * kRowFloats;
     float* Sp = S_pool + unit * kD * kD;
-    for (int e = tid; e < kD * kD / 4; e += kThreads) st_f4(Sp + 4 * e, ld_f4(Sx + 4 * e));
+    constexpr int kPer = kD * kD / 4 / kThreads;
+    float4 x[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) x[i] = ld_f4(Sx + 4 * (tid + i * kThreads));
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) st_f4(Sp + 4 * (tid + i * kThreads), x[i]);
     first = kChunk - p;
     dst = 0;
   }
-  for (int e = tid; e < (L - first) * kVecs; e += kThreads) {
-    const int r = e / kVecs, f = 4 * (e % kVecs);
-    st_f4(Rp + (dst + r) * kRowFloats + f, ld_f4(st + (first + r) * kRowFloats + f));
+  constexpr int kRowIters = (kChunk * kVecs + kThreads - 1) / kThreads;  // at most 16 rows
+  const int nvec = (L - first) * kVecs;
+  float4 y[kRowIters];
+#pragma unroll
+  for (int i = 0; i < kRowIters; ++i) {
+    const int e = tid + i * kThreads;
+    if (e < nvec) y[i] = ld_f4(st + (first + e / kVecs) * kRowFloats + 4 * (e % kVecs));
+  }
+#pragma unroll
+  for (int i = 0; i < kRowIters; ++i) {
+    const int e = tid + i * kThreads;
+    if (e < nvec) st_f4(Rp + (dst + e / kVecs) * kRowFloats + 4 * (e % kVecs), y[i]);
   }
   __syncthreads();  // every thread has read the position before it changes
   if (tid == 0) *pp = (p + L) & (kChunk - 1);
