@@ -237,8 +237,8 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : 2) void kda_contract_kernel
   load_batch<InT, MR>(in, a, h, tok0, nr, tid);
   constexpr int kRowVecs = kRowFloats / 4;
   float S[16][4];
-  if constexpr (MR == 1) {
-    // one row per call: the open rows are issued before S_e and held in registers
+  if constexpr (MR <= 8) {
+    // decode and draft blocks: the open rows are issued before S_e and held in registers
     constexpr int kRowIters = ((kChunk - 1) * kRowVecs + kThreads - 1) / kThreads;
     float4 rv[kRowIters];
 #pragma unroll
