@@ -378,10 +378,12 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : 2) void kda_contract_kernel
     const int nr_next = min(MR, count - done - nr);  // after a close the next batch starts a chunk
     if (tid >= kD) {
       const int j = tid - kD;
+      // all MR rows, also those past nr (unused, never stored as results): no
+      // per-row branches in the loop
       float acc[MR], out[MR];
 #pragma unroll
       for (int i = 0; i < MR; ++i) {
-        acc[i] = (i < nr) ? L.vv[i][j] : 0.f;
+        acc[i] = L.vv[i][j];
         out[i] = 0.f;
       }
 #pragma unroll 2
@@ -392,18 +394,14 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : 2) void kda_contract_kernel
         load_row<MR>(gq, L.gq[s]);
 #pragma unroll
         for (int i = 0; i < MR; ++i) {
-          if (i < nr) {
-            acc[i] = __builtin_fmaf(-gk[i], u, acc[i]);
-            out[i] = __builtin_fmaf(gq[i], u, out[i]);
-          }
+          acc[i] = __builtin_fmaf(-gk[i], u, acc[i]);
+          out[i] = __builtin_fmaf(gq[i], u, out[i]);
         }
       }
 #pragma unroll
       for (int i = 0; i < MR; ++i) {
-        if (i < nr) {
-          L.vv[i][j] = acc[i];
-          L.sq[i][j] = out[i];
-        }
+        L.vv[i][j] = acc[i];
+        L.sq[i][j] = out[i];
       }
     } else if (closes) {
       close_factors(L.rk, L.rb, L.gam, kChunk, tid);
