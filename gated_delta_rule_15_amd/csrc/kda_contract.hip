@@ -98,8 +98,8 @@ struct ContractArgs {
 // Rows of the batch being computed (at most MR) next to the open chunk's rows.
 template <int MR>
 struct Lds {
-  float rk[kChunk][kRS];  // k_s of the open chunk (k_s e^{b_15 - b_s} while closing)
-  float rb[kChunk][kRS];  // b_s
+  float rk[kChunk + 1][kRS];  // k_s of the open chunk (k_s e^{b_15 - b_s} while closing); last row: discard
+  float rb[kChunk + 1][kRS];  // b_s; last row: discard
   float ru[kChunk][kD];  // u_s
   float sq[MR][kD];      // scale * q_r
   float kh[MR][kD];      // k_r e^{b_r}
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : 2) void kda_contract_kernel
   // Loads in the order they are needed: the batch inputs and the open rows
   // first, S_e last, so that everything except the S_e products runs while
   // S_e streams in (loads complete in issue order).
-  BatchIn<InT, MR> in;
+  BatchIn<InT, MR> in{};  // rows past a short batch are read but unused: keep them defined
   int nr = min(min(MR, kChunk - p), count);
   load_batch<InT, MR>(in, a, h, tok0, nr, tid);
   constexpr int kRowVecs = kRowFloats / 4;
@@ -288,33 +288,35 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : 2) void kda_contract_kernel
     if (tid < kD) {
       const int c = tid;
       float b = (r0 > 0) ? L.rb[r0 - 1][c] : 0.0f;
+      // every row of the pass, without branches: rows past nr are formed from
+      // inputs that were not loaded, their open-chunk row goes to the discard
+      // row, and nothing reads them as results
 #pragma unroll
       for (int i = 0; i < MR; ++i) {
-        if (i < nr) {
-          const float kk = InT::unpack1(in.x0[i]);
-          const float sq = a.scale * InT::unpack1(in.x1[i]);
-          b = b + in.f[i];
-          const float e = exp_c(b);
-          L.rk[r0 + i][c] = kk;
-          L.rb[r0 + i][c] = b;
-          if constexpr (STASH) {  // verify: the row's key and decay, for a later commit
+        const float kk = InT::unpack1(in.x0[i]);
+        const float sq = a.scale * InT::unpack1(in.x1[i]);
+        b = b + in.f[i];
+        const float e = exp_c(b);
+        const int rr = (i < nr) ? r0 + i : kChunk;
+        L.rk[rr][c] = kk;
+        L.rb[rr][c] = b;
+        if constexpr (STASH) {  // verify: the row's key and decay, for a later commit
+          if (i < nr) {
             float* row = a.stash + unit_stash + int64_t(done + i) * kRowFloats;
             row[c] = kk;
             row[kD + c] = b;
           }
-          L.sq[i][c] = sq;
-          L.kh[i][c] = kk * e;
-          L.qh[i][c] = sq * e;
         }
+        L.sq[i][c] = sq;
+        L.kh[i][c] = kk * e;
+        L.qh[i][c] = sq * e;
       }
     } else {
       const int j = tid - kD;
 #pragma unroll
       for (int i = 0; i < MR; ++i) {
-        if (i < nr) {
-          L.vv[i][j] = InT::unpack1(in.x0[i]);
-          if (j == 0) L.bt[i] = in.f[i];
-        }
+        L.vv[i][j] = InT::unpack1(in.x0[i]);
+        if (j == 0) L.bt[i] = in.f[i];
       }
     }
     __syncthreads();
