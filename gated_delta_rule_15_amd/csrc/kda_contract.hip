@@ -289,8 +289,8 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : 2) void kda_contract_kernel
       const int c = tid;
       float b = (r0 > 0) ? L.rb[r0 - 1][c] : 0.0f;
       // every row of the pass, without branches: rows past nr are formed from
-      // inputs that were not loaded, their open-chunk row goes to the discard
-      // row, and nothing reads them as results
+      // stale inputs (zeros, or an earlier batch's), their open-chunk row goes
+      // to the discard row, and nothing reads them as results
 #pragma unroll
       for (int i = 0; i < MR; ++i) {
         const float kk = InT::unpack1(in.x0[i]);
