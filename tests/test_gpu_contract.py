@@ -445,3 +445,42 @@ def test_commit_from_the_verify_stash(G):
     _kda().kda_contract_commit(k, v, g, beta, to_dev(acc), *ref, q=q)
     torch.cuda.synchronize()
     _assert_same_state(pools, ref)
+
+
+@pytest.mark.parametrize("G", [1, 2, 3, 5, 7, 9, 12, 15])
+def test_draft_blocks_of_every_length(G):
+    """Draft blocks on both sides of the 8-row / 16-row builds, from every position in the chunk
+    (short passes, passes that close the chunk and continue): verify outputs equal decode steps bit
+    for bit with or without a stash, and the stash commit, the recomputing commit and decode steps of
+    the accepted tokens leave the same pools."""
+    N, H = 16, 2
+    p, pools, lens = _positioned_pools(60 + G, N, H, G)
+    q, k, v, g, beta = _block_inputs(p, lens, G)
+    acc = np.array([(3 * n + 1) % (G + 1) for n in range(N)], dtype=np.int32)
+    ref = [x.clone() for x in pools]
+    steps = [x.clone() for x in pools]
+    o = _kda().kda_contract_verify(q, k, v, g, beta, *pools)
+    stash = _kda().kda_contract_stash(N, G, H, DEV)
+    o_st = _kda().kda_contract_verify(q, k, v, g, beta, *pools, stash=stash)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(o), _bits(o_st))
+    full = [x.clone() for x in pools]  # every draft decoded: the verify's outputs
+    before = [x.clone() for x in steps]
+    for t in range(G):
+        tok = (q[:, t].contiguous(), k[:, t].contiguous(), v[:, t].contiguous(), g[:, t].contiguous(),
+               beta[:, t].contiguous())
+        od = _kda().kda_contract_decode(*tok, *full)
+        _kda().kda_contract_decode(*tok, *steps)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(o[:, t]), _bits(od))
+        done = [n for n in range(N) if acc[n] <= t]  # accepted prefix already ended: undo this step
+        if done:
+            idx = torch.tensor(done, dtype=torch.long, device=DEV)
+            for x, y in zip(steps, before):
+                x[idx] = y[idx]
+        before = [x.clone() for x in steps]
+    _kda().kda_contract_commit_stash(stash, to_dev(acc), *pools, G=G)
+    _kda().kda_contract_commit(k, v, g, beta, to_dev(acc), *ref, q=q)
+    torch.cuda.synchronize()
+    _assert_same_state(pools, ref)
+    _assert_same_state(pools, steps)
