@@ -35,6 +35,8 @@
 // 32w .. 32w+31 of S_e in registers: lane (m = lane >> 3, jq = lane & 7) holds
 // key rows 16m .. 16m+15 of columns 32w + 4jq .. +3, so the 8 channel groups of
 // every S_e^T x product meet inside the wave (lane bits 5, 4, 3, in that order).
+// A prefill of few (sequence, head) units splits each over four workgroups of
+// 32 columns (lane: one column, same channel groups and tree; see SPLIT).
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
@@ -115,16 +117,21 @@ struct Lds {
 
 // The chunk close on this lane's 16 x 4 block: S <- e^{b_last} S + sum_s kbar_s u_s^T
 // over rows s = 0 .. nrows-1 in order (kbar already in rk, e^{b_last} in gam).
-__device__ __forceinline__ void close_block(float (&S)[16][4], const float (*rk)[kRS], const float (*ru)[kD],
+template <int CW>
+__device__ __forceinline__ void close_block(float (&S)[16][CW], const float (*rk)[kRS], const float (*ru)[kD],
                                             const float* gam, int nrows, int c0, int j0) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const float e = gam[c0 + i];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) S[i][x] = e * S[i][x];
+    for (int x = 0; x < CW; ++x) S[i][x] = e * S[i][x];
   }
   // row s's operands are read while row s - 1's products are formed
-  float4 un = *reinterpret_cast<const float4*>(&ru[0][j0]);
+  auto ld_u = [&](int s) {
+    if constexpr (CW == 4) return *reinterpret_cast<const float4*>(&ru[s][j0]);
+    else return make_float4(ru[s][j0], 0.f, 0.f, 0.f);
+  };
+  float4 un = ld_u(0);
   float4 kn[4];
 #pragma unroll
   for (int i4 = 0; i4 < 4; ++i4) kn[i4] = *reinterpret_cast<const float4*>(&rk[0][c0 + 4 * i4]);
@@ -136,14 +143,14 @@ __device__ __forceinline__ void close_block(float (&S)[16][4], const float (*rk)
       kb[4 * i4] = kn[i4].x; kb[4 * i4 + 1] = kn[i4].y; kb[4 * i4 + 2] = kn[i4].z; kb[4 * i4 + 3] = kn[i4].w;
     }
     if (s + 1 < nrows) {
-      un = *reinterpret_cast<const float4*>(&ru[s + 1][j0]);
+      un = ld_u(s + 1);
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) kn[i4] = *reinterpret_cast<const float4*>(&rk[s + 1][c0 + 4 * i4]);
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i)
 #pragma unroll
-      for (int x = 0; x < 4; ++x) S[i][x] = __builtin_fmaf(kb[i], u[x], S[i][x]);
+      for (int x = 0; x < CW; ++x) S[i][x] = __builtin_fmaf(kb[i], u[x], S[i][x]);
   }
 }
 
@@ -200,15 +207,30 @@ __device__ __forceinline__ void load_batch(BatchIn<InT, MR>& in, const ContractA
   }
 }
 
-template <typename InT, int MR, bool STASH>
-__global__ __launch_bounds__(kThreads, MR == 1 ? 3 : 2) void kda_contract_kernel(ContractArgs a) {
+// SPLIT (prefill of small grids): four workgroups per (sequence, head), one per
+// 32 value columns; a lane holds one column of its 16 key rows (CW = 1 instead
+// of 4), so the S_e products and the close cost a quarter per lane, with the
+// same chains and the same tree.  The Gram entries, the decay and the
+// substitution are formed in each workgroup alike.  The workgroups write only
+// what they own (S_e columns, the u columns of the open rows, outputs); the
+// shared keys, decays and position are written by kda_contract_rows_kernel,
+// launched after, so that no write can overtake a sibling's read.
+template <typename InT, int MR, bool STASH, bool SPLIT = false>
+__global__ __launch_bounds__(kThreads, MR == 1 ? 3 : (SPLIT ? 1 : 2)) void kda_contract_kernel(ContractArgs a) {
+  static_assert(!SPLIT || (MR == kChunk && !STASH), "the split serves the prefill");
+  constexpr int CW = SPLIT ? 1 : 4;      // value columns per lane
+  constexpr int kSlices = SPLIT ? 4 : 1;  // workgroups per (sequence, head)
   __shared__ __align__(16) Lds<MR> L;
-  const int n = blockIdx.x / a.H;
-  const int h = blockIdx.x % a.H;
+  const int slice = blockIdx.x % kSlices;
+  const int n = (blockIdx.x / kSlices) / a.H;
+  const int h = (blockIdx.x / kSlices) % a.H;
   if (n >= a.num_seqs) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  // value threads: tid >= kD; with SPLIT the first 32 of them, for this slice's columns
+  const bool value_thread = tid >= kD && (!SPLIT || tid - kD < 32);
+  const int jv = SPLIT ? 32 * slice + (tid - kD) : tid - kD;  // value column of a value thread
 
   int tok0, count;
   if (a.cu != nullptr) {
@@ -227,7 +249,7 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : 2) void kda_contract_kernel
   int p = a.pos[unit] & (kChunk - 1);
   const int p_first = p;
   const int c0 = 16 * (lane >> 3);
-  const int j0 = 32 * wave + 4 * (lane & 7);
+  const int j0 = SPLIT ? 32 * slice + 8 * wave + (lane & 7) : 32 * wave + 4 * (lane & 7);
 
   // Loads in the order they are needed: the batch inputs and the open rows
   // first, S_e last, so that everything except the S_e products runs while
@@ -236,7 +258,7 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : 2) void kda_contract_kernel
   int nr = min(min(MR, kChunk - p), count);
   load_batch<InT, MR>(in, a, h, tok0, nr, tid);
   constexpr int kRowVecs = kRowFloats / 4;
-  float S[16][4];
+  float S[16][CW];
   if constexpr (MR <= 8) {
     // decode and draft blocks: the open rows are issued before S_e and held in registers
     constexpr int kRowIters = ((kChunk - 1) * kRowVecs + kThreads - 1) / kThreads;
@@ -266,8 +288,12 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : 2) void kda_contract_kernel
   } else {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float4 s4 = ld_f4(Sp + (c0 + i) * kD + j0);
-      S[i][0] = s4.x; S[i][1] = s4.y; S[i][2] = s4.z; S[i][3] = s4.w;
+      if constexpr (CW == 4) {
+        const float4 s4 = ld_f4(Sp + (c0 + i) * kD + j0);
+        S[i][0] = s4.x; S[i][1] = s4.y; S[i][2] = s4.z; S[i][3] = s4.w;
+      } else {
+        S[i][0] = Sp[(c0 + i) * kD + j0];
+      }
     }
     for (int e = tid; e < p * kRowVecs; e += kThreads) {
       const int s = e / kRowVecs, f = 4 * (e % kRowVecs);
@@ -378,8 +404,8 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : 2) void kda_contract_kernel
     // in vv (residuals) and sq (outputs), which are free by now.  The channel
     // threads form the close factors.
     const int nr_next = min(MR, count - done - nr);  // after a close the next batch starts a chunk
-    if (tid >= kD) {
-      const int j = tid - kD;
+    if (value_thread) {
+      const int j = jv;
       // all MR rows, also those past nr (unused, never stored as results): no
       // per-row branches in the loop
       float acc[MR], out[MR];
@@ -405,13 +431,15 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : 2) void kda_contract_kernel
         L.vv[i][j] = acc[i];
         L.sq[i][j] = out[i];
       }
-    } else if (closes) {
+    } else if (tid < kD && closes) {
       close_factors(L.rk, L.rb, L.gam, kChunk, tid);
     }
     __builtin_amdgcn_sched_barrier(0);
     // ---- C1: a = S_e^T k_hat and w = S_e^T q_hat for every batch row (wave-local)
     for (int i = 0; i < nr; ++i) {
-      float pa[4] = {0.f, 0.f, 0.f, 0.f}, pw[4] = {0.f, 0.f, 0.f, 0.f};
+      float pa[CW], pw[CW];
+#pragma unroll
+      for (int x = 0; x < CW; ++x) pa[x] = pw[x] = 0.f;
 #pragma unroll
       for (int c4 = 0; c4 < 4; ++c4) {
         const float4 k4 = *reinterpret_cast<const float4*>(&L.kh[i][c0 + 4 * c4]);
@@ -421,7 +449,7 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : 2) void kda_contract_kernel
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
-          for (int x = 0; x < 4; ++x) {
+          for (int x = 0; x < CW; ++x) {
             pa[x] = __builtin_fmaf(S[4 * c4 + cc][x], kv[cc], pa[x]);
             pw[x] = __builtin_fmaf(S[4 * c4 + cc][x], qv[cc], pw[x]);
           }
@@ -430,25 +458,37 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : 2) void kda_contract_kernel
       // (lane bit 5) and splits a / w; level 2 pairs m, m^2 (bit 4) and splits
       // the columns in halves; level 3 pairs m, m^1 (bit 3).
       const bool b3 = lane & 8, b4 = lane & 16, b5 = lane & 32;
+      if constexpr (CW == 4) {
 #pragma unroll
-      for (int x = 0; x < 4; ++x) swap32(pa[x], pw[x]);
-      float l1[4];
+        for (int x = 0; x < 4; ++x) swap32(pa[x], pw[x]);
+        float l1[4];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) l1[x] = pa[x] + pw[x];  // bit 5 = 0: a, 1: w
-      swap16(l1[0], l1[2]);
-      swap16(l1[1], l1[3]);
-      const float l2a = l1[0] + l1[2], l2b = l1[1] + l1[3];  // bit 4 = 0: columns 0, 1; 1: 2, 3
-      const float mine = b3 ? l2b : l2a;
-      const float other = b3 ? l2a : l2b;
-      const float fin = mine + dpp<0x128>(other);
-      const int col = j0 + (b4 ? 2 : 0) + (b3 ? 1 : 0);
-      (b5 ? L.ww : L.aa)[i][col] = fin;
+        for (int x = 0; x < 4; ++x) l1[x] = pa[x] + pw[x];  // bit 5 = 0: a, 1: w
+        swap16(l1[0], l1[2]);
+        swap16(l1[1], l1[3]);
+        const float l2a = l1[0] + l1[2], l2b = l1[1] + l1[3];  // bit 4 = 0: columns 0, 1; 1: 2, 3
+        const float mine = b3 ? l2b : l2a;
+        const float other = b3 ? l2a : l2b;
+        const float fin = mine + dpp<0x128>(other);
+        const int col = j0 + (b4 ? 2 : 0) + (b3 ? 1 : 0);
+        (b5 ? L.ww : L.aa)[i][col] = fin;
+      } else {
+        // one column: the same pairings in the same order (own + partner, or
+        // partner + own, which is the same sum), each level a butterfly
+        swap32(pa[0], pw[0]);
+        float v = pa[0] + pw[0];  // bit 5 = 0: a, 1: w
+        float t = v;
+        swap16(v, t);
+        v = v + t;
+        v = v + dpp<0x128>(v);
+        if (!b3 && !b4) (b5 ? L.ww : L.aa)[i][j0] = v;
+      }
     }
     __syncthreads();
     // ---- D2: the batch rows in order (value threads), each final once the
     // rows before it are in; then the outputs
-    if (tid >= kD) {
-      const int j = tid - kD;
+    if (value_thread) {
+      const int j = jv;
       // Within a step every later row of the pass is updated, also those past
       // nr (their values are unused and never stored), so the update has no
       // per-row branches; a row's arithmetic involves only the rows before it.
@@ -511,15 +551,60 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : 2) void kda_contract_kernel
   if (a.read_only) return;
   if (closed) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) st_f4(Sp + (c0 + i) * kD + j0, make_float4(S[i][0], S[i][1], S[i][2], S[i][3]));
+    for (int i = 0; i < 16; ++i) {
+      if constexpr (CW == 4) st_f4(Sp + (c0 + i) * kD + j0, make_float4(S[i][0], S[i][1], S[i][2], S[i][3]));
+      else Sp[(c0 + i) * kD + j0] = S[i][0];
+    }
   }
   const int first_new = closed ? 0 : p_first;
-  for (int e = tid; e < (p - first_new) * (kRowFloats / 4); e += kThreads) {
-    const int s = first_new + e / (kRowFloats / 4), f = 4 * (e % (kRowFloats / 4));
-    const float* src = (f < kD) ? &L.rk[s][f] : (f < 2 * kD) ? &L.rb[s][f - kD] : &L.ru[s][f - 2 * kD];
-    st_f4(Rp + s * kRowFloats + f, *reinterpret_cast<const float4*>(src));
+  if constexpr (SPLIT) {
+    // this slice's u columns of the new open rows (8 float4 per row); the keys,
+    // decays and position follow in kda_contract_rows_kernel
+    for (int e = tid; e < (p - first_new) * 8; e += kThreads) {
+      const int s = first_new + e / 8, f = 32 * slice + 4 * (e % 8);
+      st_f4(Rp + s * kRowFloats + 2 * kD + f, *reinterpret_cast<const float4*>(&L.ru[s][f]));
+    }
+  } else {
+    for (int e = tid; e < (p - first_new) * (kRowFloats / 4); e += kThreads) {
+      const int s = first_new + e / (kRowFloats / 4), f = 4 * (e % (kRowFloats / 4));
+      const float* src = (f < kD) ? &L.rk[s][f] : (f < 2 * kD) ? &L.rb[s][f - kD] : &L.ru[s][f - 2 * kD];
+      st_f4(Rp + s * kRowFloats + f, *reinterpret_cast<const float4*>(src));
+    }
+    if (tid == 0) a.pos[unit] = p;
   }
-  if (tid == 0) a.pos[unit] = p;
+}
+
+// After a SPLIT prefill: the keys and cumulative decays of the new open rows
+// and the new position of each (sequence, head), formed from the inputs with
+// the prefill's arithmetic (the same additions in the same order: from the
+// last open row's decay, or from 0 at a chunk start).  One thread per key
+// channel.
+template <typename InT>
+__global__ __launch_bounds__(kD) void kda_contract_rows_kernel(ContractArgs a) {
+  const int n = blockIdx.x / a.H;
+  const int h = blockIdx.x % a.H;
+  if (n >= a.num_seqs) return;
+  const int c = threadIdx.x;
+  const int tok0 = a.cu[n];
+  const int count = a.cu[n + 1] - tok0;
+  if (count <= 0) return;
+  const int64_t unit = int64_t(a.slots ? a.slots[n] : n) * a.H + h;
+  float* Rp = a.rows + unit * kChunk * kRowFloats;
+  const int p0 = a.pos[unit] & (kChunk - 1);
+  const int total = p0 + count;
+  const int pf = total & (kChunk - 1);
+  const bool closed = total >= kChunk;
+  const int first = closed ? 0 : p0;  // rows first .. pf-1 are new
+  float b = (!closed && p0 > 0) ? Rp[(p0 - 1) * kRowFloats + kD + c] : 0.0f;
+  const int t_first = tok0 + count - (pf - first);  // token of row `first`
+  for (int s = first; s < pf; ++s) {
+    const int64_t tok = int64_t(t_first + s - first) * a.H + h;
+    b = b + a.g[tok * kD + c];
+    Rp[s * kRowFloats + c] = InT::unpack1(InT::load1raw(a.k, tok * kD + c));
+    Rp[s * kRowFloats + kD + c] = b;
+  }
+  __syncthreads();  // every thread has read the position
+  if (c == 0) a.pos[unit] = pf;
 }
 
 // Commit from a verify's stash: the first L = accepted[n] (clamped to 0 .. gamma, gamma <= 16)
@@ -623,6 +708,17 @@ __global__ __launch_bounds__(kThreads) void kda_contract_state_kernel(const floa
 template <typename InT, int MR, bool STASH = false>
 hipError_t launch_as(const ContractArgs& a, hipStream_t stream) {
   const unsigned blocks = unsigned(a.num_seqs) * unsigned(a.H);
+  // a prefill with at most one workgroup per 4 CUs splits each (sequence, head) four ways
+  // (the split build is sized for one workgroup per CU)
+  if constexpr (MR == kChunk && !STASH) {
+    if (a.cu != nullptr && !a.read_only && 4 * blocks <= unsigned(device_cu_count())) {
+      hipLaunchKernelGGL((kda_contract_kernel<InT, MR, false, true>), dim3(4 * blocks), dim3(kThreads), 0, stream, a);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((kda_contract_rows_kernel<InT>), dim3(blocks), dim3(kD), 0, stream, a);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((kda_contract_kernel<InT, MR, STASH>), dim3(blocks), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }

@@ -484,3 +484,29 @@ def test_draft_blocks_of_every_length(G):
     torch.cuda.synchronize()
     _assert_same_state(pools, ref)
     _assert_same_state(pools, steps)
+
+
+def test_split_and_unsplit_prefill_are_bit_identical():
+    """A prefill grid of at most 64 (sequence, head) units splits each unit's value columns over four
+    workgroups (and writes the shared keys, decays and position in a second launch); a larger grid
+    does not.  72 sequences in one call (unsplit) and the same sequences in two calls of 36 (split)
+    give the same outputs, entry states, open rows and positions, bit for bit."""
+    rng = np.random.default_rng(70)
+    lens = [int(x) for x in rng.integers(0, 41, 72)]
+    lens[5], lens[40] = 16, 32  # ends exactly at a chunk close
+    p = gen.packed_batch(seed=70, seqlens=lens, H=1, dtype="bf16", init_state=True)
+    whole = _pools(p)
+    o_whole = _prefill(_slice(p, [(0, L) for L in lens]), whole)
+    parted = _pools(p)
+    outs = []
+    for seqs in (range(0, 36), range(36, 72)):  # 36 units each: split; pools rows through slots
+        idx = np.concatenate([np.arange(p.cu_seqlens[n], p.cu_seqlens[n + 1]) for n in seqs]).astype(np.int64)
+        cu = np.concatenate([[0], np.cumsum([lens[n] for n in seqs])]).astype(np.int32)
+        pick = lambda x: np.ascontiguousarray(x[idx])
+        d = dict(q=to_dev(pick(p.q), p.dtype), k=to_dev(pick(p.k), p.dtype), v=to_dev(pick(p.v), p.dtype),
+                 g=to_dev(pick(p.g)), beta=to_dev(pick(p.beta)), cu_seqlens=to_dev(cu),
+                 cu_seqlens_host=torch.from_numpy(cu.copy()))
+        slots = torch.tensor(list(seqs), dtype=torch.int32, device=DEV)
+        outs.append(_prefill(d, parted, slots=slots))
+    assert torch.equal(_bits(o_whole), _bits(torch.cat(outs)))
+    _assert_same_state(whole, parted)
