@@ -35,8 +35,8 @@
 // 32w .. 32w+31 of S_e in registers: lane (m = lane >> 3, jq = lane & 7) holds
 // key rows 16m .. 16m+15 of columns 32w + 4jq .. +3, so the 8 channel groups of
 // every S_e^T x product meet inside the wave (lane bits 5, 4, 3, in that order).
-// A prefill of few (sequence, head) units splits each over four workgroups of
-// 32 columns (lane: one column, same channel groups and tree; see SPLIT).
+// A prefill of few (sequence, head) units splits each over two or four
+// workgroups (lane: two or one columns, same channel groups and tree; see SPLITW).
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
@@ -129,6 +129,7 @@ __device__ __forceinline__ void close_block(float (&S)[16][CW], const float (*rk
   // row s's operands are read while row s - 1's products are formed
   auto ld_u = [&](int s) {
     if constexpr (CW == 4) return *reinterpret_cast<const float4*>(&ru[s][j0]);
+    else if constexpr (CW == 2) return make_float4(ru[s][j0], ru[s][j0 + 1], 0.f, 0.f);
     else return make_float4(ru[s][j0], 0.f, 0.f, 0.f);
   };
   float4 un = ld_u(0);
@@ -207,19 +208,22 @@ __device__ __forceinline__ void load_batch(BatchIn<InT, MR>& in, const ContractA
   }
 }
 
-// SPLIT (prefill of small grids): four workgroups per (sequence, head), one per
-// 32 value columns; a lane holds one column of its 16 key rows (CW = 1 instead
-// of 4), so the S_e products and the close cost a quarter per lane, with the
-// same chains and the same tree.  The Gram entries, the decay and the
+// SPLITW > 1 (prefill of small grids): SPLITW workgroups per (sequence, head),
+// one per 128 / SPLITW value columns; a lane holds CW = 4 / SPLITW columns of
+// its 16 key rows instead of 4, so the S_e products and the close cost CW / 4
+// per lane, with the same chains and the same tree.  The Gram entries, the decay and the
 // substitution are formed in each workgroup alike.  The workgroups write only
 // what they own (S_e columns, the u columns of the open rows, outputs); the
 // shared keys, decays and position are written by kda_contract_rows_kernel,
 // launched after, so that no write can overtake a sibling's read.
-template <typename InT, int MR, bool STASH, bool SPLIT = false>
-__global__ __launch_bounds__(kThreads, MR == 1 ? 3 : (SPLIT ? 1 : 2)) void kda_contract_kernel(ContractArgs a) {
-  static_assert(!SPLIT || (MR == kChunk && !STASH), "the split serves the prefill");
-  constexpr int CW = SPLIT ? 1 : 4;      // value columns per lane
-  constexpr int kSlices = SPLIT ? 4 : 1;  // workgroups per (sequence, head)
+template <typename InT, int MR, bool STASH, int SPLITW = 1>
+__global__ __launch_bounds__(kThreads, MR == 1 ? 3 : (SPLITW > 1 ? 1 : 2)) void kda_contract_kernel(ContractArgs a) {
+  static_assert(SPLITW == 1 || (MR == kChunk && !STASH), "the split serves the prefill");
+  static_assert(SPLITW == 1 || SPLITW == 2 || SPLITW == 4, "split in 2 or 4");
+  constexpr bool SPLIT = SPLITW > 1;
+  constexpr int CW = 4 / SPLITW;          // value columns per lane
+  constexpr int kSlices = SPLITW;         // workgroups per (sequence, head)
+  constexpr int kSliceCols = kD / SPLITW;  // value columns per workgroup
   __shared__ __align__(16) Lds<MR> L;
   const int slice = blockIdx.x % kSlices;
   const int n = (blockIdx.x / kSlices) / a.H;
@@ -228,9 +232,9 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : (SPLIT ? 1 : 2)) void kda_c
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  // value threads: tid >= kD; with SPLIT the first 32 of them, for this slice's columns
-  const bool value_thread = tid >= kD && (!SPLIT || tid - kD < 32);
-  const int jv = SPLIT ? 32 * slice + (tid - kD) : tid - kD;  // value column of a value thread
+  // value threads: tid >= kD; with a split the first kSliceCols of them, for this slice's columns
+  const bool value_thread = tid >= kD && tid - kD < kSliceCols;
+  const int jv = kSliceCols * slice + (tid - kD);  // value column of a value thread
 
   int tok0, count;
   if (a.cu != nullptr) {
@@ -249,7 +253,7 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : (SPLIT ? 1 : 2)) void kda_c
   int p = a.pos[unit] & (kChunk - 1);
   const int p_first = p;
   const int c0 = 16 * (lane >> 3);
-  const int j0 = SPLIT ? 32 * slice + 8 * wave + (lane & 7) : 32 * wave + 4 * (lane & 7);
+  const int j0 = kSliceCols * slice + (kSliceCols / 4) * wave + CW * (lane & 7);
 
   // Loads in the order they are needed: the batch inputs and the open rows
   // first, S_e last, so that everything except the S_e products runs while
@@ -292,7 +296,8 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : (SPLIT ? 1 : 2)) void kda_c
         const float4 s4 = ld_f4(Sp + (c0 + i) * kD + j0);
         S[i][0] = s4.x; S[i][1] = s4.y; S[i][2] = s4.z; S[i][3] = s4.w;
       } else {
-        S[i][0] = Sp[(c0 + i) * kD + j0];
+#pragma unroll
+        for (int x = 0; x < CW; ++x) S[i][x] = Sp[(c0 + i) * kD + j0 + x];
       }
     }
     for (int e = tid; e < p * kRowVecs; e += kThreads) {
@@ -472,6 +477,16 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : (SPLIT ? 1 : 2)) void kda_c
         const float fin = mine + dpp<0x128>(other);
         const int col = j0 + (b4 ? 2 : 0) + (b3 ? 1 : 0);
         (b5 ? L.ww : L.aa)[i][col] = fin;
+      } else if constexpr (CW == 2) {
+        // two columns: level 2 splits them (bit 4 = 0: column 0, 1: column 1),
+        // level 3 is a butterfly; the same pairings in the same order
+        swap32(pa[0], pw[0]);
+        swap32(pa[1], pw[1]);
+        float l1[2] = {pa[0] + pw[0], pa[1] + pw[1]};  // bit 5 = 0: a, 1: w
+        swap16(l1[0], l1[1]);
+        float v = l1[0] + l1[1];
+        v = v + dpp<0x128>(v);
+        if (!b3) (b5 ? L.ww : L.aa)[i][j0 + (b4 ? 1 : 0)] = v;
       } else {
         // one column: the same pairings in the same order (own + partner, or
         // partner + own, which is the same sum), each level a butterfly
@@ -552,16 +567,21 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : (SPLIT ? 1 : 2)) void kda_c
   if (closed) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      if constexpr (CW == 4) st_f4(Sp + (c0 + i) * kD + j0, make_float4(S[i][0], S[i][1], S[i][2], S[i][3]));
-      else Sp[(c0 + i) * kD + j0] = S[i][0];
+      if constexpr (CW == 4) {
+        st_f4(Sp + (c0 + i) * kD + j0, make_float4(S[i][0], S[i][1], S[i][2], S[i][3]));
+      } else {
+#pragma unroll
+        for (int x = 0; x < CW; ++x) Sp[(c0 + i) * kD + j0 + x] = S[i][x];
+      }
     }
   }
   const int first_new = closed ? 0 : p_first;
   if constexpr (SPLIT) {
-    // this slice's u columns of the new open rows (8 float4 per row); the keys,
-    // decays and position follow in kda_contract_rows_kernel
-    for (int e = tid; e < (p - first_new) * 8; e += kThreads) {
-      const int s = first_new + e / 8, f = 32 * slice + 4 * (e % 8);
+    // this slice's u columns of the new open rows; the keys, decays and
+    // position follow in kda_contract_rows_kernel
+    constexpr int kVecs = kSliceCols / 4;
+    for (int e = tid; e < (p - first_new) * kVecs; e += kThreads) {
+      const int s = first_new + e / kVecs, f = kSliceCols * slice + 4 * (e % kVecs);
       st_f4(Rp + s * kRowFloats + 2 * kD + f, *reinterpret_cast<const float4*>(&L.ru[s][f]));
     }
   } else {
@@ -574,7 +594,7 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : (SPLIT ? 1 : 2)) void kda_c
   }
 }
 
-// After a SPLIT prefill: the keys and cumulative decays of the new open rows
+// After a split prefill: the keys and cumulative decays of the new open rows
 // and the new position of each (sequence, head), formed from the inputs with
 // the prefill's arithmetic (the same additions in the same order: from the
 // last open row's decay, or from 0 at a chunk start).  One thread per key
@@ -708,11 +728,15 @@ __global__ __launch_bounds__(kThreads) void kda_contract_state_kernel(const floa
 template <typename InT, int MR, bool STASH = false>
 hipError_t launch_as(const ContractArgs& a, hipStream_t stream) {
   const unsigned blocks = unsigned(a.num_seqs) * unsigned(a.H);
-  // a prefill with at most one workgroup per 4 CUs splits each (sequence, head) four ways
-  // (the split build is sized for one workgroup per CU)
+  // a prefill with at most one workgroup per 4 (2) CUs splits each (sequence, head)
+  // four (two) ways; the split builds are sized for one workgroup per CU
   if constexpr (MR == kChunk && !STASH) {
-    if (a.cu != nullptr && !a.read_only && 4 * blocks <= unsigned(device_cu_count())) {
-      hipLaunchKernelGGL((kda_contract_kernel<InT, MR, false, true>), dim3(4 * blocks), dim3(kThreads), 0, stream, a);
+    const unsigned cus = unsigned(device_cu_count());
+    if (a.cu != nullptr && !a.read_only && 2 * blocks <= cus) {
+      if (4 * blocks <= cus)
+        hipLaunchKernelGGL((kda_contract_kernel<InT, MR, false, 4>), dim3(4 * blocks), dim3(kThreads), 0, stream, a);
+      else
+        hipLaunchKernelGGL((kda_contract_kernel<InT, MR, false, 2>), dim3(2 * blocks), dim3(kThreads), 0, stream, a);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL((kda_contract_rows_kernel<InT>), dim3(blocks), dim3(kD), 0, stream, a);

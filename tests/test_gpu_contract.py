@@ -486,20 +486,23 @@ def test_draft_blocks_of_every_length(G):
     _assert_same_state(pools, steps)
 
 
-def test_split_and_unsplit_prefill_are_bit_identical():
-    """A prefill grid of at most 64 (sequence, head) units splits each unit's value columns over four
-    workgroups (and writes the shared keys, decays and position in a second launch); a larger grid
-    does not.  72 sequences in one call (unsplit) and the same sequences in two calls of 36 (split)
-    give the same outputs, entry states, open rows and positions, bit for bit."""
-    rng = np.random.default_rng(70)
-    lens = [int(x) for x in rng.integers(0, 41, 72)]
+@pytest.mark.parametrize("total", [72, 144])
+def test_split_and_unsplit_prefill_are_bit_identical(total):
+    """A prefill grid of at most 64 (128) (sequence, head) units splits each unit's value columns over
+    four (two) workgroups and writes the shared keys, decays and position in a second launch; a grid
+    of more than 128 units does not split.  `total` sequences in one call and the same sequences in
+    two calls of total / 2 (72: unsplit vs four-way; 144: unsplit vs two-way) give the same outputs,
+    entry states, open rows and positions, bit for bit."""
+    rng = np.random.default_rng(70 + total)
+    lens = [int(x) for x in rng.integers(0, 41, total)]
     lens[5], lens[40] = 16, 32  # ends exactly at a chunk close
-    p = gen.packed_batch(seed=70, seqlens=lens, H=1, dtype="bf16", init_state=True)
+    p = gen.packed_batch(seed=70 + total, seqlens=lens, H=1, dtype="bf16", init_state=True)
     whole = _pools(p)
     o_whole = _prefill(_slice(p, [(0, L) for L in lens]), whole)
     parted = _pools(p)
     outs = []
-    for seqs in (range(0, 36), range(36, 72)):  # 36 units each: split; pools rows through slots
+    half = total // 2
+    for seqs in (range(0, half), range(half, total)):  # split calls; pool rows through slots
         idx = np.concatenate([np.arange(p.cu_seqlens[n], p.cu_seqlens[n + 1]) for n in seqs]).astype(np.int64)
         cu = np.concatenate([[0], np.cumsum([lens[n] for n in seqs])]).astype(np.int32)
         pick = lambda x: np.ascontiguousarray(x[idx])
