@@ -10,16 +10,18 @@ bytes come from HBM.  ``ms_per_step`` is the mean step time.
 
 The other rows of the hot path are timed in the same run and reported under
 ``rows``: chunked prefill of 4096 tokens x 12 heads (bf16), draft-block verify
-plus replay commit for 32 requests x 12 heads x 8 tokens, and (with --long)
-the 1,048,576-token + 8 ragged-sequence long-context prefill through segment
-composition.
+plus replay commit for 32 requests x 12 heads x 8 tokens, and (unless
+--no-long) the 1,048,576-token + 8 ragged-sequence long-context prefill
+through segment composition.  Decode and verify also report the median over
+11 replays of a graph of >= 100 launches, and a plain copy of the decode's
+footprint gives the measured memory roof beside the 8 TB/s one.
 
 ``roofline`` is for the decode kernel (algorithmic bytes per launch / mean
 launch time vs 8 TB/s).  ``cpu_baseline`` is the CPU oracle (fp64, token by
 token) timed on this host's cores on a bounded sample of the same decode
-workload.
+workload; ``rows.cpu_oracle_prefill`` times it on the three prefill workloads.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--long] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-long] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -133,6 +135,40 @@ def graph_time_ms(fns, warmup):
     return start.elapsed_time(end) / len(fns)
 
 
+def graph_replay_stats_ms(fns, warmup, replays=11):
+    """Capture fns (>= 100 launches) into one HIP graph and time `replays` replays of it with events
+    on the graph's stream: returns (median, min, max) of the per-launch mean of each replay."""
+    import statistics
+    import torch
+    for _ in range(warmup):
+        for f in fns[: min(len(fns), 8)]:
+            f()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for f in fns[: min(len(fns), 8)]:
+            f()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    g.replay()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(replays):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        g.replay()
+        end.record()
+        end.synchronize()
+        per.append(start.elapsed_time(end) / len(fns))
+    return statistics.median(per), min(per), max(per)
+
+
 def bench_decode(steps, warmup, n_sets=8, prologue=False):
     """The decode step (64 x 12, bf16); ``prologue``: raw inputs through kda_decode_step_prologue
     (same algorithmic bytes: q, k, g are read and o written once either way)."""
@@ -154,7 +190,30 @@ def bench_decode(steps, warmup, n_sets=8, prologue=False):
                                                    prologue=pro))
     ms = graph_time_ms(fns, warmup)
     nbytes = N * H * decode_bytes_per_head(2)
-    return dict(ms=ms, bytes=nbytes, gbps=nbytes / (ms * 1e-3) / 1e9, N=N, H=H, n_sets=n_sets)
+    out = dict(ms=ms, bytes=nbytes, gbps=nbytes / (ms * 1e-3) / 1e9, N=N, H=H, n_sets=n_sets)
+    if not prologue and not EAGER:
+        fns100 = [(lambda s=sets[i % n_sets]: kda.kda_decode_step(s["q"], s["k"], s["v"], s["g"], s["beta"],
+                                                                  s["state"], o=s["o"]))
+                  for i in range(max(100, len(fns)))]
+        med, lo, hi = graph_replay_stats_ms(fns100, warmup)
+        out.update(median_ms=med, median_gbps=nbytes / (med * 1e-3) / 1e9,
+                   median_protocol=f"median over 11 replays of a graph of {len(fns100)} launches "
+                                   f"(per-replay means {lo * 1e3:.2f}-{hi * 1e3:.2f} us)")
+    return out
+
+
+def bench_copy_probe(steps, warmup, n_sets=8):
+    """The decode's memory roof measured: a plain device copy of the same footprint (48 MiB read and
+    48 MiB written per launch, the size of the 64 x 12 state), rotating the same number of buffer
+    pairs, timed the same way."""
+    import torch
+    n = 64 * 12 * D * D
+    pairs = [(torch.ones(n, device="cuda:0"), torch.empty(n, device="cuda:0")) for _ in range(n_sets)]
+    fns = [lambda p=pairs[i % n_sets]: p[1].copy_(p[0]) for i in range(max(100, steps))]
+    med, lo, hi = graph_replay_stats_ms(fns, warmup)
+    nbytes = 2 * n * 4
+    return dict(ms=med, bytes=nbytes, gbps=nbytes / (med * 1e-3) / 1e9, n_sets=n_sets,
+                kernel="torch copy_ of an fp32 buffer (elementwise copy kernel)")
 
 
 def bench_verify(reps, warmup, n_sets=8, prologue=False):
@@ -180,8 +239,17 @@ def bench_verify(reps, warmup, n_sets=8, prologue=False):
     per_token_commit = 2 * D + 2 * D + 4 * D + 4
     acc = b.accepted_len.astype(np.int64)
     nbytes = H * (N * per_head_verify + N * 2 * STATE_BYTES + int(acc.sum()) * per_token_commit)
-    return dict(ms=ms, bytes=nbytes, gbps=nbytes / (ms * 1e-3) / 1e9, N=N, G=G, H=H,
-                mean_accepted=float(acc.mean()))
+    out = dict(ms=ms, bytes=nbytes, gbps=nbytes / (ms * 1e-3) / 1e9, frac_hbm_peak=nbytes / (ms * 1e-3) / 1e9 /
+               HBM_PEAK_GBPS, N=N, G=G, H=H, mean_accepted=float(acc.mean()))
+    if not prologue and not EAGER:
+        fns100 = [(lambda s=sets[i % n_sets]: kda.kda_verify_block(s["q"], s["k"], s["v"], s["g"], s["beta"],
+                                                                   s["state"], o=s["o"], accepted_len=s["acc"]))
+                  for i in range(max(100, reps))]
+        med, lo, hi = graph_replay_stats_ms(fns100, warmup)
+        out.update(median_ms=med, median_gbps=nbytes / (med * 1e-3) / 1e9,
+                   median_protocol=f"median over 11 replays of a graph of {len(fns100)} launches "
+                                   f"(per-replay means {lo * 1e3:.2f}-{hi * 1e3:.2f} us)")
+    return out
 
 
 def _event_time_ms(run, reps, warmup):
@@ -423,9 +491,66 @@ def _oracle_decode_worker(args):
     return time.perf_counter() - t0
 
 
+def _oracle_slice_worker(args):
+    """Replay tokens [lo, hi) of one (sequence, head) slice of a seeded workload through the oracle's
+    token recurrence (from the slice's initial state when it has one); returns the oracle's compute
+    time (input generation excluded) and the token count."""
+    import numpy as np
+    from gated_delta_rule_15_amd import inputs as gen
+    from oracle import kda_oracle as orc
+    seed, s, h, lo, hi, seq_len, dtype, with_state = args
+    S = gen.draw_state(seed, s, h, D, D).astype(np.float64) if with_state else None
+    spent = 0.0
+    for b0 in range(lo - lo % gen.BLOCK, hi, gen.BLOCK):
+        n = min(gen.BLOCK, seq_len - b0)  # the block's own length: its stream depends on it
+        q, k, v, beta, g = gen._draw_block(seed, s, h, b0 // gen.BLOCK, n, D, D)
+        a, b = max(lo, b0) - b0, min(hi, b0 + gen.BLOCK) - b0
+        q64, k64, v64 = (gen.as_f64(gen._cast(x[a:b], dtype), dtype) for x in (q, k, v))
+        g64, beta64 = g[a:b].astype(np.float64), beta[a:b].astype(np.float64)
+        t0 = time.perf_counter()
+        _, S = orc.recurrence(q64, k64, v64, g64, beta64, S)
+        spent += time.perf_counter() - t0
+    return spent, hi - lo
+
+
+def cpu_oracle_prefill_rows(cores):
+    """The oracle's prefill on host cores for the three prefill workloads: the tiny fp32 prefill (whole,
+    one core), the 4096 x 12 prefill (whole, one worker per head; and its 1-core figure, extrapolated
+    from one head), and the long-context workload (a sample of 16 blocks of 4096 tokens spread over the
+    long sequence and the extras, extrapolated to all 1,134,121 tokens x 12 heads)."""
+    from gated_delta_rule_15_amd import inputs as gen
+    rows = {}
+    t, n = _oracle_slice_worker((1, 0, 0, 0, 256, 256, "f32", False))
+    rows["tiny_prefill_f32"] = dict(tokens_per_s=n / t, cores=1, kind="oracle", sample="whole workload, 256 tokens x 1 head")
+    res = gen.pool_map(_oracle_slice_worker, [(3, 0, h, 0, 4096, 4096, "bf16", False) for h in range(12)], min(cores, 12))
+    one = sum(r[0] for r in res)   # the same work on one core
+    # heads run in parallel: the slowest head's compute time when every head has a core of its own
+    wall = max(r[0] for r in res) if cores >= 12 else one / cores
+    rows["prefill_4096x12_bf16"] = dict(tokens_per_s=4096 / wall, cores=min(cores, 12), kind="oracle",
+                                        tokens_per_s_1core=4096 / one,
+                                        sample="whole workload, one worker per head; 1-core figure = sum of the "
+                                               "12 heads' compute times")
+    lens = gen.long_context_layout(5)
+    T = sum(lens)
+    tasks = []
+    for i in range(16):  # 12 blocks over the long sequence, 4 over the extras, heads round-robin
+        s = 0 if i < 12 else 1 + 2 * (i - 12)
+        start = (i * 87_381) // gen.BLOCK * gen.BLOCK if s == 0 else 0
+        tasks.append((5, s, i % 12, start, min(start + gen.BLOCK, lens[s]), lens[s], "bf16", s > 0))
+    res = gen.pool_map(_oracle_slice_worker, tasks, min(cores, 16))
+    th_per_s_core = sum(r[1] for r in res) / sum(r[0] for r in res)  # token-heads per second per core
+    rows["long_context_1m_plus_8"] = dict(
+        tokens_per_s=th_per_s_core * cores / 12, cores=cores, kind="oracle",
+        tokens_per_s_1core=th_per_s_core / 12, projected_total_s=T * 12 / (th_per_s_core * cores),
+        sample=f"extrapolated: 16 blocks of <= 4096 tokens (12 over the 1,048,576-token sequence, 4 over the "
+               f"extras) at {th_per_s_core:.0f} token-heads/s per core, scaled to {cores} cores (108 independent "
+               f"(sequence, head) units) and {T} tokens x 12 heads")
+    return rows
+
+
 def cpu_baseline(target_s=12.0):
     """The oracle's decode step on host cores: all 64 requests x 12 heads, split over workers."""
-    import multiprocessing as mp
+    from gated_delta_rule_15_amd import inputs as gen
     cores = len(os.sched_getaffinity(0))
     cores = max(1, min(cores, 16))
     # one round of all 64 requests on one core takes t1; a worker holds 64 / cores requests,
@@ -433,9 +558,7 @@ def cpu_baseline(target_s=12.0):
     t1 = _oracle_decode_worker((2, 0, 64, 1))
     rounds = max(1, int(round(target_s * cores / max(t1, 1e-3))))
     chunks = [(2, 64 * i // cores, 64 * (i + 1) // cores, rounds) for i in range(cores)]
-    ctx = mp.get_context("spawn")
-    with ctx.Pool(cores) as pool:
-        times = pool.map(_oracle_decode_worker, chunks)
+    times = gen.pool_map(_oracle_decode_worker, chunks, cores)
     wall = max(times)  # the slowest worker's compute time (pool start-up excluded)
     nbytes = rounds * 64 * 12 * decode_bytes_per_head(2)
     return dict(value=nbytes / wall / 1e9, unit="GB/s", cores=cores, kind="oracle",
@@ -521,7 +644,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--long", action="store_true", help="also time the 1M-token long-context prefill")
+    ap.add_argument("--long", action="store_true", help="(default) time the 1M-token long-context prefill")
+    ap.add_argument("--no-long", action="store_true", help="skip the 1M-token long-context prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-decode", action="store_true", help="time only the decode rows (for profiling)")
     ap.add_argument("--only-prefill", action="store_true",
@@ -594,7 +718,7 @@ def main():
             f"{ct['contract_prefill_4096x12_bf16']['ms']:.3f} ms, 32 x 4096 x 12 "
             f"{ct['contract_prefill_32x4096x12_bf16']['ms']:.3f} ms")
         rows.update(ct)
-        if args.long:
+        if not args.no_long:
             log("long context: 1,048,576 + 8 ragged sequences x 12 heads ...")
             lc = bench_long(reps=2, gen_workers=args.gen_workers)
             log(f"long context: {lc['ms']:.2f} ms, {lc['tokens_per_s'] / 1e6:.1f} M tokens/s")
@@ -602,15 +726,26 @@ def main():
 
     khash = src_hash("kda_step.hip", "kda_common.hpp")
     traffic = traffic_from_profile(khash)
+    copy = None
+    if not EAGER:
+        copy = bench_copy_probe(args.steps, args.warmup)
+        log(f"copy probe (same footprint): {copy['ms'] * 1e3:.2f} us, {copy['gbps']:.0f} GB/s")
     roof = dict(bound="hbm", achieved=round(dec["gbps"], 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                 frac=round(dec["gbps"] / HBM_PEAK_GBPS, 4), traffic=traffic,
                 kernel="kda_decode_kernel<BF16, false>", algorithmic_bytes_per_launch=dec["bytes"],
-                mean_launch_us=round(dec["ms"] * 1e3, 3))
+                mean_launch_us=round(dec["ms"] * 1e3, 3),
+                median_launch_us=round(dec["median_ms"] * 1e3, 3) if "median_ms" in dec else None,
+                measured_copy_gbps=round(copy["gbps"], 1) if copy else None,
+                frac_of_measured_copy=round(dec["gbps"] / copy["gbps"], 4) if copy else None)
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         cpu = cpu_baseline()
         log(f"cpu baseline: {cpu['value']:.4f} GB/s on {cpu['cores']} cores")
+        if not args.only_decode:
+            rows["cpu_oracle_prefill"] = cpu_oracle_prefill_rows(cpu["cores"])
+            log("cpu oracle prefill: " + ", ".join(f"{k} {v['tokens_per_s']:.0f} tokens/s"
+                                                   for k, v in rows["cpu_oracle_prefill"].items()))
 
     line = {
         "metric": "KDA prefill tokens/s and decode state-update HBM GB/s (12 heads, 1 GPU)",

@@ -38,6 +38,8 @@ SIGNATURES = {
     "kda_compose_segments": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "kda_contract_prefill": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _F, _P, _P,
                                             _P, _P, _P, _P]),
+    "kda_contract_prefill_split": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _F, _P,
+                                                  _P, _P, _P, _P, _I, _P]),
     "kda_contract_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _F, _P, _P, _P, _P,
                                            _P, _P]),
     "kda_contract_state": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),

@@ -251,6 +251,16 @@ kda_status_t kda_contract_prefill(const void* q, const void* k, const void* v, c
                                   int32_t num_seqs, int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t dtype,
                                   float scale, float* S_pool, float* rows_pool, int32_t* pos_pool,
                                   const int32_t* slots, void* o, void* stream) {
+  return kda_contract_prefill_split(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, num_seqs, H, d_k, d_v, dtype,
+                                    scale, S_pool, rows_pool, pos_pool, slots, o, 0, stream);
+}
+
+kda_status_t kda_contract_prefill_split(const void* q, const void* k, const void* v, const float* g,
+                                        const float* beta, const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                                        int32_t num_seqs, int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t dtype,
+                                        float scale, float* S_pool, float* rows_pool, int32_t* pos_pool,
+                                        const int32_t* slots, void* o, int32_t split_width, void* stream) {
+  if (split_width != 0 && split_width != 1 && split_width != 2 && split_width != 4) return KDA_ERR_INVALID_ARG;
   if (num_seqs < 0 || H <= 0) return KDA_ERR_INVALID_ARG;
   if (!dims_ok(d_k, d_v) || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return KDA_OK;
@@ -264,6 +274,7 @@ kda_status_t kda_contract_prefill(const void* q, const void* k, const void* v, c
   if (!any_tokens) return KDA_OK;
   if (!q || !k || !v || !g || !beta) return KDA_ERR_INVALID_ARG;
   kda::ContractLaunch c{q, k, v, g, beta, cu_seqlens, slots, S_pool, rows_pool, pos_pool, o, num_seqs, H, scale};
+  c.split = split_width;
   return hip_status(kda::launch_contract(c, dtype == KDA_BF16, static_cast<hipStream_t>(stream)));
 }
 

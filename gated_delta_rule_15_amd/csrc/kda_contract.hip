@@ -726,14 +726,16 @@ __global__ __launch_bounds__(kThreads) void kda_contract_state_kernel(const floa
 }
 
 template <typename InT, int MR, bool STASH = false>
-hipError_t launch_as(const ContractArgs& a, hipStream_t stream) {
+hipError_t launch_as(const ContractArgs& a, hipStream_t stream, int split) {
   const unsigned blocks = unsigned(a.num_seqs) * unsigned(a.H);
   // a prefill with at most one workgroup per 4 (2) CUs splits each (sequence, head)
-  // four (two) ways; the split builds are sized for one workgroup per CU
+  // four (two) ways (unless the caller fixed the width); the split builds are
+  // sized for one workgroup per CU
   if constexpr (MR == kChunk && !STASH) {
     const unsigned cus = unsigned(device_cu_count());
-    if (a.cu != nullptr && !a.read_only && 2 * blocks <= cus) {
-      if (4 * blocks <= cus)
+    if (split == 0) split = 4 * blocks <= cus ? 4 : (2 * blocks <= cus ? 2 : 1);
+    if (a.cu != nullptr && !a.read_only && split > 1) {
+      if (split == 4)
         hipLaunchKernelGGL((kda_contract_kernel<InT, MR, false, 4>), dim3(4 * blocks), dim3(kThreads), 0, stream, a);
       else
         hipLaunchKernelGGL((kda_contract_kernel<InT, MR, false, 2>), dim3(2 * blocks), dim3(kThreads), 0, stream, a);
@@ -756,14 +758,15 @@ hipError_t launch_contract(const ContractLaunch& c, bool bf16, hipStream_t strea
   // Rows per pass: 1 for decode, 8 for draft blocks of up to 8 tokens, 16
   // otherwise (a row's arithmetic does not depend on it, only registers do).
   const bool block8 = c.cu_seqlens == nullptr && c.gamma <= 8;
+  const int sp = c.split;
   if (c.stash != nullptr) {
-    if (block8) return bf16 ? launch_as<BF16, 8, true>(a, stream) : launch_as<F32, 8, true>(a, stream);
-    return bf16 ? launch_as<BF16, kChunk, true>(a, stream) : launch_as<F32, kChunk, true>(a, stream);
+    if (block8) return bf16 ? launch_as<BF16, 8, true>(a, stream, 1) : launch_as<F32, 8, true>(a, stream, 1);
+    return bf16 ? launch_as<BF16, kChunk, true>(a, stream, 1) : launch_as<F32, kChunk, true>(a, stream, 1);
   }
   if (c.cu_seqlens == nullptr && c.gamma == 1)
-    return bf16 ? launch_as<BF16, 1>(a, stream) : launch_as<F32, 1>(a, stream);
-  if (block8) return bf16 ? launch_as<BF16, 8>(a, stream) : launch_as<F32, 8>(a, stream);
-  return bf16 ? launch_as<BF16, kChunk>(a, stream) : launch_as<F32, kChunk>(a, stream);
+    return bf16 ? launch_as<BF16, 1>(a, stream, 1) : launch_as<F32, 1>(a, stream, 1);
+  if (block8) return bf16 ? launch_as<BF16, 8>(a, stream, 1) : launch_as<F32, 8>(a, stream, 1);
+  return bf16 ? launch_as<BF16, kChunk>(a, stream, sp) : launch_as<F32, kChunk>(a, stream, sp);
 }
 
 hipError_t launch_contract_commit_stash(const float* stash, const int32_t* accepted, const int32_t* slots,

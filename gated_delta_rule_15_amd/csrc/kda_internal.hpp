@@ -81,6 +81,7 @@ struct ContractLaunch {
   const int32_t* counts = nullptr;  // with cu_seqlens null: device [num_seqs] tokens to apply (0..gamma)
   bool read_only = false;           // outputs only; the pools are not written (verify)
   float* stash = nullptr;           // verify: [num_seqs, H, gamma * 3 * 128 + 128 * 128] rows and closed state
+  int32_t split = 0;                // prefill: workgroups per (sequence, head), 1, 2 or 4; 0 picks by grid size
 };
 
 hipError_t launch_contract(const ContractLaunch& c, bool bf16, hipStream_t stream);

@@ -318,11 +318,30 @@ class SharedPacked(Packed):
         return int(self.q.shape[1]) if self.q is not None else self._H
 
 
+def pool_map(fn, args, workers: int, chunksize: int = 1) -> list:
+    """map() over a pool of spawned worker processes that are let exit on their own.
+
+    The pool is closed and joined rather than terminated (a context-managed pool
+    sends its idle workers SIGTERM, which a profiler's preloaded signal handler
+    turns into aborts); it is terminated only when the map itself fails.
+    """
+    import multiprocessing as mp
+    pool = mp.get_context("spawn").Pool(workers)
+    try:
+        out = pool.map(fn, args, chunksize=chunksize)
+        pool.close()
+    except BaseException:
+        pool.terminate()
+        raise
+    finally:
+        pool.join()
+    return out
+
+
 def packed_batch_parallel(seed: int, seqlens: Sequence[int], H: int, dk: int = 128, dv: int = 128,
                           dtype: str = "bf16", init_state: Sequence[bool] | bool = False,
                           workers: int = 8) -> SharedPacked:
     """Same arrays as ``packed_batch`` (identical per-block streams), drawn by a process pool."""
-    import multiprocessing as mp
     from multiprocessing import shared_memory
     seqlens = [int(s) for s in seqlens]
     N = len(seqlens)
@@ -343,8 +362,7 @@ def packed_batch_parallel(seed: int, seqlens: Sequence[int], H: int, dk: int = 1
     chunks = [units[i::workers] for i in range(workers)]
     args = [([m.name for m in shms], [sp[0] for sp in specs], [np.dtype(sp[1]).str for sp in specs], c, seed, dk, dv,
              dtype, cu) for c in chunks]
-    with mp.get_context("spawn").Pool(workers) as pool:
-        pool.map(_fill_units, args)
+    pool_map(_fill_units, args, workers)
     if isinstance(init_state, bool):
         init_state = [init_state] * N
     S0 = None

@@ -390,11 +390,12 @@ def _need_pools(S_pool, rows_pool, pos_pool, H, dev):
 
 
 def kda_contract_prefill(q, k, v, g, beta, cu_seqlens, S_pool, rows_pool, pos_pool, cu_seqlens_host=None,
-                         slots=None, o=None, scale: float = 1.0, with_output: bool = True):
+                         slots=None, o=None, scale: float = 1.0, with_output: bool = True, split_width: int = 0):
     """Packed ragged batch through the row contract, pools updated in place.
 
     q, k, v, g: [T, H, 128]; beta: [T, H]; cu_seqlens: device int32 [N + 1]; slots: int32 [N] pool rows
-    (None = 0..N-1).  Returns o [T, H, 128] (dtype of q) or None."""
+    (None = 0..N-1).  split_width: workgroups per (sequence, head), 1, 2 or 4 (kda_contract_prefill_split),
+    0 picks by grid size.  Returns o [T, H, 128] (dtype of q) or None."""
     T, H, _ = q.shape
     dt = q.dtype
     dev = q.device
@@ -422,10 +423,12 @@ def kda_contract_prefill(q, k, v, g, beta, cu_seqlens, S_pool, rows_pool, pos_po
         o = torch.empty((T, H, D), dtype=dt, device=dev)
     _need(o, "o", (T, H, D), dt, dev)
     lib = _lib.load()
-    _lib.check(lib.kda_contract_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
-                                        _ptr(cu_seqlens_host), N, H, D, D, _dtype_code(q), float(scale),
-                                        _ptr(S_pool), _ptr(rows_pool), _ptr(pos_pool), _ptr(slots), _ptr(o),
-                                        _stream()),
+    if split_width not in (0, 1, 2, 4):
+        raise ValueError("split_width must be 0, 1, 2 or 4")
+    _lib.check(lib.kda_contract_prefill_split(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                                              _ptr(cu_seqlens_host), N, H, D, D, _dtype_code(q), float(scale),
+                                              _ptr(S_pool), _ptr(rows_pool), _ptr(pos_pool), _ptr(slots), _ptr(o),
+                                              int(split_width), _stream()),
                "kda_contract_prefill")
     return o
 

@@ -98,8 +98,9 @@ def kda_prefill_segmented(q, k, v, g, beta, cu_seqlens_host, seg_len: Optional[i
 
     Same arguments and results as ``kda.kda_prefill`` (cu_seqlens_host: CPU
     int32 [N + 1]); returns (o, final_state).  ``seg_len=None`` picks it with
-    ``auto_seg_len``.  ``work`` may hold preallocated buffers from
-    ``alloc_work`` so repeated calls allocate nothing.
+    ``auto_seg_len``.  With a ``plan``, preallocated buffers ``work`` from
+    ``alloc_work`` and the outputs ``o`` and ``final_state`` passed in, a call
+    allocates no device memory.
     """
     dev = q.device
     H = q.shape[1]
@@ -125,7 +126,7 @@ def kda_prefill_segmented(q, k, v, g, beta, cu_seqlens_host, seg_len: Optional[i
     for n in plan.multi:
         r = plan.row_of_seq[n]
         nseg = len(r)
-        frag_cu_h = torch.from_numpy(plan.rows[r.start:r.start + nseg].copy())
+        frag_cu_h = work["frag_cu_h"][n]
         frag_cu_d = work["frag_cu"][n]
         M, St = work["M"][n], work["St"][n]
         # pass 1: fragments of segments 0 .. nseg-2
@@ -140,7 +141,7 @@ def kda_prefill_segmented(q, k, v, g, beta, cu_seqlens_host, seg_len: Optional[i
     # pass 2: every segment from its entry state, longest rows started first
     kda.kda_prefill_ordered(q, k, v, g, beta, work["rows_d"], work["order2"], work["rows_h"], initial_state=init2,
                             final_state=fin2, o=o, scale=scale)
-    final_state.copy_(fin2.index_select(0, work["last_rows"]))
+    torch.index_select(fin2, 0, work["last_rows"], out=final_state)
     return o, final_state
 
 
@@ -162,12 +163,13 @@ def alloc_work(plan: SegmentPlan, H: int, dev) -> dict:
         "rows_h": torch.from_numpy(plan.rows.copy()),
         "first_rows": torch.tensor([r.start for r in plan.row_of_seq], dtype=torch.long, device=dev),
         "last_rows": torch.tensor([r.stop - 1 for r in plan.row_of_seq], dtype=torch.long, device=dev),
-        "M": {}, "St": {}, "frag_cu": {},
+        "M": {}, "St": {}, "frag_cu": {}, "frag_cu_h": {},
     }
     for n in plan.multi:
         r = plan.row_of_seq[n]
         nf = len(r) - 1
         work["M"][n] = torch.empty((nf, H, D, D), dtype=torch.float32, device=dev)
         work["St"][n] = torch.empty((nf, H, D, D), dtype=torch.float32, device=dev)
-        work["frag_cu"][n] = torch.from_numpy(plan.rows[r.start:r.start + nf + 1].copy()).to(dev)
+        work["frag_cu_h"][n] = torch.from_numpy(plan.rows[r.start:r.start + nf + 1].copy())
+        work["frag_cu"][n] = work["frag_cu_h"][n].to(dev)
     return work

@@ -172,6 +172,13 @@ kda_status_t kda_verify_commit_prologue(const void* k, const void* v, const floa
  *                   final = M initial + S~ ("Kimi K3 的训练与 Serving Infra",
  *                   section 4.2, KCP fragments).
  * Empty sequences pass their initial state through.
+ * Precondition on the gates: -5 <= g <= 0 in every channel, the lower bound
+ * on log-decay that the KDA math box prints (its scaled sigmoid keeps g above
+ * g_min = -5).  The chunk products rescale by exp(+-(b_r - b_s)) over at most
+ * 16 tokens of cumulative decay, which stays inside fp32 range only under
+ * that bound; gates below it are not checked (they live in device memory) and
+ * can overflow to inf/NaN.  The row contract (kda_contract_*) has no such
+ * bound.
  */
 kda_status_t kda_prefill(const void* q, const void* k, const void* v, const float* g,
                          const float* beta, const int32_t* cu_seqlens,
@@ -294,6 +301,22 @@ kda_status_t kda_contract_prefill(const void* q, const void* k, const void* v, c
                                   int32_t num_seqs, int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t dtype,
                                   float scale, float* S_pool, float* rows_pool, int32_t* pos_pool,
                                   const int32_t* slots, void* o, void* stream);
+
+/*
+ * kda_contract_prefill_split — kda_contract_prefill with the number of
+ * workgroups that share each (sequence, head) fixed by the caller instead of
+ * picked from the grid size and the device's compute-unit count:
+ * split_width 1, 2 or 4 (each workgroup then holds 128 / split_width value
+ * columns of the state), or 0 for the automatic choice.  Every width gives the
+ * same bits (the row arithmetic is the same); a caller fixes it to reproduce a
+ * launch shape, e.g. to compare widths on a part with another CU count.
+ * Errors as kda_contract_prefill, and KDA_ERR_INVALID_ARG for another width.
+ */
+kda_status_t kda_contract_prefill_split(const void* q, const void* k, const void* v, const float* g,
+                                        const float* beta, const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                                        int32_t num_seqs, int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t dtype,
+                                        float scale, float* S_pool, float* rows_pool, int32_t* pos_pool,
+                                        const int32_t* slots, void* o, int32_t split_width, void* stream);
 
 /*
  * kda_contract_decode — one token per request (inputs laid out as for

@@ -47,3 +47,78 @@ def bf16_floor(ref) -> float:
     r32 = np.asarray(ref, dtype=np.float32)
     rb = gen.bf16_bits_to_f32(gen.f32_to_bf16_bits(r32)).astype(np.float64)
     return rel_l2(rb, ref)
+
+
+# ---------------------------------------------------------------------------
+# Localised parity: a whole-tensor norm can hide one bad sequence or head, so
+# every batched comparison also bounds each (sequence, head) or (request, head)
+# slice and each element.
+# ---------------------------------------------------------------------------
+
+def packed_slices(cu_seqlens, H):
+    """Index of every (sequence, head) slice of a packed [T, H, ...] tensor (empty sequences skipped)."""
+    cu = [int(x) for x in np.asarray(cu_seqlens)]
+    return [(f"seq {n} head {h}", np.s_[cu[n]:cu[n + 1], h])
+            for n in range(len(cu) - 1) if cu[n + 1] > cu[n] for h in range(H)]
+
+
+def unit_slices(N, H, steps=False):
+    """Index of every (request, head) slice of an [N, H, ...] tensor, or of an [N, G, H, ...]
+    tensor (all G positions of the request) when steps is set."""
+    if steps:
+        return [(f"request {n} head {h}", np.s_[n, :, h]) for n in range(N) for h in range(H)]
+    return [(f"unit {n} head {h}", np.s_[n, h]) for n in range(N) for h in range(H)]
+
+
+def check_parity(x, ref, tol, slices=None, bf16_out=False, tag=""):
+    """Assert GPU result x matches the oracle's ref (fp64); return the whole-tensor rel-L2.
+
+    * whole tensor and every slice: rel-L2 <= tol, or for an output rounded to bf16, <= max(tol,
+      1.2 x that tensor's or slice's own bf16 floor): the reference itself rounded to bf16 misses
+      tol on a slice of a few tokens, whose floor can lie above it;
+    * every element: |x - ref| <= 2^-7 |ref| + 1e-3 RMS(slice) for a bf16 output (one bf16 ulp
+      plus a small absolute part), |x - ref| <= tol (|ref| + RMS(slice)) for an fp32 result.
+    A slice whose reference is exactly zero must come out exactly zero.
+    """
+    if isinstance(x, torch.Tensor):
+        x = to_f64(x)
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert x.shape == ref.shape, (x.shape, ref.shape)
+    assert np.all(np.isfinite(x)), f"{tag}: non-finite values"
+    whole = rel_l2(x, ref) if ref.size else 0.0
+    wbound = max(tol, 1.2 * bf16_floor(ref)) if bf16_out and ref.size else tol
+    assert whole <= wbound, f"{tag}: whole-tensor rel-L2 {whole:.3e} > {wbound:.3e}"
+    if slices is None:
+        slices = [("all", np.s_[...])]
+    worst_s, worst_s_at, worst_e, worst_e_at = 0.0, "", 0.0, ""
+    for name, sl in slices:
+        xs, rs = x[sl], ref[sl]
+        if rs.size == 0:
+            continue
+        nref = float(np.linalg.norm(rs.ravel()))
+        if nref == 0.0:
+            assert float(np.max(np.abs(xs))) == 0.0, f"{tag} {name}: reference is zero, result is not"
+            continue
+        e = float(np.linalg.norm((xs - rs).ravel())) / nref
+        bound = max(tol, 1.2 * bf16_floor(rs)) if bf16_out else tol
+        assert e <= bound, f"{tag} {name}: rel-L2 {e:.3e} > {bound:.3e}"
+        if e / bound > worst_s:
+            worst_s, worst_s_at = e / bound, name
+        rms = nref / np.sqrt(rs.size)
+        if bf16_out:
+            lim = 2.0 ** -7 * np.abs(rs) + 1e-3 * rms
+        else:
+            lim = tol * (np.abs(rs) + rms)
+        ratio = np.abs(xs - rs) / lim
+        i = int(np.argmax(ratio))
+        r = float(ratio.ravel()[i])
+        assert r <= 1.0, (f"{tag} {name}: element {np.unravel_index(i, rs.shape)} off by "
+                          f"{float(np.abs(xs - rs).ravel()[i]):.3e} (ref {float(rs.ravel()[i]):.3e}, bound "
+                          f"{float(lim.ravel()[i]):.3e})")
+        if r > worst_e:
+            worst_e, worst_e_at = r, name
+    msg = (f"{tag}: rel-L2 {whole:.3e} (bar {tol:.0e}); worst slice {worst_s:.2f} of its bound ({worst_s_at}); "
+           f"worst element {worst_e:.2f} of its bound ({worst_e_at})")
+    print(msg)
+    return whole

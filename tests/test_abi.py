@@ -35,7 +35,7 @@ def test_header_declares_the_entry_points():
                  "kda_prefill_ordered", "kda_decode_step_prologue", "kda_verify_block_prologue",
                  "kda_verify_commit_prologue", "kda_prefill_prologue", "kda_contract_prefill",
                  "kda_contract_decode", "kda_contract_state", "kda_contract_verify", "kda_contract_commit",
-                 "kda_contract_commit_stash",
+                 "kda_contract_commit_stash", "kda_contract_prefill_split",
                  "kda_status_string", "kda_version"):
         assert name in syms
     assert set(syms) == set(_lib.SIGNATURES), "binding signatures and header disagree"
@@ -194,6 +194,10 @@ def test_contract_argument_errors(lib):
     assert lib.kda_contract_prefill(None, p, p, p, p, p, good, 2, 2, 128, 128, 1, 1.0, p, p, p, None, p, None) == E
     assert lib.kda_contract_prefill(p, p, p, p, p, None, good, 2, 2, 128, 128, 1, 1.0, p, p, p, None, p, None) == E
     assert lib.kda_contract_prefill(p, p, p, p, p, p, good, 2, 2, 128, 128, 3, 1.0, p, p, p, None, p, None) == U
+    for w in (3, -1, 8):  # split widths other than 0, 1, 2, 4
+        assert lib.kda_contract_prefill_split(p, p, p, p, p, p, good, 2, 2, 128, 128, 1, 1.0, p, p, p, None, p, w,
+                                              None) == E
+    assert lib.kda_contract_prefill_split(*args(bad)[:-1], 2, None) == E
     # verify (read-only; o required) and commit (q may be NULL; accepted_len required)
     assert lib.kda_contract_verify(p, p, p, p, p, 4, 0, 2, 128, 128, 1, 1.0, p, p, p, None, p, None, None) == E
     assert lib.kda_contract_verify(p, p, p, p, p, 4, 8, 2, 128, 128, 1, 1.0, p, p, p, None, None, None, None) == E

@@ -15,7 +15,7 @@ from gated_delta_rule_15_amd import inputs as gen
 from oracle import kda_contract as cf
 from oracle import kda_oracle as orc
 
-from kda_testutil import DEV, bf16_floor, rel_l2, to_dev, to_f64
+from kda_testutil import DEV, check_parity, packed_slices, rel_l2, to_dev, to_f64, unit_slices
 
 pytestmark = pytest.mark.gpu
 
@@ -128,9 +128,9 @@ def test_prefill_then_decode_match_oracle(dtype):
             o_ref[t:t + L, h] = cf.contract_tokens(states[n][h], q[s0:s0 + L, h], k[s0:s0 + L, h], v[s0:s0 + L, h],
                                                    g[s0:s0 + L, h], beta[s0:s0 + L, h], scale=0.75)
         t += L
-    eo = rel_l2(to_f64(o), o_ref)
-    print(f"contract prefill {dtype}: rel-L2 o={eo:.3e} (bf16 floor {bf16_floor(o_ref):.3e})")
-    assert eo <= TOL[dtype]
+    cu_pre = np.concatenate([[0], np.cumsum(lens)])
+    check_parity(o, o_ref, TOL[dtype], packed_slices(cu_pre, H), bf16_out=dtype == "bf16",
+                 tag=f"contract prefill {dtype} o")
     _check_pools_against_oracle(pools, states, TOL[dtype])
     # 20 decode steps on top (crossing chunk closes at different steps per sequence)
     errs = []
@@ -142,16 +142,14 @@ def test_prefill_then_decode_match_oracle(dtype):
             for h in range(H):
                 od_ref[n, h] = cf.contract_tokens(states[n][h], q[tt:tt + 1, h], k[tt:tt + 1, h], v[tt:tt + 1, h],
                                                   g[tt:tt + 1, h], beta[tt:tt + 1, h], scale=0.75)[0]
-        errs.append(rel_l2(to_f64(od), od_ref))
+        errs.append(check_parity(od, od_ref, TOL[dtype], unit_slices(len(lens), H), bf16_out=dtype == "bf16",
+                                 tag=f"contract decode step {step} {dtype} o"))
     print(f"contract decode {dtype}: max rel-L2 o over 20 steps {max(errs):.3e}")
-    assert max(errs) <= TOL[dtype]
     _check_pools_against_oracle(pools, states, TOL[dtype])
     # the running state equals the token recurrence over all tokens taken
     S_run = to_f64(_kda().kda_contract_state(*pools))
     _, S_ref = orc.prefill(q, k, v, g, beta, p.cu_seqlens, p.initial_state, scale=0.75)
-    es = rel_l2(S_run, S_ref)
-    print(f"contract running state {dtype}: rel-L2 {es:.3e}")
-    assert es <= TOL[dtype]
+    check_parity(S_run, S_ref, TOL[dtype], unit_slices(len(lens), H), tag=f"contract running state {dtype}")
 
 
 def test_paths_are_bit_identical():
@@ -233,7 +231,7 @@ def test_empty_sequences_and_slots():
     for n, (a, b) in ((1, (0, 21)), (3, (21, 37))):
         for h in range(2):
             o_ref[a:b, h] = cf.contract_tokens(states[n][h], q[a:b, h], k[a:b, h], v[a:b, h], g[a:b, h], beta[a:b, h])
-    assert rel_l2(to_f64(o), o_ref) <= 2e-3
+    check_parity(o, o_ref, 2e-3, packed_slices([0, 21, 37], 2), bf16_out=True, tag="contract with slots o")
     assert int(pools[2][int(slots[1]), 0]) == 5 and int(pools[2][int(slots[3]), 1]) == 0
     # an all-empty batch is a no-op
     _prefill(_slice(p, [(0, 0)] * 4), pools, slots=slots)
@@ -259,24 +257,24 @@ def test_decode_workload_sampled_parity():
     assert torch.equal(pools[2].cpu(), torch.tensor(np.repeat(pos[:, None], H, 1), dtype=torch.int32))
     od = _decode_token(p, [L - 1 for L in lens], pools)
     q, k, v, g, beta = (p.f64(x) for x in ("q", "k", "v", "g", "beta"))
-    for n, h in [(0, 0), (5, 11), (17, 3), (31, 7), (42, 0), (63, 11)] + [(int(np.argmax(pos == 15)), 2)]:
+    od_ref = np.empty((N, H, 128))
+    for n in range(N):
         a, b = int(p.cu_seqlens[n]), int(p.cu_seqlens[n + 1])
-        o_ref, _ = orc.recurrence(q[a:b, h], k[a:b, h], v[a:b, h], g[a:b, h], beta[a:b, h], p.initial_state[n, h])
-        assert rel_l2(to_f64(od[n, h]), o_ref[-1]) <= 2e-3
+        for h in range(H):
+            o_ref, _ = orc.recurrence(q[a:b, h], k[a:b, h], v[a:b, h], g[a:b, h], beta[a:b, h], p.initial_state[n, h])
+            od_ref[n, h] = o_ref[-1]
+    check_parity(od, od_ref, 2e-3, unit_slices(N, H), bf16_out=True, tag="contract decode 64 x 12 o")
 
 
-def test_prefill_workload_sampled_parity():
-    """4096 tokens x 12 heads in one prefill; heads 0 and 7 against the token recurrence."""
+def test_prefill_workload_parity():
+    """4096 tokens x 12 heads in one prefill; every head against the token recurrence."""
     p = gen.packed_batch(seed=36, seqlens=[4096], H=12, dtype="bf16")
     pools = _pools(p)
     o = _prefill(_slice(p, [(0, 4096)]), pools)
     S_run = to_f64(_kda().kda_contract_state(*pools))
-    q, k, v, g, beta = (p.f64(x) for x in ("q", "k", "v", "g", "beta"))
-    for h in (0, 7):
-        o_ref, S_ref = orc.recurrence(q[:, h], k[:, h], v[:, h], g[:, h], beta[:, h])
-        eo, es = rel_l2(to_f64(o[:, h]), o_ref), rel_l2(S_run[0, h], S_ref)
-        print(f"contract prefill 4096 x 12, head {h}: rel-L2 o={eo:.3e} S={es:.3e}")
-        assert eo <= 2e-3 and es <= 2e-3
+    o_ref, S_ref = orc.prefill(*(p.f64(x) for x in ("q", "k", "v", "g", "beta")), p.cu_seqlens, None)
+    check_parity(o, o_ref, 2e-3, packed_slices(p.cu_seqlens, 12), bf16_out=True, tag="contract prefill 4096 x 12 o")
+    check_parity(S_run, S_ref, 2e-3, unit_slices(1, 12), tag="contract prefill 4096 x 12 S")
     assert int(pools[2][0, 0]) == 0  # 4096 = 256 closed chunks
 
 
@@ -295,12 +293,15 @@ def test_state_handover_to_the_plain_decode(dtype):
         o = _kda().kda_decode_step(to_dev(pick(p.q), dtype), to_dev(pick(p.k), dtype), to_dev(pick(p.v), dtype),
                                    to_dev(pick(p.g)), to_dev(pick(p.beta)), S_run)
         torch.cuda.synchronize()
+        od_ref = np.empty((len(lens), 2, 128))
         for n, L in enumerate(lens):
             a = int(p.cu_seqlens[n])
             for h in range(2):
                 o_ref, _ = orc.recurrence(q[a:a + L + step + 1, h], k[a:a + L + step + 1, h], v[a:a + L + step + 1, h],
                                           g[a:a + L + step + 1, h], beta[a:a + L + step + 1, h], p.initial_state[n, h])
-                assert rel_l2(to_f64(o[n, h]), o_ref[-1]) <= TOL[dtype]
+                od_ref[n, h] = o_ref[-1]
+        check_parity(o, od_ref, TOL[dtype], unit_slices(len(lens), 2), bf16_out=dtype == "bf16",
+                     tag=f"handover step {step} {dtype}")
 
 
 def test_strong_decay_beyond_the_fused_prefill_range():
@@ -315,8 +316,8 @@ def test_strong_decay_beyond_the_fused_prefill_range():
     q, k, v, g, beta = (p.f64(x) for x in ("q", "k", "v", "g", "beta"))
     o_ref, S_ref = orc.prefill(q, k, v, g, beta, p.cu_seqlens, p.initial_state)
     assert torch.isfinite(o).all()
-    assert rel_l2(to_f64(o), o_ref) <= 1e-5
-    assert rel_l2(to_f64(_kda().kda_contract_state(*pools)), S_ref) <= 1e-5
+    check_parity(o, o_ref, 1e-5, packed_slices(p.cu_seqlens, 2), tag="contract strong decay o")
+    check_parity(_kda().kda_contract_state(*pools), S_ref, 1e-5, unit_slices(2, 2), tag="contract strong decay S")
 
 
 def test_paths_are_bit_identical_f32():
@@ -379,7 +380,8 @@ def test_verify_equals_decode_steps_and_reads_only(dtype):
             o_ref[n, :, h] = cf.contract_tokens(st, qq[a + L:a + L + G, h], kk[a + L:a + L + G, h],
                                                 vv[a + L:a + L + G, h], gg[a + L:a + L + G, h],
                                                 bb[a + L:a + L + G, h])
-    assert rel_l2(to_f64(o), o_ref) <= TOL[dtype]
+    check_parity(o, o_ref, TOL[dtype], unit_slices(N, H, steps=True), bf16_out=dtype == "bf16",
+                 tag=f"contract verify {dtype} o")
 
 
 def test_commit_equals_decode_steps():
@@ -402,8 +404,9 @@ def test_commit_equals_decode_steps():
     _assert_same_state(pools, steps)
 
 
-def test_verify_commit_workload_sampled():
-    """32 requests x 12 heads x 8 drafts (the verify workload), positions spread over the chunk."""
+def test_verify_commit_workload_parity():
+    """32 requests x 12 heads x 8 drafts (the verify workload), positions spread over the chunk; every
+    (request, head) against the token recurrence."""
     N, H, G = 32, 12, 8
     p, pools, lens = _positioned_pools(43, N, H, G)
     q, k, v, g, beta = _block_inputs(p, lens, G)
@@ -414,15 +417,19 @@ def test_verify_commit_workload_sampled():
     S_run = to_f64(_kda().kda_contract_state(*pools))
     qq, kk, vv, gg, bb = (p.f64(x) for x in ("q", "k", "v", "g", "beta"))
     accn = acc.cpu().numpy()
-    for n, h in [(0, 0), (7, 5), (15, 11), (31, 3)]:
+    o_all = np.empty((N, G, H, 128))
+    S_all = np.empty((N, H, 128, 128))
+    for n in range(N):
         a, L = int(p.cu_seqlens[n]), lens[n]
-        o_ref, _ = orc.recurrence(qq[a:a + L + G, h], kk[a:a + L + G, h], vv[a:a + L + G, h], gg[a:a + L + G, h],
-                                  bb[a:a + L + G, h], p.initial_state[n, h])
-        assert rel_l2(to_f64(o[n, :, h]), o_ref[L:]) <= 2e-3
         m = L + int(accn[n])
-        _, S_ref = orc.recurrence(qq[a:a + m, h], kk[a:a + m, h], vv[a:a + m, h], gg[a:a + m, h], bb[a:a + m, h],
-                                  p.initial_state[n, h])
-        assert rel_l2(S_run[n, h], S_ref) <= 2e-3
+        for h in range(H):
+            o_ref, _ = orc.recurrence(qq[a:a + L + G, h], kk[a:a + L + G, h], vv[a:a + L + G, h],
+                                      gg[a:a + L + G, h], bb[a:a + L + G, h], p.initial_state[n, h])
+            o_all[n, :, h] = o_ref[L:]
+            _, S_all[n, h] = orc.recurrence(qq[a:a + m, h], kk[a:a + m, h], vv[a:a + m, h], gg[a:a + m, h],
+                                            bb[a:a + m, h], p.initial_state[n, h])
+    check_parity(o, o_all, 2e-3, unit_slices(N, H, steps=True), bf16_out=True, tag="contract verify 32 x 12 x 8 o")
+    check_parity(S_run, S_all, 2e-3, unit_slices(N, H), tag="contract commit 32 x 12 x 8 S")
 
 
 @pytest.mark.parametrize("G", [8, 16])
@@ -486,13 +493,36 @@ def test_draft_blocks_of_every_length(G):
     _assert_same_state(pools, steps)
 
 
+@pytest.mark.parametrize("width", [2, 4])
+def test_split_widths_equal_unsplit_bitwise(width):
+    """The prefill with each unit's value columns split over `width` workgroups (and the shared rows
+    written by the second launch) equals the unsplit prefill bit for bit, from position 0 and from a
+    nonzero open-chunk position (a prefill cut, then a prefill of the rest), whatever the CU count."""
+    rng = np.random.default_rng(80 + width)
+    N, H = 9, 2
+    cut = [int(x) for x in rng.integers(0, 20, N)]
+    rest = [int(x) for x in rng.integers(0, 45, N)]
+    rest[2], cut[3], rest[3] = 16 - cut[2] % 16, 16, 16  # ends on a chunk close; starts at a close
+    p = gen.packed_batch(seed=80 + width, seqlens=[a + b for a, b in zip(cut, rest)], H=H, dtype="bf16",
+                         init_state=True)
+    pools = {w: _pools(p) for w in (1, width)}
+    outs = {}
+    for w, pl in pools.items():
+        o1 = _prefill(_slice(p, [(0, c) for c in cut]), pl, split_width=w)
+        o2 = _prefill(_slice(p, [(c, c + r) for c, r in zip(cut, rest)]), pl, split_width=w)
+        outs[w] = (o1, o2)
+    for a, b in zip(outs[1], outs[width]):
+        assert torch.equal(_bits(a), _bits(b))
+    _assert_same_state(pools[1], pools[width])
+
+
 @pytest.mark.parametrize("total", [72, 144])
 def test_split_and_unsplit_prefill_are_bit_identical(total):
-    """A prefill grid of at most 64 (128) (sequence, head) units splits each unit's value columns over
-    four (two) workgroups and writes the shared keys, decays and position in a second launch; a grid
-    of more than 128 units does not split.  `total` sequences in one call and the same sequences in
-    two calls of total / 2 (72: unsplit vs four-way; 144: unsplit vs two-way) give the same outputs,
-    entry states, open rows and positions, bit for bit."""
+    """The automatic split width: a grid of at most CUs / 4 (CUs / 2) (sequence, head) units splits
+    four (two) ways, a larger one does not.  `total` sequences in one call and the same sequences in two
+    calls of total / 2 give the same outputs, entry states, open rows and positions, bit for bit (on a
+    256-CU part, 72: two-way vs four-way; 144: unsplit vs two-way; each width is compared with the
+    unsplit path directly in test_split_widths_equal_unsplit_bitwise)."""
     rng = np.random.default_rng(70 + total)
     lens = [int(x) for x in rng.integers(0, 41, total)]
     lens[5], lens[40] = 16, 32  # ends exactly at a chunk close
@@ -513,3 +543,38 @@ def test_split_and_unsplit_prefill_are_bit_identical(total):
         outs.append(_prefill(d, parted, slots=slots))
     assert torch.equal(_bits(o_whole), _bits(torch.cat(outs)))
     _assert_same_state(whole, parted)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("case", ["beta1", "beta0", "g0"])
+def test_edge_gates(case, dtype):
+    """beta = 1 (the value along the key is replaced; with q = k the output is v), beta = 0 (pure channel
+    decay) and g = 0 (the plain delta rule) through a contract prefill and three decode steps: against
+    the token recurrence per slice and per element."""
+    lens = [40, 17, 5]
+    H = 2
+    p = gen.packed_batch(seed=90, seqlens=[L + 3 for L in lens], H=H, dtype=dtype, init_state=True)
+    if case == "beta1":
+        p.beta[:] = np.float32(1.0)
+        p.q[:] = p.k
+    elif case == "beta0":
+        p.beta[:] = np.float32(0.0)
+    else:
+        p.g[:] = np.float32(0.0)
+    pools = _pools(p)
+    o = _prefill(_slice(p, [(0, L) for L in lens]), pools)
+    od = [_decode_token(p, [L + s for L in lens], pools) for s in range(3)]
+    q, k, v, g, beta = (p.f64(x) for x in ("q", "k", "v", "g", "beta"))
+    o_ref, S_ref = orc.prefill(q, k, v, g, beta, p.cu_seqlens, p.initial_state)
+    pre = np.concatenate([np.arange(p.cu_seqlens[n], p.cu_seqlens[n] + L) for n, L in enumerate(lens)])
+    cu_pre = np.concatenate([[0], np.cumsum(lens)])
+    check_parity(o, o_ref[pre], TOL[dtype], packed_slices(cu_pre, H), bf16_out=dtype == "bf16",
+                 tag=f"contract edge {case} {dtype} prefill o")
+    for s in range(3):
+        idx = [int(p.cu_seqlens[n]) + L + s for n, L in enumerate(lens)]
+        check_parity(od[s], o_ref[idx], TOL[dtype], unit_slices(len(lens), H), bf16_out=dtype == "bf16",
+                     tag=f"contract edge {case} {dtype} decode {s} o")
+    check_parity(_kda().kda_contract_state(*pools), S_ref, TOL[dtype], unit_slices(len(lens), H),
+                 tag=f"contract edge {case} {dtype} running state")
+    if case == "beta1":
+        assert rel_l2(to_f64(o), v[pre]) <= (2e-2 if dtype == "bf16" else 1e-5)

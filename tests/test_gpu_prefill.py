@@ -6,7 +6,7 @@ import torch
 from gated_delta_rule_15_amd import inputs as gen
 from oracle import kda_oracle as orc
 
-from kda_testutil import bf16_floor, packed_to_dev, rel_l2, to_dev, to_f64
+from kda_testutil import check_parity, packed_slices, packed_to_dev, rel_l2, to_dev, to_f64, unit_slices
 
 pytestmark = pytest.mark.gpu
 
@@ -34,14 +34,21 @@ def _oracle(p: gen.Packed, scale=1.0):
 
 
 def _check(p, o, S, tag, scale=1.0):
+    """Outputs per (sequence, head) slice and per element, final states per (sequence, head)."""
     o_ref, S_ref = _oracle(p, scale)
-    eo = rel_l2(to_f64(o), o_ref) if o_ref.size else 0.0
-    es = rel_l2(to_f64(S), S_ref)
-    floor = bf16_floor(o_ref) if p.dtype == "bf16" and o_ref.size else 0.0
-    print(f"{tag}: rel-L2 o={eo:.3e} (bf16 floor {floor:.3e}) S={es:.3e}")
-    assert eo <= TOL[p.dtype], eo
-    assert es <= TOL[p.dtype], es
+    eo = check_parity(o, o_ref, TOL[p.dtype], packed_slices(p.cu_seqlens, p.H), bf16_out=p.dtype == "bf16",
+                      tag=f"{tag} o") if o_ref.size else 0.0
+    es = check_parity(S, S_ref, TOL[p.dtype], unit_slices(p.num_seqs, p.H), tag=f"{tag} S")
     return eo, es
+
+
+def _check_transitions(p, M, tag):
+    M_ref = np.empty((p.num_seqs, p.H, 128, 128))
+    for n in range(p.num_seqs):
+        a, b = p.cu_seqlens[n], p.cu_seqlens[n + 1]
+        for h in range(p.H):
+            M_ref[n, h] = orc.transition(p.f64("k")[a:b, h], p.f64("g")[a:b, h], p.f64("beta")[a:b, h])
+    return check_parity(M, M_ref, TOL[p.dtype], unit_slices(p.num_seqs, p.H), tag=f"{tag} M")
 
 
 def test_tiny_prefill_fp32():
@@ -101,14 +108,7 @@ def test_prefill_transition_output(dtype):
     M = torch.empty((3, 2, 128, 128), device="cuda:0")
     o, S, _ = _run(p, transition_out=M)
     _check(p, o, S, f"with transition {dtype}")
-    M_ref = np.empty((3, 2, 128, 128))
-    for n in range(3):
-        a, b = p.cu_seqlens[n], p.cu_seqlens[n + 1]
-        for h in range(2):
-            M_ref[n, h] = orc.transition(p.f64("k")[a:b, h], p.f64("g")[a:b, h], p.f64("beta")[a:b, h])
-    e = rel_l2(to_f64(M), M_ref)
-    print(f"transition {dtype}: rel-L2 M={e:.3e}")
-    assert e <= TOL[dtype]
+    _check_transitions(p, M, f"transition {dtype}")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -125,14 +125,7 @@ def test_prefill_strong_decay(dtype, gate):
     o, S, _ = _run(p, transition_out=M)
     assert torch.isfinite(o.float()).all() and torch.isfinite(S).all() and torch.isfinite(M).all()
     _check(p, o, S, f"strong decay ({gate}) {dtype}")
-    M_ref = np.empty((4, 2, 128, 128))
-    for n in range(4):
-        a, b = p.cu_seqlens[n], p.cu_seqlens[n + 1]
-        for h in range(2):
-            M_ref[n, h] = orc.transition(p.f64("k")[a:b, h], p.f64("g")[a:b, h], p.f64("beta")[a:b, h])
-    e = rel_l2(to_f64(M), M_ref)
-    print(f"strong decay ({gate}) {dtype}: rel-L2 M={e:.3e}")
-    assert e <= TOL[dtype]
+    _check_transitions(p, M, f"strong decay ({gate}) {dtype}")
 
 
 @pytest.mark.parametrize("dtype,lens,H,interval,init", [
@@ -155,9 +148,7 @@ def test_prefill_checkpoints(dtype, lens, H, interval, init):
     C_ref = orc.prefill_checkpoints(p.f64("k"), p.f64("v"), p.f64("g"), p.f64("beta"), p.cu_seqlens, interval,
                                     p.initial_state)
     assert C.shape[0] == C_ref.shape[0] == n
-    e = rel_l2(to_f64(C), C_ref)
-    print(f"checkpoints {dtype} x{n}: rel-L2 {e:.3e}")
-    assert e <= TOL[dtype]
+    check_parity(C, C_ref, TOL[dtype], unit_slices(n, H), tag=f"checkpoints {dtype} x{n}")
 
 
 def test_compose_matches_oracle():
@@ -171,8 +162,9 @@ def test_compose_matches_oracle():
     torch.cuda.synchronize()
     for h in range(H):
         ref_in, ref_fin = orc.compose(M[:, h], St[:, h], S0[h])
-        assert rel_l2(to_f64(S_in[:, h]), ref_in) <= 1e-5
-        assert rel_l2(to_f64(S_fin[h]), ref_fin) <= 1e-5
+        check_parity(S_in[:, h], ref_in, 1e-5, [(f"segment {i}", np.s_[i]) for i in range(n)],
+                     tag=f"compose head {h} entry states")
+        check_parity(S_fin[h], ref_fin, 1e-5, tag=f"compose head {h} final state")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -190,11 +182,12 @@ def test_split_prefill_composes_to_unsplit(dtype):
     o, S_seg = kda_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu, seg, initial_state=S_in)
     torch.cuda.synchronize()
     o_ref, S_ref = _oracle(p)
-    eo = rel_l2(to_f64(o), o_ref)
-    es = rel_l2(to_f64(S_fin), S_ref[0])
-    es2 = rel_l2(to_f64(S_seg[2]), S_ref[0])
-    print(f"split+compose {dtype}: o={eo:.3e} S(compose)={es:.3e} S(pass 2)={es2:.3e}")
-    assert eo <= TOL[dtype] and es <= TOL[dtype] and es2 <= TOL[dtype]
+    check_parity(o, o_ref, TOL[dtype], packed_slices([0, T], H), bf16_out=dtype == "bf16",
+                 tag=f"split+compose {dtype} o")
+    check_parity(S_fin, S_ref[0], TOL[dtype], [(f"head {h}", np.s_[h]) for h in range(H)],
+                 tag=f"split+compose {dtype} S(compose)")
+    check_parity(S_seg[2], S_ref[0], TOL[dtype], [(f"head {h}", np.s_[h]) for h in range(H)],
+                 tag=f"split+compose {dtype} S(pass 2)")
 
 
 def test_prefill_deterministic():
@@ -299,3 +292,57 @@ def test_prefill_random_batches(case):
     p = gen.packed_batch(seed=900 + case, seqlens=lens, H=H, dtype=dtype, init_state=init)
     o, S, _ = _run(p, scale=scale)
     _check(p, o, S, f"random batch {case}: H={H} lens={lens} {dtype}", scale=scale)
+
+
+def _edge_batch(case, dtype, lens=(300, 77, 5, 64), H=2, seed=17):
+    """The special cases the KDA math box prints: beta = 1 replaces the value along the key, beta = 0
+    keeps the state and only decays it, g = 0 (alpha = 1) is the plain delta rule."""
+    p = gen.packed_batch(seed=seed, seqlens=list(lens), H=H, dtype=dtype,
+                         init_state=case != "beta0_zero_state")
+    if case == "beta1":
+        p.beta[:] = np.float32(1.0)
+        p.q[:] = p.k  # then o_t = S_t^T k_t = v_t for unit keys
+    elif case in ("beta0", "beta0_zero_state"):
+        p.beta[:] = np.float32(0.0)
+    elif case == "g0":
+        p.g[:] = np.float32(0.0)
+    return p
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("case", ["beta1", "beta0", "beta0_zero_state", "g0"])
+def test_prefill_edge_gates(case, dtype):
+    """beta = 1, beta = 0 (with and without an initial state) and g = 0 on the GPU: against the oracle
+    per slice and per element, and against the closed forms these cases have."""
+    p = _edge_batch(case, dtype)
+    M = torch.empty((p.num_seqs, p.H, 128, 128), device="cuda:0")
+    o, S, _ = _run(p, transition_out=M)
+    _check(p, o, S, f"edge {case} {dtype}")
+    _check_transitions(p, M, f"edge {case} {dtype}")
+    o64, S64 = to_f64(o), to_f64(S)
+    cu = p.cu_seqlens
+    if case == "beta1":
+        # S_t^T k_t = (1 - |k|^2) (Diag(alpha) S)^T k_t + |k|^2 v_t: v_t up to the keys' norm error
+        v = p.f64("v")
+        nk = np.sum(p.f64("k") ** 2, axis=-1, keepdims=True)
+        tol = 2e-2 if dtype == "bf16" else 1e-5
+        assert np.max(np.abs(nk - 1.0)) < (1e-2 if dtype == "bf16" else 1e-6)
+        assert rel_l2(o64, v) <= tol, rel_l2(o64, v)
+    elif case.startswith("beta0"):
+        # pure channel decay: S_t = Diag(e^{b_t}) S0 and o_t = S_t^T q_t, in closed form
+        S0 = np.zeros((p.num_seqs, p.H, 128, 128)) if p.initial_state is None else p.initial_state.astype(np.float64)
+        q, g = p.f64("q"), p.f64("g")
+        o_cf = np.zeros_like(o64)
+        S_cf = np.empty_like(S64)
+        for n in range(p.num_seqs):
+            a, b = int(cu[n]), int(cu[n + 1])
+            for h in range(p.H):
+                bcum = np.cumsum(g[a:b, h], axis=0)                         # [t, d_k]
+                o_cf[a:b, h] = np.einsum("tk,kv->tv", q[a:b, h] * np.exp(bcum), S0[n, h])
+                S_cf[n, h] = np.exp(bcum[-1] if b > a else 0.0)[:, None] * S0[n, h]
+        if case == "beta0_zero_state":
+            assert torch.count_nonzero(o) == 0 and torch.count_nonzero(S) == 0
+        else:
+            check_parity(o, o_cf, TOL[dtype], packed_slices(cu, p.H), bf16_out=dtype == "bf16",
+                         tag=f"edge {case} {dtype} o vs closed form")
+            check_parity(S, S_cf, TOL[dtype], unit_slices(p.num_seqs, p.H), tag=f"edge {case} {dtype} S vs closed form")

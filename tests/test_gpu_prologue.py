@@ -8,7 +8,7 @@ from gated_delta_rule_15_amd import inputs as gen
 from oracle import kda_oracle as orc
 from oracle import kda_prologue as pro
 
-from kda_testutil import packed_to_dev, rel_l2, steps_to_dev, to_f64
+from kda_testutil import check_parity, packed_slices, packed_to_dev, rel_l2, steps_to_dev, to_f64, unit_slices
 
 pytestmark = pytest.mark.gpu
 
@@ -59,9 +59,9 @@ def test_decode_prologue_matches_oracle(dtype, l2, gate):
     torch.cuda.synchronize()
     q, k, g = _ref_inputs(b.f64("q")[:, 0], b.f64("k")[:, 0], b.f64("g")[:, 0], l2, gate)
     o_ref, S_ref = orc.decode_step(q, k, b.f64("v")[:, 0], g, b.f64("beta")[:, 0], b.f64("state"), 0.8)
-    eo, es = rel_l2(to_f64(o), o_ref), rel_l2(to_f64(d["state"]), S_ref)
-    print(f"decode prologue {dtype} l2={l2} gate={gate}: rel-L2 o={eo:.3e} S={es:.3e}")
-    assert eo <= TOL[dtype] and es <= TOL[dtype]
+    tag = f"decode prologue {dtype} l2={l2} gate={gate}"
+    check_parity(o, o_ref, TOL[dtype], unit_slices(24, 6), bf16_out=dtype == "bf16", tag=f"{tag} o")
+    check_parity(d["state"], S_ref, TOL[dtype], unit_slices(24, 6), tag=f"{tag} S")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -75,9 +75,9 @@ def test_verify_commit_prologue_matches_oracle(dtype, l2, gate):
     torch.cuda.synchronize()
     q, k, g = _ref_inputs(b.f64("q"), b.f64("k"), b.f64("g"), l2, gate)
     o_ref, S_ref = orc.verify_block(q, k, b.f64("v"), g, b.f64("beta"), b.f64("state"), b.accepted_len, 0.8)
-    eo, es = rel_l2(to_f64(o), o_ref), rel_l2(to_f64(d["state"]), S_ref)
-    print(f"verify+commit prologue {dtype} l2={l2} gate={gate}: rel-L2 o={eo:.3e} S={es:.3e}")
-    assert eo <= TOL[dtype] and es <= TOL[dtype]
+    tag = f"verify+commit prologue {dtype} l2={l2} gate={gate}"
+    check_parity(o, o_ref, TOL[dtype], unit_slices(12, 5, steps=True), bf16_out=dtype == "bf16", tag=f"{tag} o")
+    check_parity(d["state"], S_ref, TOL[dtype], unit_slices(12, 5), tag=f"{tag} S")
 
 
 @pytest.mark.parametrize("N,H", [(6, 3), (32, 12)])
@@ -132,9 +132,9 @@ def test_prefill_prologue_matches_oracle(dtype, l2, gate):
     torch.cuda.synchronize()
     q, k, g = _ref_inputs(p.f64("q"), p.f64("k"), p.f64("g"), l2, gate)
     o_ref, S_ref = orc.prefill(q, k, p.f64("v"), g, p.f64("beta"), p.cu_seqlens, p.initial_state, 0.8)
-    eo, es = rel_l2(to_f64(o), o_ref), rel_l2(to_f64(S), S_ref)
-    print(f"prefill prologue {dtype} l2={l2} gate={gate}: rel-L2 o={eo:.3e} S={es:.3e}")
-    assert eo <= TOL[dtype] and es <= TOL[dtype]
+    tag = f"prefill prologue {dtype} l2={l2} gate={gate}"
+    check_parity(o, o_ref, TOL[dtype], packed_slices(p.cu_seqlens, 3), bf16_out=dtype == "bf16", tag=f"{tag} o")
+    check_parity(S, S_ref, TOL[dtype], unit_slices(p.num_seqs, 3), tag=f"{tag} S")
 
 
 def test_prefill_prologue_wide_and_transitions():
@@ -151,11 +151,10 @@ def test_prefill_prologue_wide_and_transitions():
     torch.cuda.synchronize()
     q, k, g = _ref_inputs(p.f64("q"), p.f64("k"), p.f64("g"), True, True)
     o_ref, S_ref = orc.prefill(q, k, p.f64("v"), g, p.f64("beta"), p.cu_seqlens, p.initial_state)
-    eo, es = rel_l2(to_f64(o), o_ref), rel_l2(to_f64(S), S_ref)
     cu = p.cu_seqlens
+    check_parity(o, o_ref, 2e-3, packed_slices(cu, H), bf16_out=True, tag="prefill prologue wide o")
+    check_parity(S, S_ref, 2e-3, unit_slices(N, H), tag="prefill prologue wide S")
     M_ref = np.stack([np.stack([orc.transition(k[cu[n]:cu[n + 1], h], g[cu[n]:cu[n + 1], h],
                                                p.f64("beta")[cu[n]:cu[n + 1], h]) for h in range(H)])
                       for n in range(0, N, 5)])
-    em = rel_l2(to_f64(M)[::5], M_ref)
-    print(f"prefill prologue wide: rel-L2 o={eo:.3e} S={es:.3e} M={em:.3e}")
-    assert eo <= 2e-3 and es <= 2e-3 and em <= 2e-3
+    check_parity(to_f64(M)[::5], M_ref, 2e-3, unit_slices(M_ref.shape[0], H), tag="prefill prologue wide M")
