@@ -268,10 +268,12 @@ def _event_time_ms(run, reps, warmup):
 
 
 def bench_prefill(reps, warmup):
-    """4096 tokens x 12 heads, bf16.  Timed two ways: one kda_prefill launch over the
-    whole sequence, and the segmented driver (automatic segment length: the sequence
-    is cut so that (segment, head) units fill the GPU, then composed); the row's
-    ``ms`` is the faster of the two."""
+    """4096 tokens x 12 heads, bf16.  Timed three ways: one kda_prefill call over the
+    whole sequence on the single-kernel path, the same call on the split path (a
+    workspace: every chunk prepared in one chunk-parallel launch, then the state walk),
+    and the segmented driver (automatic segment length: the sequence is cut so that
+    (segment, head) units fill the GPU, then composed; its passes take the split path);
+    the row's ``ms`` is the fastest."""
     import numpy as np
     import torch
     from gated_delta_rule_15_amd import inputs as gen
@@ -282,7 +284,12 @@ def bench_prefill(reps, warmup):
     g, beta, cu = to_dev(p.g), to_dev(p.beta), to_dev(p.cu_seqlens)
     o = torch.empty_like(q)
     S = torch.empty((1, 12, D, D), device="cuda:0")
-    ms_kernel = _event_time_ms(lambda: kda.kda_prefill(q, k, v, g, beta, cu, o=o, final_state=S), reps, warmup)
+    cu_h = torch.from_numpy(p.cu_seqlens.copy())
+    ms_kernel = _event_time_ms(lambda: kda.kda_prefill(q, k, v, g, beta, cu, cu_h, o=o, final_state=S,
+                                                       workspace=None), reps, warmup)
+    ws = kda.kda_prefill_workspace(1, 4096, 12, q.dtype, q.device)
+    ms_split = _event_time_ms(lambda: kda.kda_prefill(q, k, v, g, beta, cu, cu_h, o=o, final_state=S,
+                                                      workspace=ws), reps, warmup)
     seg = auto_seg_len(p.cu_seqlens, 12)
     plan = plan_segments(p.cu_seqlens, seg)
     work = alloc_work(plan, 12, q.device)
@@ -291,7 +298,6 @@ def bench_prefill(reps, warmup):
     ms_seg = _event_time_ms(lambda: kda_prefill_segmented(q, k, v, g, beta, p.cu_seqlens, o=o2, final_state=S2,
                                                           plan=plan, work=work), reps, warmup)
     # checkpoints every 512 tokens (7 per sequence and head) in the single launch
-    cu_h = torch.from_numpy(p.cu_seqlens.copy())
     C = torch.empty((kda.kda_prefill_checkpoint_count(cu_h, 512), 12, D, D), device="cuda:0")
     ms_ckpt = _event_time_ms(lambda: kda.kda_prefill_checkpointed(q, k, v, g, beta, cu, cu_h, 512, o=o, final_state=S,
                                                                     checkpoints=C), reps, warmup)
@@ -299,18 +305,19 @@ def bench_prefill(reps, warmup):
     pr = gen.packed_batch(seed=3, seqlens=[4096], H=12, dtype="bf16", raw=True)
     qr, kr, gr = to_dev(pr.q, "bf16"), to_dev(pr.k, "bf16"), to_dev(pr.g)
     pro = kda.Prologue()
-    ms_pro = _event_time_ms(lambda: kda.kda_prefill(qr, kr, v, gr, beta, cu, o=o, final_state=S, prologue=pro),
-                            reps, warmup)
-    ms = min(ms_kernel, ms_seg)
+    ms_pro = _event_time_ms(lambda: kda.kda_prefill(qr, kr, v, gr, beta, cu, cu_h, o=o, final_state=S, prologue=pro,
+                                                    workspace=ws), reps, warmup)
+    paths = {"single launch": ms_kernel, "split": ms_split, "segmented": ms_seg}
+    path = min(paths, key=paths.get)
+    ms = paths[path]
     th = 4096 * 12
     flops = th * FLOP_PER_TOKEN_HEAD_PREFILL
     nbytes = th * BYTES_PER_TOKEN_HEAD_PREFILL_BF16 + 12 * STATE_BYTES
     return dict(ms=ms, tokens_per_s=4096 / (ms * 1e-3), algorithmic_tflops=flops / (ms * 1e-3) / 1e12,
                 frac_mfma_peak=flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
                 gbps=nbytes / (ms * 1e-3) / 1e9, frac_hbm_peak=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                path="segmented" if ms_seg < ms_kernel else "single launch",
-                single_launch_ms=ms_kernel, segmented_ms=ms_seg, segment_len=seg, segments=plan.n_rows,
-                single_launch_checkpoints_every_512_ms=ms_ckpt, single_launch_prologue_ms=ms_pro)
+                path=path, single_launch_ms=ms_kernel, split_ms=ms_split, segmented_ms=ms_seg, segment_len=seg,
+                segments=plan.n_rows, single_launch_checkpoints_every_512_ms=ms_ckpt, split_prologue_ms=ms_pro)
 
 
 def bench_prefill_batch(reps, warmup):
@@ -694,7 +701,8 @@ def main():
         log("prefill: 4096 tokens x 12 heads ...")
         pf = bench_prefill(reps=max(5, args.steps // 20), warmup=3)
         log(f"prefill: {pf['ms']:.3f} ms, {pf['tokens_per_s'] / 1e6:.2f} M tokens/s ({pf['path']}; single launch "
-            f"{pf['single_launch_ms']:.3f} ms, segmented x{pf['segments']} {pf['segmented_ms']:.3f} ms)")
+            f"{pf['single_launch_ms']:.3f} ms, split {pf['split_ms']:.3f} ms, segmented x{pf['segments']} "
+            f"{pf['segmented_ms']:.3f} ms)")
         rows["prefill_4096x12_bf16"] = pf
         log("prefill: 32 sequences x 4096 tokens x 12 heads ...")
         pb = bench_prefill_batch(reps=max(3, args.steps // 80), warmup=2)

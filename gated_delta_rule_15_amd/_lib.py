@@ -7,7 +7,7 @@ import threading
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
-KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP = 0, 1, 2, 3
+KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP, KDA_ERR_WORKSPACE = 0, 1, 2, 3, 4
 KDA_F32, KDA_BF16 = 0, 1
 
 # (name, restype, argtypes) for every symbol include/kda.h declares
@@ -28,6 +28,9 @@ SIGNATURES = {
     "kda_verify_commit_prologue": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_int, _P,
                                                   _P]),
     "kda_prefill": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _F, _P, _P, _P, _P, _P]),
+    "kda_prefill_workspace_size": (ctypes.c_size_t, [_I, ctypes.c_int64, _I, _I, _I, ctypes.c_int, _I]),
+    "kda_prefill_ex": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _F, _P, _P, _P, _P,
+                                      _P, _P, _P, ctypes.c_size_t, _P]),
     "kda_prefill_prologue": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _F, _P, _P,
                                             _P, _P, _P, _P]),
     "kda_prefill_ordered": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _F, _P, _P, _P,

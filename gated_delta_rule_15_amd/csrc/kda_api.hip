@@ -42,7 +42,8 @@ kda_status_t prefill_impl(const void* q, const void* k, const void* v, const flo
                           const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t H,
                           int32_t d_k, int32_t d_v, kda_dtype_t dtype, float scale, const float* initial_state,
                           float* final_state, void* o, float* transition_out, int32_t ckpt_interval,
-                          float* checkpoints, const int32_t* seq_order, const kda::Prologue* pro, void* stream) {
+                          float* checkpoints, const int32_t* seq_order, const kda::Prologue* pro, void* stream,
+                          void* workspace = nullptr, size_t workspace_bytes = 0) {
   if (num_seqs < 0 || H <= 0) return KDA_ERR_INVALID_ARG;
   if (!dims_ok(d_k, d_v) || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
   if (checkpoints && (ckpt_interval <= 0 || ckpt_interval % 64 != 0)) return KDA_ERR_INVALID_ARG;
@@ -62,6 +63,17 @@ kda_status_t prefill_impl(const void* q, const void* k, const void* v, const flo
   p.ckpt_interval = checkpoints ? ckpt_interval : 0;
   p.seq_order = seq_order;
   p.pro = pro;
+  if (workspace && !checkpoints) {
+    // the split path sizes its chunk slots from the host copy of cu_seqlens
+    if (!cu_seqlens_host) return KDA_ERR_INVALID_ARG;
+    const int64_t t_end = cu_seqlens_host[num_seqs];
+    const size_t need = kda::prefill_workspace_bytes(num_seqs, t_end, H, dtype == KDA_BF16, transition_out != nullptr);
+    if (need > 0) {
+      if (workspace_bytes < need) return KDA_ERR_WORKSPACE;
+      p.workspace = workspace;
+      p.ws_slots = kda::prefill_workspace_slots(num_seqs, t_end);
+    }
+  }
   return hip_status(kda::launch_prefill(p, dtype == KDA_BF16, static_cast<hipStream_t>(stream)));
 }
 
@@ -77,6 +89,7 @@ const char* kda_status_string(kda_status_t status) {
     case KDA_ERR_INVALID_ARG: return "invalid argument";
     case KDA_ERR_UNSUPPORTED: return "unsupported (only d_k = d_v = 128 and dtype bf16/f32)";
     case KDA_ERR_HIP: return "HIP launch failed";
+    case KDA_ERR_WORKSPACE: return "workspace too small";
   }
   return "unknown status";
 }
@@ -180,6 +193,24 @@ kda_status_t kda_verify_block_prologue(const void* q, const void* k, const void*
   if (!prologue_ok(prologue, pro)) return KDA_ERR_INVALID_ARG;
   return verify_impl(q, k, v, g, beta, state_pool, slots, N, gamma1, H, d_k, d_v, dtype, scale, o, accepted_len,
                      state_out_pool, &pro, stream);
+}
+
+size_t kda_prefill_workspace_size(int32_t num_seqs, int64_t T_total, int32_t H, int32_t d_k, int32_t d_v,
+                                  kda_dtype_t dtype, int32_t with_transitions) {
+  if (num_seqs <= 0 || T_total < 0 || H <= 0 || !dims_ok(d_k, d_v) || !dtype_ok(dtype)) return 0;
+  return kda::prefill_workspace_bytes(num_seqs, T_total, H, dtype == KDA_BF16, with_transitions != 0);
+}
+
+kda_status_t kda_prefill_ex(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                            const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t H,
+                            int32_t d_k, int32_t d_v, kda_dtype_t dtype, float scale, const float* initial_state,
+                            float* final_state, void* o, float* transition_out, const int32_t* seq_order,
+                            const kda_prologue_t* prologue, void* workspace, size_t workspace_bytes, void* stream) {
+  kda::Prologue pro;
+  if (prologue && !prologue_ok(prologue, pro)) return KDA_ERR_INVALID_ARG;
+  return prefill_impl(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, num_seqs, H, d_k, d_v, dtype, scale,
+                      initial_state, final_state, o, transition_out, 0, nullptr, seq_order, prologue ? &pro : nullptr,
+                      stream, workspace, workspace_bytes);
 }
 
 kda_status_t kda_prefill(const void* q, const void* k, const void* v, const float* g,

@@ -57,9 +57,17 @@ struct PrefillLaunch {
   int32_t ckpt_interval = 0;     // positive multiple of 64 when checkpoints is set
   const int32_t* seq_order = nullptr;  // or null: device [num_seqs], the order sequences are started in
   const Prologue* pro = nullptr;       // or null: inputs used as given
+  void* workspace = nullptr;           // or null: the split path's operand sets (prefill_workspace_bytes)
+  int64_t ws_slots = 0;                // chunk slots the workspace holds (prefill_workspace_slots)
 };
 
 hipError_t launch_prefill(const PrefillLaunch& p, bool bf16, hipStream_t stream);
+// Whether a prefill grid takes the split path when it has a workspace.
+bool prefill_split_applies(int64_t num_seqs, int64_t H, bool transitions);
+// Workspace the split path needs for tokens up to t_end (cu_seqlens[num_seqs]); 0 when the grid
+// would not take it.
+size_t prefill_workspace_bytes(int64_t num_seqs, int64_t t_end, int64_t H, bool bf16, bool transitions);
+int64_t prefill_workspace_slots(int64_t num_seqs, int64_t t_end);
 
 // ---- batch-invariant row contract (kda_contract.hip) ----------------------
 struct ContractLaunch {

@@ -50,7 +50,10 @@ constexpr int kC = 32;           // chunk length (tokens)
 // thread; PW = 8: 2 tokens x 4 channels).
 __host__ __device__ constexpr int prefill_threads(int sw, int pw) { return 64 * (sw + pw); }
 
-template <class Pol>
+// LDS layout.  NSETS operand sets (2: double-buffered between the prep and
+// state roles, or between the state walk's staging and use; 1: the prep-only
+// kernel); PREP: whether the prep scratch follows them.
+template <class Pol, int NSETS = 2, bool PREP = true>
 struct Lds {
   static constexpr int E = Pol::kElem;
   static constexpr int P = Pol::kPlanes;
@@ -78,13 +81,13 @@ struct Lds {
   static constexpr int kSetEm = kSetGamma + kD * 4;         // e^{b_mid} per channel
   static constexpr int kSetBytes = kSetEm + kD * 4;
   // prep scratch
-  static constexpr int kKc = 2 * kSetBytes;
+  static constexpr int kKc = NSETS * kSetBytes;
   static constexpr int kAop = kKc + kOpBytes;              // A_10 (beta-scaled), MFMA operand
   static constexpr int kAt = kAop + kAopBytes;             // A_II transposed, fp32: At[I][s][r]
   static constexpr int kTd = kAt + kFBytes;                // T_II column-major, fp32: Td[I][j][r]
   static constexpr int kBeta = kTd + kFBytes;              // 32 floats
   static constexpr int kNrm = kBeta + kC * 4;              // prologue: [token][prep wave][k, q] sums of squares
-  static constexpr int kBytes = kNrm + kC * 8 * 2 * 4;
+  static constexpr int kBytes = PREP ? kNrm + kC * 8 * 2 * 4 : NSETS * kSetBytes;
   static_assert(kBytes <= 160 * 1024, "LDS budget");
   static_assert(kOpRow % 16 == 0 && kKbRow % 16 == 0 && kSqRow % 16 == 0 && kSetBytes % 16 == 0, "aligned");
   static_assert(kNatRow % 8 == 0 && (E == 2 || kNatRow % 16 == 0), "aligned natural rows");
@@ -123,7 +126,25 @@ struct PrefillArgs {
   float pro_eps;
   int32_t pro_gate;         // prologue variant: g holds gate logits
   float pro_gmin;
+  char* ws;                 // split path: operand sets, [chunk slot][H] of one set each
 };
+
+// The split path's chunk slots: chunk j of sequence n lives in slot
+// (cu[n] / 32) + n + j.  Slots of different sequences never collide (a
+// sequence of L tokens has ceil(L / 32) chunks and the next one starts at
+// least that many slots later) and every slot is below cu[N] / 32 + N + 1.
+__host__ __device__ __forceinline__ int chunk_slot_base(int cu_n, int n) { return (cu_n >> 5) + n; }
+
+// Roles of one prefill kernel build.
+//   Fused: state and prep waves in one workgroup per (sequence, head, column
+//          slice), the operand sets handed over through LDS.
+//   Prep:  prep waves only, one workgroup per (chunk slot, head): builds that
+//          chunk's operand set and writes it to the workspace.
+//   State: state waves only, per (sequence, head, column slice): each chunk's
+//          operand set is staged from the workspace into LDS one chunk ahead.
+// The prep and state code is the same in every mode, so the split path (Prep,
+// then State) gives the fused path's results bit for bit.
+enum class Mode { Fused, Prep, State };
 
 // Input prologue (the KDA math-details box of the Day-0 lesson page: unit keys;
 // the log-decay bounded below by a scaled sigmoid, g_min = -5).
@@ -251,13 +272,16 @@ __device__ __forceinline__ void load_state_v(StateV<InT, JB>& sv, const PrefillA
   }
 }
 
-template <class Pol, class InT, int SW, int JB, int PW, bool CKPT, bool PRO>
+template <class Pol, class InT, int SW, int JB, int PW, bool CKPT, bool PRO, Mode MODE = Mode::Fused>
 __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(PrefillArgs a) {
   static_assert(!(CKPT && PRO), "checkpoints and the prologue are separate variants");
-  static_assert(PW == 4 || PW == 8, "prep waves");
-  constexpr int TPT = 16 / PW;  // tokens per prep thread (4 or 2)
-  constexpr int NTG = kC / TPT; // token groups per channel group (8 or 16 lanes)
-  using L = Lds<Pol>;
+  static_assert(MODE == Mode::State ? PW == 0 : (PW == 4 || PW == 8), "prep waves");
+  static_assert(MODE == Mode::Prep ? SW == 0 : SW == 4, "state waves");
+  static_assert(MODE == Mode::Fused || !CKPT, "checkpoints are written by the fused build");
+  constexpr int PWX = PW > 0 ? PW : 8;  // (role constants of a build without prep waves are unused)
+  constexpr int TPT = 16 / PWX;  // tokens per prep thread (4 or 2)
+  constexpr int NTG = kC / TPT;  // token groups per channel group (8 or 16 lanes)
+  using L = Lds<Pol, MODE == Mode::Prep ? 1 : 2, MODE != Mode::State>;
   using Frag = typename Pol::Frag;
   using Frag16 = typename Pol::Frag16;
   constexpr int E = L::E;
@@ -274,10 +298,29 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
   const int lj = lane & 15;
   const bool is_state = wave < SW;
 
-  const int slice = blockIdx.x % a.n_slices;
-  const int sh = blockIdx.x / a.n_slices;
-  const int h = sh % a.H;
-  const int seq = a.seq_order ? a.seq_order[sh / a.H] : sh / a.H;
+  int slice, h, seq, pchunk = 0;
+  if constexpr (MODE == Mode::Prep) {
+    // workgroup = (chunk slot, head); the sequence holding the slot is the last
+    // one whose first slot is at or below it (first slots increase with n)
+    slice = 0;
+    h = blockIdx.x % a.H;
+    const int slot = blockIdx.x / a.H;
+    int lo = 0, hi = a.num_seqs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (chunk_slot_base(a.cu_seqlens[mid], mid) <= slot) lo = mid;
+      else hi = mid - 1;
+    }
+    seq = lo;
+    pchunk = slot - chunk_slot_base(a.cu_seqlens[seq], seq);
+    const int len = a.cu_seqlens[seq + 1] - a.cu_seqlens[seq];
+    if (pchunk < 0 || pchunk * kC >= len) return;  // a slot between sequences
+  } else {
+    slice = blockIdx.x % a.n_slices;
+    const int sh = blockIdx.x / a.n_slices;
+    h = sh % a.H;
+    seq = a.seq_order ? a.seq_order[sh / a.H] : sh / a.H;
+  }
   if (seq < 0 || seq >= a.num_seqs) return;  // not a sequence of the batch (a bad order entry)
   const bool is_transition = slice >= a.n_value_slices;
   const int vslice = is_transition ? slice - a.n_value_slices : slice;
@@ -326,7 +369,7 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
 
   // The two roles run separate loops (so each keeps only its own values in
   // registers) with the same three barriers per step.
-  if (is_state) {
+  if constexpr (MODE != Mode::Prep) if (is_state) {
     StateV<InT, JB> sv;
     f32x4_t accR[JB][2], accO[JB][2];
     // B operand -I for the V transposition: slot e < 4 of lane group lq is
@@ -337,13 +380,47 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
       for (int e = 0; e < 4; ++e) neg_eye[e] = (4 * lq + e == lj) ? (__bf16)(-1.0f) : (__bf16)(0.0f);
     }
     Frag uf[JB];
-    // step 0: the prep waves build chunk 0; fetch chunk 0's v
+    // State build: operand sets come from the workspace, chunk c's into set
+    // c % 2, loaded into registers one step ahead and written to LDS at the
+    // end of the step that precedes their use
+    constexpr int kN16 = L::kSetBytes / 16;
+    constexpr int kStage = MODE == Mode::State ? (kN16 + 64 * SW - 1) / (64 * SW) : 1;
+    uint4 stg[kStage];
+    const int64_t slot0 = chunk_slot_base(bos, seq);
+    auto stage_load = [&](int c) {
+      const uint4* src = reinterpret_cast<const uint4*>(a.ws + ((slot0 + c) * H + h) * int64_t(L::kSetBytes));
+  #pragma unroll
+      for (int e = 0; e < kStage; ++e) {
+        const int idx = tid + 64 * SW * e;
+        if (idx < kN16) stg[e] = src[idx];
+      }
+    };
+    auto stage_store = [&](int set) {
+      uint4* dst = reinterpret_cast<uint4*>(smem + set * L::kSetBytes);
+  #pragma unroll
+      for (int e = 0; e < kStage; ++e) {
+        const int idx = tid + 64 * SW * e;
+        if (idx < kN16) dst[idx] = stg[e];
+      }
+    };
+    // step 0: the prep waves build chunk 0 (or chunk 0's set is staged); fetch chunk 0's v
     if (nch > 0) load_state_v<InT, JB>(sv, a, bos, eos - bos < kC ? eos - bos : kC, h, lq, lj, colw);
-    if constexpr (PRO) __syncthreads();  // the prep waves' chunk-0 norms
-    __syncthreads();
-    __syncthreads();
-    __syncthreads();
+    if constexpr (MODE == Mode::State) {
+      if (nch > 0) {
+        stage_load(0);
+        stage_store(0);
+      }
+      __syncthreads();
+    } else {
+      if constexpr (PRO) __syncthreads();  // the prep waves' chunk-0 norms
+      __syncthreads();
+      __syncthreads();
+      __syncthreads();
+    }
     for (int i = 1; i <= nch; ++i) {
+      if constexpr (MODE == Mode::State) {
+        if (i < nch) stage_load(i);
+      }
       // this step consumes chunk i - 1 from operand set (i - 1) % 2
       const int ts = bos + (i - 1) * kC;
       const int ns = eos - ts < kC ? eos - ts : kC;
@@ -525,20 +602,30 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
                                                         voff + ((16 * ct + e) * kD + 16 * jb) * 4, 0, 0);
           }
         }
+      if constexpr (MODE == Mode::State) {
+        if (i < nch) stage_store(i & 1);  // set i & 1 was last read in step i - 1
+      }
       __syncthreads();
     }
-  } else {
+  }
+  if constexpr (MODE != Mode::State) if (!is_state) {
+    // Prep build: one chunk, this workgroup's slot; fused: every chunk in turn
+    const int c_first = MODE == Mode::Prep ? pchunk : 0;
+    const int c_end = MODE == Mode::Prep ? pchunk + 1 : nch;
     PrepIn<InT, TPT> pin;
-    if (nch > 0) load_prep<InT, TPT>(pin, a, bos, eos - bos < kC ? eos - bos : kC, h, tg, c0, ptid, want_o);
+    if (nch > 0) {
+      const int tf = bos + c_first * kC;
+      load_prep<InT, TPT>(pin, a, tf, eos - tf < kC ? eos - tf : kC, h, tg, c0, ptid, want_o);
+    }
     if constexpr (PRO) {
       if (nch > 0) prep_prologue<InT, TPT, NTG>(pin, a, s_nrm, lane, tg, pw, want_o);
       __syncthreads();
     }
-    for (int i = 0; i < nch; ++i) {
-      // this step builds chunk i into operand set i % 2
+    for (int i = c_first; i < c_end; ++i) {
+      // this step builds chunk i into operand set i % 2 (the prep build's only set)
       const int tp = bos + i * kC;
       const int np = eos - tp < kC ? eos - tp : kC;
-      char* pset = smem + (i & 1) * L::kSetBytes;
+      char* pset = smem + (MODE == Mode::Prep ? 0 : (i & 1)) * L::kSetBytes;
       // K-bar of this chunk: computed with the other operands in phase A, split
       // and stored in phase C (the state waves first read it a step later)
       float kbv[TPT][4];
@@ -677,7 +764,7 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
             m_out[c0 + e] = emid[e];
           }
         }
-        {  // fetch chunk i + 1's inputs (clamped; unconditional so nothing waits on them)
+        if constexpr (MODE == Mode::Fused) {  // fetch chunk i + 1's inputs (clamped; unconditional so nothing waits on them)
           const int tn = bos + (i + 1 < nch ? i + 1 : nch - 1) * kC;
           load_prep<InT, TPT>(pin, a, tn, eos - tn < kC ? eos - tn : kC, h, tg, c0, ptid, want_o);
         }
@@ -841,19 +928,28 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
           }
         }
         // prologue: the next chunk's norms (its inputs arrived during this step)
-        if constexpr (PRO) {
+        if constexpr (PRO && MODE == Mode::Fused) {
           prep_prologue<InT, TPT, NTG>(pin, a, s_nrm, lane, tg, pw, want_o);
         }
       }
       __syncthreads();
     }
-    // step nch: the state waves consume the last chunk
-    __syncthreads();
-    __syncthreads();
-    __syncthreads();
+    if constexpr (MODE == Mode::Prep) {
+      // the chunk's operand set, as laid out in LDS, to its workspace slot
+      constexpr int kN16 = L::kSetBytes / 16;
+      const int64_t slot = chunk_slot_base(bos, seq) + pchunk;
+      uint4* dst = reinterpret_cast<uint4*>(a.ws + (slot * H + h) * int64_t(L::kSetBytes));
+      const uint4* src = reinterpret_cast<const uint4*>(smem);
+      for (int idx = tid; idx < kN16; idx += 64 * PW) dst[idx] = src[idx];
+    } else {
+      // step nch: the state waves consume the last chunk
+      __syncthreads();
+      __syncthreads();
+      __syncthreads();
+    }
   }
 
-  if (is_state) {
+  if constexpr (MODE != Mode::Prep) if (is_state) {
     float* const s_out = is_transition ? a.transition_out : a.final_state;
     if (s_out != nullptr) {
       float* dst = s_out + tile_base + colw + lj;
@@ -868,7 +964,35 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
 }
 
 template <class Pol, class InT, int SW, int JB, int PW>
-hipError_t launch_cfg(const PrefillLaunch& p, hipStream_t stream) {
+PrefillArgs make_args(const PrefillLaunch& p);
+
+// Split path: the prep build over every (chunk slot, head), then the state
+// build over (sequence, head, 64-column slice) reading the sets it wrote.
+template <class Pol, class InT>
+hipError_t launch_split(const PrefillLaunch& p, hipStream_t stream) {
+  PrefillArgs a = make_args<Pol, InT, 4, 1, 8>(p);
+  a.ws = static_cast<char*>(p.workspace);
+  const int64_t prep_blocks = p.ws_slots * p.H;
+  a.n_value_slices = 1;  // the prep build's one "slice" builds the set every slice reads
+  a.n_slices = 1;
+  if (p.pro)
+    hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, 0, 1, 8, false, true, Mode::Prep>), dim3(unsigned(prep_blocks)),
+                       dim3(prefill_threads(0, 8)), 0, stream, a);
+  else
+    hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, 0, 1, 8, false, false, Mode::Prep>), dim3(unsigned(prep_blocks)),
+                       dim3(prefill_threads(0, 8)), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  a.n_value_slices = kD / (16 * 4);
+  a.n_slices = a.n_value_slices * (p.transition_out ? 2 : 1);
+  const int64_t blocks = int64_t(p.num_seqs) * p.H * a.n_slices;
+  hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, 4, 1, 0, false, false, Mode::State>), dim3(unsigned(blocks)),
+                     dim3(prefill_threads(4, 0)), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <class Pol, class InT, int SW, int JB, int PW>
+PrefillArgs make_args(const PrefillLaunch& p) {
   PrefillArgs a;
   a.q = p.q; a.k = p.k; a.v = p.v; a.g = p.g; a.beta = p.beta;
   a.cu_seqlens = p.cu_seqlens;
@@ -888,6 +1012,13 @@ hipError_t launch_cfg(const PrefillLaunch& p, hipStream_t stream) {
   a.pro_eps = p.pro ? p.pro->eps : 0.0f;
   a.pro_gate = p.pro && p.pro->gate;
   a.pro_gmin = p.pro ? p.pro->g_min : 0.0f;
+  a.ws = nullptr;
+  return a;
+}
+
+template <class Pol, class InT, int SW, int JB, int PW>
+hipError_t launch_cfg(const PrefillLaunch& p, hipStream_t stream) {
+  const PrefillArgs a = make_args<Pol, InT, SW, JB, PW>(p);
   const int64_t blocks = int64_t(p.num_seqs) * p.H * a.n_slices;
   if (p.checkpoints && p.pro) return hipErrorNotSupported;
   if (p.checkpoints)
@@ -904,14 +1035,32 @@ hipError_t launch_cfg(const PrefillLaunch& p, hipStream_t stream) {
 
 }  // namespace
 
+bool prefill_split_applies(int64_t num_seqs, int64_t H, bool transitions) {
+  return num_seqs * H * (transitions ? 2 : 1) < device_cu_count();
+}
+
+size_t prefill_workspace_bytes(int64_t num_seqs, int64_t t_end, int64_t H, bool bf16, bool transitions) {
+  if (num_seqs <= 0 || !prefill_split_applies(num_seqs, H, transitions)) return 0;
+  const int64_t slots = (t_end >> 5) + num_seqs + 1;
+  const int64_t set = bf16 ? Lds<PolBF16x3>::kSetBytes : Lds<PolF32>::kSetBytes;
+  return size_t(slots * H * set);
+}
+
+int64_t prefill_workspace_slots(int64_t num_seqs, int64_t t_end) { return (t_end >> 5) + num_seqs + 1; }
+
 hipError_t launch_prefill(const PrefillLaunch& p, bool bf16, hipStream_t stream) {
   // Large grids (enough (sequence, head) work to fill the chip): 128 value
   // columns per workgroup (4 state waves x 32 columns, 4 prep waves), so each
   // chunk is prepared once per head.  Small grids: 64 value columns per
   // workgroup (4 state waves x 16 columns) and 8 prep waves, which shortens
-  // the per-chunk critical path at the cost of preparing each chunk twice.
+  // the per-chunk critical path at the cost of preparing each chunk twice;
+  // with a workspace, small grids take the split path instead: every chunk is
+  // prepared at once by a chunk-parallel launch, and the walk over the chunks
+  // runs the state waves alone.
   const int64_t units = int64_t(p.num_seqs) * p.H * (p.transition_out ? 2 : 1);
   const bool wide = units >= device_cu_count();
+  if (!wide && p.workspace != nullptr && p.checkpoints == nullptr)
+    return bf16 ? launch_split<PolBF16x3, BF16>(p, stream) : launch_split<PolF32, F32>(p, stream);
   if (bf16)
     return wide ? launch_cfg<PolBF16x3, BF16, 4, 2, 4>(p, stream) : launch_cfg<PolBF16x3, BF16, 4, 1, 8>(p, stream);
   return wide ? launch_cfg<PolF32, F32, 4, 2, 4>(p, stream) : launch_cfg<PolF32, F32, 4, 1, 8>(p, stream);

@@ -202,7 +202,7 @@ def kda_verify_commit_prologue(k, v, g, beta, state_pool, accepted_len, prologue
 
 def kda_prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host=None, initial_state=None, final_state=None,
                 o=None, transition_out=None, scale: float = 1.0, with_output: bool = True,
-                with_final_state: bool = True, prologue: Optional[Prologue] = None):
+                with_final_state: bool = True, prologue: Optional[Prologue] = None, workspace="auto"):
     """Chunked prefill of a packed ragged batch.
 
     q, k, v, g: [T, H, 128]; beta: [T, H]; cu_seqlens: int32 [N + 1] on the device
@@ -210,9 +210,35 @@ def kda_prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host=None, initial_stat
     Returns (o or None, final_state or None).  ``final_state`` may be the same
     tensor as ``initial_state`` (in-place continuation).  With ``prologue`` the call goes to
     kda_prefill_prologue (raw q, k; g may hold gate logits).
+
+    ``workspace``: "auto" allocates what ``kda_prefill_workspace_size`` asks for (nothing for a
+    grid that fills the device, without ``cu_seqlens_host``, or above AUTO_WORKSPACE_MAX), so small
+    grids take the split path (kda_prefill_ex); a device uint8 tensor is used as given; None takes
+    the single-kernel path.
     """
     return _prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, initial_state, final_state, o, transition_out,
-                    scale, with_output, with_final_state, None, prologue)
+                    scale, with_output, with_final_state, None, prologue, workspace)
+
+
+# "auto" workspaces stop here: a few long sequences on few heads would need one operand set per
+# 32-token chunk (about 2 KB per token and head); such calls run the single kernel, or go through
+# long_context.kda_prefill_segmented, which cuts them first.
+AUTO_WORKSPACE_MAX = 1 << 30
+
+
+def kda_prefill_workspace_size(num_seqs: int, T_total: int, H: int, dtype: torch.dtype,
+                               transitions: bool = False) -> int:
+    """Workspace bytes kda_prefill_ex can use (0: the call takes the single-kernel path)."""
+    code = _lib.KDA_BF16 if dtype == torch.bfloat16 else _lib.KDA_F32
+    return int(_lib.load().kda_prefill_workspace_size(int(num_seqs), int(T_total), int(H), D, D, code,
+                                                       1 if transitions else 0))
+
+
+def kda_prefill_workspace(num_seqs: int, T_total: int, H: int, dtype: torch.dtype, device,
+                          transitions: bool = False) -> Optional[torch.Tensor]:
+    """A workspace for kda_prefill(..., workspace=...) (None when the call needs none)."""
+    n = kda_prefill_workspace_size(num_seqs, T_total, H, dtype, transitions)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
 
 
 def kda_prefill_prologue(q, k, v, g, beta, cu_seqlens, prologue: Prologue, **kw):
@@ -224,17 +250,17 @@ def kda_prefill_prologue(q, k, v, g, beta, cu_seqlens, prologue: Prologue, **kw)
 
 def kda_prefill_ordered(q, k, v, g, beta, cu_seqlens, seq_order, cu_seqlens_host=None, initial_state=None,
                         final_state=None, o=None, transition_out=None, scale: float = 1.0, with_output: bool = True,
-                        with_final_state: bool = True):
+                        with_final_state: bool = True, workspace="auto"):
     """kda_prefill whose sequences are started in the order ``seq_order`` (device int32 [N], a
     permutation of 0..N-1; e.g. longest first).  Same results as kda_prefill, bit for bit."""
     if seq_order is None:
         raise ValueError("seq_order is required")
     return _prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, initial_state, final_state, o, transition_out,
-                    scale, with_output, with_final_state, seq_order, None)
+                    scale, with_output, with_final_state, seq_order, None, workspace)
 
 
 def _prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, initial_state, final_state, o, transition_out, scale,
-             with_output, with_final_state, seq_order, prologue):
+             with_output, with_final_state, seq_order, prologue, workspace="auto"):
     T, H, _ = q.shape
     dt = q.dtype
     dev = q.device
@@ -262,6 +288,30 @@ def _prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, initial_state, final
     _need(o, "o", (T, H, D), dt, dev)
     _need(transition_out, "transition_out", (N, H, D, D), torch.float32, dev)
     lib = _lib.load()
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError('workspace must be "auto", None or a device uint8 tensor')
+        workspace = None
+        if cu_seqlens_host is not None and N > 0:
+            n = kda_prefill_workspace_size(N, int(cu_seqlens_host[-1]), H, dt, transition_out is not None)
+            if 0 < n <= AUTO_WORKSPACE_MAX:
+                workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        if cu_seqlens_host is None:
+            raise ValueError("a workspace needs cu_seqlens_host")
+        if not workspace.is_cuda or workspace.device != dev or workspace.dtype != torch.uint8 \
+                or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
+        pc = prologue._c() if prologue is not None else None
+        if seq_order is not None:
+            _need(seq_order, "seq_order", (N,), torch.int32, dev)
+        _lib.check(lib.kda_prefill_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                                      _ptr(cu_seqlens_host), N, H, D, D, _dtype_code(q), float(scale),
+                                      _ptr(initial_state), _ptr(final_state), _ptr(o), _ptr(transition_out),
+                                      _ptr(seq_order), ctypes.addressof(pc) if pc is not None else None,
+                                      _ptr(workspace), workspace.numel(), _stream()),
+                   "kda_prefill_ex")
+        return o, final_state
     if prologue is not None:
         if seq_order is not None:
             raise ValueError("the prologue prefill takes no start order")

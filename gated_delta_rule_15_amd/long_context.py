@@ -109,7 +109,7 @@ def kda_prefill_segmented(q, k, v, g, beta, cu_seqlens_host, seg_len: Optional[i
     if plan is None and seg_len is None:
         seg_len = auto_seg_len(cu_host.numpy(), H)
     plan = plan or plan_segments(cu_host.numpy(), seg_len)
-    work = work or alloc_work(plan, H, dev)
+    work = work or alloc_work(plan, H, dev, q.dtype)
     if o is None:
         o = torch.empty_like(q)
     if final_state is None:
@@ -131,7 +131,7 @@ def kda_prefill_segmented(q, k, v, g, beta, cu_seqlens_host, seg_len: Optional[i
         M, St = work["M"][n], work["St"][n]
         # pass 1: fragments of segments 0 .. nseg-2
         kda.kda_prefill(q, k, v, g, beta, frag_cu_d, frag_cu_h, final_state=St, transition_out=M,
-                        with_output=False, scale=scale)
+                        with_output=False, scale=scale, workspace=work["ws1"][n])
         # compose: entry states of segments 1 .. nseg-1 (segment 0's is the sequence's own),
         # written into pass 2's rows; S_in[0] lands on row r.start, which already holds S_in0
         nf = nseg - 1
@@ -140,7 +140,7 @@ def kda_prefill_segmented(q, k, v, g, beta, cu_seqlens_host, seg_len: Optional[i
 
     # pass 2: every segment from its entry state, longest rows started first
     kda.kda_prefill_ordered(q, k, v, g, beta, work["rows_d"], work["order2"], work["rows_h"], initial_state=init2,
-                            final_state=fin2, o=o, scale=scale)
+                            final_state=fin2, o=o, scale=scale, workspace=work["ws2"])
     torch.index_select(fin2, 0, work["last_rows"], out=final_state)
     return o, final_state
 
@@ -153,8 +153,16 @@ def longest_first(rows) -> np.ndarray:
     return np.argsort(-lens, kind="stable").astype(np.int32)
 
 
-def alloc_work(plan: SegmentPlan, H: int, dev) -> dict:
+def alloc_work(plan: SegmentPlan, H: int, dev, dtype=torch.bfloat16) -> dict:
+    """Buffers of one segmented call: pass 2's entry and final states, per cut sequence its
+    fragments' transitions and states, and the split path's workspaces (one shared by the passes,
+    which run in order on one stream; none where a pass's grid fills the device)."""
     R = plan.n_rows
+    T_end = int(plan.rows[-1]) if len(plan.rows) else 0
+    sizes = [kda.kda_prefill_workspace_size(R, T_end, H, dtype)]
+    for n in plan.multi:
+        sizes.append(kda.kda_prefill_workspace_size(len(plan.row_of_seq[n]) - 1, T_end, H, dtype, transitions=True))
+    ws = torch.empty(max(sizes), dtype=torch.uint8, device=dev) if max(sizes) > 0 else None
     work = {
         "order2": torch.from_numpy(longest_first(plan.rows)).to(dev),
         "init2": torch.empty((R, H, D, D), dtype=torch.float32, device=dev),
@@ -164,12 +172,14 @@ def alloc_work(plan: SegmentPlan, H: int, dev) -> dict:
         "first_rows": torch.tensor([r.start for r in plan.row_of_seq], dtype=torch.long, device=dev),
         "last_rows": torch.tensor([r.stop - 1 for r in plan.row_of_seq], dtype=torch.long, device=dev),
         "M": {}, "St": {}, "frag_cu": {}, "frag_cu_h": {},
+        "ws2": ws if sizes[0] > 0 else None, "ws1": {},
     }
     for n in plan.multi:
         r = plan.row_of_seq[n]
         nf = len(r) - 1
         work["M"][n] = torch.empty((nf, H, D, D), dtype=torch.float32, device=dev)
         work["St"][n] = torch.empty((nf, H, D, D), dtype=torch.float32, device=dev)
+        work["ws1"][n] = ws if kda.kda_prefill_workspace_size(nf, T_end, H, dtype, transitions=True) > 0 else None
         work["frag_cu_h"][n] = torch.from_numpy(plan.rows[r.start:r.start + nf + 1].copy())
         work["frag_cu"][n] = work["frag_cu_h"][n].to(dev)
     return work

@@ -38,7 +38,8 @@ typedef enum kda_status {
   KDA_OK = 0,
   KDA_ERR_INVALID_ARG = 1, /* null pointer, bad size, inconsistent cu_seqlens_host */
   KDA_ERR_UNSUPPORTED = 2, /* d_k or d_v != 128, unknown dtype */
-  KDA_ERR_HIP = 3          /* the HIP runtime rejected a launch */
+  KDA_ERR_HIP = 3,         /* the HIP runtime rejected a launch */
+  KDA_ERR_WORKSPACE = 4    /* a workspace smaller than the call needs */
 } kda_status_t;
 
 typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
@@ -185,6 +186,45 @@ kda_status_t kda_prefill(const void* q, const void* k, const void* v, const floa
                          const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t H, int32_t d_k,
                          int32_t d_v, kda_dtype_t dtype, float scale, const float* initial_state,
                          float* final_state, void* o, float* transition_out, void* stream);
+
+/*
+ * kda_prefill_workspace_size — bytes of device workspace kda_prefill_ex can use
+ * for a call with num_seqs sequences within T_total packed tokens (every
+ * cu_seqlens value <= T_total), H heads, and transitions requested or not.
+ * 0 means the call takes the single-kernel path and needs none: that is the
+ * case when the grid, num_seqs * H (* 2 with transitions) (sequence, head)
+ * units, already fills the device's compute units.  Sizes: one operand set
+ * (66,560 bytes for bf16 inputs, 62,464 for fp32) per 32-token chunk slot and
+ * head, T_total / 32 + num_seqs + 1 slots.  Returns 0 for invalid arguments.
+ */
+size_t kda_prefill_workspace_size(int32_t num_seqs, int64_t T_total, int32_t H, int32_t d_k, int32_t d_v,
+                                  kda_dtype_t dtype, int32_t with_transitions);
+
+/*
+ * kda_prefill_ex — kda_prefill with every option: seq_order (as
+ * kda_prefill_ordered, or NULL), prologue (as kda_prefill_prologue, or NULL)
+ * and a caller-owned device workspace of workspace_bytes bytes (or NULL).
+ *
+ * With a workspace, a grid smaller than the device takes the split path
+ * (the same chunk form, "Kimi K3：架构与 SGLang Day-0 Support", KDA math box;
+ * the per-chunk factors do not depend on the state, so they are formed for all
+ * chunks at once): one launch prepares every 32-token chunk's operands (decay
+ * prefix, rescaled keys and queries, the Gram tiles and the UT factor) in
+ * parallel into the workspace, then the walk over each sequence's chunks runs
+ * only the state products.  Results are bit-identical to the single-kernel
+ * path.  The workspace then needs cu_seqlens_host (KDA_ERR_INVALID_ARG
+ * without it) and at least kda_prefill_workspace_size(...) bytes for this
+ * call's cu_seqlens_host[num_seqs] (KDA_ERR_WORKSPACE if smaller).  Its
+ * contents are scratch: nothing is kept between calls, and calls that share
+ * a workspace must not overlap.  Without a workspace, or for grids that fill
+ * the device, the call is kda_prefill's single kernel.
+ */
+kda_status_t kda_prefill_ex(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                            const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t H,
+                            int32_t d_k, int32_t d_v, kda_dtype_t dtype, float scale, const float* initial_state,
+                            float* final_state, void* o, float* transition_out, const int32_t* seq_order,
+                            const kda_prologue_t* prologue, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 /*
  * kda_prefill_prologue — kda_prefill on raw inputs: the input prologue

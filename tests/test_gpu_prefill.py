@@ -346,3 +346,68 @@ def test_prefill_edge_gates(case, dtype):
             check_parity(o, o_cf, TOL[dtype], packed_slices(cu, p.H), bf16_out=dtype == "bf16",
                          tag=f"edge {case} {dtype} o vs closed form")
             check_parity(S, S_cf, TOL[dtype], unit_slices(p.num_seqs, p.H), tag=f"edge {case} {dtype} S vs closed form")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("variant", ["plain", "transitions", "prologue", "ordered", "offset"])
+def test_split_path_bitwise_equals_fused(dtype, variant):
+    """With a workspace, a grid smaller than the device prepares every chunk in one chunk-parallel launch
+    and walks the chunks with the state waves alone; outputs, final states and transitions equal the
+    single-kernel path's bit for bit (ragged lengths, empty sequences, a batch that starts past token 0,
+    the input prologue, a start order).  Against the oracle too."""
+    from gated_delta_rule_15_amd.kda import Prologue, kda_prefill, kda_prefill_ordered, kda_prefill_workspace_size
+    lens = [300, 0, 33, 64, 1, 129, 31]
+    H = 3
+    pro = Prologue() if variant == "prologue" else None
+    p = gen.packed_batch(seed=18, seqlens=lens, H=H, dtype=dtype, init_state=[True, False] * 3 + [True],
+                         raw=variant == "prologue")
+    d = packed_to_dev(p)
+    cu_d, cu_h = d["cu_seqlens"], d["cu_seqlens_host"]
+    if variant == "offset":  # the last five sequences alone: the row set starts at token 300
+        cu_d, cu_h = cu_d[2:].contiguous(), cu_h[2:].contiguous()
+        init = d["initial_state"][2:].contiguous()
+    else:
+        init = d["initial_state"]
+    N = cu_h.shape[0] - 1
+    assert kda_prefill_workspace_size(N, p.T, H, d["q"].dtype, variant == "transitions") > 0
+    outs = []
+    for ws in (None, "auto"):
+        M = torch.full((N, H, 128, 128), 7.0, device="cuda:0") if variant == "transitions" else None
+        kw = dict(initial_state=init, transition_out=M, prologue=pro, workspace=ws)
+        if variant == "ordered":
+            order = torch.tensor(np.random.default_rng(1).permutation(N).astype(np.int32), device="cuda:0")
+            kw.pop("prologue")
+            o, S = kda_prefill_ordered(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_d, order, cu_h, **kw)
+        else:
+            o, S = kda_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_d, cu_h, **kw)
+        torch.cuda.synchronize()
+        outs.append((o, S, M))
+    (o1, S1, M1), (o2, S2, M2) = outs
+    t0 = int(cu_h[0])
+    assert torch.equal(o1[t0:].view(torch.int32 if dtype == "f32" else torch.int16),
+                       o2[t0:].view(torch.int32 if dtype == "f32" else torch.int16))
+    assert torch.equal(S1.view(torch.int32), S2.view(torch.int32))
+    if M1 is not None:
+        assert torch.equal(M1.view(torch.int32), M2.view(torch.int32))
+    if variant in ("plain", "transitions"):
+        _check(p, o2, S2, f"split path {variant} {dtype}")
+        if M2 is not None:
+            _check_transitions(p, M2, f"split path {dtype}")
+
+
+def test_split_path_workspace_errors():
+    """A workspace needs the host copy of cu_seqlens and at least the size the library asks for."""
+    from gated_delta_rule_15_amd import _lib
+    from gated_delta_rule_15_amd.kda import kda_prefill, kda_prefill_workspace_size
+    p = gen.packed_batch(seed=19, seqlens=[100, 50], H=2, dtype="bf16")
+    d = packed_to_dev(p)
+    need = kda_prefill_workspace_size(2, p.T, 2, torch.bfloat16)
+    small = torch.empty(need - 16, dtype=torch.uint8, device="cuda:0")
+    with pytest.raises(_lib.KdaError, match="workspace"):
+        kda_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], d["cu_seqlens_host"], workspace=small)
+    with pytest.raises(ValueError, match="cu_seqlens_host"):
+        kda_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], None,
+                    workspace=torch.empty(need, dtype=torch.uint8, device="cuda:0"))
+    # a grid that fills the device needs none
+    assert kda_prefill_workspace_size(256, 4096, 1, torch.bfloat16) == 0
+    assert kda_prefill_workspace_size(128, 4096, 1, torch.bfloat16, transitions=True) == 0
