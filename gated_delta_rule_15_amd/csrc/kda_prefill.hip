@@ -45,6 +45,9 @@ namespace kda {
 namespace {
 
 constexpr int kC = 32;           // chunk length (tokens)
+// s_waitcnt vmcnt(0) with the other counters left free (gfx9 encoding:
+// vmcnt[3:0] | expcnt << 4 | lgkmcnt << 8 | vmcnt[5:4] << 14)
+constexpr int kVmcnt0 = (0x7 << 4) | (0xF << 8);
 
 // SW state waves + PW prep waves (PW = 4: 4 tokens x 4 channels per prep
 // thread; PW = 8: 2 tokens x 4 channels).
@@ -92,6 +95,23 @@ struct Lds {
   static_assert(kOpRow % 16 == 0 && kKbRow % 16 == 0 && kSqRow % 16 == 0 && kSetBytes % 16 == 0, "aligned");
   static_assert(kNatRow % 8 == 0 && (E == 2 || kNatRow % 16 == 0), "aligned natural rows");
 };
+
+// Direct global-to-LDS copy of 16 bytes per lane: a wave's instruction fills
+// the 1 KiB at lds_wave_base (lane l's bytes at offset 16 l).  lds_wave_base
+// must be wave-uniform and 16-byte aligned.
+__device__ __forceinline__ void lds_dma16(const void* gsrc, char* lds_wave_base) {
+  const uint32_t la = uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(lds_wave_base)));
+  uint32_t saved;  // m0 is restored, so the asm leaves no register changed behind the compiler's back
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gsrc), "s"(la)
+      : "memory");
+}
 
 // x from lane (lane - D) of the same G-lane group, 0 for the first D lanes of
 // the group (G = 8 or 16; groups start at multiples of G).  A DPP row shift
@@ -383,33 +403,28 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
     // State build: operand sets come from the workspace, chunk c's into set
     // c % 2, loaded into registers one step ahead and written to LDS at the
     // end of the step that precedes their use
-    constexpr int kN16 = L::kSetBytes / 16;
-    constexpr int kStage = MODE == Mode::State ? (kN16 + 64 * SW - 1) / (64 * SW) : 1;
-    uint4 stg[kStage];
+    // The set is copied by direct global-to-LDS loads (16 bytes per lane, a
+    // wave's load filling one contiguous KiB), issued at the start of the step
+    // before its use and waited for (vmcnt) at that step's end, before its
+    // closing barrier; nothing passes through registers.
+    // The copies are issued as inline assembly: the compiler then places no
+    // wait of its own for them (it would have to assume that every later LDS
+    // read depends on them); the explicit vmcnt(0) at the step's end covers
+    // them, and this build issues its v loads after them, so the compiler's
+    // waits for those are not inflated either.
+    constexpr int kKiB = L::kSetBytes / 1024;
+    static_assert(MODE != Mode::State || L::kSetBytes % 1024 == 0, "sets are whole KiB");
     const int64_t slot0 = chunk_slot_base(bos, seq);
-    auto stage_load = [&](int c) {
-      const uint4* src = reinterpret_cast<const uint4*>(a.ws + ((slot0 + c) * H + h) * int64_t(L::kSetBytes));
-  #pragma unroll
-      for (int e = 0; e < kStage; ++e) {
-        const int idx = tid + 64 * SW * e;
-        if (idx < kN16) stg[e] = src[idx];
-      }
-    };
-    auto stage_store = [&](int set) {
-      uint4* dst = reinterpret_cast<uint4*>(smem + set * L::kSetBytes);
-  #pragma unroll
-      for (int e = 0; e < kStage; ++e) {
-        const int idx = tid + 64 * SW * e;
-        if (idx < kN16) dst[idx] = stg[e];
-      }
-    };
+#define KDA_STAGE_ISSUE(c, set)                                                                         \
+    {                                                                                                   \
+      const char* src_ = a.ws + ((slot0 + (c)) * H + h) * int64_t(L::kSetBytes) + lane * 16;           \
+      for (int kb = wave; kb < kKiB; kb += SW) lds_dma16(src_ + kb * 1024, smem + (set) * L::kSetBytes + kb * 1024); \
+    }
     // step 0: the prep waves build chunk 0 (or chunk 0's set is staged); fetch chunk 0's v
     if (nch > 0) load_state_v<InT, JB>(sv, a, bos, eos - bos < kC ? eos - bos : kC, h, lq, lj, colw);
     if constexpr (MODE == Mode::State) {
-      if (nch > 0) {
-        stage_load(0);
-        stage_store(0);
-      }
+      if (nch > 0) KDA_STAGE_ISSUE(0, 0)
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);
       __syncthreads();
     } else {
       if constexpr (PRO) __syncthreads();  // the prep waves' chunk-0 norms
@@ -419,7 +434,7 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
     }
     for (int i = 1; i <= nch; ++i) {
       if constexpr (MODE == Mode::State) {
-        if (i < nch) stage_load(i);
+        if (i < nch) KDA_STAGE_ISSUE(i, i & 1)  // set i & 1 was last read in step i - 1
       }
       // this step consumes chunk i - 1 from operand set (i - 1) % 2
       const int ts = bos + (i - 1) * kC;
@@ -446,6 +461,10 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
               }
               accO[jb][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             }
+          if constexpr (MODE == Mode::State) {  // fetch chunk i's v now that chunk i - 1's is consumed
+            const int tv = bos + (i < nch ? i : nch - 1) * kC;
+            load_state_v<InT, JB>(sv, a, tv, eos - tv < kC ? eos - tv : kC, h, lq, lj, colw);
+          }
           // the chunk's operands are referenced at b_mid: carry S as e^{b_mid} S
           // (rows = key channels); phase C applies e^{b_last - b_mid}
           {
@@ -573,7 +592,7 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
                 for (int jb = 0; jb < JB; ++jb) Pol::mma_part(S[jb][4 * half + c], fb[c], uf[jb], p);
           }
         }
-        {  // fetch chunk i's v (clamped to the last chunk; unconditional so nothing waits on it)
+        if constexpr (MODE != Mode::State) {  // fetch chunk i's v (clamped to the last chunk; unconditional so nothing waits on it)
           const int tv = bos + (i < nch ? i : nch - 1) * kC;
           load_state_v<InT, JB>(sv, a, tv, eos - tv < kC ? eos - tv : kC, h, lq, lj, colw);
         }
@@ -603,7 +622,7 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
           }
         }
       if constexpr (MODE == Mode::State) {
-        if (i < nch) stage_store(i & 1);  // set i & 1 was last read in step i - 1
+        __builtin_amdgcn_s_waitcnt(kVmcnt0);  // this wave's copies of chunk i's set have landed
       }
       __syncthreads();
     }
