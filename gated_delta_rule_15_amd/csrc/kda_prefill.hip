@@ -133,6 +133,8 @@ struct PrefillArgs {
   int32_t H;
   int32_t n_value_slices;  // 128 / (16 * JB * SW)
   int32_t n_slices;        // value slices (+ as many transition slices)
+  int32_t slice_base;      // first slice this launch covers
+  int32_t n_launch_slices; // slices per (sequence, head) this launch covers
   float scale;
   const float* initial_state;
   float* final_state;
@@ -292,7 +294,12 @@ __device__ __forceinline__ void load_state_v(StateV<InT, JB>& sv, const PrefillA
   }
 }
 
-template <class Pol, class InT, int SW, int JB, int PW, bool CKPT, bool PRO, Mode MODE = Mode::Fused>
+// WO: every workgroup of the launch writes outputs (value slices with o set);
+// otherwise none does.  A compile-time property so the output products carry
+// no branch inside the MFMA sequences (a runtime test there made the compiler
+// move accumulators out and back around every conditional MFMA).  The prep
+// build reads it from the arguments.
+template <class Pol, class InT, int SW, int JB, int PW, bool CKPT, bool PRO, Mode MODE, bool WO>
 __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(PrefillArgs a) {
   static_assert(!(CKPT && PRO), "checkpoints and the prologue are separate variants");
   static_assert(MODE == Mode::State ? PW == 0 : (PW == 4 || PW == 8), "prep waves");
@@ -336,8 +343,8 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
     const int len = a.cu_seqlens[seq + 1] - a.cu_seqlens[seq];
     if (pchunk < 0 || pchunk * kC >= len) return;  // a slot between sequences
   } else {
-    slice = blockIdx.x % a.n_slices;
-    const int sh = blockIdx.x / a.n_slices;
+    slice = a.slice_base + int(blockIdx.x % unsigned(a.n_launch_slices));
+    const int sh = blockIdx.x / unsigned(a.n_launch_slices);
     h = sh % a.H;
     seq = a.seq_order ? a.seq_order[sh / a.H] : sh / a.H;
   }
@@ -349,7 +356,7 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
   const int bos = a.cu_seqlens[seq];
   const int eos = a.cu_seqlens[seq + 1];
   const int nch = (eos - bos + kC - 1) / kC;
-  const bool want_o = !is_transition && a.o != nullptr;
+  const bool want_o = MODE == Mode::Prep ? a.o != nullptr : WO;
 
   // state-wave roles
   const int colw = vslice * (16 * JB * SW) + (is_state ? wave : 0) * (16 * JB);
@@ -987,6 +994,24 @@ PrefillArgs make_args(const PrefillLaunch& p);
 
 // Split path: the prep build over every (chunk slot, head), then the state
 // build over (sequence, head, 64-column slice) reading the sets it wrote.
+// The state launches of one call: value slices with outputs (WO), and value
+// slices without outputs or transition slices (!WO); one launch when the
+// call has only one kind.
+template <class K>
+hipError_t launch_slices(PrefillArgs a, const PrefillLaunch& p, K&& kernel) {
+  const int nv = a.n_value_slices;
+  auto go = [&](bool wo, int base, int count) {
+    a.slice_base = base;
+    a.n_launch_slices = count;
+    kernel(wo, a, dim3(unsigned(int64_t(p.num_seqs) * p.H * count)));
+    return hipGetLastError();
+  };
+  if (p.o == nullptr) return go(false, 0, a.n_slices);
+  const hipError_t e = go(true, 0, nv);
+  if (e != hipSuccess || p.transition_out == nullptr) return e;
+  return go(false, nv, nv);
+}
+
 template <class Pol, class InT>
 hipError_t launch_split(const PrefillLaunch& p, hipStream_t stream) {
   PrefillArgs a = make_args<Pol, InT, 4, 1, 8>(p);
@@ -994,20 +1019,26 @@ hipError_t launch_split(const PrefillLaunch& p, hipStream_t stream) {
   const int64_t prep_blocks = p.ws_slots * p.H;
   a.n_value_slices = 1;  // the prep build's one "slice" builds the set every slice reads
   a.n_slices = 1;
+  a.slice_base = 0;
+  a.n_launch_slices = 1;
   if (p.pro)
-    hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, 0, 1, 8, false, true, Mode::Prep>), dim3(unsigned(prep_blocks)),
-                       dim3(prefill_threads(0, 8)), 0, stream, a);
+    hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, 0, 1, 8, false, true, Mode::Prep, false>),
+                       dim3(unsigned(prep_blocks)), dim3(prefill_threads(0, 8)), 0, stream, a);
   else
-    hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, 0, 1, 8, false, false, Mode::Prep>), dim3(unsigned(prep_blocks)),
-                       dim3(prefill_threads(0, 8)), 0, stream, a);
+    hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, 0, 1, 8, false, false, Mode::Prep, false>),
+                       dim3(unsigned(prep_blocks)), dim3(prefill_threads(0, 8)), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   a.n_value_slices = kD / (16 * 4);
   a.n_slices = a.n_value_slices * (p.transition_out ? 2 : 1);
-  const int64_t blocks = int64_t(p.num_seqs) * p.H * a.n_slices;
-  hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, 4, 1, 0, false, false, Mode::State>), dim3(unsigned(blocks)),
-                     dim3(prefill_threads(4, 0)), 0, stream, a);
-  return hipGetLastError();
+  return launch_slices(a, p, [&](bool wo, const PrefillArgs& la, dim3 grid) {
+    if (wo)
+      hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, 4, 1, 0, false, false, Mode::State, true>), grid,
+                         dim3(prefill_threads(4, 0)), 0, stream, la);
+    else
+      hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, 4, 1, 0, false, false, Mode::State, false>), grid,
+                         dim3(prefill_threads(4, 0)), 0, stream, la);
+  });
 }
 
 template <class Pol, class InT, int SW, int JB, int PW>
@@ -1032,24 +1063,30 @@ PrefillArgs make_args(const PrefillLaunch& p) {
   a.pro_gate = p.pro && p.pro->gate;
   a.pro_gmin = p.pro ? p.pro->g_min : 0.0f;
   a.ws = nullptr;
+  a.slice_base = 0;
+  a.n_launch_slices = a.n_slices;
   return a;
+}
+
+template <class Pol, class InT, int SW, int JB, int PW, bool CKPT, bool PRO>
+void launch_fused(bool wo, const PrefillArgs& a, dim3 grid, hipStream_t stream) {
+  if (wo)
+    hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, SW, JB, PW, CKPT, PRO, Mode::Fused, true>), grid,
+                       dim3(prefill_threads(SW, PW)), 0, stream, a);
+  else
+    hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, SW, JB, PW, CKPT, PRO, Mode::Fused, false>), grid,
+                       dim3(prefill_threads(SW, PW)), 0, stream, a);
 }
 
 template <class Pol, class InT, int SW, int JB, int PW>
 hipError_t launch_cfg(const PrefillLaunch& p, hipStream_t stream) {
   const PrefillArgs a = make_args<Pol, InT, SW, JB, PW>(p);
-  const int64_t blocks = int64_t(p.num_seqs) * p.H * a.n_slices;
   if (p.checkpoints && p.pro) return hipErrorNotSupported;
-  if (p.checkpoints)
-    hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, SW, JB, PW, true, false>), dim3(unsigned(blocks)),
-                       dim3(prefill_threads(SW, PW)), 0, stream, a);
-  else if (p.pro)
-    hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, SW, JB, PW, false, true>), dim3(unsigned(blocks)),
-                       dim3(prefill_threads(SW, PW)), 0, stream, a);
-  else
-    hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, SW, JB, PW, false, false>), dim3(unsigned(blocks)),
-                       dim3(prefill_threads(SW, PW)), 0, stream, a);
-  return hipGetLastError();
+  return launch_slices(a, p, [&](bool wo, const PrefillArgs& la, dim3 grid) {
+    if (p.checkpoints) launch_fused<Pol, InT, SW, JB, PW, true, false>(wo, la, grid, stream);
+    else if (p.pro) launch_fused<Pol, InT, SW, JB, PW, false, true>(wo, la, grid, stream);
+    else launch_fused<Pol, InT, SW, JB, PW, false, false>(wo, la, grid, stream);
+  });
 }
 
 }  // namespace
