@@ -297,6 +297,10 @@ def bench_prefill(reps, warmup):
     S2 = torch.empty_like(S)
     ms_seg = _event_time_ms(lambda: kda_prefill_segmented(q, k, v, g, beta, p.cu_seqlens, o=o2, final_state=S2,
                                                           plan=plan, work=work), reps, warmup)
+    work_s = alloc_work(plan, 12, q.device, split=True)
+    ms_seg_split = _event_time_ms(lambda: kda_prefill_segmented(q, k, v, g, beta, p.cu_seqlens, o=o2, final_state=S2,
+                                                                plan=plan, work=work_s), reps, warmup)
+    del work_s
     # checkpoints every 512 tokens (7 per sequence and head) in the single launch
     C = torch.empty((kda.kda_prefill_checkpoint_count(cu_h, 512), 12, D, D), device="cuda:0")
     ms_ckpt = _event_time_ms(lambda: kda.kda_prefill_checkpointed(q, k, v, g, beta, cu, cu_h, 512, o=o, final_state=S,
@@ -307,7 +311,7 @@ def bench_prefill(reps, warmup):
     pro = kda.Prologue()
     ms_pro = _event_time_ms(lambda: kda.kda_prefill(qr, kr, v, gr, beta, cu, cu_h, o=o, final_state=S, prologue=pro,
                                                     workspace=ws), reps, warmup)
-    paths = {"single launch": ms_kernel, "split": ms_split, "segmented": ms_seg}
+    paths = {"single launch": ms_kernel, "split": ms_split, "segmented": ms_seg, "segmented, split passes": ms_seg_split}
     path = min(paths, key=paths.get)
     ms = paths[path]
     th = 4096 * 12
@@ -316,7 +320,8 @@ def bench_prefill(reps, warmup):
     return dict(ms=ms, tokens_per_s=4096 / (ms * 1e-3), algorithmic_tflops=flops / (ms * 1e-3) / 1e12,
                 frac_mfma_peak=flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
                 gbps=nbytes / (ms * 1e-3) / 1e9, frac_hbm_peak=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                path=path, single_launch_ms=ms_kernel, split_ms=ms_split, segmented_ms=ms_seg, segment_len=seg,
+                path=path, single_launch_ms=ms_kernel, split_ms=ms_split, segmented_ms=ms_seg,
+                segmented_split_passes_ms=ms_seg_split, segment_len=seg,
                 segments=plan.n_rows, single_launch_checkpoints_every_512_ms=ms_ckpt, split_prologue_ms=ms_pro)
 
 

@@ -45,9 +45,6 @@ namespace kda {
 namespace {
 
 constexpr int kC = 32;           // chunk length (tokens)
-// s_waitcnt vmcnt(0) with the other counters left free (gfx9 encoding:
-// vmcnt[3:0] | expcnt << 4 | lgkmcnt << 8 | vmcnt[5:4] << 14)
-constexpr int kVmcnt0 = (0x7 << 4) | (0xF << 8);
 
 // SW state waves + PW prep waves (PW = 4: 4 tokens x 4 channels per prep
 // thread; PW = 8: 2 tokens x 4 channels).
@@ -95,23 +92,6 @@ struct Lds {
   static_assert(kOpRow % 16 == 0 && kKbRow % 16 == 0 && kSqRow % 16 == 0 && kSetBytes % 16 == 0, "aligned");
   static_assert(kNatRow % 8 == 0 && (E == 2 || kNatRow % 16 == 0), "aligned natural rows");
 };
-
-// Direct global-to-LDS copy of 16 bytes per lane: a wave's instruction fills
-// the 1 KiB at lds_wave_base (lane l's bytes at offset 16 l).  lds_wave_base
-// must be wave-uniform and 16-byte aligned.
-__device__ __forceinline__ void lds_dma16(const void* gsrc, char* lds_wave_base) {
-  const uint32_t la = uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(lds_wave_base)));
-  uint32_t saved;  // m0 is restored, so the asm leaves no register changed behind the compiler's back
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(gsrc), "s"(la)
-      : "memory");
-}
 
 // x from lane (lane - D) of the same G-lane group, 0 for the first D lanes of
 // the group (G = 8 or 16; groups start at multiples of G).  A DPP row shift
@@ -410,28 +390,43 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
     // State build: operand sets come from the workspace, chunk c's into set
     // c % 2, loaded into registers one step ahead and written to LDS at the
     // end of the step that precedes their use
-    // The set is copied by direct global-to-LDS loads (16 bytes per lane, a
-    // wave's load filling one contiguous KiB), issued at the start of the step
-    // before its use and waited for (vmcnt) at that step's end, before its
-    // closing barrier; nothing passes through registers.
-    // The copies are issued as inline assembly: the compiler then places no
-    // wait of its own for them (it would have to assume that every later LDS
-    // read depends on them); the explicit vmcnt(0) at the step's end covers
-    // them, and this build issues its v loads after them, so the compiler's
-    // waits for those are not inflated either.
-    constexpr int kKiB = L::kSetBytes / 1024;
-    static_assert(MODE != Mode::State || L::kSetBytes % 1024 == 0, "sets are whole KiB");
+    // The set is copied through registers: seventeen 16-byte loads per thread,
+    // issued at the start of the step before its use (their latency hides
+    // under the step), written to LDS at that step's end, before its closing
+    // barrier.  (Direct global-to-LDS loads were measured to hold the issuing
+    // wave ~110 cycles each; seventeen named registers rather than an array,
+    // which the compiler had placed in scratch memory.)
+    constexpr int kN16 = L::kSetBytes / 16;
+    static_assert(MODE != Mode::State || (kN16 + 64 * SW - 1) / (64 * SW) <= 17, "seventeen staging registers");
     const int64_t slot0 = chunk_slot_base(bos, seq);
-#define KDA_STAGE_ISSUE(c, set)                                                                         \
-    {                                                                                                   \
-      const char* src_ = a.ws + ((slot0 + (c)) * H + h) * int64_t(L::kSetBytes) + lane * 16;           \
-      for (int kb = wave; kb < kKiB; kb += SW) lds_dma16(src_ + kb * 1024, smem + (set) * L::kSetBytes + kb * 1024); \
+#define KDA_REP17(X) X(0) X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14) X(15) X(16)
+#define KDA_STG_DECL(e) uint4 stg##e;
+#define KDA_STG_LD(e) stg##e = src_[tid + 64 * SW * (e) < kN16 ? tid + 64 * SW * (e) : kN16 - 1];
+#define KDA_STG_ST(e) if (tid + 64 * SW * (e) < kN16) dst_[tid + 64 * SW * (e)] = stg##e;
+    KDA_REP17(KDA_STG_DECL)
+    // (the loads are unconditional, chunk index clamped to the last chunk, so
+    // the compiler's wait for the v loads before them is not widened over a
+    // branch that skips them)
+#define KDA_STAGE_LOAD(c)                                                                               \
+    if constexpr (MODE == Mode::State) {                                                                \
+      const int64_t c_ = (c) < nch ? (c) : nch - 1;                                                     \
+      const uint4* src_ = reinterpret_cast<const uint4*>(a.ws + ((slot0 + c_) * H + h) * int64_t(L::kSetBytes)); \
+      KDA_REP17(KDA_STG_LD)                                                                             \
+    }
+#define KDA_STAGE_STORE(c, set)                                                                         \
+    if constexpr (MODE == Mode::State) {                                                                \
+      if ((c) < nch) {                                                                                  \
+        uint4* dst_ = reinterpret_cast<uint4*>(smem + (set) * L::kSetBytes);                            \
+        KDA_REP17(KDA_STG_ST)                                                                           \
+      }                                                                                                 \
     }
     // step 0: the prep waves build chunk 0 (or chunk 0's set is staged); fetch chunk 0's v
     if (nch > 0) load_state_v<InT, JB>(sv, a, bos, eos - bos < kC ? eos - bos : kC, h, lq, lj, colw);
     if constexpr (MODE == Mode::State) {
-      if (nch > 0) KDA_STAGE_ISSUE(0, 0)
-      __builtin_amdgcn_s_waitcnt(kVmcnt0);
+      if (nch > 0) {
+        KDA_STAGE_LOAD(0)
+        KDA_STAGE_STORE(0, 0)
+      }
       __syncthreads();
     } else {
       if constexpr (PRO) __syncthreads();  // the prep waves' chunk-0 norms
@@ -441,7 +436,7 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
     }
     for (int i = 1; i <= nch; ++i) {
       if constexpr (MODE == Mode::State) {
-        if (i < nch) KDA_STAGE_ISSUE(i, i & 1)  // set i & 1 was last read in step i - 1
+        KDA_STAGE_LOAD(i)  // chunk i's set, for set i & 1 (last read in step i - 1)
       }
       // this step consumes chunk i - 1 from operand set (i - 1) % 2
       const int ts = bos + (i - 1) * kC;
@@ -487,6 +482,18 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
           }
           // R = V - Kh S (accumulated as Kh S - V) and O = Qh S; each 32-row
           // block of S is split once and feeds both products
+          // (state build: every fragment of the four steps is read up front,
+          // so the LDS latency is paid once per chunk, not once per step)
+          constexpr int kPre = MODE == Mode::State ? 4 : 1;
+          Frag fk[kPre][2], fq[kPre][2];
+  #pragma unroll
+          for (int ks = 0; ks < kPre; ++ks)
+  #pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+              const int off = (16 * rt + lj) * L::kOpRow + (32 * ks + 8 * lq) * E;
+              fk[ks][rt] = Pol::load(sset + L::kSetKh, L::kOpPlane, off);
+              if (want_o) fq[ks][rt] = Pol::load(sset + L::kSetQh, L::kOpPlane, off);
+            }
   #pragma unroll
           for (int ks = 0; ks < 4; ++ks) {
             Frag sf[JB];
@@ -497,12 +504,14 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
                                    S[jb][2 * ks + 1][3]};
               sf[jb] = Pol::make(v8);
             }
-            const int koff = (32 * ks + 8 * lq) * E;
-            Frag fk[2], fq[2];
+            const int kk = kPre == 4 ? ks : 0;
+            if constexpr (kPre == 1) {
   #pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-              fk[rt] = Pol::load(sset + L::kSetKh, L::kOpPlane, (16 * rt + lj) * L::kOpRow + koff);
-              if (want_o) fq[rt] = Pol::load(sset + L::kSetQh, L::kOpPlane, (16 * rt + lj) * L::kOpRow + koff);
+              for (int rt = 0; rt < 2; ++rt) {
+                const int off = (16 * rt + lj) * L::kOpRow + (32 * ks + 8 * lq) * E;
+                fk[0][rt] = Pol::load(sset + L::kSetKh, L::kOpPlane, off);
+                if (want_o) fq[0][rt] = Pol::load(sset + L::kSetQh, L::kOpPlane, off);
+              }
             }
   #pragma unroll
             for (int p = 0; p < Pol::kParts; ++p)
@@ -510,12 +519,14 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
               for (int rt = 0; rt < 2; ++rt)
   #pragma unroll
                 for (int jb = 0; jb < JB; ++jb) {
-                  Pol::mma_part(accR[jb][rt], fk[rt], sf[jb], p);
-                  if (want_o) Pol::mma_part(accO[jb][rt], fq[rt], sf[jb], p);
+                  Pol::mma_part(accR[jb][rt], fk[kk][rt], sf[jb], p);
+                  if (want_o) Pol::mma_part(accO[jb][rt], fq[kk][rt], sf[jb], p);
                 }
           }
         }
-      __syncthreads();
+      // (the state build's set was complete when the step began and each wave
+      // works on its own columns: it needs no barrier inside the step)
+      if constexpr (MODE != Mode::State) __syncthreads();
       // ============================== phase B ==============================
         {
           // U = T' R (one 32-deep step), then O += P U and the outputs
@@ -573,30 +584,32 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
                 }
           }
         }
-      __syncthreads();
+      if constexpr (MODE != Mode::State) __syncthreads();
       // ============================== phase C ==============================
         {
-          // S = Gamma S + Kb^T U, in two halves of four row tiles
+          // S = Gamma S + Kb^T U, in two halves of four row tiles (one pass of
+          // eight in the state build, whose registers allow it)
           const float* s_gamma = reinterpret_cast<const float*>(sset + L::kSetGamma);
+          constexpr int kCt = MODE == Mode::State ? 8 : 4;
   #pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            Frag fb[4];
+          for (int half = 0; half < 8 / kCt; ++half) {
+            Frag fb[kCt];
   #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const int ct = 4 * half + c;
+            for (int c = 0; c < kCt; ++c) {
+              const int ct = kCt * half + c;
+              fb[c] = Pol::load(sset + L::kSetKb, L::kKbPlane, (16 * ct + lj) * L::kKbRow + 8 * lq * E);
               const float4 gm = *reinterpret_cast<const float4*>(s_gamma + 16 * ct + 4 * lq);
   #pragma unroll
               for (int jb = 0; jb < JB; ++jb) {
                 S[jb][ct][0] *= gm.x; S[jb][ct][1] *= gm.y; S[jb][ct][2] *= gm.z; S[jb][ct][3] *= gm.w;
               }
-              fb[c] = Pol::load(sset + L::kSetKb, L::kKbPlane, (16 * ct + lj) * L::kKbRow + 8 * lq * E);
             }
   #pragma unroll
             for (int p = 0; p < Pol::kParts; ++p)
   #pragma unroll
-              for (int c = 0; c < 4; ++c)
+              for (int c = 0; c < kCt; ++c)
   #pragma unroll
-                for (int jb = 0; jb < JB; ++jb) Pol::mma_part(S[jb][4 * half + c], fb[c], uf[jb], p);
+                for (int jb = 0; jb < JB; ++jb) Pol::mma_part(S[jb][kCt * half + c], fb[c], uf[jb], p);
           }
         }
         if constexpr (MODE != Mode::State) {  // fetch chunk i's v (clamped to the last chunk; unconditional so nothing waits on it)
@@ -629,7 +642,7 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
           }
         }
       if constexpr (MODE == Mode::State) {
-        __builtin_amdgcn_s_waitcnt(kVmcnt0);  // this wave's copies of chunk i's set have landed
+        KDA_STAGE_STORE(i, i & 1)
       }
       __syncthreads();
     }
@@ -902,7 +915,7 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
           }
         }
       }
-      __syncthreads();
+      if constexpr (MODE != Mode::State) __syncthreads();
       // ============================== phase C ==============================
       {
         if (pw == 0) {
@@ -1012,6 +1025,12 @@ hipError_t launch_slices(PrefillArgs a, const PrefillLaunch& p, K&& kernel) {
   return go(false, nv, nv);
 }
 
+// Value column tiles (16 columns each) per state wave in the split path's walk.
+// One: the walk is bound by each wave's product sequence, not by the staging
+// (two tiles, one workgroup per head, measured 8.7k against 5.8k cycles per
+// chunk).
+constexpr int kSplitJB = 1;
+
 template <class Pol, class InT>
 hipError_t launch_split(const PrefillLaunch& p, hipStream_t stream) {
   PrefillArgs a = make_args<Pol, InT, 4, 1, 8>(p);
@@ -1029,14 +1048,14 @@ hipError_t launch_split(const PrefillLaunch& p, hipStream_t stream) {
                        dim3(unsigned(prep_blocks)), dim3(prefill_threads(0, 8)), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  a.n_value_slices = kD / (16 * 4);
+  a.n_value_slices = kD / (16 * kSplitJB * 4);
   a.n_slices = a.n_value_slices * (p.transition_out ? 2 : 1);
   return launch_slices(a, p, [&](bool wo, const PrefillArgs& la, dim3 grid) {
     if (wo)
-      hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, 4, 1, 0, false, false, Mode::State, true>), grid,
+      hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, 4, kSplitJB, 0, false, false, Mode::State, true>), grid,
                          dim3(prefill_threads(4, 0)), 0, stream, la);
     else
-      hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, 4, 1, 0, false, false, Mode::State, false>), grid,
+      hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, 4, kSplitJB, 0, false, false, Mode::State, false>), grid,
                          dim3(prefill_threads(4, 0)), 0, stream, la);
   });
 }

@@ -153,15 +153,17 @@ def longest_first(rows) -> np.ndarray:
     return np.argsort(-lens, kind="stable").astype(np.int32)
 
 
-def alloc_work(plan: SegmentPlan, H: int, dev, dtype=torch.bfloat16) -> dict:
-    """Buffers of one segmented call: pass 2's entry and final states, per cut sequence its
-    fragments' transitions and states, and the split path's workspaces (one shared by the passes,
-    which run in order on one stream; none where a pass's grid fills the device)."""
+def alloc_work(plan: SegmentPlan, H: int, dev, dtype=torch.bfloat16, split: bool = False) -> dict:
+    """Buffers of one segmented call: pass 2's entry and final states, and per cut sequence its
+    fragments' transitions and states.  ``split``: also the split path's workspace (one, shared
+    by the passes, which run in order on one stream; none where a pass's grid fills the device),
+    so that passes on small grids take the split path instead of the single kernel."""
     R = plan.n_rows
     T_end = int(plan.rows[-1]) if len(plan.rows) else 0
-    sizes = [kda.kda_prefill_workspace_size(R, T_end, H, dtype)]
+    sizes = [kda.kda_prefill_workspace_size(R, T_end, H, dtype) if split else 0]
     for n in plan.multi:
-        sizes.append(kda.kda_prefill_workspace_size(len(plan.row_of_seq[n]) - 1, T_end, H, dtype, transitions=True))
+        sizes.append(kda.kda_prefill_workspace_size(len(plan.row_of_seq[n]) - 1, T_end, H, dtype, transitions=True)
+                     if split else 0)
     ws = torch.empty(max(sizes), dtype=torch.uint8, device=dev) if max(sizes) > 0 else None
     work = {
         "order2": torch.from_numpy(longest_first(plan.rows)).to(dev),
@@ -179,7 +181,8 @@ def alloc_work(plan: SegmentPlan, H: int, dev, dtype=torch.bfloat16) -> dict:
         nf = len(r) - 1
         work["M"][n] = torch.empty((nf, H, D, D), dtype=torch.float32, device=dev)
         work["St"][n] = torch.empty((nf, H, D, D), dtype=torch.float32, device=dev)
-        work["ws1"][n] = ws if kda.kda_prefill_workspace_size(nf, T_end, H, dtype, transitions=True) > 0 else None
+        work["ws1"][n] = ws if split and kda.kda_prefill_workspace_size(nf, T_end, H, dtype, transitions=True) > 0 \
+            else None
         work["frag_cu_h"][n] = torch.from_numpy(plan.rows[r.start:r.start + nf + 1].copy())
         work["frag_cu"][n] = work["frag_cu_h"][n].to(dev)
     return work
