@@ -4,6 +4,16 @@
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
+#include <mutex>
+
+// Scratch of the allocation-free prefill (kda_prefill_noalloc): the split
+// path's operand sets.  One copy per device, held from the library's load on
+// that device until the process ends; every call on a device shares it.  Host
+// code never uses this name as an address: the device address is looked up
+// once per device (scratch_on_current_device) and passed to the kernels.
+constexpr size_t kScratchBytes = size_t(128) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
 namespace {
 
 constexpr int kVersion = 100;  // 0.1.0
@@ -23,6 +33,24 @@ bool prologue_ok(const kda_prologue_t* p, kda::Prologue& out) {
   if (out.l2norm && !(out.eps >= 0.0f && out.eps <= 3.0e38f)) return false;   // finite, >= 0 (NaN fails)
   if (out.gate && !(out.g_min < 0.0f && out.g_min >= -3.0e38f)) return false;  // finite, < 0
   return true;
+}
+
+// The device address of `scratch` on the current device, looked up with that
+// device current the first time a call runs on it; nullptr if the lookup fails.
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_ptr[kMaxDevices] = {};
+
+void* scratch_on_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    scratch_ptr[dev] = ptr;
+  }
+  return scratch_ptr[dev];
 }
 
 }  // namespace
@@ -212,6 +240,25 @@ kda_status_t kda_prefill_ex(const void* q, const void* k, const void* v, const f
                       initial_state, final_state, o, transition_out, 0, nullptr, seq_order, prologue ? &pro : nullptr,
                       stream, workspace, workspace_bytes);
 }
+
+kda_status_t kda_prefill_noalloc(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                                 const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                 int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t dtype, float scale,
+                                 const float* initial_state, float* final_state, void* o, float* transition_out,
+                                 const int32_t* seq_order, const kda_prologue_t* prologue, void* stream) {
+  kda::Prologue pro;
+  if (prologue && !prologue_ok(prologue, pro)) return KDA_ERR_INVALID_ARG;
+  void* ws = nullptr;
+  if (cu_seqlens_host && num_seqs > 0 && H > 0) {
+    ws = scratch_on_current_device();
+    if (!ws) return KDA_ERR_HIP;
+  }
+  return prefill_impl(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, num_seqs, H, d_k, d_v, dtype, scale,
+                      initial_state, final_state, o, transition_out, 0, nullptr, seq_order, prologue ? &pro : nullptr,
+                      stream, ws, ws ? kScratchBytes : 0);
+}
+
+size_t kda_prefill_noalloc_max_scratch(void) { return kScratchBytes; }
 
 kda_status_t kda_prefill(const void* q, const void* k, const void* v, const float* g,
                          const float* beta, const int32_t* cu_seqlens,

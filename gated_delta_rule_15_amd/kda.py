@@ -241,6 +241,38 @@ def kda_prefill_workspace(num_seqs: int, T_total: int, H: int, dtype: torch.dtyp
     return torch.empty(n, dtype=torch.uint8, device=device) if n else None
 
 
+def kda_prefill_noalloc(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, o=None, final_state=None, initial_state=None,
+                        transition_out=None, scale: float = 1.0, seq_order=None, prologue: Optional[Prologue] = None):
+    """kda_prefill_noalloc: the prefill without any allocation, the split path's workspace being the
+    library's per-device scratch (kda_prefill_noalloc_max_scratch() bytes).  Outputs are written only
+    into the buffers passed (o [T, H, 128], final_state / transition_out [N, H, 128, 128]; None skips
+    one); this wrapper allocates nothing either.  Calls that overlap on one device race on the scratch."""
+    T, H, _ = q.shape
+    dt, dev = q.dtype, q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, (T, H, D), dt, dev)
+    _need(g, "g", (T, H, D), torch.float32, dev)
+    _need(beta, "beta", (T, H), torch.float32, dev)
+    N = cu_seqlens.shape[0] - 1
+    _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    if cu_seqlens_host is not None and (cu_seqlens_host.is_cuda or cu_seqlens_host.dtype != torch.int32
+                                        or cu_seqlens_host.shape != cu_seqlens.shape
+                                        or not cu_seqlens_host.is_contiguous()):
+        raise ValueError("cu_seqlens_host must be a contiguous CPU int32 copy of cu_seqlens")
+    for name, t in (("initial_state", initial_state), ("final_state", final_state),
+                    ("transition_out", transition_out)):
+        _need(t, name, (N, H, D, D), torch.float32, dev)
+    _need(o, "o", (T, H, D), dt, dev)
+    if seq_order is not None:
+        _need(seq_order, "seq_order", (N,), torch.int32, dev)
+    pc = prologue._c() if prologue is not None else None
+    _lib.check(_lib.load().kda_prefill_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), _ptr(cu_seqlens_host), N, H, D, D,
+        _dtype_code(q), float(scale), _ptr(initial_state), _ptr(final_state), _ptr(o), _ptr(transition_out),
+        _ptr(seq_order), ctypes.addressof(pc) if pc is not None else None, _stream()), "kda_prefill_noalloc")
+    return o, final_state
+
+
 def kda_prefill_prologue(q, k, v, g, beta, cu_seqlens, prologue: Prologue, **kw):
     """kda_prefill with the input prologue (required)."""
     if prologue is None:

@@ -227,6 +227,34 @@ kda_status_t kda_prefill_ex(const void* q, const void* k, const void* v, const f
                             void* stream);
 
 /*
+ * kda_prefill_noalloc — kda_prefill_ex for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * device allocation): the same arguments without the workspace, which is
+ * instead a scratch array the library holds on each device (allocated when
+ * the library is loaded on it, kept until the process ends; its size is
+ * kda_prefill_noalloc_max_scratch(), 128 MiB).  The call allocates and frees
+ * nothing, host or device.  A call whose split path would need more than that
+ * (more than about 128 MiB / (66,560 * H) chunk slots of 32 tokens, e.g.
+ * 4,096 tokens x 12 heads uses 104 MB) returns KDA_ERR_WORKSPACE; grids that
+ * fill the device, and calls without cu_seqlens_host, need no scratch and run
+ * the single kernel.  Results are bit-identical to kda_prefill_ex's.
+ * Every call on one device shares that device's scratch and finds the last
+ * call's contents in it (nothing needs clearing: each call writes every part
+ * it reads first), so calls that overlap in time on one device — on
+ * different streams, or from different host threads — race; serialise them.
+ * The first call on a device looks the array's address up (hipGetSymbolAddress)
+ * and KDA_ERR_HIP reports a failed lookup.
+ */
+kda_status_t kda_prefill_noalloc(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                                 const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                 int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t dtype, float scale,
+                                 const float* initial_state, float* final_state, void* o, float* transition_out,
+                                 const int32_t* seq_order, const kda_prologue_t* prologue, void* stream);
+
+/* Bytes of the per-device scratch kda_prefill_noalloc uses (the largest workspace it can serve). */
+size_t kda_prefill_noalloc_max_scratch(void);
+
+/*
  * kda_prefill_prologue — kda_prefill on raw inputs: the input prologue
  * (kda_prologue_t above) is applied to q, k and g of every token before the
  * chunk computation.  Same arguments and results as kda_prefill, plus
