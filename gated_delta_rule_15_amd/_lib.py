@@ -9,6 +9,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
 KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP, KDA_ERR_WORKSPACE = 0, 1, 2, 3, 4
 KDA_F32, KDA_BF16 = 0, 1
+KDA_WS_PREPARED, KDA_WS_KEEP_OUTPUT_OPERANDS = 1, 2
 
 # (name, restype, argtypes) for every symbol include/kda.h declares
 _P = ctypes.c_void_p
@@ -33,7 +34,7 @@ SIGNATURES = {
                                            _P, _P, _P, _P]),
     "kda_prefill_noalloc_max_scratch": (ctypes.c_size_t, []),
     "kda_prefill_ex": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _F, _P, _P, _P, _P,
-                                      _P, _P, _P, ctypes.c_size_t, _P]),
+                                      _P, _P, _P, ctypes.c_size_t, _I, _P]),
     "kda_prefill_prologue": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _F, _P, _P,
                                             _P, _P, _P, _P]),
     "kda_prefill_ordered": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _F, _P, _P, _P,

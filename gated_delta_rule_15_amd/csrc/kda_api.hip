@@ -71,7 +71,8 @@ kda_status_t prefill_impl(const void* q, const void* k, const void* v, const flo
                           int32_t d_k, int32_t d_v, kda_dtype_t dtype, float scale, const float* initial_state,
                           float* final_state, void* o, float* transition_out, int32_t ckpt_interval,
                           float* checkpoints, const int32_t* seq_order, const kda::Prologue* pro, void* stream,
-                          void* workspace = nullptr, size_t workspace_bytes = 0) {
+                          void* workspace = nullptr, size_t workspace_bytes = 0, int32_t ws_flags = 0) {
+  if (ws_flags & ~(KDA_WS_PREPARED | KDA_WS_KEEP_OUTPUT_OPERANDS)) return KDA_ERR_INVALID_ARG;
   if (num_seqs < 0 || H <= 0) return KDA_ERR_INVALID_ARG;
   if (!dims_ok(d_k, d_v) || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
   if (checkpoints && (ckpt_interval <= 0 || ckpt_interval % 64 != 0)) return KDA_ERR_INVALID_ARG;
@@ -100,6 +101,8 @@ kda_status_t prefill_impl(const void* q, const void* k, const void* v, const flo
       if (workspace_bytes < need) return KDA_ERR_WORKSPACE;
       p.workspace = workspace;
       p.ws_slots = kda::prefill_workspace_slots(num_seqs, t_end);
+      p.ws_prepared = (ws_flags & KDA_WS_PREPARED) != 0;
+      p.ws_keep_output_operands = (ws_flags & KDA_WS_KEEP_OUTPUT_OPERANDS) != 0;
     }
   }
   return hip_status(kda::launch_prefill(p, dtype == KDA_BF16, static_cast<hipStream_t>(stream)));
@@ -233,12 +236,13 @@ kda_status_t kda_prefill_ex(const void* q, const void* k, const void* v, const f
                             const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t H,
                             int32_t d_k, int32_t d_v, kda_dtype_t dtype, float scale, const float* initial_state,
                             float* final_state, void* o, float* transition_out, const int32_t* seq_order,
-                            const kda_prologue_t* prologue, void* workspace, size_t workspace_bytes, void* stream) {
+                            const kda_prologue_t* prologue, void* workspace, size_t workspace_bytes,
+                            int32_t ws_flags, void* stream) {
   kda::Prologue pro;
   if (prologue && !prologue_ok(prologue, pro)) return KDA_ERR_INVALID_ARG;
   return prefill_impl(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, num_seqs, H, d_k, d_v, dtype, scale,
                       initial_state, final_state, o, transition_out, 0, nullptr, seq_order, prologue ? &pro : nullptr,
-                      stream, workspace, workspace_bytes);
+                      stream, workspace, workspace_bytes, ws_flags);
 }
 
 kda_status_t kda_prefill_noalloc(const void* q, const void* k, const void* v, const float* g, const float* beta,

@@ -59,6 +59,8 @@ struct PrefillLaunch {
   const Prologue* pro = nullptr;       // or null: inputs used as given
   void* workspace = nullptr;           // or null: the split path's operand sets (prefill_workspace_bytes)
   int64_t ws_slots = 0;                // chunk slots the workspace holds (prefill_workspace_slots)
+  bool ws_prepared = false;            // the workspace holds these rows' operand sets already
+  bool ws_keep_output_operands = false;  // prepare the output operands even without outputs
 };
 
 hipError_t launch_prefill(const PrefillLaunch& p, bool bf16, hipStream_t stream);

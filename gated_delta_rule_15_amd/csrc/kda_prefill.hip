@@ -71,23 +71,26 @@ struct Lds {
   static constexpr int kAopBytes = P * kAopPlane;
   static constexpr int kFLd = 20;                          // fp32 [2 blocks][16][20]
   static constexpr int kFBytes = 2 * 16 * kFLd * 4;
-  // one operand set (read by the state waves)
+  // one operand set (read by the state waves); Kb^T last, so that the prep
+  // build, which writes it straight to the workspace, keeps only the rest
   static constexpr int kSetKh = 0;
   static constexpr int kSetQh = kSetKh + kOpBytes;
-  static constexpr int kSetKb = kSetQh + kOpBytes;
-  static constexpr int kSetTp = kSetKb + kKbBytes;
+  static constexpr int kSetTp = kSetQh + kOpBytes;
   static constexpr int kSetP = kSetTp + kSqBytes;
   static constexpr int kSetGamma = kSetP + kSqBytes;       // e^{b_last - b_mid} per channel
   static constexpr int kSetEm = kSetGamma + kD * 4;         // e^{b_mid} per channel
-  static constexpr int kSetBytes = kSetEm + kD * 4;
+  static constexpr int kSetKb = kSetEm + kD * 4;
+  static constexpr int kSetBytes = kSetKb + kKbBytes;
+  static constexpr int kSetInLds = NSETS == 1 ? kSetKb : kSetBytes;  // prep build: the set without Kb^T
   // prep scratch
-  static constexpr int kKc = NSETS * kSetBytes;
+  static constexpr int kKc = NSETS * kSetInLds;
   static constexpr int kAop = kKc + kOpBytes;              // A_10 (beta-scaled), MFMA operand
   static constexpr int kAt = kAop + kAopBytes;             // A_II transposed, fp32: At[I][s][r]
   static constexpr int kTd = kAt + kFBytes;                // T_II column-major, fp32: Td[I][j][r]
   static constexpr int kBeta = kTd + kFBytes;              // 32 floats
   static constexpr int kNrm = kBeta + kC * 4;              // prologue: [token][prep wave][k, q] sums of squares
   static constexpr int kBytes = PREP ? kNrm + kC * 8 * 2 * 4 : NSETS * kSetBytes;
+  static_assert(kSetKb % 16 == 0, "aligned");
   static_assert(kBytes <= 160 * 1024, "LDS budget");
   static_assert(kOpRow % 16 == 0 && kKbRow % 16 == 0 && kSqRow % 16 == 0 && kSetBytes % 16 == 0, "aligned");
   static_assert(kNatRow % 8 == 0 && (E == 2 || kNatRow % 16 == 0), "aligned natural rows");
@@ -129,6 +132,7 @@ struct PrefillArgs {
   int32_t pro_gate;         // prologue variant: g holds gate logits
   float pro_gmin;
   char* ws;                 // split path: operand sets, [chunk slot][H] of one set each
+  int32_t prep_outputs;     // prep build: also build the output operands (Qh, P)
 };
 
 // The split path's chunk slots: chunk j of sequence n lives in slot
@@ -336,7 +340,7 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
   const int bos = a.cu_seqlens[seq];
   const int eos = a.cu_seqlens[seq + 1];
   const int nch = (eos - bos + kC - 1) / kC;
-  const bool want_o = MODE == Mode::Prep ? a.o != nullptr : WO;
+  const bool want_o = MODE == Mode::Prep ? a.prep_outputs != 0 : WO;
 
   // state-wave roles
   const int colw = vslice * (16 * JB * SW) + (is_state ? wave : 0) * (16 * JB);
@@ -955,15 +959,19 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
             if (I == 0) Pol::store1(pset + L::kSetTp, L::kSqPlane, r * L::kSqRow + kperm(16 + lj) * E, 0.0f);
           }
         }
-        // K-bar^T of this chunk (every prep thread, its own tokens and channels)
+        // K-bar^T of this chunk (every prep thread, its own tokens and channels);
+        // the prep build writes it straight into the chunk's workspace set
+        char* kb_set = pset;
+        if constexpr (MODE == Mode::Prep)
+          kb_set = a.ws + ((chunk_slot_base(bos, seq) + int64_t(pchunk)) * H + h) * int64_t(L::kSetBytes);
   #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int off = (c0 + e) * L::kKbRow + kperm(TPT * tg) * E;
           if constexpr (TPT == 4) {
             const float w4[4] = {kbv[0][e], kbv[1][e], kbv[2][e], kbv[3][e]};
-            Pol::store4(pset + L::kSetKb, L::kKbPlane, off, w4);
+            Pol::store4(kb_set + L::kSetKb, L::kKbPlane, off, w4);
           } else {
-            Pol::store2(pset + L::kSetKb, L::kKbPlane, off, kbv[0][e], kbv[1][e]);
+            Pol::store2(kb_set + L::kSetKb, L::kKbPlane, off, kbv[0][e], kbv[1][e]);
           }
         }
         // prologue: the next chunk's norms (its inputs arrived during this step)
@@ -975,7 +983,8 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
     }
     if constexpr (MODE == Mode::Prep) {
       // the chunk's operand set, as laid out in LDS, to its workspace slot
-      constexpr int kN16 = L::kSetBytes / 16;
+      // (all of it but Kb^T, already there)
+      constexpr int kN16 = L::kSetInLds / 16;
       const int64_t slot = chunk_slot_base(bos, seq) + pchunk;
       uint4* dst = reinterpret_cast<uint4*>(a.ws + (slot * H + h) * int64_t(L::kSetBytes));
       const uint4* src = reinterpret_cast<const uint4*>(smem);
@@ -1040,7 +1049,10 @@ hipError_t launch_split(const PrefillLaunch& p, hipStream_t stream) {
   a.n_slices = 1;
   a.slice_base = 0;
   a.n_launch_slices = 1;
-  if (p.pro)
+  a.prep_outputs = (p.o != nullptr || p.ws_keep_output_operands) ? 1 : 0;
+  if (p.ws_prepared) {
+    // the sets are in the workspace already
+  } else if (p.pro)
     hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, 0, 1, 8, false, true, Mode::Prep, false>),
                        dim3(unsigned(prep_blocks)), dim3(prefill_threads(0, 8)), 0, stream, a);
   else
@@ -1082,6 +1094,7 @@ PrefillArgs make_args(const PrefillLaunch& p) {
   a.pro_gate = p.pro && p.pro->gate;
   a.pro_gmin = p.pro ? p.pro->g_min : 0.0f;
   a.ws = nullptr;
+  a.prep_outputs = 0;
   a.slice_base = 0;
   a.n_launch_slices = a.n_slices;
   return a;

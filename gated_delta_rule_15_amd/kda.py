@@ -202,7 +202,8 @@ def kda_verify_commit_prologue(k, v, g, beta, state_pool, accepted_len, prologue
 
 def kda_prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host=None, initial_state=None, final_state=None,
                 o=None, transition_out=None, scale: float = 1.0, with_output: bool = True,
-                with_final_state: bool = True, prologue: Optional[Prologue] = None, workspace="auto"):
+                with_final_state: bool = True, prologue: Optional[Prologue] = None, workspace="auto",
+                ws_flags: int = 0):
     """Chunked prefill of a packed ragged batch.
 
     q, k, v, g: [T, H, 128]; beta: [T, H]; cu_seqlens: int32 [N + 1] on the device
@@ -214,10 +215,11 @@ def kda_prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host=None, initial_stat
     ``workspace``: "auto" allocates what ``kda_prefill_workspace_size`` asks for (nothing for a
     grid that fills the device, without ``cu_seqlens_host``, or above AUTO_WORKSPACE_MAX), so small
     grids take the split path (kda_prefill_ex); a device uint8 tensor is used as given; None takes
-    the single-kernel path.
+    the single-kernel path.  ``ws_flags``: KDA_WS_PREPARED / KDA_WS_KEEP_OUTPUT_OPERANDS of kda_prefill_ex, for
+    two calls over the same rows that share one workspace preparation.
     """
     return _prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, initial_state, final_state, o, transition_out,
-                    scale, with_output, with_final_state, None, prologue, workspace)
+                    scale, with_output, with_final_state, None, prologue, workspace, ws_flags)
 
 
 # "auto" workspaces stop here: a few long sequences on few heads would need one operand set per
@@ -282,17 +284,17 @@ def kda_prefill_prologue(q, k, v, g, beta, cu_seqlens, prologue: Prologue, **kw)
 
 def kda_prefill_ordered(q, k, v, g, beta, cu_seqlens, seq_order, cu_seqlens_host=None, initial_state=None,
                         final_state=None, o=None, transition_out=None, scale: float = 1.0, with_output: bool = True,
-                        with_final_state: bool = True, workspace="auto"):
+                        with_final_state: bool = True, workspace="auto", ws_flags: int = 0):
     """kda_prefill whose sequences are started in the order ``seq_order`` (device int32 [N], a
     permutation of 0..N-1; e.g. longest first).  Same results as kda_prefill, bit for bit."""
     if seq_order is None:
         raise ValueError("seq_order is required")
     return _prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, initial_state, final_state, o, transition_out,
-                    scale, with_output, with_final_state, seq_order, None, workspace)
+                    scale, with_output, with_final_state, seq_order, None, workspace, ws_flags)
 
 
 def _prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, initial_state, final_state, o, transition_out, scale,
-             with_output, with_final_state, seq_order, prologue, workspace="auto"):
+             with_output, with_final_state, seq_order, prologue, workspace="auto", ws_flags: int = 0):
     T, H, _ = q.shape
     dt = q.dtype
     dev = q.device
@@ -341,7 +343,7 @@ def _prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, initial_state, final
                                       _ptr(cu_seqlens_host), N, H, D, D, _dtype_code(q), float(scale),
                                       _ptr(initial_state), _ptr(final_state), _ptr(o), _ptr(transition_out),
                                       _ptr(seq_order), ctypes.addressof(pc) if pc is not None else None,
-                                      _ptr(workspace), workspace.numel(), _stream()),
+                                      _ptr(workspace), workspace.numel(), int(ws_flags), _stream()),
                    "kda_prefill_ex")
         return o, final_state
     if prologue is not None:

@@ -31,7 +31,7 @@ from typing import List, Optional
 import numpy as np
 import torch
 
-from . import kda
+from . import _lib, kda
 
 D = 128
 
@@ -123,24 +123,32 @@ def kda_prefill_segmented(q, k, v, g, beta, cu_seqlens_host, seg_len: Optional[i
     else:
         init2.index_fill_(0, first_rows, 0.0)
 
+    ws = work["ws"]
+    if ws is not None:
+        # split path: pass 1 runs over every row (the rows it does not need cost little on a grid
+        # this small), so both passes walk the same chunks and share one preparation
+        kda.kda_prefill(q, k, v, g, beta, work["rows_d"], work["rows_h"], final_state=work["St_all"],
+                        transition_out=work["M_all"], with_output=False, scale=scale, workspace=ws,
+                        ws_flags=_lib.KDA_WS_KEEP_OUTPUT_OPERANDS)
     for n in plan.multi:
         r = plan.row_of_seq[n]
-        nseg = len(r)
-        frag_cu_h = work["frag_cu_h"][n]
-        frag_cu_d = work["frag_cu"][n]
-        M, St = work["M"][n], work["St"][n]
-        # pass 1: fragments of segments 0 .. nseg-2
-        kda.kda_prefill(q, k, v, g, beta, frag_cu_d, frag_cu_h, final_state=St, transition_out=M,
-                        with_output=False, scale=scale, workspace=work["ws1"][n])
-        # compose: entry states of segments 1 .. nseg-1 (segment 0's is the sequence's own),
+        nf = len(r) - 1
+        if ws is not None:
+            M, St = work["M_all"][r.start:r.start + nf], work["St_all"][r.start:r.start + nf]
+        else:
+            # pass 1: fragments of segments 0 .. nf-1
+            M, St = work["M"][n], work["St"][n]
+            kda.kda_prefill(q, k, v, g, beta, work["frag_cu"][n], work["frag_cu_h"][n], final_state=St,
+                            transition_out=M, with_output=False, scale=scale, workspace=None)
+        # compose: entry states of segments 1 .. nf (segment 0's is the sequence's own),
         # written into pass 2's rows; S_in[0] lands on row r.start, which already holds S_in0
-        nf = nseg - 1
         kda.kda_compose_segments(M, St, init2[r.start], S_in=init2[r.start:r.start + nf],
                                  S_final=init2[r.start + nf])
 
     # pass 2: every segment from its entry state, longest rows started first
     kda.kda_prefill_ordered(q, k, v, g, beta, work["rows_d"], work["order2"], work["rows_h"], initial_state=init2,
-                            final_state=fin2, o=o, scale=scale, workspace=work["ws2"])
+                            final_state=fin2, o=o, scale=scale, workspace=ws,
+                            ws_flags=_lib.KDA_WS_PREPARED if ws is not None else 0)
     torch.index_select(fin2, 0, work["last_rows"], out=final_state)
     return o, final_state
 
@@ -155,16 +163,13 @@ def longest_first(rows) -> np.ndarray:
 
 def alloc_work(plan: SegmentPlan, H: int, dev, dtype=torch.bfloat16, split: bool = False) -> dict:
     """Buffers of one segmented call: pass 2's entry and final states, and per cut sequence its
-    fragments' transitions and states.  ``split``: also the split path's workspace (one, shared
-    by the passes, which run in order on one stream; none where a pass's grid fills the device),
-    so that passes on small grids take the split path instead of the single kernel."""
+    fragments' transitions and states.  ``split``: when the passes' grids are small enough for
+    the split path, its workspace instead (one preparation serves both passes) and every row's
+    transition and state for a pass 1 over all rows."""
     R = plan.n_rows
     T_end = int(plan.rows[-1]) if len(plan.rows) else 0
-    sizes = [kda.kda_prefill_workspace_size(R, T_end, H, dtype) if split else 0]
-    for n in plan.multi:
-        sizes.append(kda.kda_prefill_workspace_size(len(plan.row_of_seq[n]) - 1, T_end, H, dtype, transitions=True)
-                     if split else 0)
-    ws = torch.empty(max(sizes), dtype=torch.uint8, device=dev) if max(sizes) > 0 else None
+    n_ws = kda.kda_prefill_workspace_size(R, T_end, H, dtype, transitions=True) if split else 0
+    ws = torch.empty(n_ws, dtype=torch.uint8, device=dev) if n_ws > 0 else None
     work = {
         "order2": torch.from_numpy(longest_first(plan.rows)).to(dev),
         "init2": torch.empty((R, H, D, D), dtype=torch.float32, device=dev),
@@ -173,16 +178,17 @@ def alloc_work(plan: SegmentPlan, H: int, dev, dtype=torch.bfloat16, split: bool
         "rows_h": torch.from_numpy(plan.rows.copy()),
         "first_rows": torch.tensor([r.start for r in plan.row_of_seq], dtype=torch.long, device=dev),
         "last_rows": torch.tensor([r.stop - 1 for r in plan.row_of_seq], dtype=torch.long, device=dev),
-        "M": {}, "St": {}, "frag_cu": {}, "frag_cu_h": {},
-        "ws2": ws if sizes[0] > 0 else None, "ws1": {},
+        "M": {}, "St": {}, "frag_cu": {}, "frag_cu_h": {}, "ws": ws,
     }
+    if ws is not None:
+        work["M_all"] = torch.empty((R, H, D, D), dtype=torch.float32, device=dev)
+        work["St_all"] = torch.empty((R, H, D, D), dtype=torch.float32, device=dev)
+        return work
     for n in plan.multi:
         r = plan.row_of_seq[n]
         nf = len(r) - 1
         work["M"][n] = torch.empty((nf, H, D, D), dtype=torch.float32, device=dev)
         work["St"][n] = torch.empty((nf, H, D, D), dtype=torch.float32, device=dev)
-        work["ws1"][n] = ws if split and kda.kda_prefill_workspace_size(nf, T_end, H, dtype, transitions=True) > 0 \
-            else None
         work["frag_cu_h"][n] = torch.from_numpy(plan.rows[r.start:r.start + nf + 1].copy())
         work["frag_cu"][n] = work["frag_cu_h"][n].to(dev)
     return work

@@ -224,7 +224,26 @@ kda_status_t kda_prefill_ex(const void* q, const void* k, const void* v, const f
                             int32_t d_k, int32_t d_v, kda_dtype_t dtype, float scale, const float* initial_state,
                             float* final_state, void* o, float* transition_out, const int32_t* seq_order,
                             const kda_prologue_t* prologue, void* workspace, size_t workspace_bytes,
-                            void* stream);
+                            int32_t ws_flags, void* stream);
+
+/* ws_flags of kda_prefill_ex (0 for a self-contained call).  They let two
+ * calls over the same rows share one preparation, as the two passes of a
+ * segmented prefill do (their state walks differ; the chunks' operands do
+ * not):
+ *   KDA_WS_KEEP_OUTPUT_OPERANDS  prepare the output operands (rescaled queries,
+ *                                the query-key Gram tiles) even though this
+ *                                call writes no outputs, so that a later
+ *                                KDA_WS_PREPARED call can;
+ *   KDA_WS_PREPARED              skip the preparation: the workspace holds the
+ *                                operand sets an earlier split-path call wrote
+ *                                for the same q, k, g, beta, cu_seqlens,
+ *                                prologue and scale (with outputs'
+ *                                operands if this call writes outputs), and
+ *                                nothing has overwritten it since.  The
+ *                                library cannot check this precondition.
+ * Both only matter on the split path; KDA_ERR_INVALID_ARG for other bits. */
+#define KDA_WS_PREPARED 1
+#define KDA_WS_KEEP_OUTPUT_OPERANDS 2
 
 /*
  * kda_prefill_noalloc — kda_prefill_ex for callers that cannot allocate
