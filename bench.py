@@ -278,7 +278,8 @@ def bench_prefill(reps, warmup):
     import torch
     from gated_delta_rule_15_amd import inputs as gen
     from gated_delta_rule_15_amd import kda
-    from gated_delta_rule_15_amd.long_context import alloc_work, auto_seg_len, kda_prefill_segmented, plan_segments
+    from gated_delta_rule_15_amd.long_context import (alloc_work, auto_seg_len, auto_seg_len_split,
+                                                      kda_prefill_segmented, plan_segments)
     p = gen.packed_batch(seed=3, seqlens=[4096], H=12, dtype="bf16")
     q, k, v = to_dev(p.q, "bf16"), to_dev(p.k, "bf16"), to_dev(p.v, "bf16")
     g, beta, cu = to_dev(p.g), to_dev(p.beta), to_dev(p.cu_seqlens)
@@ -297,9 +298,11 @@ def bench_prefill(reps, warmup):
     S2 = torch.empty_like(S)
     ms_seg = _event_time_ms(lambda: kda_prefill_segmented(q, k, v, g, beta, p.cu_seqlens, o=o2, final_state=S2,
                                                           plan=plan, work=work), reps, warmup)
-    work_s = alloc_work(plan, 12, q.device, split=True)
+    seg_s = auto_seg_len_split(p.cu_seqlens, 12)
+    plan_s = plan_segments(p.cu_seqlens, seg_s)
+    work_s = alloc_work(plan_s, 12, q.device, split=True)
     ms_seg_split = _event_time_ms(lambda: kda_prefill_segmented(q, k, v, g, beta, p.cu_seqlens, o=o2, final_state=S2,
-                                                                plan=plan, work=work_s), reps, warmup)
+                                                                plan=plan_s, work=work_s), reps, warmup)
     del work_s
     # checkpoints every 512 tokens (7 per sequence and head) in the single launch
     C = torch.empty((kda.kda_prefill_checkpoint_count(cu_h, 512), 12, D, D), device="cuda:0")
@@ -321,7 +324,7 @@ def bench_prefill(reps, warmup):
                 frac_mfma_peak=flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
                 gbps=nbytes / (ms * 1e-3) / 1e9, frac_hbm_peak=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                 path=path, single_launch_ms=ms_kernel, split_ms=ms_split, segmented_ms=ms_seg,
-                segmented_split_passes_ms=ms_seg_split, segment_len=seg,
+                segmented_split_passes_ms=ms_seg_split, segment_len_split_passes=seg_s, segment_len=seg,
                 segments=plan.n_rows, single_launch_checkpoints_every_512_ms=ms_ckpt, split_prologue_ms=ms_pro)
 
 

@@ -10,6 +10,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP, KDA_ERR_WORKSPACE = 0, 1, 2, 3, 4
 KDA_F32, KDA_BF16 = 0, 1
 KDA_WS_PREPARED, KDA_WS_KEEP_OUTPUT_OPERANDS = 1, 2
+KDA_PREFILL_TRANSITIONS, KDA_PREFILL_NO_OUTPUT = 1, 2
 
 # (name, restype, argtypes) for every symbol include/kda.h declares
 _P = ctypes.c_void_p

@@ -96,7 +96,8 @@ kda_status_t prefill_impl(const void* q, const void* k, const void* v, const flo
     // the split path sizes its chunk slots from the host copy of cu_seqlens
     if (!cu_seqlens_host) return KDA_ERR_INVALID_ARG;
     const int64_t t_end = cu_seqlens_host[num_seqs];
-    const size_t need = kda::prefill_workspace_bytes(num_seqs, t_end, H, dtype == KDA_BF16, transition_out != nullptr);
+    const size_t need = kda::prefill_workspace_bytes(num_seqs, t_end, H, dtype == KDA_BF16, transition_out != nullptr,
+                                                     o != nullptr);
     if (need > 0) {
       if (workspace_bytes < need) return KDA_ERR_WORKSPACE;
       p.workspace = workspace;
@@ -227,9 +228,11 @@ kda_status_t kda_verify_block_prologue(const void* q, const void* k, const void*
 }
 
 size_t kda_prefill_workspace_size(int32_t num_seqs, int64_t T_total, int32_t H, int32_t d_k, int32_t d_v,
-                                  kda_dtype_t dtype, int32_t with_transitions) {
+                                  kda_dtype_t dtype, int32_t flags) {
   if (num_seqs <= 0 || T_total < 0 || H <= 0 || !dims_ok(d_k, d_v) || !dtype_ok(dtype)) return 0;
-  return kda::prefill_workspace_bytes(num_seqs, T_total, H, dtype == KDA_BF16, with_transitions != 0);
+  if (flags & ~(KDA_PREFILL_TRANSITIONS | KDA_PREFILL_NO_OUTPUT)) return 0;
+  return kda::prefill_workspace_bytes(num_seqs, T_total, H, dtype == KDA_BF16, (flags & KDA_PREFILL_TRANSITIONS) != 0,
+                                      (flags & KDA_PREFILL_NO_OUTPUT) == 0);
 }
 
 kda_status_t kda_prefill_ex(const void* q, const void* k, const void* v, const float* g, const float* beta,

@@ -10,14 +10,15 @@
 // S_in(i) and of S~(i)), so a workgroup owns one (head, 16-column slice) and
 // runs the scan serially over segments.  Each step is a 128 x 128 x 16 fp32
 // product on fp32 MFMA (v_mfma_f32_16x16x4_f32, exact products, fp32
-// accumulation): wave w computes output rows 32w .. 32w+31 as two 16 x 16
-// tiles.  The contraction index of lane group q at step s is k = 32q + s, so
-// a lane streams 32 contiguous floats of its M row (global) and of its column
-// of the running state, which is kept transposed in LDS.  Two accumulator
-// chains per tile (even and odd s) halve the dependent MFMA latency; their sum
-// is taken in a fixed order, so results are deterministic.  The next
-// segment's M rows and S~ values are fetched into a second register set while
-// the current product runs.
+// accumulation): wave w of eight computes output rows 16w .. 16w+15 as one
+// 16 x 16 tile.  Lane group q takes the contraction indices k = 16j + 4q + e
+// (j = 0..7, e = 0..3), so one load of the four groups covers 64 contiguous
+// bytes of an M row; the running state is kept transposed in LDS.  Two
+// accumulator chains per tile (even and odd e) halve the dependent MFMA
+// latency; their sum is taken in a fixed order, so results are deterministic.
+// The next two segments' M rows and S~ values are in flight in two further
+// register sets while the current product runs (twelve loads per set and
+// wave, well inside the wave's outstanding-load counter).
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
@@ -27,26 +28,23 @@ namespace {
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 constexpr int kCols = 16;            // columns per workgroup
-constexpr int kThreads = 256;        // 4 waves x 32 output rows
+constexpr int kThreads = 512;        // 8 waves x 16 output rows
 
-// One segment's operands as this lane uses them: its two M row pieces
-// (32 contiguous floats each) and the S~ values its accumulators start from.
+// One segment's operands as this lane uses them: eight 4-float pieces of its M
+// row (its contraction indices) and the S~ values its accumulators start from.
 struct SegOps {
-  float4 a[2][8];
-  float st[2][4];
+  float4 a[8];
+  float st[4];
 };
 
 __device__ __forceinline__ void load_seg(SegOps& x, const float* __restrict__ M, const float* __restrict__ S_tilde,
                                          int64_t base, int wave, int q, int n, int c0) {
+  const float* arow = M + base + int64_t(wave * 16 + n) * kD + 4 * q;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const float* arow = M + base + int64_t(wave * 32 + t * 16 + n) * kD + 32 * q;
+  for (int s4 = 0; s4 < 8; ++s4) x.a[s4] = ld_f4(arow + 16 * s4);
+  const int row = wave * 16 + 4 * q;
 #pragma unroll
-    for (int s4 = 0; s4 < 8; ++s4) x.a[t][s4] = ld_f4(arow + 4 * s4);
-    const int row = wave * 32 + t * 16 + 4 * q;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) x.st[t][e] = S_tilde[base + int64_t(row + e) * kD + c0 + n];
-  }
+  for (int e = 0; e < 4; ++e) x.st[e] = S_tilde[base + int64_t(row + e) * kD + c0 + n];
 }
 
 __global__ __launch_bounds__(kThreads) void kda_compose_kernel(const float* __restrict__ M,
@@ -90,30 +88,23 @@ __global__ __launch_bounds__(kThreads) void kda_compose_kernel(const float* __re
   };
   // S_in(i+1) = M(i) S_in(i) + S~(i) into curT, from operands x
   auto advance = [&](const SegOps& x) {
-    f32x4v acc[2][2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      acc[t][0] = f32x4v{x.st[t][0], x.st[t][1], x.st[t][2], x.st[t][3]};
-      acc[t][1] = f32x4v{0.f, 0.f, 0.f, 0.f};
-    }
-    const float* bcol = &curT[n][32 * q];  // column n of S_in(i), rows 32q .. 32q+31
+    f32x4v acc[2];
+    acc[0] = f32x4v{x.st[0], x.st[1], x.st[2], x.st[3]};
+    acc[1] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    const float* bcol = &curT[n][4 * q];
 #pragma unroll
     for (int s4 = 0; s4 < 8; ++s4) {
-      const float4 b = *reinterpret_cast<const float4*>(bcol + 4 * s4);
+      const float4 b = *reinterpret_cast<const float4*>(bcol + 16 * s4);
       const float bv[4] = {b.x, b.y, b.z, b.w};
-      const float av0[4] = {x.a[0][s4].x, x.a[0][s4].y, x.a[0][s4].z, x.a[0][s4].w};
-      const float av1[4] = {x.a[1][s4].x, x.a[1][s4].y, x.a[1][s4].z, x.a[1][s4].w};
+      const float av[4] = {x.a[s4].x, x.a[s4].y, x.a[s4].z, x.a[s4].w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[0][e & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av0[e], bv[e], acc[0][e & 1], 0, 0, 0);
-        acc[1][e & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av1[e], bv[e], acc[1][e & 1], 0, 0, 0);
-      }
+      for (int e = 0; e < 4; ++e)
+        acc[e & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], bv[e], acc[e & 1], 0, 0, 0);
     }
     __syncthreads();  // every wave has read S_in(i) from LDS
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int row = wave * 32 + t * 16 + 4 * q;
-      const f32x4v v = acc[t][0] + acc[t][1];
+    {
+      const int row = wave * 16 + 4 * q;
+      const f32x4v v = acc[0] + acc[1];
       *reinterpret_cast<float4*>(&curT[n][row]) = make_float4(v[0], v[1], v[2], v[3]);
     }
     __syncthreads();
@@ -130,22 +121,22 @@ __global__ __launch_bounds__(kThreads) void kda_compose_kernel(const float* __re
     load_seg(X0, M, S_tilde, seg_base(0), wave, q, n, c0);
     load_seg(X1, M, S_tilde, seg_base(1), wave, q, n, c0);
   }
+  // The loop body is straight-line (every phase loads and composes, a phase
+  // past the last segment recomputes into LDS what nobody reads), so the
+  // compiler's wait counts see each set's loads issued two phases before use.
   int i = 0;
-  while (i < n_seg) {
+  for (; i < n_seg; i += 3) {
     publish(i);
     load_seg(X2, M, S_tilde, seg_base(i + 2), wave, q, n, c0);
     advance(X0);
-    if (++i >= n_seg) break;
-    publish(i);
-    load_seg(X0, M, S_tilde, seg_base(i + 2), wave, q, n, c0);
+    if (i + 1 <= n_seg) publish(i + 1);
+    load_seg(X0, M, S_tilde, seg_base(i + 3), wave, q, n, c0);
     advance(X1);
-    if (++i >= n_seg) break;
-    publish(i);
-    load_seg(X1, M, S_tilde, seg_base(i + 2), wave, q, n, c0);
+    if (i + 2 <= n_seg) publish(i + 2);
+    load_seg(X1, M, S_tilde, seg_base(i + 4), wave, q, n, c0);
     advance(X2);
-    ++i;
   }
-  publish(n_seg);
+  if (i == n_seg) publish(n_seg);
 }
 
 }  // namespace

@@ -65,10 +65,11 @@ struct PrefillLaunch {
 
 hipError_t launch_prefill(const PrefillLaunch& p, bool bf16, hipStream_t stream);
 // Whether a prefill grid takes the split path when it has a workspace.
-bool prefill_split_applies(int64_t num_seqs, int64_t H, bool transitions);
+bool prefill_split_applies(int64_t num_seqs, int64_t H, bool transitions, bool outputs);
 // Workspace the split path needs for tokens up to t_end (cu_seqlens[num_seqs]); 0 when the grid
 // would not take it.
-size_t prefill_workspace_bytes(int64_t num_seqs, int64_t t_end, int64_t H, bool bf16, bool transitions);
+size_t prefill_workspace_bytes(int64_t num_seqs, int64_t t_end, int64_t H, bool bf16, bool transitions,
+                               bool outputs);
 int64_t prefill_workspace_slots(int64_t num_seqs, int64_t t_end);
 
 // ---- batch-invariant row contract (kda_contract.hip) ----------------------

@@ -287,7 +287,9 @@ template <class Pol, class InT, int SW, int JB, int PW, bool CKPT, bool PRO, Mod
 __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(PrefillArgs a) {
   static_assert(!(CKPT && PRO), "checkpoints and the prologue are separate variants");
   static_assert(MODE == Mode::State ? PW == 0 : (PW == 4 || PW == 8), "prep waves");
-  static_assert(MODE == Mode::Prep ? SW == 0 : SW == 4, "state waves");
+  static_assert(MODE == Mode::Prep ? SW == 0 : (SW == 4 || (MODE == Mode::State && (SW == 8 || SW == 16))),
+                "state waves");
+  static_assert(!(MODE == Mode::State && SW == 16) || (JB == 1 && !WO), "the 16-wave build serves pass 1 only");
   static_assert(MODE == Mode::Fused || !CKPT, "checkpoints are written by the fused build");
   constexpr int PWX = PW > 0 ? PW : 8;  // (role constants of a build without prep waves are unused)
   constexpr int TPT = 16 / PWX;  // tokens per prep thread (4 or 2)
@@ -333,8 +335,11 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
     seq = a.seq_order ? a.seq_order[sh / a.H] : sh / a.H;
   }
   if (seq < 0 || seq >= a.num_seqs) return;  // not a sequence of the batch (a bad order entry)
-  const bool is_transition = slice >= a.n_value_slices;
-  const int vslice = is_transition ? slice - a.n_value_slices : slice;
+  // (a 16-wave state build holds the sequence's state in waves 0-7 and its
+  // transition in waves 8-15, both read from one staged set)
+  constexpr bool kBoth = MODE == Mode::State && SW == 16;
+  const bool is_transition = kBoth ? wave >= 8 : slice >= a.n_value_slices;
+  const int vslice = kBoth ? 0 : (is_transition ? slice - a.n_value_slices : slice);
   const int64_t H = a.H;
   const int64_t tile_base = (int64_t(seq) * H + h) * (kD * kD);
   const int bos = a.cu_seqlens[seq];
@@ -343,7 +348,7 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
   const bool want_o = MODE == Mode::Prep ? a.prep_outputs != 0 : WO;
 
   // state-wave roles
-  const int colw = vslice * (16 * JB * SW) + (is_state ? wave : 0) * (16 * JB);
+  const int colw = kBoth ? (wave & 7) * 16 : vslice * (16 * JB * SW) + (is_state ? wave : 0) * (16 * JB);
   // prep-thread roles: TPT consecutive tokens x 4 consecutive channels; the
   // NTG token groups of a channel group are NTG consecutive lanes of a DPP row
   const int ptid = tid - SW * 64;
@@ -405,8 +410,9 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
     const int64_t slot0 = chunk_slot_base(bos, seq);
 #define KDA_REP17(X) X(0) X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14) X(15) X(16)
 #define KDA_STG_DECL(e) uint4 stg##e;
-#define KDA_STG_LD(e) stg##e = src_[tid + 64 * SW * (e) < kN16 ? tid + 64 * SW * (e) : kN16 - 1];
-#define KDA_STG_ST(e) if (tid + 64 * SW * (e) < kN16) dst_[tid + 64 * SW * (e)] = stg##e;
+    constexpr int kStageN = (kN16 + 64 * SW - 1) / (64 * SW);  // loads per thread
+#define KDA_STG_LD(e) if constexpr ((e) < kStageN) stg##e = src_[tid + 64 * SW * (e) < kN16 ? tid + 64 * SW * (e) : kN16 - 1];
+#define KDA_STG_ST(e) if constexpr ((e) < kStageN) { if (tid + 64 * SW * (e) < kN16) dst_[tid + 64 * SW * (e)] = stg##e; }
     KDA_REP17(KDA_STG_DECL)
     // (the loads are unconditional, chunk index clamped to the last chunk, so
     // the compiler's wait for the v loads before them is not widened over a
@@ -1034,11 +1040,12 @@ hipError_t launch_slices(PrefillArgs a, const PrefillLaunch& p, K&& kernel) {
   return go(false, nv, nv);
 }
 
-// Value column tiles (16 columns each) per state wave in the split path's walk.
-// One: the walk is bound by each wave's product sequence, not by the staging
-// (two tiles, one workgroup per head, measured 8.7k against 5.8k cycles per
-// chunk).
+// The split path's walk: eight state waves of one 16-column tile each, so one
+// workgroup holds a (sequence, head)'s 128 columns and stages each chunk's set
+// once.  (Four waves of two tiles measured 8.7k cycles per chunk, four of one
+// tile 5.8k but two workgroups per head, each staging the whole set.)
 constexpr int kSplitJB = 1;
+constexpr int kSplitSW = 8;
 
 template <class Pol, class InT>
 hipError_t launch_split(const PrefillLaunch& p, hipStream_t stream) {
@@ -1060,15 +1067,26 @@ hipError_t launch_split(const PrefillLaunch& p, hipStream_t stream) {
                        dim3(unsigned(prep_blocks)), dim3(prefill_threads(0, 8)), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  a.n_value_slices = kD / (16 * kSplitJB * 4);
+  if (p.transition_out != nullptr && p.o == nullptr) {
+    // states and transitions without outputs (a segmented prefill's pass 1):
+    // one 16-wave workgroup per (sequence, head) reads each set once for both
+    a.n_value_slices = 1;
+    a.n_slices = 1;
+    a.slice_base = 0;
+    a.n_launch_slices = 1;
+    hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, 16, 1, 0, false, false, Mode::State, false>),
+                       dim3(unsigned(int64_t(p.num_seqs) * p.H)), dim3(prefill_threads(16, 0)), 0, stream, a);
+    return hipGetLastError();
+  }
+  a.n_value_slices = kD / (16 * kSplitJB * kSplitSW);
   a.n_slices = a.n_value_slices * (p.transition_out ? 2 : 1);
   return launch_slices(a, p, [&](bool wo, const PrefillArgs& la, dim3 grid) {
     if (wo)
-      hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, 4, kSplitJB, 0, false, false, Mode::State, true>), grid,
-                         dim3(prefill_threads(4, 0)), 0, stream, la);
+      hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, kSplitSW, kSplitJB, 0, false, false, Mode::State, true>), grid,
+                         dim3(prefill_threads(kSplitSW, 0)), 0, stream, la);
     else
-      hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, 4, kSplitJB, 0, false, false, Mode::State, false>), grid,
-                         dim3(prefill_threads(4, 0)), 0, stream, la);
+      hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, kSplitSW, kSplitJB, 0, false, false, Mode::State, false>),
+                         grid, dim3(prefill_threads(kSplitSW, 0)), 0, stream, la);
   });
 }
 
@@ -1123,12 +1141,16 @@ hipError_t launch_cfg(const PrefillLaunch& p, hipStream_t stream) {
 
 }  // namespace
 
-bool prefill_split_applies(int64_t num_seqs, int64_t H, bool transitions) {
-  return num_seqs * H * (transitions ? 2 : 1) < device_cu_count();
+// The split path's walk runs one workgroup per (sequence, head), two when a call asks for both
+// outputs and transitions (value and transition slices launch separately); it applies while that
+// grid leaves compute units idle.
+bool prefill_split_applies(int64_t num_seqs, int64_t H, bool transitions, bool outputs) {
+  return num_seqs * H * (transitions && outputs ? 2 : 1) < device_cu_count();
 }
 
-size_t prefill_workspace_bytes(int64_t num_seqs, int64_t t_end, int64_t H, bool bf16, bool transitions) {
-  if (num_seqs <= 0 || !prefill_split_applies(num_seqs, H, transitions)) return 0;
+size_t prefill_workspace_bytes(int64_t num_seqs, int64_t t_end, int64_t H, bool bf16, bool transitions,
+                               bool outputs) {
+  if (num_seqs <= 0 || !prefill_split_applies(num_seqs, H, transitions, outputs)) return 0;
   const int64_t slots = (t_end >> 5) + num_seqs + 1;
   const int64_t set = bf16 ? Lds<PolBF16x3>::kSetBytes : Lds<PolF32>::kSetBytes;
   return size_t(slots * H * set);
@@ -1147,7 +1169,8 @@ hipError_t launch_prefill(const PrefillLaunch& p, bool bf16, hipStream_t stream)
   // runs the state waves alone.
   const int64_t units = int64_t(p.num_seqs) * p.H * (p.transition_out ? 2 : 1);
   const bool wide = units >= device_cu_count();
-  if (!wide && p.workspace != nullptr && p.checkpoints == nullptr)
+  if (p.workspace != nullptr && p.checkpoints == nullptr &&
+      prefill_split_applies(p.num_seqs, p.H, p.transition_out != nullptr, p.o != nullptr))
     return bf16 ? launch_split<PolBF16x3, BF16>(p, stream) : launch_split<PolF32, F32>(p, stream);
   if (bf16)
     return wide ? launch_cfg<PolBF16x3, BF16, 4, 2, 4>(p, stream) : launch_cfg<PolBF16x3, BF16, 4, 1, 8>(p, stream);

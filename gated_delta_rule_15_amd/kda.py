@@ -229,17 +229,18 @@ AUTO_WORKSPACE_MAX = 1 << 30
 
 
 def kda_prefill_workspace_size(num_seqs: int, T_total: int, H: int, dtype: torch.dtype,
-                               transitions: bool = False) -> int:
-    """Workspace bytes kda_prefill_ex can use (0: the call takes the single-kernel path)."""
+                               transitions: bool = False, outputs: bool = True) -> int:
+    """Workspace bytes kda_prefill_ex can use for a call that requests transitions or not and
+    outputs or not (0: the call takes the single-kernel path)."""
     code = _lib.KDA_BF16 if dtype == torch.bfloat16 else _lib.KDA_F32
-    return int(_lib.load().kda_prefill_workspace_size(int(num_seqs), int(T_total), int(H), D, D, code,
-                                                       1 if transitions else 0))
+    flags = (_lib.KDA_PREFILL_TRANSITIONS if transitions else 0) | (0 if outputs else _lib.KDA_PREFILL_NO_OUTPUT)
+    return int(_lib.load().kda_prefill_workspace_size(int(num_seqs), int(T_total), int(H), D, D, code, flags))
 
 
 def kda_prefill_workspace(num_seqs: int, T_total: int, H: int, dtype: torch.dtype, device,
-                          transitions: bool = False) -> Optional[torch.Tensor]:
+                          transitions: bool = False, outputs: bool = True) -> Optional[torch.Tensor]:
     """A workspace for kda_prefill(..., workspace=...) (None when the call needs none)."""
-    n = kda_prefill_workspace_size(num_seqs, T_total, H, dtype, transitions)
+    n = kda_prefill_workspace_size(num_seqs, T_total, H, dtype, transitions, outputs)
     return torch.empty(n, dtype=torch.uint8, device=device) if n else None
 
 
@@ -327,7 +328,8 @@ def _prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, initial_state, final
             raise ValueError('workspace must be "auto", None or a device uint8 tensor')
         workspace = None
         if cu_seqlens_host is not None and N > 0:
-            n = kda_prefill_workspace_size(N, int(cu_seqlens_host[-1]), H, dt, transition_out is not None)
+            n = kda_prefill_workspace_size(N, int(cu_seqlens_host[-1]), H, dt, transition_out is not None,
+                                               o is not None)
             if 0 < n <= AUTO_WORKSPACE_MAX:
                 workspace = torch.empty(n, dtype=torch.uint8, device=dev)
     if workspace is not None:

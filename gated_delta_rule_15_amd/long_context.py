@@ -71,6 +71,28 @@ def auto_seg_len(cu_seqlens_host, H: int, n_cu: int = 256, min_seg: int = 512) -
     return ((seg + 63) // 64) * 64
 
 
+def auto_seg_len_split(cu_seqlens_host, H: int, n_cu: int = 256, min_seg: int = 256) -> int:
+    """Segment length for the split path (``alloc_work(..., split=True)``): each of its passes runs
+    one workgroup per (row, head) (pass 1 holds a row's state and transition together), so the
+    rule cuts the longest sequence into as many segments as keep that within ``n_cu``
+    workgroups, each at least ``min_seg`` tokens (4096 tokens x 12 heads: 256-token segments,
+    16 rows, 192 workgroups)."""
+    cu = np.asarray(cu_seqlens_host, dtype=np.int64)
+    lens = np.diff(cu)
+    t_max = int(lens.max()) if lens.size else 0
+    units = int((lens > 0).sum()) * H
+    if units == 0:
+        return 64
+    n_seg = max(1, n_cu // units)
+    seg = max(min_seg, -(-t_max // n_seg))
+    seg = ((seg + 63) // 64) * 64
+    # rounding up to 64 can leave the last segment short: more rows than wanted is still within n_cu
+    # as long as every sequence's row count stays at n_seg
+    while seg < t_max and -(-t_max // seg) > n_seg:
+        seg += 64
+    return seg
+
+
 def plan_segments(cu_seqlens_host, seg_len: int, cut_longer_than: int = 0) -> SegmentPlan:
     """Segment rows of a packed batch: every sequence longer than
     ``max(seg_len, cut_longer_than)`` tokens is cut every ``seg_len`` tokens
@@ -115,15 +137,20 @@ def kda_prefill_segmented(q, k, v, g, beta, cu_seqlens_host, seg_len: Optional[i
     if final_state is None:
         final_state = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
     init2, fin2 = work["init2"], work["fin2"]
-
-    # entry states of first segments: the caller's initial states (or zeros)
-    first_rows = work["first_rows"]
-    if initial_state is not None:
-        init2.index_copy_(0, first_rows, initial_state)
-    else:
-        init2.index_fill_(0, first_rows, 0.0)
-
     ws = work["ws"]
+    # split path with every sequence cut: pass 1 gives every row's (M, S~), so the scan runs through
+    # the last segment and yields each sequence's final state (and its first row's entry state);
+    # pass 2 then only writes outputs
+    all_cut = ws is not None and len(plan.multi) == N
+
+    if not all_cut:
+        # entry states of first segments: the caller's initial states (or zeros)
+        first_rows = work["first_rows"]
+        if initial_state is not None:
+            init2.index_copy_(0, first_rows, initial_state)
+        else:
+            init2.index_fill_(0, first_rows, 0.0)
+
     if ws is not None:
         # split path: pass 1 runs over every row (the rows it does not need cost little on a grid
         # this small), so both passes walk the same chunks and share one preparation
@@ -133,6 +160,11 @@ def kda_prefill_segmented(q, k, v, g, beta, cu_seqlens_host, seg_len: Optional[i
     for n in plan.multi:
         r = plan.row_of_seq[n]
         nf = len(r) - 1
+        if all_cut:
+            kda.kda_compose_segments(work["M_all"][r.start:r.stop], work["St_all"][r.start:r.stop],
+                                     None if initial_state is None else initial_state[n],
+                                     S_in=init2[r.start:r.stop], S_final=final_state[n])
+            continue
         if ws is not None:
             M, St = work["M_all"][r.start:r.start + nf], work["St_all"][r.start:r.start + nf]
         else:
@@ -147,9 +179,10 @@ def kda_prefill_segmented(q, k, v, g, beta, cu_seqlens_host, seg_len: Optional[i
 
     # pass 2: every segment from its entry state, longest rows started first
     kda.kda_prefill_ordered(q, k, v, g, beta, work["rows_d"], work["order2"], work["rows_h"], initial_state=init2,
-                            final_state=fin2, o=o, scale=scale, workspace=ws,
-                            ws_flags=_lib.KDA_WS_PREPARED if ws is not None else 0)
-    torch.index_select(fin2, 0, work["last_rows"], out=final_state)
+                            final_state=None if all_cut else fin2, with_final_state=not all_cut, o=o, scale=scale,
+                            workspace=ws, ws_flags=_lib.KDA_WS_PREPARED if ws is not None else 0)
+    if not all_cut:
+        torch.index_select(fin2, 0, work["last_rows"], out=final_state)
     return o, final_state
 
 
@@ -168,7 +201,7 @@ def alloc_work(plan: SegmentPlan, H: int, dev, dtype=torch.bfloat16, split: bool
     transition and state for a pass 1 over all rows."""
     R = plan.n_rows
     T_end = int(plan.rows[-1]) if len(plan.rows) else 0
-    n_ws = kda.kda_prefill_workspace_size(R, T_end, H, dtype, transitions=True) if split else 0
+    n_ws = kda.kda_prefill_workspace_size(R, T_end, H, dtype, transitions=True, outputs=False) if split else 0
     ws = torch.empty(n_ws, dtype=torch.uint8, device=dev) if n_ws > 0 else None
     work = {
         "order2": torch.from_numpy(longest_first(plan.rows)).to(dev),

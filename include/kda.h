@@ -190,15 +190,21 @@ kda_status_t kda_prefill(const void* q, const void* k, const void* v, const floa
 /*
  * kda_prefill_workspace_size — bytes of device workspace kda_prefill_ex can use
  * for a call with num_seqs sequences within T_total packed tokens (every
- * cu_seqlens value <= T_total), H heads, and transitions requested or not.
+ * cu_seqlens value <= T_total) and H heads; flags say what the call requests:
+ *   KDA_PREFILL_TRANSITIONS  transition_out is given;
+ *   KDA_PREFILL_NO_OUTPUT    o is NULL.
  * 0 means the call takes the single-kernel path and needs none: that is the
- * case when the grid, num_seqs * H (* 2 with transitions) (sequence, head)
- * units, already fills the device's compute units.  Sizes: one operand set
- * (66,560 bytes for bf16 inputs, 62,464 for fp32) per 32-token chunk slot and
- * head, T_total / 32 + num_seqs + 1 slots.  Returns 0 for invalid arguments.
+ * case when the split path's walk, num_seqs * H (sequence, head) workgroups
+ * (twice that when both outputs and transitions are requested), already fills
+ * the device's compute units.  Sizes: one operand set (66,560 bytes for bf16
+ * inputs, 62,464 for fp32) per 32-token chunk slot and head,
+ * T_total / 32 + num_seqs + 1 slots.  Returns 0 for invalid arguments
+ * (unknown flag bits included).
  */
+#define KDA_PREFILL_TRANSITIONS 1
+#define KDA_PREFILL_NO_OUTPUT 2
 size_t kda_prefill_workspace_size(int32_t num_seqs, int64_t T_total, int32_t H, int32_t d_k, int32_t d_v,
-                                  kda_dtype_t dtype, int32_t with_transitions);
+                                  kda_dtype_t dtype, int32_t flags);
 
 /*
  * kda_prefill_ex — kda_prefill with every option: seq_order (as

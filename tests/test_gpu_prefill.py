@@ -411,3 +411,7 @@ def test_split_path_workspace_errors():
     # a grid that fills the device needs none
     assert kda_prefill_workspace_size(256, 4096, 1, torch.bfloat16) == 0
     assert kda_prefill_workspace_size(128, 4096, 1, torch.bfloat16, transitions=True) == 0
+    # transitions without outputs walk one workgroup per (sequence, head)
+    assert kda_prefill_workspace_size(128, 4096, 1, torch.bfloat16, transitions=True, outputs=False) > 0
+    # unknown request flags are invalid arguments
+    assert _lib.load().kda_prefill_workspace_size(2, 4096, 1, 128, 128, _lib.KDA_BF16, 4) == 0
