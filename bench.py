@@ -205,15 +205,20 @@ def bench_decode(steps, warmup, n_sets=8, prologue=False):
 def bench_copy_probe(steps, warmup, n_sets=8):
     """The decode's memory roof measured: a plain device copy of the same footprint (48 MiB read and
     48 MiB written per launch, the size of the 64 x 12 state), rotating the same number of buffer
-    pairs, timed the same way."""
+    pairs, timed the same way: the library's probe (kda_copy_probe, nontemporal float4, eight per
+    thread) and, for context, torch's copy_."""
     import torch
+    from gated_delta_rule_15_amd import kda
     n = 64 * 12 * D * D
     pairs = [(torch.ones(n, device="cuda:0"), torch.empty(n, device="cuda:0")) for _ in range(n_sets)]
-    fns = [lambda p=pairs[i % n_sets]: p[1].copy_(p[0]) for i in range(max(100, steps))]
+    fns = [lambda p=pairs[i % n_sets]: kda.copy_probe(p[0], p[1]) for i in range(max(100, steps))]
     med, lo, hi = graph_replay_stats_ms(fns, warmup)
+    fns_t = [lambda p=pairs[i % n_sets]: p[1].copy_(p[0]) for i in range(max(100, steps))]
+    med_t, _, _ = graph_replay_stats_ms(fns_t, warmup)
     nbytes = 2 * n * 4
     return dict(ms=med, bytes=nbytes, gbps=nbytes / (med * 1e-3) / 1e9, n_sets=n_sets,
-                kernel="torch copy_ of an fp32 buffer (elementwise copy kernel)")
+                kernel="kda_copy_probe (nontemporal float4 copy, 8 per thread)",
+                torch_copy_ms=med_t, torch_copy_gbps=nbytes / (med_t * 1e-3) / 1e9)
 
 
 def bench_verify(reps, warmup, n_sets=8, prologue=False):
@@ -441,12 +446,14 @@ def bench_long(reps, warmup=1, gen_workers=None):
     """1,048,576-token sequence (16 segments of 65,536) + 8 ragged 1K-32K sequences, 12 heads, bf16.
 
     Each 65,536-token segment is computed as eight 8,192-token fragments, so pass 1
-    has 127 x 12 x 2 units and pass 2 128 x 12 + 8 x 12 (the scan over the 128
+    has 127 x 12 units (each workgroup builds a fragment's state and transition from one
+    preparation of its chunks) and pass 2 128 x 12 + 8 x 12 (the scan over the 128
     fragments equals composing each segment from its fragments and then scanning the
-    16 segments: the composition is associative).  Measured: 31.4 ms with whole
-    65,536-token segments (pass 1's 360 units take two rounds of 256 CUs), 23.4 ms
+    16 segments: the composition is associative).  Measured with separate state and
+    transition workgroups in pass 1: 31.4 ms with whole 65,536-token segments, 23.4 ms
     with 32,768-token fragments, 22.4 ms with 8,192 (pass 2 starts its longest rows
-    first).  Inputs are drawn by ``gen_workers`` spawned processes (default:
+    first); with the combined pass-1 workgroups 18.7-19.7 ms at 8,192 (20.3 ms at 4,096,
+    19.7 ms at 16,384).  Inputs are drawn by ``gen_workers`` spawned processes (default:
     the host's cores, at most 16); 1 draws them in this process (for runs under a
     profiler)."""
     import torch
@@ -667,6 +674,10 @@ def main():
                     help="time only the prefill rows, 4096 x 12 and 32 x 4096 x 12 (for profiling)")
     ap.add_argument("--only-contract", action="store_true",
                     help="time only the row-contract rows, decode 64 x 12 and prefill (for profiling)")
+    ap.add_argument("--only-verify", action="store_true",
+                    help="time only verify + commit 32 x 12 x 8 (for profiling)")
+    ap.add_argument("--only-long", action="store_true",
+                    help="time only the 1M-token long-context prefill (for profiling)")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--write-traffic", metavar="DIR",
                     help="write profiles/decode_64x12_traffic.json from rocprofv3 counter CSVs under DIR")
@@ -701,6 +712,13 @@ def main():
         return
     if args.only_contract:
         print(json.dumps(bench_contract(args.steps, args.warmup)), flush=True)
+        return
+    if args.only_verify:
+        print(json.dumps({"verify_commit_32x12x8_bf16": bench_verify(reps=max(16, args.steps // 2),
+                                                                      warmup=args.warmup)}), flush=True)
+        return
+    if args.only_long:
+        print(json.dumps({"long_context_1m_plus_8": bench_long(reps=2, gen_workers=args.gen_workers)}), flush=True)
         return
     dec = bench_decode(args.steps, args.warmup)
     log(f"decode: {dec['ms'] * 1e3:.2f} us/step, {dec['gbps']:.0f} GB/s")
@@ -745,13 +763,15 @@ def main():
     copy = None
     if not EAGER:
         copy = bench_copy_probe(args.steps, args.warmup)
-        log(f"copy probe (same footprint): {copy['ms'] * 1e3:.2f} us, {copy['gbps']:.0f} GB/s")
+        log(f"copy probe (same footprint): {copy['ms'] * 1e3:.2f} us, {copy['gbps']:.0f} GB/s "
+            f"(torch copy_ {copy['torch_copy_ms'] * 1e3:.2f} us)")
     roof = dict(bound="hbm", achieved=round(dec["gbps"], 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                 frac=round(dec["gbps"] / HBM_PEAK_GBPS, 4), traffic=traffic,
                 kernel="kda_decode_kernel<BF16, false>", algorithmic_bytes_per_launch=dec["bytes"],
                 mean_launch_us=round(dec["ms"] * 1e3, 3),
                 median_launch_us=round(dec["median_ms"] * 1e3, 3) if "median_ms" in dec else None,
                 measured_copy_gbps=round(copy["gbps"], 1) if copy else None,
+                measured_copy_kernel=copy["kernel"] if copy else None,
                 frac_of_measured_copy=round(dec["gbps"] / copy["gbps"], 4) if copy else None)
     cpu = None
     if not args.no_cpu_baseline:

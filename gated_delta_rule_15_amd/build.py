@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libkda.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["kda_step.hip", "kda_compose.hip", "kda_prefill.hip", "kda_contract.hip", "kda_api.hip"]
+SOURCES = ["kda_step.hip", "kda_compose.hip", "kda_prefill.hip", "kda_contract.hip", "kda_probe.hip", "kda_api.hip"]
 # No contraction of separate multiplies and adds into fused operations where
 # results must be bit-reproducible across code paths: the step kernels between
 # decode, verify and commit; the prefill between its two workgroup shapes (the

@@ -4,6 +4,7 @@
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
+#include <cstdint>
 #include <mutex>
 
 // Scratch of the allocation-free prefill (kda_prefill_noalloc): the split
@@ -114,6 +115,14 @@ kda_status_t prefill_impl(const void* q, const void* k, const void* v, const flo
 extern "C" {
 
 int kda_version(void) { return kVersion; }
+
+kda_status_t kda_copy_probe(const float* src, float* dst, int64_t n, void* stream) {
+  if (n < 0 || (n % 4) != 0) return KDA_ERR_INVALID_ARG;
+  if (n == 0) return KDA_OK;
+  if (!src || !dst || (reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) % 16 != 0)
+    return KDA_ERR_INVALID_ARG;
+  return hip_status(kda::launch_copy_probe(src, dst, n, static_cast<hipStream_t>(stream)));
+}
 
 const char* kda_status_string(kda_status_t status) {
   switch (status) {

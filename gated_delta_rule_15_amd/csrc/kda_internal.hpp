@@ -35,6 +35,8 @@ hipError_t launch_commit(const void* k, const void* v, const float* g, const flo
                          const Prologue* pro = nullptr);
 
 // ---- segment composition (kda_compose.hip) --------------------------------
+// Memory-roof probe: a nontemporal float4 copy of n floats (n a multiple of 4).
+hipError_t launch_copy_probe(const float* src, float* dst, int64_t n, hipStream_t stream);
 hipError_t launch_compose(const float* M, const float* S_tilde, const float* S_in0, float* S_in,
                           float* S_final, int n_seg, int H, hipStream_t stream);
 

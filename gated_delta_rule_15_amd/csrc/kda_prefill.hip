@@ -287,9 +287,17 @@ template <class Pol, class InT, int SW, int JB, int PW, bool CKPT, bool PRO, Mod
 __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(PrefillArgs a) {
   static_assert(!(CKPT && PRO), "checkpoints and the prologue are separate variants");
   static_assert(MODE == Mode::State ? PW == 0 : (PW == 4 || PW == 8), "prep waves");
-  static_assert(MODE == Mode::Prep ? SW == 0 : (SW == 4 || (MODE == Mode::State && (SW == 8 || SW == 16))),
+  static_assert(MODE == Mode::Prep ? SW == 0
+                                   : (SW == 4 || (MODE == Mode::State && (SW == 8 || SW == 16)) ||
+                                      (MODE == Mode::Fused && SW == 8 && JB == 2)),
                 "state waves");
-  static_assert(!(MODE == Mode::State && SW == 16) || (JB == 1 && !WO), "the 16-wave build serves pass 1 only");
+  // Builds that hold a (sequence, head)'s state and its transition in one
+  // workgroup (the first half of the state waves the state, the second half
+  // the transition, all 128 columns each) serve a segmented prefill's pass 1:
+  // the 16-wave state build reads each staged set once for both, the 8-wave
+  // fused build prepares each chunk once for both.
+  constexpr bool kBoth = (MODE == Mode::State && SW == 16) || (MODE == Mode::Fused && SW == 8);
+  static_assert(!kBoth || (16 * JB * (SW / 2) == kD && !WO && !CKPT), "state and transition builds serve pass 1 only");
   static_assert(MODE == Mode::Fused || !CKPT, "checkpoints are written by the fused build");
   constexpr int PWX = PW > 0 ? PW : 8;  // (role constants of a build without prep waves are unused)
   constexpr int TPT = 16 / PWX;  // tokens per prep thread (4 or 2)
@@ -335,10 +343,7 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
     seq = a.seq_order ? a.seq_order[sh / a.H] : sh / a.H;
   }
   if (seq < 0 || seq >= a.num_seqs) return;  // not a sequence of the batch (a bad order entry)
-  // (a 16-wave state build holds the sequence's state in waves 0-7 and its
-  // transition in waves 8-15, both read from one staged set)
-  constexpr bool kBoth = MODE == Mode::State && SW == 16;
-  const bool is_transition = kBoth ? wave >= 8 : slice >= a.n_value_slices;
+  const bool is_transition = kBoth ? wave >= SW / 2 : slice >= a.n_value_slices;
   const int vslice = kBoth ? 0 : (is_transition ? slice - a.n_value_slices : slice);
   const int64_t H = a.H;
   const int64_t tile_base = (int64_t(seq) * H + h) * (kD * kD);
@@ -348,7 +353,7 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
   const bool want_o = MODE == Mode::Prep ? a.prep_outputs != 0 : WO;
 
   // state-wave roles
-  const int colw = kBoth ? (wave & 7) * 16 : vslice * (16 * JB * SW) + (is_state ? wave : 0) * (16 * JB);
+  const int colw = kBoth ? (wave % (SW / 2)) * (16 * JB) : vslice * (16 * JB * SW) + (is_state ? wave : 0) * (16 * JB);
   // prep-thread roles: TPT consecutive tokens x 4 consecutive channels; the
   // NTG token groups of a channel group are NTG consecutive lanes of a DPP row
   const int ptid = tid - SW * 64;
@@ -1130,8 +1135,22 @@ void launch_fused(bool wo, const PrefillArgs& a, dim3 grid, hipStream_t stream) 
 
 template <class Pol, class InT, int SW, int JB, int PW>
 hipError_t launch_cfg(const PrefillLaunch& p, hipStream_t stream) {
-  const PrefillArgs a = make_args<Pol, InT, SW, JB, PW>(p);
+  PrefillArgs a = make_args<Pol, InT, SW, JB, PW>(p);
   if (p.checkpoints && p.pro) return hipErrorNotSupported;
+  if constexpr (SW == 4 && JB == 2) {
+    if (p.transition_out != nullptr && p.o == nullptr && p.checkpoints == nullptr && p.pro == nullptr) {
+      // states and transitions without outputs (a segmented prefill's pass 1) on
+      // a grid that fills the device: one workgroup per (sequence, head), its
+      // prep waves preparing each chunk once for the state and the transition
+      a.n_value_slices = 1;
+      a.n_slices = 1;
+      a.slice_base = 0;
+      a.n_launch_slices = 1;
+      hipLaunchKernelGGL((kda_prefill_kernel<Pol, InT, 8, 2, PW, false, false, Mode::Fused, false>),
+                         dim3(unsigned(int64_t(p.num_seqs) * p.H)), dim3(prefill_threads(8, PW)), 0, stream, a);
+      return hipGetLastError();
+    }
+  }
   return launch_slices(a, p, [&](bool wo, const PrefillArgs& la, dim3 grid) {
     if (p.checkpoints) launch_fused<Pol, InT, SW, JB, PW, true, false>(wo, la, grid, stream);
     else if (p.pro) launch_fused<Pol, InT, SW, JB, PW, false, true>(wo, la, grid, stream);

@@ -222,6 +222,16 @@ def kda_prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host=None, initial_stat
                     scale, with_output, with_final_state, None, prologue, workspace, ws_flags)
 
 
+def copy_probe(src: torch.Tensor, dst: torch.Tensor) -> None:
+    """kda_copy_probe: the memory-roof probe, a nontemporal float4 copy of src into dst (contiguous fp32
+    device tensors of one size, a multiple of 4 elements)."""
+    if src.dtype != torch.float32 or dst.dtype != torch.float32 or not src.is_cuda or dst.device != src.device:
+        raise ValueError("copy_probe takes fp32 tensors on one device")
+    if not src.is_contiguous() or not dst.is_contiguous() or src.numel() != dst.numel():
+        raise ValueError("copy_probe takes contiguous tensors of one size")
+    _lib.check(_lib.load().kda_copy_probe(_ptr(src), _ptr(dst), src.numel(), _stream()), "kda_copy_probe")
+
+
 # "auto" workspaces stop here: a few long sequences on few heads would need one operand set per
 # 32-token chunk (about 2 KB per token and head); such calls run the single kernel, or go through
 # long_context.kda_prefill_segmented, which cuts them first.

@@ -51,6 +51,16 @@ int kda_version(void);
 const char* kda_status_string(kda_status_t status);
 
 /*
+ * kda_copy_probe — measurement probe, not part of the recurrence: copies n
+ * fp32 values from src to dst (device buffers, 16-byte aligned, not
+ * overlapping, n a multiple of 4) with nontemporal 16-byte loads and stores,
+ * eight per thread.  It measures the memory roof that the state-streaming
+ * kernels (decode, commit) are compared with.  KDA_ERR_INVALID_ARG for a
+ * negative or unaligned n or misaligned pointers; n == 0 does nothing.
+ */
+kda_status_t kda_copy_probe(const float* src, float* dst, int64_t n, void* stream);
+
+/*
  * kda_decode_step — one token per request: gate, delta write, readout, in place.
  *
  * Per request n and head h (the step is the gate-then-delta split of the KDA

@@ -36,7 +36,7 @@ def test_header_declares_the_entry_points():
                  "kda_verify_commit_prologue", "kda_prefill_prologue", "kda_contract_prefill",
                  "kda_contract_decode", "kda_contract_state", "kda_contract_verify", "kda_contract_commit",
                  "kda_contract_commit_stash", "kda_contract_prefill_split",
-                 "kda_status_string", "kda_version"):
+                 "kda_copy_probe", "kda_status_string", "kda_version"):
         assert name in syms
     assert set(syms) == set(_lib.SIGNATURES), "binding signatures and header disagree"
 
@@ -225,3 +225,14 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(_lib.KdaError, match="no CPU fallback"):
         _lib.load()
+
+
+def test_copy_probe_argument_errors(lib):
+    """The memory-roof probe rejects counts that are not whole 16-byte pieces and misaligned buffers
+    before touching the device; an empty copy does nothing."""
+    p = ctypes.c_void_p(1 << 20)
+    assert lib.kda_copy_probe(p, p, -4, None) == _lib.KDA_ERR_INVALID_ARG
+    assert lib.kda_copy_probe(p, p, 6, None) == _lib.KDA_ERR_INVALID_ARG
+    assert lib.kda_copy_probe(ctypes.c_void_p((1 << 20) + 4), p, 8, None) == _lib.KDA_ERR_INVALID_ARG
+    assert lib.kda_copy_probe(None, p, 8, None) == _lib.KDA_ERR_INVALID_ARG
+    assert lib.kda_copy_probe(None, None, 0, None) == _lib.KDA_OK

@@ -415,3 +415,28 @@ def test_split_path_workspace_errors():
     assert kda_prefill_workspace_size(128, 4096, 1, torch.bfloat16, transitions=True, outputs=False) > 0
     # unknown request flags are invalid arguments
     assert _lib.load().kda_prefill_workspace_size(2, 4096, 1, 128, 128, _lib.KDA_BF16, 4) == 0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_state_and_transition_build_bitwise(dtype):
+    """A call for final states and transitions without outputs on a grid that fills the device (a
+    segmented prefill's pass 1) runs one workgroup per (sequence, head) holding both; it equals, bit
+    for bit, the same call with outputs (separate state and transition workgroups), and the oracle."""
+    from gated_delta_rule_15_amd.kda import kda_prefill
+    H = 12
+    lens = [int(x) for x in np.random.default_rng(61).integers(1, 200, size=24)]
+    lens[3] = 0
+    p = gen.packed_batch(seed=61, seqlens=lens, H=H, dtype=dtype, init_state=[i % 3 != 0 for i in range(24)])
+    d = packed_to_dev(p)
+    N = len(lens)
+    M1 = torch.empty((N, H, 128, 128), device="cuda:0")
+    M2 = torch.empty_like(M1)
+    _, S1 = kda_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], d["cu_seqlens_host"],
+                        initial_state=d["initial_state"], transition_out=M1, with_output=False, workspace=None)
+    o2, S2 = kda_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], d["cu_seqlens_host"],
+                         initial_state=d["initial_state"], transition_out=M2, workspace=None)
+    torch.cuda.synchronize()
+    assert torch.equal(S1.view(torch.int32), S2.view(torch.int32))
+    assert torch.equal(M1.view(torch.int32), M2.view(torch.int32))
+    _check(p, o2, S1, f"state+transition build {dtype}")
+    _check_transitions(p, M1, f"state+transition build {dtype}")
