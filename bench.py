@@ -221,6 +221,32 @@ def bench_copy_probe(steps, warmup, n_sets=8):
                 torch_copy_ms=med_t, torch_copy_gbps=nbytes / (med_t * 1e-3) / 1e9)
 
 
+def bench_mfma_probe(iters=8000, waves_per_simd=2):
+    """The prefill's matrix roof measured: kda_mfma_probe (a loop of bf16 16x16x32 MFMAs over eight
+    independent accumulators per wave, waves_per_simd waves on every SIMD), timed with events; the
+    median of 5 launches."""
+    import statistics
+    import torch
+    from gated_delta_rule_15_amd import kda
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks = cus * waves_per_simd  # 4 waves per workgroup: waves_per_simd waves on each of the 4 SIMDs
+    out = torch.empty(blocks * 1024, device="cuda:0")
+    kda.mfma_probe(out, blocks, 10)
+    times = []
+    for _ in range(5):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        flops = kda.mfma_probe(out, blocks, iters)
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    ms = statistics.median(times)
+    return dict(ms=ms, flops=flops, tflops=flops / (ms * 1e-3) / 1e12,
+                frac_of_peak=flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                kernel="kda_mfma_probe (v_mfma_f32_16x16x32_bf16 loop)", blocks=blocks, iters=iters)
+
+
 def bench_verify(reps, warmup, n_sets=8, prologue=False):
     import numpy as np
     import torch
@@ -758,6 +784,14 @@ def main():
             log(f"long context: {lc['ms']:.2f} ms, {lc['tokens_per_s'] / 1e6:.1f} M tokens/s")
             rows["long_context_1m_plus_8"] = lc
 
+    if not args.only_decode and not EAGER:
+        mf = bench_mfma_probe()
+        log(f"mfma probe (bf16 16x16x32 loop): {mf['tflops']:.0f} TFLOP/s ({100 * mf['frac_of_peak']:.1f} % of "
+            f"{BF16_MFMA_PEAK_TFLOPS:.0f})")
+        rows["mfma_probe"] = mf
+        for key in ("prefill_4096x12_bf16", "prefill_32x4096x12_bf16", "long_context_1m_plus_8"):
+            if key in rows and "algorithmic_tflops" in rows[key]:
+                rows[key]["frac_of_measured_mfma"] = rows[key]["algorithmic_tflops"] / mf["tflops"]
     khash = src_hash("kda_step.hip", "kda_common.hpp")
     traffic = traffic_from_profile(khash)
     copy = None

@@ -24,7 +24,10 @@ SOURCES = ["kda_step.hip", "kda_compose.hip", "kda_prefill.hip", "kda_contract.h
 # compiler's fusion choices could differ between the instantiations); the row
 # contract between its one-row and sixteen-row instantiations.
 PER_FILE_FLAGS = {"kda_step.hip": ["-ffp-contract=off"], "kda_prefill.hip": ["-ffp-contract=off"],
-                  "kda_contract.hip": ["-ffp-contract=off"]}
+                  "kda_contract.hip": ["-ffp-contract=off"],
+                  # the MFMA probe's accumulators in VGPRs: with AGPR accumulators the allocator
+                  # rotated them between loop trips (48 accumulator moves per 32 MFMAs)
+                  "kda_probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 ARCH = "gfx950"
 COMMON_FLAGS = [

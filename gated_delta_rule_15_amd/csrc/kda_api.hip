@@ -116,6 +116,12 @@ extern "C" {
 
 int kda_version(void) { return kVersion; }
 
+kda_status_t kda_mfma_probe(float* out, int32_t blocks, int32_t iters, int64_t* flops, void* stream) {
+  if (blocks <= 0 || iters <= 0 || !out || reinterpret_cast<uintptr_t>(out) % 16 != 0) return KDA_ERR_INVALID_ARG;
+  if (flops) *flops = kda::mfma_probe_flops(blocks, iters);
+  return hip_status(kda::launch_mfma_probe(out, blocks, iters, static_cast<hipStream_t>(stream)));
+}
+
 kda_status_t kda_copy_probe(const float* src, float* dst, int64_t n, void* stream) {
   if (n < 0 || (n % 4) != 0) return KDA_ERR_INVALID_ARG;
   if (n == 0) return KDA_OK;

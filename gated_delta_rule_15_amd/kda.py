@@ -232,6 +232,17 @@ def copy_probe(src: torch.Tensor, dst: torch.Tensor) -> None:
     _lib.check(_lib.load().kda_copy_probe(_ptr(src), _ptr(dst), src.numel(), _stream()), "kda_copy_probe")
 
 
+def mfma_probe(out: torch.Tensor, blocks: int, iters: int) -> int:
+    """kda_mfma_probe: the matrix-roof probe (bf16 16x16x32 MFMA loop); out: fp32 device tensor of at least
+    blocks x 1024 elements.  Returns the flops of the launch."""
+    if out.dtype != torch.float32 or not out.is_cuda or not out.is_contiguous() or out.numel() < blocks * 1024:
+        raise ValueError("mfma_probe needs a contiguous fp32 device tensor of blocks x 1024 elements")
+    flops = ctypes.c_int64(0)
+    _lib.check(_lib.load().kda_mfma_probe(_ptr(out), int(blocks), int(iters), ctypes.byref(flops), _stream()),
+               "kda_mfma_probe")
+    return int(flops.value)
+
+
 # "auto" workspaces stop here: a few long sequences on few heads would need one operand set per
 # 32-token chunk (about 2 KB per token and head); such calls run the single kernel, or go through
 # long_context.kda_prefill_segmented, which cuts them first.

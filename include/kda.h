@@ -61,6 +61,17 @@ const char* kda_status_string(kda_status_t status);
 kda_status_t kda_copy_probe(const float* src, float* dst, int64_t n, void* stream);
 
 /*
+ * kda_mfma_probe — measurement probe, not part of the recurrence: blocks
+ * workgroups of 256 threads, each wave issuing iters x 8 independent
+ * v_mfma_f32_16x16x32_bf16 (the prefill's matrix product), to measure the
+ * matrix roof the prefill is compared with.  out: device buffer of
+ * blocks x 256 x 4 floats (16-byte aligned) receiving the accumulators (so
+ * the work is kept); *flops (host, may be NULL) receives the flops of the
+ * launch.  KDA_ERR_INVALID_ARG for non-positive counts or a bad buffer.
+ */
+kda_status_t kda_mfma_probe(float* out, int32_t blocks, int32_t iters, int64_t* flops, void* stream);
+
+/*
  * kda_decode_step — one token per request: gate, delta write, readout, in place.
  *
  * Per request n and head h (the step is the gate-then-delta split of the KDA

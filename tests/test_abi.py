@@ -36,7 +36,7 @@ def test_header_declares_the_entry_points():
                  "kda_verify_commit_prologue", "kda_prefill_prologue", "kda_contract_prefill",
                  "kda_contract_decode", "kda_contract_state", "kda_contract_verify", "kda_contract_commit",
                  "kda_contract_commit_stash", "kda_contract_prefill_split",
-                 "kda_copy_probe", "kda_status_string", "kda_version"):
+                 "kda_copy_probe", "kda_mfma_probe", "kda_status_string", "kda_version"):
         assert name in syms
     assert set(syms) == set(_lib.SIGNATURES), "binding signatures and header disagree"
 
@@ -236,3 +236,11 @@ def test_copy_probe_argument_errors(lib):
     assert lib.kda_copy_probe(ctypes.c_void_p((1 << 20) + 4), p, 8, None) == _lib.KDA_ERR_INVALID_ARG
     assert lib.kda_copy_probe(None, p, 8, None) == _lib.KDA_ERR_INVALID_ARG
     assert lib.kda_copy_probe(None, None, 0, None) == _lib.KDA_OK
+
+
+def test_mfma_probe_argument_errors(lib):
+    p = ctypes.c_void_p(1 << 20)
+    assert lib.kda_mfma_probe(p, 0, 10, None, None) == _lib.KDA_ERR_INVALID_ARG
+    assert lib.kda_mfma_probe(p, 4, 0, None, None) == _lib.KDA_ERR_INVALID_ARG
+    assert lib.kda_mfma_probe(None, 4, 10, None, None) == _lib.KDA_ERR_INVALID_ARG
+    assert lib.kda_mfma_probe(ctypes.c_void_p((1 << 20) + 4), 4, 10, None, None) == _lib.KDA_ERR_INVALID_ARG
