@@ -63,7 +63,8 @@ kda_status_t kda_copy_probe(const float* src, float* dst, int64_t n, void* strea
 /*
  * kda_mfma_probe — measurement probe, not part of the recurrence: blocks
  * workgroups of 256 threads, each wave issuing iters x 8 independent
- * v_mfma_f32_16x16x32_bf16 (the prefill's matrix product), to measure the
+ * v_mfma_f32_16x16x32_bf16 (the prefill's matrix product; iters rounded up
+ * to a multiple of 4), to measure the
  * matrix roof the prefill is compared with.  out: device buffer of
  * blocks x 256 x 4 floats (16-byte aligned) receiving the accumulators (so
  * the work is kept); *flops (host, may be NULL) receives the flops of the
