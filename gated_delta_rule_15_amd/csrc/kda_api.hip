@@ -242,6 +242,33 @@ kda_status_t kda_verify_block_prologue(const void* q, const void* k, const void*
                      state_out_pool, &pro, stream);
 }
 
+kda_status_t kda_verify_block_record(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                                    const float* state_pool, const int32_t* slots, int32_t N, int32_t gamma1,
+                                    int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t dtype, float scale, void* o,
+                                    float* record, const kda_prologue_t* prologue, void* stream) {
+  kda::Prologue pro;
+  if (!prologue_ok(prologue, pro)) return KDA_ERR_INVALID_ARG;
+  if (N < 0 || H <= 0 || gamma1 <= 0) return KDA_ERR_INVALID_ARG;
+  if (!dims_ok(d_k, d_v) || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
+  if (N == 0) return KDA_OK;
+  if (!q || !k || !v || !g || !beta || !state_pool || !o || !record) return KDA_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(record) % 16 != 0) return KDA_ERR_INVALID_ARG;
+  return hip_status(kda::launch_verify(q, k, v, g, beta, state_pool, slots, N, gamma1, H, dtype == KDA_BF16, scale,
+                                       o, static_cast<hipStream_t>(stream), &pro, record));
+}
+
+kda_status_t kda_verify_commit_record(const float* record, const void* v, const float* beta, float* state_pool,
+                                      const int32_t* slots, const int32_t* accepted_len, int32_t N, int32_t gamma1,
+                                      int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t dtype, void* stream) {
+  if (N < 0 || H <= 0 || gamma1 <= 0) return KDA_ERR_INVALID_ARG;
+  if (!dims_ok(d_k, d_v) || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
+  if (N == 0) return KDA_OK;
+  if (!record || !v || !beta || !state_pool || !accepted_len) return KDA_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(record) % 16 != 0) return KDA_ERR_INVALID_ARG;
+  return hip_status(kda::launch_commit_record(record, v, beta, state_pool, state_pool, slots, accepted_len, N, gamma1,
+                                              H, dtype == KDA_BF16, static_cast<hipStream_t>(stream)));
+}
+
 size_t kda_prefill_workspace_size(int32_t num_seqs, int64_t T_total, int32_t H, int32_t d_k, int32_t d_v,
                                   kda_dtype_t dtype, int32_t flags) {
   if (num_seqs <= 0 || T_total < 0 || H <= 0 || !dims_ok(d_k, d_v) || !dtype_ok(dtype)) return 0;

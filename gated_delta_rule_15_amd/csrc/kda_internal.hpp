@@ -27,7 +27,14 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const floa
 
 hipError_t launch_verify(const void* q, const void* k, const void* v, const float* g, const float* beta,
                          const float* state, const int32_t* slots, int N, int G, int H, bool bf16,
-                         float scale, void* o, hipStream_t stream, const Prologue* pro = nullptr);
+                         float scale, void* o, hipStream_t stream, const Prologue* pro = nullptr,
+                         float* record = nullptr);
+
+// The commit of the accepted prefix from a verify's record ([N, G, H, 2, 128] fp32 keys and
+// log-decays as the prologue verify used them), v and beta as given.
+hipError_t launch_commit_record(const float* record, const void* v, const float* beta, const float* state_in,
+                                float* state_out, const int32_t* slots, const int32_t* accepted_len, int N, int G,
+                                int H, bool bf16, hipStream_t stream);
 
 hipError_t launch_commit(const void* k, const void* v, const float* g, const float* beta,
                          const float* state_in, float* state_out, const int32_t* slots,

@@ -75,7 +75,18 @@ struct StepArgs {
   float pro_eps;
   int32_t pro_gate;   // prologue kernels: g holds gate logits
   float pro_gmin;
+  float* record;          // verify with the prologue, or null: each step's key and log-decay as used
+  const float* rec_in;    // commit from a record: keys and log-decays read from it (q, k, g unused)
 };
+
+// The raw-input record of a verify ("SGLang 和 Miles 为 Kimi K3 提供首日支持",
+// section "ReplaySSM：针对 KDA 状态的原始输入重放": the verify keeps each draft
+// step's inputs and the fold consumes what it kept): per (request, step, head)
+// the key after the prologue's normalisation and the log-decay after the gate
+// map, fp32, [N, G, H, 2, 128] (1 KB per step and head).
+__device__ __forceinline__ int64_t record_offset(int n, int t, int h, const StepArgs& a) {
+  return ((int64_t(n) * a.G + t) * a.H + h) * (2 * kD);
+}
 
 // Input prologue (the KDA math-details box of the Day-0 lesson page: unit keys
 // for the readout identity; the log-decay bounded below by a scaled sigmoid,
@@ -307,9 +318,10 @@ __device__ __forceinline__ float xor_lane(float x) {  // lane ^ XOR within 32 la
   return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x1F | (XOR << 10)));
 }
 
-template <class InT, bool READOUT, bool PRO>
+template <class InT, bool READOUT, bool PRO, bool REC = false>
 __device__ __forceinline__ void stage_block(Stage& st, const StepArgs& a, int n, int h, int col0, int b0, int last,
                                             int tid) {
+  static_assert(!(REC && (READOUT || PRO)), "a record serves the commit of the plain inputs' step");
   static_assert(kBlockT * 16 == kThreads / 2, "8 channels of one token per thread in the first half");
   constexpr int kVPieces = kWgCols * kBlockHalves / 4;  // v pieces per token
   constexpr int kVRounds = (kBlockT * kVPieces + kThreads / 2 - 1) / (kThreads / 2);
@@ -317,10 +329,21 @@ __device__ __forceinline__ void stage_block(Stage& st, const StepArgs& a, int n,
     const int t = tid >> 4, c8 = 8 * (tid & 15);
     const int tt = b0 + t <= last ? b0 + t : last;
     const int64_t vec = ((int64_t(n) * a.G + tt) * a.H + h) * kD + c8;
-    const auto k0 = InT::load4raw(a.k, vec);
-    const auto k1 = InT::load4raw(a.k, vec + 4);
-    float4 g0 = ld_f4(a.g + vec);
-    float4 g1 = ld_f4(a.g + vec + 4);
+    typename InT::raw4 k0{}, k1{};
+    float4 g0, g1, kr0{}, kr1{};
+    if constexpr (REC) {
+      // the key and log-decay the verify used, as it recorded them
+      const float* rec = a.rec_in + record_offset(n, tt, h, a) + c8;
+      kr0 = ld_f4(rec);
+      kr1 = ld_f4(rec + 4);
+      g0 = ld_f4(rec + kD);
+      g1 = ld_f4(rec + kD + 4);
+    } else {
+      k0 = InT::load4raw(a.k, vec);
+      k1 = InT::load4raw(a.k, vec + 4);
+      g0 = ld_f4(a.g + vec);
+      g1 = ld_f4(a.g + vec + 4);
+    }
     typename InT::raw4 q0{}, q1{};
     if constexpr (READOUT) {
       q0 = InT::load4raw(a.q, vec);
@@ -330,8 +353,13 @@ __device__ __forceinline__ void stage_block(Stage& st, const StepArgs& a, int n,
     if (tid < kBlockT) beta = a.beta[(int64_t(n) * a.G + (b0 + tid <= last ? b0 + tid : last)) * a.H + h];
 
     float k[8];
-    InT::unpack4(k0, k);
-    InT::unpack4(k1, k + 4);
+    if constexpr (REC) {
+      k[0] = kr0.x; k[1] = kr0.y; k[2] = kr0.z; k[3] = kr0.w;
+      k[4] = kr1.x; k[5] = kr1.y; k[6] = kr1.z; k[7] = kr1.w;
+    } else {
+      InT::unpack4(k0, k);
+      InT::unpack4(k1, k + 4);
+    }
     float qs[8];
     if constexpr (READOUT) {
       InT::unpack4(q0, qs);
@@ -368,6 +396,16 @@ __device__ __forceinline__ void stage_block(Stage& st, const StepArgs& a, int n,
 #pragma unroll
           for (int e = 0; e < 8; ++e) qs[e] = qs[e] * rq;
         }
+      }
+    }
+    if constexpr (PRO && READOUT) {
+      // the record: written once per (request, step, head), by the first column half's workgroup
+      if (a.record != nullptr && col0 == 0 && b0 + t <= last) {
+        float* rec = a.record + record_offset(n, b0 + t, h, a) + c8;
+        st_f4(rec, make_float4(k[0], k[1], k[2], k[3]));
+        st_f4(rec + 4, make_float4(k[4], k[5], k[6], k[7]));
+        st_f4(rec + kD, g0);
+        st_f4(rec + kD + 4, g1);
       }
     }
     *reinterpret_cast<float4*>(&st.k[t][c8]) = make_float4(k[0], k[1], k[2], k[3]);
@@ -498,7 +536,7 @@ __device__ __forceinline__ int work_index(int bid, int nblocks) {
 // workgroups leave the chip under-occupied and each runs 16 dependent steps.
 static_assert(kBlockHalves == 1 || kBlockHalves * kWgCols == kD, "halves cover the state");
 
-template <class InT, int MODE, bool PRO>
+template <class InT, int MODE, bool PRO, bool REC>
 __global__ __launch_bounds__(kThreads) void kda_step_kernel(StepArgs a) {
   static_assert(MODE != kDecode, "decode runs kda_decode_kernel");
   constexpr bool READOUT = (MODE != kCommit);
@@ -560,7 +598,7 @@ __global__ __launch_bounds__(kThreads) void kda_step_kernel(StepArgs a) {
   int c = 0;  // token steps so far (alternates the reduction buffers)
   for (int b0 = 0; b0 < steps; b0 += kBlockT) {
     if (b0 > 0) __syncthreads();  // every step of the previous block has read the stage
-    stage_block<InT, READOUT, PRO>(st, a, n, h, col0, b0, last, tid);
+    stage_block<InT, READOUT, PRO, REC>(st, a, n, h, col0, b0, last, tid);
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < NH; ++j) {
@@ -704,13 +742,13 @@ __global__ __launch_bounds__(kThreads) void kda_decode_kernel(StepArgs a, int n_
   }
 }
 
-template <int MODE, bool PRO>
+template <int MODE, bool PRO, bool REC = false>
 hipError_t launch_step_as(const StepArgs& a, bool bf16, hipStream_t stream) {
   const int64_t blocks = int64_t(a.N) * a.H * (kWgPerHead / kBlockHalves);
   if (bf16)
-    hipLaunchKernelGGL((kda_step_kernel<BF16, MODE, PRO>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((kda_step_kernel<BF16, MODE, PRO, REC>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((kda_step_kernel<F32, MODE, PRO>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((kda_step_kernel<F32, MODE, PRO, REC>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -762,8 +800,9 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const floa
 
 hipError_t launch_verify(const void* q, const void* k, const void* v, const float* g, const float* beta,
                          const float* state, const int32_t* slots, int N, int G, int H, bool bf16,
-                         float scale, void* o, hipStream_t stream, const Prologue* pro) {
+                         float scale, void* o, hipStream_t stream, const Prologue* pro, float* record) {
   StepArgs a{q, k, v, g, beta, state, nullptr, slots, nullptr, o, N, G, H, scale, device_cu_count(), 0, 0.0f, 0, 0.0f};
+  a.record = record;
   return launch_step<kVerify>(a, bf16, stream, pro);
 }
 
@@ -774,6 +813,15 @@ hipError_t launch_commit(const void* k, const void* v, const float* g, const flo
   StepArgs a{nullptr, k, v, g, beta, state_in, state_out, slots, accepted_len, nullptr, N, G, H, 1.0f, 0, 0, 0.0f, 0,
              0.0f};
   return launch_step<kCommit>(a, bf16, stream, pro);
+}
+
+hipError_t launch_commit_record(const float* record, const void* v, const float* beta, const float* state_in,
+                                float* state_out, const int32_t* slots, const int32_t* accepted_len, int N, int G,
+                                int H, bool bf16, hipStream_t stream) {
+  StepArgs a{nullptr, nullptr, v, nullptr, beta, state_in, state_out, slots, accepted_len, nullptr, N, G, H, 1.0f,
+             0, 0, 0.0f, 0, 0.0f};
+  a.rec_in = record;
+  return launch_step_as<kCommit, false, true>(a, bf16, stream);
 }
 
 }  // namespace kda

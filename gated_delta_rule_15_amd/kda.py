@@ -193,6 +193,60 @@ def kda_verify_commit(k, v, g, beta, state_pool, accepted_len, slots=None, prolo
                    "kda_verify_commit_prologue")
 
 
+def kda_verify_block_record(q, k, v, g, beta, state_pool, prologue: Prologue, record=None, o=None, slots=None,
+                            scale: float = 1.0):
+    """kda_verify_block_record: the prologue verify that also writes its raw-input record (the key and
+    log-decay of every draft step as used, [N, G, H, 2, 128] fp32).  Returns (o, record)."""
+    if prologue is None:
+        raise ValueError("prologue is required")
+    N, G, H, _ = q.shape
+    dt, dev = q.dtype, q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, (N, G, H, D), dt, dev)
+    _need(g, "g", (N, G, H, D), torch.float32, dev)
+    _need(beta, "beta", (N, G, H), torch.float32, dev)
+    if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (H, D, D):
+        raise ValueError("state_pool must be [P, H, 128, 128]")
+    _need(state_pool, "state_pool", state_pool.shape, torch.float32, dev)
+    if slots is not None:
+        _need(slots, "slots", (N,), torch.int32, dev)
+    elif state_pool.shape[0] < N:
+        raise ValueError("state_pool has fewer rows than requests")
+    if o is None:
+        o = torch.empty((N, G, H, D), dtype=dt, device=dev)
+    _need(o, "o", (N, G, H, D), dt, dev)
+    if record is None:
+        record = torch.empty((N, G, H, 2, D), dtype=torch.float32, device=dev)
+    _need(record, "record", (N, G, H, 2, D), torch.float32, dev)
+    pc = prologue._c()
+    _lib.check(_lib.load().kda_verify_block_record(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool),
+                                                   _ptr(slots), N, G, H, D, D, _dtype_code(q), float(scale), _ptr(o),
+                                                   _ptr(record), ctypes.addressof(pc), _stream()),
+               "kda_verify_block_record")
+    return o, record
+
+
+def kda_verify_commit_record(record, v, beta, state_pool, accepted_len, slots=None):
+    """kda_verify_commit_record: replay each request's accepted prefix, in place, from the verify's record
+    (keys and log-decays as the verify used them) with v and beta as given."""
+    N, G, H, _ = v.shape
+    dev = v.device
+    _need(record, "record", (N, G, H, 2, D), torch.float32, dev)
+    _need(v, "v", (N, G, H, D), v.dtype, dev)
+    _need(beta, "beta", (N, G, H), torch.float32, dev)
+    if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (H, D, D):
+        raise ValueError("state_pool must be [P, H, 128, 128]")
+    _need(state_pool, "state_pool", state_pool.shape, torch.float32, dev)
+    _need(accepted_len, "accepted_len", (N,), torch.int32, dev)
+    if slots is not None:
+        _need(slots, "slots", (N,), torch.int32, dev)
+    elif state_pool.shape[0] < N:
+        raise ValueError("state_pool has fewer rows than requests")
+    _lib.check(_lib.load().kda_verify_commit_record(_ptr(record), _ptr(v), _ptr(beta), _ptr(state_pool), _ptr(slots),
+                                                    _ptr(accepted_len), N, G, H, D, D, _dtype_code(v), _stream()),
+               "kda_verify_commit_record")
+
+
 def kda_verify_commit_prologue(k, v, g, beta, state_pool, accepted_len, prologue: Prologue, **kw):
     """kda_verify_commit with the input prologue (required)."""
     if prologue is None:

@@ -172,6 +172,37 @@ kda_status_t kda_verify_commit_prologue(const void* k, const void* v, const floa
                                         kda_dtype_t dtype, const kda_prologue_t* prologue, void* stream);
 
 /*
+ * The raw-input record of a verify ("SGLang 和 Miles 为 Kimi K3 提供首日支持",
+ * section "ReplaySSM：针对 KDA 状态的原始输入重放": the verify keeps each draft
+ * step's inputs, about 1 KB per step, instead of a state snapshot, and the
+ * fold replays the accepted prefix from what it kept).
+ *
+ * kda_verify_block_record — kda_verify_block_prologue (no fused commit) that
+ * also writes, for every request n, draft step t and head h, the key and the
+ * log-decay the verify used after the prologue: record [N, gamma1, H, 2, 128]
+ * fp32 (device, 16-byte aligned, caller-owned), [n, t, h, 0, :] the key
+ * (normalised when l2norm_qk is set), [n, t, h, 1, :] the log-decay (mapped
+ * from the logit when gate_logits is set).  record is required
+ * (KDA_ERR_INVALID_ARG if NULL or misaligned); other arguments and errors as
+ * kda_verify_block_prologue.
+ *
+ * kda_verify_commit_record — the commit of the accepted prefix that folds the
+ * recorded keys and log-decays (no prologue, no recomputation) with v and
+ * beta as given ([N, gamma1, H, 128] in `dtype`, [N, gamma1, H] fp32), in
+ * place on state_pool; accepted_len as kda_verify_commit.  The state it
+ * writes is bit-identical to kda_verify_commit_prologue's with the verify's
+ * prologue, and so to as many prologue decode steps.
+ */
+kda_status_t kda_verify_block_record(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                                    const float* state_pool, const int32_t* slots, int32_t N, int32_t gamma1,
+                                    int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t dtype, float scale, void* o,
+                                    float* record, const kda_prologue_t* prologue, void* stream);
+
+kda_status_t kda_verify_commit_record(const float* record, const void* v, const float* beta, float* state_pool,
+                                      const int32_t* slots, const int32_t* accepted_len, int32_t N, int32_t gamma1,
+                                      int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t dtype, void* stream);
+
+/*
  * kda_prefill — chunk-parallel prefill of a packed ragged batch.
  *
  * Computes, for every sequence n (tokens cu_seqlens[n] .. cu_seqlens[n+1]-1)

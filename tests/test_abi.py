@@ -36,6 +36,7 @@ def test_header_declares_the_entry_points():
                  "kda_verify_commit_prologue", "kda_prefill_prologue", "kda_contract_prefill",
                  "kda_contract_decode", "kda_contract_state", "kda_contract_verify", "kda_contract_commit",
                  "kda_contract_commit_stash", "kda_contract_prefill_split",
+                 "kda_verify_block_record", "kda_verify_commit_record",
                  "kda_copy_probe", "kda_mfma_probe", "kda_status_string", "kda_version"):
         assert name in syms
     assert set(syms) == set(_lib.SIGNATURES), "binding signatures and header disagree"
@@ -244,3 +245,21 @@ def test_mfma_probe_argument_errors(lib):
     assert lib.kda_mfma_probe(p, 4, 0, None, None) == _lib.KDA_ERR_INVALID_ARG
     assert lib.kda_mfma_probe(None, 4, 10, None, None) == _lib.KDA_ERR_INVALID_ARG
     assert lib.kda_mfma_probe(ctypes.c_void_p((1 << 20) + 4), 4, 10, None, None) == _lib.KDA_ERR_INVALID_ARG
+
+
+def test_record_entry_points_argument_errors(lib):
+    """The record verify needs a prologue and a record buffer; the record commit needs the record."""
+    p = ctypes.c_void_p(1 << 20)
+    # no prologue
+    assert lib.kda_verify_block_record(p, p, p, p, p, p, None, 2, 8, 2, 128, 128, _lib.KDA_BF16, 1.0, p, p, None,
+                                       None) == _lib.KDA_ERR_INVALID_ARG
+    # no record
+    assert lib.kda_verify_commit_record(None, p, p, p, None, p, 2, 8, 2, 128, 128, _lib.KDA_BF16,
+                                        None) == _lib.KDA_ERR_INVALID_ARG
+    # misaligned record
+    assert lib.kda_verify_commit_record(ctypes.c_void_p((1 << 20) + 4), p, p, p, None, p, 2, 8, 2, 128, 128,
+                                        _lib.KDA_BF16, None) == _lib.KDA_ERR_INVALID_ARG
+    assert lib.kda_verify_commit_record(p, p, p, p, None, p, 2, 8, 2, 64, 128, _lib.KDA_BF16,
+                                        None) == _lib.KDA_ERR_UNSUPPORTED
+    assert lib.kda_verify_commit_record(None, None, None, None, None, None, 0, 8, 2, 128, 128, _lib.KDA_BF16,
+                                        None) == _lib.KDA_OK

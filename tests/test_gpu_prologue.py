@@ -158,3 +158,37 @@ def test_prefill_prologue_wide_and_transitions():
                                                p.f64("beta")[cu[n]:cu[n + 1], h]) for h in range(H)])
                       for n in range(0, N, 5)])
     check_parity(to_f64(M)[::5], M_ref, 2e-3, unit_slices(M_ref.shape[0], H), tag="prefill prologue wide M")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("l2,gate", VARIANTS)
+def test_record_verify_and_commit(dtype, l2, gate):
+    """The raw-input record (ReplaySSM): the recording verify gives the prologue verify's outputs bit for
+    bit; the record holds each step's key and log-decay as the prologue made them (against the oracle's
+    prologue at fp32 rounding); the commit that folds the record writes the prologue commit's state bit
+    for bit, and it matches the oracle."""
+    from gated_delta_rule_15_amd.kda import (kda_verify_block, kda_verify_block_record, kda_verify_commit,
+                                             kda_verify_commit_record)
+    N, G, H = 10, 8, 3
+    b = _valid_inputs(gen.step_batch(seed=65, N=N, G=G, H=H, dtype=dtype, accepted=True, raw=True), l2, gate)
+    d = steps_to_dev(b)
+    p = _prologue(l2, gate)
+    o_ref_gpu = kda_verify_block(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], scale=0.8, prologue=p)
+    o_rec, rec = kda_verify_block_record(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], prologue=p,
+                                         scale=0.8)
+    bits = torch.int16 if dtype == "bf16" else torch.int32
+    torch.cuda.synchronize()
+    assert torch.equal(o_rec.view(bits), o_ref_gpu.view(bits))
+    q_ref, k_ref, g_ref = _ref_inputs(b.f64("q"), b.f64("k"), b.f64("g"), l2, gate)
+    # the record's key and log-decay against the oracle's prologue (fp32 arithmetic on the device)
+    check_parity(rec[:, :, :, 0], k_ref, 1e-6, unit_slices(N, H, steps=True), tag=f"record k {dtype}")
+    check_parity(rec[:, :, :, 1], g_ref, 1e-6, unit_slices(N, H, steps=True), tag=f"record g {dtype}")
+    # the commit from the record equals the recomputing prologue commit, bit for bit
+    S_pro = d["state"].clone()
+    kda_verify_commit(d["k"], d["v"], d["g"], d["beta"], S_pro, d["accepted_len"], prologue=p)
+    S_rec = d["state"].clone()
+    kda_verify_commit_record(rec, d["v"], d["beta"], S_rec, d["accepted_len"])
+    torch.cuda.synchronize()
+    assert torch.equal(S_rec.view(torch.int32), S_pro.view(torch.int32))
+    _, S_ref = orc.verify_block(q_ref, k_ref, b.f64("v"), g_ref, b.f64("beta"), b.f64("state"), b.accepted_len, 0.8)
+    check_parity(S_rec, S_ref, TOL[dtype], unit_slices(N, H), tag=f"record commit {dtype} l2={l2} gate={gate} S")
