@@ -37,6 +37,20 @@
 // Inputs are fetched one chunk ahead into registers (prep: g, k, q, beta in
 // phase B; state: v in phase C).  Two waves share each SIMD, so one wave's
 // MFMA work overlaps the other's LDS and VALU work.
+//
+// Builds (template MODE and wave counts):
+//   Fused  the decomposition above: 4 state waves of 16 or 32 columns with 8
+//          or 4 prep waves; or, for states and transitions without outputs on
+//          a grid that fills the device, 8 state waves (4 hold the state, 4 the
+//          transition, 32 columns each) sharing 4 prep waves, so each chunk is
+//          prepared once for both.
+//   Prep   the split path's preparation: one workgroup per (chunk slot, head)
+//          builds that chunk's operand set and writes it to the caller's
+//          workspace (chunk-parallel: the sets do not depend on the state).
+//   State  the split path's walk: state waves only, one workgroup per
+//          (sequence, head), staging chunk c+1's set from the workspace while
+//          chunk c runs (8 waves of 16 columns; 16 when the transition walks
+//          beside the state).
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 #include "kda_mfma.hpp"
