@@ -360,13 +360,14 @@ def kda_prefill_prologue(q, k, v, g, beta, cu_seqlens, prologue: Prologue, **kw)
 
 def kda_prefill_ordered(q, k, v, g, beta, cu_seqlens, seq_order, cu_seqlens_host=None, initial_state=None,
                         final_state=None, o=None, transition_out=None, scale: float = 1.0, with_output: bool = True,
-                        with_final_state: bool = True, workspace="auto", ws_flags: int = 0):
+                        with_final_state: bool = True, workspace="auto", ws_flags: int = 0,
+                        prologue: Optional[Prologue] = None):
     """kda_prefill whose sequences are started in the order ``seq_order`` (device int32 [N], a
     permutation of 0..N-1; e.g. longest first).  Same results as kda_prefill, bit for bit."""
     if seq_order is None:
         raise ValueError("seq_order is required")
     return _prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, initial_state, final_state, o, transition_out,
-                    scale, with_output, with_final_state, seq_order, None, workspace, ws_flags)
+                    scale, with_output, with_final_state, seq_order, prologue, workspace, ws_flags)
 
 
 def _prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, initial_state, final_state, o, transition_out, scale,
@@ -407,12 +408,14 @@ def _prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, initial_state, final
                                                o is not None)
             if 0 < n <= AUTO_WORKSPACE_MAX:
                 workspace = torch.empty(n, dtype=torch.uint8, device=dev)
-    if workspace is not None:
-        if cu_seqlens_host is None:
-            raise ValueError("a workspace needs cu_seqlens_host")
-        if not workspace.is_cuda or workspace.device != dev or workspace.dtype != torch.uint8 \
-                or not workspace.is_contiguous():
-            raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
+    if workspace is not None or (prologue is not None and seq_order is not None):
+        # kda_prefill_ex: a workspace, or a start order with the prologue
+        if workspace is not None:
+            if cu_seqlens_host is None:
+                raise ValueError("a workspace needs cu_seqlens_host")
+            if not workspace.is_cuda or workspace.device != dev or workspace.dtype != torch.uint8 \
+                    or not workspace.is_contiguous():
+                raise ValueError("workspace must be a contiguous uint8 tensor on the inputs' device")
         pc = prologue._c() if prologue is not None else None
         if seq_order is not None:
             _need(seq_order, "seq_order", (N,), torch.int32, dev)
@@ -420,12 +423,11 @@ def _prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, initial_state, final
                                       _ptr(cu_seqlens_host), N, H, D, D, _dtype_code(q), float(scale),
                                       _ptr(initial_state), _ptr(final_state), _ptr(o), _ptr(transition_out),
                                       _ptr(seq_order), ctypes.addressof(pc) if pc is not None else None,
-                                      _ptr(workspace), workspace.numel(), int(ws_flags), _stream()),
+                                      _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                                      int(ws_flags), _stream()),
                    "kda_prefill_ex")
         return o, final_state
     if prologue is not None:
-        if seq_order is not None:
-            raise ValueError("the prologue prefill takes no start order")
         pc = prologue._c()
         _lib.check(lib.kda_prefill_prologue(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
                                             _ptr(cu_seqlens_host), N, H, D, D, _dtype_code(q), float(scale),

@@ -115,14 +115,15 @@ def plan_segments(cu_seqlens_host, seg_len: int, cut_longer_than: int = 0) -> Se
 
 def kda_prefill_segmented(q, k, v, g, beta, cu_seqlens_host, seg_len: Optional[int] = 65536, initial_state=None,
                           o=None, final_state=None, scale: float = 1.0, plan: Optional[SegmentPlan] = None,
-                          work: Optional[dict] = None):
+                          work: Optional[dict] = None, prologue: Optional[kda.Prologue] = None):
     """Prefill of a packed ragged batch with long sequences split into segments.
 
     Same arguments and results as ``kda.kda_prefill`` (cu_seqlens_host: CPU
     int32 [N + 1]); returns (o, final_state).  ``seg_len=None`` picks it with
     ``auto_seg_len``.  With a ``plan``, preallocated buffers ``work`` from
     ``alloc_work`` and the outputs ``o`` and ``final_state`` passed in, a call
-    allocates no device memory.
+    allocates no device memory.  ``prologue``: raw q, k and gate logits, as
+    ``kda.kda_prefill(..., prologue=...)``; both passes apply it.
     """
     dev = q.device
     H = q.shape[1]
@@ -156,7 +157,7 @@ def kda_prefill_segmented(q, k, v, g, beta, cu_seqlens_host, seg_len: Optional[i
         # this small), so both passes walk the same chunks and share one preparation
         kda.kda_prefill(q, k, v, g, beta, work["rows_d"], work["rows_h"], final_state=work["St_all"],
                         transition_out=work["M_all"], with_output=False, scale=scale, workspace=ws,
-                        ws_flags=_lib.KDA_WS_KEEP_OUTPUT_OPERANDS)
+                        ws_flags=_lib.KDA_WS_KEEP_OUTPUT_OPERANDS, prologue=prologue)
     for n in plan.multi:
         r = plan.row_of_seq[n]
         nf = len(r) - 1
@@ -171,7 +172,7 @@ def kda_prefill_segmented(q, k, v, g, beta, cu_seqlens_host, seg_len: Optional[i
             # pass 1: fragments of segments 0 .. nf-1
             M, St = work["M"][n], work["St"][n]
             kda.kda_prefill(q, k, v, g, beta, work["frag_cu"][n], work["frag_cu_h"][n], final_state=St,
-                            transition_out=M, with_output=False, scale=scale, workspace=None)
+                            transition_out=M, with_output=False, scale=scale, workspace=None, prologue=prologue)
         # compose: entry states of segments 1 .. nf (segment 0's is the sequence's own),
         # written into pass 2's rows; S_in[0] lands on row r.start, which already holds S_in0
         kda.kda_compose_segments(M, St, init2[r.start], S_in=init2[r.start:r.start + nf],
@@ -180,7 +181,8 @@ def kda_prefill_segmented(q, k, v, g, beta, cu_seqlens_host, seg_len: Optional[i
     # pass 2: every segment from its entry state, longest rows started first
     kda.kda_prefill_ordered(q, k, v, g, beta, work["rows_d"], work["order2"], work["rows_h"], initial_state=init2,
                             final_state=None if all_cut else fin2, with_final_state=not all_cut, o=o, scale=scale,
-                            workspace=ws, ws_flags=_lib.KDA_WS_PREPARED if ws is not None else 0)
+                            workspace=ws, ws_flags=_lib.KDA_WS_PREPARED if ws is not None else 0,
+                            prologue=prologue)
     if not all_cut:
         torch.index_select(fin2, 0, work["last_rows"], out=final_state)
     return o, final_state

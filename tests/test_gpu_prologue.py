@@ -192,3 +192,25 @@ def test_record_verify_and_commit(dtype, l2, gate):
     assert torch.equal(S_rec.view(torch.int32), S_pro.view(torch.int32))
     _, S_ref = orc.verify_block(q_ref, k_ref, b.f64("v"), g_ref, b.f64("beta"), b.f64("state"), b.accepted_len, 0.8)
     check_parity(S_rec, S_ref, TOL[dtype], unit_slices(N, H), tag=f"record commit {dtype} l2={l2} gate={gate} S")
+
+
+@pytest.mark.parametrize("lens", [[1500, 777, 64], [1500, 777]], ids=["mixed", "all_cut"])
+@pytest.mark.parametrize("split", [False, True])
+def test_segmented_prefill_with_prologue(split, lens):
+    """The segmented driver on raw inputs: both passes apply the prologue (single-kernel passes, or split
+    passes sharing one preparation), and the result matches the oracle's prologue then recurrence."""
+    from gated_delta_rule_15_amd.long_context import alloc_work, kda_prefill_segmented, plan_segments
+    p = gen.packed_batch(seed=67, seqlens=lens, H=2, dtype="bf16", init_state=[False] + [True] * (len(lens) - 1),
+                         raw=True)
+    d = packed_to_dev(p)
+    plan = plan_segments(p.cu_seqlens, 256)
+    work = alloc_work(plan, 2, d["q"].device, d["q"].dtype, split=split)
+    assert (work["ws"] is not None) == split
+    o, S = kda_prefill_segmented(d["q"], d["k"], d["v"], d["g"], d["beta"], p.cu_seqlens, plan=plan, work=work,
+                                 initial_state=d["initial_state"], scale=0.8, prologue=_prologue(True, True))
+    torch.cuda.synchronize()
+    q, k, g = _ref_inputs(p.f64("q"), p.f64("k"), p.f64("g"), True, True)
+    o_ref, S_ref = orc.prefill(q, k, p.f64("v"), g, p.f64("beta"), p.cu_seqlens, p.initial_state, 0.8)
+    tag = f"segmented prologue split={split} {len(lens)} seqs"
+    check_parity(o, o_ref, TOL["bf16"], packed_slices(p.cu_seqlens, 2), bf16_out=True, tag=f"{tag} o")
+    check_parity(S, S_ref, TOL["bf16"], unit_slices(len(lens), 2), tag=f"{tag} S")
