@@ -139,13 +139,126 @@ __global__ __launch_bounds__(kThreads) void kda_compose_kernel(const float* __re
   if (i == n_seg) publish(n_seg);
 }
 
+// Staged variant for grids that leave CUs idle (at most one workgroup per CU:
+// its LDS holds two copies of M): each segment's M is loaded with coalesced
+// 16-byte loads after the current product's MFMAs were issued, written to the
+// free LDS buffer at the end of the step, and read from LDS as the A operand
+// in the next; the contraction slots and their order are those of
+// kda_compose_kernel, so both give the same bits.  The loads leave the matrix
+// section, which measured 2.0-2.1 us per step against 2.5 us.
+constexpr int kMLd = kD + 4;         // LDS row stride of a staged M (floats)
+constexpr int kMPieces = kD * kD / 4 / kThreads;  // float4 pieces of M per thread (8)
+
+__global__ __launch_bounds__(kThreads) void kda_compose_staged_kernel(const float* __restrict__ M,
+                                                               const float* __restrict__ S_tilde,
+                                                               const float* __restrict__ S_in0,
+                                                               float* __restrict__ S_in,
+                                                               float* __restrict__ S_final, int n_seg,
+                                                               int H) {
+  const int id = blockIdx.x;  // numbered as in kda_compose_kernel
+  const int slice = (id >> 3) & 7;
+  const int h = (id >> 6) * 8 + (id & 7);
+  if (h >= H) return;
+  __shared__ __align__(16) float curT[kCols][kD + 4];  // running S_in slice, transposed: [column][row]
+  __shared__ __align__(16) float Ms[2][kD][kMLd];       // M of the current and the next segment
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int q = lane >> 4;
+  const int n = lane & 15;
+  const int c0 = slice * kCols;
+  const int64_t tile = int64_t(kD) * kD;
+  const int last = n_seg > 0 ? n_seg - 1 : 0;
+  auto seg_base = [&](int i) { return (int64_t(i <= last ? i : last) * H + h) * tile; };
+  const int row = wave * 16 + 4 * q;  // this lane's output rows row .. row + 3, column c0 + n
+
+  // M pieces: thread t takes float4 e = t + 512 j (rows 4 j .. , columns 4 (t % 32))
+  float4 mr[kMPieces];
+  auto load_m = [&](int i) {
+    const float* src = M + seg_base(i);
+#pragma unroll
+    for (int j = 0; j < kMPieces; ++j) mr[j] = ld_f4(src + 4 * (tid + kThreads * j));
+  };
+  auto store_m = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < kMPieces; ++j) {
+      const int e = tid + kThreads * j;
+      *reinterpret_cast<float4*>(&Ms[buf][e >> 5][4 * (e & 31)]) = mr[j];
+    }
+  };
+  float st[4];
+  auto load_st = [&](int i) {
+    const int64_t b = seg_base(i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) st[e] = S_tilde[b + int64_t(row + e) * kD + c0 + n];
+  };
+
+  // entry state of segment 0, and M(0) into LDS
+  for (int e = tid; e < kD * kCols; e += kThreads) {
+    const int r = e / kCols, c = e % kCols;
+    curT[c][r] = S_in0 ? S_in0[h * tile + int64_t(r) * kD + c0 + c] : 0.0f;
+  }
+  if (n_seg > 0) {
+    load_m(0);
+    store_m(0);
+    load_st(0);
+    load_m(1);
+  }
+  __syncthreads();
+
+  auto publish = [&](int i) {
+    float* dst = (i < n_seg) ? S_in + (int64_t(i) * H + h) * tile : S_final ? S_final + h * tile : nullptr;
+    static_assert(kD * kCols / 4 == kThreads, "one 16-byte piece of the slice per thread");
+    if (dst != nullptr) {
+      const int r = tid / (kCols / 4), c4 = 4 * (tid % (kCols / 4));
+      st_f4(dst + int64_t(r) * kD + c0 + c4, make_float4(curT[c4][r], curT[c4 + 1][r], curT[c4 + 2][r], curT[c4 + 3][r]));
+    }
+  };
+
+  for (int i = 0; i < n_seg; ++i) {
+    publish(i);
+    // S_in(i+1) = M(i) S_in(i) + S~(i): A from Ms[i % 2], B from curT
+    f32x4v acc[2];
+    acc[0] = f32x4v{st[0], st[1], st[2], st[3]};
+    acc[1] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    const float* arow = &Ms[i & 1][wave * 16 + n][4 * q];
+    const float* bcol = &curT[n][4 * q];
+#pragma unroll
+    for (int s4 = 0; s4 < 8; ++s4) {
+      const float4 a4 = *reinterpret_cast<const float4*>(arow + 16 * s4);
+      const float4 b4 = *reinterpret_cast<const float4*>(bcol + 16 * s4);
+      const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+      const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc[e & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], bv[e], acc[e & 1], 0, 0, 0);
+    }
+    __syncthreads();  // every wave has read S_in(i) and M(i)
+    {
+      const f32x4v v = acc[0] + acc[1];
+      *reinterpret_cast<float4*>(&curT[n][row]) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+    // M(i+1) (loaded during step i - 1) into the other buffer; then the next loads
+    store_m((i + 1) & 1);
+    load_st(i + 1);
+    load_m(i + 2);
+    __syncthreads();
+  }
+  publish(n_seg);
+}
+
 }  // namespace
 
 hipError_t launch_compose(const float* M, const float* S_tilde, const float* S_in0, float* S_in,
                           float* S_final, int n_seg, int H, hipStream_t stream) {
   const unsigned blocks = unsigned(((H + 7) / 8) * 64);
-  hipLaunchKernelGGL(kda_compose_kernel, dim3(blocks), dim3(kThreads), 0, stream, M, S_tilde, S_in0,
-                     S_in, S_final, n_seg, H);
+  if (int64_t(blocks) <= device_cu_count())
+    hipLaunchKernelGGL(kda_compose_staged_kernel, dim3(blocks), dim3(kThreads), 0, stream, M, S_tilde, S_in0,
+                       S_in, S_final, n_seg, H);
+  else
+    hipLaunchKernelGGL(kda_compose_kernel, dim3(blocks), dim3(kThreads), 0, stream, M, S_tilde, S_in0,
+                       S_in, S_final, n_seg, H);
   return hipGetLastError();
 }
 

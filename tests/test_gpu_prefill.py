@@ -440,3 +440,27 @@ def test_state_and_transition_build_bitwise(dtype):
     assert torch.equal(M1.view(torch.int32), M2.view(torch.int32))
     _check(p, o2, S1, f"state+transition build {dtype}")
     _check_transitions(p, M1, f"state+transition build {dtype}")
+
+
+@pytest.mark.parametrize("n_seg", [1, 2, 5])
+def test_compose_kernels_agree_bitwise(n_seg):
+    """A scan over few heads takes the staged kernel (M through LDS), one over many heads the register
+    kernel; they use the same contraction order, so the heads both compute come out bit for bit alike,
+    and the oracle agrees with both (40 heads: 320 workgroups, more than the CUs of the part)."""
+    from gated_delta_rule_15_amd.kda import kda_compose_segments
+    rng = np.random.default_rng(50 + n_seg)
+    H = 40
+    M = (rng.standard_normal((n_seg, H, 128, 128)) / np.sqrt(128)).astype(np.float32)
+    St = rng.standard_normal((n_seg, H, 128, 128)).astype(np.float32)
+    S0 = rng.standard_normal((H, 128, 128)).astype(np.float32)
+    big = kda_compose_segments(to_dev(M), to_dev(St), to_dev(S0))
+    few = kda_compose_segments(to_dev(np.ascontiguousarray(M[:, :3])), to_dev(np.ascontiguousarray(St[:, :3])),
+                               to_dev(np.ascontiguousarray(S0[:3])))
+    torch.cuda.synchronize()
+    assert torch.equal(big[0][:, :3].contiguous().view(torch.int32), few[0].view(torch.int32))
+    assert torch.equal(big[1][:3].contiguous().view(torch.int32), few[1].view(torch.int32))
+    for h in (0, 2, 39):
+        ref_in, ref_fin = orc.compose(M[:, h], St[:, h], S0[h])
+        check_parity(big[0][:, h], ref_in, 1e-5, [(f"segment {i}", np.s_[i]) for i in range(n_seg)],
+                     tag=f"compose 40 heads, head {h}")
+        check_parity(big[1][h], ref_fin, 1e-5, tag=f"compose 40 heads, head {h} final")
