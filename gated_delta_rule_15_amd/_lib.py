@@ -11,6 +11,7 @@ KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP, KDA_ERR_WORKSPACE
 KDA_F32, KDA_BF16 = 0, 1
 KDA_WS_PREPARED, KDA_WS_KEEP_OUTPUT_OPERANDS = 1, 2
 KDA_PREFILL_TRANSITIONS, KDA_PREFILL_NO_OUTPUT = 1, 2
+KDA_COMPOSE_SPLIT_BF16 = 1
 
 # (name, restype, argtypes) for every symbol include/kda.h declares
 _P = ctypes.c_void_p
@@ -49,6 +50,7 @@ SIGNATURES = {
                                                 _P, _I, _P, _P]),
     "kda_prefill_checkpoint_count": (ctypes.c_int64, [_P, _I, _I]),
     "kda_compose_segments": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
+    "kda_compose_segments_ex": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "kda_contract_prefill": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _F, _P, _P,
                                             _P, _P, _P, _P]),
     "kda_contract_prefill_split": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _F, _P,

@@ -365,12 +365,19 @@ int64_t kda_prefill_checkpoint_count(const int32_t* cu_seqlens_host, int32_t num
 kda_status_t kda_compose_segments(const float* M, const float* S_tilde, const float* S_in0,
                                   float* S_in, float* S_final, int32_t n_seg, int32_t H,
                                   int32_t d_k, int32_t d_v, void* stream) {
+  return kda_compose_segments_ex(M, S_tilde, S_in0, S_in, S_final, n_seg, H, d_k, d_v, 0, stream);
+}
+
+kda_status_t kda_compose_segments_ex(const float* M, const float* S_tilde, const float* S_in0,
+                                     float* S_in, float* S_final, int32_t n_seg, int32_t H,
+                                     int32_t d_k, int32_t d_v, int32_t flags, void* stream) {
   if (n_seg < 0 || H <= 0) return KDA_ERR_INVALID_ARG;
+  if (flags & ~KDA_COMPOSE_SPLIT_BF16) return KDA_ERR_INVALID_ARG;
   if (!dims_ok(d_k, d_v)) return KDA_ERR_UNSUPPORTED;
   if (n_seg == 0 && !S_final) return KDA_OK;
   if ((n_seg > 0 && (!M || !S_tilde || !S_in))) return KDA_ERR_INVALID_ARG;
   return hip_status(kda::launch_compose(M, S_tilde, S_in0, S_in, S_final, n_seg, H,
-                                        static_cast<hipStream_t>(stream)));
+                                        (flags & KDA_COMPOSE_SPLIT_BF16) != 0, static_cast<hipStream_t>(stream)));
 }
 
 kda_status_t kda_contract_prefill(const void* q, const void* k, const void* v, const float* g,

@@ -21,6 +21,7 @@
 // wave, well inside the wave's outstanding-load counter).
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
+#include "kda_mfma.hpp"
 
 namespace kda {
 namespace {
@@ -242,18 +243,159 @@ __global__ __launch_bounds__(kThreads) void kda_compose_staged_kernel(const floa
     // M(i+1) (loaded during step i - 1) into the other buffer; then the next loads
     store_m((i + 1) & 1);
     load_st(i + 1);
+    __builtin_amdgcn_sched_barrier(0);  // S~ loads first: the next step waits only for them
     load_m(i + 2);
     __syncthreads();
   }
   publish(n_seg);
 }
 
+// Split-operand variant (bf16 inputs' precision class): the same scan with
+// each step's products on bf16 MFMA (v_mfma_f32_16x16x32_bf16).  Both operands
+// are split as x = hi + lo (hi = bf16(x), lo = bf16(x - hi)) and a product is
+// hi*hi + hi*lo + lo*hi with fp32 accumulation, about 16 significant bits per
+// operand: three 32-deep MFMAs do the work of sixteen 4-deep fp32 ones, ~5x
+// the matrix rate.  M is staged through LDS as in the fp32 staged kernel, split
+// into a hi and a lo plane when written there, with its global loads two steps
+// ahead (two register sets); the running state is kept in fp32 (for
+// the published entry states) and as hi/lo planes (the B operand).  Lane group
+// q takes the contraction indices k = 32 s + 8 q + e (s = 0..3, e = 0..7), one
+// 16-byte read per plane and operand.  Three accumulators (one per part, the
+// S~ values in the first) are summed as acc0 + (acc1 + acc2).  A step measured
+// 1.8 us against 2.0 us for the fp32 staged kernel: at this size it is bound by
+// moving M (64 KB per step through the load path and LDS), not by the matrix
+// rate.  LDS: 153 KB, one workgroup per CU; larger grids run in rounds.
+constexpr int kHRow = (kD + 8) * 2;          // bytes per row of a bf16 plane (272: rows 4 banks apart)
+constexpr int kMPlane = kD * kHRow;          // one plane of a staged M
+constexpr int kBPlane = kCols * kHRow;       // one plane of the running slice, [column][row]
+
+// One step's global operands as this thread holds them: its eight 16-byte
+// pieces of the next M (staged into LDS at the end of the step) and the S~
+// values its accumulators start from.
+struct StepOps {
+  float4 m[kMPieces];
+  float st[4];
+};
+
+__global__ __launch_bounds__(kThreads) void kda_compose_split_kernel(const float* __restrict__ M,
+                                                                    const float* __restrict__ S_tilde,
+                                                                    const float* __restrict__ S_in0,
+                                                                    float* __restrict__ S_in,
+                                                                    float* __restrict__ S_final, int n_seg,
+                                                                    int H) {
+  const int id = blockIdx.x;  // numbered as in kda_compose_kernel
+  const int slice = (id >> 3) & 7;
+  const int h = (id >> 6) * 8 + (id & 7);
+  if (h >= H) return;
+  __shared__ __align__(16) float curT[kCols][kD + 4];  // running S_in slice, fp32, [column][row]
+  __shared__ __align__(16) char curB[2 * kBPlane];     // the same as hi and lo planes
+  __shared__ __align__(16) char Ms[2][2 * kMPlane];    // M of the current and the next segment, hi and lo planes
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int q = lane >> 4;
+  const int n = lane & 15;
+  const int c0 = slice * kCols;
+  const int64_t tile = int64_t(kD) * kD;
+  const int last = n_seg > 0 ? n_seg - 1 : 0;
+  auto seg_base = [&](int i) { return (int64_t(i <= last ? i : last) * H + h) * tile; };
+  const int row = wave * 16 + 4 * q;  // this lane's output rows row .. row + 3, column c0 + n
+
+  // step i reads S~(i) and stages M(i + 1): both are loaded two steps ahead,
+  // S~ first, so that a step waits only for the loads of the step before it
+  auto load_ops = [&](StepOps& x, int i) {
+    const int64_t b = seg_base(i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x.st[e] = S_tilde[b + int64_t(row + e) * kD + c0 + n];
+    __builtin_amdgcn_sched_barrier(0);
+    const float* src = M + seg_base(i + 1);
+#pragma unroll
+    for (int j = 0; j < kMPieces; ++j) x.m[j] = ld_f4(src + 4 * (tid + kThreads * j));
+  };
+  auto store_m = [&](const float4* m, int buf) {
+#pragma unroll
+    for (int j = 0; j < kMPieces; ++j) {
+      const int e = tid + kThreads * j;
+      const float v[4] = {m[j].x, m[j].y, m[j].z, m[j].w};
+      PolBF16x3::store4(Ms[buf], kMPlane, (e >> 5) * kHRow + 8 * (e & 31), v);
+    }
+  };
+
+  for (int e = tid; e < kD * kCols; e += kThreads) {
+    const int r = e / kCols, c = e % kCols;
+    const float x = S_in0 ? S_in0[h * tile + int64_t(r) * kD + c0 + c] : 0.0f;
+    curT[c][r] = x;
+    PolBF16x3::store1(curB, kBPlane, c * kHRow + 2 * r, x);
+  }
+  StepOps X0, X1;
+  if (n_seg > 0) {
+    float4 m0[kMPieces];
+    const float* src = M + seg_base(0);
+#pragma unroll
+    for (int j = 0; j < kMPieces; ++j) m0[j] = ld_f4(src + 4 * (tid + kThreads * j));
+    store_m(m0, 0);
+    load_ops(X0, 0);
+    load_ops(X1, 1);
+  }
+  __syncthreads();
+
+  auto publish = [&](int i) {
+    float* dst = (i < n_seg) ? S_in + (int64_t(i) * H + h) * tile : S_final ? S_final + h * tile : nullptr;
+    if (dst != nullptr) {
+      const int r = tid / (kCols / 4), c4 = 4 * (tid % (kCols / 4));
+      st_f4(dst + int64_t(r) * kD + c0 + c4, make_float4(curT[c4][r], curT[c4 + 1][r], curT[c4 + 2][r], curT[c4 + 3][r]));
+    }
+  };
+  // S_in(i+1) = M(i) S_in(i) + S~(i), then M(i + 1) into the other buffer and
+  // the operands of step i + 2 into x (indices past the last segment repeat it)
+  auto step = [&](int i, StepOps& x) {
+    publish(i);
+    f32x4_t acc[3];
+    acc[0] = f32x4_t{x.st[0], x.st[1], x.st[2], x.st[3]};
+    acc[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    acc[2] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    PolBF16x3::Frag fa[4], fb[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      fa[s] = PolBF16x3::load(Ms[i & 1], kMPlane, (wave * 16 + n) * kHRow + 2 * (32 * s + 8 * q));
+      fb[s] = PolBF16x3::load(curB, kBPlane, n * kHRow + 2 * (32 * s + 8 * q));
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int p = 0; p < 3; ++p) PolBF16x3::mma_part(acc[p], fa[s], fb[s], p);
+    __syncthreads();  // every wave has read S_in(i) and M(i)
+    {
+      const f32x4_t v = acc[0] + (acc[1] + acc[2]);
+      const float vv[4] = {v[0], v[1], v[2], v[3]};
+      *reinterpret_cast<float4*>(&curT[n][row]) = make_float4(v[0], v[1], v[2], v[3]);
+      PolBF16x3::store4(curB, kBPlane, n * kHRow + 2 * row, vv);
+    }
+    store_m(x.m, (i + 1) & 1);
+    load_ops(x, i + 2);
+    __syncthreads();
+  };
+  // unrolled by two so that the two operand sets keep fixed registers (the
+  // body is straight-line; an odd count ends with one more step)
+  int i = 0;
+  for (; i + 1 < n_seg; i += 2) {
+    step(i, X0);
+    step(i + 1, X1);
+  }
+  if (i < n_seg) step(i, X0);
+  publish(n_seg);
+}
+
 }  // namespace
 
 hipError_t launch_compose(const float* M, const float* S_tilde, const float* S_in0, float* S_in,
-                          float* S_final, int n_seg, int H, hipStream_t stream) {
+                          float* S_final, int n_seg, int H, bool split_operands, hipStream_t stream) {
   const unsigned blocks = unsigned(((H + 7) / 8) * 64);
-  if (int64_t(blocks) <= device_cu_count())
+  if (split_operands)
+    hipLaunchKernelGGL(kda_compose_split_kernel, dim3(blocks), dim3(kThreads), 0, stream, M, S_tilde, S_in0,
+                       S_in, S_final, n_seg, H);
+  else if (int64_t(blocks) <= device_cu_count())
     hipLaunchKernelGGL(kda_compose_staged_kernel, dim3(blocks), dim3(kThreads), 0, stream, M, S_tilde, S_in0,
                        S_in, S_final, n_seg, H);
   else

@@ -48,8 +48,9 @@ hipError_t launch_copy_probe(const float* src, float* dst, int64_t n, hipStream_
 // blocks x 256 x 4 floats.  mfma_probe_flops: the flops one launch performs.
 hipError_t launch_mfma_probe(float* out, int blocks, int iters, hipStream_t stream);
 int64_t mfma_probe_flops(int blocks, int iters);
+// split_operands: bf16 MFMA on hi/lo split operands instead of fp32 MFMA
 hipError_t launch_compose(const float* M, const float* S_tilde, const float* S_in0, float* S_in,
-                          float* S_final, int n_seg, int H, hipStream_t stream);
+                          float* S_final, int n_seg, int H, bool split_operands, hipStream_t stream);
 
 // ---- chunked prefill (kda_prefill.hip) ------------------------------------
 struct PrefillLaunch {

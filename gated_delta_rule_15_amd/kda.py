@@ -502,10 +502,12 @@ def kda_prefill_checkpointed(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, ckpt
     return o, final_state, checkpoints[:n_ckpt]
 
 
-def kda_compose_segments(M, S_tilde, S_in0=None, S_in=None, S_final=None, with_final: bool = True):
+def kda_compose_segments(M, S_tilde, S_in0=None, S_in=None, S_final=None, with_final: bool = True,
+                         split_bf16: bool = False):
     """Entry states of consecutive segments: S_in[0] = S_in0, S_in[i+1] = M[i] S_in[i] + S~[i].
 
-    M, S_tilde: [n_seg, H, 128, 128] fp32.  Returns (S_in, S_final).
+    M, S_tilde: [n_seg, H, 128, 128] fp32.  Returns (S_in, S_final).  ``split_bf16``: products on
+    bf16 MFMA with hi/lo split operands (kda_compose_segments_ex, KDA_COMPOSE_SPLIT_BF16).
     """
     n, H = S_tilde.shape[0], S_tilde.shape[1]
     dev = S_tilde.device
@@ -519,9 +521,10 @@ def kda_compose_segments(M, S_tilde, S_in0=None, S_in=None, S_final=None, with_f
         S_final = torch.empty((H, D, D), dtype=torch.float32, device=dev)
     _need(S_final, "S_final", (H, D, D), torch.float32, dev)
     lib = _lib.load()
-    _lib.check(lib.kda_compose_segments(_ptr(M), _ptr(S_tilde), _ptr(S_in0), _ptr(S_in), _ptr(S_final), n, H, D, D,
-                                        _stream()),
-               "kda_compose_segments")
+    flags = _lib.KDA_COMPOSE_SPLIT_BF16 if split_bf16 else 0
+    _lib.check(lib.kda_compose_segments_ex(_ptr(M), _ptr(S_tilde), _ptr(S_in0), _ptr(S_in), _ptr(S_final), n, H, D,
+                                           D, flags, _stream()),
+               "kda_compose_segments_ex")
     return S_in, S_final
 
 

@@ -11,9 +11,10 @@ segment computes its outputs):
   pass 1   kda_prefill over the segments 0..n-2 of every multi-segment
            sequence: zero entry state, no outputs; final state = S~, and the
            transition M (transition_out).
-  compose  kda_compose_segments per multi-segment sequence: entry states
+  compose  kda_compose_segments_ex per multi-segment sequence: entry states
            S_in(i+1) = M(i) S_in(i) + S~(i), written straight into the rows of
-           pass 2's initial-state buffer.
+           pass 2's initial-state buffer (bf16 inputs: products on split bf16
+           operands, KDA_COMPOSE_SPLIT_BF16).
   pass 2   kda_prefill over every segment of every sequence from its true entry
            state, longest rows started first (kda_prefill_ordered): the
            outputs and the final states.
@@ -115,7 +116,8 @@ def plan_segments(cu_seqlens_host, seg_len: int, cut_longer_than: int = 0) -> Se
 
 def kda_prefill_segmented(q, k, v, g, beta, cu_seqlens_host, seg_len: Optional[int] = 65536, initial_state=None,
                           o=None, final_state=None, scale: float = 1.0, plan: Optional[SegmentPlan] = None,
-                          work: Optional[dict] = None, prologue: Optional[kda.Prologue] = None):
+                          work: Optional[dict] = None, prologue: Optional[kda.Prologue] = None,
+                          compose_split_bf16: Optional[bool] = None):
     """Prefill of a packed ragged batch with long sequences split into segments.
 
     Same arguments and results as ``kda.kda_prefill`` (cu_seqlens_host: CPU
@@ -124,6 +126,8 @@ def kda_prefill_segmented(q, k, v, g, beta, cu_seqlens_host, seg_len: Optional[i
     ``alloc_work`` and the outputs ``o`` and ``final_state`` passed in, a call
     allocates no device memory.  ``prologue``: raw q, k and gate logits, as
     ``kda.kda_prefill(..., prologue=...)``; both passes apply it.
+    ``compose_split_bf16``: run the scan's products on bf16 MFMA with hi/lo split operands (the
+    precision class of the passes' own products on bf16 inputs); default: for bf16 inputs only.
     """
     dev = q.device
     H = q.shape[1]
@@ -139,6 +143,7 @@ def kda_prefill_segmented(q, k, v, g, beta, cu_seqlens_host, seg_len: Optional[i
         final_state = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
     init2, fin2 = work["init2"], work["fin2"]
     ws = work["ws"]
+    split_bf16 = q.dtype == torch.bfloat16 if compose_split_bf16 is None else compose_split_bf16
     # split path with every sequence cut: pass 1 gives every row's (M, S~), so the scan runs through
     # the last segment and yields each sequence's final state (and its first row's entry state);
     # pass 2 then only writes outputs
@@ -164,7 +169,7 @@ def kda_prefill_segmented(q, k, v, g, beta, cu_seqlens_host, seg_len: Optional[i
         if all_cut:
             kda.kda_compose_segments(work["M_all"][r.start:r.stop], work["St_all"][r.start:r.stop],
                                      None if initial_state is None else initial_state[n],
-                                     S_in=init2[r.start:r.stop], S_final=final_state[n])
+                                     S_in=init2[r.start:r.stop], S_final=final_state[n], split_bf16=split_bf16)
             continue
         if ws is not None:
             M, St = work["M_all"][r.start:r.start + nf], work["St_all"][r.start:r.start + nf]
@@ -176,7 +181,7 @@ def kda_prefill_segmented(q, k, v, g, beta, cu_seqlens_host, seg_len: Optional[i
         # compose: entry states of segments 1 .. nf (segment 0's is the sequence's own),
         # written into pass 2's rows; S_in[0] lands on row r.start, which already holds S_in0
         kda.kda_compose_segments(M, St, init2[r.start], S_in=init2[r.start:r.start + nf],
-                                 S_final=init2[r.start + nf])
+                                 S_final=init2[r.start + nf], split_bf16=split_bf16)
 
     # pass 2: every segment from its entry state, longest rows started first
     kda.kda_prefill_ordered(q, k, v, g, beta, work["rows_d"], work["order2"], work["rows_h"], initial_state=init2,

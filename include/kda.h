@@ -412,6 +412,24 @@ kda_status_t kda_compose_segments(const float* M, const float* S_tilde, const fl
                                   int32_t d_k, int32_t d_v, void* stream);
 
 /*
+ * kda_compose_segments_ex — kda_compose_segments with flags (0: the same call):
+ *   KDA_COMPOSE_SPLIT_BF16  run each step's products on bf16 MFMA with both
+ *                           operands split as x = hi + lo (hi = bf16(x),
+ *                           lo = bf16(x - hi); hi*hi + hi*lo + lo*hi, fp32
+ *                           accumulation): about 16 significant bits per
+ *                           operand instead of exact fp32 products, at several
+ *                           times the matrix rate.  The precision class of the
+ *                           chunked prefill's own products on bf16 inputs;
+ *                           results are deterministic but differ in the last
+ *                           bits from the fp32 scan.
+ * Errors as kda_compose_segments; KDA_ERR_INVALID_ARG for other flag bits.
+ */
+#define KDA_COMPOSE_SPLIT_BF16 1
+kda_status_t kda_compose_segments_ex(const float* M, const float* S_tilde, const float* S_in0,
+                                     float* S_in, float* S_final, int32_t n_seg, int32_t H,
+                                     int32_t d_k, int32_t d_v, int32_t flags, void* stream);
+
+/*
  * Batch-invariant row contract ("Kimi K3.1 Pro" inference / zero-mismatch
  * article, LLMNews 2026-11-05, section 6.1 on KDA): prefill and decode share
  * one per-row computation, so a token's output and the stored state are

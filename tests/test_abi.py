@@ -31,7 +31,7 @@ def lib():
 def test_header_declares_the_entry_points():
     syms = declared_symbols()
     for name in ("kda_prefill", "kda_decode_step", "kda_verify_block", "kda_verify_commit",
-                 "kda_compose_segments", "kda_prefill_checkpointed", "kda_prefill_checkpoint_count",
+                 "kda_compose_segments", "kda_compose_segments_ex", "kda_prefill_checkpointed", "kda_prefill_checkpoint_count",
                  "kda_prefill_ordered", "kda_decode_step_prologue", "kda_verify_block_prologue",
                  "kda_verify_commit_prologue", "kda_prefill_prologue", "kda_contract_prefill",
                  "kda_contract_decode", "kda_contract_state", "kda_contract_verify", "kda_contract_commit",
@@ -165,6 +165,11 @@ def test_compose_argument_errors(lib):
     assert lib.kda_compose_segments(None, p, None, p, None, 3, 2, 128, 128, None) == _lib.KDA_ERR_INVALID_ARG
     assert lib.kda_compose_segments(p, p, None, p, None, 3, 2, 32, 128, None) == _lib.KDA_ERR_UNSUPPORTED
     assert lib.kda_compose_segments(None, None, None, None, None, 0, 2, 128, 128, None) == 0
+    for flags in (2, -1, 1 << 30):
+        assert lib.kda_compose_segments_ex(p, p, None, p, None, 3, 2, 128, 128, flags, None) == _lib.KDA_ERR_INVALID_ARG
+    assert lib.kda_compose_segments_ex(None, p, None, p, None, 3, 2, 128, 128, 1, None) == _lib.KDA_ERR_INVALID_ARG
+    assert lib.kda_compose_segments_ex(p, p, None, p, None, 3, 2, 128, 64, 1, None) == _lib.KDA_ERR_UNSUPPORTED
+    assert lib.kda_compose_segments_ex(None, None, None, None, None, 0, 2, 128, 128, 1, None) == 0
 
 
 def test_contract_argument_errors(lib):

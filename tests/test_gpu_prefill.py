@@ -442,6 +442,44 @@ def test_state_and_transition_build_bitwise(dtype):
     _check_transitions(p, M1, f"state+transition build {dtype}")
 
 
+@pytest.mark.parametrize("n_seg", [1, 2, 5, 17])
+def test_compose_split_operands(n_seg):
+    """The scan on bf16 MFMA with hi/lo split operands (KDA_COMPOSE_SPLIT_BF16): each product keeps
+    about 16 significant bits per operand (hi*hi + hi*lo + lo*hi, the dropped lo*lo and the two
+    roundings below 2^-16 relative), so the entry states stay within 5e-5 of the fp64 scan over 17
+    steps; results are deterministic and the same for a head whatever the grid (3 heads: one round
+    of workgroups; 40 heads: 320 workgroups, more than the CUs)."""
+    from gated_delta_rule_15_amd.kda import kda_compose_segments
+    rng = np.random.default_rng(70 + n_seg)
+    H = 40
+    M = (rng.standard_normal((n_seg, H, 128, 128)) / np.sqrt(128)).astype(np.float32)
+    St = rng.standard_normal((n_seg, H, 128, 128)).astype(np.float32)
+    S0 = rng.standard_normal((H, 128, 128)).astype(np.float32)
+    big = kda_compose_segments(to_dev(M), to_dev(St), to_dev(S0), split_bf16=True)
+    again = kda_compose_segments(to_dev(M), to_dev(St), to_dev(S0), split_bf16=True)
+    few = kda_compose_segments(to_dev(np.ascontiguousarray(M[:, :3])), to_dev(np.ascontiguousarray(St[:, :3])),
+                               to_dev(np.ascontiguousarray(S0[:3])), split_bf16=True)
+    # zero entry state, no final state requested
+    zero_in, no_fin = kda_compose_segments(to_dev(np.ascontiguousarray(M[:, :2])),
+                                           to_dev(np.ascontiguousarray(St[:, :2])), None, with_final=False,
+                                           split_bf16=True)
+    torch.cuda.synchronize()
+    assert no_fin is None
+    for a, b in zip(big, again):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    assert torch.equal(big[0][:, :3].contiguous().view(torch.int32), few[0].view(torch.int32))
+    assert torch.equal(big[1][:3].contiguous().view(torch.int32), few[1].view(torch.int32))
+    for h in (0, 2, 39):
+        ref_in, ref_fin = orc.compose(M[:, h], St[:, h], S0[h])
+        check_parity(big[0][:, h], ref_in, 5e-5, [(f"segment {i}", np.s_[i]) for i in range(n_seg)],
+                     tag=f"split compose, head {h}")
+        check_parity(big[1][h], ref_fin, 5e-5, tag=f"split compose, head {h} final")
+    for h in range(2):
+        ref_in, _ = orc.compose(M[:, h], St[:, h], np.zeros((128, 128), np.float32))
+        check_parity(zero_in[:, h], ref_in, 5e-5, [(f"segment {i}", np.s_[i]) for i in range(n_seg)],
+                     tag=f"split compose from zeros, head {h}")
+
+
 @pytest.mark.parametrize("n_seg", [1, 2, 5])
 def test_compose_kernels_agree_bitwise(n_seg):
     """A scan over few heads takes the staged kernel (M through LDS), one over many heads the register
