@@ -69,6 +69,10 @@ struct BF16 {
   __device__ __forceinline__ static void store1(void* base, int64_t idx, float x) {
     reinterpret_cast<uint16_t*>(base)[idx] = uint16_t(f32_to_bf16_rne(x));
   }
+  // one element at byte offset off of a buffer resource (dropped past its range)
+  __device__ __forceinline__ static void bstore1(__amdgpu_buffer_rsrc_t rs, int off, float x) {
+    __builtin_amdgcn_raw_buffer_store_b16(uint16_t(f32_to_bf16_rne(x)), rs, off, 0, 0);
+  }
 };
 
 struct F32 {
@@ -97,6 +101,9 @@ struct F32 {
   }
   __device__ __forceinline__ static void store1(void* base, int64_t idx, float x) {
     reinterpret_cast<float*>(base)[idx] = x;
+  }
+  __device__ __forceinline__ static void bstore1(__amdgpu_buffer_rsrc_t rs, int off, float x) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rs, off, 0, 0);
   }
 };
 

@@ -590,8 +590,13 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
             uf[jb] = Pol::make(v8);
           }
           if (want_o) {
-            char* obase = reinterpret_cast<char*>(a.o) +
-                          ((int64_t(ts) * H + h) * kD + colw) * int64_t(sizeof(typename InT::storage));
+            // the chunk's rows of this head as a buffer resource whose range ends
+            // after row ns - 1: stores of rows past the chunk's end are dropped
+            // by the range check, so none of them needs a branch
+            constexpr int kEs = int(sizeof(typename InT::storage));
+            const int row_bytes = int(H * kD) * kEs;
+            const auto ors = buffer_rsrc(reinterpret_cast<char*>(a.o) + (int64_t(ts) * H + h) * (kD * kEs),
+                                         (ns - 1) * row_bytes + kD * kEs);
             Frag fp[2];
   #pragma unroll
             for (int rt = 0; rt < 2; ++rt)
@@ -609,7 +614,7 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
   #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                   const int r = 16 * rt + 4 * lq + e;
-                  if (r < ns) InT::store1(obase, r * int(H * kD) + 16 * jb + lj, accO[jb][rt][e]);
+                  InT::bstore1(ors, r * row_bytes + (colw + 16 * jb + lj) * kEs, accO[jb][rt][e]);
                 }
           }
         }
