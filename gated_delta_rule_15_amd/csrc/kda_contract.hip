@@ -191,20 +191,22 @@ struct BatchIn {
 template <typename InT, int MR>
 __device__ __forceinline__ void load_batch(BatchIn<InT, MR>& in, const ContractArgs& a, int h, int t0, int nr,
                                            int tid) {
+  // Without branches (a branch around each load made the compiler wait for
+  // every outstanding memory operation where the paths join): rows past nr
+  // read row nr - 1 again, and value threads read v in place of q (unused).
   const int c = tid & (kD - 1);
+  const bool ch = tid < kD;
+  const int64_t head = int64_t(h) * kD + c;
+  const void* p0 = ch ? a.k : a.v;
+  const void* p1 = ch ? a.q : a.v;
+  const float* pf = ch ? a.g + head : a.beta + h;
+  const int64_t fs = ch ? int64_t(a.H) * kD : int64_t(a.H);
 #pragma unroll
   for (int i = 0; i < MR; ++i) {
-    if (i < nr) {
-      const int64_t tok = int64_t(t0 + i) * a.H + h;
-      if (tid < kD) {
-        in.x0[i] = InT::load1raw(a.k, tok * kD + c);
-        in.x1[i] = InT::load1raw(a.q, tok * kD + c);
-        in.f[i] = a.g[tok * kD + c];
-      } else {
-        in.x0[i] = InT::load1raw(a.v, tok * kD + c);
-        in.f[i] = a.beta[tok];
-      }
-    }
+    const int64_t t = t0 + (i < nr ? i : nr - 1);
+    in.x0[i] = InT::load1raw(p0, t * a.H * kD + head);
+    in.x1[i] = InT::load1raw(p1, t * a.H * kD + head);
+    in.f[i] = pf[t * fs];
   }
 }
 
@@ -351,6 +353,12 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : (SPLITW > 1 ? 1 : 2)) void 
       }
     }
     __syncthreads();
+    const int nr_next = min(MR, count - done - nr);  // after a close the next batch starts a chunk
+    // split build (one workgroup per CU, registers to spare): the next batch's
+    // inputs are issued as soon as this batch's are in LDS, a whole pass ahead
+    if constexpr (SPLIT) {
+      if (nr_next > 0) load_batch<InT, MR>(in, a, h, t0 + nr, nr_next, tid);
+    }
     // ---- C2: Gram entries G_k[r, s], G_q[r, s] for s <= r, 8 lanes per entry
     {
       const int ntask = nr * (r0 + 1) + nr * (nr - 1) / 2;  // sum over i of (r0 + i + 1)
@@ -408,7 +416,6 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : (SPLITW > 1 ? 1 : 2)) void 
     // order, so that the association depends on (r, s) only.  Partials wait
     // in vv (residuals) and sq (outputs), which are free by now.  The channel
     // threads form the close factors.
-    const int nr_next = min(MR, count - done - nr);  // after a close the next batch starts a chunk
     if (value_thread) {
       const int j = jv;
       // all MR rows, also those past nr (unused, never stored as results): no
@@ -440,8 +447,14 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : (SPLITW > 1 ? 1 : 2)) void 
       close_factors(L.rk, L.rb, L.gam, kChunk, tid);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // ---- C1: a = S_e^T k_hat and w = S_e^T q_hat for every batch row (wave-local)
-    for (int i = 0; i < nr; ++i) {
+    // ---- C1: a = S_e^T k_hat and w = S_e^T q_hat for every batch row (wave-local);
+    // the split build forms four rows per step, interleaved (rows past nr of the
+    // last step are formed from stale operands into unused slots of aa and ww)
+    constexpr int RB = (SPLIT && MR % 4 == 0) ? 4 : 1;
+    for (int i0 = 0; i0 < nr; i0 += RB)
+#pragma unroll
+    for (int ii = 0; ii < RB; ++ii) {
+      const int i = i0 + ii;
       float pa[CW], pw[CW];
 #pragma unroll
       for (int x = 0; x < CW; ++x) pa[x] = pw[x] = 0.f;
@@ -537,13 +550,23 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : (SPLITW > 1 ? 1 : 2)) void 
         }
       }
       if (a.o != nullptr) {
+        // the pass's rows as a buffer resource ending after row nr - 1: stores of
+        // rows past it are dropped by the range check, without a branch per row
+        constexpr int kEs = int(sizeof(typename InT::storage));
+        const int row_bytes = a.H * kD * kEs;
+        const auto ors = buffer_rsrc(static_cast<char*>(a.o) + (int64_t(t0) * a.H + h) * (kD * kEs),
+                                     (nr - 1) * row_bytes + kD * kEs);
 #pragma unroll
-        for (int i = 0; i < MR; ++i)
-          if (i < nr) InT::store1(a.o, (int64_t(t0 + i) * a.H + h) * kD + j, out[i] + L.ww[i][j]);
+        for (int i = 0; i < MR; ++i) {
+          if constexpr (SPLIT) InT::bstore1(ors, i * row_bytes + j * kEs, out[i] + L.ww[i][j]);
+          else if (i < nr) InT::store1(a.o, (int64_t(t0 + i) * a.H + h) * kD + j, out[i] + L.ww[i][j]);
+        }
       }
     }
     // the next batch's inputs, in flight during the close
-    if (nr_next > 0) load_batch<InT, MR>(in, a, h, t0 + nr, nr_next, tid);
+    if constexpr (!SPLIT) {
+      if (nr_next > 0) load_batch<InT, MR>(in, a, h, t0 + nr, nr_next, tid);
+    }
     __syncthreads();
     p += nr;
     done += nr;
