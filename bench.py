@@ -422,12 +422,17 @@ def bench_contract(steps, warmup, n_sets=8):
         g, beta, cu = to_dev(pf.g), to_dev(pf.beta), to_dev(pf.cu_seqlens)
         o = torch.empty_like(q)
         pools = kda.kda_contract_pools(n_seq, H, "cuda:0")
-        ms = _event_time_ms(lambda: kda.kda_contract_prefill(q, k, v, g, beta, cu, *pools, o=o), 3, 1)
+        # the 12-unit prefill takes the split build, which reads the full chunks' prepared sets from a
+        # workspace (kda_contract_prefill_ex); the 384-unit batch takes the unsplit build, which reads none
+        cu_h = torch.from_numpy(pf.cu_seqlens.copy())
+        ws = kda.kda_contract_prefill_workspace(n_seq * T, H, "cuda:0") if n_seq == 1 else None
+        ms = _event_time_ms(lambda: kda.kda_contract_prefill(q, k, v, g, beta, cu, *pools, cu_seqlens_host=cu_h,
+                                                             o=o, workspace=ws), 3, 1)
         flops = n_seq * T * H * FLOP_PER_TOKEN_HEAD_CONTRACT
         res[f"contract_prefill_{'' if n_seq == 1 else '32x'}4096x12_bf16"] = dict(
             ms=ms, tokens_per_s=n_seq * T / (ms * 1e-3), fp32_tflops=flops / (ms * 1e-3) / 1e12,
-            frac_fp32_valu_peak=flops / (ms * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS)
-        del q, k, v, g, beta, o, pools
+            frac_fp32_valu_peak=flops / (ms * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS, workspace=ws is not None)
+        del q, k, v, g, beta, o, pools, ws
     # verify (read-only) + commit of 8 drafts for 32 requests x 12 heads, each request at its own position
     Nv, G = 32, 8
     posv = rng.integers(0, CONTRACT_CHUNK, Nv)

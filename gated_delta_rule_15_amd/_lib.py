@@ -55,6 +55,9 @@ SIGNATURES = {
                                             _P, _P, _P, _P]),
     "kda_contract_prefill_split": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _F, _P,
                                                   _P, _P, _P, _P, _I, _P]),
+    "kda_contract_prefill_workspace_size": (ctypes.c_size_t, [ctypes.c_int64, _I]),
+    "kda_contract_prefill_ex": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _F, _P, _P,
+                                               _P, _P, _P, _I, _P, ctypes.c_size_t, _P]),
     "kda_contract_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _F, _P, _P, _P, _P,
                                            _P, _P]),
     "kda_contract_state": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),

@@ -394,11 +394,27 @@ kda_status_t kda_contract_prefill_split(const void* q, const void* k, const void
                                         int32_t num_seqs, int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t dtype,
                                         float scale, float* S_pool, float* rows_pool, int32_t* pos_pool,
                                         const int32_t* slots, void* o, int32_t split_width, void* stream) {
+  return kda_contract_prefill_ex(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, num_seqs, H, d_k, d_v, dtype, scale,
+                                 S_pool, rows_pool, pos_pool, slots, o, split_width, nullptr, 0, stream);
+}
+
+size_t kda_contract_prefill_workspace_size(int64_t T_total, int32_t H) {
+  if (T_total <= 0 || H <= 0) return 0;
+  return kda::contract_prefill_workspace_bytes(T_total, H);
+}
+
+kda_status_t kda_contract_prefill_ex(const void* q, const void* k, const void* v, const float* g,
+                                     const float* beta, const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                                     int32_t num_seqs, int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t dtype,
+                                     float scale, float* S_pool, float* rows_pool, int32_t* pos_pool,
+                                     const int32_t* slots, void* o, int32_t split_width, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
   if (split_width != 0 && split_width != 1 && split_width != 2 && split_width != 4) return KDA_ERR_INVALID_ARG;
   if (num_seqs < 0 || H <= 0) return KDA_ERR_INVALID_ARG;
   if (!dims_ok(d_k, d_v) || !dtype_ok(dtype)) return KDA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return KDA_OK;
   if (!cu_seqlens || !S_pool || !rows_pool || !pos_pool) return KDA_ERR_INVALID_ARG;
+  if (workspace && !cu_seqlens_host) return KDA_ERR_INVALID_ARG;
   if (cu_seqlens_host) {
     if (cu_seqlens_host[0] < 0) return KDA_ERR_INVALID_ARG;
     for (int32_t i = 0; i < num_seqs; ++i)
@@ -409,6 +425,11 @@ kda_status_t kda_contract_prefill_split(const void* q, const void* k, const void
   if (!q || !k || !v || !g || !beta) return KDA_ERR_INVALID_ARG;
   kda::ContractLaunch c{q, k, v, g, beta, cu_seqlens, slots, S_pool, rows_pool, pos_pool, o, num_seqs, H, scale};
   c.split = split_width;
+  if (workspace) {
+    c.T_total = cu_seqlens_host[num_seqs];
+    if (workspace_bytes < kda::contract_prefill_workspace_bytes(c.T_total, H)) return KDA_ERR_WORKSPACE;
+    c.workspace = workspace;
+  }
   return hip_status(kda::launch_contract(c, dtype == KDA_BF16, static_cast<hipStream_t>(stream)));
 }
 

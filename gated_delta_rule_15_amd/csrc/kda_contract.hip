@@ -95,6 +95,8 @@ struct ContractArgs {
   int read_only;          // nonzero: outputs only, the pools are not written (verify)
   float* stash;           // verify, or null: per (sequence, head) the rows of its gamma tokens
                           // [gamma][3][128] and the entry state after a chunk closes [128][128]
+  float* prep;            // split prefill, or null: prepared sets of the full chunks, [prep_windows][H][kPrepFloats]
+  int prep_windows;       // 16-token windows of the packed tokens covered by prep
 };
 
 // Rows of the batch being computed (at most MR) next to the open chunk's rows.
@@ -210,6 +212,163 @@ __device__ __forceinline__ void load_batch(BatchIn<InT, MR>& in, const ContractA
   }
 }
 
+// ---- B: cumulative decay in row order, rescaled key and query (channel
+// threads), values and beta (value threads), for rows r0 .. r0 + nr - 1 of the
+// open chunk.  Every row of the pass is formed, without branches: rows past
+// nr are formed from stale inputs, their open-chunk row goes to the discard
+// row, and nothing reads them as results.  stash_rows (verify): each row's key
+// and decay, for a later commit.
+template <typename InT, int MR, bool STASH>
+__device__ __forceinline__ void form_rows(Lds<MR>& L, const BatchIn<InT, MR>& in, float scale, int r0, int nr,
+                                          int tid, float* stash_rows) {
+  if (tid < kD) {
+    const int c = tid;
+    float b = (r0 > 0) ? L.rb[r0 - 1][c] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < MR; ++i) {
+      const float kk = InT::unpack1(in.x0[i]);
+      const float sq = scale * InT::unpack1(in.x1[i]);
+      b = b + in.f[i];
+      const float e = exp_c(b);
+      const int rr = (i < nr) ? r0 + i : kChunk;
+      L.rk[rr][c] = kk;
+      L.rb[rr][c] = b;
+      if constexpr (STASH) {
+        if (i < nr) {
+          float* row = stash_rows + int64_t(i) * kRowFloats;
+          row[c] = kk;
+          row[kD + c] = b;
+        }
+      }
+      L.sq[i][c] = sq;
+      L.kh[i][c] = kk * e;
+      L.qh[i][c] = sq * e;
+    }
+  } else {
+    const int j = tid - kD;
+#pragma unroll
+    for (int i = 0; i < MR; ++i) {
+      L.vv[i][j] = InT::unpack1(in.x0[i]);
+      if (j == 0) L.bt[i] = in.f[i];
+    }
+  }
+}
+
+// ---- C2: Gram entries G_k[r, s], G_q[r, s] for s <= r (rows r of the pass),
+// 8 lanes per entry
+template <int MR>
+__device__ __forceinline__ void gram_entries(Lds<MR>& L, int r0, int nr, int tid, int lane) {
+  const int ntask = nr * (r0 + 1) + nr * (nr - 1) / 2;  // sum over i of (r0 + i + 1)
+  const int cm = 16 * (lane & 7);
+  for (int base = 0; base < ntask; base += kThreads / 8) {
+    const int task = base + (tid >> 3);
+    // task -> (batch row i, earlier row s): row i owns r0 + i + 1 entries from
+    // first(i) = i (r0 + 1) + i (i - 1) / 2, so i is the floor of the root of
+    // first(i) = task, corrected by one either way for the rounding of the root
+    int i = 0;
+    if constexpr (MR > 1) {
+      const int a2 = 2 * r0 + 1;
+      i = int((__builtin_amdgcn_sqrtf(float(a2 * a2 + 8 * task)) - float(a2)) * 0.5f);
+      if ((i + 1) * (r0 + 1) + (i + 1) * i / 2 <= task) ++i;
+      if (i * (r0 + 1) + i * (i - 1) / 2 > task) --i;
+      i = min(i, nr - 1);
+    }
+    const bool valid = task < ntask;
+    const int s = valid ? task - (i * (r0 + 1) + i * (i - 1) / 2) : 0;
+    const int r = r0 + i;
+    float pk = 0.f, pq = 0.f;
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+      const float4 br = *reinterpret_cast<const float4*>(&L.rb[r][cm + 4 * c4]);
+      const float4 bs = *reinterpret_cast<const float4*>(&L.rb[s][cm + 4 * c4]);
+      const float4 kr = *reinterpret_cast<const float4*>(&L.rk[r][cm + 4 * c4]);
+      const float4 ks = *reinterpret_cast<const float4*>(&L.rk[s][cm + 4 * c4]);
+      const float4 qr = *reinterpret_cast<const float4*>(&L.sq[i][cm + 4 * c4]);
+      const float brv[4] = {br.x, br.y, br.z, br.w}, bsv[4] = {bs.x, bs.y, bs.z, bs.w};
+      const float krv[4] = {kr.x, kr.y, kr.z, kr.w}, ksv[4] = {ks.x, ks.y, ks.z, ks.w};
+      const float qrv[4] = {qr.x, qr.y, qr.z, qr.w};
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        const float t = ksv[cc] * exp_c(brv[cc] - bsv[cc]);
+        pk = __builtin_fmaf(krv[cc], t, pk);
+        pq = __builtin_fmaf(qrv[cc], t, pq);
+      }
+    }
+    pk = pk + dpp<0xB1>(pk);  // groups g, g^1
+    pq = pq + dpp<0xB1>(pq);
+    pk = pk + dpp<0x4E>(pk);  // pairs {0,1} + {2,3} within a quad
+    pq = pq + dpp<0x4E>(pq);
+    pk = pk + dpp<0x141>(pk);  // quads {0,1} of each 8 lanes: each lane adds its mirror lane's quad sum
+    pq = pq + dpp<0x141>(pq);
+    if (valid && (lane & 7) == 0) {
+      L.gk[s][i] = pk;
+      L.gq[s][i] = pq;
+    }
+  }
+}
+
+// A full chunk's prepared set (a split prefill with a workspace): everything
+// of a chunk that does not depend on the state, formed chunk-parallel by
+// kda_contract_prep_kernel with the functions the walk uses, so its values are
+// those the walk would form: [16][128] k e^{b} (kh), scale q e^{b} (qh), the
+// close factors k e^{b_15 - b} (kb) and v; the Gram entries [16][16] each
+// (G_k, G_q, as in Lds); beta [16]; e^{b_15} [128].
+constexpr int kPrepKh = 0, kPrepQh = 16 * kD, kPrepKb = 32 * kD, kPrepV = 48 * kD, kPrepGk = 64 * kD,
+              kPrepGq = kPrepGk + kChunk * kChunk, kPrepBt = kPrepGq + kChunk * kChunk, kPrepGam = kPrepBt + kChunk;
+constexpr int kPrepFloats = kPrepGam + kD;  // 8,848 floats (35,392 bytes) per chunk and head
+static_assert(kPrepFloats % 4 == 0, "16-byte pieces");
+
+// A thread's part of a prepared set on its way from the workspace to LDS:
+// pieces tid and tid + 256 of each of the four [16][128] tables, and at most
+// one piece of the small ones.  (Fetching the next pass's set a pass ahead
+// into these registers measured slower than fetching it at the pass's start.)
+struct PrepPieces {
+  float4 t[4][2];
+  float4 gk, gq;  // Gram pieces (tid < 64), or beta / e^{b_15} in gk
+};
+
+__device__ __forceinline__ void fetch_prepared(PrepPieces& x, const float* set, int tid) {
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int e = tid + kThreads * m;
+    x.t[0][m] = ld_f4(set + kPrepKh + 4 * e);
+    x.t[1][m] = ld_f4(set + kPrepQh + 4 * e);
+    x.t[2][m] = ld_f4(set + kPrepKb + 4 * e);
+    x.t[3][m] = ld_f4(set + kPrepV + 4 * e);
+  }
+  constexpr int kSq = kChunk * kChunk / 4;  // 64 pieces per Gram table
+  if (tid < kSq) {
+    x.gk = ld_f4(set + kPrepGk + 4 * tid);
+    x.gq = ld_f4(set + kPrepGq + 4 * tid);
+  } else if (tid < kSq + kChunk / 4 + kD / 4) {
+    x.gk = ld_f4(set + kPrepBt + 4 * (tid - kSq));  // beta and e^{b_15} are contiguous
+  }
+}
+
+__device__ __forceinline__ void store_prepared(Lds<kChunk>& L, const PrepPieces& x, int tid) {
+  constexpr int kRowVec = kD / 4;
+  static_assert(16 * kRowVec == 2 * kThreads, "two pieces of each table per thread");
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int e = tid + kThreads * m;
+    const int r = e / kRowVec, f = 4 * (e % kRowVec);
+    *reinterpret_cast<float4*>(&L.kh[r][f]) = x.t[0][m];
+    *reinterpret_cast<float4*>(&L.qh[r][f]) = x.t[1][m];
+    *reinterpret_cast<float4*>(&L.rk[r][f]) = x.t[2][m];
+    *reinterpret_cast<float4*>(&L.vv[r][f]) = x.t[3][m];
+  }
+  constexpr int kSq = kChunk * kChunk / 4;
+  if (tid < kSq) {
+    const int s = tid / (kChunk / 4), f = 4 * (tid % (kChunk / 4));
+    *reinterpret_cast<float4*>(&L.gk[s][f]) = x.gk;
+    *reinterpret_cast<float4*>(&L.gq[s][f]) = x.gq;
+  } else if (tid < kSq + kChunk / 4) {
+    *reinterpret_cast<float4*>(&L.bt[4 * (tid - kSq)]) = x.gk;
+  } else if (tid < kSq + kChunk / 4 + kD / 4) {
+    *reinterpret_cast<float4*>(&L.gam[4 * (tid - kSq - kChunk / 4)]) = x.gk;
+  }
+}
+
 // SPLITW > 1 (prefill of small grids): SPLITW workgroups per (sequence, head),
 // one per 128 / SPLITW value columns; a lane holds CW = 4 / SPLITW columns of
 // its 16 key rows instead of 4, so the S_e products and the close cost CW / 4
@@ -317,98 +476,35 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : (SPLITW > 1 ? 1 : 2)) void 
     const int r0 = p;
     const int t0 = tok0 + done;
     const bool closes = (r0 + nr == kChunk);
-    // ---- B: cumulative decay in row order, rescaled key and query (channel threads)
-    if (tid < kD) {
-      const int c = tid;
-      float b = (r0 > 0) ? L.rb[r0 - 1][c] : 0.0f;
-      // every row of the pass, without branches: rows past nr are formed from
-      // stale inputs (zeros, or an earlier batch's), their open-chunk row goes
-      // to the discard row, and nothing reads them as results
-#pragma unroll
-      for (int i = 0; i < MR; ++i) {
-        const float kk = InT::unpack1(in.x0[i]);
-        const float sq = a.scale * InT::unpack1(in.x1[i]);
-        b = b + in.f[i];
-        const float e = exp_c(b);
-        const int rr = (i < nr) ? r0 + i : kChunk;
-        L.rk[rr][c] = kk;
-        L.rb[rr][c] = b;
-        if constexpr (STASH) {  // verify: the row's key and decay, for a later commit
-          if (i < nr) {
-            float* row = a.stash + unit_stash + int64_t(done + i) * kRowFloats;
-            row[c] = kk;
-            row[kD + c] = b;
-          }
-        }
-        L.sq[i][c] = sq;
-        L.kh[i][c] = kk * e;
-        L.qh[i][c] = sq * e;
+    // a split prefill's full chunk: its rows, Gram entries and close factors
+    // were prepared by kda_contract_prep_kernel with the same functions
+    bool prepared = false;
+    if constexpr (SPLIT) {
+      prepared = a.prep != nullptr && r0 == 0 && nr == kChunk && t0 / kChunk < a.prep_windows;
+      if (prepared) {
+        PrepPieces pre;
+        fetch_prepared(pre, a.prep + (int64_t(t0 / kChunk) * a.H + h) * kPrepFloats, tid);
+        store_prepared(L, pre, tid);
+      } else {
+        form_rows<InT, MR, false>(L, in, a.scale, r0, nr, tid, nullptr);
       }
     } else {
-      const int j = tid - kD;
-#pragma unroll
-      for (int i = 0; i < MR; ++i) {
-        L.vv[i][j] = InT::unpack1(in.x0[i]);
-        if (j == 0) L.bt[i] = in.f[i];
-      }
+      form_rows<InT, MR, STASH>(L, in, a.scale, r0, nr, tid,
+                                STASH ? a.stash + unit_stash + int64_t(done) * kRowFloats : nullptr);
     }
     __syncthreads();
     const int nr_next = min(MR, count - done - nr);  // after a close the next batch starts a chunk
     // split build (one workgroup per CU, registers to spare): the next batch's
     // inputs are issued as soon as this batch's are in LDS, a whole pass ahead
     if constexpr (SPLIT) {
-      if (nr_next > 0) load_batch<InT, MR>(in, a, h, t0 + nr, nr_next, tid);
+      // (a prepared next pass reads its set instead: it starts a chunk after
+      // this pass closes one)
+      const int t_next = t0 + nr;
+      const bool next_prepared = a.prep != nullptr && closes && nr_next == kChunk && t_next / kChunk < a.prep_windows;
+      if (nr_next > 0 && !next_prepared) load_batch<InT, MR>(in, a, h, t_next, nr_next, tid);
     }
-    // ---- C2: Gram entries G_k[r, s], G_q[r, s] for s <= r, 8 lanes per entry
-    {
-      const int ntask = nr * (r0 + 1) + nr * (nr - 1) / 2;  // sum over i of (r0 + i + 1)
-      const int cm = 16 * (lane & 7);
-      for (int base = 0; base < ntask; base += kThreads / 8) {
-        const int task = base + (tid >> 3);
-        // task -> (batch row i, earlier row s): row i owns r0 + i + 1 entries from
-        // first(i) = i (r0 + 1) + i (i - 1) / 2, so i is the floor of the root of
-        // first(i) = task, corrected by one either way for the rounding of the root
-        int i = 0;
-        if constexpr (MR > 1) {
-          const int a2 = 2 * r0 + 1;
-          i = int((__builtin_amdgcn_sqrtf(float(a2 * a2 + 8 * task)) - float(a2)) * 0.5f);
-          if ((i + 1) * (r0 + 1) + (i + 1) * i / 2 <= task) ++i;
-          if (i * (r0 + 1) + i * (i - 1) / 2 > task) --i;
-          i = min(i, nr - 1);
-        }
-        const bool valid = task < ntask;
-        const int s = valid ? task - (i * (r0 + 1) + i * (i - 1) / 2) : 0;
-        const int r = r0 + i;
-        float pk = 0.f, pq = 0.f;
-#pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) {
-          const float4 br = *reinterpret_cast<const float4*>(&L.rb[r][cm + 4 * c4]);
-          const float4 bs = *reinterpret_cast<const float4*>(&L.rb[s][cm + 4 * c4]);
-          const float4 kr = *reinterpret_cast<const float4*>(&L.rk[r][cm + 4 * c4]);
-          const float4 ks = *reinterpret_cast<const float4*>(&L.rk[s][cm + 4 * c4]);
-          const float4 qr = *reinterpret_cast<const float4*>(&L.sq[i][cm + 4 * c4]);
-          const float brv[4] = {br.x, br.y, br.z, br.w}, bsv[4] = {bs.x, bs.y, bs.z, bs.w};
-          const float krv[4] = {kr.x, kr.y, kr.z, kr.w}, ksv[4] = {ks.x, ks.y, ks.z, ks.w};
-          const float qrv[4] = {qr.x, qr.y, qr.z, qr.w};
-#pragma unroll
-          for (int cc = 0; cc < 4; ++cc) {
-            const float t = ksv[cc] * exp_c(brv[cc] - bsv[cc]);
-            pk = __builtin_fmaf(krv[cc], t, pk);
-            pq = __builtin_fmaf(qrv[cc], t, pq);
-          }
-        }
-        pk = pk + dpp<0xB1>(pk);  // groups g, g^1
-        pq = pq + dpp<0xB1>(pq);
-        pk = pk + dpp<0x4E>(pk);  // pairs {0,1} + {2,3} within a quad
-        pq = pq + dpp<0x4E>(pq);
-        pk = pk + dpp<0x141>(pk);  // quads {0,1} of each 8 lanes: each lane adds its mirror lane's quad sum
-        pq = pq + dpp<0x141>(pq);
-        if (valid && (lane & 7) == 0) {
-          L.gk[s][i] = pk;
-          L.gq[s][i] = pq;
-        }
-      }
-    }
+    // ---- C2: Gram entries (not for a prepared pass)
+    if (!prepared) gram_entries<MR>(L, r0, nr, tid, lane);
     __syncthreads();
     // ---- D1: the sums over the open chunk's earlier rows (value threads), in
     // row order; u_r = beta_r ((v_r - sum_{s<r} G_k[r,s] u_s) - a_r) and
@@ -443,7 +539,7 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : (SPLITW > 1 ? 1 : 2)) void 
         L.vv[i][j] = acc[i];
         L.sq[i][j] = out[i];
       }
-    } else if (tid < kD && closes) {
+    } else if (tid < kD && closes && !prepared) {
       close_factors(L.rk, L.rb, L.gam, kChunk, tid);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -617,6 +713,71 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : (SPLITW > 1 ? 1 : 2)) void 
   }
 }
 
+// Chunk-parallel preparation for a split prefill with a workspace: one
+// workgroup per (16-token window w of the packed tokens, head) forms the
+// prepared set of the full chunk that starts in tokens 16w .. 16w + 15, if
+// any, with the walk's own functions (load_batch, form_rows, gram_entries,
+// close_factors on the same LDS layout).  A sequence's full chunks start
+// (16 - p) % 16 tokens after its start (p = rows its slot holds, read before
+// the walk changes it) and every 16 tokens after that; full chunks are
+// disjoint 16-token ranges, so at most one starts in a window, and the walk
+// finds the chunk starting at token t in window t / 16.
+template <typename InT>
+__global__ __launch_bounds__(kThreads) void kda_contract_prep_kernel(ContractArgs a, int n_windows) {
+  __shared__ __align__(16) Lds<kChunk> L;
+  const int w = blockIdx.x % n_windows;
+  const int h = blockIdx.x / n_windows;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int lo = kChunk * w;
+  // first sequence that ends after token lo
+  int n0 = 0, n1 = a.num_seqs;
+  while (n0 < n1) {
+    const int m = (n0 + n1) / 2;
+    if (a.cu[m + 1] > lo) n1 = m;
+    else n0 = m + 1;
+  }
+  int start = -1;
+  for (int n = n0; n < a.num_seqs && a.cu[n] < lo + kChunk && start < 0; ++n) {
+    const int b0 = a.cu[n], b1 = a.cu[n + 1];
+    const int64_t unit = int64_t(a.slots ? a.slots[n] : n) * a.H + h;
+    const int first = b0 + ((kChunk - (a.pos[unit] & (kChunk - 1))) & (kChunk - 1));
+    const int j = lo > first ? (lo - first + kChunk - 1) / kChunk : 0;
+    const int c = first + kChunk * j;
+    if (c < lo + kChunk && c + kChunk <= b1) start = c;
+  }
+  if (start < 0) return;
+  BatchIn<InT, kChunk> in;
+  load_batch<InT, kChunk>(in, a, h, start, kChunk, tid);
+  form_rows<InT, kChunk, false>(L, in, a.scale, 0, kChunk, tid, nullptr);
+  __syncthreads();
+  gram_entries<kChunk>(L, 0, kChunk, tid, lane);
+  __syncthreads();
+  if (tid < kD) close_factors(L.rk, L.rb, L.gam, kChunk, tid);
+  __syncthreads();
+  float* set = a.prep + (int64_t(w) * a.H + h) * kPrepFloats;
+  constexpr int kRowVec = kD / 4;
+  for (int e = tid; e < 16 * kRowVec; e += kThreads) {
+    const int r = e / kRowVec, f = 4 * (e % kRowVec);
+    st_f4(set + kPrepKh + 4 * e, *reinterpret_cast<const float4*>(&L.kh[r][f]));
+    st_f4(set + kPrepQh + 4 * e, *reinterpret_cast<const float4*>(&L.qh[r][f]));
+    st_f4(set + kPrepKb + 4 * e, *reinterpret_cast<const float4*>(&L.rk[r][f]));
+    st_f4(set + kPrepV + 4 * e, *reinterpret_cast<const float4*>(&L.vv[r][f]));
+  }
+  constexpr int kSq = kChunk * kChunk / 4;
+  if (tid < kSq) {
+    const int s = tid / (kChunk / 4), f = 4 * (tid % (kChunk / 4));
+    st_f4(set + kPrepGk + 4 * tid, *reinterpret_cast<const float4*>(&L.gk[s][f]));
+    st_f4(set + kPrepGq + 4 * tid, *reinterpret_cast<const float4*>(&L.gq[s][f]));
+  } else if (tid < kSq + kChunk / 4) {
+    const int e = tid - kSq;
+    st_f4(set + kPrepBt + 4 * e, *reinterpret_cast<const float4*>(&L.bt[4 * e]));
+  } else if (tid < kSq + kChunk / 4 + kD / 4) {
+    const int e = tid - kSq - kChunk / 4;
+    st_f4(set + kPrepGam + 4 * e, *reinterpret_cast<const float4*>(&L.gam[4 * e]));
+  }
+}
+
 // After a split prefill: the keys and cumulative decays of the new open rows
 // and the new position of each (sequence, head), formed from the inputs with
 // the prefill's arithmetic (the same additions in the same order: from the
@@ -749,7 +910,7 @@ __global__ __launch_bounds__(kThreads) void kda_contract_state_kernel(const floa
 }
 
 template <typename InT, int MR, bool STASH = false>
-hipError_t launch_as(const ContractArgs& a, hipStream_t stream, int split) {
+hipError_t launch_as(ContractArgs a, hipStream_t stream, int split, int prep_windows = 0) {
   const unsigned blocks = unsigned(a.num_seqs) * unsigned(a.H);
   // a prefill with at most one workgroup per 4 (2) CUs splits each (sequence, head)
   // four (two) ways (unless the caller fixed the width); the split builds are
@@ -758,6 +919,13 @@ hipError_t launch_as(const ContractArgs& a, hipStream_t stream, int split) {
     const unsigned cus = unsigned(device_cu_count());
     if (split == 0) split = 4 * blocks <= cus ? 4 : (2 * blocks <= cus ? 2 : 1);
     if (a.cu != nullptr && !a.read_only && split > 1) {
+      if (prep_windows <= 0) a.prep = nullptr;
+      if (a.prep != nullptr) {
+        hipLaunchKernelGGL((kda_contract_prep_kernel<InT>), dim3(unsigned(prep_windows) * unsigned(a.H)),
+                           dim3(kThreads), 0, stream, a, prep_windows);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
       if (split == 4)
         hipLaunchKernelGGL((kda_contract_kernel<InT, MR, false, 4>), dim3(4 * blocks), dim3(kThreads), 0, stream, a);
       else
@@ -768,6 +936,7 @@ hipError_t launch_as(const ContractArgs& a, hipStream_t stream, int split) {
       return hipGetLastError();
     }
   }
+  a.prep = nullptr;  // only the split build reads prepared sets
   hipLaunchKernelGGL((kda_contract_kernel<InT, MR, STASH>), dim3(blocks), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
@@ -777,7 +946,10 @@ hipError_t launch_as(const ContractArgs& a, hipStream_t stream, int split) {
 hipError_t launch_contract(const ContractLaunch& c, bool bf16, hipStream_t stream) {
   if (c.num_seqs == 0) return hipSuccess;
   ContractArgs a{c.q, c.k, c.v, c.g, c.beta, c.cu_seqlens, c.slots, c.S_pool, c.rows_pool, c.pos_pool,
-                 c.o, c.num_seqs, c.H, c.scale, c.gamma, c.counts, c.read_only ? 1 : 0, c.stash};
+                 c.o, c.num_seqs, c.H, c.scale, c.gamma, c.counts, c.read_only ? 1 : 0, c.stash,
+                 c.cu_seqlens != nullptr ? static_cast<float*>(c.workspace) : nullptr,
+                 int((c.T_total + kChunk - 1) / kChunk)};
+  const int prep_windows = a.prep_windows;
   // Rows per pass: 1 for decode, 8 for draft blocks of up to 8 tokens, 16
   // otherwise (a row's arithmetic does not depend on it, only registers do).
   const bool block8 = c.cu_seqlens == nullptr && c.gamma <= 8;
@@ -789,7 +961,11 @@ hipError_t launch_contract(const ContractLaunch& c, bool bf16, hipStream_t strea
   if (c.cu_seqlens == nullptr && c.gamma == 1)
     return bf16 ? launch_as<BF16, 1>(a, stream, 1) : launch_as<F32, 1>(a, stream, 1);
   if (block8) return bf16 ? launch_as<BF16, 8>(a, stream, 1) : launch_as<F32, 8>(a, stream, 1);
-  return bf16 ? launch_as<BF16, kChunk>(a, stream, sp) : launch_as<F32, kChunk>(a, stream, sp);
+  return bf16 ? launch_as<BF16, kChunk>(a, stream, sp, prep_windows) : launch_as<F32, kChunk>(a, stream, sp, prep_windows);
+}
+
+size_t contract_prefill_workspace_bytes(int64_t T_total, int H) {
+  return size_t((T_total + kChunk - 1) / kChunk) * size_t(H) * kPrepFloats * sizeof(float);
 }
 
 hipError_t launch_contract_commit_stash(const float* stash, const int32_t* accepted, const int32_t* slots,

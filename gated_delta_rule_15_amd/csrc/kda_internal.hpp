@@ -107,7 +107,10 @@ struct ContractLaunch {
   bool read_only = false;           // outputs only; the pools are not written (verify)
   float* stash = nullptr;           // verify: [num_seqs, H, gamma * 3 * 128 + 128 * 128] rows and closed state
   int32_t split = 0;                // prefill: workgroups per (sequence, head), 1, 2 or 4; 0 picks by grid size
+  void* workspace = nullptr;        // prefill: contract_prefill_workspace_bytes(T_total, H) bytes, or null
+  int64_t T_total = 0;              // prefill with a workspace: packed tokens (cu_seqlens[num_seqs])
 };
+size_t contract_prefill_workspace_bytes(int64_t T_total, int H);
 
 hipError_t launch_contract(const ContractLaunch& c, bool bf16, hipStream_t stream);
 hipError_t launch_contract_commit_stash(const float* stash, const int32_t* accepted, const int32_t* slots,

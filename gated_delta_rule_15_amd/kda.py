@@ -556,12 +556,15 @@ def _need_pools(S_pool, rows_pool, pos_pool, H, dev):
 
 
 def kda_contract_prefill(q, k, v, g, beta, cu_seqlens, S_pool, rows_pool, pos_pool, cu_seqlens_host=None,
-                         slots=None, o=None, scale: float = 1.0, with_output: bool = True, split_width: int = 0):
+                         slots=None, o=None, scale: float = 1.0, with_output: bool = True, split_width: int = 0,
+                         workspace=None):
     """Packed ragged batch through the row contract, pools updated in place.
 
     q, k, v, g: [T, H, 128]; beta: [T, H]; cu_seqlens: device int32 [N + 1]; slots: int32 [N] pool rows
     (None = 0..N-1).  split_width: workgroups per (sequence, head), 1, 2 or 4 (kda_contract_prefill_split),
-    0 picks by grid size.  Returns o [T, H, 128] (dtype of q) or None."""
+    0 picks by grid size.  workspace: None, "auto" (allocated from kda_contract_prefill_workspace_size; needs
+    cu_seqlens_host) or a device uint8 tensor of at least that size, read by the split build only
+    (kda_contract_prefill_ex).  Returns o [T, H, 128] (dtype of q) or None."""
     T, H, _ = q.shape
     dt = q.dtype
     dev = q.device
@@ -591,12 +594,31 @@ def kda_contract_prefill(q, k, v, g, beta, cu_seqlens, S_pool, rows_pool, pos_po
     lib = _lib.load()
     if split_width not in (0, 1, 2, 4):
         raise ValueError("split_width must be 0, 1, 2 or 4")
-    _lib.check(lib.kda_contract_prefill_split(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
-                                              _ptr(cu_seqlens_host), N, H, D, D, _dtype_code(q), float(scale),
-                                              _ptr(S_pool), _ptr(rows_pool), _ptr(pos_pool), _ptr(slots), _ptr(o),
-                                              int(split_width), _stream()),
+    ws_bytes = 0
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError('workspace must be None, "auto" or a tensor')
+        if cu_seqlens_host is None:
+            raise ValueError("a workspace needs cu_seqlens_host")
+        workspace = kda_contract_prefill_workspace(int(cu_seqlens_host[-1]), H, dev)
+    if workspace is not None:
+        if cu_seqlens_host is None:
+            raise ValueError("a workspace needs cu_seqlens_host")
+        if not workspace.is_cuda or workspace.device != dev or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on the device of q")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _lib.check(lib.kda_contract_prefill_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                                           _ptr(cu_seqlens_host), N, H, D, D, _dtype_code(q), float(scale),
+                                           _ptr(S_pool), _ptr(rows_pool), _ptr(pos_pool), _ptr(slots), _ptr(o),
+                                           int(split_width), _ptr(workspace), ws_bytes, _stream()),
                "kda_contract_prefill")
     return o
+
+
+def kda_contract_prefill_workspace(T_total: int, H: int, device) -> torch.Tensor:
+    """Workspace of kda_contract_prefill_ex for T_total packed tokens and H heads (uint8)."""
+    n = int(_lib.load().kda_contract_prefill_workspace_size(int(T_total), int(H)))
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
 
 
 def kda_contract_decode(q, k, v, g, beta, S_pool, rows_pool, pos_pool, slots=None, o=None, scale: float = 1.0,

@@ -483,6 +483,32 @@ kda_status_t kda_contract_prefill_split(const void* q, const void* k, const void
                                         const int32_t* slots, void* o, int32_t split_width, void* stream);
 
 /*
+ * kda_contract_prefill_ex — kda_contract_prefill_split with a caller
+ * workspace for the split build (the automatic choice for grids of at most
+ * half the compute units' worth of (sequence, head) units, or split_width 2 or
+ * 4).  Every full 16-token chunk of the call, from the chunk grid of its
+ * slot's position, depends on the inputs alone for its decays, rescaled keys
+ * and queries, Gram entries and close factors; with a workspace these are
+ * formed chunk-parallel by a first kernel and read by the walk instead of
+ * formed inside it, with the same functions, so the results are bit-identical
+ * to kda_contract_prefill's.
+ *   workspace : device memory of kda_contract_prefill_workspace_size(T_total, H)
+ *               bytes (T_total = cu_seqlens_host[num_seqs]), caller-owned,
+ *               overwritten; or NULL for kda_contract_prefill_split's behaviour.
+ *               Not read by builds other than the split one.
+ * Errors as kda_contract_prefill_split; with a workspace, KDA_ERR_INVALID_ARG
+ * without cu_seqlens_host and KDA_ERR_WORKSPACE when workspace_bytes is
+ * smaller than the size above.
+ */
+size_t kda_contract_prefill_workspace_size(int64_t T_total, int32_t H);
+kda_status_t kda_contract_prefill_ex(const void* q, const void* k, const void* v, const float* g,
+                                     const float* beta, const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                                     int32_t num_seqs, int32_t H, int32_t d_k, int32_t d_v, kda_dtype_t dtype,
+                                     float scale, float* S_pool, float* rows_pool, int32_t* pos_pool,
+                                     const int32_t* slots, void* o, int32_t split_width, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/*
  * kda_contract_decode — one token per request (inputs laid out as for
  * kda_decode_step: q, k, g [N, H, 128], v [N, H, 128], beta [N, H]) through the
  * contract; o: [N, H, 128] in `dtype`, or NULL.  Reads the entry state and the

@@ -35,7 +35,8 @@ def test_header_declares_the_entry_points():
                  "kda_prefill_ordered", "kda_decode_step_prologue", "kda_verify_block_prologue",
                  "kda_verify_commit_prologue", "kda_prefill_prologue", "kda_contract_prefill",
                  "kda_contract_decode", "kda_contract_state", "kda_contract_verify", "kda_contract_commit",
-                 "kda_contract_commit_stash", "kda_contract_prefill_split",
+                 "kda_contract_commit_stash", "kda_contract_prefill_split", "kda_contract_prefill_ex",
+                 "kda_contract_prefill_workspace_size",
                  "kda_verify_block_record", "kda_verify_commit_record",
                  "kda_copy_probe", "kda_mfma_probe", "kda_status_string", "kda_version"):
         assert name in syms
@@ -198,6 +199,18 @@ def test_contract_argument_errors(lib):
     assert lib.kda_contract_prefill(None, None, None, None, None, p, empty, 2, 2, 128, 128, 1, 1.0, p, p, p, None,
                                     None, None) == 0  # no tokens: nothing to do, inputs may be NULL
     assert lib.kda_contract_prefill(None, p, p, p, p, p, good, 2, 2, 128, 128, 1, 1.0, p, p, p, None, p, None) == E
+    # prefill with a workspace: needs the host offsets and enough bytes (sized from cu_seqlens_host[-1])
+    ex = lambda cu_h, nbytes, w=1: (p, p, p, p, p, p, cu_h, 2, 2, 128, 128, 1, 1.0, p, p, p, None, p, 0, p if w else None,
+                                    nbytes, None)
+    need = lib.kda_contract_prefill_workspace_size(9, 2)
+    assert need == 1 * 2 * 35392  # one 16-token window of 9 tokens, 2 heads, 8,848 floats each
+    assert lib.kda_contract_prefill_workspace_size(17, 3) == 2 * 3 * 35392
+    assert lib.kda_contract_prefill_workspace_size(0, 3) == 0
+    assert lib.kda_contract_prefill_ex(*ex(None, need)) == E
+    assert lib.kda_contract_prefill_ex(*ex(good, need - 1)) == _lib.KDA_ERR_WORKSPACE
+    assert lib.kda_contract_prefill_ex(*ex(bad, need)) == E
+    assert lib.kda_contract_prefill_ex(p, p, p, p, p, p, good, 2, 2, 128, 128, 1, 1.0, p, p, p, None, p, 3, None, 0,
+                                       None) == E  # split width
     assert lib.kda_contract_prefill(p, p, p, p, p, None, good, 2, 2, 128, 128, 1, 1.0, p, p, p, None, p, None) == E
     assert lib.kda_contract_prefill(p, p, p, p, p, p, good, 2, 2, 128, 128, 3, 1.0, p, p, p, None, p, None) == U
     for w in (3, -1, 8):  # split widths other than 0, 1, 2, 4

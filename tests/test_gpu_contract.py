@@ -516,6 +516,48 @@ def test_split_widths_equal_unsplit_bitwise(width):
     _assert_same_state(pools[1], pools[width])
 
 
+@pytest.mark.parametrize("width", [2, 4])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prepared_chunks_equal_walk_bitwise(width, dtype):
+    """With a workspace the split prefill reads each full chunk's decays, rescaled keys and queries,
+    Gram entries and close factors from a chunk-parallel first kernel (kda_contract_prefill_ex): the
+    results equal the split walk without a workspace and the unsplit walk bit for bit, from position 0
+    and from a nonzero open-chunk position, with sequences shorter than a chunk, ending on a close, and
+    pool rows reached through permuted slots."""
+    rng = np.random.default_rng(90 + width)
+    N, H = 9, 2
+    cut = [int(x) for x in rng.integers(0, 20, N)]
+    rest = [int(x) for x in rng.integers(0, 70, N)]
+    rest[2], cut[3], rest[3], cut[4], rest[4] = 16 - cut[2] % 16, 16, 48, 0, 5
+    p = gen.packed_batch(seed=90 + width, seqlens=[a + b for a, b in zip(cut, rest)], H=H, dtype=dtype,
+                         init_state=True)
+    slots = torch.tensor(list(reversed(range(N))), dtype=torch.int32, device=DEV)
+    runs = {"unsplit": dict(split_width=1), "split": dict(split_width=width),
+            "prepared": dict(split_width=width, workspace="auto")}
+    pools = {name: _pools(p) for name in runs}
+    outs = {}
+    for name, kw in runs.items():
+        o1 = _prefill(_slice(p, [(0, c) for c in cut]), pools[name], slots=slots, **kw)
+        o2 = _prefill(_slice(p, [(c, c + r) for c, r in zip(cut, rest)]), pools[name], slots=slots, **kw)
+        outs[name] = (o1, o2)
+    for name in ("split", "prepared"):
+        for a, b in zip(outs["unsplit"], outs[name]):
+            assert torch.equal(_bits(a), _bits(b)), name
+        _assert_same_state(pools["unsplit"], pools[name])
+
+
+def test_prepared_chunks_4096x12_bitwise():
+    """The 4,096-token x 12-head contract prefill (four-way split on a 256-CU part) with and without the
+    workspace: bit-identical outputs, entry states, open rows and positions."""
+    p = gen.packed_batch(seed=31, seqlens=[4096], H=12, dtype="bf16", init_state=True)
+    d = _slice(p, [(0, 4096)])
+    a, b = _pools(p), _pools(p)
+    oa = _prefill(d, a)
+    ob = _prefill(d, b, workspace="auto")
+    assert torch.equal(_bits(oa), _bits(ob))
+    _assert_same_state(a, b)
+
+
 @pytest.mark.parametrize("total", [72, 144])
 def test_split_and_unsplit_prefill_are_bit_identical(total):
     """The automatic split width: a grid of at most CUs / 4 (CUs / 2) (sequence, head) units splits
