@@ -1197,16 +1197,19 @@ size_t prefill_workspace_bytes(int64_t num_seqs, int64_t t_end, int64_t H, bool 
 int64_t prefill_workspace_slots(int64_t num_seqs, int64_t t_end) { return (t_end >> 5) + num_seqs + 1; }
 
 hipError_t launch_prefill(const PrefillLaunch& p, bool bf16, hipStream_t stream) {
-  // Large grids (enough (sequence, head) work to fill the chip): 128 value
+  // Large grids (more (sequence, head) units than half the CUs): 128 value
   // columns per workgroup (4 state waves x 32 columns, 4 prep waves), so each
   // chunk is prepared once per head.  Small grids: 64 value columns per
   // workgroup (4 state waves x 16 columns) and 8 prep waves, which shortens
-  // the per-chunk critical path at the cost of preparing each chunk twice;
+  // the per-chunk critical path at the cost of preparing each chunk twice
+  // (two workgroups per unit: past half the CUs they would need a second
+  // round, and one round of the wide shape is faster: segmented 4096 x 12 on
+  // the single-kernel passes, 256-token segments, 0.162 -> 0.138 ms);
   // with a workspace, small grids take the split path instead: every chunk is
   // prepared at once by a chunk-parallel launch, and the walk over the chunks
   // runs the state waves alone.
   const int64_t units = int64_t(p.num_seqs) * p.H * (p.transition_out ? 2 : 1);
-  const bool wide = units >= device_cu_count();
+  const bool wide = 2 * units > device_cu_count();
   if (p.workspace != nullptr && p.checkpoints == nullptr &&
       prefill_split_applies(p.num_seqs, p.H, p.transition_out != nullptr, p.o != nullptr))
     return bf16 ? launch_split<PolBF16x3, BF16>(p, stream) : launch_split<PolF32, F32>(p, stream);

@@ -82,7 +82,7 @@ def test_prefill_packed_batch_with_empty_sequence(dtype):
 
 
 def test_prefill_wide_slices_many_sequences():
-    """>= 256 (sequence, head) pairs select 128-column workgroups."""
+    """More (sequence, head) pairs than half the CUs select 128-column workgroups."""
     lens = [1 + (37 * i) % 150 for i in range(32)]
     p = gen.packed_batch(seed=8, seqlens=lens, H=8, dtype="bf16", init_state=True)
     o, S, _ = _run(p)
@@ -132,7 +132,7 @@ def test_prefill_strong_decay(dtype, gate):
     ("bf16", [300, 64, 65, 0, 1, 200], 3, 64, True),
     ("f32", [300, 64, 65, 0, 1, 200], 3, 64, False),
     ("bf16", [1000, 129, 128], 2, 128, True),
-    ("bf16", [1 + (37 * i) % 300 for i in range(32)], 8, 64, True),   # >= 256 units: 128-column workgroups
+    ("bf16", [1 + (37 * i) % 300 for i in range(32)], 8, 64, True),   # 256 units: 128-column workgroups
 ])
 def test_prefill_checkpoints(dtype, lens, H, interval, init):
     """States after every `interval` tokens of each sequence, against the oracle's chained recurrence."""

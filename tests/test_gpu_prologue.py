@@ -138,7 +138,7 @@ def test_prefill_prologue_matches_oracle(dtype, l2, gate):
 
 
 def test_prefill_prologue_wide_and_transitions():
-    """>= 256 (sequence, head) units (128-column workgroups) with transitions: M of the normalised
+    """More units than half the CUs (128-column workgroups) with transitions: M of the normalised
     keys and mapped gates, so that final = M S0 + S~."""
     from gated_delta_rule_15_amd.kda import kda_prefill
     lens = [1 + (41 * i) % 120 for i in range(34)]
