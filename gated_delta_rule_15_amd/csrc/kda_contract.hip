@@ -321,7 +321,9 @@ static_assert(kPrepFloats % 4 == 0, "16-byte pieces");
 // A thread's part of a prepared set on its way from the workspace to LDS:
 // pieces tid and tid + 256 of each of the four [16][128] tables, and at most
 // one piece of the small ones.  (Fetching the next pass's set a pass ahead
-// into these registers measured slower than fetching it at the pass's start.)
+// into these registers at the start of the pass before measured slower than
+// at the pass's own start; fetching it just before the close, so that it is in
+// flight during the close and the loop's last barrier, saves ~2 %.)
 struct PrepPieces {
   float4 t[4][2];
   float4 gk, gq;  // Gram pieces (tid < 64), or beta / e^{b_15} in gk
@@ -472,6 +474,8 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : (SPLITW > 1 ? 1 : 2)) void 
 
   bool closed = false;
   int done = 0;
+  PrepPieces pre;  // split build: the next prepared pass's set, fetched before this pass's close
+  bool have_pre = false;
   while (true) {
     const int r0 = p;
     const int t0 = tok0 + done;
@@ -482,9 +486,9 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : (SPLITW > 1 ? 1 : 2)) void 
     if constexpr (SPLIT) {
       prepared = a.prep != nullptr && r0 == 0 && nr == kChunk && t0 / kChunk < a.prep_windows;
       if (prepared) {
-        PrepPieces pre;
-        fetch_prepared(pre, a.prep + (int64_t(t0 / kChunk) * a.H + h) * kPrepFloats, tid);
+        if (!have_pre) fetch_prepared(pre, a.prep + (int64_t(t0 / kChunk) * a.H + h) * kPrepFloats, tid);
         store_prepared(L, pre, tid);
+        have_pre = false;
       } else {
         form_rows<InT, MR, false>(L, in, a.scale, r0, nr, tid, nullptr);
       }
@@ -667,7 +671,13 @@ __global__ __launch_bounds__(kThreads, MR == 1 ? 3 : (SPLITW > 1 ? 1 : 2)) void 
     p += nr;
     done += nr;
     if (!closes) break;  // a batch that does not close the chunk ends the sequence
-    // ---- E: close the chunk
+    // ---- E: close the chunk (a prepared next pass's set is fetched first, in flight during the close)
+    if constexpr (SPLIT) {
+      if (a.prep != nullptr && nr_next == kChunk && (t0 + nr) / kChunk < a.prep_windows) {
+        fetch_prepared(pre, a.prep + (int64_t((t0 + nr) / kChunk) * a.H + h) * kPrepFloats, tid);
+        have_pre = true;
+      }
+    }
     close_block(S, L.rk, L.ru, L.gam, kChunk, c0, j0);
     if constexpr (STASH) {  // verify: the closed entry state, for a commit that accepts past the chunk end
       float* Sx = a.stash + unit_stash + int64_t(a.gamma) * kRowFloats;
