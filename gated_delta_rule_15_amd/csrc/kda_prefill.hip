@@ -86,14 +86,16 @@ struct Lds {
   static constexpr int kFLd = 20;                          // fp32 [2 blocks][16][20]
   static constexpr int kFBytes = 2 * 16 * kFLd * 4;
   // one operand set (read by the state waves); Kb^T last, so that the prep
-  // build, which writes it straight to the workspace, keeps only the rest
+  // build, which writes it straight to the workspace, keeps only the rest; the
+  // output operands (Qh, P) just before it, so that a walk without outputs
+  // stages the set in two ranges, [Kh, Qh) and [Kb, end)
   static constexpr int kSetKh = 0;
-  static constexpr int kSetQh = kSetKh + kOpBytes;
-  static constexpr int kSetTp = kSetQh + kOpBytes;
-  static constexpr int kSetP = kSetTp + kSqBytes;
-  static constexpr int kSetGamma = kSetP + kSqBytes;       // e^{b_last - b_mid} per channel
+  static constexpr int kSetTp = kSetKh + kOpBytes;
+  static constexpr int kSetGamma = kSetTp + kSqBytes;      // e^{b_last - b_mid} per channel
   static constexpr int kSetEm = kSetGamma + kD * 4;         // e^{b_mid} per channel
-  static constexpr int kSetKb = kSetEm + kD * 4;
+  static constexpr int kSetQh = kSetEm + kD * 4;
+  static constexpr int kSetP = kSetQh + kOpBytes;
+  static constexpr int kSetKb = kSetP + kSqBytes;
   static constexpr int kSetBytes = kSetKb + kKbBytes;
   static constexpr int kSetInLds = NSETS == 1 ? kSetKb : kSetBytes;  // prep build: the set without Kb^T
   // prep scratch
@@ -424,14 +426,19 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
     // barrier.  (Direct global-to-LDS loads were measured to hold the issuing
     // wave ~110 cycles each; seventeen named registers rather than an array,
     // which the compiler had placed in scratch memory.)
-    constexpr int kN16 = L::kSetBytes / 16;
+    // a walk without outputs skips the output operands, [Qh, Kb): piece x of
+    // what it stages is piece x (below Qh) or x + kSkip16 of the set
+    constexpr int kSkipAt16 = WO ? L::kSetBytes / 16 : L::kSetQh / 16;
+    constexpr int kSkip16 = WO ? 0 : (L::kSetKb - L::kSetQh) / 16;
+    constexpr int kN16 = L::kSetBytes / 16 - kSkip16;
     static_assert(MODE != Mode::State || (kN16 + 64 * SW - 1) / (64 * SW) <= 17, "seventeen staging registers");
     const int64_t slot0 = chunk_slot_base(bos, seq);
 #define KDA_REP17(X) X(0) X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14) X(15) X(16)
 #define KDA_STG_DECL(e) uint4 stg##e;
     constexpr int kStageN = (kN16 + 64 * SW - 1) / (64 * SW);  // loads per thread
-#define KDA_STG_LD(e) if constexpr ((e) < kStageN) stg##e = src_[tid + 64 * SW * (e) < kN16 ? tid + 64 * SW * (e) : kN16 - 1];
-#define KDA_STG_ST(e) if constexpr ((e) < kStageN) { if (tid + 64 * SW * (e) < kN16) dst_[tid + 64 * SW * (e)] = stg##e; }
+#define KDA_STG_PIECE(x) ((x) < kSkipAt16 ? (x) : (x) + kSkip16)
+#define KDA_STG_LD(e) if constexpr ((e) < kStageN) stg##e = src_[KDA_STG_PIECE(tid + 64 * SW * (e) < kN16 ? tid + 64 * SW * (e) : kN16 - 1)];
+#define KDA_STG_ST(e) if constexpr ((e) < kStageN) { if (tid + 64 * SW * (e) < kN16) dst_[KDA_STG_PIECE(tid + 64 * SW * (e))] = stg##e; }
     KDA_REP17(KDA_STG_DECL)
     // (the loads are unconditional, chunk index clamped to the last chunk, so
     // the compiler's wait for the v loads before them is not widened over a
