@@ -143,10 +143,11 @@ __global__ __launch_bounds__(kThreads) void kda_compose_kernel(const float* __re
 // Staged variant for grids that leave CUs idle (at most one workgroup per CU:
 // its LDS holds two copies of M): each segment's M is loaded with coalesced
 // 16-byte loads after the current product's MFMAs were issued, written to the
-// free LDS buffer at the end of the step, and read from LDS as the A operand
-// in the next; the contraction slots and their order are those of
+// free LDS buffer while the step's products run, and read from LDS as the A
+// operand in the next; the contraction slots and their order are those of
 // kda_compose_kernel, so both give the same bits.  The loads leave the matrix
-// section, which measured 2.0-2.1 us per step against 2.5 us.
+// section, which measured 2.0-2.1 us per step against 2.5 us (1.93 us with the
+// staging ahead of the step's first barrier).
 constexpr int kMLd = kD + 4;         // LDS row stride of a staged M (floats)
 constexpr int kMPieces = kD * kD / 4 / kThreads;  // float4 pieces of M per thread (8)
 
@@ -235,16 +236,18 @@ __global__ __launch_bounds__(kThreads) void kda_compose_staged_kernel(const floa
       for (int e = 0; e < 4; ++e)
         acc[e & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], bv[e], acc[e & 1], 0, 0, 0);
     }
-    __syncthreads();  // every wave has read S_in(i) and M(i)
-    {
-      const f32x4v v = acc[0] + acc[1];
-      *reinterpret_cast<float4*>(&curT[n][row]) = make_float4(v[0], v[1], v[2], v[3]);
-    }
-    // M(i+1) (loaded during step i - 1) into the other buffer; then the next loads
+    // while the products run: M(i+1) (loaded during step i - 1) into the other
+    // buffer (last read in step i - 1, before its closing barrier); then the
+    // next loads
     store_m((i + 1) & 1);
     load_st(i + 1);
     __builtin_amdgcn_sched_barrier(0);  // S~ loads first: the next step waits only for them
     load_m(i + 2);
+    __syncthreads();  // every wave has read S_in(i) and M(i), and stored its part of M(i + 1)
+    {
+      const f32x4v v = acc[0] + acc[1];
+      *reinterpret_cast<float4*>(&curT[n][row]) = make_float4(v[0], v[1], v[2], v[3]);
+    }
     __syncthreads();
   }
   publish(n_seg);
@@ -262,9 +265,9 @@ __global__ __launch_bounds__(kThreads) void kda_compose_staged_kernel(const floa
 // q takes the contraction indices k = 32 s + 8 q + e (s = 0..3, e = 0..7), one
 // 16-byte read per plane and operand.  Three accumulators (one per part, the
 // S~ values in the first) are summed as acc0 + (acc1 + acc2).  A step measured
-// 1.8 us against 2.0 us for the fp32 staged kernel: at this size it is bound by
-// moving M (64 KB per step through the load path and LDS), not by the matrix
-// rate.  LDS: 153 KB, one workgroup per CU; larger grids run in rounds.
+// 1.74 us against 1.93 us for the fp32 staged kernel: at this size it is bound
+// by moving M (64 KB per step through the load path and LDS), not by the
+// matrix rate.  LDS: 153 KB, one workgroup per CU; larger grids run in rounds.
 constexpr int kHRow = (kD + 8) * 2;          // bytes per row of a bf16 plane (272: rows 4 banks apart)
 constexpr int kMPlane = kD * kHRow;          // one plane of a staged M
 constexpr int kBPlane = kCols * kHRow;       // one plane of the running slice, [column][row]
@@ -365,15 +368,17 @@ __global__ __launch_bounds__(kThreads) void kda_compose_split_kernel(const float
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int p = 0; p < 3; ++p) PolBF16x3::mma_part(acc[p], fa[s], fb[s], p);
-    __syncthreads();  // every wave has read S_in(i) and M(i)
+    // while the products run: M(i + 1) into the other buffer (last read in
+    // step i - 1, before its closing barrier), then step i + 2's loads
+    store_m(x.m, (i + 1) & 1);
+    load_ops(x, i + 2);
+    __syncthreads();  // every wave has read S_in(i) and M(i), and stored its part of M(i + 1)
     {
       const f32x4_t v = acc[0] + (acc[1] + acc[2]);
       const float vv[4] = {v[0], v[1], v[2], v[3]};
       *reinterpret_cast<float4*>(&curT[n][row]) = make_float4(v[0], v[1], v[2], v[3]);
       PolBF16x3::store4(curB, kBPlane, n * kHRow + 2 * row, vv);
     }
-    store_m(x.m, (i + 1) & 1);
-    load_ops(x, i + 2);
     __syncthreads();
   };
   // unrolled by two so that the two operand sets keep fixed registers (the
