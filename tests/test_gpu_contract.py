@@ -546,6 +546,29 @@ def test_prepared_chunks_equal_walk_bitwise(width, dtype):
         _assert_same_state(pools["unsplit"], pools[name])
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_prepared_chunks_random_batches_bitwise(seed):
+    """Random batches (1-20 sequences of 0-100 tokens, 1-4 heads, resumed from random open-chunk
+    positions, bf16 or fp32): the prefill with a workspace equals the one without, bit for bit."""
+    rng = np.random.default_rng(300 + seed)
+    N, H = int(rng.integers(1, 21)), int(rng.integers(1, 5))
+    dtype = "bf16" if seed % 2 == 0 else "f32"
+    cut = [int(x) for x in rng.integers(0, 40, N)]
+    rest = [int(x) for x in rng.integers(0, 101, N)]
+    p = gen.packed_batch(seed=300 + seed, seqlens=[a + b for a, b in zip(cut, rest)], H=H, dtype=dtype,
+                         init_state=bool(seed % 3))
+    runs = {"walk": {}, "prepared": dict(workspace="auto")}
+    pools = {name: _pools(p) for name in runs}
+    outs = {}
+    for name, kw in runs.items():
+        o1 = _prefill(_slice(p, [(0, c) for c in cut]), pools[name], **kw)
+        o2 = _prefill(_slice(p, [(c, c + r) for c, r in zip(cut, rest)]), pools[name], **kw)
+        outs[name] = (o1, o2)
+    for a, b in zip(outs["walk"], outs["prepared"]):
+        assert torch.equal(_bits(a), _bits(b))
+    _assert_same_state(pools["walk"], pools["prepared"])
+
+
 def test_prepared_chunks_4096x12_bitwise():
     """The 4,096-token x 12-head contract prefill (four-way split on a 256-CU part) with and without the
     workspace: bit-identical outputs, entry states, open rows and positions."""
