@@ -3,6 +3,10 @@
 //   256 threads apart (every load instruction of a wave covers 1 KB of
 //   consecutive bytes), with nontemporal loads and stores as the decode step's
 //   state stream uses; all eight loads are issued before the first store.
+// * memory in the decode step's pattern: the same bytes as a decode of n
+//   states (each 128 x 128 fp32 read once and written once), in the decode
+//   kernel's tiling and lane order but without its arithmetic, so the decode
+//   can be compared with the copy rate of its own access pattern.
 // * matrix: a loop of v_mfma_f32_16x16x32_bf16 (the prefill's product) over
 //   eight independent accumulators per wave, so the matrix pipe never waits on
 //   a result; the accumulators are stored at the end.
@@ -34,6 +38,30 @@ __global__ __launch_bounds__(kThreads) void kda_copy_probe_kernel(const f32x4* _
     const int64_t i = base + int64_t(j) * kThreads;
     if (i < n4) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
   }
+}
+
+// One workgroup of four waves per (state, 64-column half), consecutive
+// workgroups on the two halves of one state; wave w takes the 32-column slice
+// w / 2 of its half and rows 64 (w % 2) .. 64 (w % 2) + 63; lane 8 rg + cg
+// takes rows 8 rg .. 8 rg + 7 of those and columns 4 cg .. 4 cg + 3 of the
+// slice, one 16-byte piece per row, so one load instruction of a wave covers
+// eight 128-byte row segments.  All eight loads precede the stores; src may
+// equal dst (each thread rewrites what it read).
+__global__ __launch_bounds__(kThreads) void kda_copy_probe_state_kernel(const float* src, float* dst) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int cg = lane & 7, rg = lane >> 3;
+  const int64_t state = blockIdx.x >> 1;
+  const int col = 64 * int(blockIdx.x & 1) + 32 * (wave >> 1) + 4 * cg;
+  const int row0 = 64 * (wave & 1) + 8 * rg;
+  const int64_t off = state * (128 * 128) + int64_t(row0) * 128 + col;
+  const f32x4* s = reinterpret_cast<const f32x4*>(src + off);
+  f32x4* d = reinterpret_cast<f32x4*>(dst + off);
+  f32x4 r[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = __builtin_nontemporal_load(s + i * 32);  // row stride: 32 pieces
+#pragma unroll
+  for (int i = 0; i < 8; ++i) __builtin_nontemporal_store(r[i], d + i * 32);
 }
 
 constexpr int kMfmaAcc = 8;  // independent accumulator chains per wave
@@ -85,6 +113,12 @@ hipError_t launch_copy_probe(const float* src, float* dst, int64_t n, hipStream_
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(kda_copy_probe_kernel, dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
                      reinterpret_cast<const f32x4*>(src), reinterpret_cast<f32x4*>(dst), n4);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_probe_state(const float* src, float* dst, int64_t n_states, hipStream_t stream) {
+  if (n_states <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kda_copy_probe_state_kernel, dim3(unsigned(2 * n_states)), dim3(kThreads), 0, stream, src, dst);
   return hipGetLastError();
 }
 

@@ -61,6 +61,20 @@ const char* kda_status_string(kda_status_t status);
 kda_status_t kda_copy_probe(const float* src, float* dst, int64_t n, void* stream);
 
 /*
+ * kda_copy_probe_state — measurement probe, not part of the recurrence:
+ * copies n_states 128 x 128 fp32 matrices (row-major, contiguous) from src to
+ * dst in the access pattern of kda_decode_step's state stream (one workgroup
+ * per 128 x 64 half, each wave load instruction covering eight 128-byte row
+ * segments, nontemporal loads and stores, every load of a thread before its
+ * stores), without the step's arithmetic: the copy rate of the decode's own
+ * pattern, which the decode is compared with.  src == dst copies in place (the
+ * decode updates its state in place); otherwise the ranges must not overlap.
+ * Device buffers, 16-byte aligned.  KDA_ERR_INVALID_ARG for a negative count,
+ * misaligned or null pointers, or partially overlapping ranges; 0 does nothing.
+ */
+kda_status_t kda_copy_probe_state(const float* src, float* dst, int64_t n_states, void* stream);
+
+/*
  * kda_mfma_probe — measurement probe, not part of the recurrence: blocks
  * workgroups of 256 threads, each wave issuing iters x 8 independent
  * v_mfma_f32_16x16x32_bf16 (the prefill's matrix product; iters rounded up

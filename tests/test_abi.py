@@ -38,7 +38,7 @@ def test_header_declares_the_entry_points():
                  "kda_contract_commit_stash", "kda_contract_prefill_split", "kda_contract_prefill_ex",
                  "kda_contract_prefill_workspace_size",
                  "kda_verify_block_record", "kda_verify_commit_record",
-                 "kda_copy_probe", "kda_mfma_probe", "kda_status_string", "kda_version"):
+                 "kda_copy_probe", "kda_copy_probe_state", "kda_mfma_probe", "kda_status_string", "kda_version"):
         assert name in syms
     assert set(syms) == set(_lib.SIGNATURES), "binding signatures and header disagree"
 
@@ -255,6 +255,19 @@ def test_copy_probe_argument_errors(lib):
     assert lib.kda_copy_probe(ctypes.c_void_p((1 << 20) + 4), p, 8, None) == _lib.KDA_ERR_INVALID_ARG
     assert lib.kda_copy_probe(None, p, 8, None) == _lib.KDA_ERR_INVALID_ARG
     assert lib.kda_copy_probe(None, None, 0, None) == _lib.KDA_OK
+
+
+def test_copy_probe_state_argument_errors(lib):
+    """The decode-pattern probe rejects negative counts, null or misaligned buffers and partially
+    overlapping ranges before touching the device; in place (src == dst) and empty calls are accepted."""
+    p = ctypes.c_void_p(1 << 20)
+    state = 128 * 128 * 4
+    assert lib.kda_copy_probe_state(p, p, -1, None) == _lib.KDA_ERR_INVALID_ARG
+    assert lib.kda_copy_probe_state(None, p, 1, None) == _lib.KDA_ERR_INVALID_ARG
+    assert lib.kda_copy_probe_state(ctypes.c_void_p((1 << 20) + 4), ctypes.c_void_p(1 << 24), 1, None) \
+        == _lib.KDA_ERR_INVALID_ARG
+    assert lib.kda_copy_probe_state(p, ctypes.c_void_p((1 << 20) + state), 2, None) == _lib.KDA_ERR_INVALID_ARG
+    assert lib.kda_copy_probe_state(None, None, 0, None) == _lib.KDA_OK
 
 
 def test_mfma_probe_argument_errors(lib):
