@@ -220,13 +220,19 @@ def bench_copy_probe(steps, warmup, n_sets=8):
     states = [torch.ones((64 * 12, D, D), device="cuda:0") for _ in range(n_sets)]
     fns_s = [lambda t=states[i % n_sets]: kda.copy_probe_state(t, t) for i in range(max(100, steps))]
     med_s, lo_s, hi_s = graph_replay_stats_ms(fns_s, warmup)
+    # ... and with the decode's ordering: a workgroup's stores only after all of its loads
+    fns_d = [lambda t=states[i % n_sets]: kda.copy_probe_state(t, t, True) for i in range(max(100, steps))]
+    med_d, _, _ = graph_replay_stats_ms(fns_d, warmup)
     nbytes = 2 * n * 4
     return dict(ms=med, bytes=nbytes, gbps=nbytes / (med * 1e-3) / 1e9, n_sets=n_sets,
                 kernel="kda_copy_probe (nontemporal float4 copy, 8 per thread)",
                 torch_copy_ms=med_t, torch_copy_gbps=nbytes / (med_t * 1e-3) / 1e9,
                 pattern_ms=med_s, pattern_gbps=nbytes / (med_s * 1e-3) / 1e9,
                 pattern_kernel="kda_copy_probe_state (the decode's tiling and lane order, in place, no arithmetic)",
-                pattern_spread_us=[round(lo_s * 1e3, 3), round(hi_s * 1e3, 3)])
+                pattern_spread_us=[round(lo_s * 1e3, 3), round(hi_s * 1e3, 3)],
+                dependent_ms=med_d, dependent_gbps=nbytes / (med_d * 1e-3) / 1e9,
+                dependent_kernel="kda_copy_probe_state, dependent: the same copy with every store of a workgroup "
+                                 "after all of its loads (the decode's ordering)")
 
 
 def bench_mfma_probe(iters=8000, waves_per_simd=2):
@@ -812,7 +818,8 @@ def main():
         copy = bench_copy_probe(args.steps, args.warmup)
         log(f"copy probe (same footprint): {copy['ms'] * 1e3:.2f} us, {copy['gbps']:.0f} GB/s "
             f"(torch copy_ {copy['torch_copy_ms'] * 1e3:.2f} us); in the decode's pattern "
-            f"{copy['pattern_ms'] * 1e3:.2f} us, {copy['pattern_gbps']:.0f} GB/s")
+            f"{copy['pattern_ms'] * 1e3:.2f} us, {copy['pattern_gbps']:.0f} GB/s; with its ordering "
+            f"{copy['dependent_ms'] * 1e3:.2f} us, {copy['dependent_gbps']:.0f} GB/s")
     roof = dict(bound="hbm", achieved=round(dec["gbps"], 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                 frac=round(dec["gbps"] / HBM_PEAK_GBPS, 4), traffic=traffic,
                 kernel="kda_decode_kernel<BF16, false>", algorithmic_bytes_per_launch=dec["bytes"],
@@ -825,6 +832,10 @@ def main():
                 measured_pattern_copy_kernel=copy["pattern_kernel"] if copy else None,
                 # medians over the same replay protocol on both sides
                 median_frac_of_pattern_copy=(round(dec["median_gbps"] / copy["pattern_gbps"], 4)
+                                             if copy and "median_gbps" in dec else None),
+                measured_ordered_copy_gbps=round(copy["dependent_gbps"], 1) if copy else None,
+                measured_ordered_copy_kernel=copy["dependent_kernel"] if copy else None,
+                median_frac_of_ordered_copy=(round(dec["median_gbps"] / copy["dependent_gbps"], 4)
                                              if copy and "median_gbps" in dec else None))
     cpu = None
     if not args.no_cpu_baseline:

@@ -35,7 +35,7 @@ SIGNATURES = {
                                                   _P]),
     "kda_prefill": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _F, _P, _P, _P, _P, _P]),
     "kda_copy_probe": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P]),
-    "kda_copy_probe_state": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P]),
+    "kda_copy_probe_state": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, _P]),
     "kda_mfma_probe": (ctypes.c_int, [_P, _I, _I, _P, _P]),
     "kda_prefill_workspace_size": (ctypes.c_size_t, [_I, ctypes.c_int64, _I, _I, _I, ctypes.c_int, _I]),
     "kda_prefill_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _F, _P, _P, _P,

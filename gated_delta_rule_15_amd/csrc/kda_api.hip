@@ -130,8 +130,8 @@ kda_status_t kda_copy_probe(const float* src, float* dst, int64_t n, void* strea
   return hip_status(kda::launch_copy_probe(src, dst, n, static_cast<hipStream_t>(stream)));
 }
 
-kda_status_t kda_copy_probe_state(const float* src, float* dst, int64_t n_states, void* stream) {
-  if (n_states < 0 || n_states > (int64_t(1) << 30)) return KDA_ERR_INVALID_ARG;
+kda_status_t kda_copy_probe_state(const float* src, float* dst, int64_t n_states, int32_t dependent, void* stream) {
+  if (n_states < 0 || n_states > (int64_t(1) << 30) || (dependent != 0 && dependent != 1)) return KDA_ERR_INVALID_ARG;
   if (n_states == 0) return KDA_OK;
   if (!src || !dst || (reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) % 16 != 0)
     return KDA_ERR_INVALID_ARG;
@@ -140,7 +140,7 @@ kda_status_t kda_copy_probe_state(const float* src, float* dst, int64_t n_states
     const uintptr_t bytes = uintptr_t(n_states) * 128 * 128 * sizeof(float);
     if (a < b + bytes && b < a + bytes) return KDA_ERR_INVALID_ARG;  // partial overlap
   }
-  return hip_status(kda::launch_copy_probe_state(src, dst, n_states, static_cast<hipStream_t>(stream)));
+  return hip_status(kda::launch_copy_probe_state(src, dst, n_states, dependent != 0, static_cast<hipStream_t>(stream)));
 }
 
 const char* kda_status_string(kda_status_t status) {

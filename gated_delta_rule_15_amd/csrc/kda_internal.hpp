@@ -44,7 +44,8 @@ hipError_t launch_commit(const void* k, const void* v, const float* g, const flo
 // ---- segment composition (kda_compose.hip) --------------------------------
 // Memory-roof probe: a nontemporal float4 copy of n floats (n a multiple of 4).
 hipError_t launch_copy_probe(const float* src, float* dst, int64_t n, hipStream_t stream);
-hipError_t launch_copy_probe_state(const float* src, float* dst, int64_t n_states, hipStream_t stream);
+hipError_t launch_copy_probe_state(const float* src, float* dst, int64_t n_states, bool dependent,
+                                   hipStream_t stream);
 // Matrix-roof probe: blocks x 256 threads, each wave iters x 8 bf16 16x16x32 MFMAs; out receives
 // blocks x 256 x 4 floats.  mfma_probe_flops: the flops one launch performs.
 hipError_t launch_mfma_probe(float* out, int blocks, int iters, hipStream_t stream);

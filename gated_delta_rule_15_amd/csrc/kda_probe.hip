@@ -46,7 +46,12 @@ __global__ __launch_bounds__(kThreads) void kda_copy_probe_kernel(const f32x4* _
 // takes rows 8 rg .. 8 rg + 7 of those and columns 4 cg .. 4 cg + 3 of the
 // slice, one 16-byte piece per row, so one load instruction of a wave covers
 // eight 128-byte row segments.  All eight loads precede the stores; src may
-// equal dst (each thread rewrites what it read).
+// equal dst (each thread rewrites what it read).  DEP: no store is issued
+// before every load of the workgroup has completed (a wait for the thread's
+// loads, then a workgroup barrier), the ordering the decode step has (its
+// stores need column sums over all 128 rows); otherwise each store follows
+// its own load.
+template <bool DEP>
 __global__ __launch_bounds__(kThreads) void kda_copy_probe_state_kernel(const float* src, float* dst) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -60,6 +65,10 @@ __global__ __launch_bounds__(kThreads) void kda_copy_probe_state_kernel(const fl
   f32x4 r[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) r[i] = __builtin_nontemporal_load(s + i * 32);  // row stride: 32 pieces
+  if constexpr (DEP) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
 #pragma unroll
   for (int i = 0; i < 8; ++i) __builtin_nontemporal_store(r[i], d + i * 32);
 }
@@ -116,9 +125,15 @@ hipError_t launch_copy_probe(const float* src, float* dst, int64_t n, hipStream_
   return hipGetLastError();
 }
 
-hipError_t launch_copy_probe_state(const float* src, float* dst, int64_t n_states, hipStream_t stream) {
+hipError_t launch_copy_probe_state(const float* src, float* dst, int64_t n_states, bool dependent,
+                                   hipStream_t stream) {
   if (n_states <= 0) return hipSuccess;
-  hipLaunchKernelGGL(kda_copy_probe_state_kernel, dim3(unsigned(2 * n_states)), dim3(kThreads), 0, stream, src, dst);
+  if (dependent)
+    hipLaunchKernelGGL(kda_copy_probe_state_kernel<true>, dim3(unsigned(2 * n_states)), dim3(kThreads), 0, stream,
+                       src, dst);
+  else
+    hipLaunchKernelGGL(kda_copy_probe_state_kernel<false>, dim3(unsigned(2 * n_states)), dim3(kThreads), 0, stream,
+                       src, dst);
   return hipGetLastError();
 }
 

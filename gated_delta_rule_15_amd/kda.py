@@ -286,15 +286,17 @@ def copy_probe(src: torch.Tensor, dst: torch.Tensor) -> None:
     _lib.check(_lib.load().kda_copy_probe(_ptr(src), _ptr(dst), src.numel(), _stream()), "kda_copy_probe")
 
 
-def copy_probe_state(src: torch.Tensor, dst: torch.Tensor) -> None:
+def copy_probe_state(src: torch.Tensor, dst: torch.Tensor, dependent: bool = False) -> None:
     """kda_copy_probe_state: the decode pattern's memory-roof probe, a copy of [..., 128, 128] fp32 states
-    (contiguous device tensors of one shape) in the decode step's tiling; dst may be src (in place)."""
+    (contiguous device tensors of one shape) in the decode step's tiling; dst may be src (in place).
+    ``dependent``: no store before all of the workgroup's loads are in (the decode step's ordering)."""
     if src.dtype != torch.float32 or dst.dtype != torch.float32 or not src.is_cuda or dst.device != src.device:
         raise ValueError("copy_probe_state takes fp32 tensors on one device")
     if not src.is_contiguous() or not dst.is_contiguous() or src.shape != dst.shape or src.dim() < 2 \
             or tuple(src.shape[-2:]) != (D, D):
         raise ValueError("copy_probe_state takes contiguous [..., 128, 128] tensors of one shape")
-    _lib.check(_lib.load().kda_copy_probe_state(_ptr(src), _ptr(dst), src.numel() // (D * D), _stream()),
+    _lib.check(_lib.load().kda_copy_probe_state(_ptr(src), _ptr(dst), src.numel() // (D * D), int(dependent),
+                                                _stream()),
                "kda_copy_probe_state")
 
 

@@ -67,12 +67,16 @@ kda_status_t kda_copy_probe(const float* src, float* dst, int64_t n, void* strea
  * per 128 x 64 half, each wave load instruction covering eight 128-byte row
  * segments, nontemporal loads and stores, every load of a thread before its
  * stores), without the step's arithmetic: the copy rate of the decode's own
- * pattern, which the decode is compared with.  src == dst copies in place (the
- * decode updates its state in place); otherwise the ranges must not overlap.
- * Device buffers, 16-byte aligned.  KDA_ERR_INVALID_ARG for a negative count,
- * misaligned or null pointers, or partially overlapping ranges; 0 does nothing.
+ * pattern, which the decode is compared with.  dependent = 1 also keeps the
+ * decode's ordering: no store of a workgroup is issued before all of its loads
+ * have completed (the step's stores need column sums over every row);
+ * dependent = 0 lets each store follow its own load.  src == dst copies in
+ * place (the decode updates its state in place); otherwise the ranges must not
+ * overlap.  Device buffers, 16-byte aligned.  KDA_ERR_INVALID_ARG for a
+ * negative count, dependent not 0 or 1, misaligned or null pointers, or
+ * partially overlapping ranges; 0 states do nothing.
  */
-kda_status_t kda_copy_probe_state(const float* src, float* dst, int64_t n_states, void* stream);
+kda_status_t kda_copy_probe_state(const float* src, float* dst, int64_t n_states, int32_t dependent, void* stream);
 
 /*
  * kda_mfma_probe — measurement probe, not part of the recurrence: blocks

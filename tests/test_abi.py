@@ -262,12 +262,13 @@ def test_copy_probe_state_argument_errors(lib):
     overlapping ranges before touching the device; in place (src == dst) and empty calls are accepted."""
     p = ctypes.c_void_p(1 << 20)
     state = 128 * 128 * 4
-    assert lib.kda_copy_probe_state(p, p, -1, None) == _lib.KDA_ERR_INVALID_ARG
-    assert lib.kda_copy_probe_state(None, p, 1, None) == _lib.KDA_ERR_INVALID_ARG
-    assert lib.kda_copy_probe_state(ctypes.c_void_p((1 << 20) + 4), ctypes.c_void_p(1 << 24), 1, None) \
+    assert lib.kda_copy_probe_state(p, p, -1, 0, None) == _lib.KDA_ERR_INVALID_ARG
+    assert lib.kda_copy_probe_state(p, p, 1, 2, None) == _lib.KDA_ERR_INVALID_ARG
+    assert lib.kda_copy_probe_state(None, p, 1, 0, None) == _lib.KDA_ERR_INVALID_ARG
+    assert lib.kda_copy_probe_state(ctypes.c_void_p((1 << 20) + 4), ctypes.c_void_p(1 << 24), 1, 0, None) \
         == _lib.KDA_ERR_INVALID_ARG
-    assert lib.kda_copy_probe_state(p, ctypes.c_void_p((1 << 20) + state), 2, None) == _lib.KDA_ERR_INVALID_ARG
-    assert lib.kda_copy_probe_state(None, None, 0, None) == _lib.KDA_OK
+    assert lib.kda_copy_probe_state(p, ctypes.c_void_p((1 << 20) + state), 2, 1, None) == _lib.KDA_ERR_INVALID_ARG
+    assert lib.kda_copy_probe_state(None, None, 0, 1, None) == _lib.KDA_OK
 
 
 def test_mfma_probe_argument_errors(lib):

@@ -18,17 +18,18 @@ def test_copy_probe_copies_exactly(n):
     assert torch.equal(dst[n:], torch.full((4,), 7.0, device="cuda:0"))  # nothing past the end
 
 
+@pytest.mark.parametrize("dependent", [False, True])
 @pytest.mark.parametrize("n_states", [1, 3, 64 * 12])
-def test_copy_probe_state_copies_exactly(n_states):
-    """The decode-pattern copy moves every element of every state (out of place, nothing past the end) and
-    rewrites a state unchanged in place."""
+def test_copy_probe_state_copies_exactly(n_states, dependent):
+    """The decode-pattern copy (either ordering) moves every element of every state (out of place, nothing
+    past the end) and rewrites a state unchanged in place."""
     from gated_delta_rule_15_amd.kda import copy_probe_state
     g = torch.Generator(device="cuda:0").manual_seed(n_states)
     src = torch.randn((n_states, 128, 128), device="cuda:0", generator=g)
     dst = torch.full((n_states + 1, 128, 128), 7.0, device="cuda:0")
-    copy_probe_state(src, dst[:n_states])
+    copy_probe_state(src, dst[:n_states], dependent)
     keep = src.clone()
-    copy_probe_state(src, src)
+    copy_probe_state(src, src, dependent)
     torch.cuda.synchronize()
     assert torch.equal(dst[:n_states].view(torch.int32), keep.view(torch.int32))
     assert torch.equal(dst[n_states:], torch.full((1, 128, 128), 7.0, device="cuda:0"))
