@@ -297,19 +297,26 @@ def bench_verify(reps, warmup, n_sets=8, prologue=False):
     return out
 
 
-def _event_time_ms(run, reps, warmup):
+def _event_time_ms(run, reps, warmup, groups=3):
+    """Mean ms per call of ``reps`` back-to-back calls, timed with events on the current stream after
+    ``warmup`` untimed calls; the median over ``groups`` such timed groups (the first calls over large,
+    freshly written inputs run slower: 32 x 4096 x 12 prefill 1.41 ms in the first group, 1.27 ms after)."""
+    import statistics
     import torch
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(reps):
-        run()
-    end.record()
-    end.synchronize()
-    return start.elapsed_time(end) / reps
+    per = []
+    for _ in range(groups):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(reps):
+            run()
+        end.record()
+        end.synchronize()
+        per.append(start.elapsed_time(end) / reps)
+    return statistics.median(per)
 
 
 def bench_prefill(reps, warmup):
@@ -487,7 +494,7 @@ def bench_contract(steps, warmup, n_sets=8):
 LONG_SUB_SEGMENT = 8192  # each 65,536-token segment of the long sequence runs as 8 fragments
 
 
-def bench_long(reps, warmup=1, gen_workers=None):
+def bench_long(reps, warmup=2, gen_workers=None):
     """1,048,576-token sequence (16 segments of 65,536) + 8 ragged 1K-32K sequences, 12 heads, bf16.
 
     Each 65,536-token segment is computed as eight 8,192-token fragments, so pass 1
@@ -522,17 +529,7 @@ def bench_long(reps, warmup=1, gen_workers=None):
     fs = torch.empty((len(p.cu_seqlens) - 1, H, D, D), device="cuda:0")
     run = lambda: kda_prefill_segmented(q, k, v, g, beta, p.cu_seqlens, initial_state=init, o=o, final_state=fs,
                                         plan=plan, work=work)
-    for _ in range(warmup):
-        run()
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(reps):
-        run()
-    end.record()
-    end.synchronize()
-    ms = start.elapsed_time(end) / reps
+    ms = _event_time_ms(run, reps, warmup)
     th = T * H
     flops = th * FLOP_PER_TOKEN_HEAD_PREFILL
     nbytes = th * BYTES_PER_TOKEN_HEAD_PREFILL_BF16
