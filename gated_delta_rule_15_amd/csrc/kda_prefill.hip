@@ -771,51 +771,86 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
         // rescaling exponent b - b_mid of the chunk lies within the decay of
         // 16 tokens (e^{+-80} at the lower bound g >= -5, inside fp32 range).
         static_assert(TPT == 2 || TPT == 4, "tokens per prep thread");
+        // The four channels' scans run side by side (each step for all four,
+        // then the eight broadcasts together), so their DPP and broadcast
+        // latencies overlap; every value sees the same operations in the same
+        // order as a channel-at-a-time scan.
         float bl[TPT][4], gam[4], emid[4];  // log2 cumulative decay relative to b_mid, per token
+        float bmid[4], blast[4];
+        if constexpr (TPT == 2) {  // one pair per lane, 16 lanes
+          float p[4], y[4];
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            p[e] = gq[0][e] + gq[1][e];
+            y[e] = p[e];
+          }
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] += dpp_shr_in_group<1, NTG>(y[e], tg);
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] += dpp_shr_in_group<2, NTG>(y[e], tg);
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] += dpp_shr_in_group<4, NTG>(y[e], tg);
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] += dpp_shr_in_group<8, NTG>(y[e], tg);
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            bmid[e] = __shfl(y[e], 7, NTG);
+            blast[e] = __shfl(y[e], 15, NTG);
+          }
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float ex = dpp_shr_in_group<1, NTG>(y[e], tg) - bmid[e];
+            bl[0][e] = ex + gq[0][e];
+            bl[1][e] = ex + p[e];
+          }
+        } else {  // pairs 2 tg and 2 tg + 1 in this lane, 8 lanes
+          float p0[4], p1[4], y0[4], y1[4];
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            p0[e] = gq[0][e] + gq[1][e];
+            p1[e] = gq[2][e] + gq[3][e];
+          }
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            y0[e] = p0[e] + dpp_shr_in_group<1, NTG>(p1[e], tg);
+            y1[e] = p1[e] + p0[e];
+          }
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float t0 = dpp_shr_in_group<1, NTG>(y0[e], tg), t1 = dpp_shr_in_group<1, NTG>(y1[e], tg);
+            y0[e] += t0;
+            y1[e] += t1;
+          }
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float t0 = dpp_shr_in_group<2, NTG>(y0[e], tg), t1 = dpp_shr_in_group<2, NTG>(y1[e], tg);
+            y0[e] += t0;
+            y1[e] += t1;
+          }
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float t0 = dpp_shr_in_group<4, NTG>(y0[e], tg), t1 = dpp_shr_in_group<4, NTG>(y1[e], tg);
+            y0[e] += t0;
+            y1[e] += t1;
+          }
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            bmid[e] = __shfl(y1[e], 3, NTG);
+            blast[e] = __shfl(y1[e], 7, NTG);
+          }
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float ex0 = dpp_shr_in_group<1, NTG>(y1[e], tg) - bmid[e], ex1 = y0[e] - bmid[e];
+            bl[0][e] = ex0 + gq[0][e];
+            bl[1][e] = ex0 + p0[e];
+            bl[2][e] = ex1 + gq[2][e];
+            bl[3][e] = ex1 + p1[e];
+          }
+        }
   #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float bmid, blast;
-          if constexpr (TPT == 2) {  // one pair per lane, 16 lanes
-            const float p = gq[0][e] + gq[1][e];
-            float y = p;
-            y += dpp_shr_in_group<1, NTG>(y, tg);
-            y += dpp_shr_in_group<2, NTG>(y, tg);
-            y += dpp_shr_in_group<4, NTG>(y, tg);
-            y += dpp_shr_in_group<8, NTG>(y, tg);
-            bmid = __shfl(y, 7, NTG);
-            blast = __shfl(y, 15, NTG);
-            const float ex = dpp_shr_in_group<1, NTG>(y, tg) - bmid;
-            bl[0][e] = ex + gq[0][e];
-            bl[1][e] = ex + p;
-          } else {  // pairs 2 tg and 2 tg + 1 in this lane, 8 lanes
-            const float p0 = gq[0][e] + gq[1][e], p1 = gq[2][e] + gq[3][e];
-            float y0 = p0 + dpp_shr_in_group<1, NTG>(p1, tg);
-            float y1 = p1 + p0;
-            {
-              const float t0 = dpp_shr_in_group<1, NTG>(y0, tg), t1 = dpp_shr_in_group<1, NTG>(y1, tg);
-              y0 += t0;
-              y1 += t1;
-            }
-            {
-              const float t0 = dpp_shr_in_group<2, NTG>(y0, tg), t1 = dpp_shr_in_group<2, NTG>(y1, tg);
-              y0 += t0;
-              y1 += t1;
-            }
-            {
-              const float t0 = dpp_shr_in_group<4, NTG>(y0, tg), t1 = dpp_shr_in_group<4, NTG>(y1, tg);
-              y0 += t0;
-              y1 += t1;
-            }
-            bmid = __shfl(y1, 3, NTG);
-            blast = __shfl(y1, 7, NTG);
-            const float ex0 = dpp_shr_in_group<1, NTG>(y1, tg) - bmid, ex1 = y0 - bmid;
-            bl[0][e] = ex0 + gq[0][e];
-            bl[1][e] = ex0 + p0;
-            bl[2][e] = ex1 + gq[2][e];
-            bl[3][e] = ex1 + p1;
-          }
-          gam[e] = __builtin_amdgcn_exp2f(blast - bmid);  // e^{b_last - b_mid}
-          emid[e] = __builtin_amdgcn_exp2f(bmid);         // e^{b_mid}
+          gam[e] = __builtin_amdgcn_exp2f(blast[e] - bmid[e]);  // e^{b_last - b_mid}
+          emid[e] = __builtin_amdgcn_exp2f(bmid[e]);            // e^{b_mid}
         }
   #pragma unroll
         for (int rr = 0; rr < TPT; ++rr) {
