@@ -890,6 +890,11 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
         if (pw < 2) {
           // diagonal tile A_II (I = pw), then T_II = (I + A_II)^{-1}
           const int I = pw;
+          // the rows' beta, read before the products (a read after them waited
+          // on the LDS once per row)
+          float bet[4];
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) bet[e] = s_beta[16 * I + 4 * lq + e];
           // two accumulation chains (contraction blocks 0, 1 and 2, 3), summed
           f32x4_t acc2[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
   #pragma unroll
@@ -913,7 +918,7 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
   #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int r = 4 * lq + e;
-              wp[e] = (r > lj) ? acc[e] * s_beta[16 * I + r] : 0.0f;
+              wp[e] = (r > lj) ? acc[e] * bet[e] : 0.0f;
             }
             *reinterpret_cast<float4*>(s_at + (I * 16 + lj) * L::kFLd + 4 * lq) = w;
           }
@@ -953,6 +958,9 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
           f32x4_t acc[NT];
   #pragma unroll
           for (int u = 0; u < NT; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          float bet[4];  // beta of rows 16 + r (A_10), read before the products
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) bet[e] = s_beta[16 + 4 * lq + e];
   #pragma unroll
           for (int ks = 0; ks < 4; ++ks) {
             const int koff = (32 * ks + 8 * lq) * E;
@@ -978,7 +986,7 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
             const f32x4_t& accu = acc[u];
             if (pwt == 2) {
               // A_10 (beta-scaled rows), natural order [r][s] for a 16-deep operand
-              Pol::store1(smem + L::kAop, L::kAopPlane, r * L::kNatRow + lj * E, accu[e] * s_beta[16 + r]);
+              Pol::store1(smem + L::kAop, L::kAopPlane, r * L::kNatRow + lj * E, accu[e] * bet[e]);
             } else if (pwt == 3) {
               Pol::store1(pset + L::kSetP, L::kSqPlane, r * L::kSqRow + kperm(lj) * E, (lj <= r) ? accu[e] : 0.0f);
             } else if (pwt == 4) {
@@ -996,24 +1004,25 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
       {
         if (pw == 0) {
           // T_10 = -T_11 (A_10 T_00)
+          // every LDS read of the step first (T_00, A_10, T_11, beta), then the two products
           const float4 w = *reinterpret_cast<const float4*>(s_td + (0 * 16 + lj) * L::kFLd + 4 * lq);
           const float t00[4] = {w.x, w.y, w.z, w.w};  // rows 4lq.. of column lj of T_00
           const Frag16 fa = Pol::load16(smem + L::kAop, L::kAopPlane, lj * L::kNatRow + 4 * lq * E);
-          const Frag16 fb = Pol::make16(t00);
-          f32x4_t X = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  #pragma unroll
-          for (int p = 0; p < Pol::kParts16; ++p) Pol::mma16_part(X, fa, fb, p);
           // T_11 as the A operand: row lj, columns 4lq .. 4lq+3, read from its fp32 columns
           float t11[4];
   #pragma unroll
           for (int e = 0; e < 4; ++e) t11[e] = s_td[(16 + 4 * lq + e) * L::kFLd + lj];
+          const float bj = s_beta[lj];
+          const Frag16 fb = Pol::make16(t00);
+          f32x4_t X = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+          for (int p = 0; p < Pol::kParts16; ++p) Pol::mma16_part(X, fa, fb, p);
           const Frag16 ft = Pol::make16(t11);
           const float xv[4] = {X[0], X[1], X[2], X[3]};
           const Frag16 fx = Pol::make16(xv);
           f32x4_t Y = f32x4_t{0.f, 0.f, 0.f, 0.f};
   #pragma unroll
           for (int p = 0; p < Pol::kParts16; ++p) Pol::mma16_part(Y, ft, fx, p);
-          const float bj = s_beta[lj];
   #pragma unroll
           for (int e = 0; e < 4; ++e)
             Pol::store1(pset + L::kSetTp, L::kSqPlane, (16 + 4 * lq + e) * L::kSqRow + kperm(lj) * E, -Y[e] * bj);
