@@ -117,7 +117,7 @@ struct Lds {
 // (16 lanes) moves values across the 8-lane groups of a row; those are zeroed.
 template <int D, int G>
 __device__ __forceinline__ float dpp_shr_in_group(float x, int idx_in_group) {
-  const float y = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + D, 0xF, 0xF, false));
+  const float y = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + D, 0xF, 0xF, true));
   if constexpr (G == 16) return y;
   else return idx_in_group >= D ? y : 0.0f;
 }
