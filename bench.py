@@ -353,8 +353,13 @@ def bench_prefill(reps, warmup):
     seg_s = auto_seg_len_split(p.cu_seqlens, 12)
     plan_s = plan_segments(p.cu_seqlens, seg_s)
     work_s = alloc_work(plan_s, 12, q.device, split=True)
-    ms_seg_split = _event_time_ms(lambda: kda_prefill_segmented(q, k, v, g, beta, p.cu_seqlens, o=o2, final_state=S2,
-                                                                plan=plan_s, work=work_s), reps, warmup)
+    seg_split_call = lambda: kda_prefill_segmented(q, k, v, g, beta, p.cu_seqlens, o=o2, final_state=S2, plan=plan_s,
+                                                   work=work_s)
+    ms_seg_split = _event_time_ms(seg_split_call, reps, warmup)
+    # the same calls replayed from a HIP graph (the driver's launches prebuilt; 100 calls per replay)
+    ms_seg_split_graph = None
+    if not EAGER:
+        ms_seg_split_graph, _, _ = graph_replay_stats_ms([seg_split_call] * 100, warmup)
     del work_s
     # checkpoints every 512 tokens (7 per sequence and head) in the single launch
     C = torch.empty((kda.kda_prefill_checkpoint_count(cu_h, 512), 12, D, D), device="cuda:0")
@@ -367,6 +372,8 @@ def bench_prefill(reps, warmup):
     ms_pro = _event_time_ms(lambda: kda.kda_prefill(qr, kr, v, gr, beta, cu, cu_h, o=o, final_state=S, prologue=pro,
                                                     workspace=ws), reps, warmup)
     paths = {"single launch": ms_kernel, "split": ms_split, "segmented": ms_seg, "segmented, split passes": ms_seg_split}
+    if ms_seg_split_graph is not None:
+        paths["segmented, split passes, graph replay"] = ms_seg_split_graph
     path = min(paths, key=paths.get)
     ms = paths[path]
     th = 4096 * 12
@@ -376,7 +383,8 @@ def bench_prefill(reps, warmup):
                 frac_mfma_peak=flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
                 gbps=nbytes / (ms * 1e-3) / 1e9, frac_hbm_peak=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                 path=path, single_launch_ms=ms_kernel, split_ms=ms_split, segmented_ms=ms_seg,
-                segmented_split_passes_ms=ms_seg_split, segment_len_split_passes=seg_s, segment_len=seg,
+                segmented_split_passes_ms=ms_seg_split, segmented_split_passes_graph_ms=ms_seg_split_graph,
+                segment_len_split_passes=seg_s, segment_len=seg,
                 segments=plan.n_rows, single_launch_checkpoints_every_512_ms=ms_ckpt, split_prologue_ms=ms_pro)
 
 

@@ -136,6 +136,32 @@ def test_prefill_in_a_graph():
     _replay_and_check(g, lambda: None, [o, final], expected, 2)
 
 
+def test_segmented_prefill_split_passes_in_a_graph():
+    """The segmented driver on split passes (prep build, pass 1, composition, pass 2, with a preallocated
+    plan, workspace and outputs) is kernel launches only: replays reproduce the eager call bit for bit."""
+    from gated_delta_rule_15_amd.long_context import alloc_work, auto_seg_len_split, kda_prefill_segmented, plan_segments
+    H = 4
+    p = gen.packed_batch(94, [1024], H, dtype="bf16")
+    d = packed_to_dev(p)
+    seg = auto_seg_len_split(p.cu_seqlens, H)
+    plan = plan_segments(p.cu_seqlens, seg)
+    assert plan.n_rows > 1
+    work = alloc_work(plan, H, torch.device(DEV), torch.bfloat16, split=True)
+    assert work["ws"] is not None
+    o = torch.empty((p.T, H, 128), dtype=torch.bfloat16, device=DEV)
+    final = torch.empty((1, H, 128, 128), device=DEV)
+
+    def run():
+        kda_prefill_segmented(d["q"], d["k"], d["v"], d["g"], d["beta"], p.cu_seqlens, o=o, final_state=final,
+                              plan=plan, work=work)
+
+    run()
+    torch.cuda.synchronize()
+    expected = [o.clone(), final.clone()]
+    g = _capture(run)
+    _replay_and_check(g, lambda: None, [o, final], expected, 2)
+
+
 def test_contract_prefill_and_decode_in_a_graph():
     kda = _kda()
     N, H = 4, 4
