@@ -131,7 +131,8 @@ kda_status_t kda_copy_probe(const float* src, float* dst, int64_t n, void* strea
 }
 
 kda_status_t kda_copy_probe_state(const float* src, float* dst, int64_t n_states, int32_t dependent, void* stream) {
-  if (n_states < 0 || n_states > (int64_t(1) << 30) || (dependent != 0 && dependent != 1)) return KDA_ERR_INVALID_ARG;
+  // two workgroups per state: the grid stays below 2^31 workgroups
+  if (n_states < 0 || n_states > (int64_t(1) << 29) || (dependent != 0 && dependent != 1)) return KDA_ERR_INVALID_ARG;
   if (n_states == 0) return KDA_OK;
   if (!src || !dst || (reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) % 16 != 0)
     return KDA_ERR_INVALID_ARG;

@@ -264,6 +264,7 @@ def test_copy_probe_state_argument_errors(lib):
     state = 128 * 128 * 4
     assert lib.kda_copy_probe_state(p, p, -1, 0, None) == _lib.KDA_ERR_INVALID_ARG
     assert lib.kda_copy_probe_state(p, p, 1, 2, None) == _lib.KDA_ERR_INVALID_ARG
+    assert lib.kda_copy_probe_state(p, p, (1 << 29) + 1, 0, None) == _lib.KDA_ERR_INVALID_ARG
     assert lib.kda_copy_probe_state(None, p, 1, 0, None) == _lib.KDA_ERR_INVALID_ARG
     assert lib.kda_copy_probe_state(ctypes.c_void_p((1 << 20) + 4), ctypes.c_void_p(1 << 24), 1, 0, None) \
         == _lib.KDA_ERR_INVALID_ARG
