@@ -73,8 +73,8 @@ kda_status_t kda_copy_probe(const float* src, float* dst, int64_t n, void* strea
  * dependent = 0 lets each store follow its own load.  src == dst copies in
  * place (the decode updates its state in place); otherwise the ranges must not
  * overlap.  Device buffers, 16-byte aligned.  KDA_ERR_INVALID_ARG for a
- * negative count, dependent not 0 or 1, misaligned or null pointers, or
- * partially overlapping ranges; 0 states do nothing.
+ * negative count or one above 2^29, dependent not 0 or 1, misaligned or null
+ * pointers, or partially overlapping ranges; 0 states do nothing.
  */
 kda_status_t kda_copy_probe_state(const float* src, float* dst, int64_t n_states, int32_t dependent, void* stream);
 
