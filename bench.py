@@ -757,7 +757,7 @@ def main():
     log("decode: 64 requests x 12 heads ...")
     if args.only_prefill:
         pf = bench_prefill(reps=5, warmup=2)
-        pb = bench_prefill_batch(reps=5, warmup=2)
+        pb = bench_prefill_batch(reps=10, warmup=3)
         print(json.dumps({"prefill_4096x12_bf16": pf, "prefill_32x4096x12_bf16": pb}), flush=True)
         return
     if args.only_contract:
@@ -781,7 +781,7 @@ def main():
             f"{pf['segmented_ms']:.3f} ms)")
         rows["prefill_4096x12_bf16"] = pf
         log("prefill: 32 sequences x 4096 tokens x 12 heads ...")
-        pb = bench_prefill_batch(reps=max(3, args.steps // 80), warmup=2)
+        pb = bench_prefill_batch(reps=max(10, args.steps // 40), warmup=3)
         log(f"prefill batch: {pb['ms']:.3f} ms, {pb['tokens_per_s'] / 1e6:.1f} M tokens/s")
         rows["prefill_32x4096x12_bf16"] = pb
         log("verify+commit: 32 requests x 12 heads x 8 drafts ...")
