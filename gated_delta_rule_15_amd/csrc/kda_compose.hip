@@ -325,24 +325,6 @@ __global__ __launch_bounds__(kThreads) void kda_compose_split_kernel(const float
     }
   };
 
-  for (int e = tid; e < kD * kCols; e += kThreads) {
-    const int r = e / kCols, c = e % kCols;
-    const float x = S_in0 ? S_in0[h * tile + int64_t(r) * kD + c0 + c] : 0.0f;
-    curT[c][r] = x;
-    PolBF16x3::store1(curB, kBPlane, c * kHRow + 2 * r, x);
-  }
-  StepOps X0, X1;
-  if (n_seg > 0) {
-    float4 m0[kMPieces];
-    const float* src = M + seg_base(0);
-#pragma unroll
-    for (int j = 0; j < kMPieces; ++j) m0[j] = ld_f4(src + 4 * (tid + kThreads * j));
-    store_m(m0, 0);
-    load_ops(X0, 0);
-    load_ops(X1, 1);
-  }
-  __syncthreads();
-
   auto publish = [&](int i) {
     float* dst = (i < n_seg) ? S_in + (int64_t(i) * H + h) * tile : S_final ? S_final + h * tile : nullptr;
     if (dst != nullptr) {
@@ -350,6 +332,38 @@ __global__ __launch_bounds__(kThreads) void kda_compose_split_kernel(const float
       st_f4(dst + int64_t(r) * kD + c0 + c4, make_float4(curT[c4][r], curT[c4 + 1][r], curT[c4 + 2][r], curT[c4 + 3][r]));
     }
   };
+  for (int e = tid; e < kD * kCols; e += kThreads) {
+    const int r = e / kCols, c = e % kCols;
+    const float x = S_in0 ? S_in0[h * tile + int64_t(r) * kD + c0 + c] : 0.0f;
+    curT[c][r] = x;
+    PolBF16x3::store1(curB, kBPlane, c * kHRow + 2 * r, x);
+  }
+  // From a zero entry state the first step is S_in(1) = M(0) 0 + S~(0) = S~(0):
+  // publish the zeros as S_in(0) and start from S~(0) at step 1.
+  const int i0 = (S_in0 == nullptr && n_seg > 0) ? 1 : 0;
+  if (i0 == 1) {
+    __syncthreads();
+    publish(0);
+    __syncthreads();
+    for (int e = tid; e < kD * kCols; e += kThreads) {
+      const int r = e / kCols, c = e % kCols;
+      const float x = S_tilde[seg_base(0) + int64_t(r) * kD + c0 + c];
+      curT[c][r] = x;
+      PolBF16x3::store1(curB, kBPlane, c * kHRow + 2 * r, x);
+    }
+  }
+  StepOps X0, X1;
+  if (n_seg > 0) {
+    float4 m0[kMPieces];
+    const float* src = M + seg_base(i0);
+#pragma unroll
+    for (int j = 0; j < kMPieces; ++j) m0[j] = ld_f4(src + 4 * (tid + kThreads * j));
+    store_m(m0, i0 & 1);
+    load_ops(X0, i0);
+    load_ops(X1, i0 + 1);
+  }
+  __syncthreads();
+
   // S_in(i+1) = M(i) S_in(i) + S~(i), then M(i + 1) into the other buffer and
   // the operands of step i + 2 into x (indices past the last segment repeat it)
   auto step = [&](int i, StepOps& x) {
@@ -383,7 +397,7 @@ __global__ __launch_bounds__(kThreads) void kda_compose_split_kernel(const float
   };
   // unrolled by two so that the two operand sets keep fixed registers (the
   // body is straight-line; an odd count ends with one more step)
-  int i = 0;
+  int i = i0;
   for (; i + 1 < n_seg; i += 2) {
     step(i, X0);
     step(i + 1, X1);
