@@ -110,6 +110,35 @@ struct Lds {
   static_assert(kBytes <= 160 * 1024, "LDS budget");
   static_assert(kOpRow % 16 == 0 && kKbRow % 16 == 0 && kSqRow % 16 == 0 && kSetBytes % 16 == 0, "aligned");
   static_assert(kNatRow % 8 == 0 && (E == 2 || kNatRow % 16 == 0), "aligned natural rows");
+
+  // The set as a workspace holds it: the same regions in the same order, each
+  // row without the 16 bytes of padding it carries in LDS (the padding only
+  // spreads LDS banks; in HBM it would be 12% more bytes to write and read).
+  static constexpr int kGOpRow = kD * E, kGSqRow = kC * E, kGKbRow = kC * E;
+  static constexpr int kGOpBytes = P * kC * kGOpRow, kGSqBytes = P * kC * kGSqRow;
+  static constexpr int kGKbPlane = kD * kGKbRow;
+  static constexpr int kGKh = 0;
+  static constexpr int kGTp = kGKh + kGOpBytes;
+  static constexpr int kGGamma = kGTp + kGSqBytes;
+  static constexpr int kGQh = kGGamma + 2 * kD * 4;        // Gamma and Em
+  static constexpr int kGP = kGQh + kGOpBytes;
+  static constexpr int kGKb = kGP + kGSqBytes;
+  static constexpr int kGBytes = kGKb + P * kGKbPlane;
+  static_assert(kGOpRow % 16 == 0 && kGSqRow % 16 == 0 && kGBytes % 16 == 0, "aligned");
+  static_assert(kOpRow == kGOpRow + 16 && kSqRow == kGSqRow + 16 && kKbRow == kGKbRow + 16, "one pad piece per row");
+  static_assert(kSetEm == kSetGamma + kD * 4 && kSetQh == kSetEm + kD * 4, "Gamma, Em adjacent");
+
+  // LDS 16-byte piece of the set holding workspace piece x: a padded row of n
+  // data pieces takes n + 1 pieces in LDS
+  __device__ __forceinline__ static int lds_piece(int x) {
+    if (x < kGTp / 16) return x + x / (kGOpRow / 16);
+    if (x < kGGamma / 16) { const int r = x - kGTp / 16; return kSetTp / 16 + r + r / (kGSqRow / 16); }
+    if (x < kGQh / 16) return kSetGamma / 16 + (x - kGGamma / 16);
+    if (x < kGP / 16) { const int r = x - kGQh / 16; return kSetQh / 16 + r + r / (kGOpRow / 16); }
+    if (x < kGKb / 16) { const int r = x - kGP / 16; return kSetP / 16 + r + r / (kGSqRow / 16); }
+    const int r = x - kGKb / 16;
+    return kSetKb / 16 + r + r / (kGKbRow / 16);
+  }
 };
 
 // x from lane (lane - D) of the same G-lane group, 0 for the first D lanes of
@@ -428,9 +457,10 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
     // which the compiler had placed in scratch memory.)
     // a walk without outputs skips the output operands, [Qh, Kb): piece x of
     // what it stages is piece x (below Qh) or x + kSkip16 of the set
-    constexpr int kSkipAt16 = WO ? L::kSetBytes / 16 : L::kSetQh / 16;
-    constexpr int kSkip16 = WO ? 0 : (L::kSetKb - L::kSetQh) / 16;
-    constexpr int kN16 = L::kSetBytes / 16 - kSkip16;
+    // (pieces of the workspace layout; each lands at its padded LDS place)
+    constexpr int kSkipAt16 = WO ? L::kGBytes / 16 : L::kGQh / 16;
+    constexpr int kSkip16 = WO ? 0 : (L::kGKb - L::kGQh) / 16;
+    constexpr int kN16 = L::kGBytes / 16 - kSkip16;
     static_assert(MODE != Mode::State || (kN16 + 64 * SW - 1) / (64 * SW) <= 17, "seventeen staging registers");
     const int64_t slot0 = chunk_slot_base(bos, seq);
 #define KDA_REP17(X) X(0) X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14) X(15) X(16)
@@ -438,7 +468,7 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
     constexpr int kStageN = (kN16 + 64 * SW - 1) / (64 * SW);  // loads per thread
 #define KDA_STG_PIECE(x) ((x) < kSkipAt16 ? (x) : (x) + kSkip16)
 #define KDA_STG_LD(e) if constexpr ((e) < kStageN) stg##e = src_[KDA_STG_PIECE(tid + 64 * SW * (e) < kN16 ? tid + 64 * SW * (e) : kN16 - 1)];
-#define KDA_STG_ST(e) if constexpr ((e) < kStageN) { if (tid + 64 * SW * (e) < kN16) dst_[KDA_STG_PIECE(tid + 64 * SW * (e))] = stg##e; }
+#define KDA_STG_ST(e) if constexpr ((e) < kStageN) { if (tid + 64 * SW * (e) < kN16) dst_[L::lds_piece(KDA_STG_PIECE(tid + 64 * SW * (e)))] = stg##e; }
     KDA_REP17(KDA_STG_DECL)
     // (the loads are unconditional, chunk index clamped to the last chunk, so
     // the compiler's wait for the v loads before them is not widened over a
@@ -446,7 +476,7 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
 #define KDA_STAGE_LOAD(c)                                                                               \
     if constexpr (MODE == Mode::State) {                                                                \
       const int64_t c_ = (c) < nch ? (c) : nch - 1;                                                     \
-      const uint4* src_ = reinterpret_cast<const uint4*>(a.ws + ((slot0 + c_) * H + h) * int64_t(L::kSetBytes)); \
+      const uint4* src_ = reinterpret_cast<const uint4*>(a.ws + ((slot0 + c_) * H + h) * int64_t(L::kGBytes));    \
       KDA_REP17(KDA_STG_LD)                                                                             \
     }
 #define KDA_STAGE_STORE(c, set)                                                                         \
@@ -1044,15 +1074,19 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
         // the prep build writes it straight into the chunk's workspace set
         char* kb_set = pset;
         if constexpr (MODE == Mode::Prep)
-          kb_set = a.ws + ((chunk_slot_base(bos, seq) + int64_t(pchunk)) * H + h) * int64_t(L::kSetBytes);
+          kb_set = a.ws + ((chunk_slot_base(bos, seq) + int64_t(pchunk)) * H + h) * int64_t(L::kGBytes);
+        // (in the workspace's layout: unpadded rows)
+        constexpr int kKbAt = MODE == Mode::Prep ? L::kGKb : L::kSetKb;
+        constexpr int kKbRowB = MODE == Mode::Prep ? L::kGKbRow : L::kKbRow;
+        constexpr int kKbPlaneB = MODE == Mode::Prep ? L::kGKbPlane : L::kKbPlane;
   #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int off = (c0 + e) * L::kKbRow + kperm(TPT * tg) * E;
+          const int off = (c0 + e) * kKbRowB + kperm(TPT * tg) * E;
           if constexpr (TPT == 4) {
             const float w4[4] = {kbv[0][e], kbv[1][e], kbv[2][e], kbv[3][e]};
-            Pol::store4(kb_set + L::kSetKb, L::kKbPlane, off, w4);
+            Pol::store4(kb_set + kKbAt, kKbPlaneB, off, w4);
           } else {
-            Pol::store2(kb_set + L::kSetKb, L::kKbPlane, off, kbv[0][e], kbv[1][e]);
+            Pol::store2(kb_set + kKbAt, kKbPlaneB, off, kbv[0][e], kbv[1][e]);
           }
         }
         // prologue: the next chunk's norms (its inputs arrived during this step)
@@ -1064,12 +1098,13 @@ __global__ __launch_bounds__(prefill_threads(SW, PW)) void kda_prefill_kernel(Pr
     }
     if constexpr (MODE == Mode::Prep) {
       // the chunk's operand set, as laid out in LDS, to its workspace slot
-      // (all of it but Kb^T, already there)
-      constexpr int kN16 = L::kSetInLds / 16;
+      // (all of it but Kb^T, already there), without the rows' LDS padding
+      static_assert(L::kSetInLds == L::kSetKb, "the prep build keeps the set up to Kb^T in LDS");
+      constexpr int kN16 = L::kGKb / 16;
       const int64_t slot = chunk_slot_base(bos, seq) + pchunk;
-      uint4* dst = reinterpret_cast<uint4*>(a.ws + (slot * H + h) * int64_t(L::kSetBytes));
+      uint4* dst = reinterpret_cast<uint4*>(a.ws + (slot * H + h) * int64_t(L::kGBytes));
       const uint4* src = reinterpret_cast<const uint4*>(smem);
-      for (int idx = tid; idx < kN16; idx += 64 * PW) dst[idx] = src[idx];
+      for (int idx = tid; idx < kN16; idx += 64 * PW) dst[idx] = src[L::lds_piece(idx)];
     } else {
       // step nch: the state waves consume the last chunk
       __syncthreads();
@@ -1241,7 +1276,7 @@ size_t prefill_workspace_bytes(int64_t num_seqs, int64_t t_end, int64_t H, bool 
                                bool outputs) {
   if (num_seqs <= 0 || !prefill_split_applies(num_seqs, H, transitions, outputs)) return 0;
   const int64_t slots = (t_end >> 5) + num_seqs + 1;
-  const int64_t set = bf16 ? Lds<PolBF16x3>::kSetBytes : Lds<PolF32>::kSetBytes;
+  const int64_t set = bf16 ? Lds<PolBF16x3>::kGBytes : Lds<PolF32>::kGBytes;
   return size_t(slots * H * set);
 }
 

@@ -267,8 +267,8 @@ kda_status_t kda_prefill(const void* q, const void* k, const void* v, const floa
  * 0 means the call takes the single-kernel path and needs none: that is the
  * case when the split path's walk, num_seqs * H (sequence, head) workgroups
  * (twice that when both outputs and transitions are requested), already fills
- * the device's compute units.  Sizes: one operand set (66,560 bytes for bf16
- * inputs, 62,464 for fp32) per 32-token chunk slot and head,
+ * the device's compute units.  Sizes: one operand set (58,368 bytes, for bf16
+ * and fp32 inputs alike) per 32-token chunk slot and head,
  * T_total / 32 + num_seqs + 1 slots.  Returns 0 for invalid arguments
  * (unknown flag bits included).
  */
@@ -330,8 +330,8 @@ kda_status_t kda_prefill_ex(const void* q, const void* k, const void* v, const f
  * the library is loaded on it, kept until the process ends; its size is
  * kda_prefill_noalloc_max_scratch(), 128 MiB).  The call allocates and frees
  * nothing, host or device.  A call whose split path would need more than that
- * (more than about 128 MiB / (66,560 * H) chunk slots of 32 tokens, e.g.
- * 4,096 tokens x 12 heads uses 104 MB) returns KDA_ERR_WORKSPACE; grids that
+ * (more than about 128 MiB / (58,368 * H) chunk slots of 32 tokens, e.g.
+ * 4,096 tokens x 12 heads uses 91 MB) returns KDA_ERR_WORKSPACE; grids that
  * fill the device, and calls without cu_seqlens_host, need no scratch and run
  * the single kernel.  Results are bit-identical to kda_prefill_ex's.
  * Every call on one device shares that device's scratch and finds the last
